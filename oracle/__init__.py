@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for Forecast-driven block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py; never by the HIP library, and it imports nothing
+from the library.
+"""
+from .sparda_ref import (  # noqa: F401
+    Selection,
+    attend_decode,
+    attend_prefill,
+    block_sets,
+    decode_select,
+    decode_step_lookahead,
+    forecast_proj,
+    gather_selected_blocks,
+    kth_gap,
+    kv_block_meanpool,
+    prefill_select,
+    rank_topk,
+)

@@ -1,0 +1,362 @@
+"""Plain fp64 CPU oracle for Forecast-driven block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``,
+and by nothing else.  The HIP library in ``block_sparse_long_kv_amd/`` never
+imports it, and it imports nothing from the library: the two share no code.
+
+Everything here is written for clarity, not speed: numpy float64, one loop per
+(batch, head) or (batch, head, query block), a library matmul / dot / sort as
+the only primitives.  Inputs may be any real numpy dtype (bf16 tensors are
+upcast exactly by the caller); every result is float64 or int64.
+
+Sources (web pages describing SparDA, cited below by tag):
+  [EXPL] "SparDA: a fourth projection that lets sparse attention prefetch its
+         own KV cache" (ai.thesatyajit.com/articles/sparda)
+  [OVW]  Chinese-language SparDA overview, deepresearch2agi.pages.dev
+         ("sparda_sparse_decoupled_attention"); sections named in Chinese.
+  [ABS]  "SparDA: Sparse Decoupled Attention for Efficient Long-Context LLM
+         Inference", abstract (chatpaper.ai / stacks.braintank.ai).
+
+Readings taken where the pages leave a step open (each is repeated at the
+function that uses it):
+  R1  Compressed keys: one plain mean per complete 64-token block; a block that
+      is not complete has no compressed key.
+  R2  Decode query position: the cache holds seq_len tokens including the
+      current one, so the query sits at position seq_len - 1 and its block is
+      cur = (seq_len - 1) // block.
+  R3  Local window: the n_local whole blocks ending at the query's block.
+  R4  Top-k candidates exclude the initial and local blocks and every block
+      after the causal cut: cand = { n_init <= j <= cur - n_local }.
+  R5  Fewer candidates than k: take them all; the index list is padded with -1
+      and the count carries the true size.
+  R6  Equal scores: the lower block index ranks first.
+  R7  Score: the raw dot product F . K~_j, no 1/sqrt(d), no softmax.
+  R8  Prefill: one selection per 64-token query block; its score for block j
+      is the sum over the block's tokens of F_t . K~_j.
+  R9  Attention scale and GQA map are caller-given: scale (normally
+      1/sqrt(d)); query head h reads KV head h // (Hq / Hkv).
+  R10 Prefill causality is per token: a query at position p sees keys at
+      positions <= p inside its selected blocks.
+Parity status: every function below is pinned by tests/test_oracle_pins.py
+(brute force, closed forms, textbook special cases, hand-worked fixtures under
+tests/golden/).  None is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# a1: the Forecast projection
+# --------------------------------------------------------------------------
+def forecast_proj(x, w, n_kv_heads: int, head_dim: int) -> np.ndarray:
+    """F[b, g, :] = x[b, :] @ w[:, g*d:(g+1)*d].
+
+    [EXPL] "The fourth projection", Eq. 3: the per-layer projection phi_l
+    also emits F_l; [OVW] 架构细节 and [EXPL] "One Forecast head per GQA
+    group": one Forecast head per KV head, so w has n_kv_heads * head_dim
+    columns and head g owns the g-th run of head_dim columns.
+    x: [B, hidden]; w: [hidden, n_kv_heads*head_dim].  Returns [B, Hkv, d].
+    """
+    x = _f64(x)
+    w = _f64(w)
+    B, hidden = x.shape
+    if w.shape != (hidden, n_kv_heads * head_dim):
+        raise ValueError(f"w shape {w.shape} != ({hidden}, {n_kv_heads * head_dim})")
+    return np.matmul(x, w).reshape(B, n_kv_heads, head_dim)
+
+
+# --------------------------------------------------------------------------
+# a2: block mean-pooling into compressed keys
+# --------------------------------------------------------------------------
+def kv_block_meanpool(k, block: int, seq_len=None) -> np.ndarray:
+    """K~[b, g, j, :] = mean of the keys at positions block*j .. block*j+block-1.
+
+    [EXPL] "The problem InfLLM-V2 leaves on the table": keys are mean-pooled
+    into compressed representations; [OVW] 架构细节 (block selection uses the
+    mean-compressed keys of the layer); [EXPL] "The fourth projection",
+    Alg. 2 keeps them in a per-layer cache updated incrementally.
+    Reading R1: only complete blocks get a compressed key.
+    k: [B, Hkv, T, d]; seq_len: optional [B] valid token counts (default T).
+    Returns [B, Hkv, T // block, d]; rows of blocks that are not complete for
+    batch b are NaN so that any use of them shows.
+    """
+    k = _f64(k)
+    B, H, T, d = k.shape
+    nb = T // block
+    lens = np.full(B, T, dtype=np.int64) if seq_len is None else np.asarray(seq_len, dtype=np.int64)
+    out = np.full((B, H, nb, d), np.nan)
+    for b in range(B):
+        n_complete = min(int(lens[b]), T) // block
+        for g in range(H):
+            for j in range(n_complete):
+                out[b, g, j] = k[b, g, block * j: block * (j + 1)].mean(axis=0)
+    return out
+
+
+# --------------------------------------------------------------------------
+# a3: scoring, causal top-k, union with the initial and local blocks
+# --------------------------------------------------------------------------
+@dataclass
+class Selection:
+    """Block sets for one selection call.
+
+    idx   int64 [..., U]  ascending block ids of B_init | B_local | B_topk,
+                          padded with -1 (U = topk + n_init + n_local)
+    cnt   int64 [...]     number of valid entries in idx
+    top   list            per problem, the top-k block ids in rank order
+    scores list           per problem, dict block id -> fp64 score (candidates only)
+    """
+    idx: np.ndarray
+    cnt: np.ndarray
+    top: list
+    scores: list
+
+
+def block_sets(cur: int, n_init: int, n_local: int):
+    """Initial, local and candidate block ids for a query whose block is cur.
+
+    [EXPL] "The problem InfLLM-V2 leaves on the table", block-set formula
+    B_l(i) = B_init | B_local(i) | B_topk(i).  Readings R3 and R4: the local
+    window is the n_local blocks ending at cur; the top-k candidates are the
+    causal blocks that are neither initial nor local ([EXPL] "Training",
+    the Eq. 7 selection is taken after the causal mask and without the
+    initial/local blocks).
+    """
+    init = [j for j in range(n_init) if j <= cur]
+    local = list(range(max(0, cur - n_local + 1), cur + 1))
+    cand = list(range(n_init, cur - n_local + 1))
+    return init, local, cand
+
+
+def rank_topk(scores: dict, k: int) -> list:
+    """f_top(s, k): the k best candidates by (score descending, id ascending).
+
+    [EXPL] "The fourth projection", Eq. 4 (f_top) and "One Forecast head per
+    GQA group" (Sec. 4.1 selector: a ranking of the raw scores).  Reading R6
+    breaks ties toward the lower block id; R5 takes all when fewer than k.
+    """
+    order = sorted(scores.keys(), key=lambda j: (-scores[j], j))
+    return order[:k]
+
+
+def _union(init, local, top, cap: int) -> np.ndarray:
+    u = sorted(set(init) | set(local) | set(top))
+    row = np.full(cap, -1, dtype=np.int64)
+    row[: len(u)] = u
+    return row, len(u)
+
+
+def decode_select(f, kc, seq_len, topk: int, n_init: int, n_local: int, block: int) -> Selection:
+    """Block set of one decode step for every (batch, KV head).
+
+    [EXPL] "The fourth projection", Eq. 4 and Alg. 2:
+    B = B_init | B_local | f_top(F . K~^T, k), with F the Forecast that
+    selects this layer (the previous layer's, or the separate layer-0
+    projection, [EXPL] "Training").  Scores are raw dot products (R7,
+    [EXPL] "One Forecast head per GQA group", Sec. 4.1).  Query position by
+    R2.  f: [B, Hkv, d]; kc: [B, Hkv, NB, d]; seq_len: [B].
+    """
+    f = _f64(f)
+    kc = _f64(kc)
+    B, H, d = f.shape
+    lens = np.asarray(seq_len, dtype=np.int64)
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H), dtype=np.int64)
+    tops, all_scores = [], []
+    for b in range(B):
+        cur = (int(lens[b]) - 1) // block
+        init, local, cand = block_sets(cur, n_init, n_local)
+        for g in range(H):
+            scores = {j: float(np.dot(f[b, g], kc[b, g, j])) for j in cand}
+            top = rank_topk(scores, topk)
+            idx[b, g], cnt[b, g] = _union(init, local, top, cap)
+            tops.append(top)
+            all_scores.append(scores)
+    return Selection(idx, cnt, tops, all_scores)
+
+
+def prefill_select(f_tok, kc, q_start: int, topk: int, n_init: int, n_local: int, block: int) -> Selection:
+    """Block sets of a prefill chunk, one per 64-token query block.
+
+    [EXPL] "The fourth projection", Alg. 1: top_k(F_prev @ K_compressed.T, k)
+    unioned with the initial and local blocks.  Reading R8: the tokens of a
+    query block share one selection and its score for block j is the sum of
+    their raw scores F_t . K~_j.  The chunk starts at position q_start (a
+    multiple of block); its query block qi is the global block
+    q_start // block + qi.  f_tok: [B, Hkv, Tq, d]; kc: [B, Hkv, NB, d].
+    Returns idx [B, Hkv, n_qb, U], cnt [B, Hkv, n_qb].
+    """
+    f_tok = _f64(f_tok)
+    kc = _f64(kc)
+    B, H, Tq, d = f_tok.shape
+    if q_start % block:
+        raise ValueError("q_start must be a multiple of block")
+    n_qb = -(-Tq // block)
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, n_qb, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H, n_qb), dtype=np.int64)
+    tops, all_scores = [], []
+    for b in range(B):
+        for g in range(H):
+            for qi in range(n_qb):
+                qb = q_start // block + qi
+                init, local, cand = block_sets(qb, n_init, n_local)
+                rows = f_tok[b, g, qi * block: min(Tq, (qi + 1) * block)]
+                scores = {}
+                for j in cand:
+                    per_token = rows @ kc[b, g, j]          # F_t . K~_j for each token t
+                    scores[j] = float(per_token.sum())
+                top = rank_topk(scores, topk)
+                idx[b, g, qi], cnt[b, g, qi] = _union(init, local, top, cap)
+                tops.append(top)
+                all_scores.append(scores)
+    return Selection(idx, cnt, tops, all_scores)
+
+
+# --------------------------------------------------------------------------
+# a4: attention over the selected blocks only
+# --------------------------------------------------------------------------
+def _softmax_attend(qrow, keys, vals, scale):
+    logits = (keys @ qrow) * scale
+    w = np.exp(logits - logits.max())
+    w /= w.sum()
+    return w @ vals
+
+
+def _block_tokens(blocks, block: int) -> np.ndarray:
+    if len(blocks) == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.arange(block * j, block * (j + 1)) for j in blocks])
+
+
+def attend_decode(q, k, v, idx, cnt, seq_len, scale: float, block: int) -> np.ndarray:
+    """O = softmax(q . K[B]^T * scale) V[B] over the tokens of the block set.
+
+    [EXPL] "The fourth projection", Eq. 5 and Alg. 2: the layer's own query
+    attends to K/V of its selected blocks only.  Tokens at positions
+    >= seq_len (unwritten cache) are excluded.  GQA map and scale by R9.
+    q: [B, Hq, d]; k, v: [B, Hkv, T, d]; idx: [B, Hkv, U]; cnt: [B, Hkv].
+    Returns [B, Hq, d].
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    lens = np.asarray(seq_len, dtype=np.int64)
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            toks = _block_tokens(np.asarray(idx[b, g][: int(cnt[b, g])]), block)
+            toks = toks[toks < lens[b]]
+            out[b, h] = _softmax_attend(q[b, h], k[b, g, toks], v[b, g, toks], scale)
+    return out
+
+
+def attend_prefill(q, k, v, idx, cnt, q_start: int, scale: float, block: int, rows=None) -> np.ndarray:
+    """Block-sparse causal attention for a prefill chunk.
+
+    [EXPL] "The fourth projection", Eq. 5 and Alg. 1; causality per token
+    (R10): the query at position p = q_start + t attends to the tokens of
+    its query block's selected blocks at positions <= p.
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, T, d] holding at least q_start + Tq
+    tokens; idx: [B, Hkv, n_qb, U]; cnt: [B, Hkv, n_qb].
+    rows: optional iterable of (b, h, t) to evaluate; the others stay 0.
+    Returns [B, Hq, Tq, d].
+    """
+    q = _f64(q)
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, Tq, d))
+    todo = rows if rows is not None else [(b, h, t) for b in range(B) for h in range(Hq) for t in range(Tq)]
+    for b, h, t in todo:
+        g = h // G
+        qi = t // block
+        pos = q_start + t
+        toks = _block_tokens(np.asarray(idx[b, g, qi][: int(cnt[b, g, qi])]), block)
+        toks = toks[toks <= pos]
+        kk = _f64(k[b, g, toks])
+        vv = _f64(v[b, g, toks])
+        out[b, h, t] = _softmax_attend(q[b, h, t], kk, vv, scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# a5: lookahead prefetch of the selected blocks
+# --------------------------------------------------------------------------
+def gather_selected_blocks(kv, idx, cnt, block: int) -> np.ndarray:
+    """Copy of the selected blocks of one layer, in index-list order.
+
+    [EXPL] "The fourth projection", Alg. 2 (fetch of the next layer's block
+    set from CPU pinned memory into GPU memory on a prefetch stream) and
+    [OVW] 系统实现 (the blocks a layer needs are in GPU memory when it starts).
+    The prefetch is a pure copy: slot u of (b, g) holds block idx[b, g, u].
+    kv: [B, Hkv, T, d] of any dtype; idx: [B, Hkv, U]; cnt: [B, Hkv].
+    Returns [B, Hkv, U, block, d] of kv's dtype; slots u >= cnt are zero.
+    """
+    kv = np.asarray(kv)
+    B, H, T, d = kv.shape
+    U = idx.shape[-1]
+    ring = np.zeros((B, H, U, block, d), dtype=kv.dtype)
+    for b in range(B):
+        for g in range(H):
+            for u in range(int(cnt[b, g])):
+                j = int(idx[b, g, u])
+                ring[b, g, u] = kv[b, g, block * j: block * (j + 1)]
+    return ring
+
+
+# --------------------------------------------------------------------------
+# The layer-to-layer lookahead of one decode step
+# --------------------------------------------------------------------------
+def decode_step_lookahead(layers, topk: int, n_init: int, n_local: int, block: int, scale: float):
+    """One decode step over L layers with one-layer-ahead selection.
+
+    [EXPL] "The fourth projection", Eq. 4 and Alg. 2; [EXPL] "Training":
+    layer 0 is selected by a separate projection because it has no previous
+    layer.  Each element of ``layers`` is a dict with
+      'x_sel'  [B, hidden]  the hidden state the selecting Forecast reads
+                            (layer l-1's input for l >= 1, layer 0's own input
+                            for the layer-0 projection)
+      'w_sel'  [hidden, Hkv*d] the Forecast weights that select this layer
+      'kc'     [B, Hkv, NB, d] this layer's compressed keys
+      'q'      [B, Hq, d];  'k', 'v' [B, Hkv, T, d];  'seq_len' [B]
+    Returns the list of (Selection, output) per layer.
+    """
+    results = []
+    for lay in layers:
+        Hkv, d = lay["kc"].shape[1], lay["kc"].shape[3]
+        f = forecast_proj(lay["x_sel"], lay["w_sel"], Hkv, d)
+        sel = decode_select(f, lay["kc"], lay["seq_len"], topk, n_init, n_local, block)
+        out = attend_decode(lay["q"], lay["k"], lay["v"], sel.idx, sel.cnt, lay["seq_len"], scale, block)
+        results.append((sel, out))
+    return results
+
+
+def kth_gap(scores: dict, k: int) -> float:
+    """Relative gap between the k-th and (k+1)-th best candidate scores.
+
+    (s_k - s_{k+1}) / max(|s_k|, |s_{k+1}|); +inf when there is no (k+1)-th
+    candidate (the selection is then forced).  Used by the parity checker to
+    decide where selected ids must match exactly.
+    """
+    vals = sorted(scores.values(), reverse=True)
+    if len(vals) <= k or k == 0:
+        return float("inf")
+    a, b = vals[k - 1], vals[k]
+    den = max(abs(a), abs(b))
+    if den == 0.0:
+        return 0.0
+    return (a - b) / den

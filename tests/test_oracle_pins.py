@@ -1,0 +1,418 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Every oracle function is checked here against at least one of: a hand-worked
+fixture (tests/golden/), a closed form, a brute force over all subsets or all
+tokens, or a textbook library routine it reduces to (torch's scaled dot-product
+attention in float64).  The cases are chosen so that a dropped term, a wrong
+sign, an off-by-one block index, a transposed operand or a wrong GQA map in the
+oracle fails at least one test.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from workloads import CONFIGS, decode_inputs, random_decode_case
+
+
+def _np(t):
+    return t.detach().to(torch.float64).cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as fh:
+        return json.load(fh)
+
+
+# --------------------------------------------------------------------------- a1
+def test_forecast_proj_triple_loop():
+    rng = np.random.default_rng(0)
+    B, hidden, H, d = 3, 7, 2, 4
+    x = rng.integers(-5, 6, size=(B, hidden)).astype(np.float64)
+    w = rng.integers(-5, 6, size=(hidden, H * d)).astype(np.float64)
+    f = orc.forecast_proj(x, w, H, d)
+    for b in range(B):
+        for g in range(H):
+            for c in range(d):
+                acc = 0.0
+                for r in range(hidden):
+                    acc += x[b, r] * w[r, g * d + c]
+                assert f[b, g, c] == acc
+
+
+def test_forecast_proj_head_columns():
+    # W = identity: head g must read columns g*d .. g*d+d-1, i.e. x[b, g*d:(g+1)*d].
+    B, H, d = 2, 3, 4
+    x = np.arange(B * H * d, dtype=np.float64).reshape(B, H * d)
+    f = orc.forecast_proj(x, np.eye(H * d), H, d)
+    for b in range(B):
+        for g in range(H):
+            assert np.array_equal(f[b, g], x[b, g * d:(g + 1) * d])
+
+
+# --------------------------------------------------------------------------- a2
+def test_meanpool_closed_form_and_partial_blocks():
+    B, H, T, d, blk = 2, 2, 40, 3, 8
+    t = np.arange(T, dtype=np.float64)
+    k = np.broadcast_to(t[None, None, :, None] * np.array([1.0, -2.0, 0.5]), (B, H, T, d)).copy()
+    k[1, 1] += 3.0
+    kc = orc.kv_block_meanpool(k, blk, seq_len=[40, 29])
+    for j in range(5):
+        mid = blk * j + (blk - 1) / 2.0           # mean of positions 8j .. 8j+7
+        np.testing.assert_allclose(kc[0, 0, j], mid * np.array([1.0, -2.0, 0.5]), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(kc[0, 1, j], mid * np.array([1.0, -2.0, 0.5]), rtol=0, atol=1e-12)
+    for j in range(3):
+        expect = (blk * j + 3.5) * np.array([1.0, -2.0, 0.5]) + 3.0
+        np.testing.assert_allclose(kc[1, 1, j], expect, rtol=0, atol=1e-12)
+    # seq_len 29 -> blocks 0..2 complete (24 tokens), block 3 (24..31) is not: no compressed key
+    assert np.isnan(kc[1, :, 3:]).all()
+    assert not np.isnan(kc[1, :, :3]).any()
+
+
+def test_meanpool_linearity_with_scores():
+    # F . K~_j equals the mean over the block's tokens of F . K_t (the scores of a pooled key)
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((1, 1, 64 * 3, 5))
+    f = rng.standard_normal(5)
+    kc = orc.kv_block_meanpool(k, 64)
+    for j in range(3):
+        per_tok = [sum(f[c] * k[0, 0, 64 * j + r, c] for c in range(5)) for r in range(64)]
+        assert abs(float(f @ kc[0, 0, j]) - sum(per_tok) / 64.0) < 1e-12
+
+
+# --------------------------------------------------------------------------- a3 decode
+def test_golden_decode_select_and_attend(golden_dir):
+    gx = _load(golden_dir, "decode_select_attend_hand.json")
+    blk, d, T = gx["block"], gx["d"], gx["T"]
+    keys = np.array(gx["keys"], dtype=np.float64).reshape(1, 1, T, d)
+    kc = orc.kv_block_meanpool(keys, blk, seq_len=[gx["seq_len"]])
+    np.testing.assert_array_equal(kc[0, 0, :6], np.array(gx["kc_expected"], dtype=np.float64))
+    f = np.array(gx["f"], dtype=np.float64).reshape(1, 1, d)
+    sel = orc.decode_select(f, kc, [gx["seq_len"]], gx["topk"], gx["n_init"], gx["n_local"], blk)
+    assert {str(j): s for j, s in sel.scores[0].items()} == gx["scores_expected"]
+    assert sel.top[0] == gx["top_expected"]
+    assert sel.idx[0, 0].tolist() == gx["idx_expected"]
+    assert int(sel.cnt[0, 0]) == gx["cnt_expected"]
+    v = np.zeros((1, 1, T, d))
+    v[0, 0, :, 0] = np.arange(T)
+    v[0, 0, 26:, 1] = 100.0
+    q = np.array(gx["q"], dtype=np.float64).reshape(1, 1, d)
+    out = orc.attend_decode(q, keys, v, sel.idx, sel.cnt, [gx["seq_len"]], gx["scale"], blk)
+    np.testing.assert_allclose(out[0, 0], gx["out_expected"], rtol=0, atol=1e-12)
+
+
+def test_golden_attention_gqa(golden_dir):
+    gx = _load(golden_dir, "attention_gqa_hand.json")
+    k = np.array(gx["keys"], dtype=np.float64)[None]         # [1, 2, 2, 2]
+    v = np.array(gx["values"], dtype=np.float64)[None]
+    q = np.array(gx["q"], dtype=np.float64)[None]            # [1, 4, 2]
+    idx = np.array([[[0, -1], [0, -1]]])
+    cnt = np.array([[1, 1]])
+    out = orc.attend_decode(q, k, v, idx, cnt, [gx["seq_len"]], gx["scale"], gx["block"])
+    np.testing.assert_allclose(out[0], np.array(gx["out_expected"]), rtol=0, atol=1e-12)
+
+
+def _brute_topk(scores: dict, k: int):
+    """Best k-subset by total score (unique when scores are distinct)."""
+    best, best_sum = None, -math.inf
+    for comb in itertools.combinations(sorted(scores), min(k, len(scores))):
+        s = sum(scores[j] for j in comb)
+        if s > best_sum:
+            best, best_sum = set(comb), s
+    return best or set()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_select_bruteforce_subsets(seed):
+    rng = np.random.default_rng(seed)
+    B, H, d, blk = 2, 2, 3, 4
+    T = 4 * 12
+    lens = [int(rng.integers(1, T + 1)) for _ in range(B)]
+    kc = rng.standard_normal((B, H, T // blk, d))
+    f = rng.standard_normal((B, H, d))
+    topk, n_init, n_local = 3, 1, 2
+    sel = orc.decode_select(f, kc, lens, topk, n_init, n_local, blk)
+    for b in range(B):
+        pos = lens[b] - 1
+        cur = pos // blk
+        for g in range(H):
+            # enumerate candidates from first principles: causal, not initial, not local
+            cands = [j for j in range(T // blk) if j <= cur and j >= n_init and j < cur - n_local + 1]
+            scores = {j: sum(f[b, g, c] * kc[b, g, j, c] for c in range(d)) for j in cands}
+            best = _brute_topk(scores, topk)
+            got = set(sel.top[b * H + g])
+            assert got == best
+            want_union = sorted(set(range(min(n_init, cur + 1))) | set(range(max(0, cur - n_local + 1), cur + 1)) | best)
+            row = sel.idx[b, g]
+            assert row[: sel.cnt[b, g]].tolist() == want_union
+            assert (row[sel.cnt[b, g]:] == -1).all()
+
+
+def test_decode_select_ties_prefer_lower_index():
+    kc = np.zeros((1, 1, 10, 2))
+    kc[0, 0, :, 0] = [0, 5, 3, 5, 3, 5, 0, 0, 0, 0]
+    f = np.array([[[1.0, 0.0]]])
+    sel = orc.decode_select(f, kc, [10 * 4], 4, 1, 2, 4)   # cur=9, cand 1..7
+    assert sel.top[0] == [1, 3, 5, 2]
+    assert sel.idx[0, 0].tolist() == [0, 1, 2, 3, 5, 8, 9]
+
+
+def test_decode_select_sign():
+    # the largest raw dot products win, not the smallest (and no 1/sqrt(d) or softmax changes that)
+    kc = np.zeros((1, 1, 8, 1))
+    kc[0, 0, :, 0] = [0, -4, 1, 9, -2, 7, 0, 0]
+    sel = orc.decode_select(np.ones((1, 1, 1)), kc, [32], 2, 1, 2, 4)   # cur=7, cand 1..5
+    assert sel.top[0] == [3, 5]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_select_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    blk = 8
+    for _ in range(30):
+        B, H, d = 2, 3, 4
+        T = blk * int(rng.integers(1, 20))
+        lens = [int(rng.integers(1, T + 1)) for _ in range(B)]
+        topk, n_init, n_local = int(rng.integers(0, 6)), int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        kc = rng.standard_normal((B, H, T // blk, d))
+        f = rng.standard_normal((B, H, d))
+        sel = orc.decode_select(f, kc, lens, topk, n_init, n_local, blk)
+        U = topk + n_init + n_local
+        assert sel.idx.shape == (B, H, U)
+        for b in range(B):
+            cur = (lens[b] - 1) // blk
+            n_cand = max(0, cur - n_local + 1 - n_init)
+            for g in range(H):
+                c = int(sel.cnt[b, g])
+                row = sel.idx[b, g, :c].tolist()
+                assert row == sorted(set(row)), "sorted and unique"
+                assert max(row) == cur and all(0 <= j <= cur for j in row), "no future block"
+                assert 0 in row, "initial block always present"
+                for j in range(max(0, cur - n_local + 1), cur + 1):
+                    assert j in row, "local blocks always present"
+                assert len(sel.top[b * H + g]) == min(topk, n_cand)
+                assert c <= U and (sel.idx[b, g, c:] == -1).all()
+
+
+def test_planted_config1_is_topk():
+    wl = CONFIGS[1]
+    lay = decode_inputs(wl, "cpu")[0]
+    kc = orc.kv_block_meanpool(_np(lay["k"]), wl.block)
+    sel = orc.decode_select(_np(lay["f"]), kc, _np(lay["seq_len"]).astype(np.int64), wl.topk, wl.n_init,
+                            wl.n_local, wl.block)
+    assert set(sel.top[0]) == set(lay["planted"][0, 0].tolist())
+    assert orc.kth_gap(sel.scores[0], wl.topk) > 0.5
+
+
+def test_planted_config2_is_topk():
+    wl = CONFIGS[2]
+    lay = decode_inputs(wl, "cpu")[0]
+    f = orc.forecast_proj(_np(lay["x_sel"]), _np(lay["w_sel"]), wl.Hkv, wl.d)
+    k = lay["k"]
+    for b in (0, 3):
+        kc = orc.kv_block_meanpool(_np(k[b:b + 1]), wl.block)
+        sel = orc.decode_select(f[b:b + 1], kc, [wl.T], wl.topk, wl.n_init, wl.n_local, wl.block)
+        for g in range(wl.Hkv):
+            assert set(sel.top[g]) == set(lay["planted"][b, g].tolist())
+            assert orc.kth_gap(sel.scores[g], wl.topk) > 0.5
+
+
+# --------------------------------------------------------------------------- a3 prefill
+def test_golden_prefill(golden_dir):
+    gx = _load(golden_dir, "prefill_select_attend_hand.json")
+    blk, d, Tq = gx["block"], gx["d"], gx["Tq"]
+    keys = np.array(gx["keys"], dtype=np.float64).reshape(1, 1, Tq, d)
+    f = np.array(gx["f"], dtype=np.float64).reshape(1, 1, Tq, d)
+    kc = orc.kv_block_meanpool(keys, blk)
+    sel = orc.prefill_select(f, kc, gx["q_start"], gx["topk"], gx["n_init"], gx["n_local"], blk)
+    assert {str(j): s for j, s in sel.scores[3].items()} == gx["scores_qb3_expected"]
+    assert sel.idx[0, 0].tolist() == gx["idx_expected"]
+    assert sel.cnt[0, 0].tolist() == gx["cnt_expected"]
+    v = np.zeros((1, 1, Tq, d))
+    v[0, 0, :, 0] = np.arange(Tq)
+    q = np.zeros((1, 1, Tq, d))
+    out = orc.attend_prefill(q, keys, v, sel.idx, sel.cnt, gx["q_start"], gx["scale"], blk)
+    for t, want in gx["out_first_coord_expected"].items():
+        assert abs(out[0, 0, int(t), 0] - want) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_select_bruteforce(seed):
+    rng = np.random.default_rng(200 + seed)
+    B, H, d, blk = 1, 2, 3, 4
+    T = 4 * 10
+    q_start, Tq = 16, 22                            # chunk covers query blocks 4..9, the last one partial
+    k = rng.standard_normal((B, H, T, d))
+    f = rng.standard_normal((B, H, Tq, d))
+    kc = orc.kv_block_meanpool(k, blk)
+    topk, n_init, n_local = 2, 1, 2
+    sel = orc.prefill_select(f, kc, q_start, topk, n_init, n_local, blk)
+    p = 0
+    for b in range(B):
+        for g in range(H):
+            for qi in range(-(-Tq // blk)):
+                qb = q_start // blk + qi
+                toks = [t for t in range(Tq) if (q_start + t) // blk == qb]
+                cands = [j for j in range(qb + 1) if n_init <= j <= qb - n_local]
+                # score = sum over the block's tokens of per-token scores against the block's mean key
+                scores = {}
+                for j in cands:
+                    mean_key = [sum(k[b, g, blk * j + r, c] for r in range(blk)) / blk for c in range(d)]
+                    scores[j] = sum(sum(f[b, g, t, c] * mean_key[c] for c in range(d)) for t in toks)
+                assert set(sel.top[p]) == _brute_topk(scores, topk)
+                for j, s in scores.items():
+                    assert abs(sel.scores[p][j] - s) < 1e-9
+                p += 1
+
+
+# --------------------------------------------------------------------------- a4
+def _dense_masked_decode(q, k, v, idx, cnt, lens, scale, blk):
+    """Brute force: softmax over ALL T tokens with -inf where a token is not attended."""
+    B, Hq, d = q.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            allowed = set(int(j) for j in idx[b, g, : cnt[b, g]])
+            logits = np.full(T, -np.inf)
+            for t in range(T):
+                if t // blk in allowed and t < lens[b]:
+                    logits[t] = scale * sum(q[b, h, c] * k[b, g, t, c] for c in range(d))
+            m = logits.max()
+            w = np.array([math.exp(x - m) if x > -np.inf else 0.0 for x in logits])
+            w /= w.sum()
+            for c in range(d):
+                out[b, h, c] = sum(w[t] * v[b, g, t, c] for t in range(T))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attend_decode_vs_dense_mask_bruteforce(seed):
+    c = random_decode_case(seed, B=2, Hq=4, Hkv=2, d=4, T=40, block=8, seq_len=[40, 21])
+    q, k, v = _np(c["q"]), _np(c["k"]), _np(c["v"])
+    lens = _np(c["seq_len"]).astype(np.int64)
+    kc = orc.kv_block_meanpool(k, 8, seq_len=lens)
+    sel = orc.decode_select(_np(c["f"]), kc, lens, 1, 1, 1, 8)
+    got = orc.attend_decode(q, k, v, sel.idx, sel.cnt, lens, 0.37, 8)
+    want = _dense_masked_decode(q, k, v, sel.idx, sel.cnt, lens, 0.37, 8)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def _sdpa64(q, k, v, scale, causal):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_decode_full_budget_equals_dense_attention(seed):
+    # with k >= number of candidates every causal block is selected: plain softmax attention
+    c = random_decode_case(seed, B=2, Hq=8, Hkv=2, d=16, T=256, block=16, seq_len=[256, 201])
+    q, k, v = _np(c["q"]), _np(c["k"]), _np(c["v"])
+    lens = _np(c["seq_len"]).astype(np.int64)
+    kc = orc.kv_block_meanpool(k, 16, seq_len=lens)
+    sel = orc.decode_select(_np(c["f"]), kc, lens, 100, 1, 2, 16)
+    scale = 1 / math.sqrt(16)
+    got = orc.attend_decode(q, k, v, sel.idx, sel.cnt, lens, scale, 16)
+    for b in range(2):
+        L = int(lens[b])
+        kk = np.repeat(k[b, :, :L], 4, axis=0)[None]
+        vv = np.repeat(v[b, :, :L], 4, axis=0)[None]
+        want = _sdpa64(q[b][None, :, None, :], kk, vv, scale, False)[0, :, 0]
+        np.testing.assert_allclose(got[b], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_prefill_full_budget_equals_causal_attention(seed):
+    rng = np.random.default_rng(300 + seed)
+    B, Hq, Hkv, d, T, blk = 1, 4, 2, 8, 96, 8
+    q = rng.standard_normal((B, Hq, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    f = rng.standard_normal((B, Hkv, T, d))
+    kc = orc.kv_block_meanpool(k, blk)
+    sel = orc.prefill_select(f, kc, 0, 64, 1, 2, blk)
+    scale = 1 / math.sqrt(d)
+    got = orc.attend_prefill(q, k, v, sel.idx, sel.cnt, 0, scale, blk)
+    want = _sdpa64(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), scale, True)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_chunked_prefill_equals_unchunked():
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, d, T, blk = 1, 2, 1, 4, 64, 4
+    q = rng.standard_normal((B, Hq, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    f = rng.standard_normal((B, Hkv, T, d))
+    kc = orc.kv_block_meanpool(k, blk)
+    whole_sel = orc.prefill_select(f, kc, 0, 3, 1, 2, blk)
+    whole = orc.attend_prefill(q, k, v, whole_sel.idx, whole_sel.cnt, 0, 0.5, blk)
+    for q0 in range(0, T, 16):
+        s = orc.prefill_select(f[:, :, q0:q0 + 16], kc, q0, 3, 1, 2, blk)
+        np.testing.assert_array_equal(s.idx, whole_sel.idx[:, :, q0 // blk:(q0 + 16) // blk])
+        part = orc.attend_prefill(q[:, :, q0:q0 + 16], k, v, s.idx, s.cnt, q0, 0.5, blk)
+        np.testing.assert_allclose(part, whole[:, :, q0:q0 + 16], rtol=0, atol=1e-13)
+
+
+def test_attention_is_convex_combination():
+    c = random_decode_case(5, B=1, Hq=4, Hkv=1, d=8, T=128, block=16)
+    q, k, v = _np(c["q"]) * 4, _np(c["k"]), _np(c["v"])
+    kc = orc.kv_block_meanpool(k, 16)
+    sel = orc.decode_select(_np(c["f"]), kc, [128], 2, 1, 1, 16)
+    out = orc.attend_decode(q, k, v, sel.idx, sel.cnt, [128], 1.0, 16)
+    toks = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in sel.idx[0, 0, : sel.cnt[0, 0]]])
+    sub = v[0, 0, toks]
+    assert (out[0] >= sub.min(axis=0) - 1e-12).all() and (out[0] <= sub.max(axis=0) + 1e-12).all()
+
+
+# --------------------------------------------------------------------------- a5
+def test_gather_selected_blocks_bytes():
+    rng = np.random.default_rng(9)
+    kv = rng.integers(0, 2 ** 16, size=(2, 2, 32, 3), dtype=np.uint16)
+    idx = np.array([[[0, 3, 5, -1], [1, 2, -1, -1]], [[7, -1, -1, -1], [0, 1, 2, 3]]])
+    cnt = np.array([[3, 2], [1, 4]])
+    ring = orc.gather_selected_blocks(kv, idx, cnt, 4)
+    assert ring.dtype == np.uint16
+    for b in range(2):
+        for g in range(2):
+            for u in range(4):
+                if u < cnt[b, g]:
+                    j = idx[b, g, u]
+                    assert ring[b, g, u].tobytes() == kv[b, g, 4 * j:4 * j + 4].tobytes()
+                else:
+                    assert not ring[b, g, u].any()
+
+
+# --------------------------------------------------------------------------- lookahead
+def test_lookahead_uses_each_layers_own_forecast_and_keys():
+    wl = CONFIGS[2]
+    rng = np.random.default_rng(11)
+    L, B, H, d, hidden, T, blk = 3, 1, 2, 4, 6, 64, 8
+    layers = []
+    for _ in range(L):
+        k = rng.standard_normal((B, H, T, d))
+        layers.append({"x_sel": rng.standard_normal((B, hidden)), "w_sel": rng.standard_normal((hidden, H * d)),
+                       "kc": orc.kv_block_meanpool(k, blk), "q": rng.standard_normal((B, 2 * H, d)), "k": k,
+                       "v": rng.standard_normal((B, H, T, d)), "seq_len": [T]})
+    res = orc.decode_step_lookahead(layers, 2, 1, 1, blk, 0.5)
+    for lay, (sel, out) in zip(layers, res):
+        # recompute from scratch with explicit loops: F = x W (GEMV), scores vs that layer's pooled keys
+        f = np.array([[sum(lay["x_sel"][0, r] * lay["w_sel"][r, g * d + c] for r in range(hidden))
+                       for c in range(d)] for g in range(H)])
+        for g in range(H):
+            sc = {j: float(f[g] @ lay["kc"][0, g, j]) for j in range(1, (T - 1) // blk)}
+            assert set(sel.top[g]) == _brute_topk(sc, 2)
+    assert wl.U == 35
+
+
+def test_kth_gap_values():
+    assert orc.kth_gap({1: 4.0, 2: 3.0, 3: 1.0}, 2) == pytest.approx((3.0 - 1.0) / 3.0)
+    assert orc.kth_gap({1: 4.0, 2: 3.0}, 2) == math.inf
+    assert orc.kth_gap({1: 2.0, 2: 2.0, 3: 2.0}, 1) == 0.0
