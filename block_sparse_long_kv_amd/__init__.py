@@ -1,0 +1,22 @@
+"""Python binding of libbskv (Forecast-driven block-sparse attention, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libbskv.so.  torch supplies device memory and the current stream.  The
+functions carry the names of the C ABI in include/bskv.h without the
+``bskv_`` prefix; see that header for layouts and semantics.
+
+Importing this package fails loudly when libbskv.so has not been built
+(``python -m block_sparse_long_kv_amd.build``).
+"""
+from ._lib import (  # noqa: F401
+    BskvError,
+    block_sparse_attn_decode,
+    block_sparse_attn_prefill,
+    forecast_block_score_topk,
+    forecast_proj,
+    host_device_pointer,
+    kv_block_meanpool,
+    lib,
+    prefetch_selected_blocks,
+    workspace_bytes,
+)

@@ -1,0 +1,243 @@
+"""ctypes marshalling for libbskv.so (see include/bskv.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbskv.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m block_sparse_long_kv_amd.build`")
+lib = ctypes.CDLL(_LIB_PATH)
+
+_p, _i, _i64, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_I64x3 = ctypes.c_int64 * 3
+
+
+def _proto(name, res, *args):
+    fn = getattr(lib, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_proto("bskv_version", _i)
+_proto("bskv_strerror", ctypes.c_char_p, _i)
+_proto("bskv_last_error", ctypes.c_char_p)
+_proto("bskv_forecast_proj_workspace", _sz, _i, _i, _i, _i, _i)
+_proto("bskv_forecast_proj", _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, _p)
+_proto("bskv_kv_block_meanpool", _i, _p, _i, ctypes.POINTER(_i64), _i64, _i, _i, _i, _i, _p, _i64, _i64, _i, _p, _i64,
+       _p)
+_proto("bskv_score_topk_workspace", _sz, _i, _i, _i, _i64, _i)
+_proto("bskv_forecast_block_score_topk", _i, _p, _i, _i, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
+       _p, _sz, _p)
+_proto("bskv_attn_decode_workspace", _sz, _i, _i, _i, _i, _i)
+_proto("bskv_block_sparse_attn_decode", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _i, _p, _p, _p, _i, _i, _i,
+       _i, _i, _i, _f, _p, _p, _sz, _p)
+_proto("bskv_block_sparse_attn_prefill", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _i64, _i, _i, _i,
+       _i, _i, _i, _i, _f, _p, _p)
+_proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i,
+       _i, _i, _p)
+_proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
+
+BSKV_F32, BSKV_BF16 = 0, 1
+_DT = {torch.float32: BSKV_F32, torch.bfloat16: BSKV_BF16}
+
+
+class BskvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.bskv_strerror(status).decode()
+        extra = lib.bskv_last_error().decode() if status == -5 else ""
+        super().__init__(f"{where}: status {status} ({msg}){': ' + extra if extra else ''}")
+        self.status = status
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise BskvError(rc, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _stream(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _strides3(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("K/V must be 4-D [B, Hkv, T, d] with a contiguous last dimension")
+    return _I64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+# Workspaces: one zero-filled buffer per (device, stream, call kind, layout):
+# the kernels leave their counters at zero after every call, but a buffer
+# used with another layout would hold stale partials where the new counters
+# live, so layouts never share a buffer.
+_WS: dict = {}
+
+
+def workspace_bytes(kind: str, *args) -> int:
+    fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
+          "attn": lib.bskv_attn_decode_workspace}[kind]
+    return int(fn(*args))
+
+
+def _workspace(device, nbytes: int, stream_handle: int, kind: str, layout: tuple) -> torch.Tensor:
+    key = (device.index, stream_handle, kind, layout)
+    buf = _WS.get(key)
+    if buf is None:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def forecast_proj(x, w, n_kv_heads: int, head_dim: int, out=None, ws=None, stream=None):
+    """F[b, g, :] = x[b] @ w[:, g*d:(g+1)*d] -> fp32 [B, Hkv, d]."""
+    B, hidden = x.shape
+    if w.dtype != x.dtype or not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x, w: same dtype, contiguous")
+    if out is None:
+        out = torch.empty(B, n_kv_heads, head_dim, dtype=torch.float32, device=x.device)
+    sh = _stream(stream, x.device)
+    lay = (B, hidden, n_kv_heads, head_dim, _dt(x))
+    nbytes = workspace_bytes("proj", *lay)
+    ws = ws if ws is not None else _workspace(x.device, nbytes, sh, "proj", lay)
+    _check(lib.bskv_forecast_proj(_ptr(x), _ptr(w), _dt(x), B, hidden, n_kv_heads, head_dim, _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), sh), "forecast_proj")
+    return out
+
+
+def kv_block_meanpool(k, seq_len, kc, blk_begin: int = 0, blk_end: int | None = None, newest_only: bool = False,
+                      stream=None):
+    """Write kc[b, g, j] = mean of block j's keys for complete blocks j in [blk_begin, blk_end)."""
+    B, H, _, d = k.shape
+    nb_cap = kc.shape[2]
+    if blk_end is None:
+        blk_end = nb_cap
+    if kc.dtype != torch.float32 or not kc.is_contiguous() or tuple(kc.shape) != (B, H, nb_cap, d):
+        raise ValueError("kc must be contiguous fp32 [B, Hkv, nb_cap, d]")
+    sh = _stream(stream, k.device)
+    _check(lib.bskv_kv_block_meanpool(_ptr(k), _dt(k), _strides3(k), k.shape[2], B, H, d, 64, _ptr(seq_len),
+                                      blk_begin, blk_end,
+                                      int(bool(newest_only)), _ptr(kc), nb_cap, sh), "kv_block_meanpool")
+    return kc
+
+
+def forecast_block_score_topk(f, kc, topk: int, n_init: int, n_local: int, seq_len=None, q_start: int = 0,
+                              prefill: bool = False, return_scores: bool = False, idx=None, cnt=None, ws=None,
+                              stream=None):
+    """Block selection: (idx int32 [..., U], cnt int32 [...]) [, scores]."""
+    B, H, nb_cap, d = kc.shape
+    U = topk + n_init + n_local
+    if not f.is_contiguous():
+        raise ValueError("f must be contiguous")
+    sh = _stream(stream, f.device)
+    scores = None
+    if prefill:
+        Tq = f.shape[2]
+        n_qb = math.ceil(Tq / 64)
+        idx = idx if idx is not None else torch.empty(B, H, n_qb, U, dtype=torch.int32, device=f.device)
+        cnt = cnt if cnt is not None else torch.empty(B, H, n_qb, dtype=torch.int32, device=f.device)
+        ws_ptr, ws_n = None, 0
+    else:
+        Tq = 0
+        idx = idx if idx is not None else torch.empty(B, H, U, dtype=torch.int32, device=f.device)
+        cnt = cnt if cnt is not None else torch.empty(B, H, dtype=torch.int32, device=f.device)
+        if return_scores:
+            scores = torch.full((B, H, nb_cap), float("nan"), dtype=torch.float32, device=f.device)
+        lay = (B, H, 0, nb_cap, d)
+        nbytes = workspace_bytes("score", *lay)
+        ws = ws if ws is not None else _workspace(f.device, nbytes, sh, "score", lay)
+        ws_ptr, ws_n = _ptr(ws), ws.numel() * ws.element_size()
+    _check(lib.bskv_forecast_block_score_topk(_ptr(f), _dt(f), Tq, q_start, _ptr(kc), nb_cap, _ptr(seq_len), B, H, d,
+                                              64, topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), ws_ptr,
+                                              ws_n, sh), "forecast_block_score_topk")
+    return (idx, cnt, scores) if return_scores else (idx, cnt)
+
+
+def block_sparse_attn_decode(q, k, v, idx, cnt, seq_len, scale: float | None = None, ring: bool = False, out=None,
+                             ws=None, stream=None):
+    """Decode attention over the listed blocks -> fp32 [B, Hq, d].
+
+    k, v: cache [B, Hkv, T, d] (any strides with a contiguous last dim), or,
+    with ring=True, a ring [B, Hkv, U, 64, d] filled by prefetch_selected_blocks.
+    """
+    if ring and k.dim() == 5:
+        k = k.flatten(2, 3)
+        v = v.flatten(2, 3)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    U = idx.shape[-1]
+    if k.stride() != v.stride() or k.dtype != v.dtype or q.dtype != k.dtype or not q.is_contiguous():
+        raise ValueError("q contiguous; k, v with identical strides; one dtype")
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    lay = (B, Hq, Hkv, d, U)
+    nbytes = workspace_bytes("attn", *lay)
+    ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "attn", lay)
+    _check(lib.bskv_block_sparse_attn_decode(_ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2], int(bool(ring)),
+                                             _ptr(idx), _ptr(cnt), _ptr(seq_len), B, Hq, Hkv, d, 64, U, scale, _ptr(out),
+                                             _ptr(ws), ws.numel() * ws.element_size(), sh), "block_sparse_attn_decode")
+    return out
+
+
+def block_sparse_attn_prefill(q, k, v, idx, cnt, q_start: int, scale: float | None = None, out=None, stream=None):
+    """Causal block-sparse attention for a prefill chunk -> bf16 [B, Hq, Tq, d]."""
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    U = idx.shape[-1]
+    if k.stride() != v.stride() or not q.is_contiguous():
+        raise ValueError("q contiguous; k, v with identical strides")
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty_like(q)
+    sh = _stream(stream, q.device)
+    _check(lib.bskv_block_sparse_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), _strides3(k), k.shape[2], _ptr(idx),
+                                              _ptr(cnt),
+                                              q_start, Tq, B, Hq, Hkv, d, 64, U, scale, _ptr(out), sh),
+           "block_sparse_attn_prefill")
+    return out
+
+
+def host_device_pointer(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor."""
+    dev = _p()
+    _check(lib.bskv_host_device_pointer(_p(t.data_ptr()), ctypes.byref(dev)), "host_device_pointer")
+    return dev.value
+
+
+def prefetch_selected_blocks(src_k, src_v, idx, cnt, ring_k, ring_v, n_workgroups: int | None = None, stream=None,
+                             src_k_dev: int | None = None, src_v_dev: int | None = None):
+    """ring[b, g, u] = src[b, g, block idx[b,g,u]] for u < cnt (K and V).
+
+    src_k/src_v: device tensors, or pinned host tensors (their device address
+    is looked up unless passed in src_k_dev/src_v_dev).
+    """
+    B, H, U = idx.shape
+    d = src_k.shape[-1]
+    if src_k.stride() != src_v.stride() or not ring_k.is_contiguous() or not ring_v.is_contiguous():
+        raise ValueError("src_k/src_v: identical strides; rings contiguous")
+    if src_k.is_cuda:
+        pk, pv = src_k.data_ptr(), src_v.data_ptr()
+    else:
+        if not (src_k.is_pinned() and src_v.is_pinned()):
+            raise ValueError("host sources must be pinned")
+        pk = src_k_dev if src_k_dev is not None else host_device_pointer(src_k)
+        pv = src_v_dev if src_v_dev is not None else host_device_pointer(src_v)
+    nwg = n_workgroups if n_workgroups is not None else max(1, min(B * H * U, 512))
+    sh = _stream(stream, ring_k.device)
+    _check(lib.bskv_prefetch_selected_blocks(pk, pv, _dt(ring_k), _strides3(src_k), src_k.shape[2], _ptr(idx), _ptr(cnt),
+                                             _ptr(ring_k), _ptr(ring_v), B, H, d, 64, U, nwg, sh),
+           "prefetch_selected_blocks")
+    return ring_k, ring_v

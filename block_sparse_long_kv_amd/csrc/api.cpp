@@ -1,0 +1,197 @@
+// C ABI of libbskv: host-side argument checks, workspace sizing and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees or
+// synchronises; every failed check returns before any launch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "bskv_launch.hpp"
+#include "../../include/bskv.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  const char* s = hipGetErrorString(e);
+  strncpy(g_last_error, s ? s : "unknown HIP error", sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = 0;
+  return BSKV_EHIP;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? BSKV_OK : hip_fail(e); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize_of(int dtype) { return dtype == BSKV_F32 ? 4 : (dtype == BSKV_BF16 ? 2 : 0); }
+
+bool dtype_ok(int dtype) { return dtype == BSKV_F32 || dtype == BSKV_BF16; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// K/V strides (elements) must keep every 16-byte row chunk aligned.
+bool strides_ok(const int64_t* s, int dtype) {
+  if (!s) return false;
+  const int64_t m = 16 / esize_of(dtype);
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || s[i] % m) return false;
+  return true;
+}
+
+bool group_ok(int hq, int hkv) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv) return false;
+  const int G = hq / hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bskv_version(void) { return (0 << 16) | 1; }
+
+const char* bskv_strerror(int status) {
+  switch (status) {
+    case BSKV_OK: return "ok";
+    case BSKV_EINVAL: return "invalid argument (null pointer, size, stride or alignment)";
+    case BSKV_EDTYPE: return "dtype not supported by this call";
+    case BSKV_EUNSUPPORTED: return "configuration outside what the kernels handle";
+    case BSKV_ENOSPC: return "workspace too small";
+    case BSKV_EHIP: return "HIP error (see bskv_last_error)";
+    default: return "unknown status";
+  }
+}
+
+const char* bskv_last_error(void) { return g_last_error; }
+
+size_t bskv_forecast_proj_workspace(int B, int hidden, int n_kv_heads, int head_dim, int dtype) {
+  if (B <= 0 || hidden <= 0 || n_kv_heads <= 0 || head_dim <= 0 || !dtype_ok(dtype)) return 0;
+  return bskv::proj_workspace_bytes(B, hidden, n_kv_heads * head_dim, dtype);
+}
+
+int bskv_forecast_proj(const void* x, const void* w, int dtype, int B, int hidden, int n_kv_heads, int head_dim,
+                       float* f_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (B <= 0 || hidden <= 0 || n_kv_heads <= 0 || head_dim <= 0) return BSKV_EINVAL;
+  if (!x || !w || !f_out || !ws) return BSKV_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(ws)) return BSKV_EINVAL;
+  const int N = n_kv_heads * head_dim;
+  const int tile = dtype == BSKV_F32 ? 64 : 128;
+  if (hidden % 128 || N % tile) return BSKV_EUNSUPPORTED;
+  if (ws_bytes < bskv::proj_workspace_bytes(B, hidden, N, dtype)) return BSKV_ENOSPC;
+  bskv::ProjArgs a{x, w, dtype, B, hidden, N, f_out, ws, stream};
+  return finish(bskv::launch_proj(a));
+}
+
+int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, int64_t kv_len, int B, int n_kv_heads,
+                           int head_dim,
+                           int block, const int64_t* seq_len, int64_t blk_begin, int64_t blk_end, int newest_only,
+                           float* kc, int64_t kc_nb_cap, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!k || !kc || !seq_len || !aligned16(k) || !aligned16(kc)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || kc_nb_cap <= 0 || kv_len < 0) return BSKV_EINVAL;
+  if (!strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (blk_begin < 0 || blk_end < blk_begin || blk_end > kc_nb_cap) return BSKV_EINVAL;
+  if (!newest_only && blk_end - blk_begin > 0x7fffffff) return BSKV_EUNSUPPORTED;
+  bskv::MeanpoolArgs a{k, dtype, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, B, n_kv_heads, head_dim, block,
+                       seq_len, blk_begin, blk_end, newest_only ? 1 : 0, kc, kc_nb_cap, stream};
+  return finish(bskv::launch_meanpool(a));
+}
+
+size_t bskv_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kc_nb_cap, int head_dim) {
+  if (B <= 0 || n_kv_heads <= 0 || kc_nb_cap <= 0 || n_q_tokens < 0) return 0;
+  return bskv::score_topk_workspace_bytes(B, n_kv_heads, n_q_tokens, kc_nb_cap, head_dim);
+}
+
+int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start, const float* kc,
+                                   int64_t kc_nb_cap, const int64_t* seq_len, int B, int n_kv_heads, int head_dim,
+                                   int block, int topk, int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out,
+                                   float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(f_dtype)) return BSKV_EDTYPE;
+  if (!f || !kc || !idx_out || !cnt_out || !aligned16(f) || !aligned16(kc)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || kc_nb_cap <= 0 || n_q_tokens < 0) return BSKV_EINVAL;
+  if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (kc_nb_cap > bskv::kMaxCandidates) return BSKV_EUNSUPPORTED;
+  if ((int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  const int U = topk + n_init + n_local;
+  if (n_q_tokens == 0) {
+    if (f_dtype != BSKV_F32) return BSKV_EDTYPE;
+    if (!seq_len || !ws) return BSKV_EINVAL;
+    if (ws_bytes < bskv::score_topk_workspace_bytes(B, n_kv_heads, 0, kc_nb_cap, head_dim)) return BSKV_ENOSPC;
+  } else {
+    if (q_start < 0 || q_start % block) return BSKV_EINVAL;
+    if (scores_out) return BSKV_EINVAL;
+    const int64_t n_qb = (n_q_tokens + block - 1) / block;
+    if (n_qb > 65535 || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  }
+  bskv::ScoreTopkArgs a{f, f_dtype, n_q_tokens, q_start, kc, kc_nb_cap, seq_len, B, n_kv_heads, head_dim, block,
+                        topk, n_init, n_local, U, idx_out, cnt_out, scores_out, ws, stream};
+  return finish(bskv::launch_score_topk(a));
+}
+
+size_t bskv_attn_decode_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int U) {
+  if (B <= 0 || U <= 0 || !group_ok(n_q_heads, n_kv_heads) || head_dim <= 0) return 0;
+  return bskv::attn_decode_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, U);
+}
+
+int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, int dtype, const int64_t* kv_strides,
+                                  int64_t kv_len, int kv_is_ring, const int32_t* idx, const int32_t* cnt, const int64_t* seq_len, int B,
+                                  int n_q_heads, int n_kv_heads, int head_dim, int block, int U, float scale,
+                                  float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!q || !k || !v || !idx || !cnt || !seq_len || !out || !ws) return BSKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return BSKV_EINVAL;
+  if (B <= 0 || U <= 0 || kv_len < 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if ((int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  if (ws_bytes < bskv::attn_decode_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, U)) return BSKV_ENOSPC;
+  bskv::AttnDecodeArgs a{q, k, v, dtype, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, kv_is_ring ? 1 : 0,
+                         idx, cnt, seq_len, B, n_q_heads, n_kv_heads, head_dim, block, U, scale, out, ws, stream};
+  return finish(bskv::launch_attn_decode(a));
+}
+
+int bskv_block_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype, const int64_t* kv_strides,
+                                   int64_t kv_len, const int32_t* idx, const int32_t* cnt, int64_t q_start, int n_q_tokens, int B,
+                                   int n_q_heads, int n_kv_heads, int head_dim, int block, int U, float scale,
+                                   void* out, hipStream_t stream) {
+  if (dtype != BSKV_BF16) return BSKV_EDTYPE;
+  if (!q || !k || !v || !idx || !cnt || !out) return BSKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BSKV_EINVAL;
+  if (B <= 0 || U <= 0 || n_q_tokens <= 0 || kv_len < 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (q_start < 0 || q_start % 64) return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  const int64_t n_tiles = (int64_t)((n_q_tokens + 63) / 64) * B * n_kv_heads;
+  if (n_tiles > 0x7fffffff) return BSKV_EUNSUPPORTED;
+  bskv::AttnPrefillArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, idx, cnt, q_start, n_q_tokens,
+                          B, n_q_heads, n_kv_heads, head_dim, block, U, scale, out, stream};
+  return finish(bskv::launch_attn_prefill(a));
+}
+
+int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtype, const int64_t* src_strides,
+                                  int64_t src_len, const int32_t* idx, const int32_t* cnt, void* ring_k, void* ring_v, int B,
+                                  int n_kv_heads, int head_dim, int block, int U, int n_workgroups,
+                                  hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!src_k || !src_v || !idx || !cnt || !ring_k || !ring_v) return BSKV_EINVAL;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(ring_k) || !aligned16(ring_v)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || U <= 0 || n_workgroups < 1 || src_len < 0 || !strides_ok(src_strides, dtype))
+    return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if ((int64_t)B * n_kv_heads * U > 0x7fffffff || n_workgroups > 65535) return BSKV_EUNSUPPORTED;
+  bskv::GatherArgs a{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype), idx, cnt,
+                     ring_k, ring_v, B, n_kv_heads, head_dim, block, U, n_workgroups, stream};
+  return finish(bskv::launch_gather(a));
+}
+
+int bskv_host_device_pointer(void* host_ptr, void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return BSKV_EINVAL;
+  return finish(hipHostGetDevicePointer(dev_ptr, host_ptr, 0));
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+// Block-sparse causal prefill attention on bf16 MFMA (fp32 accumulate).
+//
+// Source: "SparDA: a fourth projection that lets sparse attention prefetch
+// its own KV cache" -- "The fourth projection", Eq. 5 and Alg. 1 (attention
+// of the chunk's queries over the K/V of each query block's selected blocks).
+//
+// Design (gfx950, v_mfma_f32_16x16x32_bf16):
+//   * One workgroup per (query block of 64 tokens, KV head): 2G wavefronts,
+//     wave w serves query head g*G + w/2, rows (w%2)*32 .. +31, so the G
+//     query heads of a KV head share every K/V block staged in LDS.
+//   * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M side):
+//     the accumulator layout then gives each lane one query column, so the
+//     online-softmax statistics and the probabilities stay in the lane that
+//     owns them, and P^T feeds O^T = V^T P^T as the B operand directly.
+//   * K is staged row-major in LDS (rows padded by 16 bytes: conflict-free
+//     16-byte reads); V is staged transposed (d-major, padded) so the V^T
+//     operand is two 8-byte reads per lane.
+//   * The next block's K/V are loaded into registers while the current one
+//     is computed (one-deep software pipeline).
+//   * Workgroups are ordered so that consecutive query blocks of one KV head
+//     run on the same XCD: neighbouring query blocks share most of their
+//     local-window blocks, which then hit in that XCD's L2.
+#include "bskv_device.hpp"
+#include "bskv_launch.hpp"
+
+namespace bskv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
+
+template <int D, int G>
+__global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
+    const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,
+    int64_t sg, int64_t st, int64_t kv_len, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int64_t q_start,
+    int Tq, int Hkv, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
+  constexpr int BLK = 64;
+  constexpr int NT = G * 128;          // threads
+  constexpr int KSTR = D + 8;          // LDS row of K: D bf16 + 16 bytes
+  constexpr int VSTR = BLK + 4;        // LDS row of V^T: 64 bf16 + 8 bytes
+  constexpr int RCH = D / 8;           // 16-byte chunks per token row
+  constexpr int NCH = BLK * RCH;       // 16-byte chunks per block per tensor
+  constexpr int CPT = (NCH + NT - 1) / NT;  // chunks per thread per tensor
+  constexpr int KS = D / 32;           // k-steps of S^T
+  constexpr int MD = D / 16;           // d tiles of O^T
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[BLK * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_bits Vt[D * VSTR];
+
+  const int n_tiles = gridDim.x;
+  int lin = blockIdx.x;
+  if ((n_tiles & 7) == 0) lin = (lin & 7) * (n_tiles >> 3) + (lin >> 3);
+  const int qi = lin % n_qb, bg = lin / n_qb;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int Hq = Hkv * G;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int h = g * G + (wid >> 1);
+  const int row0 = (wid & 1) * 32;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int qb = (int)(q_start / BLK) + qi;
+  const int tq0 = qi * BLK;
+
+  // Q^T fragments (B operand of S^T): query rows row0 + 16*nq + l16
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int nq = 0; nq < 2; ++nq) {
+    const int t = tq0 + row0 + 16 * nq + l16;
+    const bf16_bits* qp = q + (((int64_t)b * Hq + h) * Tq + t) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (t < Tq) r = ld16(qp + 32 * ks);
+      qf[nq][ks] = as_bf16x8(r);
+    }
+  }
+
+  f32x4_t o[MD][2];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) o[md][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  const int64_t prob = (int64_t)bg * n_qb + qi;
+  const int c = min(cnt[prob], U);
+  const int32_t* list = idx + prob * U;
+  const bf16_bits* kb = k + b * sb + g * sg;
+  const bf16_bits* vb = v + b * sb + g * sg;
+
+  // a listed block is used only if it lies inside the K/V buffers
+  auto valid = [&](int jj) { return jj >= 0 && ((int64_t)jj + 1) * BLK <= kv_len; };
+  uint4 kreg[CPT], vreg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
+  auto gload = [&](int jj) {
+    if (!valid(jj)) return;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
+      if (NCH % NT == 0 || ch < NCH) {
+        const int64_t off = ((int64_t)jj * BLK + r) * st + cc * 8;
+        kreg[i] = ld16(kb + off);
+        vreg[i] = ld16(vb + off);
+      }
+    }
+  };
+  if (c > 0) gload(list[0]);
+
+  for (int u = 0; u < c; ++u) {
+    const int j = list[u];
+    __syncthreads();  // all waves are done reading the previous block
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
+      if (NCH % NT != 0 && ch >= NCH) continue;
+      *reinterpret_cast<uint4*>(&Ks[r * KSTR + cc * 8]) = kreg[i];
+      const uint32_t w4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(cc * 8 + 2 * e) * VSTR + r] = (bf16_bits)(w4[e] & 0xffffu);
+        Vt[(cc * 8 + 2 * e + 1) * VSTR + r] = (bf16_bits)(w4[e] >> 16);
+      }
+    }
+    __syncthreads();
+    if (u + 1 < c) gload(list[u + 1]);
+
+    // S^T tiles: keys 16*mt .. (M), queries row0 + 16*nq .. (N)
+    f32x4_t s[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) s[mt][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) s[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][ks], s[mt][nq], 0, 0, 0);
+      }
+    }
+
+    // online softmax per query column (lane-local, 2 xor-shuffles per reduction)
+    const bool diag = (j == qb);
+    const bool ok = valid(j);
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      const int rq = row0 + 16 * nq + l16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * mt + 4 * lg + i;
+          float x = s[mt][nq][i] * qscale;
+          if ((diag && key > rq) || !ok) x = -INFINITY;
+          s[mt][nq][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m_run[nq], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m_run[nq] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (mn == -INFINITY) ? 0.f : exp2f(s[mt][nq][i] - mn);
+          s[mt][nq][i] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l_run[nq] = l_run[nq] * alpha + sum;
+      m_run[nq] = mn;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md][nq] *= alpha;
+      // P^T operand for key step s2: slots 0..3 <- tile 2*s2, slots 4..7 <- tile 2*s2+1
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8_t p8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p8[e] = (__bf16)s[2 * s2][nq][e];
+          p8[4 + e] = (__bf16)s[2 * s2 + 1][nq][e];
+        }
+        pb[s2][nq] = p8;
+      }
+    }
+
+    // O^T += V^T P^T; V^T rows d = 16*md + l16, keys 32*s2 + 4*lg + {0..3} and 32*s2 + 16 + 4*lg + {0..3}
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const bf16_bits* vrow = &Vt[(16 * md + l16) * VSTR + 32 * s2 + 4 * lg];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) o[md][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[s2][nq], o[md][nq], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: O[query][d] = O^T[d][query] / l
+#pragma unroll
+  for (int nq = 0; nq < 2; ++nq) {
+    const int t = tq0 + row0 + 16 * nq + l16;
+    if (t < Tq) {
+      const float inv = l_run[nq] > 0.f ? 1.f / l_run[nq] : 0.f;
+      bf16_bits* op = out + (((int64_t)b * Hq + h) * Tq + t) * D + 4 * lg;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(o[md][nq][0] * inv) | ((uint32_t)f32_to_bf16(o[md][nq][1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(o[md][nq][2] * inv) | ((uint32_t)f32_to_bf16(o[md][nq][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + 16 * md) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+template <int D, int G>
+static void launch_prefill_t(const AttnPrefillArgs& a) {
+  const int n_qb = (a.Tq + 63) / 64;
+  const int n_tiles = n_qb * a.B * a.Hkv;
+  const float qscale = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((attn_prefill_kernel<D, G>), dim3(n_tiles), dim3(G * 128), 0, a.stream, (const bf16_bits*)a.q,
+                     (const bf16_bits*)a.k, (const bf16_bits*)a.v, a.sb, a.sg, a.st, a.kv_len, a.idx, a.cnt, a.q_start, a.Tq,
+                     a.Hkv, a.U, n_qb, qscale, (bf16_bits*)a.out);
+}
+
+template <int D>
+static void launch_prefill_d(const AttnPrefillArgs& a, int G) {
+  switch (G) {
+    case 1: launch_prefill_t<D, 1>(a); break;
+    case 2: launch_prefill_t<D, 2>(a); break;
+    case 4: launch_prefill_t<D, 4>(a); break;
+    default: launch_prefill_t<D, 8>(a); break;
+  }
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  if (a.D == 64) launch_prefill_d<64>(a, G);
+  else launch_prefill_d<128>(a, G);
+  return hipGetLastError();
+}
+
+}  // namespace bskv

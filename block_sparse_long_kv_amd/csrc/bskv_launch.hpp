@@ -1,0 +1,74 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments here are already validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bskv {
+
+struct MeanpoolArgs {
+  const void* k; int dtype; int64_t sb, sg, st; int64_t kv_len;
+  int B, H, D, block;
+  const int64_t* seq_len; int64_t blk_begin, blk_end; int newest_only;
+  float* kc; int64_t nb_cap;
+  hipStream_t stream;
+};
+hipError_t launch_meanpool(const MeanpoolArgs& a);
+
+struct ProjArgs {
+  const void* x; const void* w; int dtype;
+  int B, hidden, N;
+  float* f; void* ws;
+  hipStream_t stream;
+};
+size_t proj_workspace_bytes(int B, int hidden, int N, int dtype);
+hipError_t launch_proj(const ProjArgs& a);
+
+struct ScoreTopkArgs {
+  const void* f; int f_dtype; int n_q_tokens; int64_t q_start;
+  const float* kc; int64_t nb_cap; const int64_t* seq_len;
+  int B, H, D, block, topk, n_init, n_local, U;
+  int32_t* idx; int32_t* cnt; float* scores;
+  void* ws;
+  hipStream_t stream;
+};
+size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, int D);
+hipError_t launch_score_topk(const ScoreTopkArgs& a);
+constexpr int kMaxCandidates = 12288;  // candidate blocks per problem (48 KB of LDS keys)
+
+struct AttnDecodeArgs {
+  const void* q; const void* k; const void* v; int dtype;
+  int64_t sb, sg, st; int64_t kv_len; int ring;
+  const int32_t* idx; const int32_t* cnt; const int64_t* seq_len;
+  int B, Hq, Hkv, D, block, U; float scale;
+  float* out; void* ws;
+  hipStream_t stream;
+};
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int U);
+hipError_t launch_attn_decode(const AttnDecodeArgs& a);
+
+struct AttnPrefillArgs {
+  const void* q; const void* k; const void* v;
+  int64_t sb, sg, st; int64_t kv_len;
+  const int32_t* idx; const int32_t* cnt;
+  int64_t q_start; int Tq;
+  int B, Hq, Hkv, D, block, U; float scale;
+  void* out;
+  hipStream_t stream;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a);
+
+struct GatherArgs {
+  const void* src_k; const void* src_v; int64_t sb, sg, st;  // element strides
+  int64_t src_len;
+  int esize;
+  const int32_t* idx; const int32_t* cnt;
+  void* ring_k; void* ring_v;
+  int B, H, D, block, U, n_workgroups;
+  hipStream_t stream;
+};
+hipError_t launch_gather(const GatherArgs& a);
+
+}  // namespace bskv

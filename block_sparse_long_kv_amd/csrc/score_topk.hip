@@ -1,0 +1,213 @@
+// Forecast block scoring, causal top-k and union with the initial and local
+// blocks, for decode and for prefill chunks.
+//
+// Sources: "SparDA: a fourth projection that lets sparse attention prefetch
+// its own KV cache" -- "The fourth projection" (Eq. 4; Alg. 1 prefill and
+// Alg. 2 decode selection), "One Forecast head per GQA group" (Sec. 4.1:
+// one raw dot product per block, ranking only), "Training" (Eq. 7 comment:
+// top-k after the causal mask, without the initial and local blocks),
+// "The problem InfLLM-V2 leaves on the table" (block-set formula).
+#include "bskv_device.hpp"
+#include "bskv_launch.hpp"
+
+namespace bskv {
+
+// Scores of rows [lo, hi) of kc against the fp32 vector fv (held as F4
+// float4 per lane, 8 lanes per row).  Each 8-lane group handles one row per
+// pass; 32 rows per pass for 256 threads.  Calls sink(j, score) from the
+// group's lane 0.
+template <int D, typename Sink>
+__device__ __forceinline__ void score_rows(const float* __restrict__ kc_bg, const float4* fv, int lo, int hi,
+                                           Sink sink) {
+  constexpr int LPR = 8;
+  constexpr int F4 = D / 4 / LPR;
+  const int sub = threadIdx.x % LPR, row0 = threadIdx.x / LPR;
+  for (int j = lo + row0; j < hi; j += kThreads / LPR) {
+    const float* row = kc_bg + (int64_t)j * D;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < F4; ++i) {
+      const float4 k4 = *reinterpret_cast<const float4*>(row + (i * LPR + sub) * 4);
+      acc += fv[i].x * k4.x;
+      acc += fv[i].y * k4.y;
+      acc += fv[i].z * k4.z;
+      acc += fv[i].w * k4.w;
+    }
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (sub == 0) sink(j, acc);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_fvec(const float* src, float4* fv) {
+  constexpr int LPR = 8;
+  constexpr int F4 = D / 4 / LPR;
+  const int sub = threadIdx.x % LPR;
+#pragma unroll
+  for (int i = 0; i < F4; ++i) fv[i] = *reinterpret_cast<const float4*>(src + (i * LPR + sub) * 4);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: grid (n_splits, B*H).  Every workgroup scores a slice of the
+// candidate range of its (b, g) into the workspace; the last one to finish
+// (agent-scope counter) loads all candidate scores into LDS and runs the
+// top-k + union.  The counter is reset by that workgroup.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_topk_decode_kernel(
+    const float* __restrict__ f, const float* __restrict__ kc, int64_t nb_cap, const int64_t* __restrict__ seq_len,
+    int H, int block, int topk, int n_init, int n_local, int U, int n_splits, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ cnt_out, float* __restrict__ scores_dbg, float* __restrict__ ws_scores,
+    int* __restrict__ ws_count) {
+  extern __shared__ uint32_t keys[];
+  __shared__ TopkShared sh;
+  __shared__ int is_last;
+
+  const int bg = blockIdx.y, b = bg / H, split = blockIdx.x;
+  int64_t L = seq_len[b];
+  if (L < 1) L = 1;
+  int64_t cur64 = (L - 1) / block;
+  // never read compressed keys beyond the cache (a caller contract violation)
+  if (cur64 > nb_cap - 1 + n_local) cur64 = nb_cap - 1 + n_local;
+  const int cur = (int)cur64;
+  const int c0 = n_init, c1 = min(cur - n_local + 1, (int)nb_cap);
+  const int n = max(0, c1 - c0);
+  const int per = (n + n_splits - 1) / n_splits;
+  const int lo = c0 + split * per, hi = min(c1, lo + per);
+  const float* kc_bg = kc + (int64_t)bg * nb_cap * D;
+  float* sc = ws_scores + (int64_t)bg * nb_cap;
+
+  float4 fv[D / 32];
+  load_fvec<D>(f + (int64_t)bg * D, fv);
+  if (scores_dbg) {
+    float* dbg = scores_dbg + (int64_t)bg * nb_cap;
+    score_rows<D>(kc_bg, fv, lo, hi, [&](int j, float s) { sc[j] = s; dbg[j] = s; });
+    if (split == 0) {
+      for (int j = threadIdx.x; j <= min(cur, (int)nb_cap - 1); j += kThreads)
+        if (j < c0 || j >= c1) dbg[j] = -INFINITY;
+    }
+  } else {
+    score_rows<D>(kc_bg, fv, lo, hi, [&](int j, float s) { sc[j] = s; });
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = (atomicAdd(&ws_count[bg], 1) == n_splits - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < n; i += kThreads) keys[i] = orderable_key(sc[c0 + i]);
+  __syncthreads();
+  topk_union(keys, n, c0, topk, cur, n_init, n_local, U, idx_out + (int64_t)bg * U, cnt_out + bg, sh);
+  if (threadIdx.x == 0) ws_count[bg] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: grid (n_qb, B*H); one workgroup per query block.  It sums the
+// block's Forecast vectors (fp32), scores every candidate compressed key
+// into LDS and runs the top-k + union.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void score_topk_prefill_kernel(
+    const T* __restrict__ f, int Tq, int64_t q_start, const float* __restrict__ kc, int64_t nb_cap, int H, int block,
+    int topk, int n_init, int n_local, int U, int n_qb, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int CPR = D / VEC;
+  constexpr int RPP = kThreads / CPR;
+  extern __shared__ uint32_t keys[];
+  __shared__ TopkShared sh;
+  __shared__ float red[RPP][D + 4];
+  __shared__ float fpool[D];
+
+  const int qi = blockIdx.x, bg = blockIdx.y;
+  const int t0 = qi * block, t1 = min(Tq, t0 + block);
+  // pooled Forecast of the query block: sum of its tokens' vectors
+  {
+    const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    const T* base = f + ((int64_t)bg * Tq) * D + c * VEC;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int t = t0 + r0; t < t1; t += RPP) {
+      float x[VEC];
+      cvt16<T>(ld16(base + (int64_t)t * D), x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red[r0][c * VEC + e] = acc[e];
+    __syncthreads();
+    for (int t = threadIdx.x; t < D; t += kThreads) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) s += red[r][t];
+      fpool[t] = s;
+    }
+    __syncthreads();
+  }
+  const int cur = (int)(q_start / block) + qi;
+  const int c0 = n_init, c1 = min(cur - n_local + 1, (int)nb_cap);
+  const int n = max(0, c1 - c0);
+  float4 fv[D / 32];
+  load_fvec<D>(fpool, fv);
+  const float* kc_bg = kc + (int64_t)bg * nb_cap * D;
+  score_rows<D>(kc_bg, fv, c0, c1, [&](int j, float s) { keys[j - c0] = orderable_key(s); });
+  __syncthreads();
+  topk_union(keys, n, c0, topk, cur, n_init, n_local, U, idx_out + ((int64_t)bg * n_qb + qi) * U,
+             cnt_out + (int64_t)bg * n_qb + qi, sh);
+}
+
+static int decode_splits(int n_bg, int64_t nb_cap) {
+  // about 1024 workgroups in flight, at least 64 candidate rows each
+  int s = (1024 + n_bg - 1) / n_bg;
+  int max_s = (int)((nb_cap + 63) / 64);
+  if (s > max_s) s = max_s;
+  return s < 1 ? 1 : s;
+}
+
+size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, int D) {
+  (void)D;
+  if (n_q_tokens > 0) return 0;
+  const size_t sc = (size_t)B * H * nb_cap * sizeof(float);
+  const size_t ctr = (size_t)B * H * sizeof(int);
+  return ((sc + 255) / 256) * 256 + ((ctr + 255) / 256) * 256;
+}
+
+hipError_t launch_score_topk(const ScoreTopkArgs& a) {
+  const int n_bg = a.B * a.H;
+  const int64_t cand_cap = a.nb_cap < kMaxCandidates ? a.nb_cap : kMaxCandidates;
+  const size_t lds = (size_t)cand_cap * sizeof(uint32_t);
+  if (a.n_q_tokens == 0) {
+    const int ns = decode_splits(n_bg, a.nb_cap);
+    const size_t sc_bytes = (size_t)n_bg * a.nb_cap * sizeof(float);
+    float* sc = (float*)a.ws;
+    int* ctr = (int*)((char*)a.ws + ((sc_bytes + 255) / 256) * 256);
+    dim3 grid(ns, n_bg);
+    if (a.D == 64)
+      hipLaunchKernelGGL(score_topk_decode_kernel<64>, grid, dim3(kThreads), lds, a.stream, (const float*)a.f, a.kc,
+                         a.nb_cap, a.seq_len, a.H, a.block, a.topk, a.n_init, a.n_local, a.U, ns, a.idx, a.cnt,
+                         a.scores, sc, ctr);
+    else
+      hipLaunchKernelGGL(score_topk_decode_kernel<128>, grid, dim3(kThreads), lds, a.stream, (const float*)a.f, a.kc,
+                         a.nb_cap, a.seq_len, a.H, a.block, a.topk, a.n_init, a.n_local, a.U, ns, a.idx, a.cnt,
+                         a.scores, sc, ctr);
+    return hipGetLastError();
+  }
+  const int n_qb = (a.n_q_tokens + a.block - 1) / a.block;
+  dim3 grid(n_qb, n_bg);
+#define BSKV_PREFILL_LAUNCH(T, DD)                                                                           \
+  hipLaunchKernelGGL((score_topk_prefill_kernel<T, DD>), grid, dim3(kThreads), lds, a.stream, (const T*)a.f, \
+                     a.n_q_tokens, a.q_start, a.kc, a.nb_cap, a.H, a.block, a.topk, a.n_init, a.n_local, a.U, n_qb, \
+                     a.idx, a.cnt)
+  if (a.f_dtype == 0) {
+    if (a.D == 64) BSKV_PREFILL_LAUNCH(float, 64); else BSKV_PREFILL_LAUNCH(float, 128);
+  } else {
+    if (a.D == 64) BSKV_PREFILL_LAUNCH(bf16_bits, 64); else BSKV_PREFILL_LAUNCH(bf16_bits, 128);
+  }
+#undef BSKV_PREFILL_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace bskv

@@ -1,0 +1,240 @@
+/*
+ * bskv.h -- C ABI of libbskv.so: Forecast-driven block-sparse attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (SparDA, built on InfLLM-V2-style block selection) is described
+ * on these web pages, cited below by tag:
+ *   [EXPL] "SparDA: a fourth projection that lets sparse attention prefetch
+ *          its own KV cache" (ai.thesatyajit.com/articles/sparda)
+ *   [OVW]  Chinese-language SparDA overview (deepresearch2agi.pages.dev),
+ *          sections 架构细节 (architecture details) and 系统实现 (system
+ *          implementation)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless a parameter says otherwise.  The
+ *   caller allocates and owns every buffer, stream and workspace; the library
+ *   never allocates, frees, synchronises or creates streams inside these
+ *   calls.  Every compute call is asynchronous on `stream`.
+ * - Return value: BSKV_OK (0) or a negative bskv_status.  All arguments are
+ *   checked on the host before anything is launched; on any error nothing is
+ *   launched.  BSKV_EHIP means a HIP launch failed (bskv_last_error() has the
+ *   HIP message).  Faults inside a kernel surface at the caller's next
+ *   synchronisation, as usual in HIP.
+ * - Layouts: K/V caches are addressed as [B, Hkv, T, d] with element strides
+ *   kv_strides = {batch, kv head, token}; head_dim elements are contiguous.
+ *   Base pointers must be 16-byte aligned and strides multiples of
+ *   16 bytes / element size.  A 64-token block j of (b, g) is the contiguous
+ *   run of tokens 64j..64j+63, so the default contiguous layout is also
+ *   [B, Hkv, T/64, 64, d].
+ * - dtype: BSKV_F32 or BSKV_BF16 (raw bfloat16 bits, round-to-nearest-even).
+ *   Accumulation is always fp32.
+ * - head_dim must be 64 or 128; block must be 64 (the pages' block size).
+ * - Workspaces: a call that takes `ws` needs at least the bytes returned by
+ *   its *_workspace() query.  A workspace must be zero-filled before its
+ *   first use with a given configuration (the arguments of its *_workspace()
+ *   query); each call leaves its completion counters at zero again, so later
+ *   calls with the SAME configuration can reuse it without clearing.  Using
+ *   it with another configuration first needs a new zero fill (the counters
+ *   of the new layout may sit on old partial results).  Calls that overlap
+ *   in time must not share a workspace.
+ * - kv_len / src_len: the number of tokens the K/V buffers hold (their
+ *   allocation along the token axis, in whole blocks).  Kernels skip any
+ *   listed block that would reach beyond it, so a bad index list cannot make
+ *   them read outside the buffers.
+ * - Thread safety: the library holds no mutable state apart from the
+ *   thread-local text of the last HIP error.
+ */
+#ifndef BSKV_H
+#define BSKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSKV_OK = 0,
+  BSKV_EINVAL = -1,       /* null pointer, bad size, bad stride or alignment */
+  BSKV_EDTYPE = -2,       /* dtype not supported by this call */
+  BSKV_EUNSUPPORTED = -3, /* valid but outside what the kernels handle */
+  BSKV_ENOSPC = -4,       /* workspace too small */
+  BSKV_EHIP = -5          /* a HIP call failed */
+} bskv_status;
+
+typedef enum { BSKV_F32 = 0, BSKV_BF16 = 1 } bskv_dtype;
+
+/* Library version, (major << 16) | minor. */
+int bskv_version(void);
+
+/* Static description of a status code. */
+const char* bskv_strerror(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char* bskv_last_error(void);
+
+/* ----------------------------------------------------------------------- *
+ * a1  Forecast projection.  [EXPL] "The fourth projection", Eq. 3: the
+ * layer's projection phi_l also emits the Forecast F; [EXPL] "One Forecast
+ * head per GQA group": one Forecast head per KV head.
+ *
+ *   f_out[b, g, c] = sum_r x[b, r] * w[r, g*head_dim + c]
+ *
+ * x      [B, hidden]                 dtype, contiguous
+ * w      [hidden, n_kv_heads*head_dim] dtype, contiguous (row-major)
+ * f_out  [B, n_kv_heads, head_dim]   fp32, contiguous
+ * hidden must be a multiple of 128.  ws: bskv_forecast_proj_workspace().
+ * The same call serves the separate layer-0 projection ([EXPL] "Training"):
+ * pass that projection's weights.  Deterministic: fixed summation order.
+ * ----------------------------------------------------------------------- */
+size_t bskv_forecast_proj_workspace(int B, int hidden, int n_kv_heads, int head_dim, int dtype);
+int bskv_forecast_proj(const void* x, const void* w, int dtype, int B, int hidden, int n_kv_heads,
+                       int head_dim, float* f_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * a2  Block mean-pooling into compressed keys.  [EXPL] "The problem
+ * InfLLM-V2 leaves on the table" (keys are mean-pooled into compressed
+ * representations); [EXPL] "The fourth projection", Alg. 2 (a per-layer
+ * compressed-key cache updated incrementally during decode).
+ *
+ *   kc[b, g, j, :] = (1/block) * sum_{r<block} k[b, g, block*j + r, :]
+ *
+ * written for every j in [blk_begin, blk_end) whose block is complete for
+ * batch b (block*(j+1) <= min(seq_len[b], kv_len)); other rows are left
+ * untouched.
+ * newest_only != 0 selects the incremental decode update: for each b only
+ * the block completed by the last token (j = seq_len[b]/block - 1, when
+ * seq_len[b] is a multiple of block and j lies in the range) is written, so
+ * the same launch can be replayed every step.
+ *
+ * k        cache, dtype, strides kv_strides (host array of 3 int64)
+ * seq_len  [B] int64 (device): tokens held per batch element
+ * kc       [B, n_kv_heads, kc_nb_cap, head_dim] fp32, contiguous
+ * Requires 0 <= blk_begin <= blk_end <= kc_nb_cap.
+ * ----------------------------------------------------------------------- */
+int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, int64_t kv_len, int B, int n_kv_heads,
+                           int head_dim, int block, const int64_t* seq_len, int64_t blk_begin,
+                           int64_t blk_end, int newest_only, float* kc, int64_t kc_nb_cap,
+                           hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * a3  Forecast block scoring, causal top-k and union.  [EXPL] "The fourth
+ * projection", Eq. 4 and Algs. 1-2: B = B_init | B_local | f_top(F K~^T, k);
+ * [EXPL] "One Forecast head per GQA group", Sec. 4.1 selector: one raw dot
+ * product per block, ranking only (no 1/sqrt(d), no softmax); [EXPL]
+ * "Training", Eq. 7 comment: the top-k is taken after the causal mask and
+ * without the initial and local blocks.
+ *
+ * For a query in block cur:
+ *   B_init  = {0 .. n_init-1}             (those <= cur)
+ *   B_local = {max(0, cur-n_local+1) .. cur}
+ *   cand    = {n_init .. cur-n_local}     (complete, causal, not init/local)
+ *   s_j     = F . kc[j]   (fp32)
+ *   B_topk  = the min(topk, |cand|) best j by (s_j descending, j ascending)
+ * idx_out lists B_init | B_local | B_topk in ascending order, padded with -1
+ * up to U = topk + n_init + n_local; cnt_out holds the list length.
+ *
+ * Decode (n_q_tokens == 0): f is the fp32 Forecast [B, n_kv_heads, head_dim]
+ *   (f_dtype must be BSKV_F32); the query is the last cached token, so
+ *   cur = (seq_len[b]-1)/block.  idx_out [B, Hkv, U], cnt_out [B, Hkv].
+ *   scores_out (nullable) [B, Hkv, kc_nb_cap]: s_j for candidates, -inf
+ *   elsewhere up to cur; rows beyond cur untouched.
+ * Prefill (n_q_tokens > 0): f holds one Forecast per token
+ *   [B, Hkv, n_q_tokens, head_dim] (f_dtype F32 or BF16) for the chunk
+ *   starting at position q_start (a multiple of block).  Each query block
+ *   qi (tokens qi*block ..) is one selection problem with cur = q_start/block
+ *   + qi and s_j = sum over its tokens t of F_t . kc[j] (computed as
+ *   (sum_t F_t) . kc[j]).  seq_len is ignored.  idx_out [B, Hkv, n_qb, U],
+ *   cnt_out [B, Hkv, n_qb], n_qb = ceil(n_q_tokens/block); scores_out must
+ *   be NULL.
+ * kc must hold compressed keys for every candidate block.  The candidate
+ * count per problem is limited to 16384 (a 1M-token context).
+ * ws: bskv_score_topk_workspace() bytes (may be 0 bytes for prefill).
+ * ----------------------------------------------------------------------- */
+size_t bskv_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kc_nb_cap, int head_dim);
+int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start,
+                                   const float* kc, int64_t kc_nb_cap, const int64_t* seq_len, int B,
+                                   int n_kv_heads, int head_dim, int block, int topk, int n_init,
+                                   int n_local, int32_t* idx_out, int32_t* cnt_out, float* scores_out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * a4  Block-sparse decode attention.  [EXPL] "The fourth projection", Eq. 5
+ * and Alg. 2: the layer's own query attends to the K/V of its selected
+ * blocks only.  For query head h (KV head g = h / (n_q_heads/n_kv_heads)):
+ *
+ *   out[b, h] = softmax_t(scale * q[b,h] . k_t) v_t
+ *
+ * over the tokens t of the listed blocks idx[b, g, 0..cnt-1] with position
+ * < seq_len[b].  Split over blocks, fp32 online softmax, combined in a
+ * fixed order (deterministic).
+ * q      [B, n_q_heads, head_dim] dtype, contiguous
+ * k, v   cache (kv_is_ring == 0): block idx[u] is read at token idx[u]*block;
+ *        ring  (kv_is_ring != 0): the u-th listed block is read at token
+ *        u*block (a buffer filled by bskv_prefetch_selected_blocks).
+ * idx    [B, Hkv, U] int32, cnt [B, Hkv] int32 (as written by a3)
+ * out    [B, n_q_heads, head_dim] fp32
+ * n_q_heads/n_kv_heads must be 1, 2, 4 or 8.  ws: bskv_attn_decode_workspace().
+ * ----------------------------------------------------------------------- */
+size_t bskv_attn_decode_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int U);
+int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, int dtype,
+                                  const int64_t* kv_strides, int64_t kv_len, int kv_is_ring, const int32_t* idx,
+                                  const int32_t* cnt, const int64_t* seq_len, int B, int n_q_heads,
+                                  int n_kv_heads, int head_dim, int block, int U, float scale,
+                                  float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * a4p Block-sparse causal prefill attention (bf16 MFMA, fp32 accumulate).
+ * [EXPL] "The fourth projection", Eq. 5 and Alg. 1.  The query token at
+ * position p = q_start + t (chunk-relative t) attends to the tokens of its
+ * query block's list idx[b, g, t/block, 0..cnt-1] at positions <= p.
+ * q      [B, n_q_heads, n_q_tokens, head_dim] bf16, contiguous
+ * k, v   cache holding at least q_start + n_q_tokens tokens (bf16)
+ * idx    [B, Hkv, n_qb, U] int32, cnt [B, Hkv, n_qb] int32
+ * out    [B, n_q_heads, n_q_tokens, head_dim] bf16
+ * dtype must be BSKV_BF16; head_dim 128 or 64; q_start multiple of block.
+ * ----------------------------------------------------------------------- */
+int bskv_block_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
+                                   const int64_t* kv_strides, int64_t kv_len, const int32_t* idx, const int32_t* cnt,
+                                   int64_t q_start, int n_q_tokens, int B, int n_q_heads, int n_kv_heads,
+                                   int head_dim, int block, int U, float scale, void* out,
+                                   hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * a5  Lookahead prefetch of the selected blocks.  [EXPL] "The fourth
+ * projection", Alg. 2: the next layer's block set is fetched from CPU pinned
+ * memory to the GPU on a dedicated prefetch stream while the current layer
+ * computes; [OVW] 系统实现: the GPU reads host memory directly and the
+ * number of thread blocks is tuned to the batch size.
+ *
+ *   ring_k[b, g, u] = src_k[b, g, idx[b,g,u]*block .. +block)   u < cnt[b,g]
+ *   (same for v); slots u >= cnt are not written.
+ *
+ * src_k, src_v  device-accessible addresses of one layer's K and V: either
+ *               device memory or host-pinned memory mapped for the device
+ *               (see bskv_host_device_pointer), strides src_strides
+ * ring_k/v      [B, Hkv, U, block, head_dim] contiguous, dtype
+ * n_workgroups  number of workgroups of the copy kernel (>= 1): the pages'
+ *               batch-dependent thread-block count
+ * Ordering with the consumer is the caller's: record an event on `stream`
+ * after this call and make the attention stream wait on it; make this
+ * stream wait for the last reader of a ring slot before refilling it.
+ * ----------------------------------------------------------------------- */
+int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtype,
+                                  const int64_t* src_strides, int64_t src_len, const int32_t* idx, const int32_t* cnt,
+                                  void* ring_k, void* ring_v, int B, int n_kv_heads, int head_dim,
+                                  int block, int U, int n_workgroups, hipStream_t stream);
+
+/* Device address of host memory allocated pinned (hipHostMalloc, or a torch
+ * tensor created with pin_memory=True).  Returns BSKV_EHIP if the pointer is
+ * not pinned host memory known to HIP. */
+int bskv_host_device_pointer(void* host_ptr, void** dev_ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSKV_H */

@@ -1,0 +1,145 @@
+"""The C ABI loads, exports every symbol declared in include/bskv.h, and
+rejects bad arguments on the host before launching anything.  CPU only: every
+call here fails validation, so no kernel is launched and no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bskv.h")
+
+bskv = pytest.importorskip("block_sparse_long_kv_amd")
+lib = bskv.lib
+
+OK, EINVAL, EDTYPE, EUNSUP, ENOSPC, EHIP = 0, -1, -2, -3, -4, -5
+P = 0x10000          # a 16-byte aligned fake address: never dereferenced (validation fails first)
+MIS = 0x10008        # misaligned fake address
+S3 = (ctypes.c_int64 * 3)(8 * 131072 * 128, 131072 * 128, 128)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bskv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_hot_path_calls():
+    names = declared_functions()
+    for n in ("bskv_forecast_proj", "bskv_kv_block_meanpool", "bskv_forecast_block_score_topk",
+              "bskv_block_sparse_attn_decode", "bskv_block_sparse_attn_prefill", "bskv_prefetch_selected_blocks"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_strerror_and_version():
+    assert lib.bskv_version() >= 1
+    for code in (OK, EINVAL, EDTYPE, EUNSUP, ENOSPC, EHIP):
+        assert lib.bskv_strerror(code)
+    assert lib.bskv_strerror(-99) == b"unknown status"
+
+
+def test_workspace_queries_are_pure_host_arithmetic():
+    assert lib.bskv_forecast_proj_workspace(8, 4096, 8, 128, 1) >= 32 * 8 * 1024 * 4
+    assert lib.bskv_score_topk_workspace(8, 8, 0, 2048, 128) >= 64 * 2048 * 4
+    assert lib.bskv_score_topk_workspace(4, 8, 2048, 2048, 128) == 0
+    assert lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69) > 0
+    assert lib.bskv_attn_decode_workspace(8, 24, 8, 128, 69) == 0     # group size 3 unsupported
+    assert lib.bskv_forecast_proj_workspace(0, 4096, 8, 128, 1) == 0
+
+
+def test_forecast_proj_validation():
+    f = lib.bskv_forecast_proj
+    ws = lib.bskv_forecast_proj_workspace(4, 4096, 8, 128, 1)
+    assert f(P, P, 7, 4, 4096, 8, 128, P, P, ws, None) == EDTYPE
+    assert f(P, P, 1, 0, 4096, 8, 128, P, P, ws, None) == EINVAL
+    assert f(None, P, 1, 4, 4096, 8, 128, P, P, ws, None) == EINVAL
+    assert f(MIS, P, 1, 4, 4096, 8, 128, P, P, ws, None) == EINVAL
+    assert f(P, P, 1, 4, 4000, 8, 128, P, P, ws, None) == EUNSUP
+    assert f(P, P, 1, 4, 4096, 8, 128, P, P, ws - 1, None) == ENOSPC
+
+
+def test_meanpool_validation():
+    f = lib.bskv_kv_block_meanpool
+    T = 131072
+    assert f(P, 3, S3, T, 8, 8, 128, 64, P, 0, 10, 0, P, 2048, None) == EDTYPE
+    assert f(P, 1, S3, T, 8, 8, 96, 64, P, 0, 10, 0, P, 2048, None) == EUNSUP
+    assert f(P, 1, S3, T, 8, 8, 128, 32, P, 0, 10, 0, P, 2048, None) == EUNSUP
+    assert f(P, 1, S3, T, 8, 8, 128, 64, None, 0, 10, 0, P, 2048, None) == EINVAL
+    assert f(P, 1, S3, T, 8, 8, 128, 64, P, 5, 2049, 0, P, 2048, None) == EINVAL
+    assert f(P, 1, S3, -1, 8, 8, 128, 64, P, 0, 10, 0, P, 2048, None) == EINVAL
+    bad = (ctypes.c_int64 * 3)(8 * 131072 * 128, 131072 * 128, 100)   # token stride not 16-byte aligned
+    assert f(P, 1, bad, T, 8, 8, 128, 64, P, 0, 10, 0, P, 2048, None) == EINVAL
+
+
+def test_score_topk_validation():
+    f = lib.bskv_forecast_block_score_topk
+    ws = lib.bskv_score_topk_workspace(8, 8, 0, 2048, 128)
+    args = dict(f=P, dt=0, nq=0, q0=0, kc=P, cap=2048, sl=P, B=8, H=8, d=128, blk=64, k=64, ni=1, nl=4,
+                idx=P, cnt=P, sc=None, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["f"], a["dt"], a["nq"], a["q0"], a["kc"], a["cap"], a["sl"], a["B"], a["H"], a["d"], a["blk"],
+                 a["k"], a["ni"], a["nl"], a["idx"], a["cnt"], a["sc"], a["ws"], a["wsb"], None)
+    assert call(nl=0) == EINVAL                 # the current block must stay reachable
+    assert call(ni=0) == EINVAL
+    assert call(k=-1) == EINVAL
+    assert call(dt=1) == EDTYPE                 # decode Forecast must be fp32
+    assert call(cap=20000) == EUNSUP
+    assert call(d=96) == EUNSUP
+    assert call(wsb=ws - 4) == ENOSPC
+    assert call(sl=None) == EINVAL
+    assert call(nq=2048, q0=100) == EINVAL      # prefill chunk must start on a block boundary
+    assert call(nq=2048, sc=P) == EINVAL        # no debug scores in prefill
+
+
+def test_attn_decode_validation():
+    f = lib.bskv_block_sparse_attn_decode
+    ws = lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69)
+
+    def call(q=P, dt=1, hq=32, hkv=8, d=128, blk=64, U=69, scale=0.088, wsb=ws, strides=S3, kv_len=131072):
+        return f(q, P, P, dt, strides, kv_len, 0, P, P, P, 8, hq, hkv, d, blk, U, scale, P, P, wsb, None)
+    assert call(dt=5) == EDTYPE
+    assert call(hq=30) == EUNSUP
+    assert call(hq=24) == EUNSUP
+    assert call(d=256) == EUNSUP
+    assert call(blk=128) == EUNSUP
+    assert call(q=MIS) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(scale=0.0) == EINVAL
+    assert call(scale=float("nan")) == EINVAL
+    assert call(wsb=ws - 1) == ENOSPC
+    assert call(kv_len=-64) == EINVAL
+
+
+def test_attn_prefill_validation():
+    f = lib.bskv_block_sparse_attn_prefill
+
+    def call(dt=1, q0=0, tq=2048, hq=32, hkv=8, d=128):
+        return f(P, P, P, dt, S3, 131072, P, P, q0, tq, 4, hq, hkv, d, 64, 97, 0.088, P, None)
+    assert call(dt=0) == EDTYPE
+    assert call(q0=32) == EINVAL
+    assert call(tq=0) == EINVAL
+    assert call(hq=12) == EUNSUP
+    assert call(d=80) == EUNSUP
+
+
+def test_prefetch_validation():
+    f = lib.bskv_prefetch_selected_blocks
+    T = 131072
+    assert f(P, P, 1, S3, T, P, P, P, P, 16, 8, 128, 64, 69, 0, None) == EINVAL
+    assert f(P, P, 4, S3, T, P, P, P, P, 16, 8, 128, 64, 69, 64, None) == EDTYPE
+    assert f(P, None, 1, S3, T, P, P, P, P, 16, 8, 128, 64, 69, 64, None) == EINVAL
+    assert f(P, P, 1, S3, T, P, P, P, P, 16, 8, 128, 32, 69, 64, None) == EUNSUP
+    assert f(P, P, 1, S3, -1, P, P, P, P, 16, 8, 128, 64, 69, 64, None) == EINVAL
+
+
+def test_host_device_pointer_rejects_null():
+    out = ctypes.c_void_p()
+    assert lib.bskv_host_device_pointer(None, ctypes.byref(out)) == EINVAL

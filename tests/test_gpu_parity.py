@@ -1,0 +1,341 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on seeded inputs.
+
+Tolerances: selection ids bit-exact outside a 1e-3 relative k-th score gap
+(near-ties: rescored in fp64, see parity.check_selection); attention 1e-4
+absolute for fp32 inputs, 2e-2 absolute for bf16 inputs; compressed keys and
+Forecast vectors (fp32 sums of 64 / `hidden` terms) 1e-4 absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_kv_amd as bskv
+import oracle as orc
+from parity import check_selection, max_abs, np64
+from workloads import CONFIGS, decode_inputs, random_decode_case, random_prefill_case
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _gpu(case):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in case.items()}
+
+
+def _kc_gpu(k, seq_len, nb_cap=None):
+    B, H, T, d = k.shape
+    nb_cap = nb_cap or T // 64
+    kc = torch.full((B, H, nb_cap, d), float("nan"), dtype=torch.float32, device=DEV)
+    bskv.kv_block_meanpool(k, seq_len, kc)
+    return kc
+
+
+# ----------------------------------------------------------------------------- a2
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_meanpool_range_ragged(dtype, d):
+    lens = [64 * 20, 64 * 20 - 1, 64 * 5 + 3, 1]
+    c = _gpu(random_decode_case(1, B=4, Hq=2, Hkv=2, d=d, T=64 * 20, dtype=dtype, seq_len=lens))
+    kc = _kc_gpu(c["k"], c["seq_len"])
+    torch.cuda.synchronize()
+    want = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens)
+    got = np64(kc)
+    done = ~np.isnan(want)
+    assert np.array_equal(done, ~np.isnan(got)), "exactly the complete blocks are written"
+    assert max_abs(got[done], want[done]) < 1e-4
+
+
+def test_meanpool_newest_only_and_subrange():
+    lens = [64 * 9, 64 * 9 + 5, 64 * 3, 64 * 12]
+    c = _gpu(random_decode_case(2, B=4, Hq=4, Hkv=1, d=128, T=64 * 12, dtype="bf16", seq_len=lens))
+    kc = torch.full((4, 1, 12, 128), 7.0, dtype=torch.float32, device=DEV)
+    bskv.kv_block_meanpool(c["k"], c["seq_len"], kc, 0, 12, newest_only=True)
+    torch.cuda.synchronize()
+    want = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens)
+    got = np64(kc)
+    for b, L in enumerate(lens):
+        for j in range(12):
+            if L % 64 == 0 and j == L // 64 - 1:
+                assert max_abs(got[b, 0, j], want[b, 0, j]) < 1e-4
+            else:
+                assert (got[b, 0, j] == 7.0).all(), (b, j)
+    kc.fill_(7.0)
+    bskv.kv_block_meanpool(c["k"], c["seq_len"], kc, 2, 5)
+    torch.cuda.synchronize()
+    got = np64(kc)
+    for b, L in enumerate(lens):
+        for j in range(12):
+            if 2 <= j < 5 and 64 * (j + 1) <= L:
+                assert max_abs(got[b, 0, j], want[b, 0, j]) < 1e-4
+            else:
+                assert (got[b, 0, j] == 7.0).all(), (b, j)
+
+
+# ----------------------------------------------------------------------------- a1
+@pytest.mark.parametrize("B", [1, 3, 4, 8, 16, 20])
+def test_forecast_proj_bf16(B):
+    g = torch.Generator().manual_seed(10 + B)
+    x = torch.randn(B, 4096, generator=g).to(torch.bfloat16)
+    w = (torch.randn(4096, 1024, generator=g) * 0.02).to(torch.bfloat16)
+    f = bskv.forecast_proj(x.to(DEV), w.to(DEV), 8, 128)
+    torch.cuda.synchronize()
+    want = orc.forecast_proj(np64(x), np64(w), 8, 128)
+    assert max_abs(np64(f), want) < 1e-4
+
+
+def test_forecast_proj_f32_and_repeat():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(5, 256, generator=g)
+    w = torch.randn(256, 128, generator=g)
+    xd, wd = x.to(DEV), w.to(DEV)
+    f1 = bskv.forecast_proj(xd, wd, 2, 64).clone()
+    f2 = bskv.forecast_proj(xd, wd, 2, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2), "deterministic and the split counters are reset"
+    assert max_abs(np64(f1), orc.forecast_proj(np64(x), np64(w), 2, 64)) < 1e-3
+
+
+# ----------------------------------------------------------------------------- a3 decode
+def _decode_select_both(c, topk, n_init, n_local, hidden=None):
+    B, H, T, d = c["k"].shape
+    if "f" in c:
+        f = c["f"]
+        f_or = np64(c["f"])
+    else:
+        f = bskv.forecast_proj(c["x_sel"], c["w_sel"], H, d)
+        f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), H, d)
+    kc = _kc_gpu(c["k"], c["seq_len"])
+    idx, cnt, sc = bskv.forecast_block_score_topk(f, kc, topk, n_init, n_local, seq_len=c["seq_len"],
+                                                  return_scores=True)
+    torch.cuda.synchronize()
+    lens = c["seq_len"].cpu().numpy()
+    kc_or = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens)
+    sel = orc.decode_select(f_or, kc_or, lens, topk, n_init, n_local, 64)
+    return idx, cnt, sc, sel
+
+
+def test_decode_selection_config1():
+    wl = CONFIGS[1]
+    lay = _gpu(decode_inputs(wl, "cpu")[0])
+    idx, cnt, sc, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
+    assert check_selection(idx, cnt, sel, wl.topk) == 0
+    assert set(sel.top[0]) == set(lay["planted"][0, 0].tolist())
+    got = np64(sc)[0, 0]
+    for j, s in sel.scores[0].items():
+        assert abs(got[j] - s) <= 1e-5 * max(1.0, abs(s))
+    cur = (wl.T - 1) // 64
+    for j in list(range(wl.n_init)) + list(range(cur - wl.n_local + 1, cur + 1)):
+        assert got[j] == -math.inf
+
+
+def test_decode_selection_config2():
+    wl = CONFIGS[2]
+    lay = _gpu(decode_inputs(wl, "cpu")[0])
+    idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
+    assert check_selection(idx, cnt, sel, wl.topk) == 0
+    top = [set(t) for t in sel.top]
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            assert top[b * wl.Hkv + g] == set(lay["planted"][b, g].tolist())
+
+
+@pytest.mark.parametrize("seed,d,topk,n_local", [(0, 64, 3, 1), (1, 128, 8, 2), (2, 128, 40, 4), (3, 64, 0, 3),
+                                                 (4, 128, 5, 1)])
+def test_decode_selection_ragged(seed, d, topk, n_local):
+    lens = [64 * 37, 64 * 37 - 13, 65, 64, 1, 64 * 10 + 1]
+    c = _gpu(random_decode_case(seed, B=6, Hq=4, Hkv=2, d=d, T=64 * 37, seq_len=lens, plant=topk // 2,
+                                topk=topk, n_local=n_local))
+    idx, cnt, _, sel = _decode_select_both(c, topk, 1, n_local)
+    check_selection(idx, cnt, sel, topk)
+
+
+def test_decode_selection_exact_ties_take_lower_index():
+    B, H, d, nb = 2, 2, 64, 300
+    kc = torch.zeros(B, H, nb, d)
+    g = torch.Generator().manual_seed(5)
+    kc[..., 0] = torch.randint(-3, 4, (B, H, nb), generator=g).float()   # many exactly equal scores
+    f = torch.zeros(B, H, d)
+    f[..., 0] = 1.0
+    lens = torch.tensor([64 * nb, 64 * 200 + 7], dtype=torch.int64)
+    idx, cnt = bskv.forecast_block_score_topk(f.to(DEV), kc.to(DEV), 17, 1, 3, seq_len=lens.to(DEV))
+    torch.cuda.synchronize()
+    sel = orc.decode_select(f.numpy(), kc.numpy(), lens.numpy(), 17, 1, 3, 64)
+    assert np.array_equal(idx.cpu().numpy(), sel.idx)
+    assert np.array_equal(cnt.cpu().numpy(), sel.cnt)
+
+
+def test_decode_selection_repeatable():
+    wl = CONFIGS[2]
+    lay = _gpu(decode_inputs(wl, "cpu", B=2, T=8192)[0])
+    f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    kc = _kc_gpu(lay["k"], lay["seq_len"])
+    a = bskv.forecast_block_score_topk(f, kc, wl.topk, 1, 2, seq_len=lay["seq_len"])
+    a = [t.clone() for t in a]
+    b = bskv.forecast_block_score_topk(f, kc, wl.topk, 1, 2, seq_len=lay["seq_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- a4 decode
+def _attn_case(seed, B, Hq, Hkv, d, T, dtype, lens, topk, n_local):
+    c = _gpu(random_decode_case(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens, plant=topk,
+                                topk=topk, n_local=n_local))
+    lens_np = c["seq_len"].cpu().numpy()
+    kc_or = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens_np)
+    sel = orc.decode_select(np64(c["f"]), kc_or, lens_np, topk, 1, n_local, 64)
+    return c, sel, lens_np
+
+
+@pytest.mark.parametrize("dtype,d,G,tol", [("f32", 64, 4, 1e-4), ("f32", 128, 1, 1e-4), ("bf16", 128, 4, 2e-2),
+                                           ("bf16", 64, 8, 2e-2), ("bf16", 128, 2, 2e-2), ("f32", 64, 8, 1e-4)])
+def test_attn_decode_on_oracle_lists(dtype, d, G, tol):
+    Hkv = 2
+    lens = [64 * 40, 64 * 33 + 17, 100, 64 * 40 - 1]
+    c, sel, lens_np = _attn_case(7, 4, Hkv * G, Hkv, d, 64 * 40, dtype, lens, topk=9, n_local=2)
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    out = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    torch.cuda.synchronize()
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), sel.idx, sel.cnt, lens_np, scale, 64)
+    assert max_abs(np64(out), want) < tol
+
+
+def test_attn_decode_config1_end_to_end():
+    wl = CONFIGS[1]
+    lay = _gpu(decode_inputs(wl, "cpu")[0])
+    idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
+    assert check_selection(idx, cnt, sel, wl.topk) == 0
+    out = bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"], wl.scale)
+    torch.cuda.synchronize()
+    want = orc.attend_decode(np64(lay["q"]), np64(lay["k"]), np64(lay["v"]), sel.idx, sel.cnt, [wl.T], wl.scale, 64)
+    assert max_abs(np64(out), want) < 1e-4
+
+
+def test_attn_decode_config2_end_to_end():
+    wl = CONFIGS[2]
+    lay = _gpu(decode_inputs(wl, "cpu")[0])
+    idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
+    assert check_selection(idx, cnt, sel, wl.topk) == 0
+    out = bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"], wl.scale)
+    torch.cuda.synchronize()
+    want = orc.attend_decode(np64(lay["q"]), np64(lay["k"]), np64(lay["v"]), sel.idx, sel.cnt, [wl.T] * wl.B,
+                             wl.scale, 64)
+    assert max_abs(np64(out), want) < 2e-2
+
+
+def test_attn_decode_full_budget_is_dense_attention():
+    lens = [64 * 12, 64 * 7 + 9]
+    c, sel, lens_np = _attn_case(11, 2, 8, 2, 128, 64 * 12, "bf16", lens, topk=64, n_local=2)
+    idx, cnt = bskv.forecast_block_score_topk(c["f"], _kc_gpu(c["k"], c["seq_len"]), 64, 1, 2, seq_len=c["seq_len"])
+    out = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"])
+    torch.cuda.synchronize()
+    q, k, v = np64(c["q"]), np64(c["k"]), np64(c["v"])
+    for b, L in enumerate(lens):
+        for h in range(8):
+            g = h // 4
+            lg = k[b, g, :L] @ q[b, h] / math.sqrt(128)
+            w = np.exp(lg - lg.max())
+            w /= w.sum()
+            assert max_abs(np64(out)[b, h], w @ v[b, g, :L]) < 2e-2
+
+
+# ----------------------------------------------------------------------------- a3p / a4p prefill
+def _prefill_case(seed, B, Hq, Hkv, d, T, q_start, Tq, topk, n_local, n_plant=3):
+    c = _gpu(random_prefill_case(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, n_plant=n_plant))
+    lens = torch.full((B,), T, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(c["k"], lens)
+    f_chunk = c["f"][:, :, q_start:q_start + Tq].contiguous()
+    q_chunk = c["q"][:, :, q_start:q_start + Tq].contiguous()
+    idx, cnt = bskv.forecast_block_score_topk(f_chunk, kc, topk, 1, n_local, q_start=q_start, prefill=True)
+    torch.cuda.synchronize()
+    kc_or = orc.kv_block_meanpool(np64(c["k"]), 64)
+    sel = orc.prefill_select(np64(f_chunk), kc_or, q_start, topk, 1, n_local, 64)
+    return c, q_chunk, idx, cnt, sel
+
+
+@pytest.mark.parametrize("q_start,Tq", [(0, 1024), (1024, 1024), (512, 300)])
+def test_prefill_selection(q_start, Tq):
+    c, _, idx, cnt, sel = _prefill_case(21, 2, 8, 2, 128, 2048, q_start, Tq, topk=6, n_local=4)
+    check_selection(idx, cnt, sel, 6)
+
+
+@pytest.mark.parametrize("d,G,q_start,Tq", [(128, 4, 0, 1024), (128, 4, 1024, 1024), (128, 2, 512, 300),
+                                            (64, 8, 256, 448), (128, 1, 0, 200), (64, 4, 1536, 512)])
+def test_prefill_attention_on_oracle_lists(d, G, q_start, Tq):
+    Hkv = 2
+    c, q_chunk, _, _, sel = _prefill_case(31, 2, Hkv * G, Hkv, d, 2048, q_start, Tq, topk=5, n_local=3)
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, q_start)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = [(b, h, t) for b in range(2) for h in range(Hkv * G) for t in rng.choice(Tq, 24, replace=False)]
+    rows += [(0, 0, Tq - 1), (1, Hkv * G - 1, 0)]
+    want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), sel.idx, sel.cnt, q_start,
+                              1.0 / math.sqrt(d), 64, rows=rows)
+    got = np64(out)
+    err = max(max_abs(got[r], want[r]) for r in rows)
+    assert err < 2e-2, err
+
+
+def test_prefill_full_budget_is_causal_attention():
+    B, Hq, Hkv, d, T = 1, 4, 1, 128, 512
+    c, q_chunk, idx, cnt, _ = _prefill_case(41, B, Hq, Hkv, d, T, 0, T, topk=64, n_local=2)
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, 0)
+    torch.cuda.synchronize()
+    want = torch.nn.functional.scaled_dot_product_attention(
+        q_chunk.double().cpu(), c["k"].double().cpu().repeat_interleave(4, 1),
+        c["v"].double().cpu().repeat_interleave(4, 1), is_causal=True).numpy()
+    assert max_abs(np64(out), want) < 2e-2
+
+
+def test_chunked_prefill_matches_single_chunk():
+    c, q_all, idx_all, cnt_all, _ = _prefill_case(51, 1, 4, 1, 128, 1024, 0, 1024, topk=4, n_local=2)
+    whole = bskv.block_sparse_attn_prefill(q_all, c["k"], c["v"], idx_all, cnt_all, 0)
+    lens = torch.full((1,), 1024, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(c["k"], lens)
+    parts = []
+    for q0 in range(0, 1024, 256):
+        f = c["f"][:, :, q0:q0 + 256].contiguous()
+        i, n = bskv.forecast_block_score_topk(f, kc, 4, 1, 2, q_start=q0, prefill=True)
+        assert torch.equal(i, idx_all[:, :, q0 // 64:(q0 + 256) // 64])
+        parts.append(bskv.block_sparse_attn_prefill(q_all[:, :, q0:q0 + 256].contiguous(), c["k"], c["v"], i, n, q0))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts, dim=2), whole)
+
+
+# ----------------------------------------------------------------------------- a5
+def test_prefetch_from_pinned_host_and_ring_attention():
+    wl = CONFIGS[5]
+    B, T = 3, 64 * 50
+    lay = decode_inputs(wl, DEV, layers=1, B=B, T=T)[0]
+    kc = _kc_gpu(lay["k"], lay["seq_len"])
+    f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    idx, cnt = bskv.forecast_block_score_topk(f, kc, wl.topk, wl.n_init, wl.n_local, seq_len=lay["seq_len"])
+    hk = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hk.copy_(lay["k"])
+    hv.copy_(lay["v"])
+    U = wl.U
+    ring_k = torch.full((B, wl.Hkv, U, 64, wl.d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.full_like(ring_k, float("nan"))
+    side = torch.cuda.Stream(DEV)
+    ev = torch.cuda.Event()
+    ev.record()
+    side.wait_event(ev)
+    bskv.prefetch_selected_blocks(hk, hv, idx, cnt, ring_k, ring_v, n_workgroups=64, stream=side)
+    done = torch.cuda.Event()
+    done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    out_ring = bskv.block_sparse_attn_decode(lay["q"], ring_k, ring_v, idx, cnt, lay["seq_len"], ring=True)
+    out_res = bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"])
+    torch.cuda.synchronize()
+    want = orc.gather_selected_blocks(hk.view(torch.int16).numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), 64)
+    got = ring_k.view(torch.int16).cpu().numpy()
+    cn = cnt.cpu().numpy()
+    for b in range(B):
+        for g in range(wl.Hkv):
+            assert np.array_equal(got[b, g, :cn[b, g]], want[b, g, :cn[b, g]])
+    assert torch.equal(out_ring, out_res), "ring read must equal resident read bit for bit"
