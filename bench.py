@@ -1,0 +1,319 @@
+"""Benchmark of the Forecast-driven block-sparse attention hot path on one GPU.
+
+Default workload (one JSON line on stdout): a decode step of batch 8 at a
+131072-token context through 32 layers.  The layer-0 projection selects
+layer 0's blocks; then each layer l runs (bskv_decode_layer_lookahead,
+three kernels)
+  incremental compressed-key update of layer l (newest block)
+  + Forecast projection F_l
+  -> layer l+1's scores (F_l against its compressed keys) + layer l's
+     block-sparse attention
+  -> layer l+1's top-k / union + merge of layer l's attention splits
+with every input resident in HBM.  The step is captured once in a HIP graph
+and replayed.  `value` = batch tokens per second of the whole step.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload decode|decode-b4] [--per-op]
+
+Per-kernel durations come from HIP events around back-to-back launches of
+one kernel over all layers; the roofline object reports the dominant kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# decode workload
+# ---------------------------------------------------------------------------
+class DecodeBench:
+    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None):
+        from workloads import decode_inputs
+        self.torch, self.bskv, self.wl = torch, bskv, wl
+        self.dev = torch.device("cuda:0")
+        self.L = layers or wl.layers
+        self.B = B or wl.B
+        self.T = T or wl.T
+        t0 = time.time()
+        self.layers = decode_inputs(wl, self.dev, layers=self.L, B=self.B, T=self.T)
+        torch.cuda.synchronize()
+        log(f"[bench] generated {self.L} layers in {time.time() - t0:.1f}s")
+        B, H, d, nb = self.B, wl.Hkv, wl.d, self.T // wl.block
+        self.nb = nb
+        self.kc = [torch.empty(B, H, nb, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        for lay, kc in zip(self.layers, self.kc):
+            bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)          # cache built at prefill time
+        self.f = [torch.empty(B, H, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        self.idx = [torch.empty(B, H, wl.U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.cnt = [torch.empty(B, H, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.out = [torch.empty(B, wl.Hq, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=self.dev)  # noqa: E731
+        dt = 1 if wl.dtype == "bf16" else 0
+        self.ws_proj = z(bskv.workspace_bytes("proj", B, wl.hidden, H, d, dt))
+        self.ws_score = z(bskv.workspace_bytes("score", B, H, 0, nb, d))
+        self.ws_attn = z(bskv.workspace_bytes("attn", B, wl.Hq, H, d, wl.U))
+        self.ws_layer = z(bskv.workspace_bytes("layer", B, wl.Hq, H, d, wl.hidden, nb, wl.U, dt))
+        torch.cuda.synchronize()
+
+    # the four per-layer launches
+    def meanpool(self, l):
+        lay = self.layers[l]
+        self.bskv.kv_block_meanpool(lay["k"], lay["seq_len"], self.kc[l], 0, self.nb, newest_only=True)
+
+    def proj(self, l):
+        lay = self.layers[l]
+        self.bskv.forecast_proj(lay["x_sel"], lay["w_sel"], self.wl.Hkv, self.wl.d, out=self.f[l], ws=self.ws_proj)
+
+    def select(self, l):
+        wl = self.wl
+        self.bskv.forecast_block_score_topk(self.f[l], self.kc[l], wl.topk, wl.n_init, wl.n_local,
+                                            seq_len=self.layers[l]["seq_len"], idx=self.idx[l], cnt=self.cnt[l],
+                                            ws=self.ws_score)
+
+    def attend(self, l):
+        lay = self.layers[l]
+        self.bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], self.idx[l], self.cnt[l], lay["seq_len"],
+                                           self.wl.scale, out=self.out[l], ws=self.ws_attn)
+
+    def layer(self, l, stages=7):
+        """Layer l: newest-block update, attention over B_l, and (lookahead)
+        F_l scoring layer l+1's compressed keys -> B_{l+1}; three kernels."""
+        wl, lay = self.wl, self.layers[l]
+        nxt = l + 1 < self.L
+        n = self.layers[l + 1] if nxt else None
+        self.bskv.decode_layer_lookahead(
+            lay["q"], lay["k"], lay["v"], lay["seq_len"], self.kc[l], self.idx[l], self.cnt[l], wl.scale,
+            out=self.out[l], x=n["x_sel"] if nxt else None, w=n["w_sel"] if nxt else None,
+            kc_next=self.kc[l + 1] if nxt else None, idx_next=self.idx[l + 1] if nxt else None,
+            cnt_next=self.cnt[l + 1] if nxt else None, topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local,
+            stages=stages, ws=self.ws_layer)
+
+    def step(self):
+        # layer 0 is selected by the separate layer-0 projection; then every
+        # layer's Forecast selects the next layer while the layer attends
+        self.proj(0)
+        self.select(0)
+        for l in range(self.L):
+            self.layer(l)
+
+    def step_per_op(self):
+        self.proj(0)
+        self.select(0)
+        for l in range(self.L):
+            self.meanpool(l)
+            if l + 1 < self.L:
+                self.proj(l + 1)
+                self.select(l + 1)
+            self.attend(l)
+
+    # algorithmic HBM bytes per launch: what the method must read and write
+    # (weights, pooled keys, selected K/V, queries, block lists, outputs);
+    # partial results kept in the workspace are not counted
+    def bytes_per_launch(self):
+        wl, B = self.wl, self.B
+        H, d, U = wl.Hkv, wl.d, wl.U
+        e = 2 if wl.dtype == "bf16" else 4
+        cur = (self.T - 1) // wl.block
+        n_cand = max(0, cur - wl.n_local + 1 - wl.n_init)
+        proj = wl.hidden * H * d * e + B * wl.hidden * e + B * H * d * 4
+        pool = B * H * (wl.block * d * e + d * 4)
+        score = B * H * (n_cand * d * 4 + d * 4)
+        lists = B * H * (U + 1) * 4
+        attn = B * H * (U * wl.block * d * e * 2) + B * wl.Hq * d * e + lists
+        out = B * wl.Hq * d * 4
+        return {
+            "forecast_proj": proj, "kv_block_meanpool": pool, "score_topk": score + lists,
+            "attn_decode": attn + out,
+            "layer_k1": proj, "layer_k2": score + attn, "layer_k3": lists + out + pool,
+        }
+
+
+def time_graph(torch, fn, steps, warmup, use_graph=True):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = None
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                                   # one more eager pass on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+    run = g.replay if g is not None else fn
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, g
+
+
+def kernel_times(torch, bench, reps=3):
+    """Average duration per launch of each kernel (or per-op call), HIP
+    events around back-to-back launches over all layers on the launching
+    stream.  layer_k1/k2/k3 are the three kernels of one fused layer, each
+    launched on its own (stages 1, 2, 4) after a full pass has filled the
+    workspace it reads."""
+    res = {}
+    for l in range(bench.L):
+        bench.layer(l)
+    for name, fn in (("layer_k1", lambda l: bench.layer(l, 1)), ("layer_k2", lambda l: bench.layer(l, 2)),
+                     ("layer_k3", lambda l: bench.layer(l, 4)),
+                     ("kv_block_meanpool", bench.meanpool), ("forecast_proj", bench.proj),
+                     ("score_topk", bench.select), ("attn_decode", bench.attend)):
+        # the last layer selects nothing, so it has no projection kernel
+        layers = range(bench.L - 1) if name == "layer_k1" else range(bench.L)
+        for l in layers:   # warm
+            fn(l)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for l in layers:
+                fn(l)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e-3 / (reps * len(layers))
+    return res
+
+
+def cpu_baseline_decode(bench, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the same decode step: layer 0,
+    one sequence (batch element 0, all KV heads); repeated until the budget
+    is spent; scaled to the full step (x B sequences x L layers)."""
+    import numpy as np
+    import oracle as orc
+    torch, wl = bench.torch, bench.wl
+    lay = bench.layers[0]
+    n64 = lambda t: t.detach().to(torch.float64).cpu().numpy()  # noqa: E731
+    k = n64(lay["k"][0:1])
+    v = n64(lay["v"][0:1])
+    q = n64(lay["q"][0:1])
+    x = n64(lay["x_sel"][0:1])
+    w = n64(lay["w_sel"])
+    kc = orc.kv_block_meanpool(k, wl.block)                    # the compressed-key cache (not timed)
+    lens = np.array([bench.T], dtype=np.int64)
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max([int(p.get("num_threads", 1)) for p in info] or [1])
+    except Exception:
+        pass
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 2000:
+        t0 = time.perf_counter()
+        newest = orc.kv_block_meanpool(k[:, :, bench.T - wl.block:], wl.block)     # incremental update
+        f = orc.forecast_proj(x, w, wl.Hkv, wl.d)
+        sel = orc.decode_select(f, kc, lens, wl.topk, wl.n_init, wl.n_local, wl.block)
+        orc.attend_decode(q, k, v, sel.idx, sel.cnt, lens, wl.scale, wl.block)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        del newest
+    per_sample = t_total / reps
+    step_s = per_sample * bench.B * bench.L
+    return {"value": bench.B / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0, batch element 0 (all {wl.Hkv} KV heads), {reps} reps in {t_total:.1f}s; "
+                      f"per-step time scaled x{bench.B} sequences x{bench.L} layers",
+            "sample_seconds": round(per_sample, 4)}
+
+
+def run_decode(args, torch, bskv, wl):
+    bench = DecodeBench(wl, torch, bskv)
+    step_fn = bench.step_per_op if args.per_op else bench.step
+    step_s, _ = time_graph(torch, step_fn, args.steps, args.warmup, use_graph=not args.no_graph)
+    log(f"[bench] decode step {step_s * 1e3:.3f} ms ({'graph' if not args.no_graph else 'eager'})")
+    kt = kernel_times(torch, bench)
+    bpl = bench.bytes_per_launch()
+    kernels = {}
+    for name, t in kt.items():
+        gbs = bpl[name] / t / 1e9
+        kernels[name] = {"us": round(t * 1e6, 3), "bytes": bpl[name], "GBps": round(gbs, 1),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    step_bytes = bench.L * (bpl["layer_k1"] + bpl["layer_k2"] + bpl["layer_k3"])   # incl. the layer-0 projection
+    dom = "attn_decode" if args.per_op else "layer_k2"
+    ach = bpl[dom] / kt[dom] / 1e9
+    result = {
+        "metric": METRIC, "value": round(bench.B / step_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": bench.B, "T": bench.T, "layers": bench.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.d, "hidden": wl.hidden, "block": wl.block, "topk": wl.topk, "n_init": wl.n_init,
+                   "n_local": wl.n_local, "hip_graph": not args.no_graph,
+                   "path": "per-op" if args.per_op else "fused-layer"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": bpl[dom], "us_per_launch": round(kt[dom] * 1e6, 3)},
+        "step_hbm_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_bytes": step_bytes,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(bench, args.cpu_budget)
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4"])
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="also run one device copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path has no multi-GPU leg.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_kv_amd as bskv
+    from workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * (1 << 30))
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
+        del a, b
+    wl = CONFIGS[3] if args.workload == "decode" else CONFIGS[2]
+    result = run_decode(args, torch, bskv, wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

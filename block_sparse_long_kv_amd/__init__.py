@@ -6,12 +6,13 @@ functions carry the names of the C ABI in include/bskv.h without the
 ``bskv_`` prefix; see that header for layouts and semantics.
 
 Importing this package fails loudly when libbskv.so has not been built
-(``python -m block_sparse_long_kv_amd.build``).
+(``python block_sparse_long_kv_amd/build.py``).
 """
 from ._lib import (  # noqa: F401
     BskvError,
     block_sparse_attn_decode,
     block_sparse_attn_prefill,
+    decode_layer_lookahead,
     forecast_block_score_topk,
     forecast_proj,
     host_device_pointer,

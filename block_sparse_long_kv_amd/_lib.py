@@ -9,7 +9,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbskv.so")
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m block_sparse_long_kv_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python block_sparse_long_kv_amd/build.py`")
 lib = ctypes.CDLL(_LIB_PATH)
 
 _p, _i, _i64, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -41,6 +41,9 @@ _proto("bskv_block_sparse_attn_prefill", _i, _p, _p, _p, _i, ctypes.POINTER(_i64
 _proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i,
        _i, _i, _p)
 _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
+_proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _i, _i)
+_proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _f, _p, _p, _p,
+       _i, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
 
 BSKV_F32, BSKV_BF16 = 0, 1
 _DT = {torch.float32: BSKV_F32, torch.bfloat16: BSKV_BF16}
@@ -80,16 +83,14 @@ def _strides3(t: torch.Tensor):
     return _I64x3(t.stride(0), t.stride(1), t.stride(2))
 
 
-# Workspaces: one zero-filled buffer per (device, stream, call kind, layout):
-# the kernels leave their counters at zero after every call, but a buffer
-# used with another layout would hold stale partials where the new counters
-# live, so layouts never share a buffer.
+# Workspaces: one buffer per (device, stream, call kind, layout), allocated
+# on first use and reused by later calls of the same kind and layout.
 _WS: dict = {}
 
 
 def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
-          "attn": lib.bskv_attn_decode_workspace}[kind]
+          "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace}[kind]
     return int(fn(*args))
 
 
@@ -97,7 +98,7 @@ def _workspace(device, nbytes: int, stream_handle: int, kind: str, layout: tuple
     key = (device.index, stream_handle, kind, layout)
     buf = _WS.get(key)
     if buf is None:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
 
@@ -241,3 +242,38 @@ def prefetch_selected_blocks(src_k, src_v, idx, cnt, ring_k, ring_v, n_workgroup
                                              _ptr(ring_k), _ptr(ring_v), B, H, d, 64, U, nwg, sh),
            "prefetch_selected_blocks")
     return ring_k, ring_v
+
+
+def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None = None, out=None, x=None, w=None,
+                           kc_next=None, idx_next=None, cnt_next=None, topk: int = 0, n_init: int = 1,
+                           n_local: int = 1, stages: int = 7, ws=None, stream=None):
+    """One decode layer: newest-block update of kc, this layer's attention over
+    (idx, cnt), and (when x is given) the next layer's selection from the
+    Forecast x @ w against kc_next, written to idx_next / cnt_next.
+    stages: bit mask of the three launches (7 = all, in order)."""
+    B, Hq, d = q.shape
+    Hkv, nb_cap = kc.shape[1], kc.shape[2]
+    U = idx.shape[-1]
+    if U != topk + n_init + n_local:
+        raise ValueError("idx capacity must equal topk + n_init + n_local")
+    sel = x is not None
+    if sel:
+        hidden = x.shape[1]
+        idx_next = idx_next if idx_next is not None else torch.empty_like(idx)
+        cnt_next = cnt_next if cnt_next is not None else torch.empty_like(cnt)
+    else:
+        hidden = 0
+    if k.stride() != v.stride() or not q.is_contiguous():
+        raise ValueError("q contiguous; k, v with identical strides")
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    lay = (B, Hq, Hkv, d, hidden, nb_cap, U, _dt(k))
+    nbytes = workspace_bytes("layer", *lay)
+    ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "layer", lay)
+    _check(lib.bskv_decode_layer_lookahead(_ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2],
+                                           _ptr(seq_len), _ptr(kc), _ptr(idx), _ptr(cnt), scale, _ptr(out), _ptr(x),
+                                           _ptr(w), hidden, _ptr(kc_next), _ptr(idx_next), _ptr(cnt_next), B, Hq,
+                                           Hkv, d, 64, nb_cap, topk, n_init, n_local, stages, _ptr(ws),
+                                           ws.numel() * ws.element_size(), sh), "decode_layer_lookahead")
+    return (out, idx_next, cnt_next) if sel else (out, None, None)

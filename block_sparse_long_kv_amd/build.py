@@ -1,6 +1,6 @@
 """Build libbskv.so in-tree for gfx950 with hipcc.
 
-    python -m block_sparse_long_kv_amd.build          # compile + link
+    python block_sparse_long_kv_amd/build.py          # compile + link
 Every call recompiles all sources (objects in _build/, the library next to
 this file).  hipcc cross-compiles for gfx950 without a GPU present.
 """
@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbskv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "meanpool_proj.hip", "score_topk.hip", "attn_decode.hip", "attn_prefill.hip", "prefetch.hip"]
+SOURCES = ["api.cpp", "decode_kernels.hip", "fused_decode.hip", "score_topk.hip", "attn_prefill.hip", "prefetch.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -77,7 +77,7 @@ int bskv_forecast_proj(const void* x, const void* w, int dtype, int B, int hidde
   if (!aligned16(x) || !aligned16(w) || !aligned16(ws)) return BSKV_EINVAL;
   const int N = n_kv_heads * head_dim;
   const int tile = dtype == BSKV_F32 ? 64 : 128;
-  if (hidden % 128 || N % tile) return BSKV_EUNSUPPORTED;
+  if (hidden % 256 || N % tile) return BSKV_EUNSUPPORTED;
   if (ws_bytes < bskv::proj_workspace_bytes(B, hidden, N, dtype)) return BSKV_ENOSPC;
   bskv::ProjArgs a{x, w, dtype, B, hidden, N, f_out, ws, stream};
   return finish(bskv::launch_proj(a));
@@ -187,6 +187,50 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
   bskv::GatherArgs a{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype), idx, cnt,
                      ring_k, ring_v, B, n_kv_heads, head_dim, block, U, n_workgroups, stream};
   return finish(bskv::launch_gather(a));
+}
+
+size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,
+                                             int64_t kc_nb_cap, int U, int dtype) {
+  if (B <= 0 || U <= 0 || kc_nb_cap <= 0 || hidden < 0 || !group_ok(n_q_heads, n_kv_heads) || !dtype_ok(dtype) ||
+      !head_dim_ok(head_dim))
+    return 0;
+  return bskv::layer_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, hidden, kc_nb_cap, U, dtype);
+}
+
+int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int dtype, const int64_t* kv_strides,
+                                int64_t kv_len, const int64_t* seq_len, float* kc, const int32_t* idx,
+                                const int32_t* cnt, float scale, float* out, const void* x, const void* w_forecast,
+                                int hidden, const float* kc_next, int32_t* idx_next, int32_t* cnt_next, int B,
+                                int n_q_heads, int n_kv_heads, int head_dim, int block, int64_t kc_nb_cap, int topk,
+                                int n_init, int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!q || !k || !v || !seq_len || !kc || !idx || !cnt || !out || !ws) return BSKV_EINVAL;
+  if (stages < 1 || stages > 7) return BSKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(ws)) return BSKV_EINVAL;
+  const bool sel = x != nullptr;
+  if (sel != (w_forecast != nullptr) || sel != (kc_next != nullptr) || sel != (idx_next != nullptr) ||
+      sel != (cnt_next != nullptr))
+    return BSKV_EINVAL;   // the lookahead arguments come all together or not at all
+  if (sel && (!aligned16(x) || !aligned16(w_forecast) || !aligned16(kc_next))) return BSKV_EINVAL;
+  if (B <= 0 || kv_len < 0 || kc_nb_cap <= 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads) || !head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (kc_nb_cap > bskv::kMaxCandidates || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  const int tile = dtype == BSKV_F32 ? 64 : 128;
+  if (sel && (hidden <= 0 || hidden % 256 || (n_kv_heads * head_dim) % tile)) return BSKV_EUNSUPPORTED;
+  const int U = topk + n_init + n_local;
+  if (ws_bytes < bskv::layer_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, sel ? hidden : 0, kc_nb_cap, U,
+                                             dtype))
+    return BSKV_ENOSPC;
+  bskv::DecodeLayerArgs a;
+  a.attn = bskv::AttnDecodeArgs{q, k, v, dtype, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, 0, idx, cnt,
+                                seq_len, B, n_q_heads, n_kv_heads, head_dim, block, U, scale, out, ws, stream};
+  a.kc = kc; a.nb_cap = kc_nb_cap;
+  a.x = x; a.w = w_forecast; a.hidden = sel ? hidden : 0;
+  a.kc_next = kc_next; a.idx_next = idx_next; a.cnt_next = cnt_next;
+  a.topk = topk; a.n_init = n_init; a.n_local = n_local; a.stages = stages;
+  return finish(bskv::launch_decode_layer(a));
 }
 
 int bskv_host_device_pointer(void* host_ptr, void** dev_ptr) {

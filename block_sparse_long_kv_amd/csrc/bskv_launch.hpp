@@ -71,4 +71,16 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs& a);
 
+// One decode layer with lookahead selection of the next layer (3 kernels).
+struct DecodeLayerArgs {
+  AttnDecodeArgs attn;               // this layer's attention (ring must be 0); ws = the whole workspace
+  float* kc; int64_t nb_cap;         // this layer's compressed keys (newest block updated)
+  const void* x; const void* w; int hidden;               // Forecast projection (x == nullptr: no next layer)
+  const float* kc_next; int32_t* idx_next; int32_t* cnt_next;
+  int topk, n_init, n_local;
+  int stages;                        // bit mask of the three launches
+};
+size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype);
+hipError_t launch_decode_layer(const DecodeLayerArgs& a);
+
 }  // namespace bskv

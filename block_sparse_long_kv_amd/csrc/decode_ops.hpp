@@ -1,0 +1,576 @@
+// Workgroup-level building blocks of the decode hot path.  Each function is
+// the whole work of one workgroup for one work item, so the same code runs
+// in the per-operation kernels of the C ABI and in the fused per-layer
+// pipeline.  No function communicates with other workgroups: every
+// cross-workgroup combination (projection splits, score slices, attention
+// splits) is done by a workgroup of a LATER kernel, after the kernel
+// boundary has made the partial results visible.  (An agent-scope fence per
+// workgroup costs an L2 writeback on gfx950, which serialises per XCD.)
+//
+// Sources: "SparDA: a fourth projection that lets sparse attention prefetch
+// its own KV cache" -- "The fourth projection" (Eq. 3 projection, Eq. 4
+// selection, Eq. 5 attention, Alg. 2 decode step), "One Forecast head per
+// GQA group" (Sec. 4.1 raw-score selector, one head per KV head), "The
+// problem InfLLM-V2 leaves on the table" (mean-pooled keys, block set),
+// "Training" (Eq. 7 comment: top-k after the causal mask, without the initial
+// and local blocks).
+#pragma once
+
+#include <type_traits>
+
+#include "bskv_device.hpp"
+
+namespace bskv {
+
+constexpr int kBlk = 64;            // tokens per KV block
+constexpr int kMaxSplitsDecode = 64;
+
+// ---------------------------------------------------------------------------
+// Forecast projection, split over the hidden dimension.
+//   part[split][b][n] = sum_{r in split} x[b, r] W[r, n]
+// Workgroup (tile, split): TC = 16*VEC columns, kProjRows rows.  Thread =
+// (row lane 0..15, 16-byte column chunk 0..15) holding its kProjRows/16 rows
+// of W in registers (all loads issued first); the batch is processed in
+// passes of kProjPass rows that reuse those registers; the 16 row lanes are
+// added through LDS, one barrier pair per pass.
+// ---------------------------------------------------------------------------
+constexpr int kProjRows = 128;   // rows of W per split
+constexpr int kProjPass = 4;     // batch rows per pass
+constexpr int kProjMaxB = 16;    // batch rows staged in LDS per round
+
+struct ProjSmem {
+  float xs[kProjMaxB][kProjRows];
+  float red[16][kProjPass][132];
+};
+
+template <typename T>
+__host__ __device__ constexpr int proj_tile_cols_host() { return 16 * VecN<T>::N; }
+
+template <typename T>
+__device__ void proj_partial_wg(const T* __restrict__ x, const T* __restrict__ w, int B, int hidden, int N, int tile,
+                                int split, float* __restrict__ part, ProjSmem& sm) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int TC = 16 * VEC;
+  constexpr int RPT = kProjRows / 16;   // rows of W per thread
+  const int c = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  const int r_begin = split * kProjRows;
+  const int col0 = tile * TC + c * VEC;
+  uint4 raw[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) raw[i] = ld16(w + (int64_t)(r_begin + rl + 16 * i) * N + col0);
+  for (int b0 = 0; b0 < B; b0 += kProjMaxB) {
+    const int nb = min(kProjMaxB, B - b0);
+    // stage x[b0 .. b0+nb)[r_begin .. +kProjRows) as fp32 (16-byte loads)
+    constexpr int XV = kProjRows / VEC;   // 16-byte vectors per batch row
+    for (int i = threadIdx.x; i < nb * XV; i += kThreads) {
+      const int bb = i / XV, cv = i % XV;
+      float xv[VEC];
+      cvt16<T>(ld16(x + (int64_t)(b0 + bb) * hidden + r_begin + cv * VEC), xv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm.xs[bb][cv * VEC + e] = xv[e];
+    }
+    __syncthreads();
+    for (int p0 = 0; p0 < nb; p0 += kProjPass) {
+      float acc[kProjPass][VEC];
+#pragma unroll
+      for (int bb = 0; bb < kProjPass; ++bb)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[bb][e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        float wv[VEC];
+        cvt16<T>(raw[i], wv);
+        const int r = rl + 16 * i;
+#pragma unroll
+        for (int bb = 0; bb < kProjPass; ++bb) {
+          const float xv = (p0 + bb < nb) ? sm.xs[p0 + bb][r] : 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[bb][e] += xv * wv[e];
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < kProjPass; ++bb)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm.red[rl][bb][c * VEC + e] = acc[bb][e];
+      __syncthreads();
+      for (int t = threadIdx.x; t < kProjPass * TC; t += kThreads) {
+        const int bb = t / TC, col = t % TC;
+        if (p0 + bb < nb) {
+          float s = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) s += sm.red[q][bb][col];
+          part[((int64_t)split * B + b0 + p0 + bb) * N + tile * TC + col] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// F[b, n] = sum over splits of the partials, in split order (loads issued
+// eight at a time before they are added).
+__device__ __forceinline__ float proj_reduce_one(const float* __restrict__ part, int n_splits, int B, int N, int b,
+                                                 int n) {
+  float s = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (s0 + i < n_splits) ? part[((int64_t)(s0 + i) * B + b) * N + n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Mean-pool one 64-token block of keys (one workgroup).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct MeanpoolSmem {
+  float red[kThreads / (D / VecN<T>::N)][D + 4];
+};
+
+template <typename T, int D>
+__device__ void meanpool_wg(const T* __restrict__ kblock, int64_t st, float* __restrict__ kc_row,
+                            MeanpoolSmem<T, D>& sm) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int CPR = D / VEC;
+  constexpr int RPP = kThreads / CPR;
+  const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  constexpr int NR = kBlk / RPP;
+  uint4 raw[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) raw[i] = ld16(kblock + (int64_t)(r0 + i * RPP) * st + c * VEC);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float x[VEC];
+    cvt16<T>(raw[i], x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sm.red[r0][c * VEC + e] = acc[e];
+  __syncthreads();
+  for (int t = threadIdx.x; t < D; t += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) s += sm.red[r][t];
+    kc_row[t] = s / (float)kBlk;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode scoring of one slice of the candidate range of one (b, g).
+// fvec: the fp32 Forecast of (b, g) in LDS.  Writes raw scores sc[j].
+// 8 lanes per compressed-key row, every load of the slice issued before use.
+// ---------------------------------------------------------------------------
+struct DecodeCands {
+  int cur, c0, c1;   // query block; candidates are [c0, c1)
+};
+
+__device__ __forceinline__ DecodeCands decode_cands(int64_t L, int64_t nb_cap, int n_init, int n_local) {
+  if (L < 1) L = 1;
+  int64_t cur = (L - 1) / kBlk;
+  if (cur > nb_cap - 1 + n_local) cur = nb_cap - 1 + n_local;   // never read past the cache
+  DecodeCands r;
+  r.cur = (int)cur;
+  r.c0 = n_init;
+  r.c1 = (int)min((int64_t)(cur - n_local + 1), nb_cap);
+  if (r.c1 < r.c0) r.c1 = r.c0;
+  return r;
+}
+
+template <int D>
+__device__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_bg, int lo, int hi,
+                               float* __restrict__ sc) {
+  constexpr int LPR = 8;
+  constexpr int F4 = D / 4 / LPR;
+  constexpr int RPP = kThreads / LPR;   // 32 rows per pass
+  const int sub = threadIdx.x % LPR, row0 = threadIdx.x / LPR;
+  float4 fv[F4];
+#pragma unroll
+  for (int i = 0; i < F4; ++i) fv[i] = *reinterpret_cast<const float4*>(fvec + (i * LPR + sub) * 4);
+  constexpr int UNR = 4;
+  for (int base = lo; base < hi; base += RPP * UNR) {
+    float4 kv[UNR][F4];
+#pragma unroll
+    for (int uu = 0; uu < UNR; ++uu) {
+      const int j = base + row0 + uu * RPP;
+      if (j < hi) {
+#pragma unroll
+        for (int i = 0; i < F4; ++i)
+          kv[uu][i] = *reinterpret_cast<const float4*>(kc_bg + (int64_t)j * D + (i * LPR + sub) * 4);
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < UNR; ++uu) {
+      const int j = base + row0 + uu * RPP;
+      float acc = 0.f;
+      if (j < hi) {
+#pragma unroll
+        for (int i = 0; i < F4; ++i) {
+          acc += fv[i].x * kv[uu][i].x;
+          acc += fv[i].y * kv[uu][i].y;
+          acc += fv[i].z * kv[uu][i].z;
+          acc += fv[i].w * kv[uu][i].w;
+        }
+      }
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 1);
+      if (sub == 0 && j < hi) sc[j] = acc;
+    }
+  }
+}
+
+// Top-k + union of one decode problem from its score row (written by an
+// earlier kernel).  keys: LDS, at least (c1 - c0) entries.
+__device__ void topk_decode_wg(const float* __restrict__ sc, DecodeCands dc, int topk, int n_init, int n_local, int U,
+                               int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, uint32_t* keys,
+                               TopkShared& sh) {
+  const int n = dc.c1 - dc.c0;
+  constexpr int PB = 8;   // loads in flight per thread
+  for (int base = 0; base < n; base += PB * kThreads) {
+    float v[PB];
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = base + e * kThreads + threadIdx.x;
+      v[e] = i < n ? sc[dc.c0 + i] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = base + e * kThreads + threadIdx.x;
+      if (i < n) keys[i] = orderable_key(v[e]);
+    }
+  }
+  __syncthreads();
+  topk_union(keys, n, dc.c0, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention: one split (a run of listed blocks) of one KV head for
+// its G query heads.  K/V of the next block are loaded while the current
+// one is computed (two register sets).  Writes the split's unnormalised
+// output o[G][D] and its running max m / sum l (base-2 logits).
+// ---------------------------------------------------------------------------
+struct AttnDecodeParams {
+  const void* q; const void* k; const void* v;
+  int64_t sb, sg, st, kv_len;
+  int ring;
+  const int32_t* idx; const int32_t* cnt; const int64_t* seq_len;
+  int Hkv, U;
+  float qscale;        // scale * log2(e)
+  int bps, n_splits;   // listed blocks per split, number of splits
+  float* out;          // [B, Hq, D] fp32
+  float* ws_o;         // [B*Hkv, n_splits, G, D]
+  float* ws_ml;        // [B*Hkv, n_splits, G, 2]
+};
+
+template <int D, int G>
+struct AttnSmem {
+  float qs[G][D];        // fp32 path: scaled query
+  float sraw[G][kBlk];
+  float ps[G][kBlk];
+  float alpha[G];
+  float red[4][G][D];
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Register set of one 64-token K/V block.
+//   bf16: K as the MFMA A operand of S^T = K Q^T -- wave w owns keys
+//         16w..16w+15, lane l loads key 16w + l%16, dims 32ks + 8(l/16) ..+7
+//   fp32: 4 lanes per key, each 4 x 16-byte loads interleaved over the row
+//   V (both): lane = (16-byte column chunk, token lane) for the PV sums
+template <typename T, int D, int G>
+struct AttnRegs {
+  static constexpr bool kMfma = std::is_same<T, bf16_bits>::value;
+  static constexpr int VEC = VecN<T>::N;
+  static constexpr int NKL = kMfma ? D / 32 : D / 4 / VEC;   // K loads per lane
+  static constexpr int DCH = D / VEC;                          // 16-byte chunks per row
+  static constexpr int TL = kThreads / DCH;                    // token lanes in PV
+  static constexpr int TPL = kBlk / TL;                        // tokens per lane in PV
+  uint4 k[NKL];
+  uint4 v[TPL];
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void attn_load(AttnRegs<T, D, G>& r, const T* kb, const T* vb, int64_t st) {
+  using R = AttnRegs<T, D, G>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if constexpr (R::kMfma) {
+    const T* kp = kb + (int64_t)(16 * w + (lane & 15)) * st + 8 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16(kp + 32 * i);
+  } else {
+    const int tok = threadIdx.x >> 2, part = threadIdx.x & 3;
+#pragma unroll
+    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16(kb + (int64_t)tok * st + (i * 4 + part) * R::VEC);
+  }
+  const int dc = threadIdx.x % R::DCH, tl = threadIdx.x / R::DCH;
+#pragma unroll
+  for (int i = 0; i < R::TPL; ++i) r.v[i] = ld16(vb + (int64_t)(tl + i * R::TL) * st + dc * R::VEC);
+}
+
+// q fragments of the MFMA path: lane l holds q[head l%16][32ks + 8(l/16) ..+7]
+// (zero for the padding heads G..15), already in bf16.
+template <int D>
+struct QFrag {
+  bf16x8_t f[D / 32];
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void attn_block(const AttnRegs<T, D, G>& r, int nvalid, AttnSmem<D, G>& sm,
+                                           const QFrag<D>& qf, float qscale, float (&acc)[G][VecN<T>::N],
+                                           float* m_run, float* l_run) {
+  using R = AttnRegs<T, D, G>;
+  constexpr int VEC = R::VEC;
+  constexpr int HW = (G + 3) / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tl = tid / R::DCH;
+  if constexpr (R::kMfma) {
+    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < R::NKL; ++ks)
+      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[ks]), qf.f[ks], s4, 0, 0, 0);
+    const int h = lane & 15;
+    if (h < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * wid + 4 * (lane >> 4) + i;
+        sm.sraw[h][key] = key < nvalid ? s4[i] * qscale : -INFINITY;
+      }
+    }
+  } else {
+    const int tok = tid >> 2, part = tid & 3;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < R::NKL; ++i) {
+      float kf[VEC];
+      cvt16<T>(r.k[i], kf);
+      const int d0 = (i * 4 + part) * VEC;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[h] += kf[e] * sm.qs[h][d0 + e];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s[h] += __shfl_xor(s[h], 1);
+      s[h] += __shfl_xor(s[h], 2);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if ((h & 3) == part) sm.sraw[h][tok] = (tok < nvalid) ? s[h] : -INFINITY;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    const int h = wid + 4 * i;
+    if (h < G) {
+      const float x = sm.sraw[h][lane];
+      const float mn = fmaxf(m_run[i], wave_max(x));
+      float p, al;
+      if (mn == -INFINITY) { p = 0.f; al = 1.f; }
+      else { p = __builtin_amdgcn_exp2f(x - mn); al = __builtin_amdgcn_exp2f(m_run[i] - mn); }
+      l_run[i] = l_run[i] * al + wave_sum(p);
+      m_run[i] = mn;
+      sm.ps[h][lane] = p;
+      if (lane == 0) sm.alpha[h] = al;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float al = sm.alpha[h];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] *= al;
+  }
+#pragma unroll
+  for (int i = 0; i < R::TPL; ++i) {
+    const int t = tl + i * R::TL;
+    if (t < nvalid) {
+      float vf[VEC];
+      cvt16<T>(r.v[i], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = sm.ps[h][t];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] += p * vf[e];
+      }
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__device__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
+  using R = AttnRegs<T, D, G>;
+  constexpr int VEC = R::VEC;
+  constexpr int HW = (G + 3) / 4;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int Hq = p.Hkv * G;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int c = min(p.cnt[bg], p.U);
+  const int u0 = split * p.bps, u1 = min(c, u0 + p.bps);
+  const int64_t L = min(p.seq_len[b], p.kv_len);
+  const T* q = (const T*)p.q;
+  QFrag<D> qf;
+  if constexpr (R::kMfma) {
+    const int h = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (h < G) raw = ld16(q + ((int64_t)b * Hq + g * G + h) * D + 32 * ks + 8 * (lane >> 4));
+      qf.f[ks] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  } else {
+    for (int i = tid; i < G * D; i += kThreads)
+      sm.qs[i / D][i % D] = to_f32<T>(q[((int64_t)b * Hq + g * G) * D + i]) * p.qscale;
+  }
+  const float sscale = R::kMfma ? p.qscale : 1.f;
+  float m_run[HW], l_run[HW];
+#pragma unroll
+  for (int i = 0; i < HW; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+  float acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+  const T* kbase = (const T*)p.k + b * p.sb + g * p.sg;
+  const T* vbase = (const T*)p.v + b * p.sb + g * p.sg;
+  const int32_t* list = p.idx + (int64_t)bg * p.U;
+
+  // block u -> (token base in the buffer, valid token count); invalid ids read nothing
+  auto locate = [&](int u, int64_t& tb, int& nvalid) {
+    const int j = list[u];
+    tb = (int64_t)(p.ring ? u : j) * kBlk;
+    if (j < 0 || tb + kBlk > p.kv_len) { nvalid = -1; return; }
+    const int64_t rem = L - (int64_t)j * kBlk;
+    nvalid = rem <= 0 ? 0 : (rem >= kBlk ? kBlk : (int)rem);
+  };
+  AttnRegs<T, D, G> ra, rb;
+  int64_t tba = 0, tbb = 0;
+  int nva = -1, nvb = -1;
+  __syncthreads();
+  if (u0 < u1) {
+    locate(u0, tba, nva);
+    if (nva >= 0) attn_load<T, D, G>(ra, kbase + tba * p.st, vbase + tba * p.st, p.st);
+  }
+  for (int u = u0; u < u1; u += 2) {
+    if (u + 1 < u1) {
+      locate(u + 1, tbb, nvb);
+      if (nvb >= 0) attn_load<T, D, G>(rb, kbase + tbb * p.st, vbase + tbb * p.st, p.st);
+    }
+    attn_block<T, D, G>(ra, nva < 0 ? 0 : nva, sm, qf, sscale, acc, m_run, l_run);
+    if (u + 1 >= u1) break;
+    if (u + 2 < u1) {
+      locate(u + 2, tba, nva);
+      if (nva >= 0) attn_load<T, D, G>(ra, kbase + tba * p.st, vbase + tba * p.st, p.st);
+    }
+    attn_block<T, D, G>(rb, nvb < 0 ? 0 : nvb, sm, qf, sscale, acc, m_run, l_run);
+  }
+
+  // sum the PV token lanes: inside the wave, then across the 4 waves
+#pragma unroll
+  for (int o = R::DCH; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+  const int dc = tid % R::DCH;
+  if (lane < R::DCH) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm.red[wid][h][dc * VEC + e] = acc[h][e];
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)bg * p.n_splits + split) * G;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, d = i % D;
+    p.ws_o[(pbase + h) * D + d] = sm.red[0][h][d] + sm.red[1][h][d] + sm.red[2][h][d] + sm.red[3][h][d];
+  }
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    const int h = wid + 4 * i;
+    if (h < G && lane == 0) {
+      p.ws_ml[(pbase + h) * 2 + 0] = m_run[i];
+      p.ws_ml[(pbase + h) * 2 + 1] = l_run[i];
+    }
+  }
+}
+
+// Merge the splits of one KV head (written by an earlier kernel), in split
+// order: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+template <int D, int G>
+struct CombineSmem {
+  float ml[kMaxSplitsDecode][G][2];
+  float wts[kMaxSplitsDecode][G];
+  float den[G];
+};
+
+template <int D, int G>
+__device__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D, G>& sm) {
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int Hq = p.Hkv * G;
+  const int ns = p.n_splits;
+  const int64_t sbase = (int64_t)bg * ns * G;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < ns * G * 2; i += kThreads) (&sm.ml[0][0][0])[i] = p.ws_ml[sbase * 2 + i];
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, sm.ml[sp][tid][0]);
+    float den = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float m = sm.ml[sp][tid][0];
+      const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      sm.wts[sp][tid] = w;
+      den += w * sm.ml[sp][tid][1];
+    }
+    sm.den[tid] = den;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, d = i % D;
+    float num = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (s0 + e < ns) ? p.ws_o[(sbase + (s0 + e) * G + h) * D + d] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (s0 + e < ns) num += sm.wts[s0 + e][h] * v[e];
+    }
+    const float den = sm.den[h];
+    p.out[((int64_t)b * Hq + g * G + h) * D + d] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+// Split plan of the decode attention: about `target` workgroups, at most
+// kMaxSplitsDecode splits, every split the same number of listed blocks.
+__host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
+  const int target = 2048;
+  int ns = (target + n_bg - 1) / n_bg;
+  if (ns > U) ns = U;
+  if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;
+  if (ns < 1) ns = 1;
+  bps = (U + ns - 1) / ns;
+  n_splits = (U + bps - 1) / bps;
+}
+
+// Score split plan: about 1024 workgroups, at least 64 candidate rows each.
+__host__ __device__ inline int score_split_plan(int n_bg, int64_t nb_cap) {
+  int s = (1024 + n_bg - 1) / n_bg;
+  const int max_s = (int)((nb_cap + 63) / 64);
+  if (s > max_s) s = max_s;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace bskv

@@ -50,61 +50,6 @@ __device__ __forceinline__ void load_fvec(const float* src, float4* fv) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid (n_splits, B*H).  Every workgroup scores a slice of the
-// candidate range of its (b, g) into the workspace; the last one to finish
-// (agent-scope counter) loads all candidate scores into LDS and runs the
-// top-k + union.  The counter is reset by that workgroup.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) void score_topk_decode_kernel(
-    const float* __restrict__ f, const float* __restrict__ kc, int64_t nb_cap, const int64_t* __restrict__ seq_len,
-    int H, int block, int topk, int n_init, int n_local, int U, int n_splits, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ cnt_out, float* __restrict__ scores_dbg, float* __restrict__ ws_scores,
-    int* __restrict__ ws_count) {
-  extern __shared__ uint32_t keys[];
-  __shared__ TopkShared sh;
-  __shared__ int is_last;
-
-  const int bg = blockIdx.y, b = bg / H, split = blockIdx.x;
-  int64_t L = seq_len[b];
-  if (L < 1) L = 1;
-  int64_t cur64 = (L - 1) / block;
-  // never read compressed keys beyond the cache (a caller contract violation)
-  if (cur64 > nb_cap - 1 + n_local) cur64 = nb_cap - 1 + n_local;
-  const int cur = (int)cur64;
-  const int c0 = n_init, c1 = min(cur - n_local + 1, (int)nb_cap);
-  const int n = max(0, c1 - c0);
-  const int per = (n + n_splits - 1) / n_splits;
-  const int lo = c0 + split * per, hi = min(c1, lo + per);
-  const float* kc_bg = kc + (int64_t)bg * nb_cap * D;
-  float* sc = ws_scores + (int64_t)bg * nb_cap;
-
-  float4 fv[D / 32];
-  load_fvec<D>(f + (int64_t)bg * D, fv);
-  if (scores_dbg) {
-    float* dbg = scores_dbg + (int64_t)bg * nb_cap;
-    score_rows<D>(kc_bg, fv, lo, hi, [&](int j, float s) { sc[j] = s; dbg[j] = s; });
-    if (split == 0) {
-      for (int j = threadIdx.x; j <= min(cur, (int)nb_cap - 1); j += kThreads)
-        if (j < c0 || j >= c1) dbg[j] = -INFINITY;
-    }
-  } else {
-    score_rows<D>(kc_bg, fv, lo, hi, [&](int j, float s) { sc[j] = s; });
-  }
-
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&ws_count[bg], 1) == n_splits - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < n; i += kThreads) keys[i] = orderable_key(sc[c0 + i]);
-  __syncthreads();
-  topk_union(keys, n, c0, topk, cur, n_init, n_local, U, idx_out + (int64_t)bg * U, cnt_out + bg, sh);
-  if (threadIdx.x == 0) ws_count[bg] = 0;
-}
-
-// ---------------------------------------------------------------------------
 // Prefill: grid (n_qb, B*H); one workgroup per query block.  It sums the
 // block's Forecast vectors (fp32), scores every candidate compressed key
 // into LDS and runs the top-k + union.
@@ -159,42 +104,19 @@ __global__ __launch_bounds__(kThreads) void score_topk_prefill_kernel(
              cnt_out + (int64_t)bg * n_qb + qi, sh);
 }
 
-static int decode_splits(int n_bg, int64_t nb_cap) {
-  // about 1024 workgroups in flight, at least 64 candidate rows each
-  int s = (1024 + n_bg - 1) / n_bg;
-  int max_s = (int)((nb_cap + 63) / 64);
-  if (s > max_s) s = max_s;
-  return s < 1 ? 1 : s;
-}
+size_t score_decode_workspace_bytes(int B, int H, int64_t nb_cap);
+hipError_t launch_score_topk_decode(const ScoreTopkArgs& a);
 
 size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, int D) {
   (void)D;
-  if (n_q_tokens > 0) return 0;
-  const size_t sc = (size_t)B * H * nb_cap * sizeof(float);
-  const size_t ctr = (size_t)B * H * sizeof(int);
-  return ((sc + 255) / 256) * 256 + ((ctr + 255) / 256) * 256;
+  return n_q_tokens > 0 ? 0 : score_decode_workspace_bytes(B, H, nb_cap);
 }
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a) {
   const int n_bg = a.B * a.H;
   const int64_t cand_cap = a.nb_cap < kMaxCandidates ? a.nb_cap : kMaxCandidates;
   const size_t lds = (size_t)cand_cap * sizeof(uint32_t);
-  if (a.n_q_tokens == 0) {
-    const int ns = decode_splits(n_bg, a.nb_cap);
-    const size_t sc_bytes = (size_t)n_bg * a.nb_cap * sizeof(float);
-    float* sc = (float*)a.ws;
-    int* ctr = (int*)((char*)a.ws + ((sc_bytes + 255) / 256) * 256);
-    dim3 grid(ns, n_bg);
-    if (a.D == 64)
-      hipLaunchKernelGGL(score_topk_decode_kernel<64>, grid, dim3(kThreads), lds, a.stream, (const float*)a.f, a.kc,
-                         a.nb_cap, a.seq_len, a.H, a.block, a.topk, a.n_init, a.n_local, a.U, ns, a.idx, a.cnt,
-                         a.scores, sc, ctr);
-    else
-      hipLaunchKernelGGL(score_topk_decode_kernel<128>, grid, dim3(kThreads), lds, a.stream, (const float*)a.f, a.kc,
-                         a.nb_cap, a.seq_len, a.H, a.block, a.topk, a.n_init, a.n_local, a.U, ns, a.idx, a.cnt,
-                         a.scores, sc, ctr);
-    return hipGetLastError();
-  }
+  if (a.n_q_tokens == 0) return launch_score_topk_decode(a);
   const int n_qb = (a.n_q_tokens + a.block - 1) / a.block;
   dim3 grid(n_qb, n_bg);
 #define BSKV_PREFILL_LAUNCH(T, DD)                                                                           \

@@ -31,13 +31,10 @@
  *   Accumulation is always fp32.
  * - head_dim must be 64 or 128; block must be 64 (the pages' block size).
  * - Workspaces: a call that takes `ws` needs at least the bytes returned by
- *   its *_workspace() query.  A workspace must be zero-filled before its
- *   first use with a given configuration (the arguments of its *_workspace()
- *   query); each call leaves its completion counters at zero again, so later
- *   calls with the SAME configuration can reuse it without clearing.  Using
- *   it with another configuration first needs a new zero fill (the counters
- *   of the new layout may sit on old partial results).  Calls that overlap
- *   in time must not share a workspace.
+ *   its *_workspace() query, 16-byte aligned.  Its contents need no
+ *   initialisation: every partial result is written before it is read, and
+ *   the library keeps no counters in it.  Calls that overlap in time must not
+ *   share a workspace.
  * - kv_len / src_len: the number of tokens the K/V buffers hold (their
  *   allocation along the token axis, in whole blocks).  Kernels skip any
  *   listed block that would reach beyond it, so a bad index list cannot make
@@ -86,7 +83,8 @@ const char* bskv_last_error(void);
  * x      [B, hidden]                 dtype, contiguous
  * w      [hidden, n_kv_heads*head_dim] dtype, contiguous (row-major)
  * f_out  [B, n_kv_heads, head_dim]   fp32, contiguous
- * hidden must be a multiple of 128.  ws: bskv_forecast_proj_workspace().
+ * hidden must be a multiple of 256.  ws: bskv_forecast_proj_workspace().
+ * Two launches: 256-row partial products, then their sum in split order.
  * The same call serves the separate layer-0 projection ([EXPL] "Training"):
  * pass that projection's weights.  Deterministic: fixed summation order.
  * ----------------------------------------------------------------------- */
@@ -153,6 +151,8 @@ int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, 
  * kc must hold compressed keys for every candidate block.  The candidate
  * count per problem is limited to 16384 (a 1M-token context).
  * ws: bskv_score_topk_workspace() bytes (may be 0 bytes for prefill).
+ * Decode runs two launches: candidate scores in slices, then one top-k
+ * workgroup per (b, g); prefill runs one workgroup per query block.
  * ----------------------------------------------------------------------- */
 size_t bskv_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kc_nb_cap, int head_dim);
 int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start,
@@ -169,8 +169,8 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
  *   out[b, h] = softmax_t(scale * q[b,h] . k_t) v_t
  *
  * over the tokens t of the listed blocks idx[b, g, 0..cnt-1] with position
- * < seq_len[b].  Split over blocks, fp32 online softmax, combined in a
- * fixed order (deterministic).
+ * < seq_len[b].  Two launches: splits over the listed blocks (fp32 online
+ * softmax), then their merge in split order (deterministic).
  * q      [B, n_q_heads, head_dim] dtype, contiguous
  * k, v   cache (kv_is_ring == 0): block idx[u] is read at token idx[u]*block;
  *        ring  (kv_is_ring != 0): the u-th listed block is read at token
@@ -227,6 +227,39 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
                                   const int64_t* src_strides, int64_t src_len, const int32_t* idx, const int32_t* cnt,
                                   void* ring_k, void* ring_v, int B, int n_kv_heads, int head_dim,
                                   int block, int U, int n_workgroups, hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * One decode layer with one-layer-ahead selection.  [EXPL] "The fourth
+ * projection", Alg. 2 and Eq. 4: right after layer l's projection emits the
+ * Forecast F_l, it scores layer l+1's compressed keys and picks layer l+1's
+ * blocks while layer l attends to the blocks picked one layer earlier.
+ * Equivalent to this sequence of the calls above, in three kernels:
+ *   kv_block_meanpool(k, newest_only=1)  -> kc           (this layer)
+ *   forecast_proj(x, w_forecast)         -> F            (this layer's Forecast)
+ *   forecast_block_score_topk(F, kc_next) -> idx_next, cnt_next (next layer)
+ *   block_sparse_attn_decode(q, k, v, idx, cnt) -> out   (this layer)
+ * with the same layouts as those calls (kc and kc_next: [B, Hkv, kc_nb_cap,
+ * d]; U = topk + n_init + n_local for idx and idx_next).  The scoring of the
+ * next layer and this layer's attention share one launch.
+ * x, w_forecast, kc_next, idx_next, cnt_next are all given or all NULL
+ * (NULL: the last layer, no selection).  hidden must be a multiple of 256.
+ * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL.
+ * stages: bit 0 = K1 (projection partials), bit 1 = K2 (next-layer scores +
+ * this layer's attention splits), bit 2 = K3 (next-layer top-k + attention
+ * merge + newest-block update of kc); 7 runs the whole layer.  A later
+ * stage reads what the earlier ones left in ws, so a caller may launch them
+ * separately (to place other work between them, or to time each), in order,
+ * with the same ws and arguments.
+ * ----------------------------------------------------------------------- */
+size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,
+                                             int64_t kc_nb_cap, int U, int dtype);
+int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int dtype,
+                                const int64_t* kv_strides, int64_t kv_len, const int64_t* seq_len,
+                                float* kc, const int32_t* idx, const int32_t* cnt, float scale, float* out,
+                                const void* x, const void* w_forecast, int hidden, const float* kc_next,
+                                int32_t* idx_next, int32_t* cnt_next, int B, int n_q_heads, int n_kv_heads,
+                                int head_dim, int block, int64_t kc_nb_cap, int topk, int n_init,
+                                int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Device address of host memory allocated pinned (hipHostMalloc, or a torch
  * tensor created with pin_memory=True).  Returns BSKV_EHIP if the pointer is

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_six_hot_path_calls():
     names = declared_functions()
     for n in ("bskv_forecast_proj", "bskv_kv_block_meanpool", "bskv_forecast_block_score_topk",
-              "bskv_block_sparse_attn_decode", "bskv_block_sparse_attn_prefill", "bskv_prefetch_selected_blocks"):
+              "bskv_block_sparse_attn_decode", "bskv_block_sparse_attn_prefill", "bskv_prefetch_selected_blocks",
+              "bskv_decode_layer_lookahead"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_strerror_and_version():
 
 
 def test_workspace_queries_are_pure_host_arithmetic():
-    assert lib.bskv_forecast_proj_workspace(8, 4096, 8, 128, 1) >= 32 * 8 * 1024 * 4
+    assert lib.bskv_forecast_proj_workspace(8, 4096, 8, 128, 1) >= 16 * 8 * 1024 * 4
     assert lib.bskv_score_topk_workspace(8, 8, 0, 2048, 128) >= 64 * 2048 * 4
     assert lib.bskv_score_topk_workspace(4, 8, 2048, 2048, 128) == 0
     assert lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69) > 0
@@ -143,3 +144,22 @@ def test_prefetch_validation():
 def test_host_device_pointer_rejects_null():
     out = ctypes.c_void_p()
     assert lib.bskv_host_device_pointer(None, ctypes.byref(out)) == EINVAL
+
+
+def test_decode_layer_validation():
+    f = lib.bskv_decode_layer_lookahead
+    ws = lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 4096, 2048, 69, 1)
+    assert ws > lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 0, 2048, 69, 1)
+
+    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=7, dt=1, hq=32, nl=4, wsb=ws):
+        return f(P, P, P, dt, S3, 131072, P, P, P, P, 0.088, P, x, w, hidden, kcn, idn, cnn, 8, hq, 8, 128, 64, 2048,
+                 64, 1, nl, stages, P, wsb, None)
+    assert call(x=None) == EINVAL            # lookahead arguments: all or none
+    assert call(idn=None) == EINVAL
+    assert call(stages=0) == EINVAL
+    assert call(stages=8) == EINVAL
+    assert call(dt=3) == EDTYPE
+    assert call(hq=24) == EUNSUP
+    assert call(hidden=1000) == EUNSUP
+    assert call(nl=0) == EINVAL
+    assert call(wsb=ws - 16) == ENOSPC

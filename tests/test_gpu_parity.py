@@ -339,3 +339,68 @@ def test_prefetch_from_pinned_host_and_ring_attention():
         for g in range(wl.Hkv):
             assert np.array_equal(got[b, g, :cn[b, g]], want[b, g, :cn[b, g]])
     assert torch.equal(out_ring, out_res), "ring read must equal resident read bit for bit"
+
+
+# ----------------------------------------------------------------------------- fused decode layer
+def _layer_case(dtype, d, G, B, T, lens, seed):
+    wl = CONFIGS[2]
+    Hkv = 4
+    c = _gpu(random_decode_case(seed, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, hidden=512, seq_len=lens))
+    c2 = _gpu(random_decode_case(seed + 100, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens))
+    kc = _kc_gpu(c["k"], c["seq_len"])
+    kc_next = _kc_gpu(c2["k"], c2["seq_len"])
+    # this layer's own block lists (from any Forecast: the oracle's, on the pooled keys)
+    sel = orc.decode_select(np64(c2["f"]), orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens), lens, 6, 1, 2, 64)
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    return c, kc, kc_next, idx, cnt
+
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2), ("bf16", 64, 8)])
+def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
+    lens = [64 * 30, 64 * 30 - 5, 64 * 17, 64 * 30]
+    c, kc, kc_next, idx, cnt = _layer_case(dtype, d, G, 4, 64 * 30, lens, 3)
+    # stale rows where the newest blocks go, to see them rewritten
+    kc_a = kc.clone()
+    kc_a[:, :, 29] = float("nan")
+    kc_a[:, :, 16] = float("nan")
+    kc_b = kc_a.clone()
+    scale = 1.0 / math.sqrt(d)
+    bskv.kv_block_meanpool(c["k"], c["seq_len"], kc_a, 0, kc.shape[2], newest_only=True)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], 4, d)
+    idx_a, cnt_a = bskv.forecast_block_score_topk(f, kc_next, 6, 1, 2, seq_len=c["seq_len"])
+    out_a = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    out_b, idx_b, cnt_b = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_b, idx, cnt, scale,
+                                                      x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
+                                                      n_local=2)
+    torch.cuda.synchronize()
+    assert torch.equal(kc_a.nan_to_num(7.0), kc_b.nan_to_num(7.0))
+    assert torch.equal(idx_a, idx_b) and torch.equal(cnt_a, cnt_b)
+    assert torch.equal(out_a, out_b)
+    # and against the oracle
+    lens_np = np.array(lens)
+    f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), 4, d)
+    sel = orc.decode_select(f_or, np64(kc_next), lens_np, 6, 1, 2, 64)
+    check_selection(idx_b, cnt_b, sel, 6)
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens_np,
+                             scale, 64)
+    assert max_abs(np64(out_b), want) < (1e-4 if dtype == "f32" else 2e-2)
+
+
+def test_decode_layer_stages_and_last_layer():
+    lens = [64 * 20] * 2
+    c, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
+    kc1, kc2 = kc.clone(), kc.clone()
+    out1, i1, n1 = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc1, idx, cnt, x=c["x_sel"],
+                                               w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
+    i2, n2 = torch.empty_like(idx), torch.empty_like(cnt)
+    out2 = torch.empty_like(out1)
+    for st in (1, 2, 4):
+        bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc2, idx, cnt, out=out2, x=c["x_sel"],
+                                    w=c["w_sel"], kc_next=kc_next, idx_next=i2, cnt_next=n2, topk=6, n_init=1,
+                                    n_local=2, stages=st)
+    out3, none_i, none_c = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt,
+                                                       topk=6, n_init=1, n_local=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(i1, i2) and torch.equal(n1, n2) and torch.equal(kc1, kc2)
+    assert none_i is None and none_c is None and torch.equal(out3, out1)
