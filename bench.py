@@ -172,32 +172,42 @@ def time_graph(torch, fn, steps, warmup, use_graph=True):
 
 
 def kernel_times(torch, bench, reps=3):
-    """Average duration per launch of each kernel (or per-op call), HIP
-    events around back-to-back launches over all layers on the launching
-    stream.  layer_k1/k2/k3 are the three kernels of one fused layer, each
-    launched on its own (stages 1, 2, 4) after a full pass has filled the
-    workspace it reads."""
+    """Average duration per launch of each kernel (or per-op call): the
+    launches of one kernel over all layers, repeated `reps` times, are
+    captured in a HIP graph and its replay is timed with HIP events on the
+    stream it runs on, so host-side launch cost does not enter.  layer_k1/
+    k2/k3 are the three kernels of the fused layer, each launched on its own
+    (stages 1, 2, 4) after a full pass has filled the workspace they read."""
     res = {}
     for l in range(bench.L):
         bench.layer(l)
+    torch.cuda.synchronize()
     for name, fn in (("layer_k1", lambda l: bench.layer(l, 1)), ("layer_k2", lambda l: bench.layer(l, 2)),
                      ("layer_k3", lambda l: bench.layer(l, 4)),
                      ("kv_block_meanpool", bench.meanpool), ("forecast_proj", bench.proj),
                      ("score_topk", bench.select), ("attn_decode", bench.attend)):
         # the last layer selects nothing, so it has no projection kernel
         layers = range(bench.L - 1) if name == "layer_k1" else range(bench.L)
-        for l in layers:   # warm
-            fn(l)
+
+        def body():
+            for _ in range(reps):
+                for l in layers:
+                    fn(l)
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
-            for l in layers:
-                fn(l)
+        g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) * 1e-3 / (reps * len(layers))
+        del g
     return res
 
 

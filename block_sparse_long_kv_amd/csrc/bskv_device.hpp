@@ -29,16 +29,18 @@ template <> struct VecN<bf16_bits> { static constexpr int N = 8; };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Streamed 16-byte load that should not displace reusable lines (KV blocks
-// read once per step).
-__device__ __forceinline__ uint4 ld16_stream(const void* p) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  uint4 r;
-  r.x = __builtin_nontemporal_load(&q->x);
-  r.y = __builtin_nontemporal_load(&q->y);
-  r.z = __builtin_nontemporal_load(&q->z);
-  r.w = __builtin_nontemporal_load(&q->w);
-  return r;
+// Streamed 16-byte load (nontemporal): for data read once per step -- the
+// selected K/V blocks, compressed keys, Forecast weights -- so it does not
+// displace reusable lines.  On gfx950 streaming reads this way reach ~6.5 TB/s
+// against ~6.0 TB/s for plain loads.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld16f_nt(const float* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 template <typename T> __device__ __forceinline__ void cvt16(const uint4& r, float* o);
@@ -97,108 +99,162 @@ __device__ __forceinline__ uint32_t orderable_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Shared scratch of topk_union.
+// Shared scratch of topk_union.  The radix histogram is double buffered
+// (pass p counts into buffer p % 2 while the previous one is cleared) and has
+// kHistCopies private copies (lane l counts into copy l % kHistCopies, copies
+// 257 words apart) so that atomic adds of lanes that share a bin -- scores
+// share sign and exponent bits -- spread over several banks.
+constexpr int kHistCopies = 4;
+constexpr int kHistStride = 257;
 struct TopkShared {
-  int hist[256];
+  int hist[2][kHistCopies * kHistStride];
   int scan_tmp[4];
-  int pick[2];
+  int pick[3];
 };
 
-// Causal top-k + union for one selection problem, run by all 256 threads.
-//   keys[0..n)  orderable scores of the candidate blocks c0 .. c0+n-1 (LDS)
-//   cur         the query's block; blocks 0..cur are the causal range
-// Writes idx_out[0..U) (ascending block ids of init | local | top-k, padded
-// with -1) and *cnt_out.  Ranking: key descending, block id ascending.
-__device__ void topk_union(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init, int n_local,
-                           int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
-  const int tid = threadIdx.x;
-  uint32_t thr = 0;
-  int need = 0;
-  const bool take_none = (topk <= 0);
-  const bool take_all = !take_none && (n <= topk);
-  if (!take_all && !take_none) {
-    // MSB-first radix select of the topk-th largest key, 8 bits per pass.
-    uint32_t prefix = 0, mask = 0;
-    int kk = topk;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      sh.hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kThreads) {
-        const uint32_t key = keys[i];
-        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1);
+// Exclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_excl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  return inc - v;
+}
+
+// Top-k + union for one selection problem, run by all 256 threads.  Thread
+// t owns candidates t*KPT .. t*KPT+KPT-1 (so its keys are in block-id order);
+// with KPT <= 8 they are held in registers, above that re-read from LDS.
+template <int KPT>
+__device__ void topk_union_regs(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init, int n_local,
+                                int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int i0 = tid * KPT;
+  constexpr bool kRegs = KPT <= 8;
+  uint32_t kr[kRegs ? KPT : 1];
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) kr[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
+  }
+  auto key = [&](int e) -> uint32_t {
+    if constexpr (kRegs) return kr[e];
+    else return keys[i0 + e];
+  };
+
+  const bool take_none = topk <= 0 || n <= 0;
+  const bool take_all = !take_none && n <= topk;
+  uint32_t prefix = 0, mask = 0;
+  int kk = topk;
+  if (!take_none && !take_all) {
+    // MSB-first radix select of the topk-th largest key, 8 bits per pass,
+    // stopping as soon as the bucket holding it is taken whole.
+    for (int i = tid; i < kHistCopies * kHistStride; i += kThreads) sh.hist[0][i] = 0;
+    __syncthreads();
+    int* mine = nullptr;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      int* h = sh.hist[pass & 1];
+      mine = h + (tid & (kHistCopies - 1)) * kHistStride;
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const uint32_t k = key(e);
+        if (i0 + e < n && (k & mask) == prefix) atomicAdd(&mine[(k >> shift) & 255u], 1);
       }
       __syncthreads();
-      // Thread tid looks at digit D = 255 - tid; incl = #keys with digit >= D.
-      const int D = 255 - tid;
-      const int h = sh.hist[D];
-      int tot;
-      const int excl = block_excl_scan(h, sh.scan_tmp, tot);
-      const int above = excl;          // # with digit > D
-      const int incl = excl + h;       // # with digit >= D
-      if (above < kk && kk <= incl) {
-        sh.pick[0] = D;
-        sh.pick[1] = above;
+      if (wid == 0) {
+        // lane l looks at digits 255-4l .. 252-4l (descending)
+        int c[4], ls = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int D = 255 - 4 * lane - r;
+          int v = 0;
+#pragma unroll
+          for (int cp = 0; cp < kHistCopies; ++cp) v += h[cp * kHistStride + D];
+          c[r] = v;
+          ls += v;
+        }
+        int run = wave_excl_scan(ls);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (run < kk && kk <= run + c[r]) {
+            sh.pick[0] = 255 - 4 * lane - r;
+            sh.pick[1] = run;
+            sh.pick[2] = c[r];
+          }
+          run += c[r];
+        }
+      } else {
+        int* hn = sh.hist[(pass + 1) & 1];
+        for (int i = tid - 64; i < kHistCopies * kHistStride; i += kThreads - 64) hn[i] = 0;
       }
       __syncthreads();
       prefix |= ((uint32_t)sh.pick[0]) << shift;
       mask |= 255u << shift;
       kk -= sh.pick[1];
-      __syncthreads();
+      const bool whole = (kk == sh.pick[2]);
+      __syncthreads();   // pick is rewritten by the next pass
+      if (whole) break;
     }
-    thr = prefix;   // key of the topk-th best candidate
-    need = kk;      // how many candidates equal to thr are taken (lowest ids first)
   }
-
-  // Ordered pass over block ids 0..cur in contiguous per-thread chunks.
-  const int N = cur + 1;
-  const int E = (N + kThreads - 1) / kThreads;
-  const int j_lo = min(N, tid * E), j_hi = min(N, j_lo + E);
-  const int local_lo = cur - n_local + 1;
-  int my_ties = 0;
-  if (!take_all && !take_none) {
-    for (int j = j_lo; j < j_hi; ++j) {
-      const int i = j - c0;
-      if (i >= 0 && i < n && keys[i] == thr) ++my_ties;
+  // ties: keys whose masked value equals the threshold bucket; the kk of
+  // them with the lowest block ids are taken
+  const int need = kk;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (i0 + e < n && !take_none) {
+      if (take_all) ++gt;
+      else {
+        const uint32_t km = key(e) & mask;
+        gt += km > prefix;
+        eq += km == prefix;
+      }
     }
   }
   int tot;
-  int tie_rank = block_excl_scan(my_ties, sh.scan_tmp, tot);
-  int my_sel = 0;
-  for (int j = j_lo; j < j_hi; ++j) {
-    const int i = j - c0;
-    bool s = (j < n_init) || (j >= local_lo);
-    if (i >= 0 && i < n && !take_none) {
-      if (take_all) s = true;
-      else {
-        const uint32_t key = keys[i];
-        if (key > thr) s = true;
-        else if (key == thr) { if (tie_rank < need) s = true; ++tie_rank; }
+  const int ex = block_excl_scan((gt << 16) | eq, sh.scan_tmp, tot);
+  int gt_b = ex >> 16, eq_b = ex & 0xffff;
+  const int n_sel = take_none ? 0 : (take_all ? n : topk);
+  const int local_lo = max(0, cur - n_local + 1);
+  const int a = min(n_init, local_lo);          // initial blocks below the local window
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (i0 + e < n && !take_none) {
+      bool sel;
+      int pos;
+      if (take_all) {
+        sel = true;
+        pos = a + gt_b++;
+      } else {
+        const uint32_t km = key(e) & mask;
+        if (km > prefix) { sel = true; pos = a + gt_b + min(eq_b, need); ++gt_b; }
+        else if (km == prefix) { sel = eq_b < need; pos = a + gt_b + eq_b; ++eq_b; }
+        else { sel = false; pos = 0; }
       }
-    }
-    my_sel += s ? 1 : 0;
-  }
-  int total;
-  int pos = block_excl_scan(my_sel, sh.scan_tmp, total);
-  // second walk: recompute the same flags and write the positions
-  tie_rank = tie_rank - my_ties;  // restore this thread's starting tie rank
-  for (int j = j_lo; j < j_hi; ++j) {
-    const int i = j - c0;
-    bool s = (j < n_init) || (j >= local_lo);
-    if (i >= 0 && i < n && !take_none) {
-      if (take_all) s = true;
-      else {
-        const uint32_t key = keys[i];
-        if (key > thr) s = true;
-        else if (key == thr) { if (tie_rank < need) s = true; ++tie_rank; }
-      }
-    }
-    if (s) {
-      if (pos < U) idx_out[pos] = j;
-      ++pos;
+      if (sel && pos < U) idx_out[pos] = c0 + i0 + e;
     }
   }
+  const int n_loc = cur - local_lo + 1;
+  const int total = a + n_sel + n_loc;
+  for (int j = tid; j < a; j += kThreads) idx_out[j] = j;
+  for (int j = tid; j < n_loc; j += kThreads)
+    if (a + n_sel + j < U) idx_out[a + n_sel + j] = local_lo + j;
   for (int p = total + tid; p < U; p += kThreads) idx_out[p] = -1;
   if (tid == 0) *cnt_out = min(total, U);
+}
+
+// Causal top-k + union for one selection problem, run by all 256 threads.
+//   keys[0..n)  orderable scores of the candidate blocks c0 .. c0+n-1 (LDS)
+//   cur         the query's block; candidates are the causal blocks that are
+//               neither initial (< n_init) nor local (> cur - n_local)
+// Writes idx_out[0..U) (ascending block ids of init | top-k | local, padded
+// with -1) and *cnt_out.  Ranking: key descending, block id ascending.
+__device__ __forceinline__ void topk_union(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init,
+                                           int n_local, int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
+  if (n <= 8 * kThreads) topk_union_regs<8>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
+  else topk_union_regs<48>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
 }
 
 }  // namespace bskv

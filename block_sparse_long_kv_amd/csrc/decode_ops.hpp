@@ -23,7 +23,7 @@
 namespace bskv {
 
 constexpr int kBlk = 64;            // tokens per KV block
-constexpr int kMaxSplitsDecode = 64;
+constexpr int kMaxSplitsDecode = 32;   // attention splits per KV head
 
 // ---------------------------------------------------------------------------
 // Forecast projection, split over the hidden dimension.
@@ -57,7 +57,7 @@ __device__ void proj_partial_wg(const T* __restrict__ x, const T* __restrict__ w
   const int col0 = tile * TC + c * VEC;
   uint4 raw[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) raw[i] = ld16(w + (int64_t)(r_begin + rl + 16 * i) * N + col0);
+  for (int i = 0; i < RPT; ++i) raw[i] = ld16_nt(w + (int64_t)(r_begin + rl + 16 * i) * N + col0);
   for (int b0 = 0; b0 < B; b0 += kProjMaxB) {
     const int nb = min(kProjMaxB, B - b0);
     // stage x[b0 .. b0+nb)[r_begin .. +kProjRows) as fp32 (16-byte loads)
@@ -143,7 +143,7 @@ __device__ void meanpool_wg(const T* __restrict__ kblock, int64_t st, float* __r
   constexpr int NR = kBlk / RPP;
   uint4 raw[NR];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) raw[i] = ld16(kblock + (int64_t)(r0 + i * RPP) * st + c * VEC);
+  for (int i = 0; i < NR; ++i) raw[i] = ld16_nt(kblock + (int64_t)(r0 + i * RPP) * st + c * VEC);
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     float x[VEC];
@@ -202,7 +202,7 @@ __device__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_b
       if (j < hi) {
 #pragma unroll
         for (int i = 0; i < F4; ++i)
-          kv[uu][i] = *reinterpret_cast<const float4*>(kc_bg + (int64_t)j * D + (i * LPR + sub) * 4);
+          kv[uu][i] = ld16f_nt(kc_bg + (int64_t)j * D + (i * LPR + sub) * 4);
       }
     }
 #pragma unroll
@@ -305,15 +305,15 @@ __device__ __forceinline__ void attn_load(AttnRegs<T, D, G>& r, const T* kb, con
   if constexpr (R::kMfma) {
     const T* kp = kb + (int64_t)(16 * w + (lane & 15)) * st + 8 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16(kp + 32 * i);
+    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16_nt(kp + 32 * i);
   } else {
     const int tok = threadIdx.x >> 2, part = threadIdx.x & 3;
 #pragma unroll
-    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16(kb + (int64_t)tok * st + (i * 4 + part) * R::VEC);
+    for (int i = 0; i < R::NKL; ++i) r.k[i] = ld16_nt(kb + (int64_t)tok * st + (i * 4 + part) * R::VEC);
   }
   const int dc = threadIdx.x % R::DCH, tl = threadIdx.x / R::DCH;
 #pragma unroll
-  for (int i = 0; i < R::TPL; ++i) r.v[i] = ld16(vb + (int64_t)(tl + i * R::TL) * st + dc * R::VEC);
+  for (int i = 0; i < R::TPL; ++i) r.v[i] = ld16_nt(vb + (int64_t)(tl + i * R::TL) * st + dc * R::VEC);
 }
 
 // q fragments of the MFMA path: lane l holds q[head l%16][32ks + 8(l/16) ..+7]
@@ -537,17 +537,26 @@ __device__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D
     sm.den[tid] = den;
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += kThreads) {
+  // every partial this thread needs is requested before any is used
+  constexpr int OPT = (G * D + kThreads - 1) / kThreads;   // outputs per thread
+  float v[OPT][kMaxSplitsDecode];
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    const int i = tid + o * kThreads;
+    const int h = i / D, d = i % D;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplitsDecode; ++sp)
+      v[o][sp] = (i < G * D && sp < ns) ? p.ws_o[(sbase + sp * G + h) * D + d] : 0.f;
+  }
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    const int i = tid + o * kThreads;
+    if (i >= G * D) break;
     const int h = i / D, d = i % D;
     float num = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (s0 + e < ns) ? p.ws_o[(sbase + (s0 + e) * G + h) * D + d] : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (s0 + e < ns) num += sm.wts[s0 + e][h] * v[e];
-    }
+    for (int sp = 0; sp < kMaxSplitsDecode; ++sp)
+      if (sp < ns) num += sm.wts[sp][h] * v[o][sp];
     const float den = sm.den[h];
     p.out[((int64_t)b * Hq + g * G + h) * D + d] = den > 0.f ? num / den : 0.f;
   }
