@@ -287,12 +287,137 @@ def run_decode(args, torch, bskv, wl):
     return result
 
 
+# ---------------------------------------------------------------------------
+# chunked-prefill workload
+# ---------------------------------------------------------------------------
+class PrefillBench:
+    """B x T prefill in chunks: per chunk, pool the chunk's new key blocks,
+    select per 64-token query block (pooled Forecast scores, top-k + union),
+    then block-sparse causal attention (bf16 MFMA)."""
+
+    def __init__(self, wl, torch, bskv, B=None, T=None):
+        from workloads import prefill_inputs
+        self.torch, self.bskv, self.wl = torch, bskv, wl
+        self.dev = torch.device("cuda:0")
+        self.B = B or wl.B
+        self.T = T or wl.T
+        self.C = wl.chunk
+        t0 = time.time()
+        inp = prefill_inputs(wl, self.dev, B=self.B, T=self.T)
+        self.k, self.v = inp["k"], inp["v"]
+        n_chunks = self.T // self.C
+        # each chunk's queries and Forecast vectors come out of that chunk's
+        # projection: contiguous per chunk
+        self.q = [inp["q"][:, :, c * self.C:(c + 1) * self.C].contiguous() for c in range(n_chunks)]
+        self.f = [inp["f"][:, :, c * self.C:(c + 1) * self.C].contiguous() for c in range(n_chunks)]
+        del inp
+        self.n_chunks = n_chunks
+        nb = self.T // wl.block
+        self.kc = torch.empty(self.B, wl.Hkv, nb, wl.d, dtype=torch.float32, device=self.dev)
+        n_qb = self.C // wl.block
+        self.idx = [torch.empty(self.B, wl.Hkv, n_qb, wl.U, dtype=torch.int32, device=self.dev) for _ in range(n_chunks)]
+        self.cnt = [torch.empty(self.B, wl.Hkv, n_qb, dtype=torch.int32, device=self.dev) for _ in range(n_chunks)]
+        self.out = [torch.empty_like(self.q[0]) for _ in range(n_chunks)]
+        self.seq_len = torch.full((self.B,), self.T, dtype=torch.int64, device=self.dev)
+        torch.cuda.synchronize()
+        log(f"[bench] prefill inputs in {time.time() - t0:.1f}s")
+
+    def pool(self, c):
+        nbc = self.C // self.wl.block
+        self.bskv.kv_block_meanpool(self.k, self.seq_len, self.kc, c * nbc, (c + 1) * nbc)
+
+    def select(self, c):
+        wl = self.wl
+        self.bskv.forecast_block_score_topk(self.f[c], self.kc, wl.topk, wl.n_init, wl.n_local, q_start=c * self.C,
+                                            prefill=True, idx=self.idx[c], cnt=self.cnt[c])
+
+    def attend(self, c):
+        self.bskv.block_sparse_attn_prefill(self.q[c], self.k, self.v, self.idx[c], self.cnt[c], c * self.C,
+                                            self.wl.scale, out=self.out[c])
+
+    def step(self):
+        for c in range(self.n_chunks):
+            self.pool(c)
+            self.select(c)
+            self.attend(c)
+
+    def attention_flops(self):
+        """2*d flops for q.k and 2*d for p.v per (query head, token, attended key):
+        a listed block contributes 64 keys to each token of the query block,
+        except the diagonal block, whose token r sees r + 1 of them."""
+        wl = self.wl
+        tot = 0.0
+        for c in range(self.n_chunks):
+            cnt = self.cnt[c].to(self.torch.float64)
+            keys_per_qb = (cnt - 1) * 64 * 64 + 64 * 65 / 2          # summed over the 64 tokens
+            tot += float(keys_per_qb.sum()) * wl.G * 4 * wl.d
+        return tot
+
+
+def run_prefill(args, torch, bskv, wl):
+    bench = PrefillBench(wl, torch, bskv)
+    step_s, _ = time_graph(torch, bench.step, max(1, args.steps // 10), max(1, args.warmup // 5),
+                           use_graph=not args.no_graph)
+    flops = bench.attention_flops()
+    # per-kernel: each kernel over all chunks, graph-replayed, HIP events
+    kt = {}
+    for name, fn in (("kv_block_meanpool", bench.pool), ("score_topk_prefill", bench.select),
+                     ("attn_prefill", bench.attend)):
+        def body():
+            for c in range(bench.n_chunks):
+                fn(c)
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        kt[name] = e0.elapsed_time(e1) * 1e-3 / bench.n_chunks
+        del g
+    B, T, H, d, C = bench.B, bench.T, wl.Hkv, wl.d, bench.C
+    f_bytes = B * H * C * d * 2                                   # Forecast vectors of a chunk (bf16)
+    kc_read = B * H * sum(max(0, qb - wl.n_local + 1 - wl.n_init) for qb in range(T // 64)) * d * 4 / bench.n_chunks
+    per_chunk_flops = flops / bench.n_chunks
+    att_tf = per_chunk_flops / kt["attn_prefill"] / 1e12
+    kernels = {
+        "kv_block_meanpool": {"us": round(kt["kv_block_meanpool"] * 1e6, 2),
+                              "GBps": round(B * H * C * d * 2 / kt["kv_block_meanpool"] / 1e9, 1)},
+        "score_topk_prefill": {"us": round(kt["score_topk_prefill"] * 1e6, 2),
+                               "GBps_forecast_read": round(f_bytes / kt["score_topk_prefill"] / 1e9, 1),
+                               "pooled_key_rows_read_per_chunk_MB": round(kc_read / 1e6, 1)},
+        "attn_prefill": {"us": round(kt["attn_prefill"] * 1e6, 2), "TFLOPs": round(att_tf, 1),
+                         "mfma_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    return {
+        "metric": "prefill tokens/s at B×T (chunked, block-sparse); % bf16 MFMA peak", "value": round(B * T / step_s, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": max(1, args.steps // 10), "warmup": max(1, args.warmup // 5),
+        "ms_per_step": round(step_s * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "chunk": C, "Hq": wl.Hq, "Hkv": H, "head_dim": d,
+                   "block": wl.block, "topk": wl.topk, "n_init": wl.n_init, "n_local": wl.n_local,
+                   "hip_graph": not args.no_graph},
+        "roofline": {"bound": "mfma", "kernel": "attn_prefill", "achieved": round(att_tf, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": per_chunk_flops,
+                     "us_per_launch": round(kt["attn_prefill"] * 1e6, 2)},
+        "attention_tflop_total": round(flops / 1e12, 2),
+        "kernels": kernels,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4", "prefill"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -320,8 +445,11 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
         del a, b
-    wl = CONFIGS[3] if args.workload == "decode" else CONFIGS[2]
-    result = run_decode(args, torch, bskv, wl)
+    if args.workload == "prefill":
+        result = run_prefill(args, torch, bskv, CONFIGS[4])
+    else:
+        wl = CONFIGS[3] if args.workload == "decode" else CONFIGS[2]
+        result = run_decode(args, torch, bskv, wl)
     print(json.dumps(result), flush=True)
 
 

@@ -48,3 +48,42 @@ def test_config3_two_layers_sampled():
             want = orc.attend_decode(np64(lay["q"][b:b + 1]), k, v, idx[b:b + 1].cpu().numpy(),
                                      cnt[b:b + 1].cpu().numpy(), [wl.T], wl.scale, 64)
             assert max_abs(np64(out[b:b + 1]), want) < 2e-2
+
+
+def test_config4_prefill_chunks_sampled():
+    """B4, T=131072, 2048-token chunks, top-64 + 1 + 32 local: selection and
+    attention on sampled (batch, KV head, query block) problems of the first,
+    a middle and the last chunk, at the kernels' full launch size."""
+    import math
+    from workloads import prefill_inputs
+    wl = CONFIGS[4]
+    inp = prefill_inputs(wl, DEV)
+    lens = torch.full((wl.B,), wl.T, dtype=torch.int64, device=DEV)
+    kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
+    bskv.kv_block_meanpool(inp["k"], lens, kc)
+    samples = [(0, 0), (wl.B - 1, wl.Hkv - 1)]
+    kc_or = {s: orc.kv_block_meanpool(np64(inp["k"][s[0]:s[0] + 1, s[1]:s[1] + 1]), 64) for s in samples}
+    kv_or = {s: (np64(inp["k"][s[0]:s[0] + 1, s[1]:s[1] + 1]), np64(inp["v"][s[0]:s[0] + 1, s[1]:s[1] + 1]))
+             for s in samples}
+    for q0 in (0, wl.T // 2, wl.T - wl.chunk):
+        f = inp["f"][:, :, q0:q0 + wl.chunk].contiguous()
+        q = inp["q"][:, :, q0:q0 + wl.chunk].contiguous()
+        idx, cnt = bskv.forecast_block_score_topk(f, kc, wl.topk, wl.n_init, wl.n_local, q_start=q0, prefill=True)
+        out = bskv.block_sparse_attn_prefill(q, inp["k"], inp["v"], idx, cnt, q0, wl.scale)
+        torch.cuda.synchronize()
+        for (b, g) in samples:
+            for qi in (0, 17, 31):
+                fq = np64(f[b:b + 1, g:g + 1, qi * 64:(qi + 1) * 64])
+                sel = orc.prefill_select(fq, kc_or[(b, g)], q0 + qi * 64, wl.topk, wl.n_init, wl.n_local, 64)
+                check_selection(idx[b:b + 1, g:g + 1, qi:qi + 1], cnt[b:b + 1, g:g + 1, qi:qi + 1], sel, wl.topk)
+                # attention of two query heads of this KV head on a few tokens, on the GPU's list
+                k1, v1 = kv_or[(b, g)]
+                gi = idx[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
+                gc = cnt[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
+                for h in (g * wl.G, g * wl.G + wl.G - 1):
+                    qq = np64(q[b:b + 1, h:h + 1, qi * 64:(qi + 1) * 64])
+                    rows = [(0, 0, t) for t in (0, 31, 63)]
+                    want = orc.attend_prefill(qq, k1, v1, gi, gc, q0 + qi * 64, 1.0 / math.sqrt(wl.d), 64, rows=rows)
+                    got = np64(out[b:b + 1, h:h + 1, qi * 64:(qi + 1) * 64])
+                    for r in rows:
+                        assert max_abs(got[r], want[r]) < 2e-2
