@@ -412,12 +412,187 @@ def run_prefill(args, torch, bskv, wl):
     }
 
 
+# ---------------------------------------------------------------------------
+# offloaded lookahead decode workload
+# ---------------------------------------------------------------------------
+class OffloadBench:
+    """Decode with the whole bf16 KV cache in host-pinned memory.  The GPU
+    holds every layer's compressed keys and a 2-slot ring of selected blocks.
+    Layer l: F_l selects layer l+1 (projection + score/top-k on the compute
+    stream), the side stream gathers layer l+1's blocks from the host pool
+    into ring slot (l+1) % 2, and layer l attends from slot l % 2 once its own
+    gather (issued one layer earlier) has completed."""
+
+    def __init__(self, wl, torch, bskv, B=None, T=None, layers=None, host_layers=None):
+        from workloads import decode_inputs
+        self.torch, self.bskv, self.wl = torch, bskv, wl
+        self.dev = torch.device("cuda:0")
+        self.B = B or wl.B
+        self.T = T or wl.T
+        self.L = layers or wl.layers
+        self.HL = host_layers or wl.host_layers
+        t0 = time.time()
+        gen = decode_inputs(wl, self.dev, layers=self.HL, B=self.B, T=self.T)
+        nb = self.T // wl.block
+        self.nb = nb
+        self.kc, self.host_k, self.host_v, self.dk, self.dv = [], [], [], [], []
+        self.x, self.w, self.q, self.seq_len = [], [], [], gen[0]["seq_len"]
+        for lay in gen:
+            kc = torch.empty(self.B, wl.Hkv, nb, wl.d, dtype=torch.float32, device=self.dev)
+            bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)      # built when the cache was written
+            hk = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+            hv = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+            hk.copy_(lay["k"])
+            hv.copy_(lay["v"])
+            self.kc.append(kc)
+            self.host_k.append(hk)
+            self.host_v.append(hv)
+            self.dk.append(bskv.host_device_pointer(hk))
+            self.dv.append(bskv.host_device_pointer(hv))
+            self.x.append(lay["x_sel"])
+            self.w.append(lay["w_sel"])
+            self.q.append(lay["q"])
+            del lay["k"], lay["v"]
+        del gen
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        U, H, d = wl.U, wl.Hkv, wl.d
+        self.ring_k = [torch.empty(self.B, H, U, wl.block, d, dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
+        self.ring_v = [torch.empty_like(self.ring_k[0]) for _ in range(2)]
+        self.f = [torch.empty(self.B, H, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        self.idx = [torch.empty(self.B, H, U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.cnt = [torch.empty(self.B, H, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.out = [torch.empty(self.B, wl.Hq, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=self.dev)  # noqa: E731
+        self.ws_proj = z(bskv.workspace_bytes("proj", self.B, wl.hidden, H, d, 1))
+        self.ws_score = z(bskv.workspace_bytes("score", self.B, H, 0, nb, d))
+        self.ws_attn = z(bskv.workspace_bytes("attn", self.B, wl.Hq, H, d, U))
+        self.copy_stream = torch.cuda.Stream(self.dev)
+        self.ev_sel = [torch.cuda.Event() for _ in range(self.L)]
+        self.ev_pf = [torch.cuda.Event() for _ in range(self.L)]
+        self.ev_att = [torch.cuda.Event() for _ in range(self.L)]
+        self.n_wg = 256
+        torch.cuda.synchronize()
+        log(f"[bench] offload set-up ({self.HL} host layers, {2 * self.HL * hk.numel() * 2 / 2**30:.0f} GiB pinned) "
+            f"in {time.time() - t0:.1f}s")
+
+    def h(self, l):
+        return l % self.HL
+
+    def select(self, l):
+        wl, hl = self.wl, self.h(l)
+        self.bskv.forecast_proj(self.x[hl], self.w[hl], wl.Hkv, wl.d, out=self.f[l], ws=self.ws_proj)
+        self.bskv.forecast_block_score_topk(self.f[l], self.kc[hl], wl.topk, wl.n_init, wl.n_local,
+                                            seq_len=self.seq_len, idx=self.idx[l], cnt=self.cnt[l], ws=self.ws_score)
+
+    def prefetch(self, l, stream=None):
+        hl, slot = self.h(l), l % 2
+        self.bskv.prefetch_selected_blocks(self.host_k[hl], self.host_v[hl], self.idx[l], self.cnt[l],
+                                           self.ring_k[slot], self.ring_v[slot], n_workgroups=self.n_wg,
+                                           stream=stream, src_k_dev=self.dk[hl], src_v_dev=self.dv[hl])
+
+    def attend(self, l):
+        hl, slot = self.h(l), l % 2
+        self.bskv.block_sparse_attn_decode(self.q[hl], self.ring_k[slot], self.ring_v[slot], self.idx[l],
+                                           self.cnt[l], self.seq_len, self.wl.scale, ring=True, out=self.out[l],
+                                           ws=self.ws_attn)
+
+    def step(self, with_copy=True):
+        torch = self.torch
+        comp = torch.cuda.current_stream(self.dev)
+        cs = self.copy_stream
+        self.select(0)
+        if with_copy:
+            self.ev_sel[0].record(comp)
+            cs.wait_event(self.ev_sel[0])
+            self.prefetch(0, stream=cs)
+            self.ev_pf[0].record(cs)
+        for l in range(self.L):
+            if l + 1 < self.L:
+                self.select(l + 1)                     # F_l picks layer l+1's blocks ...
+                if with_copy:
+                    self.ev_sel[l + 1].record(comp)
+                    cs.wait_event(self.ev_sel[l + 1])
+                    if l >= 1:
+                        cs.wait_event(self.ev_att[l - 1])   # ring slot (l+1)%2 was read by layer l-1
+                    self.prefetch(l + 1, stream=cs)    # ... and their copy starts now
+                    self.ev_pf[l + 1].record(cs)
+            if with_copy:
+                comp.wait_event(self.ev_pf[l])         # layer l's blocks (copied one layer ago)
+            self.attend(l)
+            self.ev_att[l].record(comp)
+
+    def copy_only(self):
+        for l in range(self.L):
+            self.prefetch(l)
+
+
+def run_offload(args, torch, bskv, wl):
+    bench = OffloadBench(wl, torch, bskv)
+    # the pages tune the copy kernel's thread-block count to the batch: pick it here
+    bench.step(with_copy=False)
+    torch.cuda.synchronize()
+    sweep = {}
+    for nwg in (64, 128, 256, 512, 1024):
+        bench.n_wg = nwg
+        bench.prefetch(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(4):
+            bench.prefetch(l)
+        torch.cuda.synchronize()
+        sweep[nwg] = (time.perf_counter() - t0) / 4
+    bench.n_wg = min(sweep, key=sweep.get)
+    log(f"[bench] prefetch workgroups sweep (s per layer): {sweep} -> {bench.n_wg}")
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    # the host link itself: one contiguous pinned -> device copy (DMA engine)
+    src = bench.host_k[0].view(-1)[: 1 << 29]
+    dst = torch.empty(src.shape, dtype=src.dtype, device=bench.dev)
+    t_h2d = timed(lambda: dst.copy_(src, non_blocking=True), 3)
+    h2d_gbps = src.numel() * 2 / t_h2d / 1e9
+    del dst
+    n = max(1, args.steps // 25)
+    t_total = timed(bench.step, n)
+    t_compute = timed(lambda: bench.step(with_copy=False), n)
+    t_copy = timed(bench.copy_only, n)
+    hidden = max(0.0, min(1.0, (t_compute + t_copy - t_total) / t_copy))
+    U, H, d = wl.U, wl.Hkv, wl.d
+    cnt_total = sum(int(c.sum()) for c in bench.cnt)
+    copy_bytes = cnt_total * wl.block * d * 2 * 2
+    return {
+        "metric": "offloaded lookahead decode tokens/s at B×T (KV in host-pinned memory); % copy hidden",
+        "value": round(bench.B / t_total, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": 1,
+        "ms_per_step": round(t_total * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": bench.B, "T": bench.T, "layers": bench.L, "host_layers": bench.HL,
+                   "Hq": wl.Hq, "Hkv": H, "head_dim": d, "topk": wl.topk, "n_init": wl.n_init,
+                   "n_local": wl.n_local, "prefetch_workgroups": bench.n_wg},
+        "roofline": {"bound": "host-link", "kernel": "prefetch_selected_blocks",
+                     "achieved": round(copy_bytes / t_copy / 1e9, 2), "peak": 64.0, "unit": "GB/s",
+                     "frac": round(copy_bytes / t_copy / 1e9 / 64.0, 4), "traffic": None,
+                     "bytes_per_step": copy_bytes},
+        "copy_hidden_frac": round(hidden, 4),
+        "h2d_memcpy_GBps": round(h2d_gbps, 2),
+        "ms_compute_only": round(t_compute * 1e3, 3), "ms_copy_only": round(t_copy * 1e3, 3),
+        "prefetch_sweep_ms_per_layer": {str(k): round(v * 1e3, 3) for k, v in sweep.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4", "prefill"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4", "prefill", "offload"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -447,6 +622,8 @@ def main():
         del a, b
     if args.workload == "prefill":
         result = run_prefill(args, torch, bskv, CONFIGS[4])
+    elif args.workload == "offload":
+        result = run_offload(args, torch, bskv, CONFIGS[5])
     else:
         wl = CONFIGS[3] if args.workload == "decode" else CONFIGS[2]
         result = run_decode(args, torch, bskv, wl)

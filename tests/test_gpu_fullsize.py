@@ -87,3 +87,47 @@ def test_config4_prefill_chunks_sampled():
                     got = np64(out[b:b + 1, h:h + 1, qi * 64:(qi + 1) * 64])
                     for r in rows:
                         assert max_abs(got[r], want[r]) < 2e-2
+
+
+def test_config5_offload_sampled():
+    """B16, T=131072 with the KV cache in host-pinned memory: the layer-0
+    projection selects layer 0, its blocks are gathered from the host pool
+    into the ring on a side stream, and attention reads the ring.  Checked on
+    sampled batch elements against the oracle and bytewise against the host."""
+    wl = CONFIGS[5]
+    lay = decode_inputs(wl, DEV, layers=1)[0]
+    kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
+    bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
+    hk = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hk.copy_(lay["k"])
+    hv.copy_(lay["v"])
+    q = lay["q"]
+    del lay["k"], lay["v"]
+    f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    idx, cnt = bskv.forecast_block_score_topk(f, kc, wl.topk, wl.n_init, wl.n_local, seq_len=lay["seq_len"])
+    ring_k = torch.empty(wl.B, wl.Hkv, wl.U, 64, wl.d, dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.empty_like(ring_k)
+    side = torch.cuda.Stream(DEV)
+    sel_done = torch.cuda.Event()
+    sel_done.record()
+    side.wait_event(sel_done)
+    bskv.prefetch_selected_blocks(hk, hv, idx, cnt, ring_k, ring_v, n_workgroups=256, stream=side)
+    copied = torch.cuda.Event()
+    copied.record(side)
+    torch.cuda.current_stream().wait_event(copied)
+    out = bskv.block_sparse_attn_decode(q, ring_k, ring_v, idx, cnt, lay["seq_len"], wl.scale, ring=True)
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        k = hk[b:b + 1].to(torch.float64).numpy()
+        v = hv[b:b + 1].to(torch.float64).numpy()
+        fo = orc.forecast_proj(np64(lay["x_sel"][b:b + 1]), np64(lay["w_sel"]), wl.Hkv, wl.d)
+        sel = orc.decode_select(fo, orc.kv_block_meanpool(k, 64), [wl.T], wl.topk, wl.n_init, wl.n_local, 64)
+        assert check_selection(idx[b:b + 1], cnt[b:b + 1], sel, wl.topk) == 0
+        gi, gc = idx[b:b + 1].cpu().numpy(), cnt[b:b + 1].cpu().numpy()
+        ring = orc.gather_selected_blocks(hk[b:b + 1].view(torch.int16).numpy(), gi, gc, 64)
+        got = ring_k[b:b + 1].view(torch.int16).cpu().numpy()
+        for g in range(wl.Hkv):
+            assert np.array_equal(got[0, g, :gc[0, g]], ring[0, g, :gc[0, g]])
+        want = orc.attend_decode(np64(q[b:b + 1]), k, v, gi, gc, [wl.T], wl.scale, 64)
+        assert max_abs(np64(out[b:b + 1]), want) < 2e-2
