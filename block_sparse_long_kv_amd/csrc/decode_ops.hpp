@@ -418,7 +418,9 @@ __device__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, Attn
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int c = min(p.cnt[bg], p.U);
   const int u0 = split * p.bps, u1 = min(c, u0 + p.bps);
-  const int64_t L = min(p.seq_len[b], p.kv_len);
+  // tokens of the sequence; a ring holds only the listed blocks, so its
+  // length bounds ring positions, not the sequence
+  const int64_t L = p.ring ? p.seq_len[b] : min(p.seq_len[b], p.kv_len);
   const T* q = (const T*)p.q;
   QFrag<D> qf;
   if constexpr (R::kMfma) {

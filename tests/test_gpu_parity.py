@@ -308,9 +308,14 @@ def test_chunked_prefill_matches_single_chunk():
 
 # ----------------------------------------------------------------------------- a5
 def test_prefetch_from_pinned_host_and_ring_attention():
+    """The ring holds U blocks, far fewer than the sequence has: blocks whose id
+    lies past the ring's length must still be attended (ring position u holds
+    list entry u).  Ragged lengths, one with a partial newest block."""
     wl = CONFIGS[5]
-    B, T = 3, 64 * 50
+    B, T = 3, 64 * 200
     lay = decode_inputs(wl, DEV, layers=1, B=B, T=T)[0]
+    lay["seq_len"] = torch.tensor([T, T - 64 * 37 - 5, 64 * 90], dtype=torch.int64, device=DEV)
+    assert wl.U * 64 < T - 64 * 40
     kc = _kc_gpu(lay["k"], lay["seq_len"])
     f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
     idx, cnt = bskv.forecast_block_score_topk(f, kc, wl.topk, wl.n_init, wl.n_local, seq_len=lay["seq_len"])
@@ -339,6 +344,11 @@ def test_prefetch_from_pinned_host_and_ring_attention():
         for g in range(wl.Hkv):
             assert np.array_equal(got[b, g, :cn[b, g]], want[b, g, :cn[b, g]])
     assert torch.equal(out_ring, out_res), "ring read must equal resident read bit for bit"
+    gi = idx.cpu().numpy()
+    lens = lay["seq_len"].cpu().numpy()
+    assert (gi[cn > 0] >= wl.U).any(), "some selected block must lie past the ring's length"
+    want_o = orc.attend_decode(np64(lay["q"]), np64(lay["k"]), np64(lay["v"]), gi, cn, lens, wl.scale, 64)
+    assert max_abs(np64(out_ring), want_o) < 2e-2
 
 
 # ----------------------------------------------------------------------------- fused decode layer
