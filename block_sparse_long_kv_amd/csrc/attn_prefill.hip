@@ -12,11 +12,16 @@
 //     the accumulator layout then gives each lane one query column, so the
 //     online-softmax statistics and the probabilities stay in the lane that
 //     owns them, and P^T feeds O^T = V^T P^T as the B operand directly.
-//   * K is staged row-major in LDS (rows padded by 16 bytes: conflict-free
-//     16-byte reads); V is staged transposed (d-major, padded) so the V^T
-//     operand is two 8-byte reads per lane.
-//   * The next block's K/V are loaded into registers while the current one
-//     is computed (one-deep software pipeline).
+//   * K and V are staged row-major in LDS with 16-byte writes (rows padded);
+//     the V^T operand is read with gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16), two per operand.
+//   * Two LDS stages and a register prefetch: while block u is computed from
+//     LDS stage u%2, block u+1 (already in registers) is written to the other
+//     stage and block u+2 is requested from memory; one barrier per block.
+//   * Softmax VALU kept to the minimum (it is the other half of the work at
+//     head_dim 128): raw v_exp_f32, the scale folded into one FMA, the causal
+//     mask only on the diagonal block, a finite initial running max instead
+//     of -inf guards, and the output rescaled only when some row max moved.
 //   * Workgroups are ordered so that consecutive query blocks of one KV head
 //     run on the same XCD: neighbouring query blocks share most of their
 //     local-window blocks, which then hit in that XCD's L2.
@@ -27,25 +32,29 @@ namespace bskv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
 
 template <int D, int G>
 __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
     const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,
-    int64_t sg, int64_t st, int64_t kv_len, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int64_t q_start,
-    int Tq, int Hkv, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
+    int64_t sg, int64_t st, int64_t kv_len, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    int64_t q_start, int Tq, int Hkv, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
   constexpr int BLK = 64;
   constexpr int NT = G * 128;          // threads
   constexpr int KSTR = D + 8;          // LDS row of K: D bf16 + 16 bytes
-  constexpr int VSTR = BLK + 4;        // LDS row of V^T: 64 bf16 + 8 bytes
+  constexpr int VSTR = D + 16;         // LDS row of V: D bf16 + 32 bytes (transposing reads hit distinct banks)
   constexpr int RCH = D / 8;           // 16-byte chunks per token row
   constexpr int NCH = BLK * RCH;       // 16-byte chunks per block per tensor
   constexpr int CPT = (NCH + NT - 1) / NT;  // chunks per thread per tensor
   constexpr int KS = D / 32;           // k-steps of S^T
   constexpr int MD = D / 16;           // d tiles of O^T
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_bits Vt[D * VSTR];
+  // two LDS stages: block u+1 is written while block u is read
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[2][BLK * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_bits Vs[2][BLK * VSTR];
 
   const int n_tiles = gridDim.x;
   int lin = blockIdx.x;
@@ -79,7 +88,9 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) o[md][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // running max (base-2, scaled) starts finite: a fully masked block then
+  // gives p = 0 and alpha = 1 without special cases
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
 
   const int64_t prob = (int64_t)bg * n_qb + qi;
   const int c = min(cnt[prob], U);
@@ -94,35 +105,41 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   for (int i = 0; i < CPT; ++i) kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
   auto gload = [&](int jj) {
     if (!valid(jj)) return;
+    const bf16_bits* kq = kb + (int64_t)jj * BLK * st;
+    const bf16_bits* vq = vb + (int64_t)jj * BLK * st;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
       if (NCH % NT == 0 || ch < NCH) {
-        const int64_t off = ((int64_t)jj * BLK + r) * st + cc * 8;
-        kreg[i] = ld16(kb + off);
-        vreg[i] = ld16(vb + off);
+        kreg[i] = ld16(kq + (int64_t)r * st + cc * 8);
+        vreg[i] = ld16(vq + (int64_t)r * st + cc * 8);
       }
     }
   };
-  if (c > 0) gload(list[0]);
-
-  for (int u = 0; u < c; ++u) {
-    const int j = list[u];
-    __syncthreads();  // all waves are done reading the previous block
+  auto lstore = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
       if (NCH % NT != 0 && ch >= NCH) continue;
-      *reinterpret_cast<uint4*>(&Ks[r * KSTR + cc * 8]) = kreg[i];
-      const uint32_t w4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(cc * 8 + 2 * e) * VSTR + r] = (bf16_bits)(w4[e] & 0xffffu);
-        Vt[(cc * 8 + 2 * e + 1) * VSTR + r] = (bf16_bits)(w4[e] >> 16);
-      }
+      *reinterpret_cast<uint4*>(&Ks[stage][r * KSTR + cc * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&Vs[stage][r * VSTR + cc * 8]) = vreg[i];
     }
-    __syncthreads();
-    if (u + 1 < c) gload(list[u + 1]);
+  };
+  if (c > 0) {
+    gload(list[0]);
+    lstore(0);
+    if (c > 1) gload(list[1]);
+  }
+  __syncthreads();
+
+  for (int u = 0; u < c; ++u) {
+    const int j = list[u];
+    const int stage = u & 1;
+    // stage the next block into the other LDS buffer, then prefetch the one after
+    if (u + 1 < c) {
+      lstore(stage ^ 1);
+      if (u + 2 < c) gload(list[u + 2]);
+    }
 
     // S^T tiles: keys 16*mt .. (M), queries row0 + 16*nq .. (N)
     f32x4_t s[4][2];
@@ -134,40 +151,47 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
+        const bf16x8_t a =
+            as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[stage][(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq) s[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][ks], s[mt][nq], 0, 0, 0);
       }
     }
 
+    // causal mask: only the diagonal block (uniform over the workgroup);
+    // a listed block outside the buffers is masked whole
+    if (j >= qb || !valid(j)) {
+      const bool ok = valid(j);
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        const int rq = row0 + 16 * nq + l16;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!ok || 16 * mt + 4 * lg + i > rq) s[mt][nq][i] = -INFINITY;
+      }
+    }
+
     // online softmax per query column (lane-local, 2 xor-shuffles per reduction)
-    const bool diag = (j == qb);
-    const bool ok = valid(j);
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
-      const int rq = row0 + 16 * nq + l16;
-      float mx = -INFINITY;
+      float mx = s[0][nq][0];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * mt + 4 * lg + i;
-          float x = s[mt][nq][i] * qscale;
-          if ((diag && key > rq) || !ok) x = -INFINITY;
-          s[mt][nq][i] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nq][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m_run[nq], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m_run[nq] - mn);
+      const float mn = fmaxf(m_run[nq], mx * qscale);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nq] - mn);
       float sum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (mn == -INFINITY) ? 0.f : exp2f(s[mt][nq][i] - mn);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nq][i], qscale, -mn));
           s[mt][nq][i] = p;
           sum += p;
         }
@@ -175,8 +199,11 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
       sum += __shfl_xor(sum, 32);
       l_run[nq] = l_run[nq] * alpha + sum;
       m_run[nq] = mn;
+      // rescale the output only when some row's max moved (rare after the first blocks)
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int md = 0; md < MD; ++md) o[md][nq] *= alpha;
+        for (int md = 0; md < MD; ++md) o[md][nq] *= alpha;
+      }
       // P^T operand for key step s2: slots 0..3 <- tile 2*s2, slots 4..7 <- tile 2*s2+1
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -190,19 +217,24 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
       }
     }
 
-    // O^T += V^T P^T; V^T rows d = 16*md + l16, keys 32*s2 + 4*lg + {0..3} and 32*s2 + 16 + 4*lg + {0..3}
+    // O^T += V^T P^T.  The V^T operand (lane: d = 16*md + l16, keys 32*s2 + 4*lg + {0..3}
+    // and 32*s2 + 16 + 4*lg + {0..3}) comes from row-major V with transposing LDS reads:
+    // within each 16-lane group, lane 4r+c reads key row r, columns 4c..4c+3, and
+    // ds_read_b64_tr_b16 hands lane i element i%4 of lane 4r+i/4 for r = 0..3.
+    const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const bf16_bits* vrow = &Vt[(16 * md + l16) * VSTR + 32 * s2 + 4 * lg];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16_bits* v0 = &Vs[stage][(32 * s2 + tr_row) * VSTR + 16 * md + tr_col];
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * VSTR));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq) o[md][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[s2][nq], o[md][nq], 0, 0, 0);
       }
     }
+    __syncthreads();   // stage^1 is complete for everyone; stage may be overwritten next
   }
 
   // epilogue: O[query][d] = O^T[d][query] / l
