@@ -166,7 +166,8 @@ int bskv_block_sparse_attn_prefill(const void* q, const void* k, const void* v, 
   if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
   if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
-  const int64_t n_tiles = (int64_t)((n_q_tokens + 63) / 64) * B * n_kv_heads;
+  // one workgroup per (query block, KV head, group of up to four query heads)
+  const int64_t n_tiles = (int64_t)((n_q_tokens + 63) / 64) * B * n_kv_heads * ((n_q_heads / n_kv_heads + 3) / 4);
   if (n_tiles > 0x7fffffff) return BSKV_EUNSUPPORTED;
   bskv::AttnPrefillArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, idx, cnt, q_start, n_q_tokens,
                           B, n_q_heads, n_kv_heads, head_dim, block, U, scale, out, stream};

@@ -5,23 +5,31 @@
 // of the chunk's queries over the K/V of each query block's selected blocks).
 //
 // Design (gfx950, v_mfma_f32_16x16x32_bf16):
-//   * One workgroup per (query block of 64 tokens, KV head): 2G wavefronts,
-//     wave w serves query head g*G + w/2, rows (w%2)*32 .. +31, so the G
-//     query heads of a KV head share every K/V block staged in LDS.
+//   * One workgroup per (query block of 64 tokens, KV head, group of up to 4
+//     query heads): for HPW heads it runs 2*HPW wavefronts, each serving 32
+//     query rows of one head, so those heads share every K/V block staged in
+//     LDS.
 //   * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M side):
 //     the accumulator layout then gives each lane one query column, so the
 //     online-softmax statistics and the probabilities stay in the lane that
 //     owns them, and P^T feeds O^T = V^T P^T as the B operand directly.
-//   * K and V are staged row-major in LDS with 16-byte writes (rows padded);
-//     the V^T operand is read with gfx950's transposing LDS read
-//     (ds_read_b64_tr_b16), two per operand.
-//   * Two LDS stages and a register prefetch: while block u is computed from
-//     LDS stage u%2, block u+1 (already in registers) is written to the other
-//     stage and block u+2 is requested from memory; one barrier per block.
-//   * Softmax VALU kept to the minimum (it is the other half of the work at
-//     head_dim 128): raw v_exp_f32, the scale folded into one FMA, the causal
-//     mask only on the diagonal block, a finite initial running max instead
-//     of -inf guards, and the output rescaled only when some row max moved.
+//   * Ping-pong between two wave groups.  Group A (rows 0..31 of every head)
+//     and group B (rows 32..63) run the same schedule one slot apart: in a
+//     slot a wave either issues MFMAs (S for block a and O += V^T P for block
+//     a-1) or runs the softmax of block a.  Waves w and w+HPW share a SIMD, so
+//     each SIMD always has one wave on the matrix cores while the other keeps
+//     the VALU busy; one barrier closes each slot.
+//   * K and V live in two LDS stages each, staged with 16-byte writes (rows
+//     padded); K runs one block ahead of V.  The V^T operand is read with
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16), two per operand.
+//     Global loads for the next blocks are issued two slots before use.
+//   * Online softmax with a lazy maximum: the running maximum only moves when
+//     a row's block maximum exceeds it by more than 8 (base-2 units), so the
+//     output is rarely rescaled; probabilities stay below 2^8, which fp32
+//     accumulation and bf16 operands carry without loss of relative accuracy.
+//     The test runs on each lane's own maximum, so the common case needs no
+//     cross-lane traffic; row sums are kept per lane and reduced once at the
+//     end.
 //   * Workgroups are ordered so that consecutive query blocks of one KV head
 //     run on the same XCD: neighbouring query blocks share most of their
 //     local-window blocks, which then hit in that XCD's L2.
@@ -38,13 +46,13 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
 
-template <int D, int G>
-__global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
+template <int D, int HPW>
+__global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
     const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,
     int64_t sg, int64_t st, int64_t kv_len, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    int64_t q_start, int Tq, int Hkv, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
+    int64_t q_start, int Tq, int Hkv, int G, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
   constexpr int BLK = 64;
-  constexpr int NT = G * 128;          // threads
+  constexpr int NT = HPW * 128;        // threads: 2*HPW waves
   constexpr int KSTR = D + 8;          // LDS row of K: D bf16 + 16 bytes
   constexpr int VSTR = D + 16;         // LDS row of V: D bf16 + 32 bytes (transposing reads hit distinct banks)
   constexpr int RCH = D / 8;           // 16-byte chunks per token row
@@ -52,19 +60,24 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   constexpr int CPT = (NCH + NT - 1) / NT;  // chunks per thread per tensor
   constexpr int KS = D / 32;           // k-steps of S^T
   constexpr int MD = D / 16;           // d tiles of O^T
-  // two LDS stages: block u+1 is written while block u is read
+  constexpr float TAU = 8.f;           // lazy-maximum threshold (base 2)
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[2][BLK * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_bits Vs[2][BLK * VSTR];
 
   const int n_tiles = gridDim.x;
   int lin = blockIdx.x;
   if ((n_tiles & 7) == 0) lin = (lin & 7) * (n_tiles >> 3) + (lin >> 3);
-  const int qi = lin % n_qb, bg = lin / n_qb;
+  const int n_hs = G / HPW;
+  const int qi = lin % n_qb, rest = lin / n_qb;
+  const int hs = rest % n_hs, bg = rest / n_hs;
   const int b = bg / Hkv, g = bg % Hkv;
   const int Hq = Hkv * G;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int h = g * G + (wid >> 1);
-  const int row0 = (wid & 1) * 32;
+  // the wave index is made wave-uniform for the compiler, so that every
+  // slot branch below is scalar and the block list is read with scalar loads
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid / HPW;           // 0: group A, 1: group B (one slot later)
+  const int h = g * G + hs * HPW + wid % HPW;
+  const int row0 = grp * 32;
   const int l16 = lane & 15, lg = lane >> 4;
   const int qb = (int)(q_start / BLK) + qi;
   const int tq0 = qi * BLK;
@@ -88,13 +101,27 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) o[md][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t s[4][2];
+  bf16x8_t pb[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) s[mt][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) pb[s2][nq] = as_bf16x8(make_uint4(0, 0, 0, 0));
   // running max (base-2, scaled) starts finite: a fully masked block then
-  // gives p = 0 and alpha = 1 without special cases
-  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
+  // gives p = 0 without special cases; the row sum is a per-lane partial
+  float m_run[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
 
   const int64_t prob = (int64_t)bg * n_qb + qi;
   const int c = min(cnt[prob], U);
-  const int32_t* list = idx + prob * U;
+  // the block list is read through the constant address space: uniform
+  // indices then give scalar loads, which do not wait behind the K/V loads
+  // in flight (vector loads complete in order)
+  const __attribute__((address_space(4))) int32_t* list =
+      (const __attribute__((address_space(4))) int32_t*)(idx + prob * U);
   const bf16_bits* kb = k + b * sb + g * sg;
   const bf16_bits* vb = v + b * sb + g * sg;
 
@@ -103,61 +130,72 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   uint4 kreg[CPT], vreg[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int jj) {
+  auto gload = [&](uint4 (&reg)[CPT], const bf16_bits* base, int jj) {
     if (!valid(jj)) return;
-    const bf16_bits* kq = kb + (int64_t)jj * BLK * st;
-    const bf16_bits* vq = vb + (int64_t)jj * BLK * st;
+    const bf16_bits* p0 = base + (int64_t)jj * BLK * st;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
-      if (NCH % NT == 0 || ch < NCH) {
-        kreg[i] = ld16(kq + (int64_t)r * st + cc * 8);
-        vreg[i] = ld16(vq + (int64_t)r * st + cc * 8);
-      }
+      if (NCH % NT == 0 || ch < NCH) reg[i] = ld16(p0 + (int64_t)r * st + cc * 8);
     }
   };
-  auto lstore = [&](int stage) {
+  auto lstore = [&](bf16_bits* dst, int stride, const uint4 (&reg)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
       if (NCH % NT != 0 && ch >= NCH) continue;
-      *reinterpret_cast<uint4*>(&Ks[stage][r * KSTR + cc * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&Vs[stage][r * VSTR + cc * 8]) = vreg[i];
+      *reinterpret_cast<uint4*>(&dst[r * stride + cc * 8]) = reg[i];
     }
   };
-  if (c > 0) {
-    gload(list[0]);
-    lstore(0);
-    if (c > 1) gload(list[1]);
-  }
-  __syncthreads();
 
-  for (int u = 0; u < c; ++u) {
-    const int j = list[u];
-    const int stage = u & 1;
-    // stage the next block into the other LDS buffer, then prefetch the one after
-    if (u + 1 < c) {
-      lstore(stage ^ 1);
-      if (u + 2 < c) gload(list[u + 2]);
-    }
-
-    // S^T tiles: keys 16*mt .. (M), queries row0 + 16*nq .. (N)
-    f32x4_t s[4][2];
+  // MFMA slot: S^T = K(a) Q^T (a < c) and O^T += V(a-1)^T P(a-1)^T (a >= 1)
+  auto mfma_slot = [&](int a) {
+    if (a < c) {
+      const bf16_bits* kst = Ks[a & 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) s[mt][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nq = 0; nq < 2; ++nq) s[mt][nq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t a =
-            as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[stage][(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8_t a_op =
+              as_bf16x8(*reinterpret_cast<const uint4*>(&kst[(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
 #pragma unroll
-        for (int nq = 0; nq < 2; ++nq) s[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][ks], s[mt][nq], 0, 0, 0);
+          for (int nq = 0; nq < 2; ++nq)
+            s[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, qf[nq][ks], s[mt][nq], 0, 0, 0);
+        }
       }
     }
+    if (a >= 1) {
+      // The V^T operand (lane: d = 16*md + l16, keys 32*s2 + 4*lg + {0..3} and
+      // 32*s2 + 16 + 4*lg + {0..3}) comes from row-major V with transposing LDS
+      // reads: within each 16-lane group, lane 4r+c reads key row r, columns
+      // 4c..4c+3, and ds_read_b64_tr_b16 hands lane i element i%4 of lane
+      // 4r+i/4 for r = 0..3.
+      const bf16_bits* vst = Vs[(a - 1) & 1];
+      const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const bf16_bits* v0 = &vst[(32 * s2 + tr_row) * VSTR + 16 * md + tr_col];
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * VSTR));
+          const bf16x8_t a_op =
+              __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq)
+            o[md][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, pb[s2][nq], o[md][nq], 0, 0, 0);
+        }
+      }
+    }
+  };
 
+  // softmax slot of block a: S -> P (bf16 operand), running max and sum
+  auto softmax_slot = [&](int a) {
+    const int j = list[a];
     // causal mask: only the diagonal block (uniform over the workgroup);
     // a listed block outside the buffers is masked whole
     if (j >= qb || !valid(j)) {
@@ -172,9 +210,6 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
             if (!ok || 16 * mt + 4 * lg + i > rq) s[mt][nq][i] = -INFINITY;
       }
     }
-
-    // online softmax per query column (lane-local, 2 xor-shuffles per reduction)
-    bf16x8_t pb[2][2];
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
       float mx = s[0][nq][0];
@@ -182,10 +217,22 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nq][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m_run[nq], mx * qscale);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nq] - mn);
+      // The lane-local maximum decides whether the running maximum must move:
+      // usually no lane exceeds it by more than TAU and nothing crosses lanes.
+      // Otherwise the four lanes of each query column agree on the column
+      // maximum and the columns that moved rescale their output and sum.
+      if (__any(mx * qscale > m_run[nq] + TAU)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * qscale;
+        const bool up = ms > m_run[nq] + TAU;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[nq] - ms) : 1.f;
+        m_run[nq] = up ? ms : m_run[nq];
+        l_part[nq] *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[md][nq] *= alpha;
+      }
+      const float mn = m_run[nq];
       float sum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -195,15 +242,7 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
           s[mt][nq][i] = p;
           sum += p;
         }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      l_run[nq] = l_run[nq] * alpha + sum;
-      m_run[nq] = mn;
-      // rescale the output only when some row's max moved (rare after the first blocks)
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md][nq] *= alpha;
-      }
+      l_part[nq] += sum;
       // P^T operand for key step s2: slots 0..3 <- tile 2*s2, slots 4..7 <- tile 2*s2+1
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -216,33 +255,61 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
         pb[s2][nq] = p8;
       }
     }
+  };
 
-    // O^T += V^T P^T.  The V^T operand (lane: d = 16*md + l16, keys 32*s2 + 4*lg + {0..3}
-    // and 32*s2 + 16 + 4*lg + {0..3}) comes from row-major V with transposing LDS reads:
-    // within each 16-lane group, lane 4r+c reads key row r, columns 4c..4c+3, and
-    // ds_read_b64_tr_b16 hands lane i element i%4 of lane 4r+i/4 for r = 0..3.
-    const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const bf16_bits* v0 = &Vs[stage][(32 * s2 + tr_row) * VSTR + 16 * md + tr_col];
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * VSTR));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int nq = 0; nq < 2; ++nq) o[md][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[s2][nq], o[md][nq], 0, 0, 0);
-      }
-    }
-    __syncthreads();   // stage^1 is complete for everyone; stage may be overwritten next
+  // prologue: K(0) staged; K(1) and V(0) requested.  The explicit wait
+  // (vmcnt 0) tells the compiler that the Q fragments have arrived on every
+  // path, so no wait for them lands inside the slot loop, where it would
+  // also wait for the K/V requests in flight.
+  if (c > 0) {
+    gload(kreg, kb, list[0]);
+    lstore(Ks[0], KSTR, kreg);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (c > 1) gload(kreg, kb, list[1]);
+  if (c > 0) gload(vreg, vb, list[0]);
+  __syncthreads();
+
+  // Slots: group A runs M(0) S(0) M(1) S(1) ... S(c-1) M(c) in slots 0..2c,
+  // group B the same sequence in slots 1..2c+1, where M(a) is the MFMA slot
+  // of block a and S(a) its softmax slot; one barrier closes each slot.  K(u)
+  // is read in slots 2u and 2u+1, V(u) in slots 2u+2 and 2u+3.  Odd slot
+  // 2u-1 (after S(u-1) in group A, after M(u-1) in group B) stages K(u) and
+  // V(u-1) into LDS stages whose previous blocks were last read in slot 2u-3,
+  // and requests K(u+1) and V(u).
+  // The stores are unconditional: for u >= c (K) or u > c (V) they fill a
+  // stage that is not read again, and keeping them branch-free lets the
+  // compiler see that the previous loads into kreg/vreg have completed, so
+  // the new requests do not wait for anything.
+  auto stage = [&](int u) {
+    lstore(Ks[u & 1], KSTR, kreg);
+    lstore(Vs[(u - 1) & 1], VSTR, vreg);
+    if (u + 1 < c) gload(kreg, kb, list[u + 1]);
+    if (u < c) gload(vreg, vb, list[u]);
+  };
+  if (grp == 1) __syncthreads();            // slot 0: group B idle
+  for (int a = 0;; ++a) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_slot(a);
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) stage(a + 1);
+    __syncthreads();
+    if (a == c) break;
+    softmax_slot(a);
+    if (grp == 0) stage(a + 1);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();            // slot 2c+1: group A idle
 
   // epilogue: O[query][d] = O^T[d][query] / l
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq) {
+    float l = l_part[nq];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
     const int t = tq0 + row0 + 16 * nq + l16;
     if (t < Tq) {
-      const float inv = l_run[nq] > 0.f ? 1.f / l_run[nq] : 0.f;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
       bf16_bits* op = out + (((int64_t)b * Hq + h) * Tq + t) * D + 4 * lg;
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
@@ -254,14 +321,15 @@ __global__ __launch_bounds__(G * 128) void attn_prefill_kernel(
   }
 }
 
-template <int D, int G>
+template <int D, int HPW>
 static void launch_prefill_t(const AttnPrefillArgs& a) {
+  const int G = a.Hq / a.Hkv;
   const int n_qb = (a.Tq + 63) / 64;
-  const int n_tiles = n_qb * a.B * a.Hkv;
+  const int n_tiles = n_qb * a.B * a.Hkv * (G / HPW);
   const float qscale = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_prefill_kernel<D, G>), dim3(n_tiles), dim3(G * 128), 0, a.stream, (const bf16_bits*)a.q,
+  hipLaunchKernelGGL((attn_prefill_kernel<D, HPW>), dim3(n_tiles), dim3(HPW * 128), 0, a.stream, (const bf16_bits*)a.q,
                      (const bf16_bits*)a.k, (const bf16_bits*)a.v, a.sb, a.sg, a.st, a.kv_len, a.idx, a.cnt, a.q_start, a.Tq,
-                     a.Hkv, a.U, n_qb, qscale, (bf16_bits*)a.out);
+                     a.Hkv, G, a.U, n_qb, qscale, (bf16_bits*)a.out);
 }
 
 template <int D>
@@ -269,8 +337,7 @@ static void launch_prefill_d(const AttnPrefillArgs& a, int G) {
   switch (G) {
     case 1: launch_prefill_t<D, 1>(a); break;
     case 2: launch_prefill_t<D, 2>(a); break;
-    case 4: launch_prefill_t<D, 4>(a); break;
-    default: launch_prefill_t<D, 8>(a); break;
+    default: launch_prefill_t<D, 4>(a); break;   // G = 4 or 8: four query heads per workgroup
   }
 }
 

@@ -280,6 +280,31 @@ def test_prefill_attention_on_oracle_lists(d, G, q_start, Tq):
     assert err < 2e-2, err
 
 
+@pytest.mark.parametrize("d,G", [(128, 4), (128, 8), (64, 2)])
+def test_prefill_attention_wide_score_range(d, G):
+    """Queries scaled up so that scaled scores span tens of units in base 2
+    and each row's maximum keeps growing along its block list: the running
+    maximum moves many times (also mid-list), and long lists (24 blocks)
+    cover many ping-pong slots."""
+    Hkv, T, q_start, Tq = 1, 4096, 2048, 1024
+    c, q_chunk, _, _, sel = _prefill_case(61, 1, Hkv * G, Hkv, d, T, q_start, Tq, topk=16, n_local=8)
+    ramp = torch.linspace(0.5, 6.0, Tq, device=DEV).view(1, 1, Tq, 1)
+    q_chunk = (q_chunk.float() * ramp * 3.0).to(torch.bfloat16).contiguous()
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    assert int(cnt.max()) == 25
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, q_start)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = [(0, h, t) for h in range(Hkv * G) for t in rng.choice(Tq, 16, replace=False)]
+    rows += [(0, 0, Tq - 1), (0, Hkv * G - 1, 0), (0, 0, 63), (0, 0, 64)]
+    want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), sel.idx, sel.cnt, q_start,
+                              1.0 / math.sqrt(d), 64, rows=rows)
+    got = np64(out)
+    err = max(max_abs(got[r], want[r]) for r in rows)
+    assert err < 2e-2, err
+
+
 def test_prefill_full_budget_is_causal_attention():
     B, Hq, Hkv, d, T = 1, 4, 1, 128, 512
     c, q_chunk, idx, cnt, _ = _prefill_case(41, B, Hq, Hkv, d, T, 0, T, topk=64, n_local=2)
