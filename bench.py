@@ -34,6 +34,39 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
 
+# HBM bytes per launch measured with rocprofv3 counters on the default
+# workloads (FETCH_SIZE and WRITE_SIZE in separate passes, KiB per dispatch,
+# averaged over the kernel's dispatches in `bench.py --steps 2 --warmup 1
+# --no-cpu-baseline --copy-probe-gib 1`), each scaled by what the same counter
+# reads for a copy kernel of known size using the same kind of loads: the
+# runtime's device copy (nontemporal loads) and an elementwise kernel (plain
+# loads) each read 1 GiB and FETCH_SIZE reports 512 MiB for both, so fetches
+# take x2; WRITE_SIZE reports the 1 GiB written exactly (x1).
+# An entry holds the digest of the sources it was measured on and is reported
+# only while they are unchanged.
+PMC_TRAFFIC = {
+    "layer_k2": {"fetch_kib": 106906.5, "write_kib": 3515.1, "fetch_scale": 2.0, "write_scale": 1.0,
+                 "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
+                 "sha256": "e7b8f48717079ba4c968bd56fc88ce98bff8a87e875912820fcb94888d2f98d1"},
+    "attn_prefill": {"fetch_kib": 366801.9, "write_kib": 65536.1, "fetch_scale": 2.0, "write_scale": 1.0,
+                     "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
+                     "sha256": "e7993e0b54d8acf9ad839be2aaee283a5bc091019e9b1d71b2cad706e5c10322"},
+}
+
+
+def traffic_bytes(name):
+    import hashlib
+    ent = PMC_TRAFFIC.get(name)
+    if ent is None:
+        return None
+    h = hashlib.sha256()
+    for f in ent["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != ent["sha256"]:
+        return None
+    return int(round((ent["fetch_kib"] * ent["fetch_scale"] + ent["write_kib"] * ent["write_scale"]) * 1024))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -137,11 +170,22 @@ class DecodeBench:
         lists = B * H * (U + 1) * 4
         attn = B * H * (U * wl.block * d * e * 2) + B * wl.Hq * d * e + lists
         out = B * wl.Hq * d * 4
+        # the fused kernels are timed over all L layers, and the last layer
+        # selects nothing (no scoring in its K2, no lists in its K3): per-launch
+        # figures are averages over the timed launches
+        nxt = (self.L - 1) / self.L
         return {
             "forecast_proj": proj, "kv_block_meanpool": pool, "score_topk": score + lists,
             "attn_decode": attn + out,
-            "layer_k1": proj, "layer_k2": score + attn, "layer_k3": lists + out + pool,
+            "layer_k1": proj, "layer_k2": round(score * nxt + attn), "layer_k3": round(lists * nxt + out + pool),
         }
+
+    def step_bytes(self):
+        """Algorithmic bytes of one step: L projections (the layer-0 one
+        included), L selections (layer 0's by the separate score/top-k call),
+        L attentions with their merges, L newest-block updates."""
+        b = self.bytes_per_launch()
+        return self.L * (b["forecast_proj"] + b["score_topk"] + b["attn_decode"] + b["kv_block_meanpool"])
 
 
 def time_graph(torch, fn, steps, warmup, use_graph=True):
@@ -264,7 +308,7 @@ def run_decode(args, torch, bskv, wl):
         gbs = bpl[name] / t / 1e9
         kernels[name] = {"us": round(t * 1e6, 3), "bytes": bpl[name], "GBps": round(gbs, 1),
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    step_bytes = bench.L * (bpl["layer_k1"] + bpl["layer_k2"] + bpl["layer_k3"])   # incl. the layer-0 projection
+    step_bytes = bench.step_bytes()
     dom = "attn_decode" if args.per_op else "layer_k2"
     ach = bpl[dom] / kt[dom] / 1e9
     result = {
@@ -276,7 +320,7 @@ def run_decode(args, torch, bskv, wl):
                    "n_local": wl.n_local, "hip_graph": not args.no_graph,
                    "path": "per-op" if args.per_op else "fused-layer"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(dom),
                      "bytes_per_launch": bpl[dom], "us_per_launch": round(kt[dom] * 1e6, 3)},
         "step_hbm_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
@@ -340,6 +384,23 @@ class PrefillBench:
             self.pool(c)
             self.select(c)
             self.attend(c)
+
+    def min_attention_bytes(self):
+        """Least HBM bytes the attention kernel can move per chunk on average:
+        the chunk's queries and outputs (bf16), its lists, and every K/V block
+        that some query block of the chunk lists, once per (sequence, KV head)."""
+        wl = self.wl
+        e = 2
+        qo = 2 * self.B * wl.Hq * self.C * wl.d * e
+        import numpy as np
+        tot = 0.0
+        for c in range(self.n_chunks):
+            idx = self.idx[c].cpu().numpy()
+            cnt = self.cnt[c].cpu().numpy()
+            used = np.arange(idx.shape[3])[None, None, None, :] < cnt[..., None]
+            blocks = sum(np.unique(idx[b, g][used[b, g]]).size for b in range(self.B) for g in range(wl.Hkv))
+            tot += qo + blocks * 2 * wl.block * wl.d * e + idx.size * 4 + cnt.size * 4
+        return tot / self.n_chunks
 
     def attention_flops(self):
         """2*d flops for q.k and 2*d for p.v per (query head, token, attended key):
@@ -405,7 +466,8 @@ def run_prefill(args, torch, bskv, wl):
                    "hip_graph": not args.no_graph},
         "roofline": {"bound": "mfma", "kernel": "attn_prefill", "achieved": round(att_tf, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": per_chunk_flops,
+                     "traffic": traffic_bytes("attn_prefill"), "flops_per_launch": per_chunk_flops,
+                     "min_bytes_per_launch": round(bench.min_attention_bytes()),
                      "us_per_launch": round(kt["attn_prefill"] * 1e6, 2)},
         "attention_tflop_total": round(flops / 1e12, 2),
         "kernels": kernels,
@@ -613,12 +675,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.copy_probe_gib > 0:
+        # counter calibration: two copies of known size, the runtime's device
+        # copy (nontemporal loads) and an elementwise kernel (plain loads)
         n = int(args.copy_probe_gib * (1 << 30))
-        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        a = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
         b.copy_(a)
+        torch.neg(a.view(torch.bfloat16), out=b.view(torch.bfloat16))
         torch.cuda.synchronize()
-        log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
+        log(f"[bench] copy probes: {n} bytes read, {n} bytes written, each")
         del a, b
     if args.workload == "prefill":
         result = run_prefill(args, torch, bskv, CONFIGS[4])
