@@ -54,8 +54,13 @@ hipError_t launch_meanpool(const MeanpoolArgs& a) {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void proj_partial_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                               int B, int hidden, int N, float* __restrict__ part) {
-  __shared__ ProjSmem sm;
-  proj_partial_wg<T>(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
+  if constexpr (std::is_same<T, bf16_bits>::value) {
+    __shared__ ProjMfmaSmem sm;
+    proj_partial_mfma_wg(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
+  } else {
+    __shared__ ProjSmem sm;
+    proj_partial_wg<T>(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void proj_reduce_kernel(const float* __restrict__ part, int n_splits, int B,

@@ -22,6 +22,12 @@
 
 namespace bskv {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
 constexpr int kBlk = 64;            // tokens per KV block
 constexpr int kMaxSplitsDecode = 32;   // attention splits per KV head
 
@@ -107,17 +113,85 @@ __device__ void proj_partial_wg(const T* __restrict__ x, const T* __restrict__ w
   }
 }
 
-// F[b, n] = sum over splits of the partials, in split order (loads issued
-// eight at a time before they are added).
+// bf16 projection partials on MFMA (v_mfma_f32_16x16x32_bf16) for one tile
+// of 128 rows x 128 columns of W:  F^T[n][b] = sum_k W^T[n][k] x^T[k][b].
+// W is staged row-major in LDS (rows padded to 288 bytes) and read as the A
+// operand with transposing reads: within each 16-lane group, lane 4r+c reads
+// row r, columns 4c..4c+3, and ds_read_b64_tr_b16 hands lane i element i%4
+// of lane 4r+i/4, so lane (m, g) gets column m at rows 4g..4g+3 (and, from a
+// second read 16 rows down, 16+4g..16+4g+3).  x^T is the B operand, loaded
+// from memory in the same row order (lane: batch row m).  Wave w owns column
+// tiles 2w and 2w+1; one pass, no cross-lane reduction.
+constexpr int kProjWStr = 128 + 16;
+struct ProjMfmaSmem {
+  bf16_bits w[kProjRows * kProjWStr];
+};
+
+__device__ void proj_partial_mfma_wg(const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ w, int B,
+                                     int hidden, int N, int tile, int split, float* __restrict__ part,
+                                     ProjMfmaSmem& sm) {
+  constexpr int TC = 128;
+  constexpr int CPT = kProjRows * TC / 8 / kThreads;   // 16-byte chunks of the tile per thread
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int r_begin = split * kProjRows, n0 = tile * TC;
+  uint4 raw[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
+    raw[i] = ld16_nt(w + (int64_t)(r_begin + r) * N + n0 + cc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
+    *reinterpret_cast<uint4*>(&sm.w[r * kProjWStr + cc * 8]) = raw[i];
+  }
+  __syncthreads();
+  const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  for (int b0 = 0; b0 < B; b0 += 16) {
+    const int b = b0 + l16;
+    bf16x8_t xb[kProjRows / 32];
+#pragma unroll
+    for (int ks = 0; ks < kProjRows / 32; ++ks) {
+      uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+      if (b < B) {
+        const bf16_bits* xp = x + (int64_t)b * hidden + r_begin + 32 * ks + 4 * lg;
+        lo = *reinterpret_cast<const uint2*>(xp);
+        hi = *reinterpret_cast<const uint2*>(xp + 16);
+      }
+      xb[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int nt = 2 * wid + t;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kProjRows / 32; ++ks) {
+        const bf16_bits* v0 = &sm.w[(32 * ks + tr_row) * kProjWStr + 16 * nt + tr_col];
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * kProjWStr));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[ks], acc, 0, 0, 0);
+      }
+      // lane (b, lg) holds F^T[n0 + 16 nt + 4 lg + i][b], i = 0..3
+      if (b < B)
+        *reinterpret_cast<float4*>(&part[((int64_t)split * B + b) * N + n0 + 16 * nt + 4 * lg]) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
+// F[b, n] = sum over splits of the partials, in split order (up to 32 loads
+// issued before any is added: one round trip for hidden sizes up to 4096).
 __device__ __forceinline__ float proj_reduce_one(const float* __restrict__ part, int n_splits, int B, int N, int b,
                                                  int n) {
   float s = 0.f;
-  for (int s0 = 0; s0 < n_splits; s0 += 8) {
-    float v[8];
+  for (int s0 = 0; s0 < n_splits; s0 += 32) {
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (s0 + i < n_splits) ? part[((int64_t)(s0 + i) * B + b) * N + n] : 0.f;
+    for (int i = 0; i < 32; ++i) v[i] = (s0 + i < n_splits) ? part[((int64_t)(s0 + i) * B + b) * N + n] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += v[i];
+    for (int i = 0; i < 32; ++i) s += v[i];
   }
   return s;
 }
@@ -278,8 +352,6 @@ struct AttnSmem {
   float red[4][G][D];
 };
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Register set of one 64-token K/V block.
 //   bf16: K as the MFMA A operand of S^T = K Q^T -- wave w owns keys
@@ -524,6 +596,18 @@ __device__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D
   const int ns = p.n_splits;
   const int64_t sbase = (int64_t)bg * ns * G;
   const int tid = threadIdx.x;
+  // every partial this thread needs is requested first, together with the
+  // (m, l) pairs: one round trip to memory
+  constexpr int OPT = (G * D + kThreads - 1) / kThreads;   // outputs per thread
+  float v[OPT][kMaxSplitsDecode];
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    const int i = tid + o * kThreads;
+    const int h = i / D, d = i % D;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplitsDecode; ++sp)
+      v[o][sp] = (i < G * D && sp < ns) ? p.ws_o[(sbase + sp * G + h) * D + d] : 0.f;
+  }
   for (int i = tid; i < ns * G * 2; i += kThreads) (&sm.ml[0][0][0])[i] = p.ws_ml[sbase * 2 + i];
   __syncthreads();
   if (tid < G) {
@@ -539,17 +623,6 @@ __device__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D
     sm.den[tid] = den;
   }
   __syncthreads();
-  // every partial this thread needs is requested before any is used
-  constexpr int OPT = (G * D + kThreads - 1) / kThreads;   // outputs per thread
-  float v[OPT][kMaxSplitsDecode];
-#pragma unroll
-  for (int o = 0; o < OPT; ++o) {
-    const int i = tid + o * kThreads;
-    const int h = i / D, d = i % D;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplitsDecode; ++sp)
-      v[o][sp] = (i < G * D && sp < ns) ? p.ws_o[(sbase + sp * G + h) * D + d] : 0.f;
-  }
 #pragma unroll
   for (int o = 0; o < OPT; ++o) {
     const int i = tid + o * kThreads;

@@ -43,9 +43,15 @@ struct LayerParams {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
-  __shared__ ProjSmem sm;
-  proj_partial_wg<T>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, blockIdx.x % p.proj_tiles,
-                     blockIdx.x / p.proj_tiles, p.proj_part, sm);
+  if constexpr (std::is_same<T, bf16_bits>::value) {
+    __shared__ ProjMfmaSmem sm;
+    proj_partial_mfma_wg((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, blockIdx.x % p.proj_tiles,
+                         blockIdx.x / p.proj_tiles, p.proj_part, sm);
+  } else {
+    __shared__ ProjSmem sm;
+    proj_partial_wg<T>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, blockIdx.x % p.proj_tiles,
+                       blockIdx.x / p.proj_tiles, p.proj_part, sm);
+  }
 }
 
 template <typename T, int D, int G>

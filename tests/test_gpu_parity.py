@@ -84,6 +84,17 @@ def test_forecast_proj_bf16(B):
     assert max_abs(np64(f), want) < 1e-4
 
 
+@pytest.mark.parametrize("B,hidden,H,d", [(2, 512, 2, 64), (5, 768, 1, 128), (17, 256, 4, 64)])
+def test_forecast_proj_bf16_shapes(B, hidden, H, d):
+    """Other tile counts: hidden 256..768 (2..6 row splits), 128..256 columns."""
+    g = torch.Generator().manual_seed(hidden + B)
+    x = torch.randn(B, hidden, generator=g).to(torch.bfloat16)
+    w = (torch.randn(hidden, H * d, generator=g) * 0.05).to(torch.bfloat16)
+    f = bskv.forecast_proj(x.to(DEV), w.to(DEV), H, d)
+    torch.cuda.synchronize()
+    assert max_abs(np64(f), orc.forecast_proj(np64(x), np64(w), H, d)) < 1e-4
+
+
 def test_forecast_proj_f32_and_repeat():
     g = torch.Generator().manual_seed(3)
     x = torch.randn(5, 256, generator=g)
