@@ -57,15 +57,67 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<bf16_bits>(bf16_bits x) { return __uint_as_float(((uint32_t)x) << 16); }
 
+// Cross-lane reductions without LDS traffic: DPP inside rows of 16 lanes
+// (quad permutes, then the half-row and row mirrors), and gfx950's
+// v_permlane16_swap / v_permlane32_swap across rows.  A swap of a register
+// with itself leaves each lane holding its own value and that of lane l^16
+// (resp. l^32) in the two results, so combining them is an all-reduce step.
+// Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16 lanes
+
+__device__ __forceinline__ float sum4(float v) {
+  v += dpp_mov<kDppXor1>(v);
+  return v + dpp_mov<kDppXor2>(v);
+}
+__device__ __forceinline__ float sum8(float v) {
+  v = sum4(v);
+  return v + dpp_mov<kDppHalfMirror>(v);
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  return v + dpp_mov<kDppMirror>(v);
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppMirror>(v));
+}
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  float a, b;
+  v = max16(v);
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  swap32(v, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  float a, b;
+  v = sum16(v);
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
 }
 
 // Exclusive prefix sum over the 256 threads of a block (thread order).

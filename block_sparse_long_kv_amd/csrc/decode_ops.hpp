@@ -292,9 +292,7 @@ __device__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_b
           acc += fv[i].w * kv[uu][i].w;
         }
       }
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 1);
+      acc = sum8(acc);   // the 8 lanes of the row (all active together)
       if (sub == 0 && j < hi) sc[j] = acc;
     }
   }
@@ -433,10 +431,7 @@ __device__ __forceinline__ void attn_block(const AttnRegs<T, D, G>& r, int nvali
         for (int e = 0; e < VEC; ++e) s[h] += kf[e] * sm.qs[h][d0 + e];
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s[h] += __shfl_xor(s[h], 1);
-      s[h] += __shfl_xor(s[h], 2);
-    }
+    for (int h = 0; h < G; ++h) s[h] = sum4(s[h]);
 #pragma unroll
     for (int h = 0; h < G; ++h)
       if ((h & 3) == part) sm.sraw[h][tok] = (tok < nvalid) ? s[h] : -INFINITY;

@@ -33,9 +33,7 @@ __device__ __forceinline__ void score_rows(const float* __restrict__ kc_bg, cons
       acc += fv[i].z * k4.z;
       acc += fv[i].w * k4.w;
     }
-    acc += __shfl_xor(acc, 4);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 1);
+    acc = sum8(acc);   // the 8 lanes of the row (all active together)
     if (sub == 0) sink(j, acc);
   }
 }
