@@ -59,7 +59,10 @@ __global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
   __shared__ __attribute__((aligned(16))) union { AttnSmem<D, G> attn; float fvec[D]; } sm;
   const int n_bg = p.B * p.H;
   const int n_score = p.select ? p.score_splits * n_bg : 0;
-  const int bid = blockIdx.x;
+  // attention workgroups (long chains of dependent loads) are dispatched
+  // first; the short streaming score workgroups fill the tail
+  const int n_attn = p.attn.n_splits * n_bg;
+  const int bid = (int)blockIdx.x < n_attn ? (int)blockIdx.x + n_score : (int)blockIdx.x - n_attn;
   if (bid < n_score) {
     const int split = bid % p.score_splits, bg = bid / p.score_splits;
     const int b = bg / p.H, g = bg % p.H;
