@@ -120,16 +120,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return a + b;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts by 1, 2,
+// 4, 8 inside each row of 16 lanes (zero from outside the row), then lane 15
+// of row r added to row r+1 (rows 1 and 3) and lane 31 to rows 2 and 3.
+// Every lane of the wave must be active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum over the 256 threads of a block (thread order).
 // `tmp` is 4 ints of shared memory; `total` receives the sum of all values.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const int inc = wave_incl_scan(v);
   if (lane == 63) tmp[wid] = inc;
   __syncthreads();
   int off = 0, tot = 0;
@@ -165,30 +174,23 @@ struct TopkShared {
 };
 
 // Exclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_excl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  return inc - v;
-}
+__device__ __forceinline__ int wave_excl_scan(int v) { return wave_incl_scan(v) - v; }
 
 // Top-k + union for one selection problem, run by all 256 threads.  Thread
 // t owns candidates t*KPT .. t*KPT+KPT-1 (so its keys are in block-id order);
 // with KPT <= 8 they are held in registers, above that re-read from LDS.
 template <int KPT>
-__device__ void topk_union_regs(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init, int n_local,
-                                int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
+__device__ __forceinline__ void topk_union_regs(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init,
+                                                int n_local,
+                                int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh,
+                                const uint32_t* kin = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int i0 = tid * KPT;
   constexpr bool kRegs = KPT <= 8;
   uint32_t kr[kRegs ? KPT : 1];
   if constexpr (kRegs) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) kr[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
+    for (int e = 0; e < KPT; ++e) kr[e] = (i0 + e < n) ? (kin ? kin[e] : keys[i0 + e]) : 0u;
   }
   auto key = [&](int e) -> uint32_t {
     if constexpr (kRegs) return kr[e];

@@ -53,7 +53,7 @@ template <typename T>
 __host__ __device__ constexpr int proj_tile_cols_host() { return 16 * VecN<T>::N; }
 
 template <typename T>
-__device__ void proj_partial_wg(const T* __restrict__ x, const T* __restrict__ w, int B, int hidden, int N, int tile,
+__device__ __forceinline__ void proj_partial_wg(const T* __restrict__ x, const T* __restrict__ w, int B, int hidden, int N, int tile,
                                 int split, float* __restrict__ part, ProjSmem& sm) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TC = 16 * VEC;
@@ -127,7 +127,7 @@ struct ProjMfmaSmem {
   bf16_bits w[kProjRows * kProjWStr];
 };
 
-__device__ void proj_partial_mfma_wg(const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ w, int B,
+__device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ w, int B,
                                      int hidden, int N, int tile, int split, float* __restrict__ part,
                                      ProjMfmaSmem& sm) {
   constexpr int TC = 128;
@@ -205,7 +205,7 @@ struct MeanpoolSmem {
 };
 
 template <typename T, int D>
-__device__ void meanpool_wg(const T* __restrict__ kblock, int64_t st, float* __restrict__ kc_row,
+__device__ __forceinline__ void meanpool_wg(const T* __restrict__ kblock, int64_t st, float* __restrict__ kc_row,
                             MeanpoolSmem<T, D>& sm) {
   constexpr int VEC = VecN<T>::N;
   constexpr int CPR = D / VEC;
@@ -258,7 +258,7 @@ __device__ __forceinline__ DecodeCands decode_cands(int64_t L, int64_t nb_cap, i
 }
 
 template <int D>
-__device__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_bg, int lo, int hi,
+__device__ __forceinline__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_bg, int lo, int hi,
                                float* __restrict__ sc) {
   constexpr int LPR = 8;
   constexpr int F4 = D / 4 / LPR;
@@ -300,10 +300,25 @@ __device__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_b
 
 // Top-k + union of one decode problem from its score row (written by an
 // earlier kernel).  keys: LDS, at least (c1 - c0) entries.
-__device__ void topk_decode_wg(const float* __restrict__ sc, DecodeCands dc, int topk, int n_init, int n_local, int U,
+__device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, DecodeCands dc, int topk, int n_init,
+                                               int n_local, int U,
                                int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, uint32_t* keys,
                                TopkShared& sh) {
   const int n = dc.c1 - dc.c0;
+  if (n <= 8 * kThreads) {
+    // thread t's eight candidates (8t .. 8t+7) straight into registers
+    uint32_t kin[8];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * (int)threadIdx.x + e;
+      v[e] = i < n ? sc[dc.c0 + i] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kin[e] = orderable_key(v[e]);
+    topk_union_regs<8>(keys, n, dc.c0, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+    return;
+  }
   constexpr int PB = 8;   // loads in flight per thread
   for (int base = 0; base < n; base += PB * kThreads) {
     float v[PB];
@@ -476,7 +491,7 @@ __device__ __forceinline__ void attn_block(const AttnRegs<T, D, G>& r, int nvali
 }
 
 template <typename T, int D, int G>
-__device__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
+__device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
   using R = AttnRegs<T, D, G>;
   constexpr int VEC = R::VEC;
   constexpr int HW = (G + 3) / 4;
@@ -585,7 +600,7 @@ struct CombineSmem {
 };
 
 template <int D, int G>
-__device__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D, G>& sm) {
+__device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D, G>& sm) {
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int Hq = p.Hkv * G;
   const int ns = p.n_splits;
