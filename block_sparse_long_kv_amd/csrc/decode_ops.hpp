@@ -490,6 +490,50 @@ __device__ __forceinline__ void attn_block(const AttnRegs<T, D, G>& r, int nvali
   }
 }
 
+// End of a split: sum the PV token lanes (inside the wave, then across the
+// 4 waves) and write the unnormalised output and (m, l) of every head.
+template <typename T, int D, int G>
+__device__ __forceinline__ void attn_split_finish(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm,
+                                                  float (&acc)[G][VecN<T>::N], const float* m_run,
+                                                  const float* l_run) {
+  using R = AttnRegs<T, D, G>;
+  constexpr int VEC = R::VEC;
+  constexpr int HW = (G + 3) / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // token lanes are the lane bits at and above DCH (a power of two >= 8)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float v = acc[h][e], a, b;
+      if constexpr (R::DCH <= 8) v += dpp_mov<0x128>(v);   // row_ror:8 = lane ^ 8 inside the row
+      if constexpr (R::DCH <= 16) { swap16(v, a, b); v = a + b; }
+      swap32(v, a, b);
+      acc[h][e] = a + b;
+    }
+  const int dc = tid % R::DCH;
+  if (lane < R::DCH) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm.red[wid][h][dc * VEC + e] = acc[h][e];
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)bg * p.n_splits + split) * G;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, d = i % D;
+    p.ws_o[(pbase + h) * D + d] = sm.red[0][h][d] + sm.red[1][h][d] + sm.red[2][h][d] + sm.red[3][h][d];
+  }
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    const int h = wid + 4 * i;
+    if (h < G && lane == 0) {
+      p.ws_ml[(pbase + h) * 2 + 0] = m_run[i];
+      p.ws_ml[(pbase + h) * 2 + 1] = l_run[i];
+    }
+  }
+}
+
 template <typename T, int D, int G>
 __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
   using R = AttnRegs<T, D, G>;
@@ -560,34 +604,7 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
     attn_block<T, D, G>(rb, nvb < 0 ? 0 : nvb, sm, qf, sscale, acc, m_run, l_run);
   }
 
-  // sum the PV token lanes: inside the wave, then across the 4 waves
-#pragma unroll
-  for (int o = R::DCH; o < 64; o <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-  const int dc = tid % R::DCH;
-  if (lane < R::DCH) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm.red[wid][h][dc * VEC + e] = acc[h][e];
-  }
-  __syncthreads();
-  const int64_t pbase = ((int64_t)bg * p.n_splits + split) * G;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    p.ws_o[(pbase + h) * D + d] = sm.red[0][h][d] + sm.red[1][h][d] + sm.red[2][h][d] + sm.red[3][h][d];
-  }
-#pragma unroll
-  for (int i = 0; i < HW; ++i) {
-    const int h = wid + 4 * i;
-    if (h < G && lane == 0) {
-      p.ws_ml[(pbase + h) * 2 + 0] = m_run[i];
-      p.ws_ml[(pbase + h) * 2 + 1] = l_run[i];
-    }
-  }
+  attn_split_finish<T, D, G>(p, bg, split, sm, acc, m_run, l_run);
 }
 
 // Merge the splits of one KV head (written by an earlier kernel), in split

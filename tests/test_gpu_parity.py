@@ -213,6 +213,23 @@ def test_attn_decode_on_oracle_lists(dtype, d, G, tol):
     assert max_abs(np64(out), want) < tol
 
 
+@pytest.mark.parametrize("dtype,d,G,tol", [("bf16", 128, 4, 2e-2), ("bf16", 64, 8, 2e-2), ("f32", 64, 2, 1e-4)])
+def test_attn_decode_long_splits(dtype, d, G, tol):
+    """One KV head per sequence and 155 listed blocks: 32 splits of 5 blocks
+    each, i.e. the double-buffered online-softmax loop rather than the
+    all-at-once path of short splits.  Ragged lengths."""
+    lens = [64 * 300, 64 * 251 + 30]
+    c, sel, lens_np = _attn_case(13, 2, G, 1, d, 64 * 300, dtype, lens, topk=150, n_local=4)
+    assert int(sel.cnt.max()) == 155
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    out = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    torch.cuda.synchronize()
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), sel.idx, sel.cnt, lens_np, scale, 64)
+    assert max_abs(np64(out), want) < tol
+
+
 def test_attn_decode_config1_end_to_end():
     wl = CONFIGS[1]
     lay = _gpu(decode_inputs(wl, "cpu")[0])
