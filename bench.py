@@ -15,7 +15,18 @@ and replayed.  `value` = batch tokens per second of the whole step.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload decode|decode-b4] [--per-op]
 
 Per-kernel durations come from HIP events around back-to-back launches of
-one kernel over all layers; the roofline object reports the dominant kernel.
+one kernel over all layers; the roofline object reports the dominant kernel
+(`traffic`: HBM bytes per launch from rocprofv3 counters, while the kernel
+sources match those they were measured on).  Also reported: the rate without
+the Forecast projection, the box's measured device-copy rate, the selection
+cost per layer at 32K/64K/128K context, and the fp64 oracle on the host
+(`cpu_baseline`, also on one thread).
+
+  --workload decode-b4   B4 x 32K, one layer, rotated over 8 replicas so the
+                         45 MB working set is not served from the 256 MB cache
+  --workload prefill     B4 x 128K chunked prefill (MFMA-bound attention; the
+                         vendor bf16 GEMM rate on the box is reported beside it)
+  --workload offload     B16 x 128K decode with the KV cache in host memory
 """
 from __future__ import annotations
 
@@ -255,7 +266,96 @@ def kernel_times(torch, bench, reps=3):
     return res
 
 
-def cpu_baseline_decode(bench, budget_s=12.0):
+def measured_hbm_peaks(torch, gib=2.0):
+    """The box's own streaming rate, as context for the 8 TB/s figure: the
+    runtime's device copy (read + write bytes per second), HIP events on the
+    current stream."""
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, byt in (("copy_GBps", lambda: b.copy_(a), 2 * n),):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(byt * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    return out
+
+
+def measured_gemm_tflops(torch, n=8192):
+    """A plain bf16 GEMM through the vendor BLAS (n x n x n), as context for the
+    2.5 PFLOP/s figure."""
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del a, b, c
+    return round(2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def selection_sweep(torch, bench, contexts=(32768, 65536, 131072), reps=3):
+    """Selection cost against context length (decode, per layer): score + top-k
+    + union of one layer for the whole batch at seq_len = T', on the same
+    compressed keys (candidates limited by T').  Graph-replayed launches over
+    all layers, HIP events."""
+    wl, res = bench.wl, {}
+    for tc in contexts:
+        if tc > bench.T:
+            continue
+        lens = torch.full((bench.B,), tc, dtype=torch.int64, device=bench.dev)
+
+        def body():
+            for _ in range(reps):
+                for l in range(bench.L):
+                    bench.bskv.forecast_block_score_topk(bench.f[l], bench.kc[l], wl.topk, wl.n_init, wl.n_local,
+                                                         seq_len=lens, idx=bench.idx[l], cnt=bench.cnt[l],
+                                                         ws=bench.ws_score)
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        res[str(tc)] = round(e0.elapsed_time(e1) * 1e3 / (reps * bench.L), 3)
+        del g
+    # leave the lists of the full context in place for whoever runs next
+    for l in range(bench.L):
+        bench.select(l)
+    torch.cuda.synchronize()
+    return res
+
+
+def cpu_baseline_decode(bench, budget_s=12.0, layers=None):
     """The fp64 oracle on a bounded sample of the same decode step: layer 0,
     one sequence (batch element 0, all KV heads); repeated until the budget
     is spent; scaled to the full step (x B sequences x L layers)."""
@@ -288,16 +388,33 @@ def cpu_baseline_decode(bench, budget_s=12.0):
         t_total += time.perf_counter() - t0
         reps += 1
         del newest
+    n_layers = bench.L if layers is None else layers
     per_sample = t_total / reps
-    step_s = per_sample * bench.B * bench.L
+    step_s = per_sample * bench.B * n_layers
+    # the same sample on one thread, over a shorter budget
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r1, t1 = 0, 0.0
+            while t1 < budget_s / 3 and r1 < 500:
+                t0 = time.perf_counter()
+                f = orc.forecast_proj(x, w, wl.Hkv, wl.d)
+                sel = orc.decode_select(f, kc, lens, wl.topk, wl.n_init, wl.n_local, wl.block)
+                orc.attend_decode(q, k, v, sel.idx, sel.cnt, lens, wl.scale, wl.block)
+                t1 += time.perf_counter() - t0
+                r1 += 1
+            one = round(bench.B / (t1 / r1 * bench.B * n_layers), 4)
+    except Exception:
+        pass
     return {"value": bench.B / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0, batch element 0 (all {wl.Hkv} KV heads), {reps} reps in {t_total:.1f}s; "
-                      f"per-step time scaled x{bench.B} sequences x{bench.L} layers",
-            "sample_seconds": round(per_sample, 4)}
+                      f"per-step time scaled x{bench.B} sequences x{n_layers} layers",
+            "sample_seconds": round(per_sample, 4), "value_1_thread": one, "cpu_model": cpu_model()}
 
 
-def run_decode(args, torch, bskv, wl):
-    bench = DecodeBench(wl, torch, bskv)
+def run_decode(args, torch, bskv, wl, replicas=None):
+    bench = DecodeBench(wl, torch, bskv, layers=replicas)
     step_fn = bench.step_per_op if args.per_op else bench.step
     step_s, _ = time_graph(torch, step_fn, args.steps, args.warmup, use_graph=not args.no_graph)
     log(f"[bench] decode step {step_s * 1e3:.3f} ms ({'graph' if not args.no_graph else 'eager'})")
@@ -311,8 +428,17 @@ def run_decode(args, torch, bskv, wl):
     step_bytes = bench.step_bytes()
     dom = "attn_decode" if args.per_op else "layer_k2"
     ach = bpl[dom] / kt[dom] / 1e9
+    peaks = measured_hbm_peaks(torch)
+    sweep = selection_sweep(torch, bench)
+    # replicas: independent copies of one layer's inputs, rotated so that the
+    # working set does not sit in the 256 MB cache; the step then covers
+    # `replicas` layer-steps of a one-layer model
+    per_step_layers = bench.L if replicas is None else 1
+    layer_steps = bench.L // per_step_layers
+    t_step = step_s / layer_steps
+    proj_s = (kt["forecast_proj"] + (bench.L - 1) * kt["layer_k1"]) / layer_steps
     result = {
-        "metric": METRIC, "value": round(bench.B / step_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(bench.B / t_step, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": bench.B, "T": bench.T, "layers": bench.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
@@ -324,10 +450,16 @@ def run_decode(args, torch, bskv, wl):
                      "bytes_per_launch": bpl[dom], "us_per_launch": round(kt[dom] * 1e6, 3)},
         "step_hbm_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
+        "value_without_proj": round(bench.B / (t_step - proj_s), 2),
+        "measured_peaks": dict(peaks, roofline_frac_of_copy=round(ach / peaks["copy_GBps"], 4)),
+        "select_us_per_layer_vs_T": sweep,
         "kernels": kernels,
     }
+    if replicas is not None:
+        result["config"]["layers"] = 1
+        result["config"]["replicas"] = replicas
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(bench, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline_decode(bench, args.cpu_budget, layers=per_step_layers)
     return result
 
 
@@ -446,6 +578,7 @@ def run_prefill(args, torch, bskv, wl):
     f_bytes = B * H * C * d * 2                                   # Forecast vectors of a chunk (bf16)
     kc_read = B * H * sum(max(0, qb - wl.n_local + 1 - wl.n_init) for qb in range(T // 64)) * d * 4 / bench.n_chunks
     per_chunk_flops = flops / bench.n_chunks
+    gemm_tf = measured_gemm_tflops(torch)
     att_tf = per_chunk_flops / kt["attn_prefill"] / 1e12
     kernels = {
         "kv_block_meanpool": {"us": round(kt["kv_block_meanpool"] * 1e6, 2),
@@ -470,6 +603,8 @@ def run_prefill(args, torch, bskv, wl):
                      "min_bytes_per_launch": round(bench.min_attention_bytes()),
                      "us_per_launch": round(kt["attn_prefill"] * 1e6, 2)},
         "attention_tflop_total": round(flops / 1e12, 2),
+        "measured_gemm_bf16_TFLOPs": gemm_tf,
+        "roofline_frac_of_measured_gemm": round(att_tf / gemm_tf, 4),
         "kernels": kernels,
     }
 
@@ -690,8 +825,10 @@ def main():
     elif args.workload == "offload":
         result = run_offload(args, torch, bskv, CONFIGS[5])
     else:
-        wl = CONFIGS[3] if args.workload == "decode" else CONFIGS[2]
-        result = run_decode(args, torch, bskv, wl)
+        if args.workload == "decode":
+            result = run_decode(args, torch, bskv, CONFIGS[3])
+        else:
+            result = run_decode(args, torch, bskv, CONFIGS[2], replicas=8)
     print(json.dumps(result), flush=True)
 
 
