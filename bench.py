@@ -24,6 +24,7 @@ cost per layer at 32K/64K/128K context, and the fp64 oracle on the host
 
   --workload decode-b4   B4 x 32K, one layer, rotated over 8 replicas so the
                          45 MB working set is not served from the 256 MB cache
+  --workload decode-tiny B1 x 4096 fp32 (correctness configuration; us per step)
   --workload prefill     B4 x 128K chunked prefill (MFMA-bound attention; the
                          vendor bf16 GEMM rate on the box is reported beside it)
   --workload offload     B16 x 128K decode with the KV cache in host memory
@@ -464,6 +465,54 @@ def run_decode(args, torch, bskv, wl, replicas=None):
 
 
 # ---------------------------------------------------------------------------
+# tiny fp32 decode (a correctness configuration: launch-bound)
+# ---------------------------------------------------------------------------
+def run_tiny(args, torch, bskv, wl):
+    """B1 x 4096, fp32, Forecast vectors given: newest-block pooling, score +
+    top-k + union, attention (split + merge) per step.  The work is ~378 KB,
+    so the step is launch-bound; the HBM fraction is reported but not
+    meaningful."""
+    from workloads import decode_inputs
+    dev = torch.device("cuda:0")
+    lay = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in decode_inputs(wl, "cpu")[0].items()}
+    nb = wl.T // wl.block
+    kc = torch.empty(wl.B, wl.Hkv, nb, wl.d, dtype=torch.float32, device=dev)
+    bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
+    idx = torch.empty(wl.B, wl.Hkv, wl.U, dtype=torch.int32, device=dev)
+    cnt = torch.empty(wl.B, wl.Hkv, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.float32, device=dev)
+    ws_s = torch.zeros(max(256, bskv.workspace_bytes("score", wl.B, wl.Hkv, 0, nb, wl.d)), dtype=torch.uint8,
+                       device=dev)
+    ws_a = torch.zeros(max(256, bskv.workspace_bytes("attn", wl.B, wl.Hq, wl.Hkv, wl.d, wl.U)), dtype=torch.uint8,
+                       device=dev)
+
+    def step():
+        bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc, 0, nb, newest_only=True)
+        bskv.forecast_block_score_topk(lay["f"], kc, wl.topk, wl.n_init, wl.n_local, seq_len=lay["seq_len"],
+                                       idx=idx, cnt=cnt, ws=ws_s)
+        bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"], wl.scale, out=out,
+                                      ws=ws_a)
+
+    step_s, _ = time_graph(torch, step, args.steps, args.warmup, use_graph=not args.no_graph)
+    e = 4
+    n_cand = (wl.T - 1) // wl.block - wl.n_local + 1 - wl.n_init
+    byt = (wl.B * wl.Hkv * (n_cand * wl.d * 4 + wl.U * wl.block * wl.d * e * 2 + wl.block * wl.d * e)
+           + 2 * wl.B * wl.Hq * wl.d * 4)
+    ach = byt / step_s / 1e9
+    return {
+        "metric": "decode step time, tiny fp32 correctness configuration", "value": round(step_s * 1e6, 3),
+        "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.d,
+                   "topk": wl.topk, "n_init": wl.n_init, "n_local": wl.n_local, "hip_graph": not args.no_graph},
+        "roofline": {"bound": "hbm", "kernel": "whole step (launch-bound)", "achieved": round(ach, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 6), "traffic": None,
+                     "bytes_per_step": byt},
+    }
+
+
+# ---------------------------------------------------------------------------
 # chunked-prefill workload
 # ---------------------------------------------------------------------------
 class PrefillBench:
@@ -789,7 +838,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode-b4", "prefill", "offload"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode-b4", "decode-tiny", "prefill", "offload"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -820,7 +870,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probes: {n} bytes read, {n} bytes written, each")
         del a, b
-    if args.workload == "prefill":
+    if args.workload == "decode-tiny":
+        result = run_tiny(args, torch, bskv, CONFIGS[1])
+    elif args.workload == "prefill":
         result = run_prefill(args, torch, bskv, CONFIGS[4])
     elif args.workload == "offload":
         result = run_offload(args, torch, bskv, CONFIGS[5])

@@ -15,6 +15,7 @@ from .sparda_ref import (  # noqa: F401
     gather_selected_blocks,
     kth_gap,
     kv_block_meanpool,
+    multihead_select_decode,
     prefill_select,
     rank_topk,
 )

@@ -38,6 +38,12 @@ function that uses it):
       1/sqrt(d)); query head h reads KV head h // (Hq / Hkv).
   R10 Prefill causality is per token: a query at position p sees keys at
       positions <= p inside its selected blocks.
+  R11 Baseline multi-head selector (decode): the G query heads of a KV group
+      each score the candidates against the compressed keys, the G score rows
+      are summed, the sum times the attention scale goes through a softmax over
+      the candidates, and the top-k of the softmax weights (R6 ties) is united
+      with the initial and local blocks as in R3-R5.  The pages give the
+      selector for one query; prefill is not covered.
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 (brute force, closed forms, textbook special cases, hand-worked fixtures under
 tests/golden/).  None is "parity unpinned".
@@ -182,6 +188,50 @@ def decode_select(f, kc, seq_len, topk: int, n_init: int, n_local: int, block: i
             tops.append(top)
             all_scores.append(scores)
     return Selection(idx, cnt, tops, all_scores)
+
+
+def multihead_select_decode(q, kc, seq_len, topk: int, n_init: int, n_local: int, block: int,
+                            scale: float) -> Selection:
+    """Baseline selector of the InfLLM-V2 / NSA / MoBA shape, one decode step.
+
+    [EXPL] "One Forecast head per GQA group", the baseline selector listing
+    (Sec. 3.1): every query head of the group scores every candidate block,
+    the per-head scores are summed into a shared score, a softmax of the
+    shared score divided by sqrt(d) weights the candidates, and the top-k of
+    those weights is taken.  Reading R11 (scale given, normally 1/sqrt(d));
+    candidate and union rules as decode_select.  q: [B, Hq, d] (the layer's
+    own queries, query head h in group h // (Hq / Hkv)); kc: [B, Hkv, NB, d].
+    Selection.scores holds the softmax weights.
+    """
+    q = _f64(q)
+    kc = _f64(kc)
+    B, Hq, d = q.shape
+    H = kc.shape[1]
+    G = Hq // H
+    lens = np.asarray(seq_len, dtype=np.int64)
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H), dtype=np.int64)
+    tops, all_w = [], []
+    for b in range(B):
+        cur = (int(lens[b]) - 1) // block
+        init, local, cand = block_sets(cur, n_init, n_local)
+        for g in range(H):
+            shared = {j: 0.0 for j in cand}
+            for h in range(g * G, (g + 1) * G):          # G score rows, summed
+                for j in cand:
+                    shared[j] += float(np.dot(q[b, h], kc[b, g, j]))
+            w = {}
+            if cand:
+                z = np.array([shared[j] * scale for j in cand])
+                e = np.exp(z - z.max())
+                e /= e.sum()
+                w = {j: float(e[i]) for i, j in enumerate(cand)}
+            top = rank_topk(w, topk)
+            idx[b, g], cnt[b, g] = _union(init, local, top, cap)
+            tops.append(top)
+            all_w.append(w)
+    return Selection(idx, cnt, tops, all_w)
 
 
 def prefill_select(f_tok, kc, q_start: int, topk: int, n_init: int, n_local: int, block: int) -> Selection:

@@ -106,6 +106,71 @@ def test_golden_decode_select_and_attend(golden_dir):
     np.testing.assert_allclose(out[0, 0], gx["out_expected"], rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- baseline multi-head selector
+def test_golden_multihead_select(golden_dir):
+    gx = _load(golden_dir, "multihead_select_hand.json")
+    d = gx["d"]
+    nb = gx["seq_len"] // gx["block"]
+    kc = np.zeros((1, 1, nb, d))
+    for j, row in gx["kc_rows"].items():
+        kc[0, 0, int(j)] = row
+    q = np.array(gx["q"], dtype=np.float64).reshape(1, 2, d)
+    for case in gx["cases"]:
+        sel = orc.multihead_select_decode(q, kc, [gx["seq_len"]], case["topk"], gx["n_init"], gx["n_local"],
+                                          gx["block"], 1.0 / math.sqrt(d))
+        assert sel.top[0] == case["top_expected"]
+        assert sel.idx[0, 0].tolist()[: case["cnt_expected"]] == case["idx_expected"]
+        assert int(sel.cnt[0, 0]) == case["cnt_expected"]
+        for j, w in gx["weights_expected"].items():
+            assert abs(sel.scores[0][int(j)] - w) < 2e-6
+
+
+@pytest.mark.parametrize("seed,G", [(0, 4), (1, 2), (2, 8)])
+def test_multihead_select_equals_forecast_select_of_summed_queries(seed, G):
+    """Summing the G per-head score rows equals one dot product with the
+    summed query (linearity), and the softmax is monotone: the baseline's
+    sets equal the Forecast selector's with F = the group's summed query,
+    grouped by the attention map (query head h in KV head h // G), computed
+    here with torch from the same tensors."""
+    B, H, d, T, k = 2, 2, 32, 64 * 40, 6
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H * G, d, generator=g, dtype=torch.float64)
+    kc = torch.randn(B, H, T // 64, d, generator=g, dtype=torch.float64)
+    lens = [T, T - 64 * 9 - 3]
+    f = q.view(B, H, G, d).sum(2)
+    base = orc.multihead_select_decode(q.numpy(), kc.numpy(), lens, k, 1, 2, 64, 1 / math.sqrt(d))
+    ref = orc.decode_select(f.numpy(), kc.numpy(), lens, k, 1, 2, 64)
+    np.testing.assert_array_equal(base.idx, ref.idx)
+    np.testing.assert_array_equal(base.cnt, ref.cnt)
+    assert base.top == ref.top
+    # the weights are the softmax over the candidates of (summed score) * scale
+    for i in range(B * H):
+        cand = sorted(ref.scores[i])
+        z = torch.tensor([ref.scores[i][j] for j in cand], dtype=torch.float64) / math.sqrt(d)
+        w = torch.softmax(z, 0).numpy()
+        np.testing.assert_allclose([base.scores[i][j] for j in cand], w, rtol=1e-12, atol=1e-15)
+
+
+def test_multihead_select_single_head_and_head_order():
+    """G = 1: the baseline ranks the query's raw scores, i.e. the Forecast
+    selector with F = q.  Reordering the heads inside a group changes nothing;
+    moving a head to another group does."""
+    B, d, T, k = 1, 16, 64 * 30, 5
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn(B, 2, d, generator=g, dtype=torch.float64)
+    kc = torch.randn(B, 2, T // 64, d, generator=g, dtype=torch.float64)
+    one = orc.multihead_select_decode(q.numpy(), kc.numpy(), [T], k, 1, 2, 64, 0.25)
+    ref = orc.decode_select(q.numpy(), kc.numpy(), [T], k, 1, 2, 64)
+    np.testing.assert_array_equal(one.idx, ref.idx)
+    q4 = torch.randn(B, 4, d, generator=g, dtype=torch.float64)
+    kc2 = kc.clone()
+    a = orc.multihead_select_decode(q4[:, [0, 1, 2, 3]].numpy(), kc2.numpy(), [T], k, 1, 2, 64, 0.25)
+    b = orc.multihead_select_decode(q4[:, [1, 0, 3, 2]].numpy(), kc2.numpy(), [T], k, 1, 2, 64, 0.25)
+    np.testing.assert_array_equal(a.idx, b.idx)
+    c = orc.multihead_select_decode(q4[:, [0, 2, 1, 3]].numpy(), kc2.numpy(), [T], k, 1, 2, 64, 0.25)
+    assert not np.array_equal(a.idx, c.idx)
+
+
 def test_golden_attention_gqa(golden_dir):
     gx = _load(golden_dir, "attention_gqa_hand.json")
     k = np.array(gx["keys"], dtype=np.float64)[None]         # [1, 2, 2, 2]
