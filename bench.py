@@ -114,6 +114,7 @@ class DecodeBench:
         self.ws_score = z(bskv.workspace_bytes("score", B, H, 0, nb, d))
         self.ws_attn = z(bskv.workspace_bytes("attn", B, wl.Hq, H, d, wl.U))
         self.ws_layer = z(bskv.workspace_bytes("layer", B, wl.Hq, H, d, wl.hidden, nb, wl.U, dt))
+        self.ws_mh = z(bskv.workspace_bytes("multihead", B, H, nb))
         torch.cuda.synchronize()
 
     # the four per-layer launches
@@ -135,6 +136,21 @@ class DecodeBench:
         lay = self.layers[l]
         self.bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], self.idx[l], self.cnt[l], lay["seq_len"],
                                            self.wl.scale, out=self.out[l], ws=self.ws_attn)
+
+    def mh_select(self, l):
+        """Baseline selector of layer l from its own queries (comparison only)."""
+        wl, lay = self.wl, self.layers[l]
+        self.bskv.multihead_block_score_topk(lay["q"], self.kc[l], wl.topk, wl.n_init, wl.n_local, lay["seq_len"],
+                                             scale=wl.scale, idx=self.idx[l], cnt=self.cnt[l], ws=self.ws_mh)
+
+    def step_baseline(self):
+        """The serial order of a same-layer selector: layer l's blocks are
+        chosen from layer l's queries, so selection and attention of a layer
+        run one after the other (no lookahead)."""
+        for l in range(self.L):
+            self.meanpool(l)
+            self.mh_select(l)
+            self.attend(l)
 
     def layer(self, l, stages=7):
         """Layer l: newest-block update, attention over B_l, and (lookahead)
@@ -306,6 +322,51 @@ def measured_gemm_tflops(torch, n=8192):
     return round(2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
 
 
+def baseline_comparison(torch, bench, step_s, kt, args):
+    """Same-GPU comparison with the baseline multi-head selector: its
+    selection cost per layer against the Forecast selector's (both as
+    separate score + top-k launches over all layers), and a whole step in the
+    baseline's serial order against the lookahead step."""
+    def per_layer_us(fn, reps=3):
+        def body():
+            for _ in range(reps):
+                for l in range(bench.L):
+                    fn(l)
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (reps * bench.L)
+
+    mh_us = per_layer_us(bench.mh_select)
+    serial_s, _ = time_graph(torch, bench.step_baseline, max(5, args.steps // 5), 2, use_graph=not args.no_graph)
+    # leave the lookahead lists in place for whoever runs next
+    bench.proj(0)
+    bench.select(0)
+    for l in range(bench.L):
+        bench.layer(l)
+    torch.cuda.synchronize()
+    fs_us = kt["score_topk"] * 1e6
+    return {
+        "what": "multi-head selector (per-head scores summed, softmax, top-k) from the layer's own queries, "
+                "then attention, layer after layer (no lookahead)",
+        "select_us_per_layer": round(mh_us, 3), "forecast_select_us_per_layer": round(fs_us, 3),
+        "select_ratio": round(mh_us / fs_us, 3),
+        "serial_step_ms": round(serial_s * 1e3, 4), "serial_tokens_per_s": round(bench.B / serial_s, 2),
+        "step_ratio": round(serial_s / step_s, 3),
+    }
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -431,6 +492,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
     ach = bpl[dom] / kt[dom] / 1e9
     peaks = measured_hbm_peaks(torch)
     sweep = selection_sweep(torch, bench)
+    base_cmp = baseline_comparison(torch, bench, step_s, kt, args) if wl.hidden else None
     # replicas: independent copies of one layer's inputs, rotated so that the
     # working set does not sit in the 256 MB cache; the step then covers
     # `replicas` layer-steps of a one-layer model
@@ -454,6 +516,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
         "value_without_proj": round(bench.B / (t_step - proj_s), 2),
         "measured_peaks": dict(peaks, roofline_frac_of_copy=round(ach / peaks["copy_GBps"], 4)),
         "select_us_per_layer_vs_T": sweep,
+        "baseline_selector": base_cmp,
         "kernels": kernels,
     }
     if replicas is not None:

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     host_device_pointer,
     kv_block_meanpool,
     lib,
+    multihead_block_score_topk,
     prefetch_selected_blocks,
     workspace_bytes,
 )

@@ -33,6 +33,9 @@ _proto("bskv_kv_block_meanpool", _i, _p, _i, ctypes.POINTER(_i64), _i64, _i, _i,
 _proto("bskv_score_topk_workspace", _sz, _i, _i, _i, _i64, _i)
 _proto("bskv_forecast_block_score_topk", _i, _p, _i, _i, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
        _p, _sz, _p)
+_proto("bskv_multihead_score_topk_workspace", _sz, _i, _i, _i64)
+_proto("bskv_multihead_block_score_topk", _i, _p, _i, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p,
+       _p, _sz, _p)
 _proto("bskv_attn_decode_workspace", _sz, _i, _i, _i, _i, _i)
 _proto("bskv_block_sparse_attn_decode", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _i, _p, _p, _p, _i, _i, _i,
        _i, _i, _i, _f, _p, _p, _sz, _p)
@@ -90,7 +93,8 @@ _WS: dict = {}
 
 def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
-          "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace}[kind]
+          "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace,
+          "multihead": lib.bskv_multihead_score_topk_workspace}[kind]
     return int(fn(*args))
 
 
@@ -165,6 +169,31 @@ def forecast_block_score_topk(f, kc, topk: int, n_init: int, n_local: int, seq_l
                                               64, topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), ws_ptr,
                                               ws_n, sh), "forecast_block_score_topk")
     return (idx, cnt, scores) if return_scores else (idx, cnt)
+
+
+def multihead_block_score_topk(q, kc, topk: int, n_init: int, n_local: int, seq_len, scale: float | None = None,
+                               return_weights: bool = False, idx=None, cnt=None, ws=None, stream=None):
+    """Baseline multi-head selection (decode) from the layer's own queries q
+    [B, Hq, d]: (idx int32 [B, Hkv, U], cnt int32 [B, Hkv]) [, weights]."""
+    B, H, nb_cap, d = kc.shape
+    U = topk + n_init + n_local
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    sh = _stream(stream, q.device)
+    idx = idx if idx is not None else torch.empty(B, H, U, dtype=torch.int32, device=q.device)
+    cnt = cnt if cnt is not None else torch.empty(B, H, dtype=torch.int32, device=q.device)
+    weights = None
+    if return_weights:
+        weights = torch.full((B, H, nb_cap), float("nan"), dtype=torch.float32, device=q.device)
+    lay = (B, H, nb_cap)
+    nbytes = workspace_bytes("multihead", *lay)
+    ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "multihead", lay)
+    _check(lib.bskv_multihead_block_score_topk(_ptr(q), _dt(q), _ptr(kc), nb_cap, _ptr(seq_len), B, q.shape[1], H, d,
+                                               64, topk, n_init, n_local, scale, _ptr(idx), _ptr(cnt),
+                                               _ptr(weights), _ptr(ws), ws.numel() * ws.element_size(), sh),
+           "multihead_block_score_topk")
+    return (idx, cnt, weights) if return_weights else (idx, cnt)
 
 
 def block_sparse_attn_decode(q, k, v, idx, cnt, seq_len, scale: float | None = None, ring: bool = False, out=None,

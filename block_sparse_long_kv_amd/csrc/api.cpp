@@ -131,6 +131,31 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
   return finish(bskv::launch_score_topk(a));
 }
 
+size_t bskv_multihead_score_topk_workspace(int B, int n_kv_heads, int64_t kc_nb_cap) {
+  if (B <= 0 || n_kv_heads <= 0 || kc_nb_cap <= 0) return 0;
+  return bskv::multihead_select_workspace_bytes(B, n_kv_heads, kc_nb_cap);
+}
+
+int bskv_multihead_block_score_topk(const void* q, int q_dtype, const float* kc, int64_t kc_nb_cap,
+                                    const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+                                    int block, int topk, int n_init, int n_local, float scale, int32_t* idx_out,
+                                    int32_t* cnt_out, float* weights_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!dtype_ok(q_dtype)) return BSKV_EDTYPE;
+  if (!q || !kc || !seq_len || !idx_out || !cnt_out || !ws) return BSKV_EINVAL;
+  if (!aligned16(kc) || !aligned16(ws)) return BSKV_EINVAL;
+  if (B <= 0 || kc_nb_cap <= 0 || topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (kc_nb_cap > bskv::kMaxCandidates || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  if (ws_bytes < bskv::multihead_select_workspace_bytes(B, n_kv_heads, kc_nb_cap)) return BSKV_ENOSPC;
+  bskv::MultiheadSelectArgs a{q, q_dtype, kc, kc_nb_cap, seq_len, B, n_kv_heads, n_q_heads / n_kv_heads, head_dim,
+                              topk, n_init, n_local, topk + n_init + n_local, scale, idx_out, cnt_out, weights_out,
+                              ws, stream};
+  return finish(bskv::launch_multihead_select(a));
+}
+
 size_t bskv_attn_decode_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int U) {
   if (B <= 0 || U <= 0 || !group_ok(n_q_heads, n_kv_heads) || head_dim <= 0) return 0;
   return bskv::attn_decode_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, U);

@@ -38,6 +38,17 @@ size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, 
 hipError_t launch_score_topk(const ScoreTopkArgs& a);
 constexpr int kMaxCandidates = 12288;  // candidate blocks per problem (48 KB of LDS keys)
 
+struct MultiheadSelectArgs {
+  const void* q; int q_dtype;
+  const float* kc; int64_t nb_cap; const int64_t* seq_len;
+  int B, H, G, D, topk, n_init, n_local, U; float scale;
+  int32_t* idx; int32_t* cnt; float* weights;
+  void* ws;
+  hipStream_t stream;
+};
+size_t multihead_select_workspace_bytes(int B, int H, int64_t nb_cap);
+hipError_t launch_multihead_select(const MultiheadSelectArgs& a);
+
 struct AttnDecodeArgs {
   const void* q; const void* k; const void* v; int dtype;
   int64_t sb, sg, st; int64_t kv_len; int ring;

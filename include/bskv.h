@@ -148,8 +148,8 @@ int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, 
  *   (sum_t F_t) . kc[j]).  seq_len is ignored.  idx_out [B, Hkv, n_qb, U],
  *   cnt_out [B, Hkv, n_qb], n_qb = ceil(n_q_tokens/block); scores_out must
  *   be NULL.
- * kc must hold compressed keys for every candidate block.  The candidate
- * count per problem is limited to 16384 (a 1M-token context).
+ * kc must hold compressed keys for every candidate block; kc_nb_cap is
+ * limited to 12288 blocks (a 786432-token context).
  * ws: bskv_score_topk_workspace() bytes (may be 0 bytes for prefill).
  * Decode runs two launches: candidate scores in slices, then one top-k
  * workgroup per (b, g); prefill runs one workgroup per query block.
@@ -160,6 +160,38 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
                                    int n_kv_heads, int head_dim, int block, int topk, int n_init,
                                    int n_local, int32_t* idx_out, int32_t* cnt_out, float* scores_out,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * Baseline multi-head block selector (decode), the comparison point of the
+ * Forecast selector.
+ * "SparDA: a fourth projection that lets sparse attention prefetch its own
+ * KV cache" -- "One Forecast head per GQA group", baseline selector listing
+ * (Sec. 3.1): every query head of a KV group scores every candidate block
+ * against the compressed keys, the per-head scores are summed, a softmax of
+ * the sum times `scale` (normally 1/sqrt(head_dim)) weights the candidates,
+ * and the top-k of the weights is united with the initial and local blocks.
+ *
+ * q        [B, n_q_heads, head_dim], F32 or BF16 (q_dtype): the layer's own
+ *          queries; query head h belongs to KV head h / (n_q_heads/n_kv_heads)
+ * kc       [B, n_kv_heads, kc_nb_cap, head_dim] fp32 compressed keys
+ * seq_len  [B] int64; the query is the last cached token (as in decode above)
+ * Candidates, ties, union, padding, idx_out/cnt_out layouts and the 12288
+ * block limit are those of bskv_forecast_block_score_topk (decode); the
+ * ranking is by softmax weight (descending), then block id (ascending).
+ * weights_out (nullable) [B, n_kv_heads, kc_nb_cap] fp32: the softmax weight
+ *          of every candidate; other entries untouched.
+ * n_q_heads/n_kv_heads must be 1, 2, 4 or 8; head_dim 64 or 128; block 64;
+ * n_init >= 1, n_local >= 1, topk >= 0, scale > 0.
+ * ws: bskv_multihead_score_topk_workspace() bytes (the shared scores); needs
+ * no initialisation.  Two launches: score slices, then one softmax + top-k
+ * workgroup per (b, g).  Errors as everywhere (nothing launched on error).
+ * ----------------------------------------------------------------------- */
+size_t bskv_multihead_score_topk_workspace(int B, int n_kv_heads, int64_t kc_nb_cap);
+int bskv_multihead_block_score_topk(const void* q, int q_dtype, const float* kc, int64_t kc_nb_cap,
+                                    const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+                                    int block, int topk, int n_init, int n_local, float scale, int32_t* idx_out,
+                                    int32_t* cnt_out, float* weights_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
  * a4  Block-sparse decode attention.  [EXPL] "The fourth projection", Eq. 5

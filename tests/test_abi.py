@@ -100,6 +100,34 @@ def test_score_topk_validation():
     assert call(nq=2048, sc=P) == EINVAL        # no debug scores in prefill
 
 
+def test_multihead_select_validation():
+    f = lib.bskv_multihead_block_score_topk
+    ws = lib.bskv_multihead_score_topk_workspace(8, 8, 2048)
+    assert ws >= 64 * 2048 * 4
+    assert lib.bskv_multihead_score_topk_workspace(0, 8, 2048) == 0
+    args = dict(q=P, dt=1, kc=P, cap=2048, sl=P, B=8, Hq=32, H=8, d=128, blk=64, k=64, ni=1, nl=4, sc=0.088,
+                idx=P, cnt=P, w=None, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["q"], a["dt"], a["kc"], a["cap"], a["sl"], a["B"], a["Hq"], a["H"], a["d"], a["blk"], a["k"],
+                 a["ni"], a["nl"], a["sc"], a["idx"], a["cnt"], a["w"], a["ws"], a["wsb"], None)
+    assert call(dt=5) == EDTYPE
+    assert call(q=None) == EINVAL
+    assert call(sl=None) == EINVAL
+    assert call(kc=MIS) == EINVAL
+    assert call(nl=0) == EINVAL
+    assert call(ni=0) == EINVAL
+    assert call(k=-1) == EINVAL
+    assert call(sc=0.0) == EINVAL
+    assert call(sc=float("nan")) == EINVAL
+    assert call(Hq=24) == EUNSUP                # group size 3
+    assert call(d=96) == EUNSUP
+    assert call(blk=32) == EUNSUP
+    assert call(cap=20000) == EUNSUP
+    assert call(wsb=ws - 4) == ENOSPC
+
+
 def test_attn_decode_validation():
     f = lib.bskv_block_sparse_attn_decode
     ws = lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69)

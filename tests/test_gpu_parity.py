@@ -188,6 +188,56 @@ def test_decode_selection_repeatable():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+# ----------------------------------------------------------------------------- baseline multi-head selector
+@pytest.mark.parametrize("dtype,d,G,topk,lens", [("bf16", 128, 4, 32, [64 * 512] * 4),
+                                                 ("f32", 64, 2, 8, [64 * 40, 64 * 33 + 17, 100, 64 * 40 - 1]),
+                                                 ("bf16", 64, 8, 16, [64 * 300, 64 * 150 + 1]),
+                                                 ("f32", 128, 1, 64, [64 * 2048])])
+def test_multihead_select_decode(dtype, d, G, topk, lens):
+    """The baseline selector (per-head scores summed, softmax, top-k) against
+    the oracle: lists equal outside the near-tie band, softmax weights to
+    float32 accuracy.  Ragged lengths, one with fewer candidates than k."""
+    B, Hkv = len(lens), 2
+    T = max(lens) + 64
+    g = torch.Generator().manual_seed(100 + d + G)
+    q = torch.randn(B, Hkv * G, d, generator=g).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(q.dtype)
+    seq_len = torch.tensor(lens, dtype=torch.int64)
+    kc = _kc_gpu(k.to(DEV), seq_len.to(DEV))
+    idx, cnt, w = bskv.multihead_block_score_topk(q.to(DEV), kc, topk, 1, 4, seq_len.to(DEV), return_weights=True)
+    torch.cuda.synchronize()
+    kc_or = orc.kv_block_meanpool(np64(k), 64, seq_len=seq_len.numpy())
+    sel = orc.multihead_select_decode(np64(q), kc_or, seq_len.numpy(), topk, 1, 4, 64, 1.0 / math.sqrt(d))
+    assert check_selection(idx, cnt, sel, topk) == 0
+    wn = w.cpu().numpy()
+    for i, ws in enumerate(sel.scores):
+        b, gg = divmod(i, Hkv)
+        for j, wt in ws.items():
+            assert abs(wn[b, gg, j] - wt) < 1e-5 + 1e-4 * wt, (b, gg, j)
+
+
+def test_multihead_select_matches_forecast_select_on_summed_queries():
+    """Linearity on the GPU path: the baseline's lists equal the Forecast
+    selector's with F = the fp32 sum of each group's queries."""
+    B, Hkv, G, d, T = 4, 8, 4, 128, 64 * 1024
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(B, Hkv * G, d, generator=g)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    seq_len = torch.full((B,), T, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(k.to(DEV), seq_len)
+    i1, c1 = bskv.multihead_block_score_topk(q.to(DEV), kc, 64, 1, 4, seq_len)
+    i2, c2 = bskv.forecast_block_score_topk(q.view(B, Hkv, G, d).sum(2).to(DEV).contiguous(), kc, 64, 1, 4,
+                                            seq_len=seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    # the two paths add the same products in different fp32 orders: a row may
+    # differ only by a swap at the k-th place
+    a, b = i1.cpu().numpy(), i2.cpu().numpy()
+    rows = [(set(a[r, h]) ^ set(b[r, h])) for r in range(B) for h in range(Hkv)]
+    assert all(len(x) <= 2 for x in rows)
+    assert sum(1 for x in rows if x) <= 2
+
+
 # ----------------------------------------------------------------------------- a4 decode
 def _attn_case(seed, B, Hq, Hkv, d, T, dtype, lens, topk, n_local):
     c = _gpu(random_decode_case(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens, plant=topk,
