@@ -10,12 +10,15 @@ from .sparda_ref import (  # noqa: F401
     attend_prefill,
     block_sets,
     decode_select,
+    decode_select_windows,
     decode_step_lookahead,
     forecast_proj,
     gather_selected_blocks,
     kth_gap,
     kv_block_meanpool,
+    kv_window_meanpool,
     multihead_select_decode,
     prefill_select,
     rank_topk,
+    window_block_scores,
 )

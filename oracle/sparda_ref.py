@@ -38,6 +38,12 @@ function that uses it):
       1/sqrt(d)); query head h reads KV head h // (Hq / Hkv).
   R10 Prefill causality is per token: a query at position p sees keys at
       positions <= p inside its selected blocks.
+  R15 Overlapping compression (the variant the evaluated models run): a
+      compressed key per window of `window` tokens every `stride` tokens
+      (32 and 16), mean-pooled; only complete windows exist.  A block's score
+      is the maximum of the scores of the windows that share at least one
+      token with it (windows 4j-1 .. 4j+3 of block j at 32/16); with
+      window = stride = block it is the plain block mean of R1.
   R11 Baseline multi-head selector (decode): the G query heads of a KV group
       each score the candidates against the compressed keys, the G score rows
       are summed, the sum times the attention scale goes through a softmax over
@@ -105,6 +111,71 @@ def kv_block_meanpool(k, block: int, seq_len=None) -> np.ndarray:
             for j in range(n_complete):
                 out[b, g, j] = k[b, g, block * j: block * (j + 1)].mean(axis=0)
     return out
+
+
+def kv_window_meanpool(k, window: int, stride: int, seq_len=None) -> np.ndarray:
+    """K~w[b, g, w, :] = mean of the keys at positions stride*w .. stride*w +
+    window - 1, for every complete window.
+
+    [EXPL] "One Forecast head per GQA group", closing paragraph: the
+    evaluated models pool keys with a 32-token window at stride 16; reading
+    R15.  k: [B, Hkv, T, d]; seq_len: optional [B].  Returns
+    [B, Hkv, (T - window) // stride + 1, d]; windows that are not complete
+    for batch b are NaN.
+    """
+    k = _f64(k)
+    B, H, T, d = k.shape
+    nw = (T - window) // stride + 1 if T >= window else 0
+    lens = np.full(B, T, dtype=np.int64) if seq_len is None else np.asarray(seq_len, dtype=np.int64)
+    out = np.full((B, H, nw, d), np.nan)
+    for b in range(B):
+        L = min(int(lens[b]), T)
+        for g in range(H):
+            for w in range(nw):
+                if stride * w + window <= L:
+                    out[b, g, w] = k[b, g, stride * w: stride * w + window].mean(axis=0)
+    return out
+
+
+def window_block_scores(f_vec, kcw_bg, blocks, block: int, window: int, stride: int) -> dict:
+    """Block score = max over the windows sharing a token with the block of
+    f . K~w (reading R15).  kcw_bg: [NW, d] (NaN rows are incomplete windows,
+    which take no part); blocks: candidate block ids."""
+    out = {}
+    nw = kcw_bg.shape[0]
+    for j in blocks:
+        best = -np.inf
+        for w in range(nw):
+            lo, hi = stride * w, stride * w + window          # window tokens [lo, hi)
+            if hi > block * j and lo < block * (j + 1) and not np.isnan(kcw_bg[w, 0]):
+                best = max(best, float(np.dot(f_vec, kcw_bg[w])))
+        out[j] = best
+    return out
+
+
+def decode_select_windows(f, kcw, seq_len, topk: int, n_init: int, n_local: int, block: int, window: int,
+                          stride: int) -> Selection:
+    """decode_select with the overlapping compression of R15: candidates,
+    ties and union as in decode_select, block scores max-pooled from the
+    window scores.  f: [B, Hkv, d]; kcw: [B, Hkv, NW, d]."""
+    f = _f64(f)
+    kcw = _f64(kcw)
+    B, H, d = f.shape
+    lens = np.asarray(seq_len, dtype=np.int64)
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H), dtype=np.int64)
+    tops, all_scores = [], []
+    for b in range(B):
+        cur = (int(lens[b]) - 1) // block
+        init, local, cand = block_sets(cur, n_init, n_local)
+        for g in range(H):
+            scores = window_block_scores(f[b, g], kcw[b, g], cand, block, window, stride)
+            top = rank_topk(scores, topk)
+            idx[b, g], cnt[b, g] = _union(init, local, top, cap)
+            tops.append(top)
+            all_scores.append(scores)
+    return Selection(idx, cnt, tops, all_scores)
 
 
 # --------------------------------------------------------------------------

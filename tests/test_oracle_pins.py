@@ -106,6 +106,75 @@ def test_golden_decode_select_and_attend(golden_dir):
     np.testing.assert_allclose(out[0, 0], gx["out_expected"], rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- overlapping compression (R15)
+def test_golden_window_select(golden_dir):
+    gx = _load(golden_dir, "window_select_hand.json")
+    T = gx["T"]
+    k = np.array(gx["keys"], dtype=np.float64).reshape(1, 1, T, 1)
+    kcw = orc.kv_window_meanpool(k, gx["window"], gx["stride"], seq_len=[gx["seq_len"]])
+    np.testing.assert_array_equal(kcw[0, 0, :, 0], np.array(gx["windows_expected"]))
+    f = np.ones((1, 1, 1))
+    for case in gx["cases"]:
+        sel = orc.decode_select_windows(f, kcw, [gx["seq_len"]], case["topk"], gx["n_init"], gx["n_local"],
+                                        gx["block"], gx["window"], gx["stride"])
+        assert {str(j): v for j, v in sel.scores[0].items()} == gx["scores_expected"]
+        assert sel.top[0] == case["top_expected"]
+        assert sel.idx[0, 0].tolist()[: case["cnt_expected"]] == case["idx_expected"]
+        assert int(sel.cnt[0, 0]) == case["cnt_expected"]
+
+
+def test_window_meanpool_against_prefix_sums():
+    """Window means from cumulative sums (an independent formula), ragged
+    lengths: incomplete windows are NaN."""
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn(2, 3, 64 * 9, 8, generator=g, dtype=torch.float64).numpy()
+    lens = [64 * 9, 64 * 5 + 40]
+    kcw = orc.kv_window_meanpool(k, 32, 16, seq_len=lens)
+    cs = np.concatenate([np.zeros((2, 3, 1, 8)), np.cumsum(k, axis=2)], axis=2)
+    for b, L in enumerate(lens):
+        for w in range(kcw.shape[2]):
+            if 16 * w + 32 <= L:
+                np.testing.assert_allclose(kcw[b, :, w], (cs[b, :, 16 * w + 32] - cs[b, :, 16 * w]) / 32, rtol=1e-12)
+            else:
+                assert np.isnan(kcw[b, :, w]).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_window_select_with_block_sized_windows_is_block_select(seed):
+    """window = stride = block: every block has exactly one window, itself,
+    so the variant is the plain block-mean selector (R1)."""
+    c = random_decode_case(seed, B=2, Hq=4, Hkv=2, d=16, T=64 * 30, seq_len=[64 * 30, 64 * 21 + 5])
+    k, f, lens = _np(c["k"]), _np(c["f"]), _np(c["seq_len"])
+    kcw = orc.kv_window_meanpool(k, 64, 64, seq_len=lens)
+    kc = orc.kv_block_meanpool(k, 64, seq_len=lens)
+    np.testing.assert_array_equal(np.isnan(kcw), np.isnan(kc))
+    np.testing.assert_allclose(np.nan_to_num(kcw), np.nan_to_num(kc), rtol=0, atol=1e-13)
+    a = orc.decode_select_windows(f, kcw, lens, 6, 1, 2, 64, 64, 64)
+    b = orc.decode_select(f, kc, lens, 6, 1, 2, 64)
+    np.testing.assert_array_equal(a.idx, b.idx)
+    assert a.top == b.top
+
+
+def test_window_select_spike_reaches_exactly_the_blocks_of_its_windows():
+    """A large key at token p enters the windows that contain p; with the
+    32/16 grid those windows touch block p // 64 and, for the 16 tokens at
+    either edge of a block, also the neighbouring block.  Brute force over
+    positions: the blocks whose score jumps are exactly those."""
+    T, d = 64 * 12, 4
+    base = np.zeros((1, 1, T, d))
+    f = np.ones((1, 1, d))
+    for p in (64 * 5 + 3, 64 * 5 + 20, 64 * 5 + 50, 64 * 6 + 63, 64 * 3):
+        k = base.copy()
+        k[0, 0, p] = 100.0
+        kcw = orc.kv_window_meanpool(k, 32, 16)
+        sc = orc.window_block_scores(f[0, 0], kcw[0, 0], list(range(1, 10)), 64, 32, 16)
+        hit = sorted(j for j, v in sc.items() if v > 1.0)
+        w_with_p = [w for w in range(kcw.shape[2]) if 16 * w <= p < 16 * w + 32]
+        expect = sorted({j for w in w_with_p for j in range(1, 10) if 16 * w < 64 * (j + 1) and 16 * w + 32 > 64 * j})
+        assert hit == expect, (p, hit, expect)
+        assert p // 64 in hit or p // 64 not in range(1, 10)
+
+
 # --------------------------------------------------------------------------- baseline multi-head selector
 def test_golden_multihead_select(golden_dir):
     gx = _load(golden_dir, "multihead_select_hand.json")
