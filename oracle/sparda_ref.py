@@ -141,15 +141,16 @@ def window_block_scores(f_vec, kcw_bg, blocks, block: int, window: int, stride: 
     """Block score = max over the windows sharing a token with the block of
     f . K~w (reading R15).  kcw_bg: [NW, d] (NaN rows are incomplete windows,
     which take no part); blocks: candidate block ids."""
-    out = {}
     nw = kcw_bg.shape[0]
+    lo = stride * np.arange(nw)                              # window w holds tokens [lo, lo + window)
+    hi = lo + window
+    done = ~np.isnan(kcw_bg[:, 0])
+    s = np.full(nw, -np.inf)
+    s[done] = kcw_bg[done] @ np.asarray(f_vec, dtype=np.float64)
+    out = {}
     for j in blocks:
-        best = -np.inf
-        for w in range(nw):
-            lo, hi = stride * w, stride * w + window          # window tokens [lo, hi)
-            if hi > block * j and lo < block * (j + 1) and not np.isnan(kcw_bg[w, 0]):
-                best = max(best, float(np.dot(f_vec, kcw_bg[w])))
-        out[j] = best
+        touch = (hi > block * j) & (lo < block * (j + 1)) & done
+        out[j] = float(s[touch].max()) if touch.any() else -np.inf
     return out
 
 
