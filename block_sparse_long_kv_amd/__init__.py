@@ -15,8 +15,10 @@ from ._lib import (  # noqa: F401
     decode_layer_lookahead,
     forecast_block_score_topk,
     forecast_proj,
+    forecast_window_score_topk,
     host_device_pointer,
     kv_block_meanpool,
+    kv_window_meanpool,
     lib,
     multihead_block_score_topk,
     prefetch_selected_blocks,

@@ -33,6 +33,11 @@ _proto("bskv_kv_block_meanpool", _i, _p, _i, ctypes.POINTER(_i64), _i64, _i, _i,
 _proto("bskv_score_topk_workspace", _sz, _i, _i, _i, _i64, _i)
 _proto("bskv_forecast_block_score_topk", _i, _p, _i, _i, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
        _p, _sz, _p)
+_proto("bskv_kv_window_meanpool", _i, _p, _i, ctypes.POINTER(_i64), _i64, _i, _i, _i, _i, _i, _p, _i64, _i64, _i, _p,
+       _i64, _p)
+_proto("bskv_window_score_topk_workspace", _sz, _i, _i, _i64)
+_proto("bskv_forecast_window_score_topk", _i, _p, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
+       _sz, _p)
 _proto("bskv_multihead_score_topk_workspace", _sz, _i, _i, _i64)
 _proto("bskv_multihead_block_score_topk", _i, _p, _i, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p,
        _p, _sz, _p)
@@ -94,7 +99,8 @@ _WS: dict = {}
 def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
           "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace,
-          "multihead": lib.bskv_multihead_score_topk_workspace}[kind]
+          "multihead": lib.bskv_multihead_score_topk_workspace,
+          "window": lib.bskv_window_score_topk_workspace}[kind]
     return int(fn(*args))
 
 
@@ -168,6 +174,46 @@ def forecast_block_score_topk(f, kc, topk: int, n_init: int, n_local: int, seq_l
     _check(lib.bskv_forecast_block_score_topk(_ptr(f), _dt(f), Tq, q_start, _ptr(kc), nb_cap, _ptr(seq_len), B, H, d,
                                               64, topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), ws_ptr,
                                               ws_n, sh), "forecast_block_score_topk")
+    return (idx, cnt, scores) if return_scores else (idx, cnt)
+
+
+def kv_window_meanpool(k, seq_len, kcw, window: int = 32, stride: int = 16, w_begin: int = 0,
+                       w_end: int | None = None, newest_only: bool = False, stream=None):
+    """Write kcw[b, g, w] = mean of the keys of window w (positions stride*w
+    .. stride*w+window-1) for the complete windows w in [w_begin, w_end)."""
+    B, H, _, d = k.shape
+    nw_cap = kcw.shape[2]
+    if w_end is None:
+        w_end = nw_cap
+    if kcw.dtype != torch.float32 or not kcw.is_contiguous() or tuple(kcw.shape) != (B, H, nw_cap, d):
+        raise ValueError("kcw must be contiguous fp32 [B, Hkv, nw_cap, d]")
+    sh = _stream(stream, k.device)
+    _check(lib.bskv_kv_window_meanpool(_ptr(k), _dt(k), _strides3(k), k.shape[2], B, H, d, window, stride,
+                                       _ptr(seq_len), w_begin, w_end, int(bool(newest_only)), _ptr(kcw), nw_cap, sh),
+           "kv_window_meanpool")
+    return kcw
+
+
+def forecast_window_score_topk(f, kcw, topk: int, n_init: int, n_local: int, seq_len, window: int = 32,
+                               stride: int = 16, return_scores: bool = False, idx=None, cnt=None, ws=None,
+                               stream=None):
+    """Decode selection on window-compressed keys (block score = max over the
+    block's windows): (idx int32 [B, Hkv, U], cnt int32 [B, Hkv]) [, block scores]."""
+    B, H, nw_cap, d = kcw.shape
+    U = topk + n_init + n_local
+    nb = ((nw_cap - 1) * stride + window) // 64
+    if not f.is_contiguous() or f.dtype != torch.float32:
+        raise ValueError("f must be contiguous fp32")
+    sh = _stream(stream, f.device)
+    idx = idx if idx is not None else torch.empty(B, H, U, dtype=torch.int32, device=f.device)
+    cnt = cnt if cnt is not None else torch.empty(B, H, dtype=torch.int32, device=f.device)
+    scores = torch.full((B, H, nb), float("nan"), dtype=torch.float32, device=f.device) if return_scores else None
+    lay = (B, H, nw_cap)
+    nbytes = workspace_bytes("window", *lay)
+    ws = ws if ws is not None else _workspace(f.device, nbytes, sh, "window", lay)
+    _check(lib.bskv_forecast_window_score_topk(_ptr(f), _ptr(kcw), nw_cap, _ptr(seq_len), B, H, d, 64, window, stride,
+                                               topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), _ptr(ws),
+                                               ws.numel() * ws.element_size(), sh), "forecast_window_score_topk")
     return (idx, cnt, scores) if return_scores else (idx, cnt)
 
 

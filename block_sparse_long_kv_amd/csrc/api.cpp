@@ -131,6 +131,55 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
   return finish(bskv::launch_score_topk(a));
 }
 
+namespace {
+bool window_grid_ok(int window, int stride) {
+  return (window == 32 || window == 64) && (stride == 16 || stride == 32 || stride == 64) && stride <= window &&
+         window % stride == 0;
+}
+// 64-token blocks whose windows all lie inside a window array of nw entries
+int64_t window_blocks(int64_t nw, int window, int stride) { return ((nw - 1) * stride + window) / 64; }
+}  // namespace
+
+int bskv_kv_window_meanpool(const void* k, int dtype, const int64_t* kv_strides, int64_t kv_len, int B,
+                            int n_kv_heads, int head_dim, int window, int stride, const int64_t* seq_len,
+                            int64_t w_begin, int64_t w_end, int newest_only, float* kcw, int64_t kcw_nw_cap,
+                            hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!k || !kcw || !seq_len || !aligned16(k) || !aligned16(kcw)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0 || kv_len < 0) return BSKV_EINVAL;
+  if (!strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || !window_grid_ok(window, stride)) return BSKV_EUNSUPPORTED;
+  if (w_begin < 0 || w_end < w_begin || w_end > kcw_nw_cap) return BSKV_EINVAL;
+  if (!newest_only && w_end - w_begin > 0x7fffffff) return BSKV_EUNSUPPORTED;
+  if ((int64_t)B > 65535 || n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  bskv::WindowMeanpoolArgs a{k, dtype, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, B, n_kv_heads, head_dim,
+                             window, stride, seq_len, w_begin, w_end, newest_only ? 1 : 0, kcw, kcw_nw_cap, stream};
+  return finish(bskv::launch_window_meanpool(a));
+}
+
+size_t bskv_window_score_topk_workspace(int B, int n_kv_heads, int64_t kcw_nw_cap) {
+  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0) return 0;
+  return bskv::window_select_workspace_bytes(B, n_kv_heads, kcw_nw_cap);
+}
+
+int bskv_forecast_window_score_topk(const float* f, const float* kcw, int64_t kcw_nw_cap, const int64_t* seq_len,
+                                    int B, int n_kv_heads, int head_dim, int block, int window, int stride, int topk,
+                                    int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out, float* scores_out,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!f || !kcw || !seq_len || !idx_out || !cnt_out || !ws) return BSKV_EINVAL;
+  if (!aligned16(f) || !aligned16(kcw) || !aligned16(ws)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0) return BSKV_EINVAL;
+  if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || block != 64 || !window_grid_ok(window, stride)) return BSKV_EUNSUPPORTED;
+  const int64_t nb_cap = window_blocks(kcw_nw_cap, window, stride);
+  if (nb_cap < 1) return BSKV_EINVAL;
+  if (nb_cap > bskv::kMaxCandidates || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  if (ws_bytes < bskv::window_select_workspace_bytes(B, n_kv_heads, kcw_nw_cap)) return BSKV_ENOSPC;
+  bskv::WindowSelectArgs a{f, kcw, kcw_nw_cap, nb_cap, seq_len, B, n_kv_heads, head_dim, window, stride, topk, n_init,
+                           n_local, topk + n_init + n_local, idx_out, cnt_out, scores_out, ws, stream};
+  return finish(bskv::launch_window_select(a));
+}
+
 size_t bskv_multihead_score_topk_workspace(int B, int n_kv_heads, int64_t kc_nb_cap) {
   if (B <= 0 || n_kv_heads <= 0 || kc_nb_cap <= 0) return 0;
   return bskv::multihead_select_workspace_bytes(B, n_kv_heads, kc_nb_cap);

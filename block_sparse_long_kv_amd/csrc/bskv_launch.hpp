@@ -38,6 +38,25 @@ size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, 
 hipError_t launch_score_topk(const ScoreTopkArgs& a);
 constexpr int kMaxCandidates = 12288;  // candidate blocks per problem (48 KB of LDS keys)
 
+struct WindowMeanpoolArgs {
+  const void* k; int dtype; int64_t sb, sg, st; int64_t kv_len;
+  int B, H, D, window, stride;
+  const int64_t* seq_len; int64_t w_begin, w_end; int newest_only;
+  float* kcw; int64_t nw_cap;
+  hipStream_t stream;
+};
+hipError_t launch_window_meanpool(const WindowMeanpoolArgs& a);
+
+struct WindowSelectArgs {
+  const float* f; const float* kcw; int64_t nw_cap; int64_t nb_cap; const int64_t* seq_len;
+  int B, H, D, window, stride, topk, n_init, n_local, U;
+  int32_t* idx; int32_t* cnt; float* scores;
+  void* ws;
+  hipStream_t stream;
+};
+size_t window_select_workspace_bytes(int B, int H, int64_t nw_cap);
+hipError_t launch_window_select(const WindowSelectArgs& a);
+
 struct MultiheadSelectArgs {
   const void* q; int q_dtype;
   const float* kc; int64_t nb_cap; const int64_t* seq_len;

@@ -204,7 +204,8 @@ struct MeanpoolSmem {
   float red[kThreads / (D / VecN<T>::N)][D + 4];
 };
 
-template <typename T, int D>
+// ROWS consecutive token rows (a 64-token block, or a 32-token window)
+template <typename T, int D, int ROWS = kBlk>
 __device__ __forceinline__ void meanpool_wg(const T* __restrict__ kblock, int64_t st, float* __restrict__ kc_row,
                             MeanpoolSmem<T, D>& sm) {
   constexpr int VEC = VecN<T>::N;
@@ -214,7 +215,8 @@ __device__ __forceinline__ void meanpool_wg(const T* __restrict__ kblock, int64_
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  constexpr int NR = kBlk / RPP;
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "rows must fill the row lanes");
   uint4 raw[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) raw[i] = ld16_nt(kblock + (int64_t)(r0 + i * RPP) * st + c * VEC);
@@ -232,7 +234,7 @@ __device__ __forceinline__ void meanpool_wg(const T* __restrict__ kblock, int64_
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < RPP; ++r) s += sm.red[r][t];
-    kc_row[t] = s / (float)kBlk;
+    kc_row[t] = s / (float)ROWS;
   }
 }
 

@@ -128,6 +128,41 @@ def test_multihead_select_validation():
     assert call(wsb=ws - 4) == ENOSPC
 
 
+def test_window_select_validation():
+    mp = lib.bskv_kv_window_meanpool
+    assert mp(P, 5, S3, 131072, 8, 8, 128, 32, 16, P, 0, 10, 0, P, 8191, None) == EDTYPE
+    assert mp(None, 1, S3, 131072, 8, 8, 128, 32, 16, P, 0, 10, 0, P, 8191, None) == EINVAL
+    assert mp(P, 1, S3, 131072, 8, 8, 128, 48, 16, P, 0, 10, 0, P, 8191, None) == EUNSUP   # window 48
+    assert mp(P, 1, S3, 131072, 8, 8, 128, 32, 64, P, 0, 10, 0, P, 8191, None) == EUNSUP   # stride > window
+    assert mp(P, 1, S3, 131072, 8, 8, 128, 64, 24, P, 0, 10, 0, P, 8191, None) == EUNSUP   # stride 24
+    assert mp(P, 1, S3, 131072, 8, 8, 96, 32, 16, P, 0, 10, 0, P, 8191, None) == EUNSUP
+    assert mp(P, 1, S3, 131072, 8, 8, 128, 32, 16, P, 5, 4, 0, P, 8191, None) == EINVAL    # w_end < w_begin
+    assert mp(P, 1, S3, 131072, 8, 8, 128, 32, 16, P, 0, 8192, 0, P, 8191, None) == EINVAL  # past the cap
+    f = lib.bskv_forecast_window_score_topk
+    ws = lib.bskv_window_score_topk_workspace(8, 8, 8191)
+    assert ws >= 64 * 8191 * 4
+    assert lib.bskv_window_score_topk_workspace(8, 0, 8191) == 0
+    args = dict(f=P, kcw=P, cap=8191, sl=P, B=8, H=8, d=128, blk=64, win=32, st=16, k=64, ni=1, nl=4, idx=P, cnt=P,
+                sc=None, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["f"], a["kcw"], a["cap"], a["sl"], a["B"], a["H"], a["d"], a["blk"], a["win"], a["st"], a["k"],
+                 a["ni"], a["nl"], a["idx"], a["cnt"], a["sc"], a["ws"], a["wsb"], None)
+    assert call(f=None) == EINVAL
+    assert call(kcw=MIS) == EINVAL
+    assert call(ni=0) == EINVAL
+    assert call(nl=0) == EINVAL
+    assert call(k=-1) == EINVAL
+    assert call(cap=0) == EINVAL
+    assert call(d=96) == EUNSUP
+    assert call(blk=32) == EUNSUP
+    assert call(win=16, st=16) == EUNSUP
+    assert call(win=32, st=64) == EUNSUP
+    assert call(cap=8 * 12288) == EUNSUP             # more than 12288 blocks
+    assert call(wsb=ws - 4) == ENOSPC
+
+
 def test_attn_decode_validation():
     f = lib.bskv_block_sparse_attn_decode
     ws = lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69)

@@ -238,6 +238,110 @@ def test_multihead_select_matches_forecast_select_on_summed_queries():
     assert sum(1 for x in rows if x) <= 2
 
 
+# ----------------------------------------------------------------------------- a2'/a3' windows
+def _kcw_gpu(k, seq_len, window, stride, nw_cap=None):
+    B, H, T, d = k.shape
+    nw_cap = nw_cap or (T - window) // stride + 1
+    kcw = torch.full((B, H, nw_cap, d), float("nan"), dtype=torch.float32, device=DEV)
+    bskv.kv_window_meanpool(k, seq_len, kcw, window, stride)
+    return kcw
+
+
+@pytest.mark.parametrize("dtype,d,window,stride", [("bf16", 128, 32, 16), ("f32", 64, 32, 16), ("bf16", 64, 64, 16),
+                                                   ("f32", 128, 32, 32), ("bf16", 128, 64, 64)])
+def test_window_meanpool_ragged(dtype, d, window, stride):
+    """Exactly the complete windows are written, each the mean of its keys."""
+    lens = [64 * 20, 64 * 20 - 1, 64 * 5 + 3, 1, 31, 48]
+    c = _gpu(random_decode_case(11, B=6, Hq=2, Hkv=2, d=d, T=64 * 20, dtype=dtype, seq_len=lens))
+    kcw = _kcw_gpu(c["k"], c["seq_len"], window, stride)
+    torch.cuda.synchronize()
+    want = orc.kv_window_meanpool(np64(c["k"]), window, stride, seq_len=lens)
+    got = np64(kcw)
+    done = ~np.isnan(want)
+    assert np.array_equal(done, ~np.isnan(got)), "exactly the complete windows are written"
+    assert max_abs(got[done], want[done]) < 1e-4
+
+
+def test_window_meanpool_newest_only_and_subrange():
+    lens = [64 * 9, 64 * 9 + 16, 64 * 3 + 5, 32, 16]
+    T, W, S = 64 * 12, 32, 16
+    nw = (T - W) // S + 1
+    c = _gpu(random_decode_case(12, B=5, Hq=4, Hkv=1, d=128, T=T, dtype="bf16", seq_len=lens))
+    want = orc.kv_window_meanpool(np64(c["k"]), W, S, seq_len=lens)
+    kcw = torch.full((5, 1, nw, 128), 7.0, dtype=torch.float32, device=DEV)
+    bskv.kv_window_meanpool(c["k"], c["seq_len"], kcw, W, S, newest_only=True)
+    torch.cuda.synchronize()
+    got = np64(kcw)
+    for b, L in enumerate(lens):
+        newest = (L - W) // S if L >= W and (L - W) % S == 0 else None
+        for w in range(nw):
+            if w == newest:
+                assert max_abs(got[b, 0, w], want[b, 0, w]) < 1e-4
+            else:
+                assert (got[b, 0, w] == 7.0).all(), (b, w)
+    kcw.fill_(7.0)
+    bskv.kv_window_meanpool(c["k"], c["seq_len"], kcw, W, S, w_begin=5, w_end=20)
+    torch.cuda.synchronize()
+    got = np64(kcw)
+    for b, L in enumerate(lens):
+        for w in range(nw):
+            if 5 <= w < 20 and S * w + W <= L:
+                assert max_abs(got[b, 0, w], want[b, 0, w]) < 1e-4
+            else:
+                assert (got[b, 0, w] == 7.0).all(), (b, w)
+
+
+@pytest.mark.parametrize("dtype,d,window,stride,topk,lens", [
+    ("bf16", 128, 32, 16, 16, [64 * 300, 64 * 150 + 1, 64 * 150 + 16, 64 * 150 + 40]),
+    ("f32", 64, 32, 16, 8, [64 * 40, 64 * 33 + 17, 100, 64 * 40 - 1]),
+    ("bf16", 64, 64, 16, 12, [64 * 200, 64 * 77 + 63]),
+    ("f32", 128, 32, 32, 64, [64 * 2048, 64 * 1000 + 31])])
+def test_window_select_decode(dtype, d, window, stride, topk, lens):
+    """Selection on window-compressed keys against the oracle: lists equal
+    outside the near-tie band, block scores (max over each block's complete
+    windows) to float32 accuracy.  Ragged lengths: the newest block's last
+    window may or may not be complete; one sequence has fewer candidates than k."""
+    B, Hkv = len(lens), 4
+    T = max(lens) + 64
+    g = torch.Generator().manual_seed(200 + d + window + stride)
+    f = torch.randn(B, Hkv, d, generator=g)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    seq_len = torch.tensor(lens, dtype=torch.int64)
+    kcw = _kcw_gpu(k.to(DEV), seq_len.to(DEV), window, stride)
+    idx, cnt, bs = bskv.forecast_window_score_topk(f.to(DEV), kcw, topk, 1, 4, seq_len.to(DEV), window, stride,
+                                                   return_scores=True)
+    torch.cuda.synchronize()
+    kcw_or = orc.kv_window_meanpool(np64(k), window, stride, seq_len=seq_len.numpy())
+    sel = orc.decode_select_windows(np64(f), kcw_or, seq_len.numpy(), topk, 1, 4, 64, window, stride)
+    assert check_selection(idx, cnt, sel, topk) <= 1
+    bn = bs.cpu().numpy()
+    for i, sc in enumerate(sel.scores):
+        b, gg = divmod(i, Hkv)
+        for j, want in sc.items():
+            assert abs(bn[b, gg, j] - want) < 1e-4 * (1 + abs(want)), (b, gg, j)
+
+
+def test_window_select_block_sized_windows_equal_block_selector():
+    """With 64-token windows at stride 64 the windows are the blocks: the
+    window path gives the block selector's compressed keys, lists and scores
+    bit for bit."""
+    B, Hkv, d, T = 3, 8, 128, 64 * 700
+    lens = [T, T - 30, 64 * 333]
+    g = torch.Generator().manual_seed(21)
+    f = torch.randn(B, Hkv, d, generator=g).to(DEV)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16).to(DEV)
+    seq_len = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(k, seq_len)
+    kcw = _kcw_gpu(k, seq_len, 64, 64)
+    i1, c1, s1 = bskv.forecast_window_score_topk(f, kcw, 32, 1, 4, seq_len, 64, 64, return_scores=True)
+    i2, c2 = bskv.forecast_block_score_topk(f, kc, 32, 1, 4, seq_len=seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.nan_to_num(-1.0), kcw.nan_to_num(-1.0))
+    assert torch.equal(c1, c2) and torch.equal(i1, i2)
+    sc = (kc[:, :, :, :] * f[:, :, None, :]).sum(-1)
+    assert torch.isfinite(s1[:, :, 1:300]).all() and max_abs(np64(s1[:, :, 1:300]), np64(sc[:, :, 1:300])) < 1e-3
+
+
 # ----------------------------------------------------------------------------- a4 decode
 def _attn_case(seed, B, Hq, Hkv, d, T, dtype, lens, topk, n_local):
     c = _gpu(random_decode_case(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens, plant=topk,
