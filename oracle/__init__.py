@@ -19,6 +19,7 @@ from .sparda_ref import (  # noqa: F401
     kv_window_meanpool,
     multihead_select_decode,
     prefill_select,
+    prefill_select_windows,
     rank_topk,
     window_block_scores,
 )

@@ -44,7 +44,11 @@ function that uses it):
       is the maximum of the scores of the windows that share at least one
       token with it (windows 4j-1 .. 4j+3 of block j at 32/16); with
       window = stride = block it is the plain block mean of R1.
-  R11 Baseline multi-head selector (decode): the G query heads of a KV group
+  R16 Overlapping compression in prefill: query block qb scores window w by
+      the sum over its tokens of F_t . K~w (R8 applied to windows) and
+      max-pools as in R15; a window takes part only if all its tokens precede
+      the query block (the decode rule of R15 at the block's first token).
+  R14 Baseline multi-head selector (decode): the G query heads of a KV group
       each score the candidates against the compressed keys, the G score rows
       are summed, the sum times the attention scale goes through a softmax over
       the candidates, and the top-k of the softmax weights (R6 ties) is united
@@ -270,7 +274,7 @@ def multihead_select_decode(q, kc, seq_len, topk: int, n_init: int, n_local: int
     (Sec. 3.1): every query head of the group scores every candidate block,
     the per-head scores are summed into a shared score, a softmax of the
     shared score divided by sqrt(d) weights the candidates, and the top-k of
-    those weights is taken.  Reading R11 (scale given, normally 1/sqrt(d));
+    those weights is taken.  Reading R14 (scale given, normally 1/sqrt(d));
     candidate and union rules as decode_select.  q: [B, Hq, d] (the layer's
     own queries, query head h in group h // (Hq / Hkv)); kc: [B, Hkv, NB, d].
     Selection.scores holds the softmax weights.
@@ -337,6 +341,51 @@ def prefill_select(f_tok, kc, q_start: int, topk: int, n_init: int, n_local: int
                 for j in cand:
                     per_token = rows @ kc[b, g, j]          # F_t . K~_j for each token t
                     scores[j] = float(per_token.sum())
+                top = rank_topk(scores, topk)
+                idx[b, g, qi], cnt[b, g, qi] = _union(init, local, top, cap)
+                tops.append(top)
+                all_scores.append(scores)
+    return Selection(idx, cnt, tops, all_scores)
+
+
+def prefill_select_windows(f_tok, kcw, q_start: int, topk: int, n_init: int, n_local: int, block: int, window: int,
+                           stride: int) -> Selection:
+    """prefill_select with the overlapping compression (reading R16).
+
+    [EXPL] "One Forecast head per GQA group", closing paragraph (32-token
+    windows at stride 16) and "Training" (window scores max-pooled to
+    blocks).  Query block qb scores window w by the sum over its tokens of
+    F_t . K~w; block j takes the maximum over the windows that share a token
+    with it and whose tokens all precede the query block (start of window
+    w + window <= qb * block).  Candidates, ties and union as prefill_select.
+    f_tok: [B, Hkv, Tq, d]; kcw: [B, Hkv, NW, d] (NaN rows: incomplete).
+    """
+    f_tok = _f64(f_tok)
+    kcw = _f64(kcw)
+    B, H, Tq, d = f_tok.shape
+    if q_start % block:
+        raise ValueError("q_start must be a multiple of block")
+    n_qb = -(-Tq // block)
+    nw = kcw.shape[2]
+    w_start = stride * np.arange(nw)                        # window w holds tokens [w_start, w_start + window)
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, n_qb, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H, n_qb), dtype=np.int64)
+    tops, all_scores = [], []
+    for b in range(B):
+        for g in range(H):
+            done = ~np.isnan(kcw[b, g, :, 0])
+            for qi in range(n_qb):
+                qb = q_start // block + qi
+                init, local, cand = block_sets(qb, n_init, n_local)
+                rows = f_tok[b, g, qi * block: min(Tq, (qi + 1) * block)]
+                seen = done & (w_start + window <= qb * block)
+                wsc = np.full(nw, -np.inf)
+                wsc[seen] = (rows @ kcw[b, g, seen].T).sum(axis=0)     # sum over tokens of F_t . K~w
+                scores = {}
+                for j in cand:
+                    touch = seen & (w_start + window > block * j) & (w_start < block * (j + 1))
+                    scores[j] = float(wsc[touch].max()) if touch.any() else -np.inf
                 top = rank_topk(scores, topk)
                 idx[b, g, qi], cnt[b, g, qi] = _union(init, local, top, cap)
                 tops.append(top)

@@ -175,6 +175,68 @@ def test_window_select_spike_reaches_exactly_the_blocks_of_its_windows():
         assert p // 64 in hit or p // 64 not in range(1, 10)
 
 
+# --------------------------------------------------------------------------- overlapping compression in prefill (R16)
+def test_golden_prefill_window_select(golden_dir):
+    gx = _load(golden_dir, "prefill_window_select_hand.json")
+    Tq = gx["Tq"]
+    k = np.array(gx["keys"], dtype=np.float64).reshape(1, 1, Tq, 1)
+    kcw = orc.kv_window_meanpool(k, gx["window"], gx["stride"])
+    f = np.array(gx["f"], dtype=np.float64).reshape(1, 1, Tq, 1)
+    for case in gx["cases"]:
+        sel = orc.prefill_select_windows(f, kcw, gx["q_start"], case["topk"], gx["n_init"], gx["n_local"],
+                                         gx["block"], gx["window"], gx["stride"])
+        assert {str(j): v for j, v in sel.scores[2].items()} == gx["scores_qb2_expected"]
+        assert {str(j): v for j, v in sel.scores[3].items()} == gx["scores_qb3_expected"]
+        for qi, (want, c) in enumerate(zip(case["idx_expected"], case["cnt_expected"])):
+            assert int(sel.cnt[0, 0, qi]) == c
+            assert sel.idx[0, 0, qi].tolist()[:c] == want
+
+
+def test_prefill_window_select_block_sized_windows_is_prefill_select():
+    """window = stride = block: the windows are the blocks and every complete
+    block precedes the query blocks that may select it, so the variant is the
+    plain prefill selector (R8)."""
+    g = torch.Generator().manual_seed(7)
+    k = torch.randn(2, 2, 64 * 12, 8, generator=g, dtype=torch.float64).numpy()
+    f = torch.randn(2, 2, 64 * 4 + 17, 8, generator=g, dtype=torch.float64).numpy()
+    kc = orc.kv_block_meanpool(k, 64)
+    kcw = orc.kv_window_meanpool(k, 64, 64)
+    a = orc.prefill_select_windows(f, kcw, 64 * 7, 3, 1, 2, 64, 64, 64)
+    b = orc.prefill_select(f, kc, 64 * 7, 3, 1, 2, 64)
+    np.testing.assert_array_equal(a.idx, b.idx)
+    np.testing.assert_array_equal(a.cnt, b.cnt)
+    assert a.top == b.top
+    for sa, sb in zip(a.scores, b.scores):
+        assert sa.keys() == sb.keys()
+        for j in sa:
+            assert abs(sa[j] - sb[j]) <= 1e-12 * (1 + abs(sb[j]))
+
+
+@pytest.mark.parametrize("window,stride,n_local", [(32, 16, 1), (32, 16, 3), (64, 16, 2), (32, 32, 1)])
+def test_prefill_window_row_is_decode_at_the_blocks_first_token(window, stride, n_local):
+    """Each query block's selection equals the decode selection of R15 for a
+    query at the block's first token (seq_len = 64 qb + 1) with F = the sum of
+    the block's Forecast vectors: the decode window rule, summed tokens (R8)."""
+    g = torch.Generator().manual_seed(window + stride + n_local)
+    T, d, q0 = 64 * 10, 8, 64 * 6
+    k = torch.randn(1, 2, T, d, generator=g, dtype=torch.float64).numpy()
+    f = torch.randn(1, 2, T - q0, d, generator=g, dtype=torch.float64).numpy()
+    kcw = orc.kv_window_meanpool(k, window, stride)
+    p = orc.prefill_select_windows(f, kcw, q0, 2, 1, n_local, 64, window, stride)
+    n_qb = (T - q0) // 64
+    for qi in range(n_qb):
+        qb = q0 // 64 + qi
+        fsum = f[:, :, 64 * qi: 64 * (qi + 1)].sum(axis=2)
+        kv_seen = orc.kv_window_meanpool(k, window, stride, seq_len=[64 * qb + 1])
+        dsel = orc.decode_select_windows(fsum, kv_seen, [64 * qb + 1], 2, 1, n_local, 64, window, stride)
+        np.testing.assert_array_equal(p.idx[0, :, qi], dsel.idx[0])
+        for h in range(2):
+            sp, sd = p.scores[h * n_qb + qi], dsel.scores[h]
+            assert sp.keys() == sd.keys()
+            for j in sp:
+                assert abs(sp[j] - sd[j]) <= 1e-10 * (1 + abs(sd[j]))
+
+
 # --------------------------------------------------------------------------- baseline multi-head selector
 def test_golden_multihead_select(golden_dir):
     gx = _load(golden_dir, "multihead_select_hand.json")
