@@ -322,33 +322,80 @@ def measured_gemm_tflops(torch, n=8192):
     return round(2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
 
 
+def per_layer_us(torch, bench, fn, reps=3):
+    """Average time of fn(l) over all layers, graph-replayed, HIP events."""
+    def body():
+        for _ in range(reps):
+            for l in range(bench.L):
+                fn(l)
+    body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    e0.record(st)
+    g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * bench.L)
+
+
+def window_selection(torch, bench, kt, window=32, stride=16):
+    """Selection on the overlapping compression the evaluated models use
+    (32-token windows at stride 16, block scores max-pooled from the window
+    scores) against the block selector, per layer: the newest-window update
+    and the score + top-k launches, on the same Forecast vectors.  The window
+    cache holds 4x the block cache's rows, so its scoring streams ~4x the
+    bytes."""
+    wl, B, H, d = bench.wl, bench.B, bench.wl.Hkv, bench.wl.d
+    nw = (bench.T - window) // stride + 1
+    kcw = []
+    for lay in bench.layers:
+        t = torch.empty(B, H, nw, d, dtype=torch.float32, device=bench.dev)
+        bench.bskv.kv_window_meanpool(lay["k"], lay["seq_len"], t, window, stride)
+        kcw.append(t)
+    ws = torch.zeros(max(256, bench.bskv.workspace_bytes("window", B, H, 0, nw)), dtype=torch.uint8, device=bench.dev)
+    idx = torch.empty(B, H, wl.U, dtype=torch.int32, device=bench.dev)
+    cnt = torch.empty(B, H, dtype=torch.int32, device=bench.dev)
+
+    def sel(l):
+        bench.bskv.forecast_window_score_topk(bench.f[l], kcw[l], wl.topk, wl.n_init, wl.n_local,
+                                              bench.layers[l]["seq_len"], window, stride, idx=idx, cnt=cnt, ws=ws)
+
+    def pool(l):
+        lay = bench.layers[l]
+        bench.bskv.kv_window_meanpool(lay["k"], lay["seq_len"], kcw[l], window, stride, newest_only=True)
+
+    sel_us = per_layer_us(torch, bench, sel)
+    pool_us = per_layer_us(torch, bench, pool)
+    # algorithmic bytes of the window selection: the windows touching the
+    # candidate blocks (fp32 rows), the Forecast vectors, the lists
+    cur = (bench.T - 1) // wl.block
+    c0, c1 = wl.n_init, cur - wl.n_local + 1
+    w_lo = max(0, (wl.block * c0 - window) // stride + 1)
+    w_hi = min(nw, wl.block * c1 // stride)
+    nbytes = B * H * ((w_hi - w_lo) * d * 4 + d * 4 + (wl.U + 1) * 4)
+    del kcw, ws
+    torch.cuda.synchronize()
+    fs_us = kt["score_topk"] * 1e6
+    return {"window": window, "stride": stride, "windows": nw, "select_us_per_layer": round(sel_us, 3),
+            "select_bytes": nbytes, "select_GBps": round(nbytes / sel_us / 1e3, 1),
+            "select_hbm_frac": round(nbytes / sel_us / 1e3 / HBM_PEAK_GBS, 4),
+            "newest_window_pool_us_per_layer": round(pool_us, 3),
+            "block_select_us_per_layer": round(fs_us, 3), "select_ratio_vs_block": round(sel_us / fs_us, 3)}
+
+
 def baseline_comparison(torch, bench, step_s, kt, args):
     """Same-GPU comparison with the baseline multi-head selector: its
     selection cost per layer against the Forecast selector's (both as
     separate score + top-k launches over all layers), and a whole step in the
     baseline's serial order against the lookahead step."""
-    def per_layer_us(fn, reps=3):
-        def body():
-            for _ in range(reps):
-                for l in range(bench.L):
-                    fn(l)
-        body()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            body()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st = torch.cuda.current_stream()
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) * 1e3 / (reps * bench.L)
-
-    mh_us = per_layer_us(bench.mh_select)
+    mh_us = per_layer_us(torch, bench, bench.mh_select)
     serial_s, _ = time_graph(torch, bench.step_baseline, max(5, args.steps // 5), 2, use_graph=not args.no_graph)
     # leave the lookahead lists in place for whoever runs next
     bench.proj(0)
@@ -493,6 +540,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
     peaks = measured_hbm_peaks(torch)
     sweep = selection_sweep(torch, bench)
     base_cmp = baseline_comparison(torch, bench, step_s, kt, args) if wl.hidden else None
+    win_sel = window_selection(torch, bench, kt) if wl.hidden else None
     # replicas: independent copies of one layer's inputs, rotated so that the
     # working set does not sit in the 256 MB cache; the step then covers
     # `replicas` layer-steps of a one-layer model
@@ -517,6 +565,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
         "measured_peaks": dict(peaks, roofline_frac_of_copy=round(ach / peaks["copy_GBps"], 4)),
         "select_us_per_layer_vs_T": sweep,
         "baseline_selector": base_cmp,
+        "window_selector": win_sel,
         "kernels": kernels,
     }
     if replicas is not None:
@@ -607,6 +656,11 @@ class PrefillBench:
         self.cnt = [torch.empty(self.B, wl.Hkv, n_qb, dtype=torch.int32, device=self.dev) for _ in range(n_chunks)]
         self.out = [torch.empty_like(self.q[0]) for _ in range(n_chunks)]
         self.seq_len = torch.full((self.B,), self.T, dtype=torch.int64, device=self.dev)
+        # overlapping compression (32-token windows at stride 16) for the
+        # variant's selection
+        self.win, self.wst = 32, 16
+        self.nw = (self.T - self.win) // self.wst + 1
+        self.kcw = torch.empty(self.B, wl.Hkv, self.nw, wl.d, dtype=torch.float32, device=self.dev)
         torch.cuda.synchronize()
         log(f"[bench] prefill inputs in {time.time() - t0:.1f}s")
 
@@ -618,6 +672,23 @@ class PrefillBench:
         wl = self.wl
         self.bskv.forecast_block_score_topk(self.f[c], self.kc, wl.topk, wl.n_init, wl.n_local, q_start=c * self.C,
                                             prefill=True, idx=self.idx[c], cnt=self.cnt[c])
+
+    def window_pool(self, c):
+        """The windows completed inside chunk c."""
+        w0 = max(0, (c * self.C - self.win) // self.wst + 1)
+        w1 = min(self.nw, ((c + 1) * self.C - self.win) // self.wst + 1)
+        self.bskv.kv_window_meanpool(self.k, self.seq_len, self.kcw, self.win, self.wst, w0, w1)
+
+    def window_select(self, c):
+        wl = self.wl
+        self.bskv.forecast_window_score_topk(self.f[c], self.kcw, wl.topk, wl.n_init, wl.n_local, None, self.win,
+                                             self.wst, q_start=c * self.C, idx=self.idx[c], cnt=self.cnt[c])
+
+    def step_window(self):
+        for c in range(self.n_chunks):
+            self.window_pool(c)
+            self.window_select(c)
+            self.attend(c)
 
     def attend(self, c):
         self.bskv.block_sparse_attn_prefill(self.q[c], self.k, self.v, self.idx[c], self.cnt[c], c * self.C,
@@ -667,6 +738,7 @@ def run_prefill(args, torch, bskv, wl):
     # per-kernel: each kernel over all chunks, graph-replayed, HIP events
     kt = {}
     for name, fn in (("kv_block_meanpool", bench.pool), ("score_topk_prefill", bench.select),
+                     ("kv_window_meanpool", bench.window_pool), ("window_select_prefill", bench.window_select),
                      ("attn_prefill", bench.attend)):
         def body():
             for c in range(bench.n_chunks):
@@ -701,6 +773,17 @@ def run_prefill(args, torch, bskv, wl):
         "attn_prefill": {"us": round(kt["attn_prefill"] * 1e6, 2), "TFLOPs": round(att_tf, 1),
                          "mfma_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+    # the overlapping-compression variant (32/16 windows, block scores
+    # max-pooled): its pooling and selection per chunk, and its whole step
+    # (the window selection leaves the lists of the block selector's place)
+    win_step_s, _ = time_graph(torch, bench.step_window, max(1, args.steps // 10), 1, use_graph=not args.no_graph)
+    window_variant = {
+        "window": bench.win, "stride": bench.wst,
+        "kv_window_meanpool_us": round(kt["kv_window_meanpool"] * 1e6, 2),
+        "window_select_prefill_us": round(kt["window_select_prefill"] * 1e6, 2),
+        "select_ratio_vs_block": round(kt["window_select_prefill"] / kt["score_topk_prefill"], 3),
+        "step_ms": round(win_step_s * 1e3, 3), "tokens_per_s": round(B * T / win_step_s, 1),
+    }
     return {
         "metric": "prefill tokens/s at B×T (chunked, block-sparse); % bf16 MFMA peak", "value": round(B * T / step_s, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": max(1, args.steps // 10), "warmup": max(1, args.warmup // 5),
@@ -718,6 +801,7 @@ def run_prefill(args, torch, bskv, wl):
         "measured_gemm_bf16_TFLOPs": gemm_tf,
         "roofline_frac_of_measured_gemm": round(att_tf / gemm_tf, 4),
         "kernels": kernels,
+        "window_variant": window_variant,
     }
 
 

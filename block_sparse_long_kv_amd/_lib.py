@@ -35,9 +35,9 @@ _proto("bskv_forecast_block_score_topk", _i, _p, _i, _i, _i64, _p, _i64, _p, _i,
        _p, _sz, _p)
 _proto("bskv_kv_window_meanpool", _i, _p, _i, ctypes.POINTER(_i64), _i64, _i, _i, _i, _i, _i, _p, _i64, _i64, _i, _p,
        _i64, _p)
-_proto("bskv_window_score_topk_workspace", _sz, _i, _i, _i64)
-_proto("bskv_forecast_window_score_topk", _i, _p, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
-       _sz, _p)
+_proto("bskv_window_score_topk_workspace", _sz, _i, _i, _i, _i64)
+_proto("bskv_forecast_window_score_topk", _i, _p, _i, _i, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p,
+       _p, _p, _p, _sz, _p)
 _proto("bskv_multihead_score_topk_workspace", _sz, _i, _i, _i64)
 _proto("bskv_multihead_block_score_topk", _i, _p, _i, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p,
        _p, _sz, _p)
@@ -194,26 +194,35 @@ def kv_window_meanpool(k, seq_len, kcw, window: int = 32, stride: int = 16, w_be
     return kcw
 
 
-def forecast_window_score_topk(f, kcw, topk: int, n_init: int, n_local: int, seq_len, window: int = 32,
-                               stride: int = 16, return_scores: bool = False, idx=None, cnt=None, ws=None,
-                               stream=None):
-    """Decode selection on window-compressed keys (block score = max over the
-    block's windows): (idx int32 [B, Hkv, U], cnt int32 [B, Hkv]) [, block scores]."""
+def forecast_window_score_topk(f, kcw, topk: int, n_init: int, n_local: int, seq_len=None, window: int = 32,
+                               stride: int = 16, q_start: int = 0, return_scores: bool = False, idx=None, cnt=None,
+                               ws=None, stream=None):
+    """Selection on window-compressed keys (block score = max over the
+    block's visible windows).  Decode: f fp32 [B, Hkv, d] -> (idx [B, Hkv, U],
+    cnt [B, Hkv]) [, block scores].  Prefill: f [B, Hkv, Tq, d] (fp32 or
+    bf16) for the chunk at q_start -> (idx [B, Hkv, n_qb, U], cnt [B, Hkv, n_qb])."""
     B, H, nw_cap, d = kcw.shape
     U = topk + n_init + n_local
     nb = ((nw_cap - 1) * stride + window) // 64
-    if not f.is_contiguous() or f.dtype != torch.float32:
-        raise ValueError("f must be contiguous fp32")
+    if not f.is_contiguous():
+        raise ValueError("f must be contiguous")
     sh = _stream(stream, f.device)
-    idx = idx if idx is not None else torch.empty(B, H, U, dtype=torch.int32, device=f.device)
-    cnt = cnt if cnt is not None else torch.empty(B, H, dtype=torch.int32, device=f.device)
+    prefill = f.dim() == 4
+    n_q = f.shape[2] if prefill else 0
+    if prefill and return_scores:
+        raise ValueError("block scores are returned for decode only")
+    lead = (B, H, -(-n_q // 64)) if prefill else (B, H)
+    idx = idx if idx is not None else torch.empty(*lead, U, dtype=torch.int32, device=f.device)
+    cnt = cnt if cnt is not None else torch.empty(*lead, dtype=torch.int32, device=f.device)
     scores = torch.full((B, H, nb), float("nan"), dtype=torch.float32, device=f.device) if return_scores else None
-    lay = (B, H, nw_cap)
+    lay = (B, H, n_q, nw_cap)
     nbytes = workspace_bytes("window", *lay)
-    ws = ws if ws is not None else _workspace(f.device, nbytes, sh, "window", lay)
-    _check(lib.bskv_forecast_window_score_topk(_ptr(f), _ptr(kcw), nw_cap, _ptr(seq_len), B, H, d, 64, window, stride,
-                                               topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), _ptr(ws),
-                                               ws.numel() * ws.element_size(), sh), "forecast_window_score_topk")
+    if ws is None and nbytes > 0:
+        ws = _workspace(f.device, nbytes, sh, "window", lay)
+    _check(lib.bskv_forecast_window_score_topk(_ptr(f), _dt(f), n_q, q_start, _ptr(kcw), nw_cap, _ptr(seq_len), B, H,
+                                               d, 64, window, stride, topk, n_init, n_local, _ptr(idx), _ptr(cnt),
+                                               _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                               sh), "forecast_window_score_topk")
     return (idx, cnt, scores) if return_scores else (idx, cnt)
 
 

@@ -157,26 +157,36 @@ int bskv_kv_window_meanpool(const void* k, int dtype, const int64_t* kv_strides,
   return finish(bskv::launch_window_meanpool(a));
 }
 
-size_t bskv_window_score_topk_workspace(int B, int n_kv_heads, int64_t kcw_nw_cap) {
-  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0) return 0;
-  return bskv::window_select_workspace_bytes(B, n_kv_heads, kcw_nw_cap);
+size_t bskv_window_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kcw_nw_cap) {
+  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0 || n_q_tokens < 0) return 0;
+  return bskv::window_select_workspace_bytes(B, n_kv_heads, n_q_tokens, kcw_nw_cap);
 }
 
-int bskv_forecast_window_score_topk(const float* f, const float* kcw, int64_t kcw_nw_cap, const int64_t* seq_len,
-                                    int B, int n_kv_heads, int head_dim, int block, int window, int stride, int topk,
-                                    int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out, float* scores_out,
-                                    void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!f || !kcw || !seq_len || !idx_out || !cnt_out || !ws) return BSKV_EINVAL;
-  if (!aligned16(f) || !aligned16(kcw) || !aligned16(ws)) return BSKV_EINVAL;
-  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0) return BSKV_EINVAL;
+int bskv_forecast_window_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start, const float* kcw,
+                                    int64_t kcw_nw_cap, const int64_t* seq_len, int B, int n_kv_heads, int head_dim,
+                                    int block, int window, int stride, int topk, int n_init, int n_local,
+                                    int32_t* idx_out, int32_t* cnt_out, float* scores_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!dtype_ok(f_dtype)) return BSKV_EDTYPE;
+  if (!f || !kcw || !idx_out || !cnt_out || !aligned16(f) || !aligned16(kcw)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || kcw_nw_cap <= 0 || n_q_tokens < 0) return BSKV_EINVAL;
   if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
   if (!head_dim_ok(head_dim) || block != 64 || !window_grid_ok(window, stride)) return BSKV_EUNSUPPORTED;
   const int64_t nb_cap = window_blocks(kcw_nw_cap, window, stride);
   if (nb_cap < 1) return BSKV_EINVAL;
   if (nb_cap > bskv::kMaxCandidates || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
-  if (ws_bytes < bskv::window_select_workspace_bytes(B, n_kv_heads, kcw_nw_cap)) return BSKV_ENOSPC;
-  bskv::WindowSelectArgs a{f, kcw, kcw_nw_cap, nb_cap, seq_len, B, n_kv_heads, head_dim, window, stride, topk, n_init,
-                           n_local, topk + n_init + n_local, idx_out, cnt_out, scores_out, ws, stream};
+  if (n_q_tokens == 0) {
+    if (f_dtype != BSKV_F32) return BSKV_EDTYPE;
+    if (!seq_len || !ws || !aligned16(ws)) return BSKV_EINVAL;
+    if (ws_bytes < bskv::window_select_workspace_bytes(B, n_kv_heads, 0, kcw_nw_cap)) return BSKV_ENOSPC;
+  } else {
+    if (q_start < 0 || q_start % block) return BSKV_EINVAL;
+    if (scores_out) return BSKV_EINVAL;
+    if ((n_q_tokens + block - 1) / block > 65535) return BSKV_EUNSUPPORTED;
+  }
+  bskv::WindowSelectArgs a{f, f_dtype, n_q_tokens, q_start, kcw, kcw_nw_cap, nb_cap, seq_len, B, n_kv_heads,
+                           head_dim, window, stride, topk, n_init, n_local, topk + n_init + n_local, idx_out, cnt_out,
+                           scores_out, ws, stream};
   return finish(bskv::launch_window_select(a));
 }
 

@@ -53,6 +53,44 @@ template <> __device__ __forceinline__ void cvt16<bf16_bits>(const uint4& r, flo
   o[4] = bf16_lo(r.z); o[5] = bf16_hi(r.z); o[6] = bf16_lo(r.w); o[7] = bf16_hi(r.w);
 }
 
+// Sum of n (<= 64) consecutive token rows of D values (a query block's
+// Forecast vectors): 16-byte column chunks per lane, rows strided over the
+// workgroup, partial sums reduced through LDS.  Result in sm.fpool; ends with
+// a barrier.
+template <typename T, int D>
+struct PoolRowsSmem {
+  static constexpr int RPP = kThreads / (D / VecN<T>::N);
+  float red[RPP][D + 4];
+  float fpool[D];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void pool_rows(const T* __restrict__ rows, int n, PoolRowsSmem<T, D>& sm) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int CPR = D / VEC;
+  constexpr int RPP = PoolRowsSmem<T, D>::RPP;
+  const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int t = r0; t < n; t += RPP) {
+    float x[VEC];
+    cvt16<T>(ld16(rows + (int64_t)t * D + c * VEC), x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sm.red[r0][c * VEC + e] = acc[e];
+  __syncthreads();
+  for (int t = threadIdx.x; t < D; t += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) s += sm.red[r][t];
+    sm.fpool[t] = s;
+  }
+  __syncthreads();
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<bf16_bits>(bf16_bits x) { return __uint_as_float(((uint32_t)x) << 16); }

@@ -48,13 +48,14 @@ struct WindowMeanpoolArgs {
 hipError_t launch_window_meanpool(const WindowMeanpoolArgs& a);
 
 struct WindowSelectArgs {
-  const float* f; const float* kcw; int64_t nw_cap; int64_t nb_cap; const int64_t* seq_len;
+  const void* f; int f_dtype; int n_q_tokens; int64_t q_start;
+  const float* kcw; int64_t nw_cap; int64_t nb_cap; const int64_t* seq_len;
   int B, H, D, window, stride, topk, n_init, n_local, U;
   int32_t* idx; int32_t* cnt; float* scores;
   void* ws;
   hipStream_t stream;
 };
-size_t window_select_workspace_bytes(int B, int H, int64_t nw_cap);
+size_t window_select_workspace_bytes(int B, int H, int n_q_tokens, int64_t nw_cap);
 hipError_t launch_window_select(const WindowSelectArgs& a);
 
 struct MultiheadSelectArgs {

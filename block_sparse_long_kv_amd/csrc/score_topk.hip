@@ -56,45 +56,19 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void score_topk_prefill_kernel(
     const T* __restrict__ f, int Tq, int64_t q_start, const float* __restrict__ kc, int64_t nb_cap, int H, int block,
     int topk, int n_init, int n_local, int U, int n_qb, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
-  constexpr int VEC = VecN<T>::N;
-  constexpr int CPR = D / VEC;
-  constexpr int RPP = kThreads / CPR;
   extern __shared__ uint32_t keys[];
   __shared__ TopkShared sh;
-  __shared__ float red[RPP][D + 4];
-  __shared__ float fpool[D];
+  __shared__ PoolRowsSmem<T, D> ps;
 
   const int qi = blockIdx.x, bg = blockIdx.y;
   const int t0 = qi * block, t1 = min(Tq, t0 + block);
   // pooled Forecast of the query block: sum of its tokens' vectors
-  {
-    const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
-    const T* base = f + ((int64_t)bg * Tq) * D + c * VEC;
-    float acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-    for (int t = t0 + r0; t < t1; t += RPP) {
-      float x[VEC];
-      cvt16<T>(ld16(base + (int64_t)t * D), x);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += x[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) red[r0][c * VEC + e] = acc[e];
-    __syncthreads();
-    for (int t = threadIdx.x; t < D; t += kThreads) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < RPP; ++r) s += red[r][t];
-      fpool[t] = s;
-    }
-    __syncthreads();
-  }
+  pool_rows<T, D>(f + ((int64_t)bg * Tq + t0) * D, t1 - t0, ps);
   const int cur = (int)(q_start / block) + qi;
   const int c0 = n_init, c1 = min(cur - n_local + 1, (int)nb_cap);
   const int n = max(0, c1 - c0);
   float4 fv[D / 32];
-  load_fvec<D>(fpool, fv);
+  load_fvec<D>(ps.fpool, fv);
   const float* kc_bg = kc + (int64_t)bg * nb_cap * D;
   score_rows<D>(kc_bg, fv, c0, c1, [&](int j, float s) { keys[j - c0] = orderable_key(s); });
   __syncthreads();

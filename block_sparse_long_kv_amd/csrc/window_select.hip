@@ -11,10 +11,11 @@
 // Window mean-pool: one workgroup per (window, KV head, sequence), the
 // window's rows summed by 16-byte column chunks and reduced across row
 // lanes in LDS (the block mean-pool's workgroup with 32 or 64 rows).
-// Selection: window scores F . K~w over the windows touching the candidate
-// blocks, in slices (the block selector's score slices on window rows);
-// then one workgroup per (b, g) max-pools them into block scores (orderable
-// keys in LDS) and runs the radix select + union of the block selector.
+// Decode selection: window scores F . K~w over the windows touching the
+// candidate blocks, in slices (the block selector's score slices on window
+// rows); then one workgroup per (b, g) max-pools them into block scores
+// (orderable keys in LDS) and runs the radix select + union of the block
+// selector.  Prefill selection: one workgroup per query block (below).
 #include "decode_ops.hpp"
 #include "bskv_launch.hpp"
 
@@ -129,20 +130,91 @@ __global__ __launch_bounds__(kThreads) void window_topk_kernel(const float* __re
   topk_union(keys, n, dc.c0, topk, dc.cur, n_init, n_local, U, idx + (int64_t)bg * U, cnt + bg, sh);
 }
 
-size_t window_select_workspace_bytes(int B, int H, int64_t nw_cap) { return (size_t)B * H * nw_cap * sizeof(float); }
+// Prefill: grid (n_qb, B*H), one workgroup per query block.  The block's
+// Forecast vectors are summed; each candidate block's score is the maximum of
+// the pooled Forecast's dot products with the windows that touch it and whose
+// tokens all precede the query block (8 lanes per candidate, its windows in
+// turn); then the block selector's top-k + union.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void window_prefill_kernel(const T* __restrict__ f, int Tq, int64_t q_start,
+                                                                const float* __restrict__ kcw, int64_t nw_cap,
+                                                                int64_t nb_cap, int window, int stride, int topk,
+                                                                int n_init, int n_local, int U, int n_qb,
+                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+  constexpr int LPR = 8;
+  constexpr int F4 = D / 4 / LPR;
+  extern __shared__ uint32_t keys[];
+  __shared__ TopkShared sh;
+  __shared__ PoolRowsSmem<T, D> ps;
+  const int qi = blockIdx.x, bg = blockIdx.y;
+  const int t0 = qi * kBlk, t1 = min(Tq, t0 + kBlk);
+  pool_rows<T, D>(f + ((int64_t)bg * Tq + t0) * D, t1 - t0, ps);
+  const int cur = (int)(q_start / kBlk) + qi;
+  const int c0 = n_init, c1 = (int)min((int64_t)(cur - n_local + 1), nb_cap);
+  const int n = max(0, c1 - c0);
+  // windows that end at or before the query block's first token
+  const int64_t first = (int64_t)cur * kBlk;
+  const int nvis = first < window ? 0 : (int)min((first - window) / stride + 1, nw_cap);
+  const int sub = threadIdx.x % LPR, row0 = threadIdx.x / LPR;
+  float4 fv[F4];
+#pragma unroll
+  for (int i = 0; i < F4; ++i) fv[i] = *reinterpret_cast<const float4*>(ps.fpool + (i * LPR + sub) * 4);
+  const float* kcw_bg = kcw + (int64_t)bg * nw_cap * D;
+  for (int j = c0 + row0; j < c1; j += kThreads / LPR) {
+    const int lo = win_lo(j, window, stride), hi = min(win_hi(j, stride), nvis - 1);
+    float m = -INFINITY;
+    for (int w = lo; w <= hi; ++w) {   // the 8 lanes of the candidate run the same windows
+      const float* row = kcw_bg + (int64_t)w * D;
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < F4; ++i) {
+        const float4 k4 = *reinterpret_cast<const float4*>(row + (i * LPR + sub) * 4);
+        acc += fv[i].x * k4.x;
+        acc += fv[i].y * k4.y;
+        acc += fv[i].z * k4.z;
+        acc += fv[i].w * k4.w;
+      }
+      m = fmaxf(m, sum8(acc));
+    }
+    if (sub == 0) keys[j - c0] = orderable_key(m);
+  }
+  __syncthreads();
+  topk_union(keys, n, c0, topk, cur, n_init, n_local, U, idx + ((int64_t)bg * n_qb + qi) * U,
+             cnt + (int64_t)bg * n_qb + qi, sh);
+}
+
+size_t window_select_workspace_bytes(int B, int H, int n_q_tokens, int64_t nw_cap) {
+  return n_q_tokens > 0 ? 0 : (size_t)B * H * nw_cap * sizeof(float);
+}
 
 hipError_t launch_window_select(const WindowSelectArgs& a) {
   const int n_bg = a.B * a.H;
+  const int64_t cap = a.nb_cap < kMaxCandidates ? a.nb_cap : kMaxCandidates;
+  if (a.n_q_tokens > 0) {
+    const int n_qb = (a.n_q_tokens + kBlk - 1) / kBlk;
+    const dim3 grid(n_qb, n_bg);
+#define BSKV_WIN_PREFILL(T, DD)                                                                                   \
+  hipLaunchKernelGGL((window_prefill_kernel<T, DD>), grid, dim3(kThreads), (size_t)cap * sizeof(uint32_t), a.stream, \
+                     (const T*)a.f, a.n_q_tokens, a.q_start, a.kcw, a.nw_cap, a.nb_cap, a.window, a.stride, a.topk,  \
+                     a.n_init, a.n_local, a.U, n_qb, a.idx, a.cnt)
+    if (a.f_dtype == 0) {
+      if (a.D == 64) BSKV_WIN_PREFILL(float, 64); else BSKV_WIN_PREFILL(float, 128);
+    } else {
+      if (a.D == 64) BSKV_WIN_PREFILL(bf16_bits, 64); else BSKV_WIN_PREFILL(bf16_bits, 128);
+    }
+#undef BSKV_WIN_PREFILL
+    return hipGetLastError();
+  }
   const int ns = score_split_plan(n_bg, a.nw_cap);
   float* sc = (float*)a.ws;
   const dim3 grid(ns, n_bg);
+  const float* f = (const float*)a.f;
   if (a.D == 64)
-    hipLaunchKernelGGL(window_score_kernel<64>, grid, dim3(kThreads), 0, a.stream, a.f, a.kcw, a.nw_cap, a.seq_len,
+    hipLaunchKernelGGL(window_score_kernel<64>, grid, dim3(kThreads), 0, a.stream, f, a.kcw, a.nw_cap, a.seq_len,
                        a.H, a.n_init, a.n_local, a.window, a.stride, a.nb_cap, ns, sc);
   else
-    hipLaunchKernelGGL(window_score_kernel<128>, grid, dim3(kThreads), 0, a.stream, a.f, a.kcw, a.nw_cap, a.seq_len,
+    hipLaunchKernelGGL(window_score_kernel<128>, grid, dim3(kThreads), 0, a.stream, f, a.kcw, a.nw_cap, a.seq_len,
                        a.H, a.n_init, a.n_local, a.window, a.stride, a.nb_cap, ns, sc);
-  const int64_t cap = a.nb_cap < kMaxCandidates ? a.nb_cap : kMaxCandidates;
   hipLaunchKernelGGL(window_topk_kernel, dim3(n_bg), dim3(kThreads), (size_t)cap * sizeof(uint32_t), a.stream, sc,
                      a.nw_cap, a.nb_cap, a.seq_len, a.H, a.window, a.stride, a.topk, a.n_init, a.n_local, a.U, a.idx,
                      a.cnt, a.scores);

@@ -162,8 +162,8 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
- * Overlapping key compression and Forecast selection on it (decode): the
- * variant the evaluated models run.
+ * Overlapping key compression and Forecast selection on it: the variant the
+ * evaluated models run.
  * "SparDA: a fourth projection that lets sparse attention prefetch its own
  * KV cache" -- "One Forecast head per GQA group", closing paragraph (keys
  * pooled with a 32-token window at stride 16, blocks of 64) and "Training"
@@ -175,17 +175,23 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
  *   newest_only != 0, only the window the newest token completed, if any.
  *   k as for bskv_kv_block_meanpool; kcw [B, n_kv_heads, kcw_nw_cap,
  *   head_dim] fp32; other rows untouched.
- * bskv_forecast_window_score_topk: the decode selection of
- *   bskv_forecast_block_score_topk (same candidates, ties, union, idx_out /
- *   cnt_out layouts and limits) with the score of candidate block j = the
- *   maximum of f . kcw[w] over the complete windows w sharing a token with
- *   block j (w = 4j-1 .. 4j+3 on the 32/16 grid).  f fp32 [B, n_kv_heads,
- *   head_dim].  The block capacity is nb = ((kcw_nw_cap-1)*stride +
- *   window)/64 (at most 12288); scores_out (nullable) [B, n_kv_heads, nb]
- *   receives the block scores of the candidates, other entries untouched.
- *   ws: bskv_window_score_topk_workspace() bytes (window scores), no
- *   initialisation needed.  Two launches: window scores in slices, then one
- *   max-pool + top-k workgroup per (b, g).
+ * bskv_forecast_window_score_topk: bskv_forecast_block_score_topk (same
+ *   arguments, candidates, ties, union, layouts and limits) with the score of
+ *   candidate block j = the maximum of F . kcw[w] over the windows w that
+ *   share a token with block j (w = 4j-1 .. 4j+3 on the 32/16 grid) and are
+ *   visible to the query:
+ *   decode (n_q_tokens == 0): the complete windows of the sequence; f fp32
+ *     [B, n_kv_heads, head_dim]; scores_out (nullable) [B, n_kv_heads, nb]
+ *     receives the candidates' block scores, other entries untouched;
+ *   prefill (n_q_tokens > 0): F = the sum of the query block's Forecast
+ *     vectors (f [B, n_kv_heads, n_q_tokens, head_dim], F32 or BF16), and
+ *     only windows whose tokens all precede the query block take part;
+ *     scores_out must be NULL; seq_len is ignored.
+ *   The block capacity is nb = ((kcw_nw_cap-1)*stride + window)/64 (at most
+ *   12288).  ws: bskv_window_score_topk_workspace() bytes (window scores in
+ *   decode, none in prefill), no initialisation needed.  Decode runs two
+ *   launches (window scores in slices, then one max-pool + top-k workgroup
+ *   per (b, g)); prefill one workgroup per query block.
  * Both: (window, stride) with window 32 or 64, stride 16, 32 or 64 dividing
  * window; block 64; head_dim 64 or 128.  Errors as everywhere.
  * ----------------------------------------------------------------------- */
@@ -193,11 +199,12 @@ int bskv_kv_window_meanpool(const void* k, int dtype, const int64_t* kv_strides,
                             int n_kv_heads, int head_dim, int window, int stride, const int64_t* seq_len,
                             int64_t w_begin, int64_t w_end, int newest_only, float* kcw, int64_t kcw_nw_cap,
                             hipStream_t stream);
-size_t bskv_window_score_topk_workspace(int B, int n_kv_heads, int64_t kcw_nw_cap);
-int bskv_forecast_window_score_topk(const float* f, const float* kcw, int64_t kcw_nw_cap, const int64_t* seq_len,
-                                    int B, int n_kv_heads, int head_dim, int block, int window, int stride, int topk,
-                                    int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out, float* scores_out,
-                                    void* ws, size_t ws_bytes, hipStream_t stream);
+size_t bskv_window_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kcw_nw_cap);
+int bskv_forecast_window_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start, const float* kcw,
+                                    int64_t kcw_nw_cap, const int64_t* seq_len, int B, int n_kv_heads, int head_dim,
+                                    int block, int window, int stride, int topk, int n_init, int n_local,
+                                    int32_t* idx_out, int32_t* cnt_out, float* scores_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
  * Baseline multi-head block selector (decode), the comparison point of the

@@ -139,28 +139,35 @@ def test_window_select_validation():
     assert mp(P, 1, S3, 131072, 8, 8, 128, 32, 16, P, 5, 4, 0, P, 8191, None) == EINVAL    # w_end < w_begin
     assert mp(P, 1, S3, 131072, 8, 8, 128, 32, 16, P, 0, 8192, 0, P, 8191, None) == EINVAL  # past the cap
     f = lib.bskv_forecast_window_score_topk
-    ws = lib.bskv_window_score_topk_workspace(8, 8, 8191)
+    ws = lib.bskv_window_score_topk_workspace(8, 8, 0, 8191)
     assert ws >= 64 * 8191 * 4
-    assert lib.bskv_window_score_topk_workspace(8, 0, 8191) == 0
-    args = dict(f=P, kcw=P, cap=8191, sl=P, B=8, H=8, d=128, blk=64, win=32, st=16, k=64, ni=1, nl=4, idx=P, cnt=P,
-                sc=None, ws=P, wsb=ws)
+    assert lib.bskv_window_score_topk_workspace(8, 0, 0, 8191) == 0
+    assert lib.bskv_window_score_topk_workspace(8, 8, 2048, 8191) == 0      # prefill needs none
+    args = dict(f=P, fdt=0, nq=0, q0=0, kcw=P, cap=8191, sl=P, B=8, H=8, d=128, blk=64, win=32, st=16, k=64, ni=1,
+                nl=4, idx=P, cnt=P, sc=None, ws=P, wsb=ws)
 
     def call(**kw):
         a = {**args, **kw}
-        return f(a["f"], a["kcw"], a["cap"], a["sl"], a["B"], a["H"], a["d"], a["blk"], a["win"], a["st"], a["k"],
-                 a["ni"], a["nl"], a["idx"], a["cnt"], a["sc"], a["ws"], a["wsb"], None)
+        return f(a["f"], a["fdt"], a["nq"], a["q0"], a["kcw"], a["cap"], a["sl"], a["B"], a["H"], a["d"], a["blk"],
+                 a["win"], a["st"], a["k"], a["ni"], a["nl"], a["idx"], a["cnt"], a["sc"], a["ws"], a["wsb"], None)
+    assert call(fdt=5) == EDTYPE
+    assert call(fdt=1) == EDTYPE                      # decode Forecast must be fp32
     assert call(f=None) == EINVAL
     assert call(kcw=MIS) == EINVAL
+    assert call(sl=None) == EINVAL
     assert call(ni=0) == EINVAL
     assert call(nl=0) == EINVAL
     assert call(k=-1) == EINVAL
     assert call(cap=0) == EINVAL
+    assert call(nq=-1) == EINVAL
     assert call(d=96) == EUNSUP
     assert call(blk=32) == EUNSUP
     assert call(win=16, st=16) == EUNSUP
     assert call(win=32, st=64) == EUNSUP
     assert call(cap=8 * 12288) == EUNSUP             # more than 12288 blocks
     assert call(wsb=ws - 4) == ENOSPC
+    assert call(nq=2048, q0=100, fdt=1) == EINVAL    # prefill chunk start not a multiple of the block
+    assert call(nq=2048, sc=P, fdt=1) == EINVAL      # no scores in prefill
 
 
 def test_attn_decode_validation():

@@ -342,6 +342,43 @@ def test_window_select_block_sized_windows_equal_block_selector():
     assert torch.isfinite(s1[:, :, 1:300]).all() and max_abs(np64(s1[:, :, 1:300]), np64(sc[:, :, 1:300])) < 1e-3
 
 
+@pytest.mark.parametrize("dtype,d,window,stride,n_local,q_start,Tq", [
+    ("bf16", 128, 32, 16, 32, 64 * 64, 2048), ("f32", 64, 32, 16, 1, 64 * 3, 64 * 9 + 17),
+    ("bf16", 64, 64, 16, 2, 0, 64 * 20), ("f32", 128, 32, 32, 1, 64 * 40, 64 * 6)])
+def test_window_select_prefill(dtype, d, window, stride, n_local, q_start, Tq):
+    """Prefill selection on window-compressed keys against the oracle: each
+    query block sums its Forecast vectors, max-pools the visible windows'
+    scores per candidate block; a ragged last query block; n_local = 1 makes
+    the windows that reach into the query block matter."""
+    B, Hkv, topk = 2, 2, 8
+    T = q_start + Tq
+    g = torch.Generator().manual_seed(300 + d + window + n_local)
+    cdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    f = torch.randn(B, Hkv, Tq, d, generator=g).to(cdt)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(cdt)
+    seq_len = torch.full((B,), T, dtype=torch.int64)
+    kcw = _kcw_gpu(k.to(DEV), seq_len.to(DEV), window, stride)
+    idx, cnt = bskv.forecast_window_score_topk(f.to(DEV), kcw, topk, 1, n_local, None, window, stride, q_start=q_start)
+    torch.cuda.synchronize()
+    kcw_or = orc.kv_window_meanpool(np64(k), window, stride)
+    sel = orc.prefill_select_windows(np64(f), kcw_or, q_start, topk, 1, n_local, 64, window, stride)
+    assert check_selection(idx, cnt, sel, topk) <= 2
+
+
+def test_window_select_prefill_block_sized_windows_equal_block_selector():
+    B, Hkv, d, T, q0 = 2, 4, 128, 64 * 300, 64 * 200
+    g = torch.Generator().manual_seed(31)
+    f = torch.randn(B, Hkv, T - q0, d, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16).to(DEV)
+    seq_len = torch.full((B,), T, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(k, seq_len)
+    kcw = _kcw_gpu(k, seq_len, 64, 64)
+    i1, c1 = bskv.forecast_window_score_topk(f, kcw, 16, 1, 3, None, 64, 64, q_start=q0)
+    i2, c2 = bskv.forecast_block_score_topk(f, kc, 16, 1, 3, q_start=q0, prefill=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(i1, i2)
+
+
 # ----------------------------------------------------------------------------- a4 decode
 def _attn_case(seed, B, Hq, Hkv, d, T, dtype, lens, topk, n_local):
     c = _gpu(random_decode_case(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens, plant=topk,
