@@ -8,6 +8,7 @@ from .sparda_ref import (  # noqa: F401
     Selection,
     attend_decode,
     attend_prefill,
+    block_cache_plan,
     block_sets,
     decode_select,
     decode_select_windows,

@@ -48,6 +48,16 @@ function that uses it):
       the sum over its tokens of F_t . K~w (R8 applied to windows) and
       max-pools as in R15; a window takes part only if all its tokens precede
       the query block (the decode rule of R15 at the block's first token).
+  R17 Resident block cache for offloaded decode (not described on the pages;
+      their offloaded decode throughput at batch 64 and 128K, [EXPL] "Three
+      speedups, three different baselines" (Table 4), implies that most
+      selected blocks are reused from one decode step to the next): per
+      (batch, KV head) a cache of S block slots
+      with least-recently-used replacement.  A call lists the blocks one
+      layer needs: listed blocks already held keep their slot; the others
+      take, in list order, the unlisted slots in order of (last use, slot),
+      empty slots first; every listed slot is then stamped with
+      (call number, list position).
   R14 Baseline multi-head selector (decode): the G query heads of a KV group
       each score the candidates against the compressed keys, the G score rows
       are summed, the sum times the attention scale goes through a softmax over
@@ -487,6 +497,54 @@ def gather_selected_blocks(kv, idx, cnt, block: int) -> np.ndarray:
                 j = int(idx[b, g, u])
                 ring[b, g, u] = kv[b, g, block * j: block * (j + 1)]
     return ring
+
+
+def block_cache_plan(tags, stamps, clock, idx, cnt):
+    """One lookup of a resident block cache (reading R17), updating the
+    cache state in place.
+
+    tags   int [B, Hkv, S]   block id held by each slot, -1 when empty
+    stamps int [B, Hkv, S]   last use of each slot as call * U + list position,
+                             -1 when never used
+    clock  int [B, Hkv]      calls made so far
+    idx    int [B, Hkv, U]   the blocks one layer needs (ascending, -1 padded)
+    cnt    int [B, Hkv]      valid entries of idx
+    Returns (slot [B, Hkv, U], fill [B, Hkv, U], n_fill [B, Hkv]): slot[u]
+    is the slot that holds idx[u] after the call; fill[u] = idx[u] when that
+    block has to be copied into the slot (it was not held), else -1; entries
+    u >= cnt are -1.  Needs cnt <= S.
+    """
+    B, H, U = idx.shape
+    S = tags.shape[-1]
+    slot = np.full((B, H, U), -1, dtype=np.int64)
+    fill = np.full((B, H, U), -1, dtype=np.int64)
+    n_fill = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for g in range(H):
+            c = int(cnt[b, g])
+            if c > S:
+                raise ValueError("more listed blocks than cache slots")
+            listed = [int(j) for j in idx[b, g, :c]]
+            held = {int(tags[b, g, s]): s for s in range(S) if tags[b, g, s] >= 0}
+            kept = set()
+            for u, j in enumerate(listed):           # listed blocks already held keep their slot
+                if j in held:
+                    slot[b, g, u] = held[j]
+                    kept.add(held[j])
+            free = sorted((int(stamps[b, g, s]), s) for s in range(S) if s not in kept)
+            k = 0
+            for u, j in enumerate(listed):           # the others take the least recently used slots
+                if slot[b, g, u] < 0:
+                    s_new = free[k][1]
+                    k += 1
+                    tags[b, g, s_new] = j
+                    slot[b, g, u] = s_new
+                    fill[b, g, u] = j
+            n_fill[b, g] = k
+            clock[b, g] += 1
+            for u in range(c):
+                stamps[b, g, slot[b, g, u]] = int(clock[b, g]) * U + u
+    return slot, fill, n_fill
 
 
 # --------------------------------------------------------------------------

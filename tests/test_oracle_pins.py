@@ -237,6 +237,87 @@ def test_prefill_window_row_is_decode_at_the_blocks_first_token(window, stride, 
                 assert abs(sp[j] - sd[j]) <= 1e-10 * (1 + abs(sd[j]))
 
 
+# --------------------------------------------------------------------------- resident block cache (R17)
+def test_golden_block_cache_lru(golden_dir):
+    gx = _load(golden_dir, "block_cache_lru_hand.json")
+    S, U = gx["S"], gx["U"]
+    tags = np.full((1, 1, S), -1, dtype=np.int64)
+    stamps = np.full((1, 1, S), -1, dtype=np.int64)
+    clock = np.zeros((1, 1), dtype=np.int64)
+    for call in gx["calls"]:
+        idx = np.array(call["idx"], dtype=np.int64).reshape(1, 1, U)
+        cnt = np.array([[call["cnt"]]])
+        slot, fill, n_fill = orc.block_cache_plan(tags, stamps, clock, idx, cnt)
+        assert slot[0, 0].tolist() == call["slot"]
+        assert fill[0, 0].tolist() == call["fill"]
+        assert int(n_fill[0, 0]) == call["n_fill"]
+        assert tags[0, 0].tolist() == call["tags"]
+        assert stamps[0, 0].tolist() == call["stamps"]
+
+
+def _lists_with_drift(rng, n_calls, B, H, U, universe, churn):
+    """Sorted lists of U blocks per call; each call swaps `churn` of the
+    previous list's blocks for others (a drifting working set)."""
+    cur = [[sorted(rng.choice(universe, U, replace=False).tolist()) for _ in range(H)] for _ in range(B)]
+    out = []
+    for _ in range(n_calls):
+        idx = np.full((B, H, U), -1, dtype=np.int64)
+        cnt = np.zeros((B, H), dtype=np.int64)
+        for b in range(B):
+            for g in range(H):
+                keep = set(rng.choice(cur[b][g], U - churn, replace=False).tolist())
+                rest = [j for j in range(universe) if j not in keep]
+                new = set(rng.choice(rest, churn, replace=False).tolist())
+                cur[b][g] = sorted(keep | new)
+                c = int(rng.integers(U - 2, U + 1))           # some lists shorter (padded)
+                idx[b, g, :c] = cur[b][g][:c]
+                cnt[b, g] = c
+        out.append((idx, cnt))
+    return out
+
+
+@pytest.mark.parametrize("S,U,universe,churn", [(8, 5, 12, 2), (16, 6, 40, 3), (6, 6, 20, 1)])
+def test_block_cache_is_a_textbook_lru(S, U, universe, churn):
+    """Against an OrderedDict LRU of capacity S (most recent at the end):
+    room is made for the missing blocks by evicting from the front, skipping
+    listed blocks; then every listed block is touched (moved or inserted at
+    the end) in list order.  The resident sets and the blocks copied agree
+    call by call; and the slot map is consistent (each listed block sits in
+    its slot, held blocks never move)."""
+    from collections import OrderedDict
+    rng = np.random.default_rng(S * 100 + U)
+    B, H = 2, 3
+    tags = np.full((B, H, S), -1, dtype=np.int64)
+    stamps = np.full((B, H, S), -1, dtype=np.int64)
+    clock = np.zeros((B, H), dtype=np.int64)
+    lru = [[OrderedDict() for _ in range(H)] for _ in range(B)]
+    for idx, cnt in _lists_with_drift(rng, 25, B, H, U, universe, churn):
+        before = tags.copy()
+        slot, fill, n_fill = orc.block_cache_plan(tags, stamps, clock, idx, cnt)
+        for b in range(B):
+            for g in range(H):
+                c = int(cnt[b, g])
+                listed = idx[b, g, :c].tolist()
+                od = lru[b][g]
+                missing = [j for j in listed if j not in od]
+                victims = [j for j in od if j not in listed][:max(0, len(od) + len(missing) - S)]
+                for j in victims:
+                    del od[j]
+                for j in listed:
+                    od[j] = True
+                    od.move_to_end(j)
+                assert set(od) == {int(t) for t in tags[b, g] if t >= 0}
+                assert [int(j) for j in fill[b, g] if j >= 0] == missing
+                assert int(n_fill[b, g]) == len(missing)
+                for u, j in enumerate(listed):
+                    s = int(slot[b, g, u])
+                    assert tags[b, g, s] == j
+                    if j in before[b, g]:
+                        assert before[b, g, s] == j            # a held block is never moved or copied again
+                assert len(set(slot[b, g, :c].tolist())) == c
+                assert (slot[b, g, c:] == -1).all() and (fill[b, g, c:] == -1).all()
+
+
 # --------------------------------------------------------------------------- baseline multi-head selector
 def test_golden_multihead_select(golden_dir):
     gx = _load(golden_dir, "multihead_select_hand.json")
