@@ -9,8 +9,11 @@ Importing this package fails loudly when libbskv.so has not been built
 (``python block_sparse_long_kv_amd/build.py``).
 """
 from ._lib import (  # noqa: F401
+    BlockCache,
     BskvError,
+    block_cache_plan,
     block_sparse_attn_decode,
+    block_sparse_attn_decode_cached,
     block_sparse_attn_prefill,
     decode_layer_lookahead,
     forecast_block_score_topk,
@@ -21,6 +24,7 @@ from ._lib import (  # noqa: F401
     kv_window_meanpool,
     lib,
     multihead_block_score_topk,
+    prefetch_cache_fill,
     prefetch_selected_blocks,
     workspace_bytes,
 )

@@ -49,6 +49,12 @@ _proto("bskv_block_sparse_attn_prefill", _i, _p, _p, _p, _i, ctypes.POINTER(_i64
 _proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i,
        _i, _i, _p)
 _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
+_proto("bskv_block_cache_reset", _i, _p, _p, _p, _i, _i, _i, _p)
+_proto("bskv_block_cache_plan", _i, _p, _p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p)
+_proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+       _i, _p)
+_proto("bskv_block_sparse_attn_decode_cached", _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p,
+       _p, _sz, _p)
 _proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _i, _i)
 _proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _f, _p, _p, _p,
        _i, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
@@ -326,6 +332,83 @@ def prefetch_selected_blocks(src_k, src_v, idx, cnt, ring_k, ring_v, n_workgroup
                                              _ptr(ring_k), _ptr(ring_v), B, H, d, 64, U, nwg, sh),
            "prefetch_selected_blocks")
     return ring_k, ring_v
+
+
+class BlockCache:
+    """A resident block cache of one layer: n_slots K/V block slots per
+    (b, g) on the device and their slot table (least recently used)."""
+
+    def __init__(self, B: int, n_kv_heads: int, n_slots: int, head_dim: int, dtype=torch.bfloat16, device="cuda",
+                 stream=None):
+        dev = torch.device(device)
+        self.B, self.H, self.S, self.d = B, n_kv_heads, n_slots, head_dim
+        self.k = torch.empty(B, n_kv_heads, n_slots, 64, head_dim, dtype=dtype, device=dev)
+        self.v = torch.empty_like(self.k)
+        self.tags = torch.empty(B, n_kv_heads, n_slots, dtype=torch.int32, device=dev)
+        self.stamps = torch.empty(B, n_kv_heads, n_slots, dtype=torch.int64, device=dev)
+        self.clock = torch.empty(B, n_kv_heads, dtype=torch.int64, device=dev)
+        self.reset(stream)
+
+    def reset(self, stream=None):
+        sh = _stream(stream, self.k.device)
+        _check(lib.bskv_block_cache_reset(_ptr(self.tags), _ptr(self.stamps), _ptr(self.clock), self.B, self.H, self.S,
+                                          sh), "block_cache_reset")
+
+
+def block_cache_plan(cache: "BlockCache", idx, cnt, slot=None, fill=None, n_fill=None, stream=None):
+    """Look one layer's lists up in the cache: (slot, fill, n_fill) int32."""
+    B, H, U = idx.shape
+    slot = slot if slot is not None else torch.empty(B, H, U, dtype=torch.int32, device=idx.device)
+    fill = fill if fill is not None else torch.empty(B, H, U, dtype=torch.int32, device=idx.device)
+    n_fill = n_fill if n_fill is not None else torch.empty(B, H, dtype=torch.int32, device=idx.device)
+    sh = _stream(stream, idx.device)
+    _check(lib.bskv_block_cache_plan(_ptr(idx), _ptr(cnt), B, H, U, _ptr(cache.tags), _ptr(cache.stamps),
+                                     _ptr(cache.clock), cache.S, _ptr(slot), _ptr(fill), _ptr(n_fill), sh),
+           "block_cache_plan")
+    return slot, fill, n_fill
+
+
+def prefetch_cache_fill(src_k, src_v, fill, slot, cache: "BlockCache", n_workgroups: int | None = None, stream=None,
+                        src_k_dev: int | None = None, src_v_dev: int | None = None):
+    """Copy the blocks `fill` names from src (device or pinned host) into
+    their cache slots."""
+    B, H, U = fill.shape
+    d = src_k.shape[-1]
+    if src_k.stride() != src_v.stride():
+        raise ValueError("src_k/src_v: identical strides")
+    if src_k.is_cuda:
+        pk, pv = src_k.data_ptr(), src_v.data_ptr()
+    else:
+        if not (src_k.is_pinned() and src_v.is_pinned()):
+            raise ValueError("host sources must be pinned")
+        pk = src_k_dev if src_k_dev is not None else host_device_pointer(src_k)
+        pv = src_v_dev if src_v_dev is not None else host_device_pointer(src_v)
+    nwg = n_workgroups if n_workgroups is not None else max(1, min(B * H * U, 512))
+    sh = _stream(stream, cache.k.device)
+    _check(lib.bskv_prefetch_cache_fill(pk, pv, _dt(cache.k), _strides3(src_k), src_k.shape[2], _ptr(fill), _ptr(slot),
+                                        _ptr(cache.k), _ptr(cache.v), B, H, d, 64, U, cache.S, nwg, sh),
+           "prefetch_cache_fill")
+
+
+def block_sparse_attn_decode_cached(q, cache: "BlockCache", slot, idx, cnt, seq_len, scale: float | None = None,
+                                    out=None, ws=None, stream=None):
+    """Decode attention over the listed blocks read from a block cache -> fp32 [B, Hq, d]."""
+    B, Hq, d = q.shape
+    Hkv = cache.H
+    U = idx.shape[-1]
+    if q.dtype != cache.k.dtype or not q.is_contiguous():
+        raise ValueError("q contiguous, of the cache's dtype")
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    lay = (B, Hq, Hkv, d, U)
+    nbytes = workspace_bytes("attn", *lay)
+    ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "attn", lay)
+    _check(lib.bskv_block_sparse_attn_decode_cached(_ptr(q), _ptr(cache.k), _ptr(cache.v), _dt(q), cache.S, _ptr(slot),
+                                                    _ptr(idx), _ptr(cnt), _ptr(seq_len), B, Hq, Hkv, d, 64, U, scale,
+                                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), sh),
+           "block_sparse_attn_decode_cached")
+    return out
 
 
 def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None = None, out=None, x=None, w=None,

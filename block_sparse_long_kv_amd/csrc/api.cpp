@@ -274,6 +274,70 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
   return finish(bskv::launch_gather(a));
 }
 
+namespace {
+constexpr int kCacheMaxSlots = 1024;   // slots per (b, g) of a block cache
+}  // namespace
+
+int bskv_block_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int B, int n_kv_heads, int n_slots,
+                           hipStream_t stream) {
+  if (!tags || !stamps || !clock) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || n_slots <= 0) return BSKV_EINVAL;
+  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  return finish(bskv::launch_cache_reset(tags, stamps, clock, B * n_kv_heads, n_slots, stream));
+}
+
+int bskv_block_cache_plan(const int32_t* idx, const int32_t* cnt, int B, int n_kv_heads, int U, int32_t* tags,
+                          int64_t* stamps, int64_t* clock, int n_slots, int32_t* slot_out, int32_t* fill_out,
+                          int32_t* n_fill_out, hipStream_t stream) {
+  if (!idx || !cnt || !tags || !stamps || !clock || !slot_out || !fill_out) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || U <= 0 || n_slots <= 0) return BSKV_EINVAL;
+  if (U > n_slots) return BSKV_EINVAL;   // every listed block needs a slot
+  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  bskv::CachePlanArgs a{idx, cnt, U, tags, stamps, clock, n_slots, slot_out, fill_out, n_fill_out,
+                        B * n_kv_heads, stream};
+  return finish(bskv::launch_cache_plan(a));
+}
+
+int bskv_prefetch_cache_fill(const void* src_k, const void* src_v, int dtype, const int64_t* src_strides,
+                             int64_t src_len, const int32_t* fill, const int32_t* slot, void* cache_k, void* cache_v,
+                             int B, int n_kv_heads, int head_dim, int block, int U, int n_slots, int n_workgroups,
+                             hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!src_k || !src_v || !fill || !slot || !cache_k || !cache_v) return BSKV_EINVAL;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(cache_k) || !aligned16(cache_v)) return BSKV_EINVAL;
+  if (B <= 0 || n_kv_heads <= 0 || U <= 0 || n_slots <= 0 || n_workgroups < 1 || src_len < 0 ||
+      !strides_ok(src_strides, dtype))
+    return BSKV_EINVAL;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads * U > 0x7fffffff || n_workgroups > 65535)
+    return BSKV_EUNSUPPORTED;
+  bskv::GatherArgs a{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype), fill,
+                     nullptr, cache_k, cache_v, B, n_kv_heads, head_dim, block, U, n_workgroups, stream, slot,
+                     n_slots};
+  return finish(bskv::launch_gather(a));
+}
+
+int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, const void* cache_v, int dtype,
+                                         int n_slots, const int32_t* slot, const int32_t* idx, const int32_t* cnt,
+                                         const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+                                         int block, int U, float scale, float* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!q || !cache_k || !cache_v || !slot || !idx || !cnt || !seq_len || !out || !ws) return BSKV_EINVAL;
+  if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(ws)) return BSKV_EINVAL;
+  if (B <= 0 || U <= 0 || n_slots <= 0) return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  if (ws_bytes < bskv::attn_decode_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, U)) return BSKV_ENOSPC;
+  // cache layout [B, n_kv_heads, n_slots, block, head_dim], contiguous
+  const int64_t st = head_dim, sg = (int64_t)n_slots * block * head_dim, sb = sg * n_kv_heads;
+  bskv::AttnDecodeArgs a{q, cache_k, cache_v, dtype, sb, sg, st, (int64_t)n_slots * block, 1, idx, cnt, seq_len, B,
+                         n_q_heads, n_kv_heads, head_dim, block, U, scale, out, ws, stream, slot};
+  return finish(bskv::launch_attn_decode(a));
+}
+
 size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,
                                              int64_t kc_nb_cap, int U, int dtype) {
   if (B <= 0 || U <= 0 || kc_nb_cap <= 0 || hidden < 0 || !group_ok(n_q_heads, n_kv_heads) || !dtype_ok(dtype) ||

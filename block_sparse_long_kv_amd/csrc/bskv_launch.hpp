@@ -76,6 +76,7 @@ struct AttnDecodeArgs {
   int B, Hq, Hkv, D, block, U; float scale;
   float* out; void* ws;
   hipStream_t stream;
+  const int32_t* slot = nullptr;     // block cache: listed block u is read from slot[u] of k, v
 };
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int U);
 hipError_t launch_attn_decode(const AttnDecodeArgs& a);
@@ -95,12 +96,25 @@ struct GatherArgs {
   const void* src_k; const void* src_v; int64_t sb, sg, st;  // element strides
   int64_t src_len;
   int esize;
-  const int32_t* idx; const int32_t* cnt;
+  const int32_t* idx; const int32_t* cnt;   // source block of entry u (< 0: skip); cnt nullable (all U)
   void* ring_k; void* ring_v;
   int B, H, D, block, U, n_workgroups;
   hipStream_t stream;
+  const int32_t* dst_slot = nullptr;        // destination slot of entry u (nullptr: slot u)
+  int S = 0;                                // destination slots per (b, g) (0: U)
 };
 hipError_t launch_gather(const GatherArgs& a);
+
+// Resident block cache (least recently used, per (b, g)).
+struct CachePlanArgs {
+  const int32_t* idx; const int32_t* cnt; int U;
+  int32_t* tags; int64_t* stamps; int64_t* clock; int S;
+  int32_t* slot; int32_t* fill; int32_t* n_fill;
+  int n_bg;
+  hipStream_t stream;
+};
+hipError_t launch_cache_plan(const CachePlanArgs& a);
+hipError_t launch_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int n_bg, int S, hipStream_t stream);
 
 // One decode layer with lookahead selection of the next layer (3 kernels).
 struct DecodeLayerArgs {

@@ -186,7 +186,7 @@ AttnDecodeParams make_attn_params(const AttnDecodeArgs& a, void* ws) {
   const int n_bg = a.B * a.Hkv, G = a.Hq / a.Hkv;
   attn_split_plan(n_bg, a.U, ns, bps);
   p.q = a.q; p.k = a.k; p.v = a.v;
-  p.sb = a.sb; p.sg = a.sg; p.st = a.st; p.kv_len = a.kv_len; p.ring = a.ring;
+  p.sb = a.sb; p.sg = a.sg; p.st = a.st; p.kv_len = a.kv_len; p.ring = a.ring; p.slot = a.slot;
   p.idx = a.idx; p.cnt = a.cnt; p.seq_len = a.seq_len;
   p.Hkv = a.Hkv; p.U = a.U;
   p.qscale = a.scale * 1.4426950408889634f;

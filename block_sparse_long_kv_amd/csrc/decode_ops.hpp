@@ -349,6 +349,7 @@ struct AttnDecodeParams {
   const void* q; const void* k; const void* v;
   int64_t sb, sg, st, kv_len;
   int ring;
+  const int32_t* slot;   // block cache: listed block u sits in slot[u] (nullptr: cache or ring)
   const int32_t* idx; const int32_t* cnt; const int64_t* seq_len;
   int Hkv, U;
   float qscale;        // scale * log2(e)
@@ -546,9 +547,9 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int c = min(p.cnt[bg], p.U);
   const int u0 = split * p.bps, u1 = min(c, u0 + p.bps);
-  // tokens of the sequence; a ring holds only the listed blocks, so its
-  // length bounds ring positions, not the sequence
-  const int64_t L = p.ring ? p.seq_len[b] : min(p.seq_len[b], p.kv_len);
+  // tokens of the sequence; a ring or a block cache holds only some blocks,
+  // so its length bounds positions in it, not the sequence
+  const int64_t L = (p.ring || p.slot) ? p.seq_len[b] : min(p.seq_len[b], p.kv_len);
   const T* q = (const T*)p.q;
   QFrag<D> qf;
   if constexpr (R::kMfma) {
@@ -579,8 +580,9 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
   // block u -> (token base in the buffer, valid token count); invalid ids read nothing
   auto locate = [&](int u, int64_t& tb, int& nvalid) {
     const int j = list[u];
-    tb = (int64_t)(p.ring ? u : j) * kBlk;
-    if (j < 0 || tb + kBlk > p.kv_len) { nvalid = -1; return; }
+    const int loc = p.slot ? p.slot[(int64_t)bg * p.U + u] : (p.ring ? u : j);
+    tb = (int64_t)loc * kBlk;
+    if (j < 0 || loc < 0 || tb + kBlk > p.kv_len) { nvalid = -1; return; }
     const int64_t rem = L - (int64_t)j * kBlk;
     nvalid = rem <= 0 ? 0 : (rem >= kBlk ? kBlk : (int)rem);
   };

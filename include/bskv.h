@@ -306,6 +306,54 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
                                   int block, int U, int n_workgroups, hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
+ * Resident block cache for offloaded decode.  The pages do not describe
+ * one; their offloaded decode throughput at batch 64 and 128K ("SparDA: a
+ * fourth projection that lets sparse attention prefetch its own KV cache"
+ * -- "Three speedups, three different baselines", Table 4) needs most
+ * selected blocks to stay on the GPU between decode steps.  Per (b, g) the
+ * cache has n_slots block slots (<= 1024) in
+ *   cache_k, cache_v  [B, n_kv_heads, n_slots, block, head_dim] contiguous
+ * and a slot table owned by the caller:
+ *   tags   int32 [B, n_kv_heads, n_slots]  block id held by the slot, -1 empty
+ *   stamps int64 [B, n_kv_heads, n_slots]  last use (lookup * U + list position)
+ *   clock  int64 [B, n_kv_heads]           lookups so far
+ * bskv_block_cache_reset empties the table (a kernel: safe under graph
+ * capture).
+ * bskv_block_cache_plan looks one layer's list up (idx [B, Hkv, U]: distinct
+ *   ascending block ids, as the selectors write them; cnt [B, Hkv]) and
+ *   updates the table, least recently used first: listed blocks already held
+ *   keep their slot; the others take, in list order, the unlisted slots in
+ *   order of (stamp, slot), empty slots first.  Writes slot_out [B, Hkv, U]
+ *   (the slot of each listed block, -1 past cnt), fill_out [B, Hkv, U] (the
+ *   block to copy into that slot, -1 when it is already held or past cnt)
+ *   and, when not NULL, n_fill_out [B, Hkv] (the number of copies).
+ *   Requires U <= n_slots.  One workgroup per (b, g).
+ * bskv_prefetch_cache_fill copies the blocks fill_out names from a layer's
+ *   K/V (device or host-mapped memory, as for bskv_prefetch_selected_blocks)
+ *   into their slots; entries with fill < 0 are skipped.
+ * bskv_block_sparse_attn_decode_cached: bskv_block_sparse_attn_decode with
+ *   listed block u (logical id idx[u], masked by seq_len) read from cache slot
+ *   slot[u]; ws as bskv_attn_decode_workspace().
+ * Ordering is the caller's: plan on the compute stream after the selection,
+ * fill on the copy stream after the plan, attend after the fill; a layer's
+ * plan must follow that layer's previous attention (slots are reused).
+ * ----------------------------------------------------------------------- */
+int bskv_block_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int B, int n_kv_heads, int n_slots,
+                           hipStream_t stream);
+int bskv_block_cache_plan(const int32_t* idx, const int32_t* cnt, int B, int n_kv_heads, int U, int32_t* tags,
+                          int64_t* stamps, int64_t* clock, int n_slots, int32_t* slot_out, int32_t* fill_out,
+                          int32_t* n_fill_out, hipStream_t stream);
+int bskv_prefetch_cache_fill(const void* src_k, const void* src_v, int dtype, const int64_t* src_strides,
+                             int64_t src_len, const int32_t* fill, const int32_t* slot, void* cache_k, void* cache_v,
+                             int B, int n_kv_heads, int head_dim, int block, int U, int n_slots, int n_workgroups,
+                             hipStream_t stream);
+int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, const void* cache_v, int dtype,
+                                         int n_slots, const int32_t* slot, const int32_t* idx, const int32_t* cnt,
+                                         const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+                                         int block, int U, float scale, float* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
  * One decode layer with one-layer-ahead selection.  [EXPL] "The fourth
  * projection", Alg. 2 and Eq. 4: right after layer l's projection emits the
  * Forecast F_l, it scores layer l+1's compressed keys and picks layer l+1's

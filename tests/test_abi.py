@@ -170,6 +170,36 @@ def test_window_select_validation():
     assert call(nq=2048, sc=P, fdt=1) == EINVAL      # no scores in prefill
 
 
+def test_block_cache_validation():
+    assert lib.bskv_block_cache_reset(None, P, P, 2, 8, 128, None) == EINVAL
+    assert lib.bskv_block_cache_reset(P, P, P, 2, 8, 0, None) == EINVAL
+    assert lib.bskv_block_cache_reset(P, P, P, 2, 8, 2048, None) == EUNSUP
+    plan = lib.bskv_block_cache_plan
+    assert plan(P, P, 2, 8, 69, P, P, P, 128, None, P, None, None) == EINVAL      # no slot output
+    assert plan(P, P, 2, 8, 129, P, P, P, 128, P, P, None, None) == EINVAL       # more list entries than slots
+    assert plan(P, P, 0, 8, 69, P, P, P, 128, P, P, None, None) == EINVAL
+    assert plan(P, P, 2, 8, 69, P, P, P, 4096, P, P, None, None) == EUNSUP
+    fillf = lib.bskv_prefetch_cache_fill
+    assert fillf(P, P, 5, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EDTYPE
+    assert fillf(P, P, 1, S3, 131072, None, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EINVAL
+    assert fillf(MIS, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EINVAL
+    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 0, None) == EINVAL    # no workgroups
+    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 96, 64, 69, 128, 64, None) == EUNSUP
+    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 2048, 64, None) == EUNSUP
+    att = lib.bskv_block_sparse_attn_decode_cached
+    ws = lib.bskv_attn_decode_workspace(2, 32, 8, 128, 69)
+
+    def call(dt=1, hq=32, d=128, S=128, slot=P, sc=0.088, wsb=ws):
+        return att(P, P, P, dt, S, slot, P, P, P, 2, hq, 8, d, 64, 69, sc, P, P, wsb, None)
+    assert call(dt=5) == EDTYPE
+    assert call(slot=None) == EINVAL
+    assert call(hq=24) == EUNSUP
+    assert call(d=96) == EUNSUP
+    assert call(S=2048) == EUNSUP
+    assert call(sc=0.0) == EINVAL
+    assert call(wsb=ws - 4) == ENOSPC
+
+
 def test_attn_decode_validation():
     f = lib.bskv_block_sparse_attn_decode
     ws = lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69)

@@ -595,6 +595,120 @@ def test_prefetch_from_pinned_host_and_ring_attention():
     assert max_abs(np64(out_ring), want_o) < 2e-2
 
 
+# ----------------------------------------------------------------------------- resident block cache
+def _drifting_lists(rng, n_calls, B, H, U, universe, churn):
+    """Sorted distinct lists of up to U blocks per (b, g); each call swaps
+    `churn` blocks of the previous list for others; some lists are short."""
+    cur = [[sorted(rng.choice(universe, U, replace=False).tolist()) for _ in range(H)] for _ in range(B)]
+    out = []
+    for _ in range(n_calls):
+        idx = np.full((B, H, U), -1, dtype=np.int32)
+        cnt = np.zeros((B, H), dtype=np.int32)
+        for b in range(B):
+            for g in range(H):
+                keep = set(rng.choice(cur[b][g], U - churn, replace=False).tolist())
+                pool = np.setdiff1d(np.arange(universe), np.array(sorted(keep)))
+                new = set(rng.choice(pool, churn, replace=False).tolist())
+                cur[b][g] = sorted(keep | new)
+                c = int(rng.integers(max(0, U - 3), U + 1))
+                idx[b, g, :c] = cur[b][g][:c]
+                cnt[b, g] = c
+        out.append((idx, cnt))
+    return out
+
+
+@pytest.mark.parametrize("S,U,universe,churn,calls", [(8, 5, 14, 2, 30), (128, 69, 2043, 4, 40),
+                                                      (96, 96, 400, 10, 12), (1024, 1000, 5000, 50, 6)])
+def test_block_cache_plan_matches_oracle(S, U, universe, churn, calls):
+    """The slot table, slot map, copies and counts equal the oracle's LRU
+    exactly, lookup after lookup (integer work: bit-exact)."""
+    rng = np.random.default_rng(S + U)
+    B, H = 2, 3
+    cache = bskv.BlockCache(B, H, S, 64, device=DEV)
+    tags = np.full((B, H, S), -1, dtype=np.int64)
+    stamps = np.full((B, H, S), -1, dtype=np.int64)
+    clock = np.zeros((B, H), dtype=np.int64)
+    for idx, cnt in _drifting_lists(rng, calls, B, H, U, universe, churn):
+        slot, fill, n_fill = bskv.block_cache_plan(cache, torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV))
+        torch.cuda.synchronize()
+        w_slot, w_fill, w_n = orc.block_cache_plan(tags, stamps, clock, idx, cnt)
+        assert np.array_equal(slot.cpu().numpy(), w_slot)
+        assert np.array_equal(fill.cpu().numpy(), w_fill)
+        assert np.array_equal(n_fill.cpu().numpy(), w_n)
+        assert np.array_equal(cache.tags.cpu().numpy(), tags)
+        assert np.array_equal(cache.stamps.cpu().numpy(), stamps)
+        assert np.array_equal(cache.clock.cpu().numpy(), clock)
+    cache.reset()
+    torch.cuda.synchronize()
+    assert (cache.tags == -1).all() and (cache.stamps == -1).all() and (cache.clock == 0).all()
+
+
+@pytest.mark.parametrize("host", [True, False])
+def test_cache_fill_and_cached_attention_over_steps(host):
+    """Three decode steps of one layer through a block cache smaller than the
+    sequence: lookup, copy of the missing blocks (from pinned host memory or
+    from device memory), attention from the cache.  The cache slots hold the
+    listed blocks bytewise, the cached attention equals the resident one bit
+    for bit and the oracle within bf16 tolerance.  Ragged lengths, a partial
+    newest block."""
+    wl = CONFIGS[5]
+    B, T, S = 3, 64 * 200, 96
+    lay = decode_inputs(wl, DEV, layers=1, B=B, T=T)[0]
+    lay["seq_len"] = torch.tensor([T, T - 64 * 37 - 5, 64 * 90], dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(lay["k"], lay["seq_len"])
+    if host:
+        src_k = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+        src_v = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+        src_k.copy_(lay["k"])
+        src_v.copy_(lay["v"])
+    else:
+        src_k, src_v = lay["k"], lay["v"]
+    cache = bskv.BlockCache(B, wl.Hkv, S, wl.d, device=DEV)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    g = torch.Generator(device=DEV).manual_seed(9)
+    resident = [set() for _ in range(B * wl.Hkv)]
+    kh = lay["k"].view(torch.int16).cpu().numpy()
+    f0 = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    # step 0 fills the cache; step 1's unrelated Forecast lists other blocks
+    # (evictions); step 2 returns to the first lists (part resident, part refetched)
+    forecasts = [f0, torch.randn(f0.shape, generator=g, device=DEV), f0]
+    for step, f in enumerate(forecasts):
+        idx, cnt = bskv.forecast_block_score_topk(f.contiguous(), kc, wl.topk, wl.n_init, wl.n_local,
+                                                  seq_len=lay["seq_len"])
+        slot, fill, n_fill = bskv.block_cache_plan(cache, idx, cnt)
+        side = torch.cuda.Stream(DEV)
+        ev = torch.cuda.Event()
+        ev.record()
+        side.wait_event(ev)
+        bskv.prefetch_cache_fill(src_k, src_v, fill, slot, cache, n_workgroups=64, stream=side)
+        done = torch.cuda.Event()
+        done.record(side)
+        torch.cuda.current_stream().wait_event(done)
+        out_c = bskv.block_sparse_attn_decode_cached(lay["q"], cache, slot, idx, cnt, lay["seq_len"])
+        out_r = bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"])
+        torch.cuda.synchronize()
+        gi, cn, sl = idx.cpu().numpy(), cnt.cpu().numpy(), slot.cpu().numpy()
+        fl, nf = fill.cpu().numpy(), n_fill.cpu().numpy()
+        ck = cache.k.view(torch.int16).cpu().numpy()
+        for b in range(B):
+            for h in range(wl.Hkv):
+                c = int(cn[b, h])
+                listed = set(gi[b, h, :c].tolist())
+                assert int(nf[b, h]) == len(listed - resident[b * wl.Hkv + h])
+                assert set(fl[b, h][fl[b, h] >= 0].tolist()) == listed - resident[b * wl.Hkv + h]
+                resident[b * wl.Hkv + h] = set(cache.tags[b, h].cpu().numpy().tolist()) - {-1}
+                for u in range(c):
+                    j = int(gi[b, h, u])
+                    assert np.array_equal(ck[b, h, sl[b, h, u]], kh[b, h, 64 * j: 64 * (j + 1)]), (step, b, h, u)
+        assert torch.equal(out_c, out_r), "cached read must equal resident read bit for bit"
+        want = orc.attend_decode(np64(lay["q"]), np64(lay["k"]), np64(lay["v"]), gi, cn,
+                                 lay["seq_len"].cpu().numpy(), wl.scale, 64)
+        assert max_abs(np64(out_c), want) < 2e-2
+        if step > 0:
+            assert 0 < nf.sum() < cn.sum(), "a later step reuses some resident blocks and fetches others"
+
+
 # ----------------------------------------------------------------------------- fused decode layer
 def _layer_case(dtype, d, G, B, T, lens, seed):
     wl = CONFIGS[2]
