@@ -980,14 +980,259 @@ def run_offload(args, torch, bskv, wl):
     }
 
 
+# ---------------------------------------------------------------------------
+# steady-state offloaded decode: resident block cache + model stand-in
+# ---------------------------------------------------------------------------
+class SteadyOffloadBench:
+    """Decode steps with the whole bf16 KV cache in host-pinned memory and,
+    per layer, a GPU-resident cache of S blocks per (b, g) (least recently
+    used).  Per layer l of a step, on the compute stream: the layer's Q/K/V
+    projection GEMM (stand-in), the selection of layer l+1 from F_l
+    (projection + score/top-k), the cache lookup of layer l+1; on the copy
+    stream: the copy of layer l+1's missing blocks from host memory; back on
+    the compute stream, once layer l's copy is done: attention of layer l from
+    its cache, then the output projection and FFN GEMMs of an 8B-class layer
+    (stand-ins: random bf16 weights, hipBLASLt through torch).  The Forecast
+    input of every layer drifts by a random walk from step to step, which
+    sets how many selected blocks change per step."""
+
+    def __init__(self, wl, torch, bskv, n_steps, S=128, drift=None):
+        from workloads import decode_inputs, drift_walk
+        self.torch, self.bskv, self.wl = torch, bskv, wl
+        self.dev = torch.device("cuda:0")
+        self.B, self.T, self.L, self.HL, self.S = wl.B, wl.T, wl.layers, wl.host_layers, S
+        self.drift = wl.drift if drift is None else drift
+        t0 = time.time()
+        gen = decode_inputs(wl, self.dev, layers=self.HL)
+        nb = self.T // wl.block
+        H, d, U = wl.Hkv, wl.d, wl.U
+        self.kc, self.host_k, self.host_v, self.dk, self.dv, self.w, self.q = [], [], [], [], [], [], []
+        x0 = []
+        self.seq_len = gen[0]["seq_len"]
+        for lay in gen:
+            kc = torch.empty(self.B, H, nb, d, dtype=torch.float32, device=self.dev)
+            bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
+            hk = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+            hv = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+            hk.copy_(lay["k"])
+            hv.copy_(lay["v"])
+            self.kc.append(kc)
+            self.host_k.append(hk)
+            self.host_v.append(hv)
+            self.dk.append(bskv.host_device_pointer(hk))
+            self.dv.append(bskv.host_device_pointer(hv))
+            self.w.append(lay["w_sel"])
+            self.q.append(lay["q"])
+            x0.append(lay["x_sel"])
+            del lay["k"], lay["v"]
+        del gen
+        # per-layer Forecast inputs of every step: independent random walks
+        x0 = torch.stack([x0[l % self.HL] for l in range(self.L)])            # [L, B, hidden]
+        self.xs = drift_walk(x0, n_steps, self.drift, wl.seed + 1000)         # [steps, L, B, hidden]
+        # stand-in weights of an 8B-class layer: Q/K/V projection, output
+        # projection, gate+up and down projections of the FFN
+        hid, ffn = wl.hidden, 14336
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(wl.seed + 2000)
+        rnd = lambda *sh: (torch.randn(*sh, generator=g, device=self.dev) * 0.02).to(torch.bfloat16)  # noqa: E731
+        self.w_qkv = [rnd(hid, wl.Hq * d + 2 * H * d) for _ in range(self.L)]
+        self.w_o = [rnd(wl.Hq * d, hid) for _ in range(self.L)]
+        self.w_gu = [rnd(hid, 2 * ffn) for _ in range(self.L)]
+        self.w_down = [rnd(ffn, hid) for _ in range(self.L)]
+        self.standin_bytes = sum(t.numel() * 2 for t in (self.w_qkv[0], self.w_o[0], self.w_gu[0], self.w_down[0]))
+        self.ffn = ffn
+        self.caches = [bskv.BlockCache(self.B, H, S, d, device=self.dev) for _ in range(self.L)]
+        self.f = [torch.empty(self.B, H, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        self.idx = [torch.empty(self.B, H, U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.cnt = [torch.empty(self.B, H, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.slot = [torch.empty(self.B, H, U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.fill = [torch.empty(self.B, H, U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
+        self.n_fill = torch.zeros(self.L, self.B, H, dtype=torch.int32, device=self.dev)
+        self.fills = torch.zeros((), dtype=torch.int64, device=self.dev)      # blocks copied, summed over steps
+        self.xbuf = torch.empty_like(self.xs[0])                              # this step's Forecast inputs
+        self.out = [torch.empty(self.B, wl.Hq, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=self.dev)  # noqa: E731
+        self.ws_proj = z(bskv.workspace_bytes("proj", self.B, hid, H, d, 1))
+        self.ws_score = z(bskv.workspace_bytes("score", self.B, H, 0, nb, d))
+        self.ws_attn = z(bskv.workspace_bytes("attn", self.B, wl.Hq, H, d, U))
+        self.copy_stream = torch.cuda.Stream(self.dev)
+        self.ev_plan = [torch.cuda.Event() for _ in range(self.L)]
+        self.ev_fill = [torch.cuda.Event() for _ in range(self.L)]
+        self.n_wg = self.B * H
+        torch.cuda.synchronize()
+        log(f"[bench] steady offload set-up ({self.HL} host layers pinned, {self.L} caches of {S} slots, "
+            f"{self.L * self.standin_bytes / 1e9:.1f} GB stand-in weights) in {time.time() - t0:.1f}s")
+
+    def select_plan(self, l):
+        wl, hl = self.wl, l % self.HL
+        self.bskv.forecast_proj(self.xbuf[l], self.w[hl], wl.Hkv, wl.d, out=self.f[l], ws=self.ws_proj)
+        self.bskv.forecast_block_score_topk(self.f[l], self.kc[hl], wl.topk, wl.n_init, wl.n_local,
+                                            seq_len=self.seq_len, idx=self.idx[l], cnt=self.cnt[l], ws=self.ws_score)
+        self.bskv.block_cache_plan(self.caches[l], self.idx[l], self.cnt[l], slot=self.slot[l], fill=self.fill[l],
+                                   n_fill=self.n_fill[l])
+
+    def fill_cache(self, l, stream=None):
+        hl = l % self.HL
+        self.bskv.prefetch_cache_fill(self.host_k[hl], self.host_v[hl], self.idx[l], self.slot[l], self.fill[l],
+                                      self.n_fill[l], self.caches[l], n_workgroups=self.n_wg, stream=stream,
+                                      src_k_dev=self.dk[hl], src_v_dev=self.dv[hl])
+
+    def standin_pre(self, l):
+        return self.xbuf[l] @ self.w_qkv[l]
+
+    def standin_post(self, l):
+        torch = self.torch
+        a = self.out[l].view(self.B, -1).to(torch.bfloat16)
+        h = a @ self.w_o[l]
+        gu = h @ self.w_gu[l]
+        act = torch.nn.functional.silu(gu[:, : self.ffn]) * gu[:, self.ffn:]
+        return act @ self.w_down[l]
+
+    def attend(self, l):
+        hl = l % self.HL
+        self.bskv.block_sparse_attn_decode_cached(self.q[hl], self.caches[l], self.slot[l], self.idx[l], self.cnt[l],
+                                                  self.seq_len, self.wl.scale, out=self.out[l], ws=self.ws_attn)
+
+    def body(self, with_copy=True, standin=True):
+        """One decode step on the Forecast inputs in xbuf (graph-capturable)."""
+        torch = self.torch
+        comp = torch.cuda.current_stream(self.dev)
+        cs = self.copy_stream
+
+        def issue(l):
+            self.select_plan(l)
+            if with_copy:
+                self.ev_plan[l].record(comp)
+                cs.wait_event(self.ev_plan[l])
+                self.fill_cache(l, stream=cs)
+                self.ev_fill[l].record(cs)
+
+        issue(0)
+        for l in range(self.L):
+            if standin:
+                self.standin_pre(l)
+            if l + 1 < self.L:
+                issue(l + 1)                 # F_l selects layer l+1; its missing blocks start copying
+            if with_copy:
+                comp.wait_event(self.ev_fill[l])
+            self.attend(l)
+            if standin:
+                self.standin_post(l)
+
+    def copy_only(self):
+        for l in range(self.L):
+            self.fill_cache(l)
+
+
+def run_offload_steady(args, torch, bskv, wl):
+    warm, n = max(3, args.warmup), max(5, args.steps // 5)
+    n_comp = max(3, n // 2)
+    wg_sweep, n_sweep = (16, 32, 64, 128), 4
+    total = warm + len(wg_sweep) * n_sweep + n + 2 * n_comp
+    bench = SteadyOffloadBench(wl, torch, bskv, total, drift=args.drift)
+    sync = torch.cuda.synchronize
+    graphs = {}
+
+    def graph(with_copy=True, standin=True):
+        key = (with_copy, standin, bench.n_wg)
+        if args.no_graph:
+            return None
+        if key not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                bench.body(with_copy=with_copy, standin=standin)
+            graphs[key] = g
+        return graphs[key]
+
+    def run(t0, t1, **kw):
+        g = graph(**kw)
+        sync()
+        a = time.perf_counter()
+        for t in range(t0, t1):
+            bench.xbuf.copy_(bench.xs[t])
+            if g is None:
+                bench.body(**kw)
+            else:
+                g.replay()
+            bench.fills += bench.n_fill.sum()       # outside the graph
+        sync()
+        return (time.perf_counter() - a) / (t1 - t0)
+
+    # warm-up: eager steps fill the caches, then the graphs are captured
+    # (capture itself runs nothing) and replayed
+    for t in range(warm):
+        bench.xbuf.copy_(bench.xs[t])
+        bench.body()
+    sync()
+    # the copy kernel shares the GPU with the layer's compute: pick its
+    # workgroup count (the pages tune it to the batch) on whole steps
+    t = warm
+    sweep = {}
+    for nwg in wg_sweep:
+        bench.n_wg = nwg
+        run(t, t + 1)
+        sweep[nwg] = run(t + 1, t + n_sweep)
+        t += n_sweep
+    bench.n_wg = min(sweep, key=sweep.get)
+    for kw in ({}, {"with_copy": False}, {"with_copy": False, "standin": False}):
+        graph(**kw)
+    sync()
+    bench.fills.zero_()
+    t_total = run(t, t + n)
+    t += n
+    fills_per_step = float(bench.fills) / n
+    last_fill = float(bench.n_fill.to(torch.int64).sum())
+    sync()
+    a = time.perf_counter()
+    bench.copy_only()                                                # the last step's copies, alone
+    sync()
+    t_copy_last = time.perf_counter() - a
+    # same steps without the copies (lists and lookups still run), with and
+    # without the model stand-in
+    t_comp = run(t, t + n_comp, with_copy=False)
+    t_path = run(t + n_comp, t + 2 * n_comp, with_copy=False, standin=False)
+    blk = wl.block * wl.d * 2 * 2                                    # one block's K and V (bf16)
+    copy_bytes = fills_per_step * blk
+    copy_gbps = last_fill * blk / t_copy_last / 1e9 if t_copy_last > 0 else None
+    t_copy = copy_bytes / (copy_gbps * 1e9) if copy_gbps else 0.0
+    hidden = max(0.0, min(1.0, (t_comp + t_copy - t_total) / t_copy)) if t_copy > 0 else 1.0
+    nbg = bench.B * wl.Hkv
+    return {
+        "metric": "steady-state offloaded decode tokens/s at B×T (KV in host-pinned memory, resident block cache); "
+                  "% copy hidden",
+        "value": round(bench.B / t_total, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": warm,
+        "ms_per_step": round(t_total * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": bench.B, "T": bench.T, "layers": bench.L, "host_layers": bench.HL,
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.d, "topk": wl.topk, "n_init": wl.n_init,
+                   "n_local": wl.n_local, "planted": wl.plant, "cache_slots": bench.S, "drift": bench.drift,
+                   "standin": "per layer x@W_qkv (4096x6144), o-proj (4096x4096), FFN gate+up (4096x28672), "
+                              "down (14336x4096), bf16",
+                   "prefetch_workgroups": bench.n_wg, "hip_graph": not args.no_graph},
+        "roofline": {"bound": "host-link", "kernel": "prefetch_cache_fill", "achieved": round(copy_gbps, 2)
+                     if copy_gbps else None, "peak": 64.0, "unit": "GB/s",
+                     "frac": round(copy_gbps / 64.0, 4) if copy_gbps else None, "traffic": None,
+                     "bytes_per_step": round(copy_bytes)},
+        "blocks_fetched_per_bg_layer_step": round(fills_per_step / (nbg * bench.L), 3),
+        "fetched_frac_of_union": round(fills_per_step / (nbg * bench.L * wl.U), 4),
+        "copy_hidden_frac": round(hidden, 4),
+        "ms_compute_only": round(t_comp * 1e3, 3), "ms_path_only": round(t_path * 1e3, 3),
+        "ms_copy_only": round(t_copy * 1e3, 3),
+        "standin_GB_per_step": round(bench.L * bench.standin_bytes / 1e9, 2),
+        "fill_workgroups_sweep_ms_per_step": {str(k): round(v * 1e3, 3) for k, v in sweep.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-b4", "decode-tiny", "prefill", "offload"])
+                    choices=["decode", "decode-b4", "decode-tiny", "prefill", "offload", "offload-steady"])
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--drift", type=float, default=None,
+                    help="offload-steady: random-walk step of the Forecast input per decode step")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -1023,6 +1268,8 @@ def main():
         result = run_prefill(args, torch, bskv, CONFIGS[4])
     elif args.workload == "offload":
         result = run_offload(args, torch, bskv, CONFIGS[5])
+    elif args.workload == "offload-steady":
+        result = run_offload_steady(args, torch, bskv, CONFIGS[6])
     else:
         if args.workload == "decode":
             result = run_decode(args, torch, bskv, CONFIGS[3])

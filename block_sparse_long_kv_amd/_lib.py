@@ -51,8 +51,8 @@ _proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i
 _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
 _proto("bskv_block_cache_reset", _i, _p, _p, _p, _i, _i, _i, _p)
 _proto("bskv_block_cache_plan", _i, _p, _p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p)
-_proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
-       _i, _p)
+_proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
+       _i, _i, _i, _p)
 _proto("bskv_block_sparse_attn_decode_cached", _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p,
        _p, _sz, _p)
 _proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _i, _i)
@@ -356,7 +356,8 @@ class BlockCache:
 
 
 def block_cache_plan(cache: "BlockCache", idx, cnt, slot=None, fill=None, n_fill=None, stream=None):
-    """Look one layer's lists up in the cache: (slot, fill, n_fill) int32."""
+    """Look one layer's lists up in the cache: (slot, fill, n_fill) int32;
+    fill[:n_fill] are the list positions of the blocks to copy."""
     B, H, U = idx.shape
     slot = slot if slot is not None else torch.empty(B, H, U, dtype=torch.int32, device=idx.device)
     fill = fill if fill is not None else torch.empty(B, H, U, dtype=torch.int32, device=idx.device)
@@ -368,10 +369,11 @@ def block_cache_plan(cache: "BlockCache", idx, cnt, slot=None, fill=None, n_fill
     return slot, fill, n_fill
 
 
-def prefetch_cache_fill(src_k, src_v, fill, slot, cache: "BlockCache", n_workgroups: int | None = None, stream=None,
-                        src_k_dev: int | None = None, src_v_dev: int | None = None):
-    """Copy the blocks `fill` names from src (device or pinned host) into
-    their cache slots."""
+def prefetch_cache_fill(src_k, src_v, idx, slot, fill, n_fill, cache: "BlockCache", n_workgroups: int | None = None,
+                        stream=None, src_k_dev: int | None = None, src_v_dev: int | None = None):
+    """Copy the blocks a cache lookup found missing (block idx[u] for the
+    list positions u in fill[:n_fill]) from src (device or pinned host) into
+    their cache slots slot[u]."""
     B, H, U = fill.shape
     d = src_k.shape[-1]
     if src_k.stride() != src_v.stride():
@@ -383,11 +385,11 @@ def prefetch_cache_fill(src_k, src_v, fill, slot, cache: "BlockCache", n_workgro
             raise ValueError("host sources must be pinned")
         pk = src_k_dev if src_k_dev is not None else host_device_pointer(src_k)
         pv = src_v_dev if src_v_dev is not None else host_device_pointer(src_v)
-    nwg = n_workgroups if n_workgroups is not None else max(1, min(B * H * U, 512))
+    nwg = n_workgroups if n_workgroups is not None else B * H
     sh = _stream(stream, cache.k.device)
-    _check(lib.bskv_prefetch_cache_fill(pk, pv, _dt(cache.k), _strides3(src_k), src_k.shape[2], _ptr(fill), _ptr(slot),
-                                        _ptr(cache.k), _ptr(cache.v), B, H, d, 64, U, cache.S, nwg, sh),
-           "prefetch_cache_fill")
+    _check(lib.bskv_prefetch_cache_fill(pk, pv, _dt(cache.k), _strides3(src_k), src_k.shape[2], _ptr(idx), _ptr(slot),
+                                        _ptr(fill), _ptr(n_fill), _ptr(cache.k), _ptr(cache.v), B, H, d, 64, U, cache.S,
+                                        nwg, sh), "prefetch_cache_fill")
 
 
 def block_sparse_attn_decode_cached(q, cache: "BlockCache", slot, idx, cnt, seq_len, scale: float | None = None,

@@ -289,7 +289,7 @@ int bskv_block_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int B
 int bskv_block_cache_plan(const int32_t* idx, const int32_t* cnt, int B, int n_kv_heads, int U, int32_t* tags,
                           int64_t* stamps, int64_t* clock, int n_slots, int32_t* slot_out, int32_t* fill_out,
                           int32_t* n_fill_out, hipStream_t stream) {
-  if (!idx || !cnt || !tags || !stamps || !clock || !slot_out || !fill_out) return BSKV_EINVAL;
+  if (!idx || !cnt || !tags || !stamps || !clock || !slot_out || !fill_out || !n_fill_out) return BSKV_EINVAL;
   if (B <= 0 || n_kv_heads <= 0 || U <= 0 || n_slots <= 0) return BSKV_EINVAL;
   if (U > n_slots) return BSKV_EINVAL;   // every listed block needs a slot
   if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
@@ -299,22 +299,21 @@ int bskv_block_cache_plan(const int32_t* idx, const int32_t* cnt, int B, int n_k
 }
 
 int bskv_prefetch_cache_fill(const void* src_k, const void* src_v, int dtype, const int64_t* src_strides,
-                             int64_t src_len, const int32_t* fill, const int32_t* slot, void* cache_k, void* cache_v,
-                             int B, int n_kv_heads, int head_dim, int block, int U, int n_slots, int n_workgroups,
-                             hipStream_t stream) {
+                             int64_t src_len, const int32_t* idx, const int32_t* slot, const int32_t* fill,
+                             const int32_t* n_fill, void* cache_k, void* cache_v, int B, int n_kv_heads, int head_dim,
+                             int block, int U, int n_slots, int n_workgroups, hipStream_t stream) {
   if (!dtype_ok(dtype)) return BSKV_EDTYPE;
-  if (!src_k || !src_v || !fill || !slot || !cache_k || !cache_v) return BSKV_EINVAL;
+  if (!src_k || !src_v || !idx || !slot || !fill || !n_fill || !cache_k || !cache_v) return BSKV_EINVAL;
   if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(cache_k) || !aligned16(cache_v)) return BSKV_EINVAL;
   if (B <= 0 || n_kv_heads <= 0 || U <= 0 || n_slots <= 0 || n_workgroups < 1 || src_len < 0 ||
       !strides_ok(src_strides, dtype))
     return BSKV_EINVAL;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
-  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads * U > 0x7fffffff || n_workgroups > 65535)
-    return BSKV_EUNSUPPORTED;
-  bskv::GatherArgs a{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype), fill,
-                     nullptr, cache_k, cache_v, B, n_kv_heads, head_dim, block, U, n_workgroups, stream, slot,
-                     n_slots};
-  return finish(bskv::launch_gather(a));
+  if (n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535 || n_workgroups > 65535) return BSKV_EUNSUPPORTED;
+  bskv::CacheFillArgs a{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype), idx,
+                        slot, fill, n_fill, cache_k, cache_v, B, n_kv_heads, head_dim, block, U, n_slots,
+                        n_workgroups, stream};
+  return finish(bskv::launch_cache_fill(a));
 }
 
 int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, const void* cache_v, int dtype,

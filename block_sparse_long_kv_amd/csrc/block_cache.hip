@@ -15,7 +15,9 @@
 // missing entries are numbered by a block scan over the list; the unlisted
 // slots are ranked by (stamp, slot) with one comparison per pair (S <= 1024
 // slots, a few thousand LDS reads per thread at most); the k-th missing entry
-// takes the slot of rank k.
+// takes the slot of rank k.  The copies are listed compactly (list positions
+// of the missing entries, in list order), so the copy kernel touches only
+// the (b, g) that miss something: at steady state most have nothing to copy.
 #include "bskv_device.hpp"
 #include "bskv_launch.hpp"
 
@@ -110,14 +112,14 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
   for (int e = 0; e < PPT; ++e) {
     const int u = u0 + e;
     if (u < c && sm.slot_of[u] < 0) {
-      const int s = sm.victim[rank++];
+      const int s = sm.victim[rank];
       sm.slot_of[u] = s;
       sm.tag[s] = sm.list[u];
-      fill_out[(int64_t)bg * U + u] = sm.list[u];
-    } else if (u < U) {
-      fill_out[(int64_t)bg * U + u] = -1;
+      fill_out[(int64_t)bg * U + rank] = u;   // the rank-th copy: list position u
+      ++rank;
     }
   }
+  for (int k = n_miss + tid; k < U; k += kThreads) fill_out[(int64_t)bg * U + k] = -1;
   __syncthreads();
   const int64_t now = clock[bg] + 1;
   for (int u = tid; u < U; u += kThreads) {
@@ -130,6 +132,72 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
     clock[bg] = now;
     if (n_fill_out) n_fill_out[bg] = n_miss;
   }
+}
+
+// Copy of the missing blocks into their slots: workgroup w takes the (b, g)
+// w, w + grid, ...; for each, its n_fill blocks one after another (K and V,
+// all 16-byte loads of a block issued before its stores, as in the ring
+// prefetch).  A (b, g) with nothing to copy costs one load.
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void cache_fill_kernel(const uint4* __restrict__ src_k,
+                                                            const uint4* __restrict__ src_v, int64_t sb, int64_t sg,
+                                                            int64_t st, int64_t src_len, int row16,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ slot,
+                                                            const int32_t* __restrict__ fill,
+                                                            const int32_t* __restrict__ n_fill,
+                                                            uint4* __restrict__ cache_k, uint4* __restrict__ cache_v,
+                                                            int H, int U, int S, int block, int n_bg) {
+  // strides sb, sg, st in 16-byte units; row16 = 16-byte chunks per token
+  const int per_item = block * row16;
+  for (int bg = blockIdx.x; bg < n_bg; bg += gridDim.x) {
+    const int nf = min(n_fill[bg], U);
+    const int b = bg / H, g = bg % H;
+    for (int k = 0; k < nf; ++k) {
+      const int u = fill[(int64_t)bg * U + k];
+      if (u < 0 || u >= U) continue;
+      const int j = idx[(int64_t)bg * U + u];
+      const int s = slot[(int64_t)bg * U + u];
+      if (j < 0 || ((int64_t)j + 1) * block > src_len || s < 0 || s >= S) continue;   // stay inside both buffers
+      const int64_t sbase = b * sb + g * sg + (int64_t)j * block * st;
+      const int64_t dbase = ((int64_t)bg * S + s) * per_item;
+      uint4 rk[CPT], rv[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int ch = threadIdx.x + i * kThreads;
+        if (ch < per_item) {
+          const int t = ch / row16, w = ch % row16;
+          rk[i] = src_k[sbase + t * st + w];
+          rv[i] = src_v[sbase + t * st + w];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int ch = threadIdx.x + i * kThreads;
+        if (ch < per_item) {
+          cache_k[dbase + ch] = rk[i];
+          cache_v[dbase + ch] = rv[i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_cache_fill(const CacheFillArgs& a) {
+  const int row16 = a.D * a.esize / 16;
+  const int per_item = a.block * row16;
+  const int n_bg = a.B * a.H;
+  const int64_t sb = a.sb * a.esize / 16, sg = a.sg * a.esize / 16, st = a.st * a.esize / 16;
+  const dim3 grid(a.n_workgroups < n_bg ? a.n_workgroups : n_bg);
+#define BSKV_FILL(CPT)                                                                                           \
+  hipLaunchKernelGGL(cache_fill_kernel<CPT>, grid, dim3(kThreads), 0, a.stream, (const uint4*)a.src_k,             \
+                     (const uint4*)a.src_v, sb, sg, st, a.src_len, row16, a.idx, a.slot, a.fill, a.n_fill,         \
+                     (uint4*)a.cache_k, (uint4*)a.cache_v, a.H, a.U, a.S, a.block, n_bg)
+  if (per_item <= 2 * kThreads) BSKV_FILL(2);
+  else if (per_item <= 4 * kThreads) BSKV_FILL(4);
+  else BSKV_FILL(8);
+#undef BSKV_FILL
+  return hipGetLastError();
 }
 
 hipError_t launch_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int n_bg, int S, hipStream_t stream) {

@@ -96,12 +96,10 @@ struct GatherArgs {
   const void* src_k; const void* src_v; int64_t sb, sg, st;  // element strides
   int64_t src_len;
   int esize;
-  const int32_t* idx; const int32_t* cnt;   // source block of entry u (< 0: skip); cnt nullable (all U)
+  const int32_t* idx; const int32_t* cnt;
   void* ring_k; void* ring_v;
   int B, H, D, block, U, n_workgroups;
   hipStream_t stream;
-  const int32_t* dst_slot = nullptr;        // destination slot of entry u (nullptr: slot u)
-  int S = 0;                                // destination slots per (b, g) (0: U)
 };
 hipError_t launch_gather(const GatherArgs& a);
 
@@ -114,6 +112,16 @@ struct CachePlanArgs {
   hipStream_t stream;
 };
 hipError_t launch_cache_plan(const CachePlanArgs& a);
+struct CacheFillArgs {
+  const void* src_k; const void* src_v; int64_t sb, sg, st;  // element strides
+  int64_t src_len;
+  int esize;
+  const int32_t* idx; const int32_t* slot; const int32_t* fill; const int32_t* n_fill;
+  void* cache_k; void* cache_v;
+  int B, H, D, block, U, S, n_workgroups;
+  hipStream_t stream;
+};
+hipError_t launch_cache_fill(const CacheFillArgs& a);
 hipError_t launch_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int n_bg, int S, hipStream_t stream);
 
 // One decode layer with lookahead selection of the next layer (3 kernels).

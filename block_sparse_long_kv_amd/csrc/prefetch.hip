@@ -25,19 +25,17 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restric
                                                         int64_t st, int64_t src_len, int row16, const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ cnt, uint4* __restrict__ ring_k,
                                                         uint4* __restrict__ ring_v, int H, int U, int block,
-                                                        int total, const int32_t* __restrict__ dst_slot, int S) {
+                                                        int total) {
   // strides sb, sg, st are in 16-byte units; row16 = 16-byte chunks per token
   const int per_item = block * row16;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int bg = item / U, u = item % U;
-    if (cnt && u >= cnt[bg]) continue;
+    if (u >= cnt[bg]) continue;
     const int j = idx[(int64_t)bg * U + u];
     if (j < 0 || ((int64_t)j + 1) * block > src_len) continue;  // never read outside the source
-    const int s = dst_slot ? dst_slot[(int64_t)bg * U + u] : u;
-    if (s < 0 || s >= S) continue;                               // never write outside the destination
     const int b = bg / H, g = bg % H;
     const int64_t sbase = b * sb + g * sg + (int64_t)j * block * st;
-    const int64_t dbase = ((int64_t)bg * S + s) * per_item;
+    const int64_t dbase = ((int64_t)bg * U + u) * per_item;
     uint4 rk[CPT], rv[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -68,7 +66,7 @@ hipError_t launch_gather(const GatherArgs& a) {
 #define BSKV_GATHER(CPT)                                                                                         \
   hipLaunchKernelGGL(gather_kernel<CPT>, grid, dim3(kThreads), 0, a.stream, (const uint4*)a.src_k,                 \
                      (const uint4*)a.src_v, sb, sg, st, a.src_len, row16, a.idx, a.cnt, (uint4*)a.ring_k, (uint4*)a.ring_v, a.H, \
-                     a.U, a.block, total, a.dst_slot, a.S > 0 ? a.S : a.U)
+                     a.U, a.block, total)
   if (per_item <= 2 * kThreads) BSKV_GATHER(2);
   else if (per_item <= 4 * kThreads) BSKV_GATHER(4);
   else BSKV_GATHER(8);

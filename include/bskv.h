@@ -324,13 +324,15 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
  *   updates the table, least recently used first: listed blocks already held
  *   keep their slot; the others take, in list order, the unlisted slots in
  *   order of (stamp, slot), empty slots first.  Writes slot_out [B, Hkv, U]
- *   (the slot of each listed block, -1 past cnt), fill_out [B, Hkv, U] (the
- *   block to copy into that slot, -1 when it is already held or past cnt)
- *   and, when not NULL, n_fill_out [B, Hkv] (the number of copies).
- *   Requires U <= n_slots.  One workgroup per (b, g).
- * bskv_prefetch_cache_fill copies the blocks fill_out names from a layer's
- *   K/V (device or host-mapped memory, as for bskv_prefetch_selected_blocks)
- *   into their slots; entries with fill < 0 are skipped.
+ *   (the slot of each listed block, -1 past cnt), n_fill_out [B, Hkv] (the
+ *   number of blocks to copy) and fill_out [B, Hkv, U]: its first n_fill
+ *   entries are the list positions u of the blocks to copy (the listed blocks
+ *   not held before), ascending; the rest -1.  Requires U <= n_slots.  One
+ *   workgroup per (b, g).
+ * bskv_prefetch_cache_fill copies those blocks (idx[u], from a layer's K/V
+ *   in device or host-mapped memory, as for bskv_prefetch_selected_blocks)
+ *   into their slots slot[u].  Workgroup w serves the (b, g) w, w +
+ *   n_workgroups, ...; a (b, g) with nothing to copy costs one load.
  * bskv_block_sparse_attn_decode_cached: bskv_block_sparse_attn_decode with
  *   listed block u (logical id idx[u], masked by seq_len) read from cache slot
  *   slot[u]; ws as bskv_attn_decode_workspace().
@@ -344,9 +346,9 @@ int bskv_block_cache_plan(const int32_t* idx, const int32_t* cnt, int B, int n_k
                           int64_t* stamps, int64_t* clock, int n_slots, int32_t* slot_out, int32_t* fill_out,
                           int32_t* n_fill_out, hipStream_t stream);
 int bskv_prefetch_cache_fill(const void* src_k, const void* src_v, int dtype, const int64_t* src_strides,
-                             int64_t src_len, const int32_t* fill, const int32_t* slot, void* cache_k, void* cache_v,
-                             int B, int n_kv_heads, int head_dim, int block, int U, int n_slots, int n_workgroups,
-                             hipStream_t stream);
+                             int64_t src_len, const int32_t* idx, const int32_t* slot, const int32_t* fill,
+                             const int32_t* n_fill, void* cache_k, void* cache_v, int B, int n_kv_heads, int head_dim,
+                             int block, int U, int n_slots, int n_workgroups, hipStream_t stream);
 int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, const void* cache_v, int dtype,
                                          int n_slots, const int32_t* slot, const int32_t* idx, const int32_t* cnt,
                                          const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,

@@ -510,9 +510,10 @@ def block_cache_plan(tags, stamps, clock, idx, cnt):
     idx    int [B, Hkv, U]   the blocks one layer needs (ascending, -1 padded)
     cnt    int [B, Hkv]      valid entries of idx
     Returns (slot [B, Hkv, U], fill [B, Hkv, U], n_fill [B, Hkv]): slot[u]
-    is the slot that holds idx[u] after the call; fill[u] = idx[u] when that
-    block has to be copied into the slot (it was not held), else -1; entries
-    u >= cnt are -1.  Needs cnt <= S.
+    is the slot that holds idx[u] after the call (-1 for u >= cnt); the
+    listed blocks that were not held have to be copied into their slots:
+    there are n_fill of them, and fill[:n_fill] lists their positions u in
+    the list, ascending (-1 after).  Needs cnt <= S.
     """
     B, H, U = idx.shape
     S = tags.shape[-1]
@@ -536,10 +537,10 @@ def block_cache_plan(tags, stamps, clock, idx, cnt):
             for u, j in enumerate(listed):           # the others take the least recently used slots
                 if slot[b, g, u] < 0:
                     s_new = free[k][1]
-                    k += 1
                     tags[b, g, s_new] = j
                     slot[b, g, u] = s_new
-                    fill[b, g, u] = j
+                    fill[b, g, k] = u
+                    k += 1
             n_fill[b, g] = k
             clock[b, g] += 1
             for u in range(c):

@@ -175,17 +175,22 @@ def test_block_cache_validation():
     assert lib.bskv_block_cache_reset(P, P, P, 2, 8, 0, None) == EINVAL
     assert lib.bskv_block_cache_reset(P, P, P, 2, 8, 2048, None) == EUNSUP
     plan = lib.bskv_block_cache_plan
-    assert plan(P, P, 2, 8, 69, P, P, P, 128, None, P, None, None) == EINVAL      # no slot output
-    assert plan(P, P, 2, 8, 129, P, P, P, 128, P, P, None, None) == EINVAL       # more list entries than slots
-    assert plan(P, P, 0, 8, 69, P, P, P, 128, P, P, None, None) == EINVAL
-    assert plan(P, P, 2, 8, 69, P, P, P, 4096, P, P, None, None) == EUNSUP
+    assert plan(P, P, 2, 8, 69, P, P, P, 128, None, P, P, None) == EINVAL      # no slot output
+    assert plan(P, P, 2, 8, 69, P, P, P, 128, P, P, None, None) == EINVAL      # no copy count
+    assert plan(P, P, 2, 8, 129, P, P, P, 128, P, P, P, None) == EINVAL       # more list entries than slots
+    assert plan(P, P, 0, 8, 69, P, P, P, 128, P, P, P, None) == EINVAL
+    assert plan(P, P, 2, 8, 69, P, P, P, 4096, P, P, P, None) == EUNSUP
     fillf = lib.bskv_prefetch_cache_fill
-    assert fillf(P, P, 5, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EDTYPE
-    assert fillf(P, P, 1, S3, 131072, None, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EINVAL
-    assert fillf(MIS, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 64, None) == EINVAL
-    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 128, 0, None) == EINVAL    # no workgroups
-    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 96, 64, 69, 128, 64, None) == EUNSUP
-    assert fillf(P, P, 1, S3, 131072, P, P, P, P, 2, 8, 128, 64, 69, 2048, 64, None) == EUNSUP
+
+    def fcall(src=P, dt=1, fill=P, nf=P, d=128, S=128, nwg=64):
+        return fillf(src, P, dt, S3, 131072, P, P, fill, nf, P, P, 2, 8, d, 64, 69, S, nwg, None)
+    assert fcall(dt=5) == EDTYPE
+    assert fcall(fill=None) == EINVAL
+    assert fcall(nf=None) == EINVAL
+    assert fcall(src=MIS) == EINVAL
+    assert fcall(nwg=0) == EINVAL
+    assert fcall(d=96) == EUNSUP
+    assert fcall(S=2048) == EUNSUP
     att = lib.bskv_block_sparse_attn_decode_cached
     ws = lib.bskv_attn_decode_workspace(2, 32, 8, 128, 69)
 

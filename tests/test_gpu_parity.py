@@ -681,7 +681,7 @@ def test_cache_fill_and_cached_attention_over_steps(host):
         ev = torch.cuda.Event()
         ev.record()
         side.wait_event(ev)
-        bskv.prefetch_cache_fill(src_k, src_v, fill, slot, cache, n_workgroups=64, stream=side)
+        bskv.prefetch_cache_fill(src_k, src_v, idx, slot, fill, n_fill, cache, n_workgroups=17, stream=side)
         done = torch.cuda.Event()
         done.record(side)
         torch.cuda.current_stream().wait_event(done)
@@ -696,7 +696,7 @@ def test_cache_fill_and_cached_attention_over_steps(host):
                 c = int(cn[b, h])
                 listed = set(gi[b, h, :c].tolist())
                 assert int(nf[b, h]) == len(listed - resident[b * wl.Hkv + h])
-                assert set(fl[b, h][fl[b, h] >= 0].tolist()) == listed - resident[b * wl.Hkv + h]
+                assert {int(gi[b, h, u]) for u in fl[b, h, :nf[b, h]]} == listed - resident[b * wl.Hkv + h]
                 resident[b * wl.Hkv + h] = set(cache.tags[b, h].cpu().numpy().tolist()) - {-1}
                 for u in range(c):
                     j = int(gi[b, h, u])

@@ -307,15 +307,17 @@ def test_block_cache_is_a_textbook_lru(S, U, universe, churn):
                     od[j] = True
                     od.move_to_end(j)
                 assert set(od) == {int(t) for t in tags[b, g] if t >= 0}
-                assert [int(j) for j in fill[b, g] if j >= 0] == missing
-                assert int(n_fill[b, g]) == len(missing)
+                nf = int(n_fill[b, g])
+                assert nf == len(missing)
+                assert [int(idx[b, g, u]) for u in fill[b, g, :nf]] == missing
+                assert (fill[b, g, nf:] == -1).all()
                 for u, j in enumerate(listed):
                     s = int(slot[b, g, u])
                     assert tags[b, g, s] == j
                     if j in before[b, g]:
                         assert before[b, g, s] == j            # a held block is never moved or copied again
                 assert len(set(slot[b, g, :c].tolist())) == c
-                assert (slot[b, g, c:] == -1).all() and (fill[b, g, c:] == -1).all()
+                assert (slot[b, g, c:] == -1).all()
 
 
 # --------------------------------------------------------------------------- baseline multi-head selector

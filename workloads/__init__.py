@@ -7,6 +7,7 @@ each compute everything from the tensors drawn here.
 from .configs import CONFIGS, Workload  # noqa: F401
 from .synth import (  # noqa: F401
     decode_inputs,
+    drift_walk,
     prefill_inputs,
     random_decode_case,
     random_prefill_case,

@@ -1,4 +1,4 @@
-"""The five workloads, by shape.
+"""The workloads, by shape.
 
 Shapes follow the pages' setting (64-token blocks, 8B-class heads: 32 query
 heads, 8 KV heads, head_dim 128, hidden 4096; 128K contexts; a 2048-token
@@ -33,6 +33,8 @@ class Workload:
     chunk: int | None = None         # prefill query-chunk length
     plant_frac: float | None = None  # prefill: fraction of blocks with an offset
     host_layers: int | None = None   # offload: distinct host KV layers (layer l uses l % host_layers)
+    plant: int | None = None         # decode: planted blocks per (b, g) (None: topk)
+    drift: float | None = None       # steady-state offload: random-walk step of the Forecast input per decode step
 
     @property
     def G(self) -> int:
@@ -64,4 +66,7 @@ CONFIGS = {
     5: Workload(5, "offload-decode-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128,
                 hidden=4096, T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=4,
                 host_layers=4),
+    6: Workload(6, "offload-steady-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128, hidden=4096,
+                T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=5, host_layers=4, plant=32,
+                drift=0.05),
 }

@@ -65,7 +65,7 @@ def decode_inputs(wl: Workload, device="cpu", layers: int | None = None, B: int 
     gen = _gen(wl.seed, device)
     cur = (T - 1) // wl.block
     n_cand = cur - wl.n_local - wl.n_init + 1
-    n_plant = min(wl.topk, max(n_cand, 0))
+    n_plant = min(wl.topk if wl.plant is None else wl.plant, max(n_cand, 0))
     out = []
     for _ in range(L):
         lay = {}
@@ -94,6 +94,21 @@ def decode_inputs(wl: Workload, device="cpu", layers: int | None = None, B: int 
         lay["planted"] = planted
         lay["seq_len"] = torch.full((B,), T, dtype=torch.int64, device=device)
         out.append(lay)
+    return out
+
+
+def drift_walk(x0, n_steps: int, step: float, seed: int):
+    """Forecast inputs of successive decode steps: a random walk from x0,
+    x_t = (x_{t-1} + step * e_t) / sqrt(1 + step^2) with e_t ~ N(0, I), which
+    keeps the entries' variance.  x0: [..., hidden]; returns
+    [n_steps, ..., hidden] of x0's dtype (x_0 itself excluded)."""
+    gen = _gen(seed, x0.device)
+    x = x0.float()
+    out = torch.empty((n_steps,) + tuple(x0.shape), dtype=x0.dtype, device=x0.device)
+    norm = (1.0 + step * step) ** 0.5
+    for t in range(n_steps):
+        x = (x + step * torch.randn(x.shape, generator=gen, device=x.device)) / norm
+        out[t] = x.to(x0.dtype)
     return out
 
 
