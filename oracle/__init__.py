@@ -20,7 +20,10 @@ from .sparda_ref import (  # noqa: F401
     kv_window_meanpool,
     multihead_select_decode,
     prefill_select,
+    prefill_select_pooled,
     prefill_select_windows,
+    qkvf_proj,
+    qkvf_proj_prefill,
     rank_topk,
     window_block_scores,
 )

@@ -58,6 +58,10 @@ function that uses it):
       take, in list order, the unlisted slots in order of (last use, slot),
       empty slots first; every listed slot is then stamped with
       (call number, list position).
+  R18 Widened projection: the columns of the layer's projection matrix are
+      the query heads, then the key, value and Forecast heads (head_dim
+      columns each); in prefill only each query block's summed Forecast
+      leaves the projection (R8).
   R14 Baseline multi-head selector (decode): the G query heads of a KV group
       each score the candidates against the compressed keys, the G score rows
       are summed, the sum times the attention scale goes through a softmax over
@@ -97,6 +101,57 @@ def forecast_proj(x, w, n_kv_heads: int, head_dim: int) -> np.ndarray:
     if w.shape != (hidden, n_kv_heads * head_dim):
         raise ValueError(f"w shape {w.shape} != ({hidden}, {n_kv_heads * head_dim})")
     return np.matmul(x, w).reshape(B, n_kv_heads, head_dim)
+
+
+def qkvf_proj(x, w, n_q_heads: int, n_kv_heads: int, head_dim: int):
+    """The widened per-layer projection of one decode token:
+    (Q, K, V, F) = x @ [W_Q | W_K | W_V | W_F].
+
+    [EXPL] "The fourth projection", Eq. 3: the layer's existing linear
+    projection, widened by one small head group, emits the Forecast next to
+    Q, K and V.  Reading R18: the columns of w are the query heads, then the
+    key heads, the value heads and the Forecast heads (n_kv_heads of each
+    of the last three), head_dim columns per head.  x: [B, hidden]; w:
+    [hidden, (n_q_heads + 3 n_kv_heads) * head_dim].  Returns q [B, Hq, d],
+    k, v, f [B, Hkv, d] (float64).
+    """
+    x = _f64(x)
+    w = _f64(w)
+    B, hidden = x.shape
+    Hq, H, d = n_q_heads, n_kv_heads, head_dim
+    if w.shape != (hidden, (Hq + 3 * H) * d):
+        raise ValueError(f"w shape {w.shape} != ({hidden}, {(Hq + 3 * H) * d})")
+    y = np.matmul(x, w)
+    q = y[:, : Hq * d].reshape(B, Hq, d)
+    k = y[:, Hq * d: (Hq + H) * d].reshape(B, H, d)
+    v = y[:, (Hq + H) * d: (Hq + 2 * H) * d].reshape(B, H, d)
+    f = y[:, (Hq + 2 * H) * d:].reshape(B, H, d)
+    return q, k, v, f
+
+
+def qkvf_proj_prefill(x, w, n_q_heads: int, n_kv_heads: int, head_dim: int, block: int):
+    """The widened projection of a prefill chunk, with the Forecast summed
+    per query block instead of kept per token.
+
+    [EXPL] "The fourth projection", Eq. 3 and Alg. 1; reading R8: a query
+    block's selection uses the sum of its tokens' Forecast vectors, so only
+    that sum leaves the projection.  x: [B, Tq, hidden].  Returns q
+    [B, Hq, Tq, d], k, v [B, Hkv, Tq, d] and f_pooled [B, Hkv, ceil(Tq /
+    block), d] (the last query block may be partial).
+    """
+    x = _f64(x)
+    B, Tq, hidden = x.shape
+    Hq, H, d = n_q_heads, n_kv_heads, head_dim
+    q = np.zeros((B, Hq, Tq, d))
+    k = np.zeros((B, H, Tq, d))
+    v = np.zeros((B, H, Tq, d))
+    n_qb = -(-Tq // block)
+    f_pooled = np.zeros((B, H, n_qb, d))
+    for t in range(Tq):
+        qt, kt, vt, ft = qkvf_proj(x[:, t], w, Hq, H, d)
+        q[:, :, t], k[:, :, t], v[:, :, t] = qt, kt, vt
+        f_pooled[:, :, t // block] += ft
+    return q, k, v, f_pooled
 
 
 # --------------------------------------------------------------------------
@@ -396,6 +451,36 @@ def prefill_select_windows(f_tok, kcw, q_start: int, topk: int, n_init: int, n_l
                 for j in cand:
                     touch = seen & (w_start + window > block * j) & (w_start < block * (j + 1))
                     scores[j] = float(wsc[touch].max()) if touch.any() else -np.inf
+                top = rank_topk(scores, topk)
+                idx[b, g, qi], cnt[b, g, qi] = _union(init, local, top, cap)
+                tops.append(top)
+                all_scores.append(scores)
+    return Selection(idx, cnt, tops, all_scores)
+
+
+def prefill_select_pooled(f_pooled, kc, q_start: int, topk: int, n_init: int, n_local: int, block: int) -> Selection:
+    """prefill_select from the summed Forecast of each query block.
+
+    Reading R8: query block qi scores block j by F_pooled[qi] . K~_j, with
+    F_pooled[qi] the sum of its tokens' Forecast vectors (as the widened
+    projection delivers it).  f_pooled: [B, Hkv, n_qb, d]; kc:
+    [B, Hkv, NB, d]; the chunk starts at q_start (a multiple of block).
+    """
+    f_pooled = _f64(f_pooled)
+    kc = _f64(kc)
+    B, H, n_qb, d = f_pooled.shape
+    if q_start % block:
+        raise ValueError("q_start must be a multiple of block")
+    cap = topk + n_init + n_local
+    idx = np.full((B, H, n_qb, cap), -1, dtype=np.int64)
+    cnt = np.zeros((B, H, n_qb), dtype=np.int64)
+    tops, all_scores = [], []
+    for b in range(B):
+        for g in range(H):
+            for qi in range(n_qb):
+                qb = q_start // block + qi
+                init, local, cand = block_sets(qb, n_init, n_local)
+                scores = {j: float(np.dot(f_pooled[b, g, qi], kc[b, g, j])) for j in cand}
                 top = rank_topk(scores, topk)
                 idx[b, g, qi], cnt[b, g, qi] = _union(init, local, top, cap)
                 tops.append(top)

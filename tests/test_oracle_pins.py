@@ -106,6 +106,95 @@ def test_golden_decode_select_and_attend(golden_dir):
     np.testing.assert_allclose(out[0, 0], gx["out_expected"], rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- widened projection (R18)
+def test_qkvf_proj_triple_loop():
+    """Small integer inputs, every output element from an explicit sum over
+    the hidden axis with the column map written out: query heads first, then
+    key, value and Forecast heads."""
+    rng = np.random.default_rng(1)
+    B, hidden, Hq, H, d = 2, 5, 4, 2, 3
+    x = rng.integers(-4, 5, size=(B, hidden)).astype(np.float64)
+    w = rng.integers(-4, 5, size=(hidden, (Hq + 3 * H) * d)).astype(np.float64)
+    q, k, v, f = orc.qkvf_proj(x, w, Hq, H, d)
+
+    def col_sum(b, c):
+        return sum(x[b, i] * w[i, c] for i in range(hidden))
+    for b in range(B):
+        for h in range(Hq):
+            for e in range(d):
+                assert q[b, h, e] == col_sum(b, h * d + e)
+        for g in range(H):
+            for e in range(d):
+                assert k[b, g, e] == col_sum(b, (Hq + g) * d + e)
+                assert v[b, g, e] == col_sum(b, (Hq + H + g) * d + e)
+                assert f[b, g, e] == col_sum(b, (Hq + 2 * H + g) * d + e)
+
+
+def test_qkvf_forecast_part_is_the_forecast_projection():
+    rng = np.random.default_rng(2)
+    B, hidden, Hq, H, d = 3, 16, 8, 2, 4
+    x = rng.standard_normal((B, hidden))
+    w = rng.standard_normal((hidden, (Hq + 3 * H) * d))
+    f = orc.qkvf_proj(x, w, Hq, H, d)[3]
+    np.testing.assert_allclose(f, orc.forecast_proj(x, w[:, (Hq + 2 * H) * d:], H, d), rtol=1e-13, atol=1e-13)
+
+
+def test_qkvf_prefill_pools_the_forecast_per_query_block():
+    """Per-token Q/K/V equal the one-token projection; the pooled Forecast
+    equals the plain sum of the tokens' Forecast vectors, block by block,
+    with a partial last block."""
+    rng = np.random.default_rng(3)
+    B, Tq, hidden, Hq, H, d, blk = 2, 11, 6, 2, 1, 3, 4
+    x = rng.standard_normal((B, Tq, hidden))
+    w = rng.standard_normal((hidden, (Hq + 3 * H) * d))
+    q, k, v, fp = orc.qkvf_proj_prefill(x, w, Hq, H, d, blk)
+    assert fp.shape == (B, H, 3, d)
+    f_tok = np.einsum("bth,hc->btc", x, w[:, (Hq + 2 * H) * d:]).reshape(B, Tq, H, d)
+    for t in range(Tq):
+        qt, kt, vt, _ = orc.qkvf_proj(x[:, t], w, Hq, H, d)
+        np.testing.assert_allclose(q[:, :, t], qt, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(k[:, :, t], kt, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(v[:, :, t], vt, rtol=1e-13, atol=1e-13)
+    for qi, (t0, t1) in enumerate([(0, 4), (4, 8), (8, 11)]):
+        np.testing.assert_allclose(fp[:, :, qi], f_tok[:, t0:t1].sum(axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_golden_prefill_select_pooled(golden_dir):
+    """The hand-worked prefill chunk, selected from each query block's summed
+    Forecast: the same scores and block sets as per-token scoring (R8)."""
+    gx = _load(golden_dir, "prefill_select_attend_hand.json")
+    blk, d, Tq = gx["block"], gx["d"], gx["Tq"]
+    keys = np.array(gx["keys"], dtype=np.float64).reshape(1, 1, Tq, d)
+    f = np.array(gx["f"], dtype=np.float64).reshape(1, 1, Tq // blk, blk, d).sum(axis=3)
+    kc = orc.kv_block_meanpool(keys, blk)
+    sel = orc.prefill_select_pooled(f, kc, gx["q_start"], gx["topk"], gx["n_init"], gx["n_local"], blk)
+    assert {str(j): s for j, s in sel.scores[3].items()} == gx["scores_qb3_expected"]
+    assert sel.idx[0, 0].tolist() == gx["idx_expected"]
+    assert sel.cnt[0, 0].tolist() == gx["cnt_expected"]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_select_pooled_equals_per_token_selection(seed):
+    rng = np.random.default_rng(400 + seed)
+    B, H, d, blk, T = 2, 2, 5, 4, 4 * 12
+    q_start, Tq = 16, 27
+    k = rng.standard_normal((B, H, T, d))
+    f = rng.standard_normal((B, H, Tq, d))
+    kc = orc.kv_block_meanpool(k, blk)
+    n_qb = -(-Tq // blk)
+    fp = np.zeros((B, H, n_qb, d))
+    for t in range(Tq):
+        fp[:, :, t // blk] += f[:, :, t]
+    a = orc.prefill_select_pooled(fp, kc, q_start, 3, 1, 2, blk)
+    b = orc.prefill_select(f, kc, q_start, 3, 1, 2, blk)
+    np.testing.assert_array_equal(a.idx, b.idx)
+    np.testing.assert_array_equal(a.cnt, b.cnt)
+    for sa, sb in zip(a.scores, b.scores):
+        assert sa.keys() == sb.keys()
+        for j in sa:
+            assert abs(sa[j] - sb[j]) <= 1e-12 * (1 + abs(sb[j]))
+
+
 # --------------------------------------------------------------------------- overlapping compression (R15)
 def test_golden_window_select(golden_dir):
     gx = _load(golden_dir, "window_select_hand.json")
