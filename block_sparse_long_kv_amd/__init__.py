@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     block_sparse_attn_prefill,
     decode_layer_lookahead,
     forecast_block_score_topk,
+    forecast_block_score_topk_pooled,
     forecast_proj,
     forecast_window_score_topk,
     host_device_pointer,
@@ -26,5 +27,7 @@ from ._lib import (  # noqa: F401
     multihead_block_score_topk,
     prefetch_cache_fill,
     prefetch_selected_blocks,
+    qkvf_proj_decode,
+    qkvf_proj_prefill,
     workspace_bytes,
 )

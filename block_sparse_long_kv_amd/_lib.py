@@ -49,6 +49,12 @@ _proto("bskv_block_sparse_attn_prefill", _i, _p, _p, _p, _i, ctypes.POINTER(_i64
 _proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i,
        _i, _i, _p)
 _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
+_proto("bskv_qkvf_proj_workspace", _sz, _i, _i, _i, _i, _i)
+_proto("bskv_qkvf_proj_decode", _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p, _p, _p, _sz,
+       _p)
+_proto("bskv_qkvf_proj_prefill", _i, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p,
+       _p)
+_proto("bskv_forecast_block_score_topk_pooled", _i, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p)
 _proto("bskv_block_cache_reset", _i, _p, _p, _p, _i, _i, _i, _p)
 _proto("bskv_block_cache_plan", _i, _p, _p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p)
 _proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
@@ -106,7 +112,8 @@ def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
           "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace,
           "multihead": lib.bskv_multihead_score_topk_workspace,
-          "window": lib.bskv_window_score_topk_workspace}[kind]
+          "window": lib.bskv_window_score_topk_workspace,
+          "qkvf": lib.bskv_qkvf_proj_workspace}[kind]
     return int(fn(*args))
 
 
@@ -332,6 +339,68 @@ def prefetch_selected_blocks(src_k, src_v, idx, cnt, ring_k, ring_v, n_workgroup
                                              _ptr(ring_k), _ptr(ring_v), B, H, d, 64, U, nwg, sh),
            "prefetch_selected_blocks")
     return ring_k, ring_v
+
+
+def qkvf_proj_decode(x, w, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, seq_len, q_out=None, f_out=None,
+                     ws=None, stream=None):
+    """Widened projection of one token per sequence: returns (q bf16
+    [B, Hq, d], f fp32 [B, Hkv, d]); the token's K/V go into the caches at
+    position seq_len - 1."""
+    B, hidden = x.shape
+    d = k_cache.shape[-1]
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
+        raise TypeError("bf16 only")
+    if k_cache.stride() != v_cache.stride() or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x, w contiguous; k/v caches with identical strides")
+    q_out = q_out if q_out is not None else torch.empty(B, n_q_heads, d, dtype=torch.bfloat16, device=x.device)
+    f_out = f_out if f_out is not None else torch.empty(B, n_kv_heads, d, dtype=torch.float32, device=x.device)
+    sh = _stream(stream, x.device)
+    lay = (B, hidden, n_q_heads, n_kv_heads, d)
+    nbytes = workspace_bytes("qkvf", *lay)
+    ws = ws if ws is not None else _workspace(x.device, nbytes, sh, "qkvf", lay)
+    _check(lib.bskv_qkvf_proj_decode(_ptr(x), _ptr(w), B, hidden, n_q_heads, n_kv_heads, d, _ptr(q_out), _ptr(k_cache),
+                                     _ptr(v_cache), _strides3(k_cache), k_cache.shape[2], _ptr(seq_len), _ptr(f_out),
+                                     _ptr(ws), ws.numel() * ws.element_size(), sh), "qkvf_proj_decode")
+    return q_out, f_out
+
+
+def qkvf_proj_prefill(x, w, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, q_start: int = 0, q_out=None,
+                      f_pooled=None, stream=None):
+    """Widened projection of a prefill chunk x [B, Tq, hidden]: returns (q bf16
+    [B, Hq, Tq, d], f_pooled fp32 [B, Hkv, ceil(Tq/64), d]); K/V go into the
+    caches at positions q_start + t."""
+    B, Tq, hidden = x.shape
+    d = k_cache.shape[-1]
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
+        raise TypeError("bf16 only")
+    if k_cache.stride() != v_cache.stride() or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x, w contiguous; k/v caches with identical strides")
+    n_qb = -(-Tq // 64)
+    q_out = q_out if q_out is not None else torch.empty(B, n_q_heads, Tq, d, dtype=torch.bfloat16, device=x.device)
+    f_pooled = f_pooled if f_pooled is not None else torch.empty(B, n_kv_heads, n_qb, d, dtype=torch.float32,
+                                                                 device=x.device)
+    sh = _stream(stream, x.device)
+    _check(lib.bskv_qkvf_proj_prefill(_ptr(x), _ptr(w), B, Tq, hidden, n_q_heads, n_kv_heads, d, q_start, _ptr(q_out),
+                                      _ptr(k_cache), _ptr(v_cache), _strides3(k_cache), k_cache.shape[2],
+                                      _ptr(f_pooled), sh), "qkvf_proj_prefill")
+    return q_out, f_pooled
+
+
+def forecast_block_score_topk_pooled(f_pooled, kc, topk: int, n_init: int, n_local: int, q_start: int = 0, idx=None,
+                                     cnt=None, stream=None):
+    """Prefill selection from each query block's summed Forecast
+    f_pooled [B, Hkv, n_qb, d] fp32: (idx [B, Hkv, n_qb, U], cnt [B, Hkv, n_qb])."""
+    B, H, n_qb, d = f_pooled.shape
+    U = topk + n_init + n_local
+    if f_pooled.dtype != torch.float32 or not f_pooled.is_contiguous():
+        raise ValueError("f_pooled must be contiguous fp32")
+    idx = idx if idx is not None else torch.empty(B, H, n_qb, U, dtype=torch.int32, device=f_pooled.device)
+    cnt = cnt if cnt is not None else torch.empty(B, H, n_qb, dtype=torch.int32, device=f_pooled.device)
+    sh = _stream(stream, f_pooled.device)
+    _check(lib.bskv_forecast_block_score_topk_pooled(_ptr(f_pooled), n_qb, q_start, _ptr(kc), kc.shape[2], B, H, d, 64,
+                                                     topk, n_init, n_local, _ptr(idx), _ptr(cnt), sh),
+           "forecast_block_score_topk_pooled")
+    return idx, cnt
 
 
 class BlockCache:

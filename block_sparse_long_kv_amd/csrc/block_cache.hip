@@ -164,20 +164,16 @@ __global__ __launch_bounds__(kThreads) void cache_fill_kernel(const uint4* __res
       uint4 rk[CPT], rv[CPT];
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int ch = threadIdx.x + i * kThreads;
-        if (ch < per_item) {
-          const int t = ch / row16, w = ch % row16;
-          rk[i] = src_k[sbase + t * st + w];
-          rv[i] = src_v[sbase + t * st + w];
-        }
+        const int ch = threadIdx.x + i * kThreads;   // per_item == CPT * kThreads
+        const int t = ch / row16, w = ch % row16;
+        rk[i] = src_k[sbase + t * st + w];
+        rv[i] = src_v[sbase + t * st + w];
       }
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int ch = threadIdx.x + i * kThreads;
-        if (ch < per_item) {
-          cache_k[dbase + ch] = rk[i];
-          cache_v[dbase + ch] = rv[i];
-        }
+        cache_k[dbase + ch] = rk[i];
+        cache_v[dbase + ch] = rv[i];
       }
     }
   }
@@ -193,8 +189,9 @@ hipError_t launch_cache_fill(const CacheFillArgs& a) {
   hipLaunchKernelGGL(cache_fill_kernel<CPT>, grid, dim3(kThreads), 0, a.stream, (const uint4*)a.src_k,             \
                      (const uint4*)a.src_v, sb, sg, st, a.src_len, row16, a.idx, a.slot, a.fill, a.n_fill,         \
                      (uint4*)a.cache_k, (uint4*)a.cache_v, a.H, a.U, a.S, a.block, n_bg)
-  if (per_item <= 2 * kThreads) BSKV_FILL(2);
-  else if (per_item <= 4 * kThreads) BSKV_FILL(4);
+  // per_item = 64 rows x (head_dim x element size / 16) = 512, 1024 or 2048 chunks
+  if (per_item == 2 * kThreads) BSKV_FILL(2);
+  else if (per_item == 4 * kThreads) BSKV_FILL(4);
   else BSKV_FILL(8);
 #undef BSKV_FILL
   return hipGetLastError();

@@ -25,6 +25,31 @@ struct ProjArgs {
 };
 size_t proj_workspace_bytes(int B, int hidden, int N, int dtype);
 hipError_t launch_proj(const ProjArgs& a);
+int proj_splits(int hidden);
+template <typename T>
+void launch_proj_partial(const void* x, const void* w, int B, int hidden, int N, float* part, hipStream_t s);
+
+// Widened projection (Q, K, V, F) = X [W_Q | W_K | W_V | W_F], bf16.
+struct QkvfDecodeArgs {
+  const void* x; const void* w;
+  int B, hidden, Hq, H, D;
+  void* q; void* k; void* v; int64_t sb, sg, st, kv_len; const int64_t* seq_len;
+  float* f; void* ws;
+  hipStream_t stream;
+};
+size_t qkvf_decode_workspace_bytes(int B, int hidden, int N);
+hipError_t launch_qkvf_decode(const QkvfDecodeArgs& a);
+struct QkvfPrefillArgs {
+  const void* x; const void* w;
+  int B, Tq, hidden, Hq, H, D; int64_t q_start;
+  void* q; void* k; void* v; int64_t sb, sg, st, kv_len;
+  float* f_pooled;
+  hipStream_t stream;
+};
+hipError_t launch_qkvf_prefill(const QkvfPrefillArgs& a);
+hipError_t launch_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,
+                                   int64_t nb_cap, int B, int H, int D, int topk, int n_init, int n_local,
+                                   int32_t* idx, int32_t* cnt, hipStream_t stream);
 
 struct ScoreTopkArgs {
   const void* f; int f_dtype; int n_q_tokens; int64_t q_start;

@@ -39,20 +39,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restric
     uint4 rk[CPT], rv[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int ch = threadIdx.x + i * kThreads;
-      if (ch < per_item) {
-        const int t = ch / row16, w = ch % row16;
-        rk[i] = src_k[sbase + t * st + w];
-        rv[i] = src_v[sbase + t * st + w];
-      }
+      const int ch = threadIdx.x + i * kThreads;   // per_item == CPT * kThreads
+      const int t = ch / row16, w = ch % row16;
+      rk[i] = src_k[sbase + t * st + w];
+      rv[i] = src_v[sbase + t * st + w];
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = threadIdx.x + i * kThreads;
-      if (ch < per_item) {
-        ring_k[dbase + ch] = rk[i];
-        ring_v[dbase + ch] = rv[i];
-      }
+      ring_k[dbase + ch] = rk[i];
+      ring_v[dbase + ch] = rv[i];
     }
   }
 }
@@ -67,8 +63,9 @@ hipError_t launch_gather(const GatherArgs& a) {
   hipLaunchKernelGGL(gather_kernel<CPT>, grid, dim3(kThreads), 0, a.stream, (const uint4*)a.src_k,                 \
                      (const uint4*)a.src_v, sb, sg, st, a.src_len, row16, a.idx, a.cnt, (uint4*)a.ring_k, (uint4*)a.ring_v, a.H, \
                      a.U, a.block, total)
-  if (per_item <= 2 * kThreads) BSKV_GATHER(2);
-  else if (per_item <= 4 * kThreads) BSKV_GATHER(4);
+  // per_item = 64 rows x (head_dim x element size / 16) = 512, 1024 or 2048 chunks
+  if (per_item == 2 * kThreads) BSKV_GATHER(2);
+  else if (per_item == 4 * kThreads) BSKV_GATHER(4);
   else BSKV_GATHER(8);
 #undef BSKV_GATHER
   return hipGetLastError();

@@ -52,7 +52,9 @@ __device__ __forceinline__ void load_fvec(const float* src, float4* fv) {
 // block's Forecast vectors (fp32), scores every candidate compressed key
 // into LDS and runs the top-k + union.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// POOLED: f already holds each query block's Forecast sum, fp32
+// [B*H, n_qb, D] (as the widened projection writes it); Tq is unused.
+template <typename T, int D, bool POOLED = false>
 __global__ __launch_bounds__(kThreads) void score_topk_prefill_kernel(
     const T* __restrict__ f, int Tq, int64_t q_start, const float* __restrict__ kc, int64_t nb_cap, int H, int block,
     int topk, int n_init, int n_local, int U, int n_qb, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
@@ -61,9 +63,14 @@ __global__ __launch_bounds__(kThreads) void score_topk_prefill_kernel(
   __shared__ PoolRowsSmem<T, D> ps;
 
   const int qi = blockIdx.x, bg = blockIdx.y;
-  const int t0 = qi * block, t1 = min(Tq, t0 + block);
-  // pooled Forecast of the query block: sum of its tokens' vectors
-  pool_rows<T, D>(f + ((int64_t)bg * Tq + t0) * D, t1 - t0, ps);
+  if constexpr (POOLED) {
+    for (int t = threadIdx.x; t < D; t += kThreads) ps.fpool[t] = f[((int64_t)bg * n_qb + qi) * D + t];
+    __syncthreads();
+  } else {
+    // pooled Forecast of the query block: sum of its tokens' vectors
+    const int t0 = qi * block, t1 = min(Tq, t0 + block);
+    pool_rows<T, D>(f + ((int64_t)bg * Tq + t0) * D, t1 - t0, ps);
+  }
   const int cur = (int)(q_start / block) + qi;
   const int c0 = n_init, c1 = min(cur - n_local + 1, (int)nb_cap);
   const int n = max(0, c1 - c0);
@@ -82,6 +89,22 @@ hipError_t launch_score_topk_decode(const ScoreTopkArgs& a);
 size_t score_topk_workspace_bytes(int B, int H, int n_q_tokens, int64_t nb_cap, int D) {
   (void)D;
   return n_q_tokens > 0 ? 0 : score_decode_workspace_bytes(B, H, nb_cap);
+}
+
+hipError_t launch_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,
+                                   int64_t nb_cap, int B, int H, int D, int topk, int n_init, int n_local,
+                                   int32_t* idx, int32_t* cnt, hipStream_t stream) {
+  const int64_t cand_cap = nb_cap < kMaxCandidates ? nb_cap : kMaxCandidates;
+  const size_t lds = (size_t)cand_cap * sizeof(uint32_t);
+  const dim3 grid(n_qb, B * H);
+  const int U = topk + n_init + n_local;
+  if (D == 64)
+    hipLaunchKernelGGL((score_topk_prefill_kernel<float, 64, true>), grid, dim3(kThreads), lds, stream, f_pooled, 0,
+                       q_start, kc, nb_cap, H, 64, topk, n_init, n_local, U, n_qb, idx, cnt);
+  else
+    hipLaunchKernelGGL((score_topk_prefill_kernel<float, 128, true>), grid, dim3(kThreads), lds, stream, f_pooled, 0,
+                       q_start, kc, nb_cap, H, 64, topk, n_init, n_local, U, n_qb, idx, cnt);
+  return hipGetLastError();
 }
 
 hipError_t launch_score_topk(const ScoreTopkArgs& a) {

@@ -205,6 +205,46 @@ def test_block_cache_validation():
     assert call(wsb=ws - 4) == ENOSPC
 
 
+def test_qkvf_proj_validation():
+    ws = lib.bskv_qkvf_proj_workspace(8, 4096, 32, 8, 128)
+    assert ws >= 16 * 8 * (32 + 24) * 128 * 4
+    assert lib.bskv_qkvf_proj_workspace(8, 4096, 32, 8, 96) == 0
+    dec = lib.bskv_qkvf_proj_decode
+
+    def dcall(x=P, B=8, hidden=4096, hq=32, hkv=8, d=128, sl=P, wsb=ws):
+        return dec(x, P, B, hidden, hq, hkv, d, P, P, P, S3, 131072, sl, P, P, wsb, None)
+    assert dcall(x=None) == EINVAL
+    assert dcall(x=MIS) == EINVAL
+    assert dcall(sl=None) == EINVAL
+    assert dcall(d=96) == EUNSUP
+    assert dcall(hidden=4000) == EUNSUP
+    assert dcall(hq=3, hkv=2, d=64) == EUNSUP          # 9 heads of 64 columns: not a whole number of 128-column tiles
+    assert dcall(wsb=ws - 4) == ENOSPC
+    pre = lib.bskv_qkvf_proj_prefill
+
+    def pcall(B=4, tq=2048, hidden=4096, hq=32, hkv=8, d=128, q0=0, kv_len=131072, fp=P):
+        return pre(P, P, B, tq, hidden, hq, hkv, d, q0, P, P, P, S3, kv_len, fp, None)
+    assert pcall(fp=None) == EINVAL
+    assert pcall(fp=MIS) == EINVAL
+    assert pcall(q0=32) == EINVAL                     # chunk start off the block grid
+    assert pcall(q0=131072 - 1024) == EINVAL          # chunk past the cache
+    assert pcall(tq=0) == EINVAL
+    assert pcall(d=96) == EUNSUP
+    assert pcall(hidden=4000) == EUNSUP
+    assert pcall(hkv=1, d=64) == EUNSUP               # a 64-column head group would straddle a tile
+    pooled = lib.bskv_forecast_block_score_topk_pooled
+
+    def scall(fp=P, nqb=32, q0=0, d=128, blk=64, ni=1, nl=4, cap=2048):
+        return pooled(fp, nqb, q0, P, cap, 4, 8, d, blk, 64, ni, nl, P, P, None)
+    assert scall(fp=None) == EINVAL
+    assert scall(nqb=0) == EINVAL
+    assert scall(q0=32) == EINVAL
+    assert scall(ni=0) == EINVAL
+    assert scall(d=96) == EUNSUP
+    assert scall(blk=128) == EUNSUP
+    assert scall(cap=20000) == EUNSUP
+
+
 def test_attn_decode_validation():
     f = lib.bskv_block_sparse_attn_decode
     ws = lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69)

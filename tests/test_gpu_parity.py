@@ -595,6 +595,88 @@ def test_prefetch_from_pinned_host_and_ring_attention():
     assert max_abs(np64(out_ring), want_o) < 2e-2
 
 
+# ----------------------------------------------------------------------------- widened projection
+def _bf16_close(got, want, rel=2.0 ** -8, abs_tol=1e-3):
+    """bf16 outputs of fp32 sums against the fp64 oracle: one rounding to
+    bf16 (half an ulp, 2^-9 relative) plus the fp32 summation error."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return bool(np.all(np.abs(got - want) <= rel * np.abs(want) + abs_tol))
+
+
+@pytest.mark.parametrize("B,hidden,Hq,Hkv,d", [(3, 512, 8, 2, 128), (16, 4096, 32, 8, 128), (5, 768, 4, 4, 64)])
+def test_qkvf_proj_decode(B, hidden, Hq, Hkv, d):
+    g = torch.Generator().manual_seed(B + hidden)
+    x = torch.randn(B, hidden, generator=g).to(torch.bfloat16)
+    w = (torch.randn(hidden, (Hq + 3 * Hkv) * d, generator=g) * 0.02).to(torch.bfloat16)
+    T = 64 * 4
+    kc = torch.full((B, Hkv, T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    lens = torch.tensor([(37 * b) % T + 1 for b in range(B)], dtype=torch.int64)
+    q, f = bskv.qkvf_proj_decode(x.to(DEV), w.to(DEV), Hq, Hkv, kc, vc, lens.to(DEV))
+    torch.cuda.synchronize()
+    wq, wk, wv, wf = orc.qkvf_proj(np64(x), np64(w), Hq, Hkv, d)
+    assert _bf16_close(np64(q), wq)
+    assert max_abs(np64(f), wf) < 1e-3
+    kn, vn = np64(kc), np64(vc)
+    for b, L in enumerate(lens.tolist()):
+        assert _bf16_close(kn[b, :, L - 1], wk[b]) and _bf16_close(vn[b, :, L - 1], wv[b])
+        rest = np.delete(kn[b], L - 1, axis=1)
+        assert np.isnan(rest).all(), "only the new token's row is written"
+
+
+@pytest.mark.parametrize("B,Tq,hidden,Hq,Hkv,d,q_start", [(2, 256, 512, 8, 2, 128, 0), (1, 64 * 5 + 17, 512, 8, 2, 128, 128),
+                                                         (2, 512, 256, 32, 8, 128, 64), (3, 200, 192, 4, 2, 64, 0)])
+def test_qkvf_proj_prefill(B, Tq, hidden, Hq, Hkv, d, q_start):
+    """Q/K/V per token (bf16) and each query block's Forecast sum (fp32)
+    against the oracle; a ragged last block; an 8 x 8 tile case takes the
+    XCD-aware tile order."""
+    g = torch.Generator().manual_seed(Tq + hidden + Hq)
+    x = torch.randn(B, Tq, hidden, generator=g).to(torch.bfloat16)
+    w = (torch.randn(hidden, (Hq + 3 * Hkv) * d, generator=g) * 0.05).to(torch.bfloat16)
+    T = q_start + Tq + 64
+    kc = torch.full((B, Hkv, T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.to(DEV), Hq, Hkv, kc, vc, q_start=q_start)
+    torch.cuda.synchronize()
+    wq, wk, wv, wfp = orc.qkvf_proj_prefill(np64(x), np64(w), Hq, Hkv, d, 64)
+    assert _bf16_close(np64(q), wq)
+    kn, vn = np64(kc), np64(vc)
+    assert _bf16_close(kn[:, :, q_start:q_start + Tq], wk) and _bf16_close(vn[:, :, q_start:q_start + Tq], wv)
+    assert np.isnan(kn[:, :, :q_start]).all() and np.isnan(kn[:, :, q_start + Tq:]).all()
+    scale = np.abs(wfp).max()
+    assert max_abs(np64(fp), wfp) < 2e-5 * scale + 1e-4
+
+
+def test_qkvf_prefill_chunk_end_to_end():
+    """One prefill chunk through the widened projection: its K/V land in the
+    cache, the compressed keys are pooled, each query block is selected from
+    its summed Forecast and attends with the projected queries; against the
+    oracle chain on the same bf16 inputs."""
+    B, Hq, Hkv, d, hidden, T = 2, 8, 2, 128, 256, 64 * 24
+    q_start, Tq = 64 * 8, 64 * 16
+    g = torch.Generator().manual_seed(77)
+    x = torch.randn(B, Tq, hidden, generator=g).to(torch.bfloat16)
+    w = (torch.randn(hidden, (Hq + 3 * Hkv) * d, generator=g) * 0.05).to(torch.bfloat16)
+    k_prev = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    v_prev = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    kc_cache, vc_cache = k_prev.clone().to(DEV), v_prev.clone().to(DEV)
+    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.to(DEV), Hq, Hkv, kc_cache, vc_cache, q_start=q_start)
+    seq_len = torch.full((B,), q_start + Tq, dtype=torch.int64, device=DEV)
+    kcmp = _kc_gpu(kc_cache, seq_len)
+    idx, cnt = bskv.forecast_block_score_topk_pooled(fp, kcmp, 4, 1, 2, q_start=q_start)
+    out = bskv.block_sparse_attn_prefill(q, kc_cache, vc_cache, idx, cnt, q_start)
+    torch.cuda.synchronize()
+    # oracle chain on the GPU's bf16 Q/K/V (the bf16 rounding of the projection is the kernel's)
+    k_all, v_all = np64(kc_cache), np64(vc_cache)
+    wq, wk, wv, wfp = orc.qkvf_proj_prefill(np64(x), np64(w), Hq, Hkv, d, 64)
+    kc_or = orc.kv_block_meanpool(k_all, 64, seq_len=seq_len.cpu().numpy())
+    sel = orc.prefill_select_pooled(wfp, kc_or, q_start, 4, 1, 2, 64)
+    assert check_selection(idx, cnt, sel, 4) <= 2
+    want = orc.attend_prefill(np64(q), k_all, v_all, idx.cpu().numpy(), cnt.cpu().numpy(), q_start, 1 / math.sqrt(d), 64)
+    assert max_abs(np64(out), want) < 2e-2
+
+
 # ----------------------------------------------------------------------------- resident block cache
 def _drifting_lists(rng, n_calls, B, H, U, universe, churn):
     """Sorted distinct lists of up to U blocks per (b, g); each call swaps
