@@ -345,6 +345,39 @@ def per_layer_us(torch, bench, fn, reps=3):
     return e0.elapsed_time(e1) * 1e3 / (reps * bench.L)
 
 
+def widened_projection_decode(torch, bench, kt):
+    """The layer's projection widened by the Forecast heads for one decode
+    token per sequence (Q, the new token's K/V into the cache, F), per layer;
+    a GEMV bound by the weight read."""
+    wl, B, dev = bench.wl, bench.B, bench.dev
+    hid, H, d = wl.hidden, wl.Hkv, wl.d
+    N = (wl.Hq + 3 * H) * d
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 600)
+    ws = [(torch.randn(hid, N, generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(8)]
+    x = torch.randn(B, hid, generator=g, device=dev).to(torch.bfloat16)
+    kcache = torch.empty(B, H, 64, d, dtype=torch.bfloat16, device=dev)
+    vcache = torch.empty_like(kcache)
+    lens = torch.full((B,), 64, dtype=torch.int64, device=dev)
+    q = torch.empty(B, wl.Hq, d, dtype=torch.bfloat16, device=dev)
+    f = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    wsp = torch.zeros(max(256, bench.bskv.workspace_bytes("qkvf", B, hid, wl.Hq, H, d)), dtype=torch.uint8, device=dev)
+
+    class _L:   # eight weight replicas rotated so the 59 MB matrix is not served from the last-level cache
+        L = 8
+
+    def fn(l):
+        bench.bskv.qkvf_proj_decode(x, ws[l], wl.Hq, H, kcache, vcache, lens, q_out=q, f_out=f, ws=wsp)
+
+    t = per_layer_us(torch, _L, fn)
+    nbytes = hid * N * 2 + B * hid * 2 + B * (wl.Hq + 2 * H) * d * 2 + B * H * d * 4
+    del ws
+    torch.cuda.synchronize()
+    return {"shape": f"x [{B} x {hid}] @ W [{hid} x {N}]", "us_per_layer": round(t, 3), "bytes": nbytes,
+            "GBps": round(nbytes / t / 1e3, 1), "hbm_frac": round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4),
+            "forecast_only_proj_us": round(kt["forecast_proj"] * 1e6, 3)}
+
+
 def window_selection(torch, bench, kt, window=32, stride=16):
     """Selection on the overlapping compression the evaluated models use
     (32-token windows at stride 16, block scores max-pooled from the window
@@ -541,6 +574,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
     sweep = selection_sweep(torch, bench)
     base_cmp = baseline_comparison(torch, bench, step_s, kt, args) if wl.hidden else None
     win_sel = window_selection(torch, bench, kt) if wl.hidden else None
+    widened = widened_projection_decode(torch, bench, kt) if wl.hidden else None
     # replicas: independent copies of one layer's inputs, rotated so that the
     # working set does not sit in the 256 MB cache; the step then covers
     # `replicas` layer-steps of a one-layer model
@@ -566,6 +600,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
         "select_us_per_layer_vs_T": sweep,
         "baseline_selector": base_cmp,
         "window_selector": win_sel,
+        "widened_projection": widened,
         "kernels": kernels,
     }
     if replicas is not None:
@@ -730,6 +765,76 @@ class PrefillBench:
         return tot
 
 
+def widened_projection_prefill(torch, bench, kt, args):
+    """The layer's projection widened by the Forecast heads, per 2048-token
+    chunk: (Q, K, V, F) = X [W_Q | W_K | W_V | W_F] with K/V written into the
+    cache and only each query block's Forecast sum kept; against the same
+    GEMM through the vendor BLAS; the selection from the sums; and the whole
+    chunked prefill with the projection in front (projection, pooling,
+    selection, attention)."""
+    wl, B, C, dev = bench.wl, bench.B, bench.C, bench.dev
+    hid, H, d = 4096, wl.Hkv, wl.d
+    N = (wl.Hq + 3 * H) * d
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 500)
+    x = torch.randn(B, C, hid, generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn(hid, N, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    kc2 = torch.empty_like(bench.k)
+    vc2 = torch.empty_like(bench.v)
+    n_qb = C // wl.block
+    q = torch.empty(B, wl.Hq, C, d, dtype=torch.bfloat16, device=dev)
+    fp = torch.empty(B, H, n_qb, d, dtype=torch.float32, device=dev)
+    kcmp = torch.empty_like(bench.kc)
+    out = torch.empty_like(q)
+
+    def proj(c):
+        bench.bskv.qkvf_proj_prefill(x, w, wl.Hq, H, kc2, vc2, q_start=c * C, q_out=q, f_pooled=fp)
+
+    def select(c):
+        bench.bskv.forecast_block_score_topk_pooled(fp, kcmp, wl.topk, wl.n_init, wl.n_local, q_start=c * C,
+                                                    idx=bench.idx[c], cnt=bench.cnt[c])
+
+    def blas(c):
+        return x.view(-1, hid) @ w
+
+    def step():
+        for c in range(bench.n_chunks):
+            proj(c)
+            bench.bskv.kv_block_meanpool(kc2, bench.seq_len, kcmp, c * n_qb, (c + 1) * n_qb)
+            select(c)
+            bench.bskv.block_sparse_attn_prefill(q, kc2, vc2, bench.idx[c], bench.cnt[c], c * C, wl.scale, out=out)
+
+    def per_call(fn, reps=8):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(r % bench.n_chunks)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    step()                                   # fills the caches and compressed keys of every chunk
+    torch.cuda.synchronize()
+    t_proj, t_blas, t_sel = per_call(proj), per_call(blas), per_call(select)
+    flops = 2.0 * B * C * hid * N
+    step_s, _ = time_graph(torch, step, max(1, args.steps // 10), 1, use_graph=not args.no_graph)
+    del kc2, vc2, x, w
+    torch.cuda.synchronize()
+    return {
+        "shape": f"X [{B * C} x {hid}] @ W [{hid} x {N}] per chunk (Q {wl.Hq}, K/V/F {H} heads of {d})",
+        "qkvf_proj_prefill_us": round(t_proj * 1e6, 2), "TFLOPs": round(flops / t_proj / 1e12, 1),
+        "mfma_frac": round(flops / t_proj / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "vendor_blas_same_gemm_us": round(t_blas * 1e6, 2),
+        "vendor_blas_TFLOPs": round(flops / t_blas / 1e12, 1),
+        "pooled_select_us": round(t_sel * 1e6, 2),
+        "per_token_select_us": round(kt["score_topk_prefill"] * 1e6, 2),
+        "step_with_projection_ms": round(step_s * 1e3, 3),
+        "tokens_per_s_with_projection": round(B * bench.T / step_s, 1),
+    }
+
+
 def run_prefill(args, torch, bskv, wl):
     bench = PrefillBench(wl, torch, bskv)
     step_s, _ = time_graph(torch, bench.step, max(1, args.steps // 10), max(1, args.warmup // 5),
@@ -773,6 +878,7 @@ def run_prefill(args, torch, bskv, wl):
         "attn_prefill": {"us": round(kt["attn_prefill"] * 1e6, 2), "TFLOPs": round(att_tf, 1),
                          "mfma_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+    widened = widened_projection_prefill(torch, bench, kt, args)
     # the overlapping-compression variant (32/16 windows, block scores
     # max-pooled): its pooling and selection per chunk, and its whole step
     # (the window selection leaves the lists of the block selector's place)
@@ -802,6 +908,7 @@ def run_prefill(args, torch, bskv, wl):
         "roofline_frac_of_measured_gemm": round(att_tf / gemm_tf, 4),
         "kernels": kernels,
         "window_variant": window_variant,
+        "widened_projection": widened,
     }
 
 
