@@ -354,20 +354,19 @@ def widened_projection_decode(torch, bench, kt):
     N = (wl.Hq + 3 * H) * d
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed + 600)
-    ws = [(torch.randn(hid, N, generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(8)]
+    ws = [(torch.randn(N, hid, generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(8)]
     x = torch.randn(B, hid, generator=g, device=dev).to(torch.bfloat16)
     kcache = torch.empty(B, H, 64, d, dtype=torch.bfloat16, device=dev)
     vcache = torch.empty_like(kcache)
     lens = torch.full((B,), 64, dtype=torch.int64, device=dev)
     q = torch.empty(B, wl.Hq, d, dtype=torch.bfloat16, device=dev)
     f = torch.empty(B, H, d, dtype=torch.float32, device=dev)
-    wsp = torch.zeros(max(256, bench.bskv.workspace_bytes("qkvf", B, hid, wl.Hq, H, d)), dtype=torch.uint8, device=dev)
 
     class _L:   # eight weight replicas rotated so the 59 MB matrix is not served from the last-level cache
         L = 8
 
     def fn(l):
-        bench.bskv.qkvf_proj_decode(x, ws[l], wl.Hq, H, kcache, vcache, lens, q_out=q, f_out=f, ws=wsp)
+        bench.bskv.qkvf_proj_decode(x, ws[l], wl.Hq, H, kcache, vcache, lens, q_out=q, f_out=f)
 
     t = per_layer_us(torch, _L, fn)
     nbytes = hid * N * 2 + B * hid * 2 + B * (wl.Hq + 2 * H) * d * 2 + B * H * d * 4
@@ -778,7 +777,7 @@ def widened_projection_prefill(torch, bench, kt, args):
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed + 500)
     x = torch.randn(B, C, hid, generator=g, device=dev).to(torch.bfloat16)
-    w = (torch.randn(hid, N, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w = (torch.randn(N, hid, generator=g, device=dev) * 0.02).to(torch.bfloat16)      # W^T: one row per column
     kc2 = torch.empty_like(bench.k)
     vc2 = torch.empty_like(bench.v)
     n_qb = C // wl.block
@@ -795,7 +794,7 @@ def widened_projection_prefill(torch, bench, kt, args):
                                                     idx=bench.idx[c], cnt=bench.cnt[c])
 
     def blas(c):
-        return x.view(-1, hid) @ w
+        return x.view(-1, hid) @ w.t()
 
     def step():
         for c in range(bench.n_chunks):
@@ -823,7 +822,8 @@ def widened_projection_prefill(torch, bench, kt, args):
     del kc2, vc2, x, w
     torch.cuda.synchronize()
     return {
-        "shape": f"X [{B * C} x {hid}] @ W [{hid} x {N}] per chunk (Q {wl.Hq}, K/V/F {H} heads of {d})",
+        "shape": f"X [{B * C} x {hid}] @ W [{hid} x {N}] per chunk (Q {wl.Hq}, K/V/F {H} heads of {d}); "
+                 f"W stored as W^T [{N} x {hid}]",
         "qkvf_proj_prefill_us": round(t_proj * 1e6, 2), "TFLOPs": round(flops / t_proj / 1e12, 1),
         "mfma_frac": round(flops / t_proj / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "vendor_blas_same_gemm_us": round(t_blas * 1e6, 2),

@@ -49,9 +49,7 @@ _proto("bskv_block_sparse_attn_prefill", _i, _p, _p, _p, _i, ctypes.POINTER(_i64
 _proto("bskv_prefetch_selected_blocks", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _i, _i, _i, _i,
        _i, _i, _p)
 _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
-_proto("bskv_qkvf_proj_workspace", _sz, _i, _i, _i, _i, _i)
-_proto("bskv_qkvf_proj_decode", _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p, _p, _p, _sz,
-       _p)
+_proto("bskv_qkvf_proj_decode", _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p, _p, _p)
 _proto("bskv_qkvf_proj_prefill", _i, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p,
        _p)
 _proto("bskv_forecast_block_score_topk_pooled", _i, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p)
@@ -112,8 +110,7 @@ def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
           "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace,
           "multihead": lib.bskv_multihead_score_topk_workspace,
-          "window": lib.bskv_window_score_topk_workspace,
-          "qkvf": lib.bskv_qkvf_proj_workspace}[kind]
+          "window": lib.bskv_window_score_topk_workspace}[kind]
     return int(fn(*args))
 
 
@@ -341,40 +338,38 @@ def prefetch_selected_blocks(src_k, src_v, idx, cnt, ring_k, ring_v, n_workgroup
     return ring_k, ring_v
 
 
-def qkvf_proj_decode(x, w, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, seq_len, q_out=None, f_out=None,
-                     ws=None, stream=None):
-    """Widened projection of one token per sequence: returns (q bf16
-    [B, Hq, d], f fp32 [B, Hkv, d]); the token's K/V go into the caches at
-    position seq_len - 1."""
+def qkvf_proj_decode(x, w_t, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, seq_len, q_out=None, f_out=None,
+                     stream=None):
+    """Widened projection of one token per sequence (w_t [N, hidden], one row
+    per output column): returns (q bf16 [B, Hq, d], f fp32 [B, Hkv, d]); the
+    token's K/V go into the caches at position seq_len - 1."""
     B, hidden = x.shape
     d = k_cache.shape[-1]
-    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
+    if x.dtype != torch.bfloat16 or w_t.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
         raise TypeError("bf16 only")
-    if k_cache.stride() != v_cache.stride() or not x.is_contiguous() or not w.is_contiguous():
-        raise ValueError("x, w contiguous; k/v caches with identical strides")
+    if k_cache.stride() != v_cache.stride() or not x.is_contiguous() or not w_t.is_contiguous():
+        raise ValueError("x, w_t contiguous; k/v caches with identical strides")
     q_out = q_out if q_out is not None else torch.empty(B, n_q_heads, d, dtype=torch.bfloat16, device=x.device)
     f_out = f_out if f_out is not None else torch.empty(B, n_kv_heads, d, dtype=torch.float32, device=x.device)
     sh = _stream(stream, x.device)
-    lay = (B, hidden, n_q_heads, n_kv_heads, d)
-    nbytes = workspace_bytes("qkvf", *lay)
-    ws = ws if ws is not None else _workspace(x.device, nbytes, sh, "qkvf", lay)
-    _check(lib.bskv_qkvf_proj_decode(_ptr(x), _ptr(w), B, hidden, n_q_heads, n_kv_heads, d, _ptr(q_out), _ptr(k_cache),
-                                     _ptr(v_cache), _strides3(k_cache), k_cache.shape[2], _ptr(seq_len), _ptr(f_out),
-                                     _ptr(ws), ws.numel() * ws.element_size(), sh), "qkvf_proj_decode")
+    _check(lib.bskv_qkvf_proj_decode(_ptr(x), _ptr(w_t), B, hidden, n_q_heads, n_kv_heads, d, _ptr(q_out),
+                                     _ptr(k_cache), _ptr(v_cache), _strides3(k_cache), k_cache.shape[2], _ptr(seq_len),
+                                     _ptr(f_out), sh), "qkvf_proj_decode")
     return q_out, f_out
 
 
-def qkvf_proj_prefill(x, w, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, q_start: int = 0, q_out=None,
+def qkvf_proj_prefill(x, w_t, n_q_heads: int, n_kv_heads: int, k_cache, v_cache, q_start: int = 0, q_out=None,
                       f_pooled=None, stream=None):
-    """Widened projection of a prefill chunk x [B, Tq, hidden]: returns (q bf16
-    [B, Hq, Tq, d], f_pooled fp32 [B, Hkv, ceil(Tq/64), d]); K/V go into the
-    caches at positions q_start + t."""
+    """Widened projection of a prefill chunk x [B, Tq, hidden] (w_t [N,
+    hidden]): returns (q bf16 [B, Hq, Tq, d], f_pooled fp32 [B, Hkv,
+    ceil(Tq/64), d]); K/V go into the caches at positions q_start + t."""
     B, Tq, hidden = x.shape
     d = k_cache.shape[-1]
+    w = w_t
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
         raise TypeError("bf16 only")
     if k_cache.stride() != v_cache.stride() or not x.is_contiguous() or not w.is_contiguous():
-        raise ValueError("x, w contiguous; k/v caches with identical strides")
+        raise ValueError("x, w_t contiguous; k/v caches with identical strides")
     n_qb = -(-Tq // 64)
     q_out = q_out if q_out is not None else torch.empty(B, n_q_heads, Tq, d, dtype=torch.bfloat16, device=x.device)
     f_pooled = f_pooled if f_pooled is not None else torch.empty(B, n_kv_heads, n_qb, d, dtype=torch.float32,

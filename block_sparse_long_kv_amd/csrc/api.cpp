@@ -337,33 +337,27 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
   return finish(bskv::launch_attn_decode(a));
 }
 
-size_t bskv_qkvf_proj_workspace(int B, int hidden, int n_q_heads, int n_kv_heads, int head_dim) {
-  if (B <= 0 || hidden <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !head_dim_ok(head_dim)) return 0;
-  return bskv::qkvf_decode_workspace_bytes(B, hidden, (n_q_heads + 3 * n_kv_heads) * head_dim);
-}
-
-int bskv_qkvf_proj_decode(const void* x, const void* w, int B, int hidden, int n_q_heads, int n_kv_heads,
+int bskv_qkvf_proj_decode(const void* x, const void* w_t, int B, int hidden, int n_q_heads, int n_kv_heads,
                           int head_dim, void* q_out, void* k_cache, void* v_cache, const int64_t* kv_strides,
-                          int64_t kv_len, const int64_t* seq_len, float* f_out, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
-  if (!x || !w || !q_out || !k_cache || !v_cache || !seq_len || !f_out || !ws) return BSKV_EINVAL;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(ws)) return BSKV_EINVAL;
+                          int64_t kv_len, const int64_t* seq_len, float* f_out, hipStream_t stream) {
+  if (!x || !w_t || !q_out || !k_cache || !v_cache || !seq_len || !f_out) return BSKV_EINVAL;
+  if (!aligned16(x) || !aligned16(w_t)) return BSKV_EINVAL;
   if (B <= 0 || hidden <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || kv_len < 0) return BSKV_EINVAL;
   if (!strides_ok(kv_strides, BSKV_BF16)) return BSKV_EINVAL;
   if (!head_dim_ok(head_dim)) return BSKV_EUNSUPPORTED;
   const int64_t N = (int64_t)(n_q_heads + 3 * n_kv_heads) * head_dim;
-  if (hidden % 256 || N % 128 || (int64_t)B * N > 0x7fffffff) return BSKV_EUNSUPPORTED;
-  if (ws_bytes < bskv::qkvf_decode_workspace_bytes(B, hidden, (int)N)) return BSKV_ENOSPC;
-  bskv::QkvfDecodeArgs a{x, w, B, hidden, n_q_heads, n_kv_heads, head_dim, q_out, k_cache, v_cache, kv_strides[0],
-                         kv_strides[1], kv_strides[2], kv_len, seq_len, f_out, ws, stream};
+  // four waves split the hidden axis in steps of 8 x 32
+  if (hidden % 1024 || B > 64 || N / 16 > 0x7fffffff) return BSKV_EUNSUPPORTED;
+  bskv::QkvfDecodeArgs a{x, w_t, B, hidden, n_q_heads, n_kv_heads, head_dim, q_out, k_cache, v_cache, kv_strides[0],
+                         kv_strides[1], kv_strides[2], kv_len, seq_len, f_out, stream};
   return finish(bskv::launch_qkvf_decode(a));
 }
 
-int bskv_qkvf_proj_prefill(const void* x, const void* w, int B, int n_q_tokens, int hidden, int n_q_heads,
+int bskv_qkvf_proj_prefill(const void* x, const void* w_t, int B, int n_q_tokens, int hidden, int n_q_heads,
                            int n_kv_heads, int head_dim, int64_t q_start, void* q_out, void* k_cache, void* v_cache,
                            const int64_t* kv_strides, int64_t kv_len, float* f_pooled, hipStream_t stream) {
-  if (!x || !w || !q_out || !k_cache || !v_cache || !f_pooled) return BSKV_EINVAL;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) ||
+  if (!x || !w_t || !q_out || !k_cache || !v_cache || !f_pooled) return BSKV_EINVAL;
+  if (!aligned16(x) || !aligned16(w_t) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(f_pooled))
     return BSKV_EINVAL;
   if (B <= 0 || n_q_tokens <= 0 || hidden <= 0 || n_q_heads <= 0 || n_kv_heads <= 0) return BSKV_EINVAL;
@@ -375,7 +369,7 @@ int bskv_qkvf_proj_prefill(const void* x, const void* w, int B, int n_q_tokens, 
     return BSKV_EUNSUPPORTED;
   const int64_t n_tiles = (int64_t)(n_q_heads + 3 * n_kv_heads) * head_dim / 128 * ((n_q_tokens + 127) / 128) * B;
   if (n_tiles > 0x7fffffff) return BSKV_EUNSUPPORTED;
-  bskv::QkvfPrefillArgs a{x, w, B, n_q_tokens, hidden, n_q_heads, n_kv_heads, head_dim, q_start, q_out, k_cache,
+  bskv::QkvfPrefillArgs a{x, w_t, B, n_q_tokens, hidden, n_q_heads, n_kv_heads, head_dim, q_start, q_out, k_cache,
                           v_cache, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, f_pooled, stream};
   return finish(bskv::launch_qkvf_prefill(a));
 }

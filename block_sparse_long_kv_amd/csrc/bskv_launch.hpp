@@ -34,10 +34,9 @@ struct QkvfDecodeArgs {
   const void* x; const void* w;
   int B, hidden, Hq, H, D;
   void* q; void* k; void* v; int64_t sb, sg, st, kv_len; const int64_t* seq_len;
-  float* f; void* ws;
+  float* f;
   hipStream_t stream;
 };
-size_t qkvf_decode_workspace_bytes(int B, int hidden, int N);
 hipError_t launch_qkvf_decode(const QkvfDecodeArgs& a);
 struct QkvfPrefillArgs {
   const void* x; const void* w;

@@ -8,79 +8,134 @@
 // the sum over its tokens).  Columns of W: query heads, key heads, value
 // heads, Forecast heads, head_dim columns each.
 //
-// Decode (one token per sequence): split-K partials on MFMA (the Forecast
-// projection's kernel, over all columns), then one pass that adds the splits
-// and scatters: Q (bf16), the new token's K and V (bf16, into the cache at
-// position seq_len-1) and F (fp32).
+// Decode (one token per sequence): one GEMV kernel on MFMA whose waves split
+// the hidden axis and meet in LDS, then write Q (bf16), the new token's K and
+// V (bf16, into the cache at position seq_len-1) and F (fp32).
 //
-// Prefill: a bf16 MFMA GEMM computing C^T = W^T X^T per 128 x 128 tile
-// (columns x tokens of one sequence), hidden in steps of 64 staged through
-// LDS in two buffers (the next step's global loads are issued before the
-// current step's MFMAs).  W^T is read from its row-major tile with the
-// transposing LDS read (as in the Forecast projection), X^T straight from
-// the token rows.  Each wave owns 64 columns x 64 tokens -- one query block
-// -- so the epilogue writes Q/K/V rows as bf16 and, for the Forecast
-// columns, adds the wave's 64 tokens in registers and across the 16 lanes of
-// each row group: only the per-query-block sum leaves the kernel.
+// Prefill: a bf16 MFMA GEMM computing C^T = W^T X^T per tile of columns x
+// tokens of one sequence, hidden in steps of 64 staged through LDS in two
+// buffers (the next step's global loads are issued before the current
+// step's MFMAs).  The weight is taken as W^T [N, hidden] and X is
+// [tokens, hidden], so both operands are hidden-major.  Each wave owns whole
+// 64-token query blocks, so the epilogue writes Q/K/V rows as bf16 and, for
+// the Forecast columns, adds each query block's tokens in registers and
+// across the 16 lanes of each row group: only the per-query-block sum
+// leaves the kernel.
 #include "decode_ops.hpp"
 #include "bskv_launch.hpp"
 
 namespace bskv {
 
 // ------------------------------------------------------------------ decode
-__global__ __launch_bounds__(kThreads) void qkvf_scatter_kernel(const float* __restrict__ part, int n_splits, int B,
-                                                              int Hq, int H, int D, bf16_bits* __restrict__ q,
-                                                              bf16_bits* __restrict__ kc, bf16_bits* __restrict__ vc,
-                                                              int64_t sb, int64_t sg, int64_t st, int64_t kv_len,
-                                                              const int64_t* __restrict__ seq_len,
-                                                              float* __restrict__ f) {
-  const int N = (Hq + 3 * H) * D;
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= B * N) return;
-  const int b = i / N, n = i % N;
-  const float y = proj_reduce_one(part, n_splits, B, N, b, n);
-  const int head = n / D, e = n % D;
-  if (head < Hq) {
-    q[((int64_t)b * Hq + head) * D + e] = f32_to_bf16(y);
-    return;
-  }
-  const int r = head - Hq;
-  if (r < 2 * H) {
-    const int64_t pos = seq_len[b] - 1;
-    if (pos < 0 || pos >= kv_len) return;      // the new token's row must be inside the cache
-    const int g = r % H;
-    bf16_bits* dst = r < H ? kc : vc;
-    dst[b * sb + g * sg + pos * st + e] = f32_to_bf16(y);
-    return;
-  }
-  f[((int64_t)b * H + (r - 2 * H)) * D + e] = y;
-}
+// GEMV on W^T [N, hidden]: workgroup = 16 output columns; its waves split
+// the hidden axis evenly and run their range in steps of 32 with
+// v_mfma_f32_16x16x32_bf16: A = 16 rows of W^T (one 16-byte load per lane),
+// B = the batch's x rows (up to 16 sequences per MFMA, several chunks for
+// larger batches); the waves' partial sums meet in LDS and wave 0 scatters:
+// Q (bf16), the new token's K and V into the cache (bf16) and F (fp32).
+constexpr int kQkvfMaxBatch = 64;
 
-size_t qkvf_decode_workspace_bytes(int B, int hidden, int N) {
-  return (size_t)proj_splits(hidden) * B * N * sizeof(float);
+// NW waves split the hidden axis; NB batch chunks of 16; UN hidden steps of
+// 32 per load batch (hidden / NW a multiple of 32 UN)
+template <int NW, int NB, int UN>
+__global__ __launch_bounds__(NW * 64) void qkvf_decode_kernel(const bf16_bits* __restrict__ x,
+                                                             const bf16_bits* __restrict__ w, int B, int hidden,
+                                                             int Hq, int H, int D, bf16_bits* __restrict__ q,
+                                                             bf16_bits* __restrict__ kc, bf16_bits* __restrict__ vc,
+                                                             int64_t sb, int64_t sg, int64_t st, int64_t kv_len,
+                                                             const int64_t* __restrict__ seq_len,
+                                                             float* __restrict__ f) {
+  __shared__ float red[NW][NB][64][4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int kq = hidden / NW, k_begin = wid * kq;
+  const bf16_bits* wrow = w + (int64_t)(n0 + l16) * hidden + 8 * lg;
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = k_begin; k < k_begin + kq; k += 32 * UN) {
+    uint4 a[UN];
+#pragma unroll
+    // plain loads: one instruction reads 64 of a row's 128-byte line, the
+    // next the other half, which then comes from L2 (a nontemporal load
+    // would fetch the line twice)
+    for (int u = 0; u < UN; ++u) a[u] = ld16(wrow + k + 32 * u);
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const int b = 16 * c + l16;
+      uint4 xb[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        xb[u] = b < B ? ld16(x + (int64_t)b * hidden + k + 32 * u + 8 * lg) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
+                                                         __builtin_bit_cast(bf16x8_t, xb[u]), acc[c], 0, 0, 0);
+    }
+  }
+  // lane (b = l16, lg) of chunk c holds column n0 + 4lg + i for sequence 16c + l16
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wid][c][lane][i] = acc[c][i];
+  __syncthreads();
+  if (wid != 0) return;
+  const int64_t seg_q = (int64_t)Hq * D, seg_kv = (int64_t)H * D;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int b = 16 * c + l16;
+    if (b >= B) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) y += red[v][c][lane][i];
+      const int n = n0 + 4 * lg + i;
+      if (n < seg_q) {
+        q[(int64_t)b * seg_q + n] = f32_to_bf16(y);
+      } else if (n < seg_q + 2 * seg_kv) {
+        const int64_t pos = seq_len[b] - 1;
+        if (pos < 0 || pos >= kv_len) continue;   // the new token's row must be inside the cache
+        const int r = n - (int)seg_q, g = (r / D) % H;
+        (r < seg_kv ? kc : vc)[b * sb + g * sg + pos * st + r % D] = f32_to_bf16(y);
+      } else {
+        f[(int64_t)b * seg_kv + (n - seg_q - 2 * seg_kv)] = y;
+      }
+    }
+  }
 }
 
 hipError_t launch_qkvf_decode(const QkvfDecodeArgs& a) {
   const int N = (a.Hq + 3 * a.H) * a.D;
-  float* part = (float*)a.ws;
-  launch_proj_partial<bf16_bits>(a.x, a.w, a.B, a.hidden, N, part, a.stream);
-  const int n = a.B * N;
-  hipLaunchKernelGGL(qkvf_scatter_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, a.stream, part,
-                     proj_splits(a.hidden), a.B, a.Hq, a.H, a.D, (bf16_bits*)a.q, (bf16_bits*)a.k, (bf16_bits*)a.v,
-                     a.sb, a.sg, a.st, a.kv_len, a.seq_len, a.f);
+  const dim3 grid(N / 16);
+#define BSKV_QKVF_DEC(NW, NB, UN)                                                                                 \
+  hipLaunchKernelGGL((qkvf_decode_kernel<NW, NB, UN>), grid, dim3(NW * 64), 0, a.stream, (const bf16_bits*)a.x,   \
+                     (const bf16_bits*)a.w, a.B, a.hidden, a.Hq, a.H, a.D, (bf16_bits*)a.q, (bf16_bits*)a.k,       \
+                     (bf16_bits*)a.v, a.sb, a.sg, a.st, a.kv_len, a.seq_len, a.f)
+  // hidden is a multiple of 1024.  Up to 16 sequences, hidden a multiple of
+  // 4096: eight waves of 512 hidden columns each issue all their weight loads
+  // at once; otherwise four waves in steps of 8 x 32 (a quarter of hidden is
+  // a multiple of 256)
+  if (a.B <= 16 && a.hidden % 4096 == 0) BSKV_QKVF_DEC(8, 1, 8);
+  else if (a.B <= 16) BSKV_QKVF_DEC(4, 1, 8);
+  else if (a.B <= 32) BSKV_QKVF_DEC(4, 2, 8);
+  else BSKV_QKVF_DEC(4, 4, 8);
+#undef BSKV_QKVF_DEC
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ prefill
-constexpr int kGemmBM = 128;              // tokens per tile
-constexpr int kGemmBN = 128;              // output columns per tile
-constexpr int kGemmBK = 64;               // hidden rows per stage
-constexpr int kGemmWStr = kGemmBN + 16;   // W tile row: 288 bytes (conflict-free transposing reads)
-constexpr int kGemmXStr = kGemmBK + 8;    // X tile row: 144 bytes
+// W^T [N, hidden] row-major (one row per output column, as a linear layer
+// stores its weight) and X [tokens, hidden]: both operands are hidden-major,
+// so every MFMA operand fragment is one 16-byte LDS read.
+constexpr int kGemmBK = 64;               // hidden columns per stage
+constexpr int kGemmStr = kGemmBK + 8;     // LDS row: 144 bytes (16 rows x 16 bytes hit all 64 banks once)
 
+template <int BM, int BN>
 struct QkvfGemmSmem {
-  bf16_bits w[2][kGemmBK * kGemmWStr];
-  bf16_bits x[2][kGemmBM * kGemmXStr];
+  bf16_bits x[2][BM * kGemmStr];
+  bf16_bits w[2][BN * kGemmStr];
 };
 
 struct QkvfPrefillParams {
@@ -93,16 +148,22 @@ struct QkvfPrefillParams {
   float* f_pooled;
 };
 
-__global__ __launch_bounds__(kThreads, 2) void qkvf_prefill_kernel(QkvfPrefillParams p) {
-  __shared__ __attribute__((aligned(16))) QkvfGemmSmem sm;
-  constexpr int CW = kGemmBK * kGemmBN / 8 / kThreads;   // 16-byte chunks of the W tile per thread (4)
-  constexpr int CX = kGemmBM * kGemmBK / 8 / kThreads;   // of the X tile (4)
+// C^T = W^T X^T per BN x BM tile (columns x tokens of one sequence); four
+// waves, each WN columns x WM tokens (WM a multiple of 64: whole query blocks).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads, 1) void qkvf_prefill_kernel(QkvfPrefillParams p) {
+  static_assert((BM / WM) * (BN / WN) == 4 && WM % 64 == 0 && WN % 16 == 0, "four waves of whole query blocks");
+  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int CX = BM * kGemmBK / 8 / kThreads;   // 16-byte chunks of the X tile per thread
+  constexpr int CW = BN * kGemmBK / 8 / kThreads;   // of the W^T tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  QkvfGemmSmem<BM, BN>& sm = *reinterpret_cast<QkvfGemmSmem<BM, BN>*>(smem_raw);
   const int N = (p.Hq + 3 * p.H) * p.D;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2).  With the swizzle, XCD x takes a contiguous run of the tile space
-  // in 8 x 8 groups of (token tile, column tile): the ~64 workgroups one XCD
-  // runs at a time share 8 token tiles and 8 column tiles, so each K-step's
-  // operands are fetched into that L2 once and read by 8 workgroups.
+  // in 8 x 8 groups of (token tile, column tile): the workgroups one XCD runs
+  // at a time share a few token tiles and column tiles, so each K-step's
+  // operands are fetched into that L2 once and read by several workgroups.
   int tn, tm;
   {
     const int bid = blockIdx.x, n_m = p.n_tiles_t * p.B;
@@ -119,46 +180,45 @@ __global__ __launch_bounds__(kThreads, 2) void qkvf_prefill_kernel(QkvfPrefillPa
     }
   }
   const int b = tm / p.n_tiles_t;
-  const int n0 = tn * kGemmBN, t0 = (tm % p.n_tiles_t) * kGemmBM;
+  const int n0 = tn * BN, t0 = (tm % p.n_tiles_t) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int wn = wid & 1, wm = wid >> 1;
+  const int wn = wid % (BN / WN), wm = wid / (BN / WN);
   const bf16_bits* xb = p.x + (int64_t)b * p.Tq * p.hidden;
 
-  uint4 rw[CW], rx[CX];
+  uint4 rx[CX], rw[CW];
   auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int c = tid + i * kThreads, r = c >> 4, cc = c & 15;
-      rw[i] = ld16(p.w + (int64_t)(k0 + r) * N + n0 + cc * 8);
-    }
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
       const int t = t0 + r;
       rx[i] = t < p.Tq ? ld16(xb + (int64_t)t * p.hidden + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
+      rw[i] = ld16(p.w + (int64_t)(n0 + r) * p.hidden + k0 + cc * 8);
+    }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int c = tid + i * kThreads, r = c >> 4, cc = c & 15;
-      *reinterpret_cast<uint4*>(&sm.w[buf][r * kGemmWStr + cc * 8]) = rw[i];
-    }
-#pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sm.x[buf][r * kGemmXStr + cc * 8]) = rx[i];
+      *reinterpret_cast<uint4*>(&sm.x[buf][r * kGemmStr + cc * 8]) = rx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&sm.w[buf][r * kGemmStr + cc * 8]) = rw[i];
     }
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[NI][MI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
   const int n_steps = p.hidden / kGemmBK;
   gload(0);
   lstore(0);
@@ -168,27 +228,21 @@ __global__ __launch_bounds__(kThreads, 2) void qkvf_prefill_kernel(QkvfPrefillPa
     if (s + 1 < n_steps) gload((s + 1) * kGemmBK);
 #pragma unroll
     for (int ks = 0; ks < kGemmBK / 32; ++ks) {
-      bf16x8_t a[4], bx[4];
+      // A = W^T rows (lane: column l16, hidden 8lg..8lg+7); B = X^T (lane:
+      // token l16, the same hidden columns)
+      bf16x8_t a[NI], bx[MI];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        // A = W^T: lane (column l16, group lg) holds hidden rows 4lg..4lg+3 and 16+4lg..16+4lg+3
-        const bf16_bits* v0 = &sm.w[buf][(32 * ks + tr_row) * kGemmWStr + 64 * wn + 16 * ni + tr_col];
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * kGemmWStr));
-        a[ni] = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      }
+      for (int ni = 0; ni < NI; ++ni)
+        a[ni] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                 &sm.w[buf][(WN * wn + 16 * ni + l16) * kGemmStr + 32 * ks + 8 * lg]));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        // B = X^T: lane (token l16, group lg) holds the same hidden rows of its token
-        const bf16_bits* xp = &sm.x[buf][(64 * wm + 16 * mi + l16) * kGemmXStr + 32 * ks + 4 * lg];
-        const uint2 lo = *reinterpret_cast<const uint2*>(xp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(xp + 16);
-        bx[mi] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
+      for (int mi = 0; mi < MI; ++mi)
+        bx[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                  &sm.x[buf][(WM * wm + 16 * mi + l16) * kGemmStr + 32 * ks + 8 * lg]));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
           acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ni], bx[mi], acc[ni][mi], 0, 0, 0);
     }
     if (s + 1 < n_steps) {
@@ -197,15 +251,15 @@ __global__ __launch_bounds__(kThreads, 2) void qkvf_prefill_kernel(QkvfPrefillPa
     }
   }
 
-  // lane (l16, lg) of tile (ni, mi) holds C[token 64wm + 16mi + l16][column 64wn + 16ni + 4lg + i], i < 4
+  // lane (l16, lg) of tile (ni, mi) holds C[token WM wm + 16mi + l16][column WN wn + 16ni + 4lg + i], i < 4
   const int seg_q = p.Hq * p.D, seg_k = seg_q + p.H * p.D, seg_v = seg_k + p.H * p.D;
   if (n0 < seg_v) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int n = n0 + 64 * wn + 16 * ni + 4 * lg;
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = n0 + WN * wn + 16 * ni + 4 * lg;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int t = t0 + 64 * wm + 16 * mi + l16;
+      for (int mi = 0; mi < MI; ++mi) {
+        const int t = t0 + WM * wm + 16 * mi + l16;
         if (t >= p.Tq) continue;
         const uint32_t w01 = (uint32_t)f32_to_bf16(acc[ni][mi][0]) | ((uint32_t)f32_to_bf16(acc[ni][mi][1]) << 16);
         const uint32_t w23 = (uint32_t)f32_to_bf16(acc[ni][mi][2]) | ((uint32_t)f32_to_bf16(acc[ni][mi][3]) << 16);
@@ -222,26 +276,40 @@ __global__ __launch_bounds__(kThreads, 2) void qkvf_prefill_kernel(QkvfPrefillPa
       }
     }
   } else {
-    // Forecast columns: the wave's 64 tokens are one query block
-    const int qb = (t0 + 64 * wm) / kBlk;
-    if (qb * kBlk >= p.Tq) return;
+    // Forecast columns: each run of four token tiles is one query block
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      float s[4];
+    for (int qs = 0; qs < WM / 64; ++qs) {
+      const int qb = (t0 + WM * wm + 64 * qs) / kBlk;
+      if (qb * kBlk >= p.Tq) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = 0.f;
+      for (int ni = 0; ni < NI; ++ni) {
+        float sum[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) v += acc[ni][mi][i];
-        s[i] = sum16(v);                           // the 16 tokens of each lane row group
-      }
-      if (l16 == 0) {
-        const int r = n0 + 64 * wn + 16 * ni + 4 * lg - seg_v, g = r / p.D;
-        *reinterpret_cast<float4*>(p.f_pooled + (((int64_t)b * p.H + g) * p.n_qb + qb) * p.D + r % p.D) =
-            make_float4(s[0], s[1], s[2], s[3]);
+        for (int i = 0; i < 4; ++i) {
+          float v = 0.f;
+#pragma unroll
+          for (int mi = 4 * qs; mi < 4 * qs + 4; ++mi) v += acc[ni][mi][i];
+          sum[i] = sum16(v);                         // the 16 tokens of each lane row group
+        }
+        if (l16 == 0) {
+          const int r = n0 + WN * wn + 16 * ni + 4 * lg - seg_v, g = r / p.D;
+          *reinterpret_cast<float4*>(p.f_pooled + (((int64_t)b * p.H + g) * p.n_qb + qb) * p.D + r % p.D) =
+              make_float4(sum[0], sum[1], sum[2], sum[3]);
+        }
       }
     }
   }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_qkvf_prefill_t(QkvfPrefillParams p, int N, hipStream_t stream) {
+  p.n_tiles_n = N / BN;
+  p.n_tiles_t = (p.Tq + BM - 1) / BM;
+  const int n_m = p.n_tiles_t * p.B, total = n_m * p.n_tiles_n;
+  p.swizzle = (n_m % 8 == 0 && p.n_tiles_n % 8 == 0) ? 1 : 0;   // then total is a multiple of 64
+  const size_t lds = sizeof(QkvfGemmSmem<BM, BN>);
+  hipLaunchKernelGGL((qkvf_prefill_kernel<BM, BN, WM, WN>), dim3(total), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_qkvf_prefill(const QkvfPrefillArgs& a) {
@@ -254,12 +322,11 @@ hipError_t launch_qkvf_prefill(const QkvfPrefillArgs& a) {
   p.sb = a.sb; p.sg = a.sg; p.st = a.st; p.kv_len = a.kv_len;
   p.f_pooled = a.f_pooled;
   const int N = (a.Hq + 3 * a.H) * a.D;
-  p.n_tiles_n = N / kGemmBN;
-  p.n_tiles_t = (a.Tq + kGemmBM - 1) / kGemmBM;
-  const int n_m = p.n_tiles_t * a.B, total = n_m * p.n_tiles_n;
-  p.swizzle = (n_m % 8 == 0 && p.n_tiles_n % 8 == 0) ? 1 : 0;   // then total is a multiple of 64
-  hipLaunchKernelGGL(qkvf_prefill_kernel, dim3(total), dim3(kThreads), 0, a.stream, p);
-  return hipGetLastError();
+  // 128 x 128 tiles, two workgroups per CU: measured faster than 256 x 128
+  // and 256 x 256 tiles at one workgroup per CU (770 and 605 us against
+  // 563 us per 8192 x 4096 x 7168 chunk), whose single register-staged
+  // prefetch stage leaves the loads' latency exposed
+  return launch_qkvf_prefill_t<128, 128, 64, 64>(p, N, a.stream);
 }
 
 }  // namespace bskv

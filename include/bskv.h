@@ -311,18 +311,19 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
  * -- "The fourth projection", Eq. 3: (Q, K, V, F) = phi_l(X), phi_l the
  * existing linear projection widened by one small head group.
  *
- * w  [hidden, (n_q_heads + 3 n_kv_heads) * head_dim] bf16 row-major; its
- *    columns are the query heads, then the key, value and Forecast heads
- *    (head_dim columns per head).  All inputs and Q/K/V outputs bf16
- *    (rounded to nearest even from fp32 sums); F fp32.
+ * w_t  [N, hidden] bf16 row-major, N = (n_q_heads + 3 n_kv_heads) *
+ *      head_dim: row n holds the weights of output column n (the layout a
+ *      linear layer stores, out x in); the columns are the query heads, then
+ *      the key, value and Forecast heads (head_dim columns per head).  All
+ *      inputs and Q/K/V outputs bf16 (rounded to nearest even from fp32
+ *      sums); F fp32.
  *
- * bskv_qkvf_proj_decode: one token per sequence, x [B, hidden].
+ * bskv_qkvf_proj_decode: one token per sequence, x [B, hidden], B <= 64.
  *   q_out [B, n_q_heads, head_dim]; the token's K and V are written into
  *   the caches (strides kv_strides, as for the attention calls) at position
  *   seq_len[b] - 1 (rows outside [0, kv_len) are not written); f_out
- *   [B, n_kv_heads, head_dim] fp32, ready for the decode selection.
- *   ws: bskv_qkvf_proj_workspace() bytes (split partials).  hidden a
- *   multiple of 256, the column count a multiple of 128.
+ *   [B, n_kv_heads, head_dim] fp32, ready for the decode selection.  One
+ *   launch, no workspace.  hidden a multiple of 1024.
  * bskv_qkvf_proj_prefill: a chunk of n_q_tokens tokens per sequence,
  *   x [B, n_q_tokens, hidden], starting at position q_start (a multiple of
  *   64; q_start + n_q_tokens <= kv_len).  q_out [B, n_q_heads, n_q_tokens,
@@ -336,12 +337,10 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
  *   bskv_forecast_block_score_topk from f_pooled (n_qb query blocks starting
  *   at global block q_start/64), same candidates, ties, union and outputs.
  * ----------------------------------------------------------------------- */
-size_t bskv_qkvf_proj_workspace(int B, int hidden, int n_q_heads, int n_kv_heads, int head_dim);
-int bskv_qkvf_proj_decode(const void* x, const void* w, int B, int hidden, int n_q_heads, int n_kv_heads,
+int bskv_qkvf_proj_decode(const void* x, const void* w_t, int B, int hidden, int n_q_heads, int n_kv_heads,
                           int head_dim, void* q_out, void* k_cache, void* v_cache, const int64_t* kv_strides,
-                          int64_t kv_len, const int64_t* seq_len, float* f_out, void* ws, size_t ws_bytes,
-                          hipStream_t stream);
-int bskv_qkvf_proj_prefill(const void* x, const void* w, int B, int n_q_tokens, int hidden, int n_q_heads,
+                          int64_t kv_len, const int64_t* seq_len, float* f_out, hipStream_t stream);
+int bskv_qkvf_proj_prefill(const void* x, const void* w_t, int B, int n_q_tokens, int hidden, int n_q_heads,
                            int n_kv_heads, int head_dim, int64_t q_start, void* q_out, void* k_cache, void* v_cache,
                            const int64_t* kv_strides, int64_t kv_len, float* f_pooled, hipStream_t stream);
 int bskv_forecast_block_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,

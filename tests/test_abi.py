@@ -206,20 +206,17 @@ def test_block_cache_validation():
 
 
 def test_qkvf_proj_validation():
-    ws = lib.bskv_qkvf_proj_workspace(8, 4096, 32, 8, 128)
-    assert ws >= 16 * 8 * (32 + 24) * 128 * 4
-    assert lib.bskv_qkvf_proj_workspace(8, 4096, 32, 8, 96) == 0
     dec = lib.bskv_qkvf_proj_decode
 
-    def dcall(x=P, B=8, hidden=4096, hq=32, hkv=8, d=128, sl=P, wsb=ws):
-        return dec(x, P, B, hidden, hq, hkv, d, P, P, P, S3, 131072, sl, P, P, wsb, None)
+    def dcall(x=P, B=8, hidden=4096, hq=32, hkv=8, d=128, sl=P):
+        return dec(x, P, B, hidden, hq, hkv, d, P, P, P, S3, 131072, sl, P, None)
     assert dcall(x=None) == EINVAL
     assert dcall(x=MIS) == EINVAL
     assert dcall(sl=None) == EINVAL
+    assert dcall(B=0) == EINVAL
     assert dcall(d=96) == EUNSUP
-    assert dcall(hidden=4000) == EUNSUP
-    assert dcall(hq=3, hkv=2, d=64) == EUNSUP          # 9 heads of 64 columns: not a whole number of 128-column tiles
-    assert dcall(wsb=ws - 4) == ENOSPC
+    assert dcall(hidden=3584) == EUNSUP               # not a multiple of 1024
+    assert dcall(B=65) == EUNSUP
     pre = lib.bskv_qkvf_proj_prefill
 
     def pcall(B=4, tq=2048, hidden=4096, hq=32, hkv=8, d=128, q0=0, kv_len=131072, fp=P):

@@ -604,7 +604,8 @@ def _bf16_close(got, want, rel=2.0 ** -8, abs_tol=1e-3):
     return bool(np.all(np.abs(got - want) <= rel * np.abs(want) + abs_tol))
 
 
-@pytest.mark.parametrize("B,hidden,Hq,Hkv,d", [(3, 512, 8, 2, 128), (16, 4096, 32, 8, 128), (5, 768, 4, 4, 64)])
+@pytest.mark.parametrize("B,hidden,Hq,Hkv,d", [(3, 1024, 8, 2, 128), (16, 4096, 32, 8, 128), (5, 2048, 4, 4, 64),
+                                           (40, 1024, 8, 2, 64), (64, 1024, 4, 1, 128)])
 def test_qkvf_proj_decode(B, hidden, Hq, Hkv, d):
     g = torch.Generator().manual_seed(B + hidden)
     x = torch.randn(B, hidden, generator=g).to(torch.bfloat16)
@@ -613,7 +614,7 @@ def test_qkvf_proj_decode(B, hidden, Hq, Hkv, d):
     kc = torch.full((B, Hkv, T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     vc = torch.full_like(kc, float("nan"))
     lens = torch.tensor([(37 * b) % T + 1 for b in range(B)], dtype=torch.int64)
-    q, f = bskv.qkvf_proj_decode(x.to(DEV), w.to(DEV), Hq, Hkv, kc, vc, lens.to(DEV))
+    q, f = bskv.qkvf_proj_decode(x.to(DEV), w.t().contiguous().to(DEV), Hq, Hkv, kc, vc, lens.to(DEV))
     torch.cuda.synchronize()
     wq, wk, wv, wf = orc.qkvf_proj(np64(x), np64(w), Hq, Hkv, d)
     assert _bf16_close(np64(q), wq)
@@ -637,7 +638,7 @@ def test_qkvf_proj_prefill(B, Tq, hidden, Hq, Hkv, d, q_start):
     T = q_start + Tq + 64
     kc = torch.full((B, Hkv, T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     vc = torch.full_like(kc, float("nan"))
-    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.to(DEV), Hq, Hkv, kc, vc, q_start=q_start)
+    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.t().contiguous().to(DEV), Hq, Hkv, kc, vc, q_start=q_start)
     torch.cuda.synchronize()
     wq, wk, wv, wfp = orc.qkvf_proj_prefill(np64(x), np64(w), Hq, Hkv, d, 64)
     assert _bf16_close(np64(q), wq)
@@ -661,7 +662,7 @@ def test_qkvf_prefill_chunk_end_to_end():
     k_prev = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
     v_prev = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
     kc_cache, vc_cache = k_prev.clone().to(DEV), v_prev.clone().to(DEV)
-    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.to(DEV), Hq, Hkv, kc_cache, vc_cache, q_start=q_start)
+    q, fp = bskv.qkvf_proj_prefill(x.to(DEV), w.t().contiguous().to(DEV), Hq, Hkv, kc_cache, vc_cache, q_start=q_start)
     seq_len = torch.full((B,), q_start + Tq, dtype=torch.int64, device=DEV)
     kcmp = _kc_gpu(kc_cache, seq_len)
     idx, cnt = bskv.forecast_block_score_topk_pooled(fp, kcmp, 4, 1, 2, q_start=q_start)
