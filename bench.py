@@ -57,12 +57,12 @@ METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
 # An entry holds the digest of the sources it was measured on and is reported
 # only while they are unchanged.
 PMC_TRAFFIC = {
-    "layer_k2": {"fetch_kib": 106877.3, "write_kib": 3515.4, "fetch_scale": 2.0, "write_scale": 1.0,
+    "layer_k2": {"fetch_kib": 106878.8, "write_kib": 3515.5, "fetch_scale": 2.0, "write_scale": 1.0,
                  "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                 "sha256": "b7c717bec220d5b7671228251db60a1e87afb714a8ef0f766edb3bfe83898583"},
-    "attn_prefill": {"fetch_kib": 366930.5, "write_kib": 65536.9, "fetch_scale": 2.0, "write_scale": 1.0,
+                 "sha256": "b42ab6e9d1ce782bf73f8ae3caeee87f81eb1f783c565eb012ca108c23065965"},
+    "attn_prefill": {"fetch_kib": 366930.5, "write_kib": 65536.1, "fetch_scale": 2.0, "write_scale": 1.0,
                      "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                     "sha256": "6a78de9b8288707e6f12d5b9db69ce2ff021dd111d2d94e5f123bff784e4f861"},
+                     "sha256": "50b4bde0514c3f4abde6a4f4d0db4684b7c2044d0f1862ab0ad0a90c8298eebd"},
 }
 
 
@@ -571,9 +571,10 @@ def run_decode(args, torch, bskv, wl, replicas=None):
     ach = bpl[dom] / kt[dom] / 1e9
     peaks = measured_hbm_peaks(torch)
     sweep = selection_sweep(torch, bench)
-    base_cmp = baseline_comparison(torch, bench, step_s, kt, args) if wl.hidden else None
-    win_sel = window_selection(torch, bench, kt) if wl.hidden else None
-    widened = widened_projection_decode(torch, bench, kt) if wl.hidden else None
+    extra = wl.hidden and not args.core_only
+    base_cmp = baseline_comparison(torch, bench, step_s, kt, args) if extra else None
+    win_sel = window_selection(torch, bench, kt) if extra else None
+    widened = widened_projection_decode(torch, bench, kt) if extra else None
     # replicas: independent copies of one layer's inputs, rotated so that the
     # working set does not sit in the 256 MB cache; the step then covers
     # `replicas` layer-steps of a one-layer model
@@ -842,9 +843,10 @@ def run_prefill(args, torch, bskv, wl):
     flops = bench.attention_flops()
     # per-kernel: each kernel over all chunks, graph-replayed, HIP events
     kt = {}
-    for name, fn in (("kv_block_meanpool", bench.pool), ("score_topk_prefill", bench.select),
-                     ("kv_window_meanpool", bench.window_pool), ("window_select_prefill", bench.window_select),
-                     ("attn_prefill", bench.attend)):
+    timed = [("kv_block_meanpool", bench.pool), ("score_topk_prefill", bench.select), ("attn_prefill", bench.attend)]
+    if not args.core_only:
+        timed[2:2] = [("kv_window_meanpool", bench.window_pool), ("window_select_prefill", bench.window_select)]
+    for name, fn in timed:
         def body():
             for c in range(bench.n_chunks):
                 fn(c)
@@ -878,18 +880,24 @@ def run_prefill(args, torch, bskv, wl):
         "attn_prefill": {"us": round(kt["attn_prefill"] * 1e6, 2), "TFLOPs": round(att_tf, 1),
                          "mfma_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
-    widened = widened_projection_prefill(torch, bench, kt, args)
-    # the overlapping-compression variant (32/16 windows, block scores
-    # max-pooled): its pooling and selection per chunk, and its whole step
-    # (the window selection leaves the lists of the block selector's place)
-    win_step_s, _ = time_graph(torch, bench.step_window, max(1, args.steps // 10), 1, use_graph=not args.no_graph)
-    window_variant = {
-        "window": bench.win, "stride": bench.wst,
-        "kv_window_meanpool_us": round(kt["kv_window_meanpool"] * 1e6, 2),
-        "window_select_prefill_us": round(kt["window_select_prefill"] * 1e6, 2),
-        "select_ratio_vs_block": round(kt["window_select_prefill"] / kt["score_topk_prefill"], 3),
-        "step_ms": round(win_step_s * 1e3, 3), "tokens_per_s": round(B * T / win_step_s, 1),
-    }
+    # least bytes of the attention, from the block selector's lists (the
+    # variants below overwrite them)
+    min_bytes = bench.min_attention_bytes()
+    widened = window_variant = None
+    if not args.core_only:
+        widened = widened_projection_prefill(torch, bench, kt, args)
+        # the overlapping-compression variant (32/16 windows, block scores
+        # max-pooled): its pooling and selection per chunk, and its whole step
+        # (the window selection leaves the lists of the block selector's place)
+        win_step_s, _ = time_graph(torch, bench.step_window, max(1, args.steps // 10), 1,
+                                   use_graph=not args.no_graph)
+        window_variant = {
+            "window": bench.win, "stride": bench.wst,
+            "kv_window_meanpool_us": round(kt["kv_window_meanpool"] * 1e6, 2),
+            "window_select_prefill_us": round(kt["window_select_prefill"] * 1e6, 2),
+            "select_ratio_vs_block": round(kt["window_select_prefill"] / kt["score_topk_prefill"], 3),
+            "step_ms": round(win_step_s * 1e3, 3), "tokens_per_s": round(B * T / win_step_s, 1),
+        }
     return {
         "metric": "prefill tokens/s at B×T (chunked, block-sparse); % bf16 MFMA peak", "value": round(B * T / step_s, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": max(1, args.steps // 10), "warmup": max(1, args.warmup // 5),
@@ -901,7 +909,7 @@ def run_prefill(args, torch, bskv, wl):
         "roofline": {"bound": "mfma", "kernel": "attn_prefill", "achieved": round(att_tf, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_bytes("attn_prefill"), "flops_per_launch": per_chunk_flops,
-                     "min_bytes_per_launch": round(bench.min_attention_bytes()),
+                     "min_bytes_per_launch": round(min_bytes),
                      "us_per_launch": round(kt["attn_prefill"] * 1e6, 2)},
         "attention_tflop_total": round(flops / 1e12, 2),
         "measured_gemm_bf16_TFLOPs": gemm_tf,
@@ -1342,6 +1350,9 @@ def main():
                     help="offload-steady: random-walk step of the Forecast input per decode step")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--core-only", action="store_true",
+                    help="only the workload's own path: no comparison selectors, variants or widened projection "
+                         "(for kernel traces and counters)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run one device copy of this many GiB (counter calibration)")
