@@ -131,3 +131,109 @@ def test_config5_offload_sampled():
             assert np.array_equal(got[0, g, :gc[0, g]], ring[0, g, :gc[0, g]])
         want = orc.attend_decode(np64(q[b:b + 1]), k, v, gi, gc, [wl.T], wl.scale, 64)
         assert max_abs(np64(out[b:b + 1]), want) < 2e-2
+
+
+def test_steady_offload_cache_full_size():
+    """B16, T=131072, the KV cache in host-pinned memory and a 128-slot cache
+    per (b, g): two decode steps with different Forecasts.  The lookups equal
+    the oracle's LRU exactly for every (b, g); the slots hold the host blocks
+    bytewise and the cached attention matches the oracle on sampled batch
+    elements."""
+    wl = CONFIGS[6]
+    lay = decode_inputs(wl, DEV, layers=1)[0]
+    kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
+    bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
+    hk = torch.empty(lay["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(lay["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hk.copy_(lay["k"])
+    hv.copy_(lay["v"])
+    q = lay["q"]
+    del lay["k"], lay["v"]
+    S = 128
+    cache = bskv.BlockCache(wl.B, wl.Hkv, S, wl.d, device=DEV)
+    tags = np.full((wl.B, wl.Hkv, S), -1, dtype=np.int64)
+    stamps = np.full((wl.B, wl.Hkv, S), -1, dtype=np.int64)
+    clock = np.zeros((wl.B, wl.Hkv), dtype=np.int64)
+    f0 = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    for f in (f0, f0 + 0.3 * f0.norm(dim=-1, keepdim=True) * torch.randn(f0.shape, generator=g, device=DEV) / 11.3):
+        idx, cnt = bskv.forecast_block_score_topk(f.contiguous(), kc, wl.topk, wl.n_init, wl.n_local,
+                                                  seq_len=lay["seq_len"])
+        slot, fill, n_fill = bskv.block_cache_plan(cache, idx, cnt)
+        bskv.prefetch_cache_fill(hk, hv, idx, slot, fill, n_fill, cache, n_workgroups=64)
+        out = bskv.block_sparse_attn_decode_cached(q, cache, slot, idx, cnt, lay["seq_len"], wl.scale)
+        torch.cuda.synchronize()
+        gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+        w_slot, w_fill, w_n = orc.block_cache_plan(tags, stamps, clock, gi, gc)
+        assert np.array_equal(slot.cpu().numpy(), w_slot) and np.array_equal(fill.cpu().numpy(), w_fill)
+        assert np.array_equal(n_fill.cpu().numpy(), w_n)
+        assert np.array_equal(cache.tags.cpu().numpy(), tags)
+        for b in (0, wl.B - 1):
+            ck = cache.k[b].view(torch.int16).cpu().numpy()
+            hb = hk[b].view(torch.int16).numpy()
+            for h in range(wl.Hkv):
+                for u in range(int(gc[b, h])):
+                    j = int(gi[b, h, u])
+                    assert np.array_equal(ck[h, w_slot[b, h, u]], hb[h, 64 * j: 64 * (j + 1)])
+            k = hk[b:b + 1].to(torch.float64).numpy()
+            v = hv[b:b + 1].to(torch.float64).numpy()
+            want = orc.attend_decode(np64(q[b:b + 1]), k, v, gi[b:b + 1], gc[b:b + 1], [wl.T], wl.scale, 64)
+            assert max_abs(np64(out[b:b + 1]), want) < 2e-2
+
+
+def test_window_select_config3_sampled():
+    """B8, T=131072: 32-token windows at stride 16 over every (b, g), decode
+    selection with block scores max-pooled from the windows, checked on two
+    sampled batch elements (all KV heads) against the oracle."""
+    wl = CONFIGS[3]
+    lay = decode_inputs(wl, DEV, layers=1)[0]
+    nw = (wl.T - 32) // 16 + 1
+    kcw = torch.empty(wl.B, wl.Hkv, nw, wl.d, dtype=torch.float32, device=DEV)
+    bskv.kv_window_meanpool(lay["k"], lay["seq_len"], kcw, 32, 16)
+    f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
+    idx, cnt = bskv.forecast_window_score_topk(f, kcw, wl.topk, wl.n_init, wl.n_local, lay["seq_len"], 32, 16)
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        k = np64(lay["k"][b:b + 1])
+        kw_or = orc.kv_window_meanpool(k, 32, 16)
+        fo = orc.forecast_proj(np64(lay["x_sel"][b:b + 1]), np64(lay["w_sel"]), wl.Hkv, wl.d)
+        sel = orc.decode_select_windows(fo, kw_or, [wl.T], wl.topk, wl.n_init, wl.n_local, 64, 32, 16)
+        assert check_selection(idx[b:b + 1], cnt[b:b + 1], sel, wl.topk) <= 1
+        assert max_abs(np64(kcw[b:b + 1, :, :64]), kw_or[:, :, :64]) < 1e-5
+
+
+def test_widened_projection_full_size_sampled():
+    """Decode: x [8 x 4096] @ W [4096 x 7168] (32 query heads, 8 KV and 8
+    Forecast heads of 128), every output against the oracle.  Prefill: one
+    2048-token chunk of four sequences, sampled tokens' Q/K/V and sampled
+    query blocks' Forecast sums."""
+    g = torch.Generator(device=DEV).manual_seed(11)
+    B, hid, Hq, H, d = 8, 4096, 32, 8, 128
+    N = (Hq + 3 * H) * d
+    w_t = (torch.randn(N, hid, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    x = torch.randn(B, hid, generator=g, device=DEV).to(torch.bfloat16)
+    T = 4096
+    kc = torch.zeros(B, H, T, d, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    lens = torch.full((B,), T, dtype=torch.int64, device=DEV)
+    q, f = bskv.qkvf_proj_decode(x, w_t, Hq, H, kc, vc, lens)
+    torch.cuda.synchronize()
+    w64 = np64(w_t).T
+    wq, wk, wv, wf = orc.qkvf_proj(np64(x), w64, Hq, H, d)
+    assert np.all(np.abs(np64(q) - wq) <= 2.0 ** -8 * np.abs(wq) + 1e-3)
+    assert np.all(np.abs(np64(kc[:, :, T - 1]) - wk) <= 2.0 ** -8 * np.abs(wk) + 1e-3)
+    assert max_abs(np64(f), wf) < 1e-3
+    Bp, C, q0, Tc = 4, 2048, 4096, 8192
+    xp = torch.randn(Bp, C, hid, generator=g, device=DEV).to(torch.bfloat16)
+    kcp = torch.zeros(Bp, H, Tc, d, dtype=torch.bfloat16, device=DEV)
+    vcp = torch.zeros_like(kcp)
+    qp, fp = bskv.qkvf_proj_prefill(xp, w_t, Hq, H, kcp, vcp, q_start=q0)
+    torch.cuda.synchronize()
+    for b, qi in ((0, 0), (Bp - 1, 31), (2, 13)):
+        xs = np64(xp[b:b + 1, 64 * qi:64 * (qi + 1)])
+        oq, ok_, ov, of = orc.qkvf_proj_prefill(xs, w64, Hq, H, d, 64)
+        gq = np64(qp[b:b + 1, :, 64 * qi:64 * (qi + 1)])
+        assert np.all(np.abs(gq - oq) <= 2.0 ** -8 * np.abs(oq) + 1e-3)
+        gk = np64(kcp[b:b + 1, :, q0 + 64 * qi:q0 + 64 * (qi + 1)])
+        assert np.all(np.abs(gk - ok_) <= 2.0 ** -8 * np.abs(ok_) + 1e-3)
+        assert max_abs(np64(fp[b:b + 1, :, qi:qi + 1]), of) < 2e-5 * np.abs(of).max() + 1e-3
