@@ -691,6 +691,8 @@ class PrefillBench:
         self.cnt = [torch.empty(self.B, wl.Hkv, n_qb, dtype=torch.int32, device=self.dev) for _ in range(n_chunks)]
         self.out = [torch.empty_like(self.q[0]) for _ in range(n_chunks)]
         self.seq_len = torch.full((self.B,), self.T, dtype=torch.int64, device=self.dev)
+        self.ws_sel = torch.zeros(max(256, bskv.workspace_bytes("score", self.B, wl.Hkv, self.C, nb, wl.d)),
+                                  dtype=torch.uint8, device=self.dev)
         # overlapping compression (32-token windows at stride 16) for the
         # variant's selection
         self.win, self.wst = 32, 16
@@ -706,7 +708,7 @@ class PrefillBench:
     def select(self, c):
         wl = self.wl
         self.bskv.forecast_block_score_topk(self.f[c], self.kc, wl.topk, wl.n_init, wl.n_local, q_start=c * self.C,
-                                            prefill=True, idx=self.idx[c], cnt=self.cnt[c])
+                                            prefill=True, idx=self.idx[c], cnt=self.cnt[c], ws=self.ws_sel)
 
     def window_pool(self, c):
         """The windows completed inside chunk c."""
@@ -786,13 +788,15 @@ def widened_projection_prefill(torch, bench, kt, args):
     fp = torch.empty(B, H, n_qb, d, dtype=torch.float32, device=dev)
     kcmp = torch.empty_like(bench.kc)
     out = torch.empty_like(q)
+    ws_sel = torch.zeros(max(256, bench.bskv.workspace_bytes("pooled", B, H, n_qb, kcmp.shape[2], d)),
+                         dtype=torch.uint8, device=dev)
 
     def proj(c):
         bench.bskv.qkvf_proj_prefill(x, w, wl.Hq, H, kc2, vc2, q_start=c * C, q_out=q, f_pooled=fp)
 
     def select(c):
         bench.bskv.forecast_block_score_topk_pooled(fp, kcmp, wl.topk, wl.n_init, wl.n_local, q_start=c * C,
-                                                    idx=bench.idx[c], cnt=bench.cnt[c])
+                                                    idx=bench.idx[c], cnt=bench.cnt[c], ws=ws_sel)
 
     def blas(c):
         return x.view(-1, hid) @ w.t()

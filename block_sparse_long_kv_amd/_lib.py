@@ -52,7 +52,9 @@ _proto("bskv_host_device_pointer", _i, _p, ctypes.POINTER(_p))
 _proto("bskv_qkvf_proj_decode", _i, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p, _p, _p)
 _proto("bskv_qkvf_proj_prefill", _i, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, ctypes.POINTER(_i64), _i64, _p,
        _p)
-_proto("bskv_forecast_block_score_topk_pooled", _i, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p)
+_proto("bskv_score_topk_pooled_workspace", _sz, _i, _i, _i, _i64, _i)
+_proto("bskv_forecast_block_score_topk_pooled", _i, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
+       _sz, _p)
 _proto("bskv_block_cache_reset", _i, _p, _p, _p, _i, _i, _i, _p)
 _proto("bskv_block_cache_plan", _i, _p, _p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p)
 _proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
@@ -110,7 +112,8 @@ def workspace_bytes(kind: str, *args) -> int:
     fn = {"proj": lib.bskv_forecast_proj_workspace, "score": lib.bskv_score_topk_workspace,
           "attn": lib.bskv_attn_decode_workspace, "layer": lib.bskv_decode_layer_lookahead_workspace,
           "multihead": lib.bskv_multihead_score_topk_workspace,
-          "window": lib.bskv_window_score_topk_workspace}[kind]
+          "window": lib.bskv_window_score_topk_workspace,
+          "pooled": lib.bskv_score_topk_pooled_workspace}[kind]
     return int(fn(*args))
 
 
@@ -170,17 +173,16 @@ def forecast_block_score_topk(f, kc, topk: int, n_init: int, n_local: int, seq_l
         n_qb = math.ceil(Tq / 64)
         idx = idx if idx is not None else torch.empty(B, H, n_qb, U, dtype=torch.int32, device=f.device)
         cnt = cnt if cnt is not None else torch.empty(B, H, n_qb, dtype=torch.int32, device=f.device)
-        ws_ptr, ws_n = None, 0
     else:
         Tq = 0
         idx = idx if idx is not None else torch.empty(B, H, U, dtype=torch.int32, device=f.device)
         cnt = cnt if cnt is not None else torch.empty(B, H, dtype=torch.int32, device=f.device)
         if return_scores:
             scores = torch.full((B, H, nb_cap), float("nan"), dtype=torch.float32, device=f.device)
-        lay = (B, H, 0, nb_cap, d)
-        nbytes = workspace_bytes("score", *lay)
-        ws = ws if ws is not None else _workspace(f.device, nbytes, sh, "score", lay)
-        ws_ptr, ws_n = _ptr(ws), ws.numel() * ws.element_size()
+    lay = (B, H, Tq, nb_cap, d)
+    nbytes = workspace_bytes("score", *lay)
+    ws = ws if ws is not None else _workspace(f.device, nbytes, sh, "score", lay)
+    ws_ptr, ws_n = _ptr(ws), ws.numel() * ws.element_size()
     _check(lib.bskv_forecast_block_score_topk(_ptr(f), _dt(f), Tq, q_start, _ptr(kc), nb_cap, _ptr(seq_len), B, H, d,
                                               64, topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(scores), ws_ptr,
                                               ws_n, sh), "forecast_block_score_topk")
@@ -382,7 +384,7 @@ def qkvf_proj_prefill(x, w_t, n_q_heads: int, n_kv_heads: int, k_cache, v_cache,
 
 
 def forecast_block_score_topk_pooled(f_pooled, kc, topk: int, n_init: int, n_local: int, q_start: int = 0, idx=None,
-                                     cnt=None, stream=None):
+                                     cnt=None, ws=None, stream=None):
     """Prefill selection from each query block's summed Forecast
     f_pooled [B, Hkv, n_qb, d] fp32: (idx [B, Hkv, n_qb, U], cnt [B, Hkv, n_qb])."""
     B, H, n_qb, d = f_pooled.shape
@@ -392,8 +394,12 @@ def forecast_block_score_topk_pooled(f_pooled, kc, topk: int, n_init: int, n_loc
     idx = idx if idx is not None else torch.empty(B, H, n_qb, U, dtype=torch.int32, device=f_pooled.device)
     cnt = cnt if cnt is not None else torch.empty(B, H, n_qb, dtype=torch.int32, device=f_pooled.device)
     sh = _stream(stream, f_pooled.device)
+    lay = (B, H, n_qb, kc.shape[2], d)
+    nbytes = workspace_bytes("pooled", *lay)
+    ws = ws if ws is not None else _workspace(f_pooled.device, nbytes, sh, "pooled", lay)
     _check(lib.bskv_forecast_block_score_topk_pooled(_ptr(f_pooled), n_qb, q_start, _ptr(kc), kc.shape[2], B, H, d, 64,
-                                                     topk, n_init, n_local, _ptr(idx), _ptr(cnt), sh),
+                                                     topk, n_init, n_local, _ptr(idx), _ptr(cnt), _ptr(ws),
+                                                     ws.numel() * ws.element_size(), sh),
            "forecast_block_score_topk_pooled")
     return idx, cnt
 

@@ -122,9 +122,11 @@ int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, i
     if (ws_bytes < bskv::score_topk_workspace_bytes(B, n_kv_heads, 0, kc_nb_cap, head_dim)) return BSKV_ENOSPC;
   } else {
     if (q_start < 0 || q_start % block) return BSKV_EINVAL;
-    if (scores_out) return BSKV_EINVAL;
+    if (scores_out || !ws || !aligned16(ws)) return BSKV_EINVAL;
     const int64_t n_qb = (n_q_tokens + block - 1) / block;
     if (n_qb > 65535 || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+    if (ws_bytes < bskv::score_topk_workspace_bytes(B, n_kv_heads, n_q_tokens, kc_nb_cap, head_dim))
+      return BSKV_ENOSPC;
   }
   bskv::ScoreTopkArgs a{f, f_dtype, n_q_tokens, q_start, kc, kc_nb_cap, seq_len, B, n_kv_heads, head_dim, block,
                         topk, n_init, n_local, U, idx_out, cnt_out, scores_out, ws, stream};
@@ -374,18 +376,26 @@ int bskv_qkvf_proj_prefill(const void* x, const void* w_t, int B, int n_q_tokens
   return finish(bskv::launch_qkvf_prefill(a));
 }
 
+size_t bskv_score_topk_pooled_workspace(int B, int n_kv_heads, int n_qb, int64_t kc_nb_cap, int head_dim) {
+  if (B <= 0 || n_kv_heads <= 0 || n_qb <= 0 || kc_nb_cap <= 0 || !head_dim_ok(head_dim)) return 0;
+  return bskv::prefill_select_workspace_bytes(B * n_kv_heads, n_qb, kc_nb_cap, head_dim, true);
+}
+
 int bskv_forecast_block_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,
                                           int64_t kc_nb_cap, int B, int n_kv_heads, int head_dim, int block, int topk,
-                                          int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out,
-                                          hipStream_t stream) {
-  if (!f_pooled || !kc || !idx_out || !cnt_out || !aligned16(f_pooled) || !aligned16(kc)) return BSKV_EINVAL;
+                                          int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  if (!f_pooled || !kc || !idx_out || !cnt_out || !ws) return BSKV_EINVAL;
+  if (!aligned16(f_pooled) || !aligned16(kc) || !aligned16(ws)) return BSKV_EINVAL;
   if (B <= 0 || n_kv_heads <= 0 || n_qb <= 0 || kc_nb_cap <= 0) return BSKV_EINVAL;
   if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
   if (q_start < 0 || q_start % 64) return BSKV_EINVAL;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
   if (kc_nb_cap > bskv::kMaxCandidates || n_qb > 65535 || (int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
+  if (ws_bytes < bskv::prefill_select_workspace_bytes(B * n_kv_heads, n_qb, kc_nb_cap, head_dim, true))
+    return BSKV_ENOSPC;
   return finish(bskv::launch_score_topk_pooled(f_pooled, n_qb, q_start, kc, kc_nb_cap, B, n_kv_heads, head_dim, topk,
-                                               n_init, n_local, idx_out, cnt_out, stream));
+                                               n_init, n_local, idx_out, cnt_out, ws, stream));
 }
 
 size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,

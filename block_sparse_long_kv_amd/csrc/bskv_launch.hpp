@@ -48,7 +48,8 @@ struct QkvfPrefillArgs {
 hipError_t launch_qkvf_prefill(const QkvfPrefillArgs& a);
 hipError_t launch_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,
                                    int64_t nb_cap, int B, int H, int D, int topk, int n_init, int n_local,
-                                   int32_t* idx, int32_t* cnt, hipStream_t stream);
+                                   int32_t* idx, int32_t* cnt, void* ws, hipStream_t stream);
+size_t prefill_select_workspace_bytes(int n_bg, int n_qb, int64_t nb_cap, int D, bool pooled);
 
 struct ScoreTopkArgs {
   const void* f; int f_dtype; int n_q_tokens; int64_t q_start;

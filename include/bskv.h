@@ -150,9 +150,14 @@ int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, 
  *   be NULL.
  * kc must hold compressed keys for every candidate block; kc_nb_cap is
  * limited to 12288 blocks (a 786432-token context).
- * ws: bskv_score_topk_workspace() bytes (may be 0 bytes for prefill).
+ * ws: bskv_score_topk_workspace() bytes, no initialisation needed (decode:
+ * candidate scores; prefill: each query block's summed Forecast and its
+ * score row).
  * Decode runs two launches: candidate scores in slices, then one top-k
- * workgroup per (b, g); prefill runs one workgroup per query block.
+ * workgroup per (b, g).  Prefill runs three: the Forecast sum of each query
+ * block; the scores of all query blocks of the chunk against the causal
+ * compressed keys as one fp32 MFMA contraction per (b, g); one top-k
+ * workgroup per query block.
  * ----------------------------------------------------------------------- */
 size_t bskv_score_topk_workspace(int B, int n_kv_heads, int n_q_tokens, int64_t kc_nb_cap, int head_dim);
 int bskv_forecast_block_score_topk(const void* f, int f_dtype, int n_q_tokens, int64_t q_start,
@@ -335,7 +340,8 @@ int bskv_prefetch_selected_blocks(const void* src_k, const void* src_v, int dtyp
  *   pointers 16-byte aligned.  No workspace.
  * bskv_forecast_block_score_topk_pooled: the prefill selection of
  *   bskv_forecast_block_score_topk from f_pooled (n_qb query blocks starting
- *   at global block q_start/64), same candidates, ties, union and outputs.
+ *   at global block q_start/64), same candidates, ties, union and outputs;
+ *   ws: bskv_score_topk_pooled_workspace() bytes (score rows).
  * ----------------------------------------------------------------------- */
 int bskv_qkvf_proj_decode(const void* x, const void* w_t, int B, int hidden, int n_q_heads, int n_kv_heads,
                           int head_dim, void* q_out, void* k_cache, void* v_cache, const int64_t* kv_strides,
@@ -343,10 +349,11 @@ int bskv_qkvf_proj_decode(const void* x, const void* w_t, int B, int hidden, int
 int bskv_qkvf_proj_prefill(const void* x, const void* w_t, int B, int n_q_tokens, int hidden, int n_q_heads,
                            int n_kv_heads, int head_dim, int64_t q_start, void* q_out, void* k_cache, void* v_cache,
                            const int64_t* kv_strides, int64_t kv_len, float* f_pooled, hipStream_t stream);
+size_t bskv_score_topk_pooled_workspace(int B, int n_kv_heads, int n_qb, int64_t kc_nb_cap, int head_dim);
 int bskv_forecast_block_score_topk_pooled(const float* f_pooled, int n_qb, int64_t q_start, const float* kc,
                                           int64_t kc_nb_cap, int B, int n_kv_heads, int head_dim, int block, int topk,
-                                          int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out,
-                                          hipStream_t stream);
+                                          int n_init, int n_local, int32_t* idx_out, int32_t* cnt_out, void* ws,
+                                          size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
  * Resident block cache for offloaded decode.  The pages do not describe

@@ -48,7 +48,7 @@ def test_strerror_and_version():
 def test_workspace_queries_are_pure_host_arithmetic():
     assert lib.bskv_forecast_proj_workspace(8, 4096, 8, 128, 1) >= 16 * 8 * 1024 * 4
     assert lib.bskv_score_topk_workspace(8, 8, 0, 2048, 128) >= 64 * 2048 * 4
-    assert lib.bskv_score_topk_workspace(4, 8, 2048, 2048, 128) == 0
+    assert lib.bskv_score_topk_workspace(4, 8, 2048, 2048, 128) >= 32 * 32 * 2048 * 4     # prefill score rows
     assert lib.bskv_attn_decode_workspace(8, 32, 8, 128, 69) > 0
     assert lib.bskv_attn_decode_workspace(8, 24, 8, 128, 69) == 0     # group size 3 unsupported
     assert lib.bskv_forecast_proj_workspace(0, 4096, 8, 128, 1) == 0
@@ -230,9 +230,13 @@ def test_qkvf_proj_validation():
     assert pcall(hidden=4000) == EUNSUP
     assert pcall(hkv=1, d=64) == EUNSUP               # a 64-column head group would straddle a tile
     pooled = lib.bskv_forecast_block_score_topk_pooled
+    pws = lib.bskv_score_topk_pooled_workspace(4, 8, 32, 2048, 128)
+    assert pws >= 32 * 32 * 2048 * 4
 
-    def scall(fp=P, nqb=32, q0=0, d=128, blk=64, ni=1, nl=4, cap=2048):
-        return pooled(fp, nqb, q0, P, cap, 4, 8, d, blk, 64, ni, nl, P, P, None)
+    def scall(fp=P, nqb=32, q0=0, d=128, blk=64, ni=1, nl=4, cap=2048, ws=P, wsb=pws):
+        return pooled(fp, nqb, q0, P, cap, 4, 8, d, blk, 64, ni, nl, P, P, ws, wsb, None)
+    assert scall(ws=None) == EINVAL
+    assert scall(wsb=pws - 4) == ENOSPC
     assert scall(fp=None) == EINVAL
     assert scall(nqb=0) == EINVAL
     assert scall(q0=32) == EINVAL

@@ -366,6 +366,9 @@ def test_window_select_prefill(dtype, d, window, stride, n_local, q_start, Tq):
 
 
 def test_window_select_prefill_block_sized_windows_equal_block_selector():
+    """Block-sized windows give the block selector's prefill lists: both
+    GPU paths (per-query-block window scoring; the MFMA score contraction)
+    against the oracle's block selection, near-tie swaps only."""
     B, Hkv, d, T, q0 = 2, 4, 128, 64 * 300, 64 * 200
     g = torch.Generator().manual_seed(31)
     f = torch.randn(B, Hkv, T - q0, d, generator=g).to(torch.bfloat16).to(DEV)
@@ -376,7 +379,8 @@ def test_window_select_prefill_block_sized_windows_equal_block_selector():
     i1, c1 = bskv.forecast_window_score_topk(f, kcw, 16, 1, 3, None, 64, 64, q_start=q0)
     i2, c2 = bskv.forecast_block_score_topk(f, kc, 16, 1, 3, q_start=q0, prefill=True)
     torch.cuda.synchronize()
-    assert torch.equal(c1, c2) and torch.equal(i1, i2)
+    sel = orc.prefill_select(np64(f), orc.kv_block_meanpool(np64(k), 64), q0, 16, 1, 3, 64)
+    assert check_selection(i1, c1, sel, 16) <= 2 and check_selection(i2, c2, sel, 16) <= 2
 
 
 # ----------------------------------------------------------------------------- a4 decode
@@ -478,6 +482,23 @@ def _prefill_case(seed, B, Hq, Hkv, d, T, q_start, Tq, topk, n_local, n_plant=3)
 def test_prefill_selection(q_start, Tq):
     c, _, idx, cnt, sel = _prefill_case(21, 2, 8, 2, 128, 2048, q_start, Tq, topk=6, n_local=4)
     check_selection(idx, cnt, sel, 6)
+
+
+@pytest.mark.parametrize("d,q_start,Tq,n_local", [(128, 64 * 2500, 64 * 40 + 5, 2), (64, 64 * 70, 64 * 33, 1)])
+def test_prefill_selection_long_context(d, q_start, Tq, n_local):
+    """Query blocks with more than 2048 candidates (the top-k's streaming
+    path), more than 32 query blocks per chunk (two query-block tiles of the
+    score contraction), a ragged last query block."""
+    B, Hkv, T = 1, 2, q_start + Tq
+    g = torch.Generator().manual_seed(d + Tq)
+    f = torch.randn(B, Hkv, Tq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    lens = torch.full((B,), T, dtype=torch.int64, device=DEV)
+    kc = _kc_gpu(k.to(DEV), lens)
+    idx, cnt = bskv.forecast_block_score_topk(f.to(DEV), kc, 16, 1, n_local, q_start=q_start, prefill=True)
+    torch.cuda.synchronize()
+    sel = orc.prefill_select(np64(f), orc.kv_block_meanpool(np64(k), 64), q_start, 16, 1, n_local, 64)
+    assert check_selection(idx, cnt, sel, 16) <= 4
 
 
 @pytest.mark.parametrize("d,G,q_start,Tq", [(128, 4, 0, 1024), (128, 4, 1024, 1024), (128, 2, 512, 300),
