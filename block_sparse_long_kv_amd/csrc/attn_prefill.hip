@@ -19,10 +19,14 @@
 //     a-1) or runs the softmax of block a.  Waves w and w+HPW share a SIMD, so
 //     each SIMD always has one wave on the matrix cores while the other keeps
 //     the VALU busy; one barrier closes each slot.
-//   * K and V live in two LDS stages each, staged with 16-byte writes (rows
-//     padded); K runs one block ahead of V.  The V^T operand is read with
-//     gfx950's transposing LDS read (ds_read_b64_tr_b16), two per operand.
-//     Global loads for the next blocks are issued two slots before use.
+//   * K and V live in LDS rings (four stages each with four heads per
+//     workgroup, else two) filled by gfx950's global-to-LDS copies
+//     (global_load_lds_dwordx4): no registers hold the blocks in transit and
+//     no LDS writes are issued, and with four stages a block's copy is issued
+//     four slots before its first read.  Rows are unpadded (a copy writes
+//     1024 contiguous bytes) with 16-byte chunks XOR-swizzled per row, which
+//     keeps the K fragment reads and the transposing V reads
+//     (ds_read_b64_tr_b16, two per operand) free of extra bank conflicts.
 //   * Online softmax with a lazy maximum: the running maximum only moves when
 //     a row's block maximum exceeds it by more than 8 (base-2 units), so the
 //     output is rarely rescaled; probabilities stay below 2^8, which fp32
@@ -46,6 +50,30 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
 
+// Copy of 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i of the wave writes bytes [16 i, 16 i + 16)
+// after the wave-uniform LDS address `lds`.  The copy is counted by the
+// wave's vmcnt like any load and has no register result; the caller waits
+// for it (s_waitcnt vmcnt) and then synchronises the workgroup before any
+// wave reads the bytes.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt with vmcnt = n (n < 64) and the other counters left open
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
     const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,
@@ -53,16 +81,25 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
     int64_t q_start, int Tq, int Hkv, int G, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {
   constexpr int BLK = 64;
   constexpr int NT = HPW * 128;        // threads: 2*HPW waves
-  constexpr int KSTR = D + 8;          // LDS row of K: D bf16 + 16 bytes
-  constexpr int VSTR = D + 16;         // LDS row of V: D bf16 + 32 bytes (transposing reads hit distinct banks)
-  constexpr int RCH = D / 8;           // 16-byte chunks per token row
-  constexpr int NCH = BLK * RCH;       // 16-byte chunks per block per tensor
-  constexpr int CPT = (NCH + NT - 1) / NT;  // chunks per thread per tensor
+  constexpr int NW = NT / 64;
+  constexpr int RB = D * 2;            // bytes per K/V row
+  constexpr int RCH = D / 8;           // 16-byte chunks per row
+  constexpr int TILE = BLK * RB;       // bytes of one K or V block
+  constexpr int PPW = TILE / 1024 / NW;  // 1024-byte copy pieces per wave per tile
+  static_assert(PPW >= 1 && PPW * NW * 1024 == TILE, "copy pieces");
+  // ring stages: four (a copy is issued four slots before its block is
+  // read) for four heads per workgroup, two otherwise (so that two
+  // workgroups still share a CU)
+  constexpr int NST = HPW == 4 ? 4 : 2;
   constexpr int KS = D / 32;           // k-steps of S^T
   constexpr int MD = D / 16;           // d tiles of O^T
   constexpr float TAU = 8.f;           // lazy-maximum threshold (base 2)
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[2][BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_bits Vs[2][BLK * VSTR];
+  // Unpadded rows with 16-byte chunks XOR-swizzled per row (the copies write
+  // whole 1024-byte pieces, so rows cannot be padded): K chunk c of row r
+  // sits at chunk c ^ (r % RCH), V chunk c at c ^ 2 (r % MD).  Both keep the
+  // MFMA fragment reads below at the bank-conflict level of padded rows.
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[NST][TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[NST][TILE];
 
   const int n_tiles = gridDim.x;
   int lin = blockIdx.x;
@@ -81,6 +118,21 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
   const int l16 = lane & 15, lg = lane >> 4;
   const int qb = (int)(q_start / BLK) + qi;
   const int tq0 = qi * BLK;
+
+  // no block lies inside K/V shorter than one block: every query row has
+  // nothing to attend to and its output is zero
+  if (kv_len < BLK) {
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      const int t = tq0 + row0 + 16 * nq + l16;
+      if (t < Tq) {
+        bf16_bits* op = out + (((int64_t)b * Hq + h) * Tq + t) * D + 4 * lg;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) *reinterpret_cast<uint2*>(op + 16 * md) = make_uint2(0, 0);
+      }
+    }
+    return;
+  }
 
   // Q^T fragments (B operand of S^T): query rows row0 + 16*nq + l16
   bf16x8_t qf[2][KS];
@@ -115,43 +167,65 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
   // gives p = 0 without special cases; the row sum is a per-lane partial
   float m_run[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
 
+  // The Q fragments have arrived before any copy is issued (vmcnt 0); the
+  // compiler, which does not see the copies, then places no wait for them
+  // inside the slot loop, where it would also wait for the copies in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
   const int64_t prob = (int64_t)bg * n_qb + qi;
   const int c = min(cnt[prob], U);
   // the block list is read through the constant address space: uniform
-  // indices then give scalar loads, which do not wait behind the K/V loads
-  // in flight (vector loads complete in order)
+  // indices then give scalar loads, which do not wait behind the copies in
+  // flight (vector memory operations complete in order)
   const __attribute__((address_space(4))) int32_t* list =
       (const __attribute__((address_space(4))) int32_t*)(idx + prob * U);
   const bf16_bits* kb = k + b * sb + g * sg;
   const bf16_bits* vb = v + b * sb + g * sg;
 
-  // a listed block is used only if it lies inside the K/V buffers
+  // a listed block is used only if it lies inside the K/V buffers; a block
+  // outside them is masked whole and its copy reads block 0 instead (K/V
+  // hold at least one block here), so the stage holds finite values
   auto valid = [&](int jj) { return jj >= 0 && ((int64_t)jj + 1) * BLK <= kv_len; };
-  uint4 kreg[CPT], vreg[CPT];
+  // this lane's share of a tile: piece wid*PPW + i covers LDS chunks
+  // 64 (wid*PPW + i) + lane, i.e. row r, stored chunk cs; the global chunk
+  // is the logical one, cs ^ swizzle(r)
+  const uint32_t ks_base = lds_u32(&Ks[0][0]), vs_base = lds_u32(&Vs[0][0]);
+  auto copy_tile = [&](const bf16_bits* base, uint32_t lds_stage, int jj, bool is_v) {
+    const bf16_bits* p0 = base + (int64_t)(valid(jj) ? jj : 0) * BLK * st;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
-  auto gload = [&](uint4 (&reg)[CPT], const bf16_bits* base, int jj) {
-    if (!valid(jj)) return;
-    const bf16_bits* p0 = base + (int64_t)jj * BLK * st;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
-      if (NCH % NT == 0 || ch < NCH) reg[i] = ld16(p0 + (int64_t)r * st + cc * 8);
+    for (int i = 0; i < PPW; ++i) {
+      const int piece = wid * PPW + i;
+      const int qc = piece * 64 + lane, r = qc / RCH, cs = qc % RCH;
+      const int cl = cs ^ (is_v ? 2 * (r % MD) : r % RCH);
+      lds_dma16(p0 + (int64_t)r * st + cl * 8, __builtin_amdgcn_readfirstlane(lds_stage + piece * 1024));
     }
   };
-  auto lstore = [&](bf16_bits* dst, int stride, const uint4 (&reg)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * NT, r = ch / RCH, cc = ch % RCH;
-      if (NCH % NT != 0 && ch >= NCH) continue;
-      *reinterpret_cast<uint4*>(&dst[r * stride + cc * 8]) = reg[i];
-    }
+  // copies issued at the start of even slot 2m: V(m-2+NST), then
+  // K(m-1+NST), into the stages their blocks' predecessors left in slot 2m-1
+  auto issue = [&](int m) {
+    const int jv = m - 2 + NST, jk = m - 1 + NST;
+    if (jv >= 0 && jv < c) copy_tile(vb, vs_base + (jv % NST) * TILE, list[jv], true);
+    if (jk >= 0 && jk < c) copy_tile(kb, ks_base + (jk % NST) * TILE, list[jk], false);
   };
+  // before the barrier that opens slot 2m: K(m) and V(m-1) have landed.  They
+  // were issued in slot 2(m-NST+1); every later slot issued 2 PPW copies
+  // while the blocks exist, else nothing is left in flight that matters.
+  auto wait_copies = [&](int m) {
+    if (m + NST - 2 < c) wait_vm<2 * (NST - 2) * PPW>();
+    else wait_vm<0>();
+  };
+
+  // per-lane LDS byte offsets of the fragment reads
+  int kofs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = l16 * RB + 16 * ((4 * ks + lg) ^ (l16 % RCH));
+  const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  const int vrow = tr_row * RB + 16 * (tr_col >> 3) + 2 * (tr_col & 7), vsw = tr_row % MD;
 
   // MFMA slot: S^T = K(a) Q^T (a < c) and O^T += V(a-1)^T P(a-1)^T (a >= 1)
   auto mfma_slot = [&](int a) {
     if (a < c) {
-      const bf16_bits* kst = Ks[a & 1];
+      const unsigned char* kst = &Ks[a % NST][0];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -160,8 +234,7 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const bf16x8_t a_op =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&kst[(16 * mt + l16) * KSTR + 32 * ks + 8 * lg]));
+          const bf16x8_t a_op = as_bf16x8(*reinterpret_cast<const uint4*>(kst + kofs[ks] + mt * 16 * RB));
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq)
             s[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, qf[nq][ks], s[mt][nq], 0, 0, 0);
@@ -173,16 +246,16 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
       // 32*s2 + 16 + 4*lg + {0..3}) comes from row-major V with transposing LDS
       // reads: within each 16-lane group, lane 4r+c reads key row r, columns
       // 4c..4c+3, and ds_read_b64_tr_b16 hands lane i element i%4 of lane
-      // 4r+i/4 for r = 0..3.
-      const bf16_bits* vst = Vs[(a - 1) & 1];
-      const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
+      // 4r+i/4 for r = 0..3.  Rows 32*s2 + tr_row and 16 below it share the
+      // row swizzle, so only the d tile's chunk pair moves: md ^ (row % MD).
+      const unsigned char* vst = &Vs[(a - 1) % NST][0];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const bf16_bits* v0 = &vst[(32 * s2 + tr_row) * VSTR + 16 * md + tr_col];
+          const unsigned char* v0 = vst + 32 * s2 * RB + vrow + 32 * (md ^ vsw);
           const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * VSTR));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * RB));
           const bf16x8_t a_op =
               __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
@@ -257,49 +330,37 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
     }
   };
 
-  // prologue: K(0) staged; K(1) and V(0) requested.  The explicit wait
-  // (vmcnt 0) tells the compiler that the Q fragments have arrived on every
-  // path, so no wait for them lands inside the slot loop, where it would
-  // also wait for the K/V requests in flight.
-  if (c > 0) {
-    gload(kreg, kb, list[0]);
-    lstore(Ks[0], KSTR, kreg);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  if (c > 1) gload(kreg, kb, list[1]);
-  if (c > 0) gload(vreg, vb, list[0]);
-  __syncthreads();
-
   // Slots: group A runs M(0) S(0) M(1) S(1) ... S(c-1) M(c) in slots 0..2c,
   // group B the same sequence in slots 1..2c+1, where M(a) is the MFMA slot
   // of block a and S(a) its softmax slot; one barrier closes each slot.  K(u)
-  // is read in slots 2u and 2u+1, V(u) in slots 2u+2 and 2u+3.  Odd slot
-  // 2u-1 (after S(u-1) in group A, after M(u-1) in group B) stages K(u) and
-  // V(u-1) into LDS stages whose previous blocks were last read in slot 2u-3,
-  // and requests K(u+1) and V(u).
-  // The stores are unconditional: for u >= c (K) or u > c (V) they fill a
-  // stage that is not read again, and keeping them branch-free lets the
-  // compiler see that the previous loads into kreg/vreg have completed, so
-  // the new requests do not wait for anything.
-  auto stage = [&](int u) {
-    lstore(Ks[u & 1], KSTR, kreg);
-    lstore(Vs[(u - 1) & 1], VSTR, vreg);
-    if (u + 1 < c) gload(kreg, kb, list[u + 1]);
-    if (u < c) gload(vreg, vb, list[u]);
-  };
-  if (grp == 1) __syncthreads();            // slot 0: group B idle
+  // is read in slots 2u and 2u+1, V(u) in slots 2u+2 and 2u+3.  Every wave
+  // copies its share of each tile: at the start of even slot 2m the copies
+  // of V(m-2+NST) and K(m-1+NST) go into the stages of V(m-2) and K(m-1),
+  // last read in slot 2m-1; before the barrier closing slot 2m-1 each wave
+  // waits for its copies of K(m) and V(m-1).  The prologue issues the copies
+  // of the slots before 0 (K(0..NST-2), V(0..NST-3)) and waits for K(0).
+#pragma unroll
+  for (int m = 1 - NST; m < 0; ++m) issue(m);
+  wait_copies(0);
+  __syncthreads();
+  if (grp == 1) {                      // slot 0: group B idle
+    issue(0);
+    __syncthreads();
+  }
   for (int a = 0;; ++a) {
+    if (grp == 0) issue(a);            // A: slot 2a
     __builtin_amdgcn_s_setprio(1);
     mfma_slot(a);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) stage(a + 1);
+    if (grp == 1) wait_copies(a + 1);  // B: slot 2a+1 closes
     __syncthreads();
     if (a == c) break;
+    if (grp == 1) issue(a + 1);        // B: slot 2a+2
     softmax_slot(a);
-    if (grp == 0) stage(a + 1);
+    if (grp == 0) wait_copies(a + 1);  // A: slot 2a+1 closes
     __syncthreads();
   }
-  if (grp == 0) __syncthreads();            // slot 2c+1: group A idle
+  if (grp == 0) __syncthreads();       // slot 2c+1: group A idle
 
   // epilogue: O[query][d] = O^T[d][query] / l
 #pragma unroll
