@@ -152,9 +152,9 @@ class DecodeBench:
             self.mh_select(l)
             self.attend(l)
 
-    def layer(self, l, stages=7):
+    def layer(self, l, stages=3):
         """Layer l: newest-block update, attention over B_l, and (lookahead)
-        F_l scoring layer l+1's compressed keys -> B_{l+1}; three kernels."""
+        F_l scoring layer l+1's compressed keys -> B_{l+1}; two kernels."""
         wl, lay = self.wl, self.layers[l]
         nxt = l + 1 < self.L
         n = self.layers[l + 1] if nxt else None
@@ -199,13 +199,13 @@ class DecodeBench:
         attn = B * H * (U * wl.block * d * e * 2) + B * wl.Hq * d * e + lists
         out = B * wl.Hq * d * 4
         # the fused kernels are timed over all L layers, and the last layer
-        # selects nothing (no scoring in its K2, no lists in its K3): per-launch
-        # figures are averages over the timed launches
+        # selects nothing (no scoring or lists in its K2): per-launch figures
+        # are averages over the timed launches
         nxt = (self.L - 1) / self.L
         return {
             "forecast_proj": proj, "kv_block_meanpool": pool, "score_topk": score + lists,
             "attn_decode": attn + out,
-            "layer_k1": proj, "layer_k2": round(score * nxt + attn), "layer_k3": round(lists * nxt + out + pool),
+            "layer_k1": proj, "layer_k2": round((score + lists) * nxt + attn + out + pool),
         }
 
     def step_bytes(self):
@@ -248,14 +248,13 @@ def kernel_times(torch, bench, reps=3):
     launches of one kernel over all layers, repeated `reps` times, are
     captured in a HIP graph and its replay is timed with HIP events on the
     stream it runs on, so host-side launch cost does not enter.  layer_k1/
-    k2/k3 are the three kernels of the fused layer, each launched on its own
-    (stages 1, 2, 4) after a full pass has filled the workspace they read."""
+    k2 are the two kernels of the fused layer, each launched on its own
+    (stages 1, 2) after a full pass has filled the workspace they read."""
     res = {}
     for l in range(bench.L):
         bench.layer(l)
     torch.cuda.synchronize()
     for name, fn in (("layer_k1", lambda l: bench.layer(l, 1)), ("layer_k2", lambda l: bench.layer(l, 2)),
-                     ("layer_k3", lambda l: bench.layer(l, 4)),
                      ("kv_block_meanpool", bench.meanpool), ("forecast_proj", bench.proj),
                      ("score_topk", bench.select), ("attn_decode", bench.attend)):
         # the last layer selects nothing, so it has no projection kernel

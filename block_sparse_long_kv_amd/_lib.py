@@ -104,7 +104,8 @@ def _strides3(t: torch.Tensor):
 
 
 # Workspaces: one buffer per (device, stream, call kind, layout), allocated
-# on first use and reused by later calls of the same kind and layout.
+# zero-filled on first use (the decode layer's arrival counters start at
+# zero) and reused by later calls of the same kind and layout.
 _WS: dict = {}
 
 
@@ -121,7 +122,7 @@ def _workspace(device, nbytes: int, stream_handle: int, kind: str, layout: tuple
     key = (device.index, stream_handle, kind, layout)
     buf = _WS.get(key)
     if buf is None:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
 
@@ -485,11 +486,11 @@ def block_sparse_attn_decode_cached(q, cache: "BlockCache", slot, idx, cnt, seq_
 
 def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None = None, out=None, x=None, w=None,
                            kc_next=None, idx_next=None, cnt_next=None, topk: int = 0, n_init: int = 1,
-                           n_local: int = 1, stages: int = 7, ws=None, stream=None):
+                           n_local: int = 1, stages: int = 3, ws=None, stream=None):
     """One decode layer: newest-block update of kc, this layer's attention over
     (idx, cnt), and (when x is given) the next layer's selection from the
     Forecast x @ w against kc_next, written to idx_next / cnt_next.
-    stages: bit mask of the three launches (7 = all, in order)."""
+    stages: bit mask of the two launches (3 = both, in order)."""
     B, Hq, d = q.shape
     Hkv, nb_cap = kc.shape[1], kc.shape[2]
     U = idx.shape[-1]

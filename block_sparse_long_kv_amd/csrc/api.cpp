@@ -414,7 +414,7 @@ int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int
                                 int n_init, int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return BSKV_EDTYPE;
   if (!q || !k || !v || !seq_len || !kc || !idx || !cnt || !out || !ws) return BSKV_EINVAL;
-  if (stages < 1 || stages > 7) return BSKV_EINVAL;
+  if (stages < 1 || stages > 3) return BSKV_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(ws)) return BSKV_EINVAL;
   const bool sel = x != nullptr;
   if (sel != (w_forecast != nullptr) || sel != (kc_next != nullptr) || sel != (idx_next != nullptr) ||

@@ -156,7 +156,7 @@ struct DecodeLayerArgs {
   const void* x; const void* w; int hidden;               // Forecast projection (x == nullptr: no next layer)
   const float* kc_next; int32_t* idx_next; int32_t* cnt_next;
   int topk, n_init, n_local;
-  int stages;                        // bit mask of the three launches
+  int stages;                        // bit mask of the two launches
 };
 size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype);
 hipError_t launch_decode_layer(const DecodeLayerArgs& a);

@@ -259,7 +259,20 @@ __device__ __forceinline__ DecodeCands decode_cands(int64_t L, int64_t nb_cap, i
   return r;
 }
 
-template <int D>
+// Agent-coherent 32-bit store and load (relaxed atomics at device scope):
+// every XCD sees the value without cache maintenance, so workgroups of one
+// launch can hand results to each other through an arrival counter (the
+// writer waits for its stores to complete before it counts).
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// CO: the scores are stored agent-coherent (read by another workgroup of the
+// same launch)
+template <int D, bool CO = false>
 __device__ __forceinline__ void score_slice_wg(const float* fvec, const float* __restrict__ kc_bg, int lo, int hi,
                                float* __restrict__ sc) {
   constexpr int LPR = 8;
@@ -295,13 +308,18 @@ __device__ __forceinline__ void score_slice_wg(const float* fvec, const float* _
         }
       }
       acc = sum8(acc);   // the 8 lanes of the row (all active together)
-      if (sub == 0 && j < hi) sc[j] = acc;
+      if (sub == 0 && j < hi) {
+        if constexpr (CO) st_agent(sc + j, acc);
+        else sc[j] = acc;
+      }
     }
   }
 }
 
 // Top-k + union of one decode problem from its score row (written by an
-// earlier kernel).  keys: LDS, at least (c1 - c0) entries.
+// earlier kernel, or agent-coherent by this one when CO).  keys: LDS, at
+// least (c1 - c0) entries.
+template <bool CO = false>
 __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, DecodeCands dc, int topk, int n_init,
                                                int n_local, int U,
                                int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, uint32_t* keys,
@@ -314,7 +332,7 @@ __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, Dec
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = 8 * (int)threadIdx.x + e;
-      v[e] = i < n ? sc[dc.c0 + i] : 0.f;
+      v[e] = i < n ? (CO ? ld_agent(sc + dc.c0 + i) : sc[dc.c0 + i]) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) kin[e] = orderable_key(v[e]);
@@ -327,7 +345,7 @@ __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, Dec
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
       const int i = base + e * kThreads + threadIdx.x;
-      v[e] = i < n ? sc[dc.c0 + i] : 0.f;
+      v[e] = i < n ? (CO ? ld_agent(sc + dc.c0 + i) : sc[dc.c0 + i]) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
@@ -495,7 +513,7 @@ __device__ __forceinline__ void attn_block(const AttnRegs<T, D, G>& r, int nvali
 
 // End of a split: sum the PV token lanes (inside the wave, then across the
 // 4 waves) and write the unnormalised output and (m, l) of every head.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool CO>
 __device__ __forceinline__ void attn_split_finish(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm,
                                                   float (&acc)[G][VecN<T>::N], const float* m_run,
                                                   const float* l_run) {
@@ -525,19 +543,28 @@ __device__ __forceinline__ void attn_split_finish(const AttnDecodeParams& p, int
   const int64_t pbase = ((int64_t)bg * p.n_splits + split) * G;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i % D;
-    p.ws_o[(pbase + h) * D + d] = sm.red[0][h][d] + sm.red[1][h][d] + sm.red[2][h][d] + sm.red[3][h][d];
+    const float o = sm.red[0][h][d] + sm.red[1][h][d] + sm.red[2][h][d] + sm.red[3][h][d];
+    if constexpr (CO) st_agent(p.ws_o + (pbase + h) * D + d, o);
+    else p.ws_o[(pbase + h) * D + d] = o;
   }
 #pragma unroll
   for (int i = 0; i < HW; ++i) {
     const int h = wid + 4 * i;
     if (h < G && lane == 0) {
-      p.ws_ml[(pbase + h) * 2 + 0] = m_run[i];
-      p.ws_ml[(pbase + h) * 2 + 1] = l_run[i];
+      if constexpr (CO) {
+        st_agent(p.ws_ml + (pbase + h) * 2 + 0, m_run[i]);
+        st_agent(p.ws_ml + (pbase + h) * 2 + 1, l_run[i]);
+      } else {
+        p.ws_ml[(pbase + h) * 2 + 0] = m_run[i];
+        p.ws_ml[(pbase + h) * 2 + 1] = l_run[i];
+      }
     }
   }
 }
 
-template <typename T, int D, int G>
+// CO: the partials are stored agent-coherent (merged by another workgroup
+// of the same launch)
+template <typename T, int D, int G, bool CO = false>
 __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
   using R = AttnRegs<T, D, G>;
   constexpr int VEC = R::VEC;
@@ -608,7 +635,7 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
     attn_block<T, D, G>(rb, nvb < 0 ? 0 : nvb, sm, qf, sscale, acc, m_run, l_run);
   }
 
-  attn_split_finish<T, D, G>(p, bg, split, sm, acc, m_run, l_run);
+  attn_split_finish<T, D, G, CO>(p, bg, split, sm, acc, m_run, l_run);
 }
 
 // Merge the splits of one KV head (written by an earlier kernel), in split
@@ -620,7 +647,7 @@ struct CombineSmem {
   float den[G];
 };
 
-template <int D, int G>
+template <int D, int G, bool CO = false>
 __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int bg, CombineSmem<D, G>& sm) {
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int Hq = p.Hkv * G;
@@ -637,9 +664,12 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
     const int h = i / D, d = i % D;
 #pragma unroll
     for (int sp = 0; sp < kMaxSplitsDecode; ++sp)
-      v[o][sp] = (i < G * D && sp < ns) ? p.ws_o[(sbase + sp * G + h) * D + d] : 0.f;
+      v[o][sp] = (i < G * D && sp < ns)
+                     ? (CO ? ld_agent(p.ws_o + (sbase + sp * G + h) * D + d) : p.ws_o[(sbase + sp * G + h) * D + d])
+                     : 0.f;
   }
-  for (int i = tid; i < ns * G * 2; i += kThreads) (&sm.ml[0][0][0])[i] = p.ws_ml[sbase * 2 + i];
+  for (int i = tid; i < ns * G * 2; i += kThreads)
+    (&sm.ml[0][0][0])[i] = CO ? ld_agent(p.ws_ml + sbase * 2 + i) : p.ws_ml[sbase * 2 + i];
   __syncthreads();
   if (tid < G) {
     float M = -INFINITY;

@@ -1,4 +1,4 @@
-// One decode layer with one-layer-ahead selection, as three kernels.
+// One decode layer with one-layer-ahead selection, as two kernels.
 //
 // Source: "SparDA: a fourth projection that lets sparse attention prefetch
 // its own KV cache" -- "The fourth projection", Eq. 4 and Alg. 2: right
@@ -8,19 +8,21 @@
 // (deepresearch2agi.pages.dev), 架构细节: the selection of the next layer runs
 // beside the current layer's attention.
 //
-// The three launches keep the real data dependencies of a layer (the output
+// The two launches keep the real data dependencies of a layer (the output
 // of layer l feeds the next layer's input, hence its Forecast):
 //   K1  Forecast projection partials of F_l (128-row splits)
 //   K2  scores of layer l+1's candidates (each workgroup first adds the
-//       projection splits of its (b, g) in order)
-//       + attention splits of layer l over its listed blocks
-//   K3  top-k + union of layer l+1 (one workgroup per (b, g))
-//       + merge of layer l's attention splits
-//       + incremental compressed-key update of layer l (newest block)
+//       projection splits of its (b, g) in order); the last score workgroup
+//       of a (b, g) to finish runs that (b, g)'s top-k + union
+//       + attention splits of layer l over its listed blocks; the last split
+//       of a (b, g) to finish merges the splits and updates layer l's
+//       compressed keys with the newest block
 // K2 streams the compressed keys of l+1 and the selected K/V of l together,
 // so the scoring and the attention share the HBM pipe instead of running
-// back to back.  Roles are assigned by workgroup index; no workgroup waits
-// for another.
+// back to back, and the per-(b, g) follow-up work (top-k, merge) runs while
+// other workgroups still stream instead of in a third launch.  Roles are
+// assigned by workgroup index; no workgroup waits for another: the last one
+// to arrive at a (b, g)'s counter does the follow-up.
 #include "bskv_launch.hpp"
 #include "decode_ops.hpp"
 
@@ -39,7 +41,29 @@ struct LayerParams {
   const float* kc_next; float* scores; int score_splits;
   int32_t* idx_next; int32_t* cnt_next;
   int B, H, topk, n_init, n_local, U;
+  // arrival counters of K2: [0, B*H) score workgroups, [B*H, 2*B*H)
+  // attention splits; zero before a launch (a zero-filled workspace) and
+  // left at zero by each counter's last arrival
+  int32_t* sync;
 };
+
+// Arrival of this workgroup at a counter shared by n workgroups of one
+// launch.  Returns true in the last one to arrive, which resets the counter
+// to zero.  What the others hand over is stored and loaded agent-coherent:
+// each thread waits until its stores have completed (vmcnt 0) before the
+// workgroup counts, and the last one loads only after it has seen the final
+// count, so no cache write-back or invalidation is needed.
+__device__ __forceinline__ bool arrive_last(int32_t* ctr, int n, int& flag) {
+  __builtin_amdgcn_s_waitcnt(0);             // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(ctr, 1);
+    flag = old == n - 1;
+    if (flag) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // every arrival has counted
+  }
+  __syncthreads();
+  return flag;
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
@@ -56,7 +80,15 @@ __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
-  __shared__ __attribute__((aligned(16))) union { AttnSmem<D, G> attn; float fvec[D]; } sm;
+  extern __shared__ uint32_t keys[];   // top-k keys of problems above 8 * kThreads candidates
+  __shared__ __attribute__((aligned(16))) union {
+    AttnSmem<D, G> attn;
+    float fvec[D];
+    TopkShared topk;
+    CombineSmem<D, G> comb;
+    MeanpoolSmem<T, D> mp;
+  } sm;
+  __shared__ int last_flag;
   const int n_bg = p.B * p.H;
   const int n_score = p.select ? p.score_splits * n_bg : 0;
   // attention workgroups (long chains of dependent loads) are dispatched
@@ -73,32 +105,24 @@ __global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
     const int n = dc.c1 - dc.c0;
     const int per = (n + p.score_splits - 1) / p.score_splits;
     const int lo = dc.c0 + split * per, hi = min(dc.c1, lo + per);
-    score_slice_wg<D>(sm.fvec, p.kc_next + (int64_t)bg * p.nb_cap * D, lo, hi, p.scores + (int64_t)bg * p.nb_cap);
+    score_slice_wg<D, true>(sm.fvec, p.kc_next + (int64_t)bg * p.nb_cap * D, lo, hi,
+                            p.scores + (int64_t)bg * p.nb_cap);
+    // the last score workgroup of (b, g): top-k + union of layer l+1
+    if (arrive_last(p.sync + bg, p.score_splits, last_flag))
+      topk_decode_wg<true>(p.scores + (int64_t)bg * p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
+                     p.idx_next + (int64_t)bg * p.U, p.cnt_next + bg, keys, sm.topk);
     return;
   }
   const int a = bid - n_score;
-  attn_split_wg<T, D, G>(p.attn, a / p.attn.n_splits, a % p.attn.n_splits, sm.attn);
-}
-
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void layer_k3(LayerParams p) {
-  extern __shared__ uint32_t keys[];
-  __shared__ union { TopkShared topk; CombineSmem<D, G> comb; MeanpoolSmem<T, D> mp; } sm;
-  const int n_bg = p.B * p.H;
-  const int n_topk = p.select ? n_bg : 0;
-  const int bid = blockIdx.x;
-  if (bid < n_topk) {
-    const DecodeCands dc = decode_cands(p.seq_len[bid / p.H], p.nb_cap, p.n_init, p.n_local);
-    topk_decode_wg(p.scores + (int64_t)bid * p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
-                   p.idx_next + (int64_t)bid * p.U, p.cnt_next + bid, keys, sm.topk);
-    return;
-  }
-  if (bid < n_topk + n_bg) {
-    attn_combine_wg<D, G>(p.attn, bid - n_topk, sm.comb);
-    return;
-  }
-  // incremental compressed-key update: the block the newest token completed
-  const int bg = bid - n_topk - n_bg, b = bg / p.H, g = bg % p.H;
+  const int bg = a / p.attn.n_splits;
+  attn_split_wg<T, D, G, true>(p.attn, bg, a % p.attn.n_splits, sm.attn);
+  // the last attention split of (b, g): merge of the splits, then the
+  // newest-block update of this layer's compressed keys (the block the
+  // newest token completed)
+  if (!arrive_last(p.sync + n_bg + bg, p.attn.n_splits, last_flag)) return;
+  attn_combine_wg<D, G, true>(p.attn, bg, sm.comb);
+  __syncthreads();
+  const int b = bg / p.H, g = bg % p.H;
   const int64_t L = min(p.seq_len[b], p.kv_len);
   if (L <= 0 || (L % kBlk) != 0) return;
   const int64_t j = L / kBlk - 1;
@@ -117,7 +141,7 @@ static size_t al256(size_t x) { return ((x + 255) / 256) * 256; }
 
 size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype) {
   return al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) + al256((size_t)B * Hkv * nb_cap * sizeof(float)) +
-         attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
+         al256((size_t)2 * B * Hkv * sizeof(int32_t)) + attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
 }
 
 template <typename T, int D, int G>
@@ -126,12 +150,10 @@ static void launch_layer_t(const LayerParams& p, int stages, hipStream_t s) {
   const int n_proj = p.select ? p.proj_tiles * p.proj_splits : 0;
   if ((stages & 1) && n_proj > 0) hipLaunchKernelGGL((layer_k1<T>), dim3(n_proj), dim3(kThreads), 0, s, p);
   const int n_score = p.select ? p.score_splits * n_bg : 0;
-  if (stages & 2)
-    hipLaunchKernelGGL((layer_k2<T, D, G>), dim3(n_score + p.attn.n_splits * n_bg), dim3(kThreads), 0, s, p);
   const int64_t cap = p.nb_cap < kMaxCandidates ? p.nb_cap : kMaxCandidates;
-  const size_t lds = p.select ? (size_t)cap * sizeof(uint32_t) : 0;
-  if (stages & 4)
-    hipLaunchKernelGGL((layer_k3<T, D, G>), dim3((p.select ? n_bg : 0) + 2 * n_bg), dim3(kThreads), lds, s, p);
+  const size_t lds = (p.select && cap > 8 * kThreads) ? (size_t)cap * sizeof(uint32_t) : 0;
+  if (stages & 2)
+    hipLaunchKernelGGL((layer_k2<T, D, G>), dim3(n_score + p.attn.n_splits * n_bg), dim3(kThreads), lds, s, p);
 }
 
 template <typename T, int D>
@@ -151,8 +173,10 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   const int H = a.attn.Hkv, D = a.attn.D, B = a.attn.B;
   const size_t proj_b = al256(proj_workspace_bytes(B, a.hidden, H * D, a.attn.dtype));
   const size_t score_b = al256((size_t)B * H * a.nb_cap * sizeof(float));
+  const size_t sync_b = al256((size_t)2 * B * H * sizeof(int32_t));
   char* ws = (char*)a.attn.ws;
-  p.attn = make_attn_params(a.attn, ws + proj_b + score_b);
+  p.sync = (int32_t*)(ws + proj_b + score_b);
+  p.attn = make_attn_params(a.attn, ws + proj_b + score_b + sync_b);
   p.select = a.x != nullptr;
   p.x = a.x; p.w = a.w; p.hidden = a.hidden; p.N = H * D;
   p.proj_part = (float*)ws;

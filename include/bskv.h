@@ -410,23 +410,28 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
  * projection", Alg. 2 and Eq. 4: right after layer l's projection emits the
  * Forecast F_l, it scores layer l+1's compressed keys and picks layer l+1's
  * blocks while layer l attends to the blocks picked one layer earlier.
- * Equivalent to this sequence of the calls above, in three kernels:
+ * Equivalent to this sequence of the calls above, in two kernels:
  *   kv_block_meanpool(k, newest_only=1)  -> kc           (this layer)
  *   forecast_proj(x, w_forecast)         -> F            (this layer's Forecast)
  *   forecast_block_score_topk(F, kc_next) -> idx_next, cnt_next (next layer)
  *   block_sparse_attn_decode(q, k, v, idx, cnt) -> out   (this layer)
  * with the same layouts as those calls (kc and kc_next: [B, Hkv, kc_nb_cap,
- * d]; U = topk + n_init + n_local for idx and idx_next).  The scoring of the
- * next layer and this layer's attention share one launch.
+ * d]; U = topk + n_init + n_local for idx and idx_next; kc and kc_next must
+ * not overlap).  The scoring of the next layer and this layer's attention
+ * share one launch, which also runs each (b, g)'s top-k as soon as its last
+ * score slice is written and each (b, g)'s merge of the attention splits
+ * (then the newest-block update of kc) as soon as its last split is done.
  * x, w_forecast, kc_next, idx_next, cnt_next are all given or all NULL
  * (NULL: the last layer, no selection).  hidden must be a multiple of 256.
- * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL.
- * stages: bit 0 = K1 (projection partials), bit 1 = K2 (next-layer scores +
- * this layer's attention splits), bit 2 = K3 (next-layer top-k + attention
- * merge + newest-block update of kc); 7 runs the whole layer.  A later
- * stage reads what the earlier ones left in ws, so a caller may launch them
+ * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL,
+ * zero-filled once before its first use: it holds K2's arrival counters,
+ * which every complete call leaves at zero again (calls that share one ws
+ * must not overlap in time).
+ * stages: bit 0 = K1 (projection partials), bit 1 = K2 (next-layer scores
+ * and top-k, this layer's attention, merge and kc update); 3 runs the whole
+ * layer.  K2 reads what K1 left in ws, so a caller may launch them
  * separately (to place other work between them, or to time each), in order,
- * with the same ws and arguments.
+ * with the same ws and arguments.  Stages outside 1..3: BSKV_EINVAL.
  * ----------------------------------------------------------------------- */
 size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,
                                              int64_t kc_nb_cap, int U, int dtype);

@@ -297,13 +297,13 @@ def test_decode_layer_validation():
     ws = lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 4096, 2048, 69, 1)
     assert ws > lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 0, 2048, 69, 1)
 
-    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=7, dt=1, hq=32, nl=4, wsb=ws):
+    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=3, dt=1, hq=32, nl=4, wsb=ws):
         return f(P, P, P, dt, S3, 131072, P, P, P, P, 0.088, P, x, w, hidden, kcn, idn, cnn, 8, hq, 8, 128, 64, 2048,
                  64, 1, nl, stages, P, wsb, None)
     assert call(x=None) == EINVAL            # lookahead arguments: all or none
     assert call(idn=None) == EINVAL
     assert call(stages=0) == EINVAL
-    assert call(stages=8) == EINVAL
+    assert call(stages=4) == EINVAL
     assert call(dt=3) == EDTYPE
     assert call(hq=24) == EUNSUP
     assert call(hidden=1000) == EUNSUP

@@ -859,6 +859,50 @@ def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     assert max_abs(np64(out_b), want) < (1e-4 if dtype == "f32" else 2e-2)
 
 
+def test_decode_layer_graph_replays():
+    """The one-launch follow-up work (top-k of the last score slice, merge of
+    the last attention split) hands results over through arrival counters in
+    the workspace, which every launch leaves at zero: replays of a captured
+    layer, with eager calls between them, match the eager result exactly."""
+    lens = [64 * 20, 64 * 20 - 3]
+    c, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 21)
+    kc_e = kc.clone()
+    out_e, i_e, n_e = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_e, idx, cnt,
+                                                  x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
+                                                  n_local=2)
+    torch.cuda.synchronize()
+    kc_g = kc.clone()
+    out_g, i_g, n_g = torch.empty_like(out_e), torch.empty_like(i_e), torch.empty_like(n_e)
+    ws = torch.zeros(bskv.workspace_bytes("layer", 2, 16, 4, 128, 512, kc.shape[2], 9, 1), dtype=torch.uint8,
+                     device=DEV)
+
+    def call():
+        bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_g, idx, cnt, out=out_g, x=c["x_sel"],
+                                    w=c["w_sel"], kc_next=kc_next, idx_next=i_g, cnt_next=n_g, topk=6, n_init=1,
+                                    n_local=2, ws=ws)
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        call()
+    torch.cuda.current_stream().wait_stream(s_)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        out_g.zero_()
+        i_g.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(i_g, i_e) and torch.equal(n_g, n_e), rep
+        # rows of blocks that are not complete yet hold NaN in both
+        assert torch.equal(torch.nan_to_num(kc_g, nan=7.0), torch.nan_to_num(kc_e, nan=7.0)), rep
+        # eager work between the replays, on the same workspace
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(i_g, i_e), rep
+
+
 def test_decode_layer_stages_and_last_layer():
     lens = [64 * 20] * 2
     c, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
@@ -867,7 +911,7 @@ def test_decode_layer_stages_and_last_layer():
                                                w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
     i2, n2 = torch.empty_like(idx), torch.empty_like(cnt)
     out2 = torch.empty_like(out1)
-    for st in (1, 2, 4):
+    for st in (1, 2):
         bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc2, idx, cnt, out=out2, x=c["x_sel"],
                                     w=c["w_sel"], kc_next=kc_next, idx_next=i2, cnt_next=n2, topk=6, n_init=1,
                                     n_local=2, stages=st)
