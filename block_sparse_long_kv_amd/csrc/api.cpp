@@ -35,7 +35,14 @@ bool strides_ok(const int64_t* s, int dtype) {
   const int64_t m = 16 / esize_of(dtype);
   for (int i = 0; i < 3; ++i)
     if (s[i] < 0 || s[i] % m) return false;
+  // 64 rows of one block span less than 2 GiB (32-bit per-lane load offsets)
+  if (s[2] * 64 * esize_of(dtype) >= (int64_t(1) << 31)) return false;
   return true;
+}
+
+// the decode attention reads K/V of one (b, g) through 32-bit byte offsets
+bool span_ok(int64_t kv_len, const int64_t* s, int dtype) {
+  return kv_len * s[2] * esize_of(dtype) < (int64_t(1) << 31);
 }
 
 bool group_ok(int hq, int hkv) {
@@ -230,6 +237,7 @@ int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, i
   if (!q || !k || !v || !idx || !cnt || !seq_len || !out || !ws) return BSKV_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return BSKV_EINVAL;
   if (B <= 0 || U <= 0 || kv_len < 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (!span_ok(kv_len, kv_strides, dtype)) return BSKV_EUNSUPPORTED;
   if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
   if ((int64_t)B * n_kv_heads > 65535) return BSKV_EUNSUPPORTED;
@@ -422,6 +430,7 @@ int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int
     return BSKV_EINVAL;   // the lookahead arguments come all together or not at all
   if (sel && (!aligned16(x) || !aligned16(w_forecast) || !aligned16(kc_next))) return BSKV_EINVAL;
   if (B <= 0 || kv_len < 0 || kc_nb_cap <= 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (!span_ok(kv_len, kv_strides, dtype)) return BSKV_EUNSUPPORTED;
   if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
   if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
   if (!group_ok(n_q_heads, n_kv_heads) || !head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;

@@ -422,6 +422,51 @@ __device__ __forceinline__ void attn_load(AttnRegs<T, D, G>& r, const T* kb, con
   for (int i = 0; i < R::TPL; ++i) r.v[i] = ld16_nt(vb + (int64_t)(tl + i * R::TL) * st + dc * R::VEC);
 }
 
+// bf16 block loads through buffer resources: the resource holds the
+// (b, g) base and the byte count of its K (or V) rows, each lane a fixed
+// 32-bit offset, each block a wave-uniform offset.  No per-block address
+// arithmetic lands in vector registers, so no such register can be one a
+// load in flight still owes (which would make the compiler wait for every
+// load), and accesses past the rows read zero.
+struct BufBlock {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t ko, vo;     // per-lane byte offsets of the K fragment and V rows
+  uint32_t vstep;      // bytes between the V rows one lane loads
+};
+
+template <int D>
+__device__ __forceinline__ BufBlock make_buf_block(const bf16_bits* kb, const bf16_bits* vb, int64_t st,
+                                                   int64_t kv_len) {
+  constexpr int VEC = 8, DCH = D / VEC, TL = kThreads / DCH;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t span = kv_len > 0 ? ((kv_len - 1) * st + D) * 2 : 0;
+  const int nrec = (int)(span < 0x7fffffff ? span : 0x7fffffff);
+  BufBlock bb;
+  bb.rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec, 0x00020000);
+  bb.rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nrec, 0x00020000);
+  bb.ko = (uint32_t)(((16 * w + (lane & 15)) * (uint32_t)st + 8 * (lane >> 4)) * 2);
+  const int dc = threadIdx.x % DCH, tl = threadIdx.x / DCH;
+  bb.vo = (uint32_t)((tl * (uint32_t)st + dc * VEC) * 2);
+  bb.vstep = (uint32_t)(TL * st * 2);
+  return bb;
+}
+
+template <int D, int G>
+__device__ __forceinline__ void attn_load_buf(AttnRegs<bf16_bits, D, G>& r, const BufBlock& bb, uint32_t boff) {
+  using R = AttnRegs<bf16_bits, D, G>;
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < R::NKL; ++i) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(bb.rk, bb.ko + 64 * i, (int)boff, 2);
+    r.k[i] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+#pragma unroll
+  for (int i = 0; i < R::TPL; ++i) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(bb.rv, bb.vo, (int)(boff + i * bb.vstep), 2);
+    r.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
 // q fragments of the MFMA path: lane l holds q[head l%16][32ks + 8(l/16) ..+7]
 // (zero for the padding heads G..15), already in bf16.
 template <int D>
@@ -604,35 +649,42 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
   const T* vbase = (const T*)p.v + b * p.sb + g * p.sg;
   const int32_t* list = p.idx + (int64_t)bg * p.U;
 
-  // block u -> (token base in the buffer, valid token count); invalid ids read nothing
+  // block u -> (block slot in the buffer, valid token count); invalid ids
+  // read nothing.  The tests run in 32-bit scalar arithmetic on per-split
+  // constants: 64-bit compares would go through vector registers, and the
+  // compiler may pick one that a load in flight still owes, waiting for all.
+  const int nblk_buf = (int)min(p.kv_len / kBlk, (int64_t)0x7fffffff);       // whole blocks in the buffer
+  const int Lc = (int)min(L, (int64_t)0x7fffffff - kBlk);
+  const int jend = (Lc + kBlk - 1) / kBlk;                                    // blocks holding tokens
   auto locate = [&](int u, int64_t& tb, int& nvalid) {
     const int j = list[u];
     const int loc = p.slot ? p.slot[(int64_t)bg * p.U + u] : (p.ring ? u : j);
     tb = (int64_t)loc * kBlk;
-    if (j < 0 || loc < 0 || tb + kBlk > p.kv_len) { nvalid = -1; return; }
-    const int64_t rem = L - (int64_t)j * kBlk;
-    nvalid = rem <= 0 ? 0 : (rem >= kBlk ? kBlk : (int)rem);
+    if (j < 0 || loc < 0 || loc >= nblk_buf) { nvalid = -1; return; }
+    nvalid = j >= jend ? 0 : min(kBlk, Lc - j * kBlk);
   };
-  AttnRegs<T, D, G> ra, rb;
-  int64_t tba = 0, tbb = 0;
-  int nva = -1, nvb = -1;
+  // One register set: each block is requested, then computed.  With ~100
+  // VGPRs four workgroups share a SIMD and cover each other's load latency;
+  // two register sets (the next block requested before the current one is
+  // computed) need ~190 VGPRs, two workgroups per SIMD, and measured slower
+  // (B8 x 128K: 44.7 vs 40.7 us for the fused layer's kernel).  A block outside
+  // the buffer is masked whole (nothing is read); K/V shorter than one block
+  // hold no valid block.
+  AttnRegs<T, D, G> ra;
+  int64_t tba = 0;
+  int nva = -1;
+  BufBlock bb;
+  if constexpr (R::kMfma) bb = make_buf_block<D>((const bf16_bits*)kbase, (const bf16_bits*)vbase, p.st, p.kv_len);
   __syncthreads();
-  if (u0 < u1) {
-    locate(u0, tba, nva);
-    if (nva >= 0) attn_load<T, D, G>(ra, kbase + tba * p.st, vbase + tba * p.st, p.st);
-  }
-  for (int u = u0; u < u1; u += 2) {
-    if (u + 1 < u1) {
-      locate(u + 1, tbb, nvb);
-      if (nvb >= 0) attn_load<T, D, G>(rb, kbase + tbb * p.st, vbase + tbb * p.st, p.st);
+  for (int u = u0; u < u1; ++u) {
+    locate(u, tba, nva);
+    if (nva >= 0) {
+      if constexpr (R::kMfma)
+        attn_load_buf<D, G>(ra, bb, __builtin_amdgcn_readfirstlane((uint32_t)(tba * p.st * 2)));
+      else
+        attn_load<T, D, G>(ra, kbase + tba * p.st, vbase + tba * p.st, p.st);
     }
     attn_block<T, D, G>(ra, nva < 0 ? 0 : nva, sm, qf, sscale, acc, m_run, l_run);
-    if (u + 1 >= u1) break;
-    if (u + 2 < u1) {
-      locate(u + 2, tba, nva);
-      if (nva >= 0) attn_load<T, D, G>(ra, kbase + tba * p.st, vbase + tba * p.st, p.st);
-    }
-    attn_block<T, D, G>(rb, nvb < 0 ? 0 : nvb, sm, qf, sscale, acc, m_run, l_run);
   }
 
   attn_split_finish<T, D, G, CO>(p, bg, split, sm, acc, m_run, l_run);
@@ -700,10 +752,10 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
 
 // Split plan of the decode attention: about `target` workgroups, at most
 // kMaxSplitsDecode splits, every split the same number of listed blocks.
-// 768 is the best of 512..2048 measured at B8 x 128K (U = 69 blocks: 12
-// splits of 6 blocks); more, shorter splits add merge work and arrivals.
+// 1024 is the best of 512..2048 measured at B8 x 128K (U = 69 blocks: 14
+// splits of 5 blocks); more, shorter splits add merge work and arrivals.
 __host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
-  const int target = 768;
+  const int target = 1024;
   int ns = (target + n_bg - 1) / n_bg;
   if (ns > U) ns = U;
   if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;

@@ -24,7 +24,10 @@
  * - Layouts: K/V caches are addressed as [B, Hkv, T, d] with element strides
  *   kv_strides = {batch, kv head, token}; head_dim elements are contiguous.
  *   Base pointers must be 16-byte aligned and strides multiples of
- *   16 bytes / element size.  A 64-token block j of (b, g) is the contiguous
+ *   16 bytes / element size; 64 token strides must span less than 2 GiB
+ *   (else BSKV_EINVAL), and for the decode attention calls kv_len token
+ *   strides of one (b, g) too (else BSKV_EUNSUPPORTED: its loads use 32-bit
+ *   byte offsets).  A 64-token block j of (b, g) is the contiguous
  *   run of tokens 64j..64j+63, so the default contiguous layout is also
  *   [B, Hkv, T/64, 64, d].
  * - dtype: BSKV_F32 or BSKV_BF16 (raw bfloat16 bits, round-to-nearest-even).
