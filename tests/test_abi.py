@@ -263,6 +263,12 @@ def test_attn_decode_validation():
     assert call(scale=float("nan")) == EINVAL
     assert call(wsb=ws - 1) == ENOSPC
     assert call(kv_len=-64) == EINVAL
+    # one (b, g)'s K/V must span less than 2 GiB (32-bit load offsets) ...
+    big = (ctypes.c_int64 * 3)(1 << 40, 1 << 30, 1 << 14)
+    assert call(strides=big, kv_len=1 << 16) == EUNSUP
+    # ... and 64 token strides of any call less than 2 GiB
+    huge = (ctypes.c_int64 * 3)(1 << 40, 1 << 30, 1 << 24)
+    assert call(strides=huge, kv_len=64) == EINVAL
 
 
 def test_attn_prefill_validation():
