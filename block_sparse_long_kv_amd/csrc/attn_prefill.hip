@@ -50,30 +50,6 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
 
-// Copy of 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane i of the wave writes bytes [16 i, 16 i + 16)
-// after the wave-uniform LDS address `lds`.  The copy is counted by the
-// wave's vmcnt like any load and has no register result; the caller waits
-// for it (s_waitcnt vmcnt) and then synchronises the workgroup before any
-// wave reads the bytes.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// s_waitcnt with vmcnt = n (n < 64) and the other counters left open
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int D, int HPW>
 __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
     const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,

@@ -1,7 +1,7 @@
 // Device helpers shared by the gfx950 kernels of libbskv: 16-byte vector
-// loads with bf16/fp32 conversion, wavefront (64-lane) reductions, a
-// 256-thread block scan, and the order-preserving float -> uint32 key used by
-// the top-k selection.
+// loads with bf16/fp32 conversion, global-to-LDS copies, wavefront (64-lane)
+// reductions, a 256-thread block scan, and the order-preserving float ->
+// uint32 key used by the top-k selection.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -347,6 +347,30 @@ __device__ __forceinline__ void topk_union(const uint32_t* keys, int n, int c0, 
                                            int n_local, int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
   if (n <= 8 * kThreads) topk_union_regs<8>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
   else topk_union_regs<48>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
+}
+
+// Copy of 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i of the wave writes bytes [16 i, 16 i + 16)
+// after the wave-uniform LDS address `lds`.  The copy is counted by the
+// wave's vmcnt like any load and has no register result; the caller waits
+// for it (s_waitcnt vmcnt) and then synchronises the workgroup before any
+// wave reads the bytes.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt with vmcnt = n (n < 64) and the other counters left open
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 }  // namespace bskv

@@ -130,14 +130,6 @@ hipError_t launch_qkvf_decode(const QkvfDecodeArgs& a) {
 // stores its weight) and X [tokens, hidden]: both operands are hidden-major,
 // so every MFMA operand fragment is one 16-byte LDS read.
 constexpr int kGemmBK = 64;               // hidden columns per stage
-constexpr int kGemmStr = kGemmBK + 8;     // LDS row: 144 bytes (16 rows x 16 bytes hit all 64 banks once)
-
-template <int BM, int BN>
-struct QkvfGemmSmem {
-  bf16_bits x[2][BM * kGemmStr];
-  bf16_bits w[2][BN * kGemmStr];
-};
-
 struct QkvfPrefillParams {
   const bf16_bits* x; const bf16_bits* w;
   int B, Tq, hidden, Hq, H, D, n_qb;
@@ -148,109 +140,12 @@ struct QkvfPrefillParams {
   float* f_pooled;
 };
 
-// C^T = W^T X^T per BN x BM tile (columns x tokens of one sequence); four
-// waves, each WN columns x WM tokens (WM a multiple of 64: whole query blocks).
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads, 1) void qkvf_prefill_kernel(QkvfPrefillParams p) {
-  static_assert((BM / WM) * (BN / WN) == 4 && WM % 64 == 0 && WN % 16 == 0, "four waves of whole query blocks");
-  constexpr int MI = WM / 16, NI = WN / 16;
-  constexpr int CX = BM * kGemmBK / 8 / kThreads;   // 16-byte chunks of the X tile per thread
-  constexpr int CW = BN * kGemmBK / 8 / kThreads;   // of the W^T tile
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  QkvfGemmSmem<BM, BN>& sm = *reinterpret_cast<QkvfGemmSmem<BM, BN>*>(smem_raw);
-  const int N = (p.Hq + 3 * p.H) * p.D;
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-  // L2).  With the swizzle, XCD x takes a contiguous run of the tile space
-  // in 8 x 8 groups of (token tile, column tile): the workgroups one XCD runs
-  // at a time share a few token tiles and column tiles, so each K-step's
-  // operands are fetched into that L2 once and read by several workgroups.
-  int tn, tm;
-  {
-    const int bid = blockIdx.x, n_m = p.n_tiles_t * p.B;
-    if (p.swizzle) {
-      const int per_xcd = (int)gridDim.x / 8;
-      const int L = (bid % 8) * per_xcd + bid / 8;
-      const int within = L % 64, group = L / 64;
-      const int groups_m = n_m / 8;
-      tm = (group % groups_m) * 8 + within % 8;
-      tn = (group / groups_m) * 8 + within / 8;
-    } else {
-      tm = bid % n_m;
-      tn = bid / n_m;
-    }
-  }
-  const int b = tm / p.n_tiles_t;
-  const int n0 = tn * BN, t0 = (tm % p.n_tiles_t) * BM;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int wn = wid % (BN / WN), wm = wid / (BN / WN);
-  const bf16_bits* xb = p.x + (int64_t)b * p.Tq * p.hidden;
-
-  uint4 rx[CX], rw[CW];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
-      const int t = t0 + r;
-      rx[i] = t < p.Tq ? ld16(xb + (int64_t)t * p.hidden + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
-      rw[i] = ld16(p.w + (int64_t)(n0 + r) * p.hidden + k0 + cc * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sm.x[buf][r * kGemmStr + cc * 8]) = rx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int c = tid + i * kThreads, r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sm.w[buf][r * kGemmStr + cc * 8]) = rw[i];
-    }
-  };
-
-  f32x4_t acc[NI][MI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < MI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int n_steps = p.hidden / kGemmBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < n_steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < n_steps) gload((s + 1) * kGemmBK);
-#pragma unroll
-    for (int ks = 0; ks < kGemmBK / 32; ++ks) {
-      // A = W^T rows (lane: column l16, hidden 8lg..8lg+7); B = X^T (lane:
-      // token l16, the same hidden columns)
-      bf16x8_t a[NI], bx[MI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        a[ni] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                 &sm.w[buf][(WN * wn + 16 * ni + l16) * kGemmStr + 32 * ks + 8 * lg]));
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        bx[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                  &sm.x[buf][(WM * wm + 16 * mi + l16) * kGemmStr + 32 * ks + 8 * lg]));
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ni], bx[mi], acc[ni][mi], 0, 0, 0);
-    }
-    if (s + 1 < n_steps) {
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
+// Epilogue of one wave's WN x WM accumulator tile: Q rows to q, K and V
+// rows into the caches at their positions, and the Forecast columns summed
+// over each 64-token query block into f_pooled.
+template <int MI, int NI, int WM, int WN>
+__device__ __forceinline__ void qkvf_epilogue(const QkvfPrefillParams& p, const f32x4_t (&acc)[NI][MI], int b, int n0,
+                                              int t0, int wm, int wn, int l16, int lg) {
   // lane (l16, lg) of tile (ni, mi) holds C[token WM wm + 16mi + l16][column WN wn + 16ni + 4lg + i], i < 4
   const int seg_q = p.Hq * p.D, seg_k = seg_q + p.H * p.D, seg_v = seg_k + p.H * p.D;
   if (n0 < seg_v) {
@@ -301,14 +196,127 @@ __global__ __launch_bounds__(kThreads, 1) void qkvf_prefill_kernel(QkvfPrefillPa
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_qkvf_prefill_t(QkvfPrefillParams p, int N, hipStream_t stream) {
+// C^T = W^T X^T per BN x BM tile (columns x tokens of one sequence), NW
+// waves of WN columns x WM tokens (WM a multiple of 64: whole query blocks).
+// The operand tiles are copied straight from HBM into an NSTG-stage LDS ring
+// (global_load_lds_dwordx4, 1024 contiguous LDS bytes per wave
+// instruction): no registers hold tiles in transit, no LDS writes are
+// issued, and a stage's copy is issued NSTG-1 K-steps before its use.
+// LDS rows are the K-step's 64 hidden columns (128 bytes) with 16-byte
+// chunks XOR-swizzled per row (chunk c of row r at c ^ ((r / 2) % 8)), so the
+// 16 rows of a fragment read cover all banks.  Token rows past the chunk are
+// copied from its last row and then zeroed in LDS, so they add nothing to
+// the pooled Forecast.
+template <int BM, int BN, int WM, int WN, int NSTG>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void qkvf_prefill_ring_kernel(QkvfPrefillParams p) {
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int RB = kGemmBK * 2;                 // bytes per LDS row
+  constexpr int XT = BM * RB, WT = BN * RB;       // bytes of one stage's X and W^T tiles
+  constexpr int PX = XT / 1024, PW = WT / 1024;   // 1024-byte copy pieces
+  constexpr int PPW = (PX + PW) / NW;             // pieces per wave per stage
+  static_assert(WM % 64 == 0 && WN % 16 == 0 && (PX + PW) % NW == 0 && NSTG >= 2, "tiling");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  int tn, tm;
+  {
+    const int bid = blockIdx.x, n_m = p.n_tiles_t * p.B;
+    if (p.swizzle) {
+      const int per_xcd = (int)gridDim.x / 8;
+      const int L = (bid % 8) * per_xcd + bid / 8;
+      const int within = L % 64, group = L / 64;
+      const int groups_m = n_m / 8;
+      tm = (group % groups_m) * 8 + within % 8;
+      tn = (group / groups_m) * 8 + within / 8;
+    } else {
+      tm = bid % n_m;
+      tn = bid / n_m;
+    }
+  }
+  const int b = tm / p.n_tiles_t;
+  const int n0 = tn * BN, t0 = (tm % p.n_tiles_t) * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wn = wid % (BN / WN), wm = wid / (BN / WN);
+  const bf16_bits* xb = p.x + (int64_t)b * p.Tq * p.hidden;
+  const bool tail = t0 + BM > p.Tq;
+  const uint32_t lds0 = lds_u32(smem_raw);
+
+  // this lane's chunk of each of the wave's pieces: row r, stored chunk q & 7
+  auto issue = [&](int s) {
+    const int k0 = s * kGemmBK;
+    const uint32_t base = lds0 + (uint32_t)((s % NSTG) * (XT + WT));
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int piece = wid * PPW + i;
+      const bool is_x = piece < PX;
+      const int pc = is_x ? piece : piece - PX;
+      const int q = pc * 64 + lane, r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+      const bf16_bits* src = is_x ? xb + (int64_t)min(t0 + r, p.Tq - 1) * p.hidden + k0 + 8 * c
+                                  : p.w + (int64_t)(n0 + r) * p.hidden + k0 + 8 * c;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(base + (uint32_t)((is_x ? 0 : XT) + pc * 1024)));
+    }
+  };
+  // token rows past the chunk: this lane's X chunks of stage s read zero
+  auto zero_tail = [&](int s) {
+    unsigned char* base = smem_raw + (s % NSTG) * (XT + WT);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int piece = wid * PPW + i;
+      if (piece < PX && t0 + ((piece * 64 + lane) >> 3) >= p.Tq)
+        *reinterpret_cast<uint4*>(base + piece * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment offsets: row 16 x + l16 of a tile, chunk 4 ks + lg, swizzle (l16 / 2)
+  const int swz = l16 >> 1;
+  const int off0 = l16 * RB + 16 * ((0 + lg) ^ swz), off1 = l16 * RB + 16 * ((4 + lg) ^ swz);
+
+  const int n_steps = p.hidden / kGemmBK;
+#pragma unroll
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < n_steps) issue(s);
+  for (int s = 0; s < n_steps; ++s) {
+    if (s + NSTG - 2 < n_steps) wait_vm<(NSTG - 2) * PPW>();
+    else wait_vm<0>();
+    if (tail) zero_tail(s);
+    __syncthreads();                  // stage s complete; stage s-1 read by every wave
+    if (s + NSTG - 1 < n_steps) issue(s + NSTG - 1);
+    const unsigned char* xs = smem_raw + (s % NSTG) * (XT + WT);
+    const unsigned char* ws = xs + XT;
+#pragma unroll
+    for (int ks = 0; ks < kGemmBK / 32; ++ks) {
+      const int off = ks == 0 ? off0 : off1;
+      bf16x8_t a[NI], bx[MI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        a[ni] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + (WN * wn + 16 * ni) * RB + off));
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        bx[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + (WM * wm + 16 * mi) * RB + off));
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ni], bx[mi], acc[ni][mi], 0, 0, 0);
+    }
+  }
+  qkvf_epilogue<MI, NI, WM, WN>(p, acc, b, n0, t0, wm, wn, l16, lg);
+}
+
+template <int BM, int BN, int WM, int WN, int NSTG>
+static hipError_t launch_qkvf_prefill_ring_t(QkvfPrefillParams p, int N, hipStream_t stream) {
   p.n_tiles_n = N / BN;
   p.n_tiles_t = (p.Tq + BM - 1) / BM;
   const int n_m = p.n_tiles_t * p.B, total = n_m * p.n_tiles_n;
-  p.swizzle = (n_m % 8 == 0 && p.n_tiles_n % 8 == 0) ? 1 : 0;   // then total is a multiple of 64
-  const size_t lds = sizeof(QkvfGemmSmem<BM, BN>);
-  hipLaunchKernelGGL((qkvf_prefill_kernel<BM, BN, WM, WN>), dim3(total), dim3(kThreads), lds, stream, p);
+  p.swizzle = (n_m % 8 == 0 && p.n_tiles_n % 8 == 0) ? 1 : 0;
+  const size_t lds = (size_t)NSTG * (BM + BN) * kGemmBK * 2;
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  hipLaunchKernelGGL((qkvf_prefill_ring_kernel<BM, BN, WM, WN, NSTG>), dim3(total), dim3(NT), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -322,11 +330,14 @@ hipError_t launch_qkvf_prefill(const QkvfPrefillArgs& a) {
   p.sb = a.sb; p.sg = a.sg; p.st = a.st; p.kv_len = a.kv_len;
   p.f_pooled = a.f_pooled;
   const int N = (a.Hq + 3 * a.H) * a.D;
-  // 128 x 128 tiles, two workgroups per CU: measured faster than 256 x 128
-  // and 256 x 256 tiles at one workgroup per CU (770 and 605 us against
-  // 563 us per 8192 x 4096 x 7168 chunk), whose single register-staged
-  // prefetch stage leaves the loads' latency exposed
-  return launch_qkvf_prefill_t<128, 128, 64, 64>(p, N, a.stream);
+  // Two-stage LDS ring.  Per 8192 x 4096 x 7168 chunk: 256 x 256 tiles (eight
+  // waves, one workgroup per CU) 411 us = 1.17 PFLOP/s; 128 x 128 tiles (two
+  // workgroups per CU) 424 us, and the same tiles staged through registers
+  // 549 us; 256 x 128 with three stages 451 us; 128 x 128 with four stages
+  // 592 us.  A 256-column tile must not straddle the Forecast columns.
+  const int seg_v = (a.Hq + 2 * a.H) * a.D;
+  if (N % 256 == 0 && seg_v % 256 == 0) return launch_qkvf_prefill_ring_t<256, 256, 128, 64, 2>(p, N, a.stream);
+  return launch_qkvf_prefill_ring_t<128, 128, 64, 64, 2>(p, N, a.stream);
 }
 
 }  // namespace bskv
