@@ -59,7 +59,7 @@ METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
 PMC_TRAFFIC = {
     "layer_k2": {"fetch_kib": 106903.8, "write_kib": 3060.7, "fetch_scale": 2.0, "write_scale": 1.0,
                  "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                 "sha256": "b3429f5d4d8f44e3952b591a92ee95e1b84c6cbaa9be551410f1c719bd77081c"},
+                 "sha256": "224be205cf10aaf40ad486e8ed4b3064440d91728f8eb5ff253ecf0244307946"},
     "attn_prefill": {"fetch_kib": 366773.6, "write_kib": 65536.8, "fetch_scale": 2.0, "write_scale": 1.0,
                      "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
                      "sha256": "020ed1804106f3d38f17f8f90df91fe42bd829bf4070ca593a700da6d8b81dbf"},

@@ -359,9 +359,9 @@ __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, Dec
 
 // ---------------------------------------------------------------------------
 // Decode attention: one split (a run of listed blocks) of one KV head for
-// its G query heads.  K/V of the next block are loaded while the current
-// one is computed (two register sets).  Writes the split's unnormalised
-// output o[G][D] and its running max m / sum l (base-2 logits).
+// its G query heads, one block at a time (one register set; other
+// workgroups on the SIMD cover the load latency).  Writes the split's
+// unnormalised output o[G][D] and its running max m / sum l (base-2 logits).
 // ---------------------------------------------------------------------------
 struct AttnDecodeParams {
   const void* q; const void* k; const void* v;
