@@ -752,10 +752,13 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
 
 // Split plan of the decode attention: about `target` workgroups, at most
 // kMaxSplitsDecode splits, every split the same number of listed blocks.
-// 1024 is the best of 512..2048 measured at B8 x 128K (U = 69 blocks: 14
-// splits of 5 blocks); more, shorter splits add merge work and arrivals.
+// Measured at B8 x 128K (U = 69 blocks) over targets 512..2048: 768 (12
+// splits of 6 blocks) runs the attention alone 5% faster than 1024 (14 of
+// 5) and is level with it inside the fused layer kernel; 640 (10 of 7) and
+// fewer splits are slower, and more, shorter splits add merge work and
+// arrivals.
 __host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
-  const int target = 1024;
+  const int target = 768;
   int ns = (target + n_bg - 1) / n_bg;
   if (ns > U) ns = U;
   if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;
