@@ -135,22 +135,10 @@ __device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int r_begin = split * kProjRows, n0 = tile * TC;
-  uint4 raw[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
-    raw[i] = ld16_nt(w + (int64_t)(r_begin + r) * N + n0 + cc * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
-    *reinterpret_cast<uint4*>(&sm.w[r * kProjWStr + cc * 8]) = raw[i];
-  }
-  __syncthreads();
-  const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
-  for (int b0 = 0; b0 < B; b0 += 16) {
+  // x^T fragments (B operand) of batch rows b0 + l16, in the row order of
+  // the transposed W reads
+  auto load_x = [&](int b0, bf16x8_t (&xb)[kProjRows / 32]) {
     const int b = b0 + l16;
-    bf16x8_t xb[kProjRows / 32];
 #pragma unroll
     for (int ks = 0; ks < kProjRows / 32; ++ks) {
       uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
@@ -161,6 +149,26 @@ __device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict
       }
       xb[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
+  };
+  uint4 raw[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
+    raw[i] = ld16_nt(w + (int64_t)(r_begin + r) * N + n0 + cc * 8);
+  }
+  // the first 16 batch rows travel beside the W tile, not after it
+  bf16x8_t xb[kProjRows / 32];
+  load_x(0, xb);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads, r = ch >> 4, cc = ch & 15;
+    *reinterpret_cast<uint4*>(&sm.w[r * kProjWStr + cc * 8]) = raw[i];
+  }
+  __syncthreads();
+  const int tr_row = 4 * lg + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  for (int b0 = 0; b0 < B; b0 += 16) {
+    const int b = b0 + l16;
+    if (b0 > 0) load_x(b0, xb);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int nt = 2 * wid + t;
