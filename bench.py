@@ -553,11 +553,35 @@ def cpu_baseline_decode(bench, budget_s=12.0, layers=None):
             "sample_seconds": round(per_sample, 4), "value_1_thread": one, "cpu_model": cpu_model()}
 
 
+def check_step_outputs(torch, bench):
+    """The timed step's outputs (as its last replay left them) against the
+    per-op path run afterwards on the same inputs: every layer's block lists
+    and counts must be identical and its attention output bit-identical (the
+    fused kernels run the same arithmetic in the same order).  Raises on any
+    difference, so no throughput is reported for a step that computes
+    something else."""
+    snap = [(i.clone(), c.clone(), o.clone()) for i, c, o in zip(bench.idx, bench.cnt, bench.out)]
+    for o in bench.out:
+        o.fill_(float("nan"))
+    bench.step_per_op()
+    torch.cuda.synchronize()
+    bad = [l for l, (i, c, o) in enumerate(snap)
+           if not (torch.equal(i, bench.idx[l]) and torch.equal(c, bench.cnt[l]) and torch.equal(o, bench.out[l]))]
+    if bad:
+        raise RuntimeError(f"timed decode step differs from the per-op path in layers {bad}")
+    finite = all(bool(torch.isfinite(o).all()) for _, _, o in snap)
+    if not finite:
+        raise RuntimeError("timed decode step left non-finite outputs")
+    return {"layers_checked": len(snap), "lists_equal": True, "outputs_bit_equal": True}
+
+
 def run_decode(args, torch, bskv, wl, replicas=None):
     bench = DecodeBench(wl, torch, bskv, layers=replicas)
     step_fn = bench.step_per_op if args.per_op else bench.step
     step_s, _ = time_graph(torch, step_fn, args.steps, args.warmup, use_graph=not args.no_graph)
     log(f"[bench] decode step {step_s * 1e3:.3f} ms ({'graph' if not args.no_graph else 'eager'})")
+    post_check = check_step_outputs(torch, bench)
+    log(f"[bench] timed step outputs match the per-op path: {post_check}")
     kt = kernel_times(torch, bench)
     bpl = bench.bytes_per_launch()
     kernels = {}
@@ -601,6 +625,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
         "window_selector": win_sel,
         "widened_projection": widened,
         "kernels": kernels,
+        "post_timing_check": post_check,
     }
     if replicas is not None:
         result["config"]["layers"] = 1

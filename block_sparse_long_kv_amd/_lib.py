@@ -97,6 +97,12 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _whole_blocks(k: torch.Tensor, where: str):
+    if k.shape[2] % 64:
+        raise ValueError(f"{where}: the K/V buffers must hold whole 64-token blocks (token axis {k.shape[2]}); "
+                         "allocate the cache in whole blocks, tokens past seq_len are masked")
+
+
 def _strides3(t: torch.Tensor):
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("K/V must be 4-D [B, Hkv, T, d] with a contiguous last dimension")
@@ -285,6 +291,7 @@ def block_sparse_attn_decode(q, k, v, idx, cnt, seq_len, scale: float | None = N
     lay = (B, Hq, Hkv, d, U)
     nbytes = workspace_bytes("attn", *lay)
     ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "attn", lay)
+    _whole_blocks(k, "block_sparse_attn_decode")
     _check(lib.bskv_block_sparse_attn_decode(_ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2], int(bool(ring)),
                                              _ptr(idx), _ptr(cnt), _ptr(seq_len), B, Hq, Hkv, d, 64, U, scale, _ptr(out),
                                              _ptr(ws), ws.numel() * ws.element_size(), sh), "block_sparse_attn_decode")
@@ -301,6 +308,7 @@ def block_sparse_attn_prefill(q, k, v, idx, cnt, q_start: int, scale: float | No
     scale = (1.0 / math.sqrt(d)) if scale is None else scale
     out = out if out is not None else torch.empty_like(q)
     sh = _stream(stream, q.device)
+    _whole_blocks(k, "block_sparse_attn_prefill")
     _check(lib.bskv_block_sparse_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), _strides3(k), k.shape[2], _ptr(idx),
                                               _ptr(cnt),
                                               q_start, Tq, B, Hq, Hkv, d, 64, U, scale, _ptr(out), sh),
@@ -511,6 +519,7 @@ def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None =
     lay = (B, Hq, Hkv, d, hidden, nb_cap, U, _dt(k))
     nbytes = workspace_bytes("layer", *lay)
     ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "layer", lay)
+    _whole_blocks(k, "decode_layer_lookahead")
     _check(lib.bskv_decode_layer_lookahead(_ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2],
                                            _ptr(seq_len), _ptr(kc), _ptr(idx), _ptr(cnt), scale, _ptr(out), _ptr(x),
                                            _ptr(w), hidden, _ptr(kc_next), _ptr(idx_next), _ptr(cnt_next), B, Hq,

@@ -237,6 +237,7 @@ int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, i
   if (!q || !k || !v || !idx || !cnt || !seq_len || !out || !ws) return BSKV_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return BSKV_EINVAL;
   if (B <= 0 || U <= 0 || kv_len < 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (kv_len % 64) return BSKV_EINVAL;   // the K/V buffers hold whole blocks
   if (!span_ok(kv_len, kv_strides, dtype)) return BSKV_EUNSUPPORTED;
   if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
@@ -256,6 +257,7 @@ int bskv_block_sparse_attn_prefill(const void* q, const void* k, const void* v, 
   if (!q || !k || !v || !idx || !cnt || !out) return BSKV_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BSKV_EINVAL;
   if (B <= 0 || U <= 0 || n_q_tokens <= 0 || kv_len < 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (kv_len % 64) return BSKV_EINVAL;   // the K/V buffers hold whole blocks
   if (q_start < 0 || q_start % 64) return BSKV_EINVAL;
   if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
   if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
@@ -430,6 +432,7 @@ int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int
     return BSKV_EINVAL;   // the lookahead arguments come all together or not at all
   if (sel && (!aligned16(x) || !aligned16(w_forecast) || !aligned16(kc_next))) return BSKV_EINVAL;
   if (B <= 0 || kv_len < 0 || kc_nb_cap <= 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
+  if (kv_len % 64) return BSKV_EINVAL;   // the K/V buffers hold whole blocks
   if (!span_ok(kv_len, kv_strides, dtype)) return BSKV_EUNSUPPORTED;
   if (topk < 0 || n_init < 1 || n_local < 1) return BSKV_EINVAL;
   if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;

@@ -245,10 +245,11 @@ __global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
   // softmax slot of block a: S -> P (bf16 operand), running max and sum
   auto softmax_slot = [&](int a) {
     const int j = list[a];
-    // causal mask: only the diagonal block (uniform over the workgroup);
-    // a listed block outside the buffers is masked whole
+    // causal mask: the diagonal block per token (uniform over the
+    // workgroup); a listed block after the query block, or outside the
+    // buffers, is masked whole
     if (j >= qb || !valid(j)) {
-      const bool ok = valid(j);
+      const bool ok = valid(j) && j == qb;
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         const int rq = row0 + 16 * nq + l16;

@@ -139,9 +139,15 @@ int proj_tiles(int N, int dtype);
 
 static size_t al256(size_t x) { return ((x + 255) / 256) * 256; }
 
+// Workspace layout: the arrival counters first, at offset 0 whatever the
+// other arguments are, so one workspace can serve layers with and without a
+// lookahead (whose projection partials are absent) and the counters always
+// land on the words every earlier call left at zero; then the projection
+// partials, the candidate scores and the attention split partials, which
+// every call writes before it reads them.
 size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype) {
-  return al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) + al256((size_t)B * Hkv * nb_cap * sizeof(float)) +
-         al256((size_t)2 * B * Hkv * sizeof(int32_t)) + attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
+  return al256((size_t)2 * B * Hkv * sizeof(int32_t)) + al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) +
+         al256((size_t)B * Hkv * nb_cap * sizeof(float)) + attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
 }
 
 template <typename T, int D, int G>
@@ -175,14 +181,14 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   const size_t score_b = al256((size_t)B * H * a.nb_cap * sizeof(float));
   const size_t sync_b = al256((size_t)2 * B * H * sizeof(int32_t));
   char* ws = (char*)a.attn.ws;
-  p.sync = (int32_t*)(ws + proj_b + score_b);
-  p.attn = make_attn_params(a.attn, ws + proj_b + score_b + sync_b);
+  p.sync = (int32_t*)ws;
+  p.attn = make_attn_params(a.attn, ws + sync_b + proj_b + score_b);
   p.select = a.x != nullptr;
   p.x = a.x; p.w = a.w; p.hidden = a.hidden; p.N = H * D;
-  p.proj_part = (float*)ws;
+  p.proj_part = (float*)(ws + sync_b);
   p.proj_tiles = p.select ? proj_tiles(H * D, a.attn.dtype) : 0;
   p.proj_splits = p.select ? proj_splits(a.hidden) : 0;
-  p.kc_next = a.kc_next; p.scores = (float*)(ws + proj_b);
+  p.kc_next = a.kc_next; p.scores = (float*)(ws + sync_b + proj_b);
   p.score_splits = score_split_plan(B * H, a.nb_cap);
   p.idx_next = a.idx_next; p.cnt_next = a.cnt_next;
   p.B = B; p.H = H; p.topk = a.topk; p.n_init = a.n_init; p.n_local = a.n_local; p.U = a.attn.U;

@@ -34,14 +34,20 @@
  *   Accumulation is always fp32.
  * - head_dim must be 64 or 128; block must be 64 (the pages' block size).
  * - Workspaces: a call that takes `ws` needs at least the bytes returned by
- *   its *_workspace() query, 16-byte aligned.  Its contents need no
- *   initialisation: every partial result is written before it is read, and
- *   the library keeps no counters in it.  Calls that overlap in time must not
+ *   its *_workspace() query, 16-byte aligned.  Every partial result in it is
+ *   written before it is read.  One exception holds state between calls:
+ *   bskv_decode_layer_lookahead keeps arrival counters at the start of its
+ *   workspace, which must be zero-filled once before its first use and which
+ *   every complete call leaves at zero (see that call).  All other
+ *   workspaces need no initialisation.  Calls that overlap in time must not
  *   share a workspace.
  * - kv_len / src_len: the number of tokens the K/V buffers hold (their
- *   allocation along the token axis, in whole blocks).  Kernels skip any
- *   listed block that would reach beyond it, so a bad index list cannot make
- *   them read outside the buffers.
+ *   allocation along the token axis).  For the attention calls and the
+ *   decode layer it must be a whole number of blocks (else BSKV_EINVAL):
+ *   allocate caches in whole blocks; tokens past seq_len (decode) or past
+ *   the query position (prefill) are masked.  Kernels skip any listed block
+ *   that would reach beyond kv_len, so a bad index list cannot make them
+ *   read outside the buffers.
  * - Thread safety: the library holds no mutable state apart from the
  *   thread-local text of the last HIP error.
  */
@@ -275,7 +281,9 @@ int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, i
  * a4p Block-sparse causal prefill attention (bf16 MFMA, fp32 accumulate).
  * [EXPL] "The fourth projection", Eq. 5 and Alg. 1.  The query token at
  * position p = q_start + t (chunk-relative t) attends to the tokens of its
- * query block's list idx[b, g, t/block, 0..cnt-1] at positions <= p.
+ * query block's list idx[b, g, t/block, 0..cnt-1] at positions <= p: a
+ * listed block before the query block is used whole, the query block itself
+ * up to p, and a listed block after it not at all.
  * q      [B, n_q_heads, n_q_tokens, head_dim] bf16, contiguous
  * k, v   cache holding at least q_start + n_q_tokens tokens (bf16)
  * idx    [B, Hkv, n_qb, U] int32, cnt [B, Hkv, n_qb] int32
@@ -427,9 +435,12 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
  * x, w_forecast, kc_next, idx_next, cnt_next are all given or all NULL
  * (NULL: the last layer, no selection).  hidden must be a multiple of 256.
  * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL,
- * zero-filled once before its first use: it holds K2's arrival counters,
- * which every complete call leaves at zero again (calls that share one ws
- * must not overlap in time).
+ * zero-filled once before its first use: its first 2*B*n_kv_heads int32
+ * words are K2's arrival counters, at that fixed offset for every call, and
+ * every complete call leaves them at zero again.  One ws may therefore serve
+ * every layer of a model, last layer included (size it for the largest
+ * layout, i.e. with the lookahead's hidden); calls that share one ws must
+ * not overlap in time.
  * stages: bit 0 = K1 (projection partials), bit 1 = K2 (next-layer scores
  * and top-k, this layer's attention, merge and kc update); 3 runs the whole
  * layer.  K2 reads what K1 left in ws, so a caller may launch them

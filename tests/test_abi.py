@@ -10,7 +10,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bskv.h")
 
-bskv = pytest.importorskip("block_sparse_long_kv_amd")
+# a missing build is a failure, not a skip: these checks are the boundary's contract
+import block_sparse_long_kv_amd as bskv  # noqa: E402
 lib = bskv.lib
 
 OK, EINVAL, EDTYPE, EUNSUP, ENOSPC, EHIP = 0, -1, -2, -3, -4, -5
@@ -263,6 +264,8 @@ def test_attn_decode_validation():
     assert call(scale=float("nan")) == EINVAL
     assert call(wsb=ws - 1) == ENOSPC
     assert call(kv_len=-64) == EINVAL
+    assert call(kv_len=131072 - 5) == EINVAL     # K/V buffers hold whole blocks
+    assert call(kv_len=300) == EINVAL
     # one (b, g)'s K/V must span less than 2 GiB (32-bit load offsets) ...
     big = (ctypes.c_int64 * 3)(1 << 40, 1 << 30, 1 << 14)
     assert call(strides=big, kv_len=1 << 16) == EUNSUP
@@ -274,9 +277,10 @@ def test_attn_decode_validation():
 def test_attn_prefill_validation():
     f = lib.bskv_block_sparse_attn_prefill
 
-    def call(dt=1, q0=0, tq=2048, hq=32, hkv=8, d=128):
-        return f(P, P, P, dt, S3, 131072, P, P, q0, tq, 4, hq, hkv, d, 64, 97, 0.088, P, None)
+    def call(dt=1, q0=0, tq=2048, hq=32, hkv=8, d=128, kv_len=131072):
+        return f(P, P, P, dt, S3, kv_len, P, P, q0, tq, 4, hq, hkv, d, 64, 97, 0.088, P, None)
     assert call(dt=0) == EDTYPE
+    assert call(kv_len=300, tq=300) == EINVAL    # K/V buffers hold whole blocks
     assert call(q0=32) == EINVAL
     assert call(tq=0) == EINVAL
     assert call(hq=12) == EUNSUP
@@ -303,9 +307,10 @@ def test_decode_layer_validation():
     ws = lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 4096, 2048, 69, 1)
     assert ws > lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 0, 2048, 69, 1)
 
-    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=3, dt=1, hq=32, nl=4, wsb=ws):
-        return f(P, P, P, dt, S3, 131072, P, P, P, P, 0.088, P, x, w, hidden, kcn, idn, cnn, 8, hq, 8, 128, 64, 2048,
+    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=3, dt=1, hq=32, nl=4, wsb=ws, kv_len=131072):
+        return f(P, P, P, dt, S3, kv_len, P, P, P, P, 0.088, P, x, w, hidden, kcn, idn, cnn, 8, hq, 8, 128, 64, 2048,
                  64, 1, nl, stages, P, wsb, None)
+    assert call(kv_len=131072 - 1) == EINVAL     # K/V buffers hold whole blocks
     assert call(x=None) == EINVAL            # lookahead arguments: all or none
     assert call(idn=None) == EINVAL
     assert call(stages=0) == EINVAL

@@ -545,6 +545,70 @@ def test_prefill_attention_wide_score_range(d, G):
     assert err < 2e-2, err
 
 
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 2)])
+def test_prefill_attention_ignores_listed_future_blocks(d, G):
+    """A list passed through the boundary may name blocks after the query
+    block: none of their tokens is attended (all lie after every query
+    position of the block), while the query block itself stays causal per
+    token.  Each query block's list gets two future blocks in place of two
+    top-k entries (kept ascending, the count unchanged)."""
+    Hkv, T, q_start, Tq = 2, 2048, 512, 1024
+    c, q_chunk, _, _, sel = _prefill_case(71, 1, Hkv * G, Hkv, d, T, q_start, Tq, topk=6, n_local=3)
+    NB = T // 64
+    idx_np, cnt_np = sel.idx.copy(), sel.cnt.copy()
+    n_future = 0
+    for g in range(Hkv):
+        for qi in range(idx_np.shape[2]):
+            qb = q_start // 64 + qi
+            c0 = int(cnt_np[0, g, qi])
+            lst = [int(j) for j in idx_np[0, g, qi, :c0]]
+            keep = [j for j in lst if j >= qb - 2 or j == 0]       # initial + local blocks
+            top = [j for j in lst if j not in keep]
+            fut = [j for j in (qb + 1, qb + 7) if j < NB][: len(top)]
+            new = sorted(keep + top[: len(top) - len(fut)] + fut)
+            assert len(new) == c0
+            idx_np[0, g, qi, :c0] = new
+            n_future += len(fut)
+    assert n_future > 0
+    idx = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(cnt_np.astype(np.int32)).to(DEV)
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, q_start)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = [(0, h, t) for h in range(Hkv * G) for t in rng.choice(Tq, 24, replace=False)]
+    rows += [(0, 0, 0), (0, 0, 63), (0, Hkv * G - 1, Tq - 1)]
+    want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), idx_np, cnt_np, q_start,
+                              1.0 / math.sqrt(d), 64, rows=rows)
+    got = np64(out)
+    err = max(max_abs(got[r], want[r]) for r in rows)
+    assert err < 2e-2, err
+
+
+def test_partial_kv_blocks_are_rejected():
+    """K/V buffers whose token axis is not a whole number of blocks are
+    refused (the binding raises before calling; the C ABI returns
+    BSKV_EINVAL), instead of silently dropping the partial block."""
+    c = _gpu(random_decode_case(3, B=1, Hq=4, Hkv=1, d=128, T=300, dtype="bf16", seq_len=[300]))
+    idx = torch.tensor([[[0, 4]]], dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([[2]], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="whole 64-token blocks"):
+        bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"])
+    q = torch.zeros(1, 4, 300, 128, dtype=torch.bfloat16, device=DEV)
+    pidx = torch.zeros(1, 1, 5, 2, dtype=torch.int32, device=DEV)
+    pcnt = torch.ones(1, 1, 5, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="whole 64-token blocks"):
+        bskv.block_sparse_attn_prefill(q, c["k"], c["v"], pidx, pcnt, 0)
+    # a cache allocated in whole blocks with a ragged length works
+    kp = torch.zeros(1, 1, 320, 128, dtype=torch.bfloat16, device=DEV)
+    vp = torch.zeros_like(kp)
+    kp[:, :, :300], vp[:, :, :300] = c["k"], c["v"]
+    out = bskv.block_sparse_attn_decode(c["q"], kp, vp, idx, cnt, c["seq_len"])
+    torch.cuda.synchronize()
+    want = orc.attend_decode(np64(c["q"]), np64(kp), np64(vp), idx.cpu().numpy(), cnt.cpu().numpy(), [300],
+                             1 / math.sqrt(128), 64)
+    assert max_abs(np64(out), want) < 2e-2
+
+
 def test_prefill_full_budget_is_causal_attention():
     B, Hq, Hkv, d, T = 1, 4, 1, 128, 512
     c, q_chunk, idx, cnt, _ = _prefill_case(41, B, Hq, Hkv, d, T, 0, T, topk=64, n_local=2)
@@ -825,13 +889,13 @@ def _layer_case(dtype, d, G, B, T, lens, seed):
     sel = orc.decode_select(np64(c2["f"]), orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens), lens, 6, 1, 2, 64)
     idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
     cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
-    return c, kc, kc_next, idx, cnt
+    return c, c2, kc, kc_next, idx, cnt
 
 
 @pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2), ("bf16", 64, 8)])
 def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     lens = [64 * 30, 64 * 30 - 5, 64 * 17, 64 * 30]
-    c, kc, kc_next, idx, cnt = _layer_case(dtype, d, G, 4, 64 * 30, lens, 3)
+    c, c2, kc, kc_next, idx, cnt = _layer_case(dtype, d, G, 4, 64 * 30, lens, 3)
     # stale rows where the newest blocks go, to see them rewritten
     kc_a = kc.clone()
     kc_a[:, :, 29] = float("nan")
@@ -852,7 +916,8 @@ def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     # and against the oracle
     lens_np = np.array(lens)
     f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), 4, d)
-    sel = orc.decode_select(f_or, np64(kc_next), lens_np, 6, 1, 2, 64)
+    kc_next_or = orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens)
+    sel = orc.decode_select(f_or, kc_next_or, lens_np, 6, 1, 2, 64)
     check_selection(idx_b, cnt_b, sel, 6)
     want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens_np,
                              scale, 64)
@@ -865,7 +930,7 @@ def test_decode_layer_graph_replays():
     the workspace, which every launch leaves at zero: replays of a captured
     layer, with eager calls between them, match the eager result exactly."""
     lens = [64 * 20, 64 * 20 - 3]
-    c, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 21)
+    c, _, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 21)
     kc_e = kc.clone()
     out_e, i_e, n_e = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_e, idx, cnt,
                                                   x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
@@ -905,7 +970,7 @@ def test_decode_layer_graph_replays():
 
 def test_decode_layer_stages_and_last_layer():
     lens = [64 * 20] * 2
-    c, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
+    c, _, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
     kc1, kc2 = kc.clone(), kc.clone()
     out1, i1, n1 = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc1, idx, cnt, x=c["x_sel"],
                                                w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
@@ -920,3 +985,66 @@ def test_decode_layer_stages_and_last_layer():
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(i1, i2) and torch.equal(n1, n2) and torch.equal(kc1, kc2)
     assert none_i is None and none_c is None and torch.equal(out3, out1)
+
+
+def test_decode_layer_shared_workspace_across_lookahead_and_last_layer():
+    """One workspace serves a layer with a lookahead, a last layer (no
+    projection partials in its layout) and another lookahead layer, in that
+    order, as a model's layers share it: each call must equal the same call
+    on a fresh zero-filled workspace."""
+    lens = [64 * 40, 64 * 40 - 9]
+    c, _, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 40, lens, 31)
+    nb = kc.shape[2]
+    ws = torch.zeros(bskv.workspace_bytes("layer", 2, 16, 4, 128, 512, nb, 9, 1), dtype=torch.uint8, device=DEV)
+
+    def run(shared, sel):
+        kw = dict(x=c["x_sel"], w=c["w_sel"], kc_next=kc_next) if sel else {}
+        own = ws if shared else torch.zeros_like(ws)
+        return bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, topk=6,
+                                           n_init=1, n_local=2, ws=own, **kw)
+    for rnd in range(2):
+        for sel in (True, False, True):
+            got = run(True, sel)
+            want = run(False, sel)
+            torch.cuda.synchronize()
+            assert torch.equal(got[0], want[0]), (rnd, sel)
+            if sel:
+                assert torch.equal(got[1], want[1]) and torch.equal(got[2], want[2]), (rnd, sel)
+    # every complete call leaves the arrival counters (the first words) at zero
+    assert int(ws[: 2 * 2 * 4 * 4].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("lens", [[64 * 300, 64 * 300 - 17], [64 * 300 - 63, 64 * 131 + 5]])
+def test_decode_layer_multi_slice_multi_block_splits(lens):
+    """B2 x 4 KV heads with 300 blocks and top-64: several score slices per
+    (b, g) arrive at the top-k, and each attention split covers several
+    blocks.  The next layer's compressed keys are pooled by the oracle, not
+    taken from the GPU."""
+    T, topk = 64 * 300, 64
+    c = _gpu(random_decode_case(41, B=2, Hq=16, Hkv=4, d=128, T=T, dtype="bf16", hidden=512, seq_len=lens))
+    c2 = _gpu(random_decode_case(42, B=2, Hq=16, Hkv=4, d=128, T=T, dtype="bf16", seq_len=lens, plant=20,
+                                 n_local=2))
+    kc = _kc_gpu(c["k"], c["seq_len"])
+    kc_next = _kc_gpu(c2["k"], c2["seq_len"])
+    lens_np = np.array(lens)
+    kc_or = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens)
+    kc_next_or = orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens)
+    own = orc.decode_select(np64(c2["f"]), kc_or, lens_np, topk, 1, 2, 64)
+    idx = torch.from_numpy(own.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(own.cnt.astype(np.int32)).to(DEV)
+    U = topk + 3
+    ws = torch.zeros(bskv.workspace_bytes("layer", 2, 16, 4, 128, 512, 300, U, 1), dtype=torch.uint8, device=DEV)
+    for rep in range(2):                      # the second call reuses the counters the first left at zero
+        kc_l = kc.clone()
+        out, i_n, c_n = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_l, idx, cnt,
+                                                    x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk,
+                                                    n_init=1, n_local=2, ws=ws)
+        torch.cuda.synchronize()
+        f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), 4, 128)
+        sel = orc.decode_select(f_or, kc_next_or, lens_np, topk, 1, 2, 64)
+        check_selection(i_n, c_n, sel, topk)
+        want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), own.idx, own.cnt, lens_np,
+                                 1 / math.sqrt(128), 64)
+        assert max_abs(np64(out), want) < 2e-2, rep
+        done = ~np.isnan(kc_or)
+        assert max_abs(np64(kc_l)[done], kc_or[done]) < 1e-4
