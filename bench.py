@@ -998,70 +998,44 @@ class OffloadBench:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         U, H, d = wl.U, wl.Hkv, wl.d
-        self.ring_k = [torch.empty(self.B, H, U, wl.block, d, dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
-        self.ring_v = [torch.empty_like(self.ring_k[0]) for _ in range(2)]
+        from block_sparse_long_kv_amd.offload import LookaheadRing, OffloadLayer
         self.f = [torch.empty(self.B, H, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
         self.idx = [torch.empty(self.B, H, U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
         self.cnt = [torch.empty(self.B, H, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
         self.out = [torch.empty(self.B, wl.Hq, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        # layer l reads host layer l mod host_layers (the pinned pool holds host_layers distinct layers)
+        self.layers = [OffloadLayer(self.host_k[self.h(l)], self.host_v[self.h(l)], self.kc[self.h(l)],
+                                    self.x[self.h(l)], self.w[self.h(l)], self.q[self.h(l)], self.seq_len,
+                                    self.f[l], self.idx[l], self.cnt[l], self.out[l],
+                                    host_k_dev=self.dk[self.h(l)], host_v_dev=self.dv[self.h(l)])
+                       for l in range(self.L)]
         z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=self.dev)  # noqa: E731
         self.ws_proj = z(bskv.workspace_bytes("proj", self.B, wl.hidden, H, d, 1))
         self.ws_score = z(bskv.workspace_bytes("score", self.B, H, 0, nb, d))
         self.ws_attn = z(bskv.workspace_bytes("attn", self.B, wl.Hq, H, d, U))
-        self.copy_stream = torch.cuda.Stream(self.dev)
-        self.ev_sel = [torch.cuda.Event() for _ in range(self.L)]
-        self.ev_pf = [torch.cuda.Event() for _ in range(self.L)]
-        self.ev_att = [torch.cuda.Event() for _ in range(self.L)]
-        self.n_wg = 256
+        self.ring = LookaheadRing(self.B, H, U, d, device=self.dev, n_workgroups=256)
         torch.cuda.synchronize()
         log(f"[bench] offload set-up ({self.HL} host layers, {2 * self.HL * hk.numel() * 2 / 2**30:.0f} GiB pinned) "
             f"in {time.time() - t0:.1f}s")
 
+    @property
+    def n_wg(self):
+        return self.ring.n_workgroups
+
+    @n_wg.setter
+    def n_wg(self, v):
+        self.ring.n_workgroups = v
+
     def h(self, l):
         return l % self.HL
 
-    def select(self, l):
-        wl, hl = self.wl, self.h(l)
-        self.bskv.forecast_proj(self.x[hl], self.w[hl], wl.Hkv, wl.d, out=self.f[l], ws=self.ws_proj)
-        self.bskv.forecast_block_score_topk(self.f[l], self.kc[hl], wl.topk, wl.n_init, wl.n_local,
-                                            seq_len=self.seq_len, idx=self.idx[l], cnt=self.cnt[l], ws=self.ws_score)
-
     def prefetch(self, l, stream=None):
-        hl, slot = self.h(l), l % 2
-        self.bskv.prefetch_selected_blocks(self.host_k[hl], self.host_v[hl], self.idx[l], self.cnt[l],
-                                           self.ring_k[slot], self.ring_v[slot], n_workgroups=self.n_wg,
-                                           stream=stream, src_k_dev=self.dk[hl], src_v_dev=self.dv[hl])
-
-    def attend(self, l):
-        hl, slot = self.h(l), l % 2
-        self.bskv.block_sparse_attn_decode(self.q[hl], self.ring_k[slot], self.ring_v[slot], self.idx[l],
-                                           self.cnt[l], self.seq_len, self.wl.scale, ring=True, out=self.out[l],
-                                           ws=self.ws_attn)
+        self.ring.prefetch(self.layers[l], l % 2, stream=stream)
 
     def step(self, with_copy=True):
-        torch = self.torch
-        comp = torch.cuda.current_stream(self.dev)
-        cs = self.copy_stream
-        self.select(0)
-        if with_copy:
-            self.ev_sel[0].record(comp)
-            cs.wait_event(self.ev_sel[0])
-            self.prefetch(0, stream=cs)
-            self.ev_pf[0].record(cs)
-        for l in range(self.L):
-            if l + 1 < self.L:
-                self.select(l + 1)                     # F_l picks layer l+1's blocks ...
-                if with_copy:
-                    self.ev_sel[l + 1].record(comp)
-                    cs.wait_event(self.ev_sel[l + 1])
-                    if l >= 1:
-                        cs.wait_event(self.ev_att[l - 1])   # ring slot (l+1)%2 was read by layer l-1
-                    self.prefetch(l + 1, stream=cs)    # ... and their copy starts now
-                    self.ev_pf[l + 1].record(cs)
-            if with_copy:
-                comp.wait_event(self.ev_pf[l])         # layer l's blocks (copied one layer ago)
-            self.attend(l)
-            self.ev_att[l].record(comp)
+        wl = self.wl
+        self.ring.step(self.layers, wl.topk, wl.n_init, wl.n_local, wl.scale, ws_proj=self.ws_proj,
+                       ws_score=self.ws_score, ws_attn=self.ws_attn, with_copy=with_copy)
 
     def copy_only(self):
         for l in range(self.L):
@@ -1203,27 +1177,28 @@ class SteadyOffloadBench:
         self.ws_proj = z(bskv.workspace_bytes("proj", self.B, hid, H, d, 1))
         self.ws_score = z(bskv.workspace_bytes("score", self.B, H, 0, nb, d))
         self.ws_attn = z(bskv.workspace_bytes("attn", self.B, wl.Hq, H, d, U))
-        self.copy_stream = torch.cuda.Stream(self.dev)
-        self.ev_plan = [torch.cuda.Event() for _ in range(self.L)]
-        self.ev_fill = [torch.cuda.Event() for _ in range(self.L)]
-        self.n_wg = self.B * H
+        from block_sparse_long_kv_amd.offload import CachedLookahead, OffloadLayer
+        self.layers = [OffloadLayer(self.host_k[l % self.HL], self.host_v[l % self.HL], self.kc[l % self.HL],
+                                    self.xbuf[l], self.w[l % self.HL], self.q[l % self.HL], self.seq_len,
+                                    self.f[l], self.idx[l], self.cnt[l], self.out[l],
+                                    host_k_dev=self.dk[l % self.HL], host_v_dev=self.dv[l % self.HL])
+                       for l in range(self.L)]
+        self.sched = CachedLookahead(self.caches, self.slot, self.fill, [self.n_fill[l] for l in range(self.L)],
+                                     device=self.dev, n_workgroups=self.B * H)
         torch.cuda.synchronize()
         log(f"[bench] steady offload set-up ({self.HL} host layers pinned, {self.L} caches of {S} slots, "
             f"{self.L * self.standin_bytes / 1e9:.1f} GB stand-in weights) in {time.time() - t0:.1f}s")
 
-    def select_plan(self, l):
-        wl, hl = self.wl, l % self.HL
-        self.bskv.forecast_proj(self.xbuf[l], self.w[hl], wl.Hkv, wl.d, out=self.f[l], ws=self.ws_proj)
-        self.bskv.forecast_block_score_topk(self.f[l], self.kc[hl], wl.topk, wl.n_init, wl.n_local,
-                                            seq_len=self.seq_len, idx=self.idx[l], cnt=self.cnt[l], ws=self.ws_score)
-        self.bskv.block_cache_plan(self.caches[l], self.idx[l], self.cnt[l], slot=self.slot[l], fill=self.fill[l],
-                                   n_fill=self.n_fill[l])
+    @property
+    def n_wg(self):
+        return self.sched.n_workgroups
+
+    @n_wg.setter
+    def n_wg(self, v):
+        self.sched.n_workgroups = v
 
     def fill_cache(self, l, stream=None):
-        hl = l % self.HL
-        self.bskv.prefetch_cache_fill(self.host_k[hl], self.host_v[hl], self.idx[l], self.slot[l], self.fill[l],
-                                      self.n_fill[l], self.caches[l], n_workgroups=self.n_wg, stream=stream,
-                                      src_k_dev=self.dk[hl], src_v_dev=self.dv[hl])
+        self.sched.fill_cache(self.layers[l], l, stream=stream)
 
     def standin_pre(self, l):
         return self.xbuf[l] @ self.w_qkv[l]
@@ -1236,36 +1211,13 @@ class SteadyOffloadBench:
         act = torch.nn.functional.silu(gu[:, : self.ffn]) * gu[:, self.ffn:]
         return act @ self.w_down[l]
 
-    def attend(self, l):
-        hl = l % self.HL
-        self.bskv.block_sparse_attn_decode_cached(self.q[hl], self.caches[l], self.slot[l], self.idx[l], self.cnt[l],
-                                                  self.seq_len, self.wl.scale, out=self.out[l], ws=self.ws_attn)
-
     def body(self, with_copy=True, standin=True):
         """One decode step on the Forecast inputs in xbuf (graph-capturable)."""
-        torch = self.torch
-        comp = torch.cuda.current_stream(self.dev)
-        cs = self.copy_stream
-
-        def issue(l):
-            self.select_plan(l)
-            if with_copy:
-                self.ev_plan[l].record(comp)
-                cs.wait_event(self.ev_plan[l])
-                self.fill_cache(l, stream=cs)
-                self.ev_fill[l].record(cs)
-
-        issue(0)
-        for l in range(self.L):
-            if standin:
-                self.standin_pre(l)
-            if l + 1 < self.L:
-                issue(l + 1)                 # F_l selects layer l+1; its missing blocks start copying
-            if with_copy:
-                comp.wait_event(self.ev_fill[l])
-            self.attend(l)
-            if standin:
-                self.standin_post(l)
+        wl = self.wl
+        self.sched.step(self.layers, wl.topk, wl.n_init, wl.n_local, wl.scale, ws_proj=self.ws_proj,
+                        ws_score=self.ws_score, ws_attn=self.ws_attn, with_copy=with_copy,
+                        before_layer=self.standin_pre if standin else None,
+                        after_layer=self.standin_post if standin else None)
 
     def copy_only(self):
         for l in range(self.L):
