@@ -88,9 +88,10 @@ def log(*a):
 # decode workload
 # ---------------------------------------------------------------------------
 class DecodeBench:
-    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None):
+    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None, select_mode="deferred"):
         from workloads import decode_inputs
         self.torch, self.bskv, self.wl = torch, bskv, wl
+        self.select_mode = select_mode
         self.dev = torch.device("cuda:0")
         self.L = layers or wl.layers
         self.B = B or wl.B
@@ -108,6 +109,8 @@ class DecodeBench:
         self.idx = [torch.empty(B, H, wl.U, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
         self.cnt = [torch.empty(B, H, dtype=torch.int32, device=self.dev) for _ in range(self.L)]
         self.out = [torch.empty(B, wl.Hq, d, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
+        # candidate scores of layer l, written by layer l-1's call, read by layer l's
+        self.scores = [torch.empty(B, H, nb, dtype=torch.float32, device=self.dev) for _ in range(self.L)]
         z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=self.dev)  # noqa: E731
         dt = 1 if wl.dtype == "bf16" else 0
         self.ws_proj = z(bskv.workspace_bytes("proj", B, wl.hidden, H, d, dt))
@@ -115,6 +118,8 @@ class DecodeBench:
         self.ws_attn = z(bskv.workspace_bytes("attn", B, wl.Hq, H, d, wl.U))
         self.ws_layer = z(bskv.workspace_bytes("layer", B, wl.Hq, H, d, wl.hidden, nb, wl.U, dt))
         self.ws_mh = z(bskv.workspace_bytes("multihead", B, H, nb))
+        self.side = torch.cuda.Stream(self.dev)
+        self.ev_side = {(k, l): torch.cuda.Event() for k in ("start", "sel", "att") for l in range(self.L)}
         torch.cuda.synchronize()
 
     # the four per-layer launches
@@ -154,16 +159,24 @@ class DecodeBench:
 
     def layer(self, l, stages=3):
         """Layer l: newest-block update, attention over B_l, and (lookahead)
-        F_l scoring layer l+1's compressed keys -> B_{l+1}; two kernels."""
+        F_l selecting layer l+1; two kernels.  Immediate mode: B_{l+1} is
+        complete when the call ends (the top-k runs in its second kernel).
+        Deferred mode: the call leaves layer l+1's candidate scores and the
+        next call starts with their top-k."""
         wl, lay = self.wl, self.layers[l]
         nxt = l + 1 < self.L
         n = self.layers[l + 1] if nxt else None
+        deferred = self.select_mode == "deferred"
+        kw = {}
+        if nxt and deferred:
+            kw["scores_next"] = self.scores[l + 1]
+        elif nxt:
+            kw["idx_next"], kw["cnt_next"] = self.idx[l + 1], self.cnt[l + 1]
         self.bskv.decode_layer_lookahead(
             lay["q"], lay["k"], lay["v"], lay["seq_len"], self.kc[l], self.idx[l], self.cnt[l], wl.scale,
             out=self.out[l], x=n["x_sel"] if nxt else None, w=n["w_sel"] if nxt else None,
-            kc_next=self.kc[l + 1] if nxt else None, idx_next=self.idx[l + 1] if nxt else None,
-            cnt_next=self.cnt[l + 1] if nxt else None, topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local,
-            stages=stages, ws=self.ws_layer)
+            kc_next=self.kc[l + 1] if nxt else None, scores=self.scores[l] if (deferred and l > 0) else None,
+            topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local, stages=stages, ws=self.ws_layer, **kw)
 
     def step(self):
         # layer 0 is selected by the separate layer-0 projection; then every
@@ -172,6 +185,44 @@ class DecodeBench:
         self.select(0)
         for l in range(self.L):
             self.layer(l)
+
+    def attend_layer(self, l):
+        """Layer l's attention over B_l with the merge and the newest-block
+        update (the fused layer call without a lookahead: one launch)."""
+        wl, lay = self.wl, self.layers[l]
+        self.bskv.decode_layer_lookahead(lay["q"], lay["k"], lay["v"], lay["seq_len"], self.kc[l], self.idx[l],
+                                         self.cnt[l], wl.scale, out=self.out[l], topk=wl.topk, n_init=wl.n_init,
+                                         n_local=wl.n_local, ws=self.ws_layer)
+
+    def step_two_streams(self):
+        """One-layer-ahead selection on a side stream: the selection of
+        layer l+1 (F_l = x_l W_F, scores against layer l+1's compressed
+        keys, top-k + union) runs while layer l attends on the compute
+        stream.  It starts once layer l-1 has attended (x_l is computed from
+        layer l-1's output in a model); layer l+1 attends once its list is
+        complete."""
+        torch = self.torch
+        main = torch.cuda.current_stream(self.dev)
+        side = self.side
+        ev_start = self.ev_side[("start", 0)]
+        ev_start.record(main)
+        side.wait_event(ev_start)
+        with torch.cuda.stream(side):
+            self.proj(0)
+            self.select(0)
+        self.ev_side[("sel", 0)].record(side)
+        for l in range(self.L):
+            if l + 1 < self.L:
+                if l >= 1:
+                    side.wait_event(self.ev_side[("att", l - 1)])
+                with torch.cuda.stream(side):
+                    self.proj(l + 1)
+                    self.select(l + 1)
+                self.ev_side[("sel", l + 1)].record(side)
+            main.wait_event(self.ev_side[("sel", l)])
+            self.attend_layer(l)
+            self.ev_side[("att", l)].record(main)
+        main.wait_stream(side)
 
     def step_per_op(self):
         self.proj(0)
@@ -198,15 +249,27 @@ class DecodeBench:
         lists = B * H * (U + 1) * 4
         attn = B * H * (U * wl.block * d * e * 2) + B * wl.Hq * d * e + lists
         out = B * wl.Hq * d * 4
-        # the fused kernels are timed over all L layers, and the last layer
-        # selects nothing (no scoring or lists in its K2): per-launch figures
+        # the fused kernels are timed over all L layers: K1 of layer 0 has no
+        # top-k (its list comes from the separate layer-0 selection) and K1 /
+        # K2 of the last layer no projection / scoring; per-launch figures
         # are averages over the timed launches
         nxt = (self.L - 1) / self.L
-        return {
-            "forecast_proj": proj, "kv_block_meanpool": pool, "score_topk": score + lists,
-            "attn_decode": attn + out,
-            "layer_k1": proj, "layer_k2": round((score + lists) * nxt + attn + out + pool),
-        }
+        res = {"forecast_proj": proj, "kv_block_meanpool": pool, "score_topk": score + lists,
+               "attn_decode": attn + out}
+        if self.select_mode == "deferred":
+            # K1 of every layer but the first runs the top-k, K1 of every
+            # layer but the last the projection (timed over all L launches);
+            # the candidate scores handed from K2 to the next K1 are an
+            # intermediate of this split (0.5 MB each way at B8 x 128K) and
+            # are not counted
+            res["layer_k1"] = round((proj + lists) * nxt)
+            res["layer_k2"] = round(score * nxt + attn + out + pool)
+        else:
+            # K1 (projection) is launched by every layer but the last and
+            # timed over those; K2 of the last layer has no scoring
+            res["layer_k1"] = proj
+            res["layer_k2"] = round((score + lists) * nxt + attn + out + pool)
+        return res
 
     def step_bytes(self):
         """Algorithmic bytes of one step: L projections (the layer-0 one
@@ -257,8 +320,8 @@ def kernel_times(torch, bench, reps=3):
     for name, fn in (("layer_k1", lambda l: bench.layer(l, 1)), ("layer_k2", lambda l: bench.layer(l, 2)),
                      ("kv_block_meanpool", bench.meanpool), ("forecast_proj", bench.proj),
                      ("score_topk", bench.select), ("attn_decode", bench.attend)):
-        # the last layer selects nothing, so it has no projection kernel
-        layers = range(bench.L - 1) if name == "layer_k1" else range(bench.L)
+        # immediate mode: the last layer has no first kernel (no projection)
+        layers = range(bench.L - 1) if (name == "layer_k1" and bench.select_mode != "deferred") else range(bench.L)
 
         def body():
             for _ in range(reps):

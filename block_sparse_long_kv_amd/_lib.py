@@ -62,8 +62,8 @@ _proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _
 _proto("bskv_block_sparse_attn_decode_cached", _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p,
        _p, _sz, _p)
 _proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _i, _i)
-_proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _f, _p, _p, _p,
-       _i, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
+_proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _f, _p, _p,
+       _p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
 
 BSKV_F32, BSKV_BF16 = 0, 1
 _DT = {torch.float32: BSKV_F32, torch.bfloat16: BSKV_BF16}
@@ -493,26 +493,38 @@ def block_sparse_attn_decode_cached(q, cache: "BlockCache", slot, idx, cnt, seq_
 
 
 def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None = None, out=None, x=None, w=None,
-                           kc_next=None, idx_next=None, cnt_next=None, topk: int = 0, n_init: int = 1,
-                           n_local: int = 1, stages: int = 3, ws=None, stream=None):
-    """One decode layer: newest-block update of kc, this layer's attention over
-    (idx, cnt), and (when x is given) the next layer's selection from the
-    Forecast x @ w against kc_next, written to idx_next / cnt_next.
-    stages: bit mask of the two launches (3 = both, in order)."""
+                           kc_next=None, scores=None, scores_next=None, idx_next=None, cnt_next=None, topk: int = 0,
+                           n_init: int = 1, n_local: int = 1, stages: int = 3, ws=None, stream=None):
+    """One decode layer: (when `scores` is given) this layer's top-k + union
+    from the candidate scores the previous layer's call wrote, into idx/cnt;
+    the newest-block update of kc; this layer's attention over (idx, cnt);
+    and (when x is given) the next layer's selection from the Forecast
+    x @ w against kc_next: its lists into idx_next / cnt_next when those are
+    given (immediate mode), else the raw scores of its candidates into
+    scores_next (deferred mode; allocated when not given).
+    stages: bit mask of the two launches (3 = both, in order).
+    Returns (out, scores_next) (scores_next None without a lookahead or in
+    immediate mode)."""
     B, Hq, d = q.shape
     Hkv, nb_cap = kc.shape[1], kc.shape[2]
     U = idx.shape[-1]
     if U != topk + n_init + n_local:
         raise ValueError("idx capacity must equal topk + n_init + n_local")
     sel = x is not None
+    immediate = idx_next is not None or cnt_next is not None
     if sel:
         hidden = x.shape[1]
-        idx_next = idx_next if idx_next is not None else torch.empty_like(idx)
-        cnt_next = cnt_next if cnt_next is not None else torch.empty_like(cnt)
+        if immediate and (idx_next is None or cnt_next is None or scores_next is not None):
+            raise ValueError("immediate mode takes idx_next and cnt_next (and no scores_next)")
+        if not immediate and scores_next is None:
+            scores_next = torch.empty(B, Hkv, nb_cap, dtype=torch.float32, device=q.device)
     else:
         hidden = 0
     if k.stride() != v.stride() or not q.is_contiguous():
         raise ValueError("q contiguous; k, v with identical strides")
+    for t in (scores, scores_next):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (B, Hkv, nb_cap)):
+            raise ValueError("scores / scores_next: contiguous fp32 [B, Hkv, kc_nb_cap]")
     scale = (1.0 / math.sqrt(d)) if scale is None else scale
     out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
     sh = _stream(stream, q.device)
@@ -521,8 +533,9 @@ def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None =
     ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "layer", lay)
     _whole_blocks(k, "decode_layer_lookahead")
     _check(lib.bskv_decode_layer_lookahead(_ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2],
-                                           _ptr(seq_len), _ptr(kc), _ptr(idx), _ptr(cnt), scale, _ptr(out), _ptr(x),
-                                           _ptr(w), hidden, _ptr(kc_next), _ptr(idx_next), _ptr(cnt_next), B, Hq,
-                                           Hkv, d, 64, nb_cap, topk, n_init, n_local, stages, _ptr(ws),
-                                           ws.numel() * ws.element_size(), sh), "decode_layer_lookahead")
-    return (out, idx_next, cnt_next) if sel else (out, None, None)
+                                           _ptr(seq_len), _ptr(kc), _ptr(scores), _ptr(idx), _ptr(cnt), scale,
+                                           _ptr(out), _ptr(x), _ptr(w), hidden, _ptr(kc_next), _ptr(scores_next),
+                                           _ptr(idx_next), _ptr(cnt_next), B, Hq, Hkv, d, 64, nb_cap, topk, n_init,
+                                           n_local, stages, _ptr(ws), ws.numel() * ws.element_size(), sh),
+           "decode_layer_lookahead")
+    return out, (scores_next if sel else None)

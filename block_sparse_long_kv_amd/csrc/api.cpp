@@ -417,19 +417,22 @@ size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_head
 }
 
 int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int dtype, const int64_t* kv_strides,
-                                int64_t kv_len, const int64_t* seq_len, float* kc, const int32_t* idx,
-                                const int32_t* cnt, float scale, float* out, const void* x, const void* w_forecast,
-                                int hidden, const float* kc_next, int32_t* idx_next, int32_t* cnt_next, int B,
-                                int n_q_heads, int n_kv_heads, int head_dim, int block, int64_t kc_nb_cap, int topk,
-                                int n_init, int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                int64_t kv_len, const int64_t* seq_len, float* kc, const float* scores, int32_t* idx,
+                                int32_t* cnt, float scale, float* out, const void* x, const void* w_forecast,
+                                int hidden, const float* kc_next, float* scores_next, int32_t* idx_next,
+                                int32_t* cnt_next, int B, int n_q_heads,
+                                int n_kv_heads, int head_dim, int block, int64_t kc_nb_cap, int topk, int n_init,
+                                int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return BSKV_EDTYPE;
   if (!q || !k || !v || !seq_len || !kc || !idx || !cnt || !out || !ws) return BSKV_EINVAL;
   if (stages < 1 || stages > 3) return BSKV_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(ws)) return BSKV_EINVAL;
   const bool sel = x != nullptr;
-  if (sel != (w_forecast != nullptr) || sel != (kc_next != nullptr) || sel != (idx_next != nullptr) ||
-      sel != (cnt_next != nullptr))
+  const bool deferred = scores_next != nullptr, immediate = idx_next != nullptr || cnt_next != nullptr;
+  if (sel != (w_forecast != nullptr) || sel != (kc_next != nullptr) || sel != (deferred || immediate))
     return BSKV_EINVAL;   // the lookahead arguments come all together or not at all
+  if (deferred && immediate) return BSKV_EINVAL;           // one form of the next layer's selection
+  if (immediate && (!idx_next || !cnt_next)) return BSKV_EINVAL;
   if (sel && (!aligned16(x) || !aligned16(w_forecast) || !aligned16(kc_next))) return BSKV_EINVAL;
   if (B <= 0 || kv_len < 0 || kc_nb_cap <= 0 || !strides_ok(kv_strides, dtype)) return BSKV_EINVAL;
   if (kv_len % 64) return BSKV_EINVAL;   // the K/V buffers hold whole blocks
@@ -448,8 +451,9 @@ int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int
   a.attn = bskv::AttnDecodeArgs{q, k, v, dtype, kv_strides[0], kv_strides[1], kv_strides[2], kv_len, 0, idx, cnt,
                                 seq_len, B, n_q_heads, n_kv_heads, head_dim, block, U, scale, out, ws, stream};
   a.kc = kc; a.nb_cap = kc_nb_cap;
+  a.scores = scores; a.idx = idx; a.cnt = cnt;
   a.x = x; a.w = w_forecast; a.hidden = sel ? hidden : 0;
-  a.kc_next = kc_next; a.idx_next = idx_next; a.cnt_next = cnt_next;
+  a.kc_next = kc_next; a.scores_next = scores_next; a.idx_next = idx_next; a.cnt_next = cnt_next;
   a.topk = topk; a.n_init = n_init; a.n_local = n_local; a.stages = stages;
   return finish(bskv::launch_decode_layer(a));
 }

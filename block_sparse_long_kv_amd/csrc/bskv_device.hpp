@@ -206,7 +206,10 @@ __device__ __forceinline__ uint32_t orderable_key(float f) {
 constexpr int kHistCopies = 4;
 constexpr int kHistStride = 257;
 struct TopkShared {
-  int hist[2][kHistCopies * kHistStride];
+  union {
+    int hist[2][kHistCopies * kHistStride];   // topk_union_regs (keys re-read from LDS)
+    int whist[2][4][2][256];                  // topk_union_fast: [pass & 1][wave][lane & 1][digit]
+  };
   int scan_tmp[4];
   int pick[3];
 };
@@ -337,6 +340,130 @@ __device__ __forceinline__ void topk_union_regs(const uint32_t* keys, int n, int
   if (tid == 0) *cnt_out = min(total, U);
 }
 
+// Top-k + union for one selection problem of at most 8 * kThreads
+// candidates, run by all 256 threads, thread t holding the keys of
+// candidates 8t .. 8t+7 in registers (so its keys are in block-id order).
+// Same result as topk_union_regs<8> (MSB-first radix select, 8 bits per
+// pass, stopping once the bucket holding the topk-th key is taken whole;
+// ties to the lowest block ids), with one barrier per radix pass and one for
+// the output positions: each wave counts into its own histogram copies
+// (two per wave, double buffered over passes, cleared by the wave itself),
+// and every wave scans all copies and finds the threshold bucket on its own,
+// so nothing is broadcast.
+__device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur, int n_init, int n_local, int U,
+                                                int32_t* idx_out, int32_t* cnt_out, TopkShared& sh,
+                                                const uint32_t (&kin)[8]) {
+  constexpr int KPT = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int i0 = tid * KPT;
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) kr[e] = (i0 + e < n) ? kin[e] : 0u;
+  const bool take_none = topk <= 0 || n <= 0;
+  const bool take_all = !take_none && n <= topk;
+  uint32_t prefix = 0, mask = 0;
+  int kk = topk;
+  if (!take_none && !take_all) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      int(*h)[2][256] = sh.whist[pass & 1];
+      // this wave's two copies: cleared in order before its own adds (LDS
+      // operations of one wave complete in order); the other waves read them
+      // only after the barrier, and reuse of this buffer two passes later is
+      // behind the next pass's barrier
+      for (int i = lane; i < 2 * 256; i += kWave) (&h[wid][0][0])[i] = 0;
+      int* mine = h[wid][lane & 1];
+#pragma unroll
+      for (int e = 0; e < KPT; ++e)
+        if (i0 + e < n && (kr[e] & mask) == prefix) atomicAdd(&mine[(kr[e] >> shift) & 255u], 1);
+      __syncthreads();
+      // lane l looks at digits 255-4l .. 252-4l (descending) over all copies
+      int c[4], ls = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int D = 255 - 4 * lane - r;
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v += h[w][0][D] + h[w][1][D];
+        c[r] = v;
+        ls += v;
+      }
+      int run = wave_excl_scan(ls);
+      int pick = -1, below = 0, in_bucket = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (run < kk && kk <= run + c[r]) {
+          pick = 255 - 4 * lane - r;
+          below = run;
+          in_bucket = c[r];
+        }
+        run += c[r];
+      }
+      const uint64_t found = __ballot(pick >= 0);
+      if (found == 0) break;   // unreachable: kk never exceeds the keys under the prefix
+      const int src = __builtin_ctzll(found);
+      pick = __builtin_amdgcn_readlane(pick, src);
+      below = __builtin_amdgcn_readlane(below, src);
+      in_bucket = __builtin_amdgcn_readlane(in_bucket, src);
+      prefix |= ((uint32_t)pick) << shift;
+      mask |= 255u << shift;
+      kk -= below;
+      if (kk == in_bucket) break;   // the bucket is taken whole
+    }
+  }
+  // ties: keys whose masked value equals the threshold bucket; the kk of
+  // them with the lowest block ids are taken
+  const int need = kk;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (i0 + e < n && !take_none) {
+      if (take_all) ++gt;
+      else {
+        const uint32_t km = kr[e] & mask;
+        gt += km > prefix;
+        eq += km == prefix;
+      }
+    }
+  }
+  // exclusive scan of (gt, eq) over the workgroup in thread order: one barrier
+  const int v = (gt << 16) | eq;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) sh.scan_tmp[wid] = inc;
+  __syncthreads();
+  int ex = inc - v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) ex += (w < wid) ? sh.scan_tmp[w] : 0;
+  int gt_b = ex >> 16, eq_b = ex & 0xffff;
+  const int n_sel = take_none ? 0 : (take_all ? n : topk);
+  const int local_lo = max(0, cur - n_local + 1);
+  const int a = min(n_init, local_lo);          // initial blocks below the local window
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (i0 + e < n && !take_none) {
+      bool sel;
+      int pos;
+      if (take_all) {
+        sel = true;
+        pos = a + gt_b++;
+      } else {
+        const uint32_t km = kr[e] & mask;
+        if (km > prefix) { sel = true; pos = a + gt_b + min(eq_b, need); ++gt_b; }
+        else if (km == prefix) { sel = eq_b < need; pos = a + gt_b + eq_b; ++eq_b; }
+        else { sel = false; pos = 0; }
+      }
+      if (sel && pos < U) idx_out[pos] = c0 + i0 + e;
+    }
+  }
+  const int n_loc = cur - local_lo + 1;
+  const int total = a + n_sel + n_loc;
+  for (int j = tid; j < a; j += kThreads) idx_out[j] = j;
+  for (int j = tid; j < n_loc; j += kThreads)
+    if (a + n_sel + j < U) idx_out[a + n_sel + j] = local_lo + j;
+  for (int q = total + tid; q < U; q += kThreads) idx_out[q] = -1;
+  if (tid == 0) *cnt_out = min(total, U);
+}
+
 // Causal top-k + union for one selection problem, run by all 256 threads.
 //   keys[0..n)  orderable scores of the candidate blocks c0 .. c0+n-1 (LDS)
 //   cur         the query's block; candidates are the causal blocks that are
@@ -345,8 +472,15 @@ __device__ __forceinline__ void topk_union_regs(const uint32_t* keys, int n, int
 // with -1) and *cnt_out.  Ranking: key descending, block id ascending.
 __device__ __forceinline__ void topk_union(const uint32_t* keys, int n, int c0, int topk, int cur, int n_init,
                                            int n_local, int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh) {
-  if (n <= 8 * kThreads) topk_union_regs<8>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
-  else topk_union_regs<48>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
+  if (n <= 8 * kThreads) {
+    uint32_t kin[8];
+    const int i0 = (int)threadIdx.x * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kin[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
+    topk_union_fast(n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+  } else {
+    topk_union_regs<48>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
+  }
 }
 
 // Copy of 16 bytes per lane from global memory straight into LDS

@@ -153,8 +153,11 @@ hipError_t launch_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, in
 struct DecodeLayerArgs {
   AttnDecodeArgs attn;               // this layer's attention (ring must be 0); ws = the whole workspace
   float* kc; int64_t nb_cap;         // this layer's compressed keys (newest block updated)
+  const float* scores;               // this layer's candidate scores (nullptr: idx/cnt are given)
+  int32_t* idx; int32_t* cnt;        // this layer's lists (written from scores when given)
   const void* x; const void* w; int hidden;               // Forecast projection (x == nullptr: no next layer)
-  const float* kc_next; int32_t* idx_next; int32_t* cnt_next;
+  const float* kc_next; float* scores_next;           // deferred mode: the next layer's scores
+  int32_t* idx_next; int32_t* cnt_next;                 // immediate mode: the next layer's lists
   int topk, n_init, n_local;
   int stages;                        // bit mask of the two launches
 };

@@ -324,6 +324,62 @@ __device__ __forceinline__ void score_slice_wg(const float* fvec, const float* _
   }
 }
 
+// Scoring of one slice of a (b, g)'s candidates with the Forecast taken
+// from the projection splits (written by an earlier kernel).  The loads of
+// the slice's first rows are issued before the splits are added, so both
+// round trips overlap; then as score_slice_wg.  CO: the scores are stored
+// agent-coherent (read by another workgroup of the same launch); else plain
+// stores (read by a later kernel).
+template <int D, bool CO>
+__device__ __forceinline__ void score_slice_proj_wg(const float* __restrict__ part, int n_splits, int B, int N, int b,
+                                                    int g, const float* __restrict__ kc_bg, int lo, int hi,
+                                                    float* __restrict__ sc, float* fvec) {
+  constexpr int LPR = 8;
+  constexpr int F4 = D / 4 / LPR;
+  constexpr int RPP = kThreads / LPR;   // 32 rows per pass
+  constexpr int UNR = 4;
+  const int sub = threadIdx.x % LPR, row0 = threadIdx.x / LPR;
+  float4 kv[UNR][F4];
+  auto issue = [&](int base) {
+#pragma unroll
+    for (int uu = 0; uu < UNR; ++uu) {
+      const int j = base + row0 + uu * RPP;
+      if (j < hi) {
+#pragma unroll
+        for (int i = 0; i < F4; ++i) kv[uu][i] = ld16f_nt(kc_bg + (int64_t)j * D + (i * LPR + sub) * 4);
+      }
+    }
+  };
+  issue(lo);
+  for (int i = threadIdx.x; i < D; i += kThreads) fvec[i] = proj_reduce_one(part, n_splits, B, N, b, g * D + i);
+  __syncthreads();
+  float4 fv[F4];
+#pragma unroll
+  for (int i = 0; i < F4; ++i) fv[i] = *reinterpret_cast<const float4*>(fvec + (i * LPR + sub) * 4);
+  for (int base = lo; base < hi; base += RPP * UNR) {
+    if (base != lo) issue(base);
+#pragma unroll
+    for (int uu = 0; uu < UNR; ++uu) {
+      const int j = base + row0 + uu * RPP;
+      float acc = 0.f;
+      if (j < hi) {
+#pragma unroll
+        for (int i = 0; i < F4; ++i) {
+          acc += fv[i].x * kv[uu][i].x;
+          acc += fv[i].y * kv[uu][i].y;
+          acc += fv[i].z * kv[uu][i].z;
+          acc += fv[i].w * kv[uu][i].w;
+        }
+      }
+      acc = sum8(acc);   // the 8 lanes of the row (all active together)
+      if (sub == 0 && j < hi) {
+        if constexpr (CO) st_agent(sc + j, acc);
+        else sc[j] = acc;
+      }
+    }
+  }
+}
+
 // Top-k + union of one decode problem from its score row (written by an
 // earlier kernel, or agent-coherent by this one when CO).  keys: LDS, at
 // least (c1 - c0) entries.
@@ -344,7 +400,7 @@ __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, Dec
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) kin[e] = orderable_key(v[e]);
-    topk_union_regs<8>(keys, n, dc.c0, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+    topk_union_fast(n, dc.c0, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
     return;
   }
   constexpr int PB = 8;   // loads in flight per thread
@@ -393,6 +449,22 @@ struct AttnSmem {
   float alpha[G];
   float red[4][G][D];
 };
+
+// bf16 path (attn_split_mfma_wg): each wave's 16 V rows of the current
+// block, XOR-swizzled in 16-byte chunks; after the block loop the same bytes
+// hold the four waves' unnormalised outputs for the merge.
+template <int D, int G>
+struct AttnMfmaSmem {
+  static_assert(4 * G * D * sizeof(float) <= 4 * 16 * 2 * D, "merge buffer fits the V rows");
+  union {
+    unsigned char v[4][16 * 2 * D];
+    float mo[4][G][D];
+  };
+  float ml[4][G][2];
+};
+
+template <typename T, int D, int G> struct AttnSmemSel { using type = AttnSmem<D, G>; };
+template <int D, int G> struct AttnSmemSel<bf16_bits, D, G> { using type = AttnMfmaSmem<D, G>; };
 
 
 // Register set of one 64-token K/V block.
@@ -615,10 +687,195 @@ __device__ __forceinline__ void attn_split_finish(const AttnDecodeParams& p, int
   }
 }
 
-// CO: the partials are stored agent-coherent (merged by another workgroup
-// of the same launch)
-template <typename T, int D, int G, bool CO = false>
-__device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
+// bf16 decode attention of one split on the matrix cores, one online
+// softmax per wave.  Wave w owns keys 16w..16w+15 of every listed block:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, K straight from 16-byte loads
+//                 (lane: key 16w + l%16, dims 32ks + 8(l/16)..+7), q padded
+//                 to 16 heads; lane l gets keys 4(l/16)+i of head l%16
+//   P^T           the exponentials of those scores, rounded to bf16, are
+//                 already the B operand of v_mfma_f32_16x16x16_bf16 (lane:
+//                 keys 4(l/16)..+3 of head l%16)
+//   O^T += V^T P^T  per 16-column tile of V; V^T comes from the wave's 16 V
+//                 rows staged in its own LDS region and read back with the
+//                 transposing ds_read_b64_tr_b16 (lane 4r+c of each 16-lane
+//                 group reads row r, columns 4c..4c+3; lane i receives column
+//                 i of the four rows)
+// No barrier inside the block loop: a wave touches only its own LDS rows,
+// and LDS operations of one wave complete in order.  The running maximum
+// is lazy: it moves only when some lane's block maximum exceeds it by more
+// than kLazyTau (base 2), so most blocks exchange nothing across lanes and
+// rescale nothing; the four lanes of a head agree on it whenever it moves.
+// The waves' (m, l, O) are merged through LDS once per split.
+constexpr float kLazyTau = 8.f;
+
+template <int D, int G, bool CO>
+__device__ __forceinline__ void attn_split_mfma_wg(const AttnDecodeParams& p, int bg, int split,
+                                                   AttnMfmaSmem<D, G>& sm) {
+  static_assert(G <= 16, "query heads of a group fit the 16 MFMA columns");
+  constexpr int RB = 2 * D;          // bytes of one K/V row
+  constexpr int KS = D / 32;         // k-steps of the QK product
+  constexpr int DT = D / 16;         // 16-column tiles of V
+  constexpr int NVC = D / 32;        // 16-byte V loads per lane (16 rows x D/8 chunks over 64 lanes)
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int Hq = p.Hkv * G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int c = min(p.cnt[bg], p.U);
+  const int u0 = split * p.bps, u1 = min(c, u0 + p.bps);
+  const int64_t L = (p.ring || p.slot) ? p.seq_len[b] : min(p.seq_len[b], p.kv_len);
+
+  // q as the B operand: lane l holds q[head l%16][dims 32ks + 8(l/16) ..+7]
+  const bf16_bits* q = (const bf16_bits*)p.q;
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (l16 < G) raw = ld16(q + ((int64_t)b * Hq + g * G + l16) * D + 32 * ks + 8 * lg);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
+  }
+
+  // buffer resources over this (b, g)'s K and V rows; per-lane byte offsets
+  const bf16_bits* kbase = (const bf16_bits*)p.k + b * p.sb + g * p.sg;
+  const bf16_bits* vbase = (const bf16_bits*)p.v + b * p.sb + g * p.sg;
+  const int64_t span = p.kv_len > 0 ? ((p.kv_len - 1) * p.st + D) * 2 : 0;
+  const int nrec = (int)(span < 0x7fffffff ? span : 0x7fffffff);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
+  const uint32_t ko = (uint32_t)(((16 * w + l16) * (uint32_t)p.st + 8 * lg) * 2);
+  // V: each load instruction of the wave reads whole rows (1 KB contiguous
+  // at D = 128): load i, lane l -> row i * RPI + l / CPR, chunk l % CPR
+  constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                       // rows per load instruction
+  const int vrow = lane / CPR, vch = lane % CPR;
+  const uint32_t vo = (uint32_t)(((16 * w + vrow) * (uint32_t)p.st + 8 * vch) * 2);
+  const uint32_t vstep = (uint32_t)(RPI * p.st * 2);
+  // LDS: row r, logical chunk c at chunk c ^ 2(r mod D/16)
+  unsigned char* vs = sm.v[w];
+  const int tr_r = 4 * lg + (l16 >> 2);               // row of this lane's transposing read
+  const int tr_off = tr_r * RB + 8 * (l16 & 3);
+  const int tr_sw = 2 * (tr_r % (D / 16));
+
+  float m_run = -1e30f, l_part = 0.f;                 // finite start: a masked key gives p = 0
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* list = p.idx + (int64_t)bg * p.U;
+  const int nblk_buf = (int)min(p.kv_len / kBlk, (int64_t)0x7fffffff);
+  const int Lc = (int)min(L, (int64_t)0x7fffffff - kBlk);
+  const int jend = (Lc + kBlk - 1) / kBlk;
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  for (int u = u0; u < u1; ++u) {
+    const int j = list[u];
+    const int loc = p.slot ? p.slot[(int64_t)bg * p.U + u] : (p.ring ? u : j);
+    if (j < 0 || loc < 0 || loc >= nblk_buf || j >= jend) continue;   // nothing of this block is attended
+    const int nvalid = min(kBlk, Lc - j * kBlk);
+    const uint32_t boff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)loc * kBlk * p.st * 2));
+    uint4 kr[KS], vr[NVC];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * ks, (int)boff, 2);
+      kr[ks] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NVC; ++i) {
+      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * vstep, (int)boff, 2);
+      vr[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[ks]), qf[ks], s4, 0, 0, 0);
+    float sv[4], lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (16 * w + 4 * lg + i < nvalid) ? s4[i] * p.qscale : -INFINITY;
+      lmax = fmaxf(lmax, sv[i]);
+    }
+    if (__any(lmax > m_run + kLazyTau)) {
+      float a, bb;
+      swap16(lmax, a, bb);
+      float mx = fmaxf(a, bb);
+      swap32(mx, a, bb);
+      mx = fmaxf(a, bb);
+      const bool up = mx > m_run + kLazyTau;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = up ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    s16x4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h = (__bf16)__builtin_amdgcn_exp2f(sv[i] - m_run);
+      l_part += (float)h;
+      pb[i] = __builtin_bit_cast(short, h);
+    }
+    // V rows of the wave's keys into its LDS rows (rows past the valid keys
+    // as zeros: they meet p = 0, and 0 * NaN would not vanish)
+#pragma unroll
+    for (int i = 0; i < NVC; ++i) {
+      const int r = i * RPI + vrow;
+      *reinterpret_cast<uint4*>(vs + r * RB + (vch ^ (2 * (r % (D / 16)))) * 16) =
+          (16 * w + r < nvalid) ? vr[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + tr_off + ((2 * dt) ^ tr_sw) * 16));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
+    }
+  }
+
+  // merge the four waves: lane l holds O[head l%16][d = 16dt + 4(l/16) + i]
+  {
+    float a, bb;
+    swap16(l_part, a, bb);
+    const float l2 = a + bb;
+    swap32(l2, a, bb);
+    l_part = a + bb;
+  }
+  __syncthreads();                                    // every wave is done with its V rows
+  if (l16 < G) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(&sm.mo[w][l16][16 * dt + 4 * lg]) = o[dt];
+    if (lg == 0) {
+      sm.ml[w][l16][0] = m_run;
+      sm.ml[w][l16][1] = l_part;
+    }
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)bg * p.n_splits + split) * G;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, d = i % D;
+    const float M = fmaxf(fmaxf(sm.ml[0][h][0], sm.ml[1][h][0]), fmaxf(sm.ml[2][h][0], sm.ml[3][h][0]));
+    float acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) acc += __builtin_amdgcn_exp2f(sm.ml[ww][h][0] - M) * sm.mo[ww][h][d];
+    if constexpr (CO) st_agent(p.ws_o + (pbase + h) * D + d, acc);
+    else p.ws_o[(pbase + h) * D + d] = acc;
+  }
+  if (tid < G) {
+    const int h = tid;
+    const float M = fmaxf(fmaxf(sm.ml[0][h][0], sm.ml[1][h][0]), fmaxf(sm.ml[2][h][0], sm.ml[3][h][0]));
+    float l = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) l += __builtin_amdgcn_exp2f(sm.ml[ww][h][0] - M) * sm.ml[ww][h][1];
+    if constexpr (CO) {
+      st_agent(p.ws_ml + (pbase + h) * 2 + 0, M);
+      st_agent(p.ws_ml + (pbase + h) * 2 + 1, l);
+    } else {
+      p.ws_ml[(pbase + h) * 2 + 0] = M;
+      p.ws_ml[(pbase + h) * 2 + 1] = l;
+    }
+  }
+}
+
+// fp32 decode attention of one split (VALU): one block at a time for the
+// whole workgroup, scores and softmax weights exchanged through LDS.
+template <typename T, int D, int G, bool CO>
+__device__ __forceinline__ void attn_split_valu_wg(const AttnDecodeParams& p, int bg, int split, AttnSmem<D, G>& sm) {
   using R = AttnRegs<T, D, G>;
   constexpr int VEC = R::VEC;
   constexpr int HW = (G + 3) / 4;
@@ -696,6 +953,18 @@ __device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg,
   }
 
   attn_split_finish<T, D, G, CO>(p, bg, split, sm, acc, m_run, l_run);
+}
+
+// CO: the partials are stored agent-coherent (merged by another workgroup
+// of the same launch)
+template <typename T, int D, int G, bool CO = false>
+__device__ __forceinline__ void attn_split_wg(const AttnDecodeParams& p, int bg, int split,
+                                              typename AttnSmemSel<T, D, G>::type& sm) {
+  if constexpr (std::is_same<T, bf16_bits>::value) {
+    attn_split_mfma_wg<D, G, CO>(p, bg, split, sm);
+  } else {
+    attn_split_valu_wg<T, D, G, CO>(p, bg, split, sm);
+  }
 }
 
 // Merge the splits of one KV head (written by an earlier kernel), in split

@@ -3,26 +3,31 @@
 // Source: "SparDA: a fourth projection that lets sparse attention prefetch
 // its own KV cache" -- "The fourth projection", Eq. 4 and Alg. 2: right
 // after layer l's projection emits the Forecast F_l, it scores layer l+1's
-// compressed keys and picks layer l+1's blocks, while layer l attends to the
-// blocks picked one layer earlier.  Chinese SparDA overview
+// compressed keys, which picks layer l+1's blocks, while layer l attends to
+// the blocks picked one layer earlier.  Chinese SparDA overview
 // (deepresearch2agi.pages.dev), 架构细节: the selection of the next layer runs
 // beside the current layer's attention.
 //
 // The two launches keep the real data dependencies of a layer (the output
 // of layer l feeds the next layer's input, hence its Forecast):
-//   K1  Forecast projection partials of F_l (128-row splits)
+//   K1  the top-k + union of THIS layer's blocks, from the candidate scores
+//       the previous layer's call left (when given), beside the Forecast
+//       projection partials of F_l (128-row splits)
 //   K2  scores of layer l+1's candidates (each workgroup first adds the
-//       projection splits of its (b, g) in order); the last score workgroup
-//       of a (b, g) to finish runs that (b, g)'s top-k + union
+//       projection splits of its (b, g) in order), stored for the next
+//       layer's call
 //       + attention splits of layer l over its listed blocks; the last split
 //       of a (b, g) to finish merges the splits and updates layer l's
 //       compressed keys with the newest block
-// K2 streams the compressed keys of l+1 and the selected K/V of l together,
-// so the scoring and the attention share the HBM pipe instead of running
-// back to back, and the per-(b, g) follow-up work (top-k, merge) runs while
-// other workgroups still stream instead of in a third launch.  Roles are
-// assigned by workgroup index; no workgroup waits for another: the last one
-// to arrive at a (b, g)'s counter does the follow-up.
+// The top-k of layer l+1 then runs in the next call's K1, where it shares a
+// short, latency-bound launch with the projection (deferred mode).  In the
+// immediate mode the scores go to the workspace instead and the last score
+// workgroup of each (b, g) to finish runs that (b, g)'s top-k inside K2,
+// while the long attention chains are still streaming.  K2 streams the
+// compressed keys of l+1 and the selected K/V of l together, so the scoring
+// and the attention share the HBM pipe.  Roles are assigned by workgroup
+// index; no workgroup waits for another: the last attention split to arrive
+// at a (b, g)'s counter does the merge.
 #include "bskv_launch.hpp"
 #include "decode_ops.hpp"
 
@@ -32,18 +37,22 @@ struct LayerParams {
   // this layer: incremental compressed-key update
   const void* k; int64_t sb, sg, st, kv_len; const int64_t* seq_len;
   float* kc; int64_t nb_cap;
-  // this layer: attention (q, k, v, idx, cnt, out inside)
+  // this layer: top-k + union from the previous call's scores (nullptr: the
+  // lists are given), then attention (q, k, v, idx, cnt, out inside)
+  const float* scores_in; int32_t* idx; int32_t* cnt;
   AttnDecodeParams attn;
-  // lookahead: Forecast of this layer -> selection of the next layer
+  // lookahead: Forecast of this layer -> scores of the next layer
   int select;                       // 0: no next layer
   const void* x; const void* w; int hidden, N;
   float* proj_part; int proj_tiles, proj_splits;
-  const float* kc_next; float* scores; int score_splits;
+  const float* kc_next; float* scores_next; int score_splits;
+  // immediate mode (idx_next != nullptr): the scores go to the workspace
+  // and the last score workgroup of each (b, g) runs the next layer's top-k
   int32_t* idx_next; int32_t* cnt_next;
   int B, H, topk, n_init, n_local, U;
-  // arrival counters of K2: [0, B*H) score workgroups, [B*H, 2*B*H)
-  // attention splits; zero before a launch (a zero-filled workspace) and
-  // left at zero by each counter's last arrival
+  // arrival counters of K2: [0, B*H) attention splits, [B*H, 2*B*H) score
+  // slices (immediate mode), one per (b, g); zero before a launch (a
+  // zero-filled workspace) and left at zero by each counter's last arrival
   int32_t* sync;
 };
 
@@ -67,26 +76,39 @@ __device__ __forceinline__ bool arrive_last(int32_t* ctr, int n, int& flag) {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
-  if constexpr (std::is_same<T, bf16_bits>::value) {
-    __shared__ ProjMfmaSmem sm;
-    proj_partial_mfma_wg((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, blockIdx.x % p.proj_tiles,
-                         blockIdx.x / p.proj_tiles, p.proj_part, sm);
-  } else {
-    __shared__ ProjSmem sm;
-    proj_partial_wg<T>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, blockIdx.x % p.proj_tiles,
-                       blockIdx.x / p.proj_tiles, p.proj_part, sm);
+  extern __shared__ uint32_t keys[];   // top-k keys of problems above 8 * kThreads candidates
+  constexpr bool kMfma = std::is_same<T, bf16_bits>::value;
+  __shared__ __attribute__((aligned(16))) union {
+    typename std::conditional<kMfma, ProjMfmaSmem, ProjSmem>::type proj;
+    TopkShared topk;
+  } sm;
+  const int n_topk = p.scores_in ? p.B * p.H : 0;
+  if ((int)blockIdx.x < n_topk) {
+    // this layer's top-k + union (the longer chain: its workgroups go first)
+    const int bg = blockIdx.x;
+    const DecodeCands dc = decode_cands(p.seq_len[bg / p.H], p.nb_cap, p.n_init, p.n_local);
+    topk_decode_wg(p.scores_in + (int64_t)bg * p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
+                   p.idx + (int64_t)bg * p.U, p.cnt + bg, keys, sm.topk);
+    return;
   }
+  const int pid = (int)blockIdx.x - n_topk;
+  if constexpr (kMfma)
+    proj_partial_mfma_wg((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles, pid / p.proj_tiles,
+                         p.proj_part, sm.proj);
+  else
+    proj_partial_wg<T>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles, pid / p.proj_tiles,
+                       p.proj_part, sm.proj);
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
-  extern __shared__ uint32_t keys[];   // top-k keys of problems above 8 * kThreads candidates
+__global__ __launch_bounds__(kThreads, 4) void layer_k2(LayerParams p) {
+  extern __shared__ uint32_t keys[];   // immediate mode: top-k keys of problems above 8 * kThreads candidates
   __shared__ __attribute__((aligned(16))) union {
-    AttnSmem<D, G> attn;
+    typename AttnSmemSel<T, D, G>::type attn;
     float fvec[D];
-    TopkShared topk;
     CombineSmem<D, G> comb;
     MeanpoolSmem<T, D> mp;
+    TopkShared topk;
   } sm;
   __shared__ int last_flag;
   const int n_bg = p.B * p.H;
@@ -98,19 +120,22 @@ __global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
   if (bid < n_score) {
     const int split = bid % p.score_splits, bg = bid / p.score_splits;
     const int b = bg / p.H, g = bg % p.H;
-    for (int i = threadIdx.x; i < D; i += kThreads)
-      sm.fvec[i] = proj_reduce_one(p.proj_part, p.proj_splits, p.B, p.N, b, g * D + i);
-    __syncthreads();
     const DecodeCands dc = decode_cands(p.seq_len[b], p.nb_cap, p.n_init, p.n_local);
     const int n = dc.c1 - dc.c0;
     const int per = (n + p.score_splits - 1) / p.score_splits;
     const int lo = dc.c0 + split * per, hi = min(dc.c1, lo + per);
-    score_slice_wg<D, true>(sm.fvec, p.kc_next + (int64_t)bg * p.nb_cap * D, lo, hi,
-                            p.scores + (int64_t)bg * p.nb_cap);
-    // the last score workgroup of (b, g): top-k + union of layer l+1
-    if (arrive_last(p.sync + bg, p.score_splits, last_flag))
-      topk_decode_wg<true>(p.scores + (int64_t)bg * p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
-                     p.idx_next + (int64_t)bg * p.U, p.cnt_next + bg, keys, sm.topk);
+    float* sc = p.scores_next + (int64_t)bg * p.nb_cap;
+    if (!p.idx_next) {
+      score_slice_proj_wg<D, false>(p.proj_part, p.proj_splits, p.B, p.N, b, g, p.kc_next + (int64_t)bg * p.nb_cap * D,
+                                    lo, hi, sc, sm.fvec);
+      return;
+    }
+    score_slice_proj_wg<D, true>(p.proj_part, p.proj_splits, p.B, p.N, b, g, p.kc_next + (int64_t)bg * p.nb_cap * D,
+                                 lo, hi, sc, sm.fvec);
+    // the last score workgroup of (b, g): top-k + union of the next layer
+    if (arrive_last(p.sync + n_bg + bg, p.score_splits, last_flag))
+      topk_decode_wg<true>(sc, dc, p.topk, p.n_init, p.n_local, p.U, p.idx_next + (int64_t)bg * p.U, p.cnt_next + bg,
+                           keys, sm.topk);
     return;
   }
   const int a = bid - n_score;
@@ -119,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void layer_k2(LayerParams p) {
   // the last attention split of (b, g): merge of the splits, then the
   // newest-block update of this layer's compressed keys (the block the
   // newest token completed)
-  if (!arrive_last(p.sync + n_bg + bg, p.attn.n_splits, last_flag)) return;
+  if (!arrive_last(p.sync + bg, p.attn.n_splits, last_flag)) return;
   attn_combine_wg<D, G, true>(p.attn, bg, sm.comb);
   __syncthreads();
   const int b = bg / p.H, g = bg % p.H;
@@ -143,8 +168,8 @@ static size_t al256(size_t x) { return ((x + 255) / 256) * 256; }
 // other arguments are, so one workspace can serve layers with and without a
 // lookahead (whose projection partials are absent) and the counters always
 // land on the words every earlier call left at zero; then the projection
-// partials, the candidate scores and the attention split partials, which
-// every call writes before it reads them.
+// partials, the next layer's candidate scores (immediate mode) and the
+// attention split partials, which every call writes before it reads them.
 size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype) {
   return al256((size_t)2 * B * Hkv * sizeof(int32_t)) + al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) +
          al256((size_t)B * Hkv * nb_cap * sizeof(float)) + attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
@@ -153,13 +178,16 @@ size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t 
 template <typename T, int D, int G>
 static void launch_layer_t(const LayerParams& p, int stages, hipStream_t s) {
   const int n_bg = p.B * p.H;
+  const int n_topk = p.scores_in ? n_bg : 0;
   const int n_proj = p.select ? p.proj_tiles * p.proj_splits : 0;
-  if ((stages & 1) && n_proj > 0) hipLaunchKernelGGL((layer_k1<T>), dim3(n_proj), dim3(kThreads), 0, s, p);
-  const int n_score = p.select ? p.score_splits * n_bg : 0;
   const int64_t cap = p.nb_cap < kMaxCandidates ? p.nb_cap : kMaxCandidates;
-  const size_t lds = (p.select && cap > 8 * kThreads) ? (size_t)cap * sizeof(uint32_t) : 0;
+  const size_t lds = (n_topk > 0 && cap > 8 * kThreads) ? (size_t)cap * sizeof(uint32_t) : 0;
+  if ((stages & 1) && n_topk + n_proj > 0)
+    hipLaunchKernelGGL((layer_k1<T>), dim3(n_topk + n_proj), dim3(kThreads), lds, s, p);
+  const int n_score = p.select ? p.score_splits * n_bg : 0;
+  const size_t lds2 = (p.select && p.idx_next && cap > 8 * kThreads) ? (size_t)cap * sizeof(uint32_t) : 0;
   if (stages & 2)
-    hipLaunchKernelGGL((layer_k2<T, D, G>), dim3(n_score + p.attn.n_splits * n_bg), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL((layer_k2<T, D, G>), dim3(n_score + p.attn.n_splits * n_bg), dim3(kThreads), lds2, s, p);
 }
 
 template <typename T, int D>
@@ -176,10 +204,11 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   LayerParams p;
   p.k = a.attn.k; p.sb = a.attn.sb; p.sg = a.attn.sg; p.st = a.attn.st; p.kv_len = a.attn.kv_len;
   p.seq_len = a.attn.seq_len; p.kc = a.kc; p.nb_cap = a.nb_cap;
+  p.scores_in = a.scores; p.idx = a.idx; p.cnt = a.cnt;
   const int H = a.attn.Hkv, D = a.attn.D, B = a.attn.B;
+  const size_t sync_b = al256((size_t)2 * B * H * sizeof(int32_t));
   const size_t proj_b = al256(proj_workspace_bytes(B, a.hidden, H * D, a.attn.dtype));
   const size_t score_b = al256((size_t)B * H * a.nb_cap * sizeof(float));
-  const size_t sync_b = al256((size_t)2 * B * H * sizeof(int32_t));
   char* ws = (char*)a.attn.ws;
   p.sync = (int32_t*)ws;
   p.attn = make_attn_params(a.attn, ws + sync_b + proj_b + score_b);
@@ -188,9 +217,10 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   p.proj_part = (float*)(ws + sync_b);
   p.proj_tiles = p.select ? proj_tiles(H * D, a.attn.dtype) : 0;
   p.proj_splits = p.select ? proj_splits(a.hidden) : 0;
-  p.kc_next = a.kc_next; p.scores = (float*)(ws + sync_b + proj_b);
-  p.score_splits = score_split_plan(B * H, a.nb_cap);
+  p.kc_next = a.kc_next;
   p.idx_next = a.idx_next; p.cnt_next = a.cnt_next;
+  p.scores_next = a.idx_next ? (float*)(ws + sync_b + proj_b) : a.scores_next;
+  p.score_splits = score_split_plan(B * H, a.nb_cap);
   p.B = B; p.H = H; p.topk = a.topk; p.n_init = a.n_init; p.n_local = a.n_local; p.U = a.attn.U;
   const int G = a.attn.Hq / H;
   if (a.attn.dtype == 0) {

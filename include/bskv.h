@@ -419,21 +419,38 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
 /* ----------------------------------------------------------------------- *
  * One decode layer with one-layer-ahead selection.  [EXPL] "The fourth
  * projection", Alg. 2 and Eq. 4: right after layer l's projection emits the
- * Forecast F_l, it scores layer l+1's compressed keys and picks layer l+1's
- * blocks while layer l attends to the blocks picked one layer earlier.
+ * Forecast F_l, it scores layer l+1's compressed keys, which picks layer
+ * l+1's blocks, while layer l attends to the blocks picked one layer earlier.
  * Equivalent to this sequence of the calls above, in two kernels:
- *   kv_block_meanpool(k, newest_only=1)  -> kc           (this layer)
- *   forecast_proj(x, w_forecast)         -> F            (this layer's Forecast)
- *   forecast_block_score_topk(F, kc_next) -> idx_next, cnt_next (next layer)
- *   block_sparse_attn_decode(q, k, v, idx, cnt) -> out   (this layer)
- * with the same layouts as those calls (kc and kc_next: [B, Hkv, kc_nb_cap,
- * d]; U = topk + n_init + n_local for idx and idx_next; kc and kc_next must
- * not overlap).  The scoring of the next layer and this layer's attention
- * share one launch, which also runs each (b, g)'s top-k as soon as its last
- * score slice is written and each (b, g)'s merge of the attention splits
- * (then the newest-block update of kc) as soon as its last split is done.
- * x, w_forecast, kc_next, idx_next, cnt_next are all given or all NULL
- * (NULL: the last layer, no selection).  hidden must be a multiple of 256.
+ *   [scores != NULL] top-k + union of this layer from `scores`
+ *                                          -> idx, cnt     (this layer)
+ *   kv_block_meanpool(k, newest_only=1)    -> kc           (this layer)
+ *   forecast_proj(x, w_forecast)           -> F            (this layer's Forecast)
+ *   the next layer's selection from F against kc_next, in one of two forms:
+ *     immediate (idx_next, cnt_next given): forecast_block_score_topk(F,
+ *       kc_next) -> idx_next, cnt_next; the top-k of each (b, g) runs inside
+ *       the second kernel as soon as that (b, g)'s scores are complete
+ *     deferred (scores_next given): only the raw scores of the next layer's
+ *       candidate blocks, scores_next[b, g, j] = F[b, g] . kc_next[b, g, j]
+ *       (the causal blocks that are neither initial nor local, see
+ *       bskv_forecast_block_score_topk; other entries are not written); the
+ *       next layer's call, given them as `scores`, turns them into its list
+ *       in its first kernel, beside its projection
+ *   block_sparse_attn_decode(q, k, v, idx, cnt) -> out     (this layer)
+ * Both forms give the same lists (same ranking and union as
+ * bskv_forecast_block_score_topk).  Pass scores = NULL when idx/cnt already
+ * hold this layer's list (layer 0, selected by its own projection, or any
+ * layer after an immediate-mode call).
+ * Layouts as in those calls: kc, kc_next [B, Hkv, kc_nb_cap, d] fp32 (must
+ * not overlap); scores, scores_next [B, Hkv, kc_nb_cap] fp32; idx, idx_next
+ * [B, Hkv, U] int32 with U = topk + n_init + n_local, cnt, cnt_next [B, Hkv]
+ * int32 (idx/cnt are outputs when scores != NULL, inputs otherwise).  The
+ * attention's split partials are merged by the last split of each (b, g) to
+ * finish, which then updates kc with the newest block.
+ * x, w_forecast, kc_next and one form of the next layer's selection
+ * (scores_next, or idx_next with cnt_next) are all given or all NULL (NULL:
+ * the last layer, no lookahead); giving both forms is BSKV_EINVAL.  hidden
+ * must be a multiple of 256.
  * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL,
  * zero-filled once before its first use: its first 2*B*n_kv_heads int32
  * words are K2's arrival counters, at that fixed offset for every call, and
@@ -441,21 +458,24 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
  * every layer of a model, last layer included (size it for the largest
  * layout, i.e. with the lookahead's hidden); calls that share one ws must
  * not overlap in time.
- * stages: bit 0 = K1 (projection partials), bit 1 = K2 (next-layer scores
- * and top-k, this layer's attention, merge and kc update); 3 runs the whole
- * layer.  K2 reads what K1 left in ws, so a caller may launch them
- * separately (to place other work between them, or to time each), in order,
- * with the same ws and arguments.  Stages outside 1..3: BSKV_EINVAL.
+ * stages: bit 0 = K1 (this layer's top-k when scores is given, projection
+ * partials when x is given), bit 1 = K2 (next-layer scores [and top-k], this
+ * layer's attention, merge and kc update); 3 runs the whole layer.  K2 reads
+ * what K1 left in ws and idx/cnt, so a caller may launch them separately (to
+ * place other work between them, or to time each), in order, with the same
+ * ws and arguments.  Stages outside 1..3: BSKV_EINVAL.
  * ----------------------------------------------------------------------- */
 size_t bskv_decode_layer_lookahead_workspace(int B, int n_q_heads, int n_kv_heads, int head_dim, int hidden,
                                              int64_t kc_nb_cap, int U, int dtype);
 int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int dtype,
                                 const int64_t* kv_strides, int64_t kv_len, const int64_t* seq_len,
-                                float* kc, const int32_t* idx, const int32_t* cnt, float scale, float* out,
-                                const void* x, const void* w_forecast, int hidden, const float* kc_next,
-                                int32_t* idx_next, int32_t* cnt_next, int B, int n_q_heads, int n_kv_heads,
-                                int head_dim, int block, int64_t kc_nb_cap, int topk, int n_init,
-                                int n_local, int stages, void* ws, size_t ws_bytes, hipStream_t stream);
+                                float* kc, const float* scores, int32_t* idx, int32_t* cnt, float scale,
+                                float* out, const void* x, const void* w_forecast, int hidden,
+                                const float* kc_next, float* scores_next, int32_t* idx_next,
+                                int32_t* cnt_next, int B, int n_q_heads,
+                                int n_kv_heads, int head_dim, int block, int64_t kc_nb_cap, int topk,
+                                int n_init, int n_local, int stages, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* Device address of host memory allocated pinned (hipHostMalloc, or a torch
  * tensor created with pin_memory=True).  Returns BSKV_EHIP if the pointer is

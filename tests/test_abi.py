@@ -307,12 +307,16 @@ def test_decode_layer_validation():
     ws = lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 4096, 2048, 69, 1)
     assert ws > lib.bskv_decode_layer_lookahead_workspace(8, 32, 8, 128, 0, 2048, 69, 1)
 
-    def call(x=P, w=P, kcn=P, idn=P, cnn=P, hidden=4096, stages=3, dt=1, hq=32, nl=4, wsb=ws, kv_len=131072):
-        return f(P, P, P, dt, S3, kv_len, P, P, P, P, 0.088, P, x, w, hidden, kcn, idn, cnn, 8, hq, 8, 128, 64, 2048,
-                 64, 1, nl, stages, P, wsb, None)
+    def call(x=P, w=P, kcn=P, scn=P, sc=P, hidden=4096, stages=3, dt=1, hq=32, nl=4, wsb=ws, kv_len=131072,
+             idx=P, idn=None, cnn=None):
+        return f(P, P, P, dt, S3, kv_len, P, P, sc, idx, P, 0.088, P, x, w, hidden, kcn, scn, idn, cnn, 8, hq, 8, 128,
+                 64, 2048, 64, 1, nl, stages, P, wsb, None)
     assert call(kv_len=131072 - 1) == EINVAL     # K/V buffers hold whole blocks
     assert call(x=None) == EINVAL            # lookahead arguments: all or none
-    assert call(idn=None) == EINVAL
+    assert call(scn=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(idn=P, cnn=P) == EINVAL           # both forms of the next selection
+    assert call(scn=None, idn=P) == EINVAL        # immediate mode needs both lists
     assert call(stages=0) == EINVAL
     assert call(stages=4) == EINVAL
     assert call(dt=3) == EDTYPE

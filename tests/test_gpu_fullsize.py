@@ -15,7 +15,8 @@ DEV = torch.device("cuda:0")
 
 def test_config3_two_layers_sampled():
     """B8, T=131072, top-64 + 1 + 4: layer 0 selected by the layer-0
-    projection, layer 1 by layer 0's Forecast (fused layer call)."""
+    projection, layer 1 by layer 0's Forecast (the fused layer calls: layer
+    0's call scores layer 1's candidates, layer 1's call selects from them)."""
     wl = CONFIGS[3]
     L = 2
     layers = decode_inputs(wl, DEV, layers=L)
@@ -28,11 +29,12 @@ def test_config3_two_layers_sampled():
     f0 = bskv.forecast_proj(layers[0]["x_sel"], layers[0]["w_sel"], wl.Hkv, wl.d)
     idx0, cnt0 = bskv.forecast_block_score_topk(f0, kc[0], wl.topk, wl.n_init, wl.n_local, seq_len=layers[0]["seq_len"])
     l0, l1 = layers
-    out0, idx1, cnt1 = bskv.decode_layer_lookahead(l0["q"], l0["k"], l0["v"], l0["seq_len"], kc[0], idx0, cnt0,
-                                                   wl.scale, x=l1["x_sel"], w=l1["w_sel"], kc_next=kc[1],
-                                                   topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local)
-    out1, _, _ = bskv.decode_layer_lookahead(l1["q"], l1["k"], l1["v"], l1["seq_len"], kc[1], idx1, cnt1, wl.scale,
-                                             topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local)
+    out0, sc1 = bskv.decode_layer_lookahead(l0["q"], l0["k"], l0["v"], l0["seq_len"], kc[0], idx0, cnt0,
+                                            wl.scale, x=l1["x_sel"], w=l1["w_sel"], kc_next=kc[1],
+                                            topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local)
+    idx1, cnt1 = torch.empty_like(idx0), torch.empty_like(cnt0)
+    out1, _ = bskv.decode_layer_lookahead(l1["q"], l1["k"], l1["v"], l1["seq_len"], kc[1], idx1, cnt1, wl.scale,
+                                          scores=sc1, topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local)
     torch.cuda.synchronize()
     sel_gpu = [(idx0, cnt0, out0), (idx1, cnt1, out1)]
     for b in (0, wl.B - 1):

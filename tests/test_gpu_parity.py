@@ -892,6 +892,19 @@ def _layer_case(dtype, d, G, B, T, lens, seed):
     return c, c2, kc, kc_next, idx, cnt
 
 
+def _next_lists(c, kc, scores, topk, n_init, n_local, ws=None):
+    """The next layer's lists from the scores a lookahead call left: the
+    top-k stage alone (stage 1, scores given, no lookahead)."""
+    U = topk + n_init + n_local
+    B, Hkv = kc.shape[0], kc.shape[1]
+    idx = torch.full((B, Hkv, U), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    kw = {} if ws is None else {"ws": ws}
+    bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc, idx, cnt, scores=scores, topk=topk,
+                                n_init=n_init, n_local=n_local, stages=1, **kw)
+    return idx, cnt
+
+
 @pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2), ("bf16", 64, 8)])
 def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     lens = [64 * 30, 64 * 30 - 5, 64 * 17, 64 * 30]
@@ -906,9 +919,10 @@ def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     f = bskv.forecast_proj(c["x_sel"], c["w_sel"], 4, d)
     idx_a, cnt_a = bskv.forecast_block_score_topk(f, kc_next, 6, 1, 2, seq_len=c["seq_len"])
     out_a = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
-    out_b, idx_b, cnt_b = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_b, idx, cnt, scale,
-                                                      x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
-                                                      n_local=2)
+    out_b, sc_next = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_b, idx, cnt, scale,
+                                                 x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
+                                                 n_local=2)
+    idx_b, cnt_b = _next_lists(c2, kc_next, sc_next, 6, 1, 2)
     torch.cuda.synchronize()
     assert torch.equal(kc_a.nan_to_num(7.0), kc_b.nan_to_num(7.0))
     assert torch.equal(idx_a, idx_b) and torch.equal(cnt_a, cnt_b)
@@ -919,32 +933,62 @@ def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     kc_next_or = orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens)
     sel = orc.decode_select(f_or, kc_next_or, lens_np, 6, 1, 2, 64)
     check_selection(idx_b, cnt_b, sel, 6)
+    # the raw candidate scores handed to the next call, against the oracle's
+    sc = np64(sc_next)
+    for bg in range(sc.shape[0] * sc.shape[1]):
+        b, g = divmod(bg, sc.shape[1])
+        for j, v in sel.scores[bg].items():
+            assert abs(sc[b, g, j] - v) <= 1e-4 * max(1.0, abs(v)), (b, g, j)
     want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens_np,
                              scale, 64)
     assert max_abs(np64(out_b), want) < (1e-4 if dtype == "f32" else 2e-2)
 
 
-def test_decode_layer_graph_replays():
-    """The one-launch follow-up work (top-k of the last score slice, merge of
-    the last attention split) hands results over through arrival counters in
-    the workspace, which every launch leaves at zero: replays of a captured
-    layer, with eager calls between them, match the eager result exactly."""
-    lens = [64 * 20, 64 * 20 - 3]
-    c, _, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 21)
-    kc_e = kc.clone()
-    out_e, i_e, n_e = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_e, idx, cnt,
-                                                  x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
-                                                  n_local=2)
+def test_decode_layer_top_k_from_scores_in_the_same_call():
+    """A call given the previous call's scores writes its own lists first
+    and attends over them: equal to the lists and output of the per-op
+    selection and attention."""
+    lens = [64 * 30, 64 * 23 + 9]
+    c, c2, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 30, lens, 13)
+    scale = 1.0 / math.sqrt(128)
+    _, sc1 = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, scale,
+                                         x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
+    # layer 1 (c2's q/k/v), selected by layer 0's scores, is also the last layer
+    i1 = torch.full_like(idx, -7)
+    n1 = torch.full_like(cnt, -7)
+    out1, none = bskv.decode_layer_lookahead(c2["q"], c2["k"], c2["v"], c2["seq_len"], kc_next.clone(), i1, n1, scale,
+                                             scores=sc1, topk=6, n_init=1, n_local=2)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], 4, 128)
+    i_ref, n_ref = bskv.forecast_block_score_topk(f, kc_next, 6, 1, 2, seq_len=c["seq_len"])
+    out_ref = bskv.block_sparse_attn_decode(c2["q"], c2["k"], c2["v"], i_ref, n_ref, c2["seq_len"], scale)
     torch.cuda.synchronize()
-    kc_g = kc.clone()
-    out_g, i_g, n_g = torch.empty_like(out_e), torch.empty_like(i_e), torch.empty_like(n_e)
+    assert none is None
+    assert torch.equal(i1, i_ref) and torch.equal(n1, n_ref) and torch.equal(out1, out_ref)
+
+
+def test_decode_layer_graph_replays():
+    """The merge of the last attention split hands results over through
+    arrival counters in the workspace, which every launch leaves at zero:
+    replays of a captured pair of layer calls (lookahead, then the next
+    layer from its scores), with eager calls between them, match the eager
+    result exactly."""
+    lens = [64 * 20, 64 * 20 - 3]
+    c, c2, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 21)
     ws = torch.zeros(bskv.workspace_bytes("layer", 2, 16, 4, 128, 512, kc.shape[2], 9, 1), dtype=torch.uint8,
                      device=DEV)
+    kc_g, kcn_g = kc.clone(), kc_next.clone()
+    out_g, out2_g = torch.empty(2, 16, 128, device=DEV), torch.empty(2, 16, 128, device=DEV)
+    sc = torch.empty(2, 4, kc.shape[2], device=DEV)
+    i_g, n_g = torch.empty_like(idx), torch.empty_like(cnt)
 
     def call():
         bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_g, idx, cnt, out=out_g, x=c["x_sel"],
-                                    w=c["w_sel"], kc_next=kc_next, idx_next=i_g, cnt_next=n_g, topk=6, n_init=1,
-                                    n_local=2, ws=ws)
+                                    w=c["w_sel"], kc_next=kc_next, scores_next=sc, topk=6, n_init=1, n_local=2, ws=ws)
+        bskv.decode_layer_lookahead(c2["q"], c2["k"], c2["v"], c2["seq_len"], kcn_g, i_g, n_g, out=out2_g, scores=sc,
+                                    topk=6, n_init=1, n_local=2, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out_g, out2_g, i_g, n_g, kc_g, kcn_g)]
     s_ = torch.cuda.Stream()
     s_.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s_):
@@ -956,35 +1000,37 @@ def test_decode_layer_graph_replays():
         call()
     for rep in range(3):
         out_g.zero_()
+        out2_g.zero_()
         i_g.fill_(-7)
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out_g, out_e) and torch.equal(i_g, i_e) and torch.equal(n_g, n_e), rep
-        # rows of blocks that are not complete yet hold NaN in both
-        assert torch.equal(torch.nan_to_num(kc_g, nan=7.0), torch.nan_to_num(kc_e, nan=7.0)), rep
-        # eager work between the replays, on the same workspace
-        call()
+        got = (out_g, out2_g, i_g, n_g, kc_g, kcn_g)
+        for a_, b_ in zip(got, ref):
+            assert torch.equal(torch.nan_to_num(a_, nan=7.0), torch.nan_to_num(b_, nan=7.0)), rep
+        call()                     # eager work between the replays, on the same workspace
         torch.cuda.synchronize()
-        assert torch.equal(out_g, out_e) and torch.equal(i_g, i_e), rep
+        assert torch.equal(out2_g, ref[1]) and torch.equal(i_g, ref[2]), rep
 
 
 def test_decode_layer_stages_and_last_layer():
     lens = [64 * 20] * 2
-    c, _, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
+    c, c2, kc, kc_next, idx, cnt = _layer_case("bf16", 128, 4, 2, 64 * 20, lens, 9)
     kc1, kc2 = kc.clone(), kc.clone()
-    out1, i1, n1 = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc1, idx, cnt, x=c["x_sel"],
-                                               w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
-    i2, n2 = torch.empty_like(idx), torch.empty_like(cnt)
+    out1, s1 = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc1, idx, cnt, x=c["x_sel"],
+                                           w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1, n_local=2)
+    s2 = torch.empty_like(s1)
     out2 = torch.empty_like(out1)
     for st in (1, 2):
         bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc2, idx, cnt, out=out2, x=c["x_sel"],
-                                    w=c["w_sel"], kc_next=kc_next, idx_next=i2, cnt_next=n2, topk=6, n_init=1,
-                                    n_local=2, stages=st)
-    out3, none_i, none_c = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt,
-                                                       topk=6, n_init=1, n_local=2)
+                                    w=c["w_sel"], kc_next=kc_next, scores_next=s2, topk=6, n_init=1, n_local=2,
+                                    stages=st)
+    out3, none = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, topk=6,
+                                             n_init=1, n_local=2)
     torch.cuda.synchronize()
-    assert torch.equal(out1, out2) and torch.equal(i1, i2) and torch.equal(n1, n2) and torch.equal(kc1, kc2)
-    assert none_i is None and none_c is None and torch.equal(out3, out1)
+    # scores are written for the candidates only; compare those
+    cand = slice(1, 20 - 2)
+    assert torch.equal(out1, out2) and torch.equal(s1[:, :, cand], s2[:, :, cand]) and torch.equal(kc1, kc2)
+    assert none is None and torch.equal(out3, out1)
 
 
 def test_decode_layer_shared_workspace_across_lookahead_and_last_layer():
@@ -1000,8 +1046,9 @@ def test_decode_layer_shared_workspace_across_lookahead_and_last_layer():
     def run(shared, sel):
         kw = dict(x=c["x_sel"], w=c["w_sel"], kc_next=kc_next) if sel else {}
         own = ws if shared else torch.zeros_like(ws)
-        return bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, topk=6,
-                                           n_init=1, n_local=2, ws=own, **kw)
+        out, sc = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, topk=6,
+                                              n_init=1, n_local=2, ws=own, **kw)
+        return out, (sc[:, :, 1:nb - 2] if sel else None)
     for rnd in range(2):
         for sel in (True, False, True):
             got = run(True, sel)
@@ -1009,17 +1056,17 @@ def test_decode_layer_shared_workspace_across_lookahead_and_last_layer():
             torch.cuda.synchronize()
             assert torch.equal(got[0], want[0]), (rnd, sel)
             if sel:
-                assert torch.equal(got[1], want[1]) and torch.equal(got[2], want[2]), (rnd, sel)
+                assert torch.equal(got[1], want[1]), (rnd, sel)
     # every complete call leaves the arrival counters (the first words) at zero
-    assert int(ws[: 2 * 2 * 4 * 4].view(torch.int32).abs().sum()) == 0
+    assert int(ws[: 2 * 4 * 4].view(torch.int32).abs().sum()) == 0
 
 
 @pytest.mark.parametrize("lens", [[64 * 300, 64 * 300 - 17], [64 * 300 - 63, 64 * 131 + 5]])
 def test_decode_layer_multi_slice_multi_block_splits(lens):
     """B2 x 4 KV heads with 300 blocks and top-64: several score slices per
-    (b, g) arrive at the top-k, and each attention split covers several
-    blocks.  The next layer's compressed keys are pooled by the oracle, not
-    taken from the GPU."""
+    (b, g), and each attention split covers several blocks.  The next
+    layer's compressed keys are pooled by the oracle, not taken from the
+    GPU; the next layer's lists come from the scores by its own call."""
     T, topk = 64 * 300, 64
     c = _gpu(random_decode_case(41, B=2, Hq=16, Hkv=4, d=128, T=T, dtype="bf16", hidden=512, seq_len=lens))
     c2 = _gpu(random_decode_case(42, B=2, Hq=16, Hkv=4, d=128, T=T, dtype="bf16", seq_len=lens, plant=20,
@@ -1036,9 +1083,9 @@ def test_decode_layer_multi_slice_multi_block_splits(lens):
     ws = torch.zeros(bskv.workspace_bytes("layer", 2, 16, 4, 128, 512, 300, U, 1), dtype=torch.uint8, device=DEV)
     for rep in range(2):                      # the second call reuses the counters the first left at zero
         kc_l = kc.clone()
-        out, i_n, c_n = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_l, idx, cnt,
-                                                    x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk,
-                                                    n_init=1, n_local=2, ws=ws)
+        out, sc = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_l, idx, cnt, x=c["x_sel"],
+                                              w=c["w_sel"], kc_next=kc_next, topk=topk, n_init=1, n_local=2, ws=ws)
+        i_n, c_n = _next_lists(c2, kc_next, sc, topk, 1, 2, ws=ws)
         torch.cuda.synchronize()
         f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), 4, 128)
         sel = orc.decode_select(f_or, kc_next_or, lens_np, topk, 1, 2, 64)
@@ -1048,3 +1095,45 @@ def test_decode_layer_multi_slice_multi_block_splits(lens):
         assert max_abs(np64(out), want) < 2e-2, rep
         done = ~np.isnan(kc_or)
         assert max_abs(np64(kc_l)[done], kc_or[done]) < 1e-4
+
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2)])
+def test_decode_layer_immediate_mode_equals_deferred_and_per_op(dtype, d, G):
+    """Immediate mode (the next layer's top-k inside the second kernel, from
+    agent-coherent scores handed over through an arrival counter) gives the
+    lists of the deferred mode and of the per-op selection, with several
+    score slices per (b, g), and leaves its counters at zero for a reused
+    workspace."""
+    lens = [64 * 300, 64 * 300 - 17, 64 * 131 + 5, 64 * 300]
+    B, Hkv, T, topk = 4, 4, 64 * 300, 32
+    c = _gpu(random_decode_case(51, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, hidden=512, seq_len=lens))
+    c2 = _gpu(random_decode_case(52, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens))
+    kc, kc_next = _kc_gpu(c["k"], c["seq_len"]), _kc_gpu(c2["k"], c2["seq_len"])
+    own = orc.decode_select(np64(c2["f"]), orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens), np.array(lens),
+                            topk, 1, 2, 64)
+    idx = torch.from_numpy(own.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(own.cnt.astype(np.int32)).to(DEV)
+    U = topk + 3
+    ws = torch.zeros(bskv.workspace_bytes("layer", B, Hkv * G, Hkv, d, 512, 300, U, 1 if dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=DEV)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], Hkv, d)
+    i_ref, n_ref = bskv.forecast_block_score_topk(f, kc_next, topk, 1, 2, seq_len=c["seq_len"])
+    for rep in range(2):
+        i_im = torch.full_like(idx, -7)
+        n_im = torch.full_like(cnt, -7)
+        out_im, none = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt,
+                                                   x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, idx_next=i_im,
+                                                   cnt_next=n_im, topk=topk, n_init=1, n_local=2, ws=ws)
+        out_de, sc = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt,
+                                                 x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk, n_init=1,
+                                                 n_local=2, ws=ws)
+        i_de, n_de = _next_lists(c2, kc_next, sc, topk, 1, 2, ws=ws)
+        torch.cuda.synchronize()
+        assert none is None
+        assert torch.equal(i_im, i_ref) and torch.equal(n_im, n_ref), rep
+        assert torch.equal(i_de, i_ref) and torch.equal(n_de, n_ref), rep
+        assert torch.equal(out_im, out_de), rep
+    assert int(ws[: 2 * B * Hkv * 4].view(torch.int32).abs().sum()) == 0
+    sel = orc.decode_select(orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), Hkv, d),
+                            orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens), np.array(lens), topk, 1, 2, 64)
+    check_selection(i_im, n_im, sel, topk)
