@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     block_sparse_attn_decode_cached,
     block_sparse_attn_prefill,
     decode_layer_lookahead,
+    decode_layer_lookahead_noalloc,
     forecast_block_score_topk,
     forecast_block_score_topk_pooled,
     forecast_proj,

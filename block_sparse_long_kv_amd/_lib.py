@@ -65,6 +65,10 @@ _proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _
 _proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _f, _p, _p,
        _p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
 
+_proto("bskv_decode_layer_lookahead_noalloc_capacity", _sz)
+_proto("bskv_decode_layer_lookahead_noalloc", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _f,
+       _p, _p, _p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p)
+
 BSKV_F32, BSKV_BF16 = 0, 1
 _DT = {torch.float32: BSKV_F32, torch.bfloat16: BSKV_BF16}
 
@@ -538,4 +542,43 @@ def decode_layer_lookahead(q, k, v, seq_len, kc, idx, cnt, scale: float | None =
                                            _ptr(idx_next), _ptr(cnt_next), B, Hq, Hkv, d, 64, nb_cap, topk, n_init,
                                            n_local, stages, _ptr(ws), ws.numel() * ws.element_size(), sh),
            "decode_layer_lookahead")
+    return out, (scores_next if sel else None)
+
+
+def decode_layer_lookahead_noalloc(q, k, v, seq_len, kc, idx, cnt, scale: float | None = None, out=None, x=None,
+                                   w=None, kc_next=None, scores=None, scores_next=None, idx_next=None, cnt_next=None,
+                                   topk: int = 0, n_init: int = 1, n_local: int = 1, stages: int = 3, stream=None):
+    """decode_layer_lookahead with its workspace in the library's static
+    device array (no workspace argument, nothing allocated by the library;
+    `out` / `scores_next` are allocated here when not given).  Raises
+    BskvError (BSKV_ENOSPC) when the layer's workspace exceeds the array."""
+    B, Hq, d = q.shape
+    Hkv, nb_cap = kc.shape[1], kc.shape[2]
+    U = idx.shape[-1]
+    if U != topk + n_init + n_local:
+        raise ValueError("idx capacity must equal topk + n_init + n_local")
+    sel = x is not None
+    immediate = idx_next is not None or cnt_next is not None
+    if sel:
+        hidden = x.shape[1]
+        if immediate and (idx_next is None or cnt_next is None or scores_next is not None):
+            raise ValueError("immediate mode takes idx_next and cnt_next (and no scores_next)")
+        if not immediate and scores_next is None:
+            scores_next = torch.empty(B, Hkv, nb_cap, dtype=torch.float32, device=q.device)
+    else:
+        hidden = 0
+    if k.stride() != v.stride() or not q.is_contiguous():
+        raise ValueError("q contiguous; k, v with identical strides")
+    for t in (scores, scores_next):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (B, Hkv, nb_cap)):
+            raise ValueError("scores / scores_next: contiguous fp32 [B, Hkv, kc_nb_cap]")
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    _whole_blocks(k, "decode_layer_lookahead_noalloc")
+    _check(lib.bskv_decode_layer_lookahead_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _dt(k), _strides3(k), k.shape[2], _ptr(seq_len), _ptr(kc), _ptr(scores), _ptr(idx),
+        _ptr(cnt), scale, _ptr(out), _ptr(x), _ptr(w), hidden, _ptr(kc_next), _ptr(scores_next), _ptr(idx_next),
+        _ptr(cnt_next), B, Hq, Hkv, d, 64, nb_cap, topk, n_init, n_local, stages, sh),
+        "decode_layer_lookahead_noalloc")
     return out, (scores_next if sel else None)

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libbskv.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "decode_kernels.hip", "fused_decode.hip", "score_topk.hip", "attn_prefill.hip", "prefetch.hip",
-           "multihead_select.hip", "window_select.hip", "block_cache.hip", "qkvf_proj.hip"]
+           "multihead_select.hip", "window_select.hip", "block_cache.hip", "qkvf_proj.hip", "noalloc.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

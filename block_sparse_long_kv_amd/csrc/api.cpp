@@ -53,6 +53,15 @@ bool group_ok(int hq, int hkv) {
 
 }  // namespace
 
+namespace bskv {
+// for other translation units of the library (the allocation-free entry point)
+void set_last_error(const char* msg) {
+  strncpy(g_last_error, msg ? msg : "", sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = 0;
+}
+int report_hip(hipError_t e) { return finish(e); }
+}  // namespace bskv
+
 extern "C" {
 
 int bskv_version(void) { return (0 << 16) | 1; }

@@ -477,6 +477,32 @@ int bskv_decode_layer_lookahead(const void* q, const void* k, const void* v, int
                                 int n_init, int n_local, int stages, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* ----------------------------------------------------------------------- *
+ * For callers that cannot allocate device memory -- code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid allocation: the fused
+ * decode layer with its workspace in a static device array of the library
+ * (bskv_decode_layer_lookahead_noalloc_capacity() bytes, 16 MiB, one per
+ * GPU, held until the process ends) instead of a caller buffer.  Arguments
+ * and results as bskv_decode_layer_lookahead without ws / ws_bytes; the
+ * device is the one current on the calling thread (it must be the stream's).
+ * Returns BSKV_ENOSPC, before touching the device, when the layer's
+ * workspace (bskv_decode_layer_lookahead_workspace) exceeds the array.  The
+ * first call on a device looks the array up and clears its arrival counters
+ * with a small kernel on `stream`; no call allocates or frees anything.
+ * Every call on one device shares that device's array and keeps its last
+ * contents (the counters are left at zero): calls that overlap in time on
+ * one device race, so they must be ordered (one stream, or events).
+ * ----------------------------------------------------------------------- */
+size_t bskv_decode_layer_lookahead_noalloc_capacity(void);
+int bskv_decode_layer_lookahead_noalloc(const void* q, const void* k, const void* v, int dtype,
+                                        const int64_t* kv_strides, int64_t kv_len, const int64_t* seq_len,
+                                        float* kc, const float* scores, int32_t* idx, int32_t* cnt, float scale,
+                                        float* out, const void* x, const void* w_forecast, int hidden,
+                                        const float* kc_next, float* scores_next, int32_t* idx_next,
+                                        int32_t* cnt_next, int B, int n_q_heads, int n_kv_heads, int head_dim,
+                                        int block, int64_t kc_nb_cap, int topk, int n_init, int n_local,
+                                        int stages, hipStream_t stream);
+
 /* Device address of host memory allocated pinned (hipHostMalloc, or a torch
  * tensor created with pin_memory=True).  Returns BSKV_EHIP if the pointer is
  * not pinned host memory known to HIP. */

@@ -324,3 +324,19 @@ def test_decode_layer_validation():
     assert call(hidden=1000) == EUNSUP
     assert call(nl=0) == EINVAL
     assert call(wsb=ws - 16) == ENOSPC
+
+
+def test_noalloc_layer_rejects_oversized_workspace_on_the_host():
+    """The allocation-free layer refuses, before touching any device, a
+    layer whose workspace exceeds its static array (and bad sizes)."""
+    cap = lib.bskv_decode_layer_lookahead_noalloc_capacity()
+    assert cap == 16 << 20
+    f = lib.bskv_decode_layer_lookahead_noalloc
+
+    def call(B=8, hq=32, hkv=8, nb=2048):
+        return f(P, P, P, 1, S3, 131072, P, P, None, P, P, 0.088, P, P, P, 4096, P, P, None, None, B, hq, hkv, 128, 64,
+                 nb, 64, 1, 4, 3, None)
+    assert lib.bskv_decode_layer_lookahead_workspace(512, 32, 8, 128, 4096, 2048, 69, 1) > cap
+    assert call(B=512) == ENOSPC
+    assert b"16 MiB" in lib.bskv_last_error()
+    assert call(hq=24) == EINVAL
