@@ -56,6 +56,12 @@ struct LayerParams {
   int32_t* sync;
 };
 
+// The counter region opens every workspace with a fixed size, the counters
+// of the largest B * H the calls accept, whatever this call's B * H is:
+// only counters ever use those bytes, so a workspace shared by calls of
+// different shapes still finds them zero.
+constexpr size_t kSyncWords = (size_t)2 * 65535;
+
 // Arrival of this workgroup at a counter shared by n workgroups of one
 // launch.  Returns true in the last one to arrive, which resets the counter
 // to zero.  What the others hand over is stored and loaded agent-coherent:
@@ -164,14 +170,15 @@ int proj_tiles(int N, int dtype);
 
 static size_t al256(size_t x) { return ((x + 255) / 256) * 256; }
 
-// Workspace layout: the arrival counters first, at offset 0 whatever the
-// other arguments are, so one workspace can serve layers with and without a
-// lookahead (whose projection partials are absent) and the counters always
-// land on the words every earlier call left at zero; then the projection
-// partials, the next layer's candidate scores (immediate mode) and the
-// attention split partials, which every call writes before it reads them.
+// Workspace layout: the counter region first (kSyncWords int32, the same
+// size for every call), so one workspace can serve layers with and without
+// a lookahead (whose projection partials are absent) and calls of any
+// shape, and the counters always land on words every earlier call left at
+// zero; then the projection partials, the next layer's candidate scores
+// (immediate mode) and the attention split partials, which every call
+// writes before it reads them.
 size_t layer_workspace_bytes(int B, int Hq, int Hkv, int D, int hidden, int64_t nb_cap, int U, int dtype) {
-  return al256((size_t)2 * B * Hkv * sizeof(int32_t)) + al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) +
+  return al256(kSyncWords * sizeof(int32_t)) + al256(proj_workspace_bytes(B, hidden, Hkv * D, dtype)) +
          al256((size_t)B * Hkv * nb_cap * sizeof(float)) + attn_decode_workspace_bytes(B, Hq, Hkv, D, U);
 }
 
@@ -206,7 +213,7 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   p.seq_len = a.attn.seq_len; p.kc = a.kc; p.nb_cap = a.nb_cap;
   p.scores_in = a.scores; p.idx = a.idx; p.cnt = a.cnt;
   const int H = a.attn.Hkv, D = a.attn.D, B = a.attn.B;
-  const size_t sync_b = al256((size_t)2 * B * H * sizeof(int32_t));
+  const size_t sync_b = al256(kSyncWords * sizeof(int32_t));
   const size_t proj_b = al256(proj_workspace_bytes(B, a.hidden, H * D, a.attn.dtype));
   const size_t score_b = al256((size_t)B * H * a.nb_cap * sizeof(float));
   char* ws = (char*)a.attn.ws;

@@ -24,8 +24,8 @@
 namespace {
 
 constexpr size_t kScratchBytes = size_t(16) << 20;       // 16 MiB per device
-// the counters occupy the first 2 * B * n_kv_heads int32 words, and
-// B * n_kv_heads is at most 65535
+// the counter region: the first 2 * 65535 int32 words of every layer
+// workspace, whatever the call's shape
 constexpr size_t kCounterBytes = size_t(2) * 65535 * 4;
 constexpr int kMaxDevices = 64;
 

@@ -452,12 +452,12 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
  * the last layer, no lookahead); giving both forms is BSKV_EINVAL.  hidden
  * must be a multiple of 256.
  * ws: bskv_decode_layer_lookahead_workspace() with hidden = 0 when x is NULL,
- * zero-filled once before its first use: its first 2*B*n_kv_heads int32
- * words are K2's arrival counters, at that fixed offset for every call, and
- * every complete call leaves them at zero again.  One ws may therefore serve
- * every layer of a model, last layer included (size it for the largest
- * layout, i.e. with the lookahead's hidden); calls that share one ws must
- * not overlap in time.
+ * zero-filled once before its first use: its first 2 * 65535 int32 words
+ * (the same for every shape) are the second kernel's arrival counters, and
+ * every complete call leaves them at zero again.  One ws may therefore
+ * serve every layer of a model, last layer included, and calls of other
+ * shapes (size it for the largest layout, i.e. with the lookahead's
+ * hidden); calls that share one ws must not overlap in time.
  * stages: bit 0 = K1 (this layer's top-k when scores is given, projection
  * partials when x is given), bit 1 = K2 (next-layer scores [and top-k], this
  * layer's attention, merge and kc update); 3 runs the whole layer.  K2 reads

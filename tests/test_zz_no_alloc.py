@@ -37,8 +37,11 @@ def _case(seed, B, T, lens, topk):
 @pytest.mark.parametrize("mode", ["deferred", "immediate"])
 def test_noalloc_layer_equals_the_workspace_call(mode):
     topk = 16
+    # the second call is smaller; a third, larger again, finds the counters
+    # the smaller layout left at zero
     for B, T, lens in ((4, 64 * 300, [64 * 300, 64 * 300 - 11, 64 * 150, 64 * 299 + 1]),
-                       (2, 64 * 120, [64 * 120, 64 * 77 + 3])):        # the second call is smaller
+                       (2, 64 * 120, [64 * 120, 64 * 77 + 3]),
+                       (6, 64 * 200, [64 * 200] * 5 + [64 * 100 + 1])):
         c, c2, kc, kc_next, idx, cnt = _case(60 + B, B, T, lens, topk)
         U = topk + 3
         kw = dict(x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk, n_init=1, n_local=2)
