@@ -43,3 +43,21 @@ def check_selection(gpu_idx, gpu_cnt, sel, topk, rel=1e-3):
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+def fp32_sum_tol(abs_terms_sum, n_terms):
+    """Error bound of an fp32 sum of n products (inputs rounded to bf16 or
+    fp32 once, products formed and added in fp32), against the exact sum:
+    each product within 2^-24 relative, the sum's rounding errors a random
+    walk of n steps bounded at 4 standard deviations, all scaled by the sum
+    of the products' magnitudes: (4 sqrt(n) + 1) 2^-24 sum |x_i w_i|, plus
+    the smallest normal so an all-zero sum still compares.  abs_terms_sum is
+    sum |x_i w_i| per output (e.g. |x| @ |w|)."""
+    u = 2.0 ** -24
+    return (4.0 * np.sqrt(n_terms) + 1.0) * u * np.asarray(abs_terms_sum, dtype=np.float64) + 1.2e-38
+
+
+def fp32_sum_close(got, want, abs_terms_sum, n_terms):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return bool(np.all(np.abs(got - want) <= fp32_sum_tol(abs_terms_sum, n_terms)))

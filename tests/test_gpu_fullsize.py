@@ -6,7 +6,7 @@ import torch
 
 import block_sparse_long_kv_amd as bskv
 import oracle as orc
-from parity import check_selection, max_abs, np64
+from parity import check_selection, fp32_sum_close, max_abs, np64
 from workloads import CONFIGS, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,11 @@ def test_config3_two_layers_sampled():
 def test_config4_prefill_chunks_sampled():
     """B4, T=131072, 2048-token chunks, top-64 + 1 + 32 local: selection and
     attention on sampled (batch, KV head, query block) problems of the first,
-    a middle and the last chunk, at the kernels' full launch size."""
+    a middle and the last chunk, at the kernels' full launch size.  Every
+    token of each sampled query block, for every query head of the KV head,
+    is compared (2 x 3 x 7 x 4 x 64 = 10,752 rows), on the oracle's own lists
+    whenever the GPU's selection equals them (no near-tie swap), else on the
+    GPU's lists."""
     import math
     from workloads import prefill_inputs
     wl = CONFIGS[4]
@@ -67,6 +71,7 @@ def test_config4_prefill_chunks_sampled():
     kc_or = {s: orc.kv_block_meanpool(np64(inp["k"][s[0]:s[0] + 1, s[1]:s[1] + 1]), 64) for s in samples}
     kv_or = {s: (np64(inp["k"][s[0]:s[0] + 1, s[1]:s[1] + 1]), np64(inp["v"][s[0]:s[0] + 1, s[1]:s[1] + 1]))
              for s in samples}
+    rows_checked, on_oracle_lists = 0, 0
     for q0 in (0, wl.T // 2, wl.T - wl.chunk):
         f = inp["f"][:, :, q0:q0 + wl.chunk].contiguous()
         q = inp["q"][:, :, q0:q0 + wl.chunk].contiguous()
@@ -74,21 +79,26 @@ def test_config4_prefill_chunks_sampled():
         out = bskv.block_sparse_attn_prefill(q, inp["k"], inp["v"], idx, cnt, q0, wl.scale)
         torch.cuda.synchronize()
         for (b, g) in samples:
-            for qi in (0, 17, 31):
+            k1, v1 = kv_or[(b, g)]
+            for qi in (0, 5, 11, 17, 23, 29, 31):
                 fq = np64(f[b:b + 1, g:g + 1, qi * 64:(qi + 1) * 64])
                 sel = orc.prefill_select(fq, kc_or[(b, g)], q0 + qi * 64, wl.topk, wl.n_init, wl.n_local, 64)
-                check_selection(idx[b:b + 1, g:g + 1, qi:qi + 1], cnt[b:b + 1, g:g + 1, qi:qi + 1], sel, wl.topk)
-                # attention of two query heads of this KV head on a few tokens, on the GPU's list
-                k1, v1 = kv_or[(b, g)]
-                gi = idx[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
-                gc = cnt[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
-                for h in (g * wl.G, g * wl.G + wl.G - 1):
-                    qq = np64(q[b:b + 1, h:h + 1, qi * 64:(qi + 1) * 64])
-                    rows = [(0, 0, t) for t in (0, 31, 63)]
-                    want = orc.attend_prefill(qq, k1, v1, gi, gc, q0 + qi * 64, 1.0 / math.sqrt(wl.d), 64, rows=rows)
-                    got = np64(out[b:b + 1, h:h + 1, qi * 64:(qi + 1) * 64])
-                    for r in rows:
-                        assert max_abs(got[r], want[r]) < 2e-2
+                swaps = check_selection(idx[b:b + 1, g:g + 1, qi:qi + 1], cnt[b:b + 1, g:g + 1, qi:qi + 1], sel,
+                                        wl.topk)
+                if swaps == 0:
+                    li, lc = sel.idx, sel.cnt
+                    on_oracle_lists += 1
+                else:
+                    li = idx[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
+                    lc = cnt[b:b + 1, g:g + 1, qi:qi + 1].cpu().numpy()
+                heads = list(range(g * wl.G, (g + 1) * wl.G))
+                qq = np64(q[b:b + 1, heads[0]:heads[-1] + 1, qi * 64:(qi + 1) * 64])
+                want = orc.attend_prefill(qq, k1, v1, li, lc, q0 + qi * 64, 1.0 / math.sqrt(wl.d), 64)
+                got = np64(out[b:b + 1, heads[0]:heads[-1] + 1, qi * 64:(qi + 1) * 64])
+                err = max_abs(got, want)
+                assert err < 2e-2, (q0, b, g, qi, err)
+                rows_checked += want.shape[1] * want.shape[2]
+    assert rows_checked >= 10_000 and on_oracle_lists > 0
 
 
 def test_config5_offload_sampled():
@@ -224,7 +234,8 @@ def test_widened_projection_full_size_sampled():
     wq, wk, wv, wf = orc.qkvf_proj(np64(x), w64, Hq, H, d)
     assert np.all(np.abs(np64(q) - wq) <= 2.0 ** -8 * np.abs(wq) + 1e-3)
     assert np.all(np.abs(np64(kc[:, :, T - 1]) - wk) <= 2.0 ** -8 * np.abs(wk) + 1e-3)
-    assert max_abs(np64(f), wf) < 1e-3
+    mag_f = (np.abs(np64(x)) @ np.abs(w64))[:, (Hq + 2 * H) * d:].reshape(wf.shape)
+    assert fp32_sum_close(np64(f), wf, mag_f, hid)
     Bp, C, q0, Tc = 4, 2048, 4096, 8192
     xp = torch.randn(Bp, C, hid, generator=g, device=DEV).to(torch.bfloat16)
     kcp = torch.zeros(Bp, H, Tc, d, dtype=torch.bfloat16, device=DEV)
@@ -238,4 +249,5 @@ def test_widened_projection_full_size_sampled():
         assert np.all(np.abs(gq - oq) <= 2.0 ** -8 * np.abs(oq) + 1e-3)
         gk = np64(kcp[b:b + 1, :, q0 + 64 * qi:q0 + 64 * (qi + 1)])
         assert np.all(np.abs(gk - ok_) <= 2.0 ** -8 * np.abs(ok_) + 1e-3)
-        assert max_abs(np64(fp[b:b + 1, :, qi:qi + 1]), of) < 2e-5 * np.abs(of).max() + 1e-3
+        mag_p = (np.abs(xs[0]) @ np.abs(w64)[:, (Hq + 2 * H) * d:]).sum(0).reshape(of.shape)
+        assert fp32_sum_close(np64(fp[b:b + 1, :, qi:qi + 1]), of, mag_p, 64 * hid)
