@@ -17,8 +17,8 @@
 //       projection splits of its (b, g) in order), stored for the next
 //       layer's call
 //       + attention splits of layer l over its listed blocks; the last split
-//       of a (b, g) to finish merges the splits and updates layer l's
-//       compressed keys with the newest block
+//       of a (b, g) to finish merges the splits, and the (b, g)'s last split
+//       in list order updates layer l's compressed keys with the newest block
 // The top-k of layer l+1 then runs in the next call's K1, where it shares a
 // short, latency-bound launch with the projection (deferred mode).  In the
 // immediate mode the scores go to the workspace instead and the last score
@@ -145,21 +145,25 @@ __global__ __launch_bounds__(kThreads, 4) void layer_k2(LayerParams p) {
     return;
   }
   const int a = bid - n_score;
-  const int bg = a / p.attn.n_splits;
-  attn_split_wg<T, D, G, true>(p.attn, bg, a % p.attn.n_splits, sm.attn);
-  // the last attention split of (b, g): merge of the splits, then the
-  // newest-block update of this layer's compressed keys (the block the
-  // newest token completed)
+  const int bg = a / p.attn.n_splits, split = a % p.attn.n_splits;
+  attn_split_wg<T, D, G, true>(p.attn, bg, split, sm.attn);
+  // the newest-block update of this layer's compressed keys (the block the
+  // newest token completed) by the (b, g)'s last split, which has the
+  // fewest blocks: off the merge's critical path.  No split reads that row
+  // (the newest block is local, never a scored candidate).
+  if (split == p.attn.n_splits - 1) {
+    const int b = bg / p.H, g = bg % p.H;
+    const int64_t L = min(p.seq_len[b], p.kv_len);
+    const int64_t j = L / kBlk - 1;
+    if (L > 0 && (L % kBlk) == 0 && j < p.nb_cap) {
+      __syncthreads();
+      meanpool_wg<T, D>((const T*)p.k + b * p.sb + g * p.sg + j * kBlk * p.st, p.st,
+                        p.kc + ((int64_t)bg * p.nb_cap + j) * D, sm.mp);
+    }
+  }
+  // the last attention split of (b, g) to finish merges the splits
   if (!arrive_last(p.sync + bg, p.attn.n_splits, last_flag)) return;
   attn_combine_wg<D, G, true>(p.attn, bg, sm.comb);
-  __syncthreads();
-  const int b = bg / p.H, g = bg % p.H;
-  const int64_t L = min(p.seq_len[b], p.kv_len);
-  if (L <= 0 || (L % kBlk) != 0) return;
-  const int64_t j = L / kBlk - 1;
-  if (j >= p.nb_cap) return;
-  meanpool_wg<T, D>((const T*)p.k + b * p.sb + g * p.sg + j * kBlk * p.st, p.st,
-                    p.kc + ((int64_t)bg * p.nb_cap + j) * D, sm.mp);
 }
 
 size_t proj_workspace_bytes(int B, int hidden, int N, int dtype);
