@@ -88,7 +88,7 @@ def log(*a):
 # decode workload
 # ---------------------------------------------------------------------------
 class DecodeBench:
-    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None, select_mode="deferred"):
+    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None, select_mode="immediate"):
         from workloads import decode_inputs
         self.torch, self.bskv, self.wl = torch, bskv, wl
         self.select_mode = select_mode

@@ -1029,13 +1029,13 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
 
 // Split plan of the decode attention: about `target` workgroups, at most
 // kMaxSplitsDecode splits, every split the same number of listed blocks.
-// Measured at B8 x 128K (U = 69 blocks) over targets 512..2048: 768 (12
-// splits of 6 blocks) runs the attention alone 5% faster than 1024 (14 of
-// 5) and is level with it inside the fused layer kernel; 640 (10 of 7) and
-// fewer splits are slower, and more, shorter splits add merge work and
-// arrivals.
+// Measured inside the fused decode layer (immediate top-k), same box,
+// interleaved: B8 x 128K (64 (b, g) units, U = 69) 512 workgroups (8 splits
+// of 9 blocks) with 512 score workgroups ran the step ~2% faster than 768
+// (12 of 6) with 768; B4 x 32K (32 units, U = 35) 384-512 beat 768 by 4%.
+// Above 64 units the earlier 768 is kept (at B16 it still gives 6 splits).
 __host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
-  const int target = 768;
+  const int target = n_bg <= 64 ? 512 : 768;
   int ns = (target + n_bg - 1) / n_bg;
   if (ns > U) ns = U;
   if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;
@@ -1044,12 +1044,11 @@ __host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, 
   n_splits = (U + bps - 1) / bps;
 }
 
-// Score split plan: about 768 workgroups, at least 64 candidate rows each.
-// Measured at B8 x 128K next to the 768-workgroup attention plan: 12 slices
-// of ~171 rows per (b, g) beat 8 slices by ~2% per decode step (every one of
-// five interleaved pairs), 16 slices sit between them, 6 are slower.
+// Score split plan: about 512 workgroups (768 above 64 (b, g) units), at
+// least 64 candidate rows each.
 __host__ __device__ inline int score_split_plan(int n_bg, int64_t nb_cap) {
-  int s = (768 + n_bg - 1) / n_bg;
+  const int target = n_bg <= 64 ? 512 : 768;
+  int s = (target + n_bg - 1) / n_bg;
   const int max_s = (int)((nb_cap + 63) / 64);
   if (s > max_s) s = max_s;
   return s < 1 ? 1 : s;
