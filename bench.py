@@ -1391,6 +1391,36 @@ def run_offload_steady(args, torch, bskv, wl):
     }
 
 
+def _core_args(args, steps=None):
+    import copy
+    a = copy.copy(args)
+    a.core_only, a.no_cpu_baseline, a.per_op = True, True, False
+    if steps is not None:
+        a.steps = steps
+    return a
+
+
+def side_decode_b4(args, torch, bskv, wl):
+    """The B4 x 32K decode workload (one layer, eight replicas rotated so the
+    45 MB working set is not served from the last-level cache), compactly."""
+    r = run_decode(_core_args(args), torch, bskv, wl, replicas=8)
+    k2 = r["kernels"]["layer_k2"]
+    return {"workload": wl.name, "tokens_per_s": r["value"], "us_per_layer_step": round(r["ms_per_step"] * 1e3 / 8, 3),
+            "step_hbm_frac": r["step_hbm_frac"], "layer_k2_us": k2["us"], "layer_k2_hbm_frac": k2["hbm_frac"],
+            "layer_k1_us": r["kernels"]["layer_k1"]["us"], "outputs_checked": r["post_timing_check"]}
+
+
+def side_prefill(args, torch, bskv, wl):
+    """The B4 x 128K chunked prefill (pool + select + attend per 2048-token
+    chunk), compactly; its parity is covered by the full-size GPU test."""
+    r = run_prefill(_core_args(args), torch, bskv, wl)
+    at = r["kernels"]["attn_prefill"]
+    return {"workload": wl.name, "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"],
+            "attn_ms_per_chunk": round(at["us"] / 1e3, 4), "attn_TFLOPs": at["TFLOPs"], "attn_mfma_frac": at["mfma_frac"],
+            "score_topk_us_per_chunk": r["kernels"]["score_topk_prefill"]["us"],
+            "parity": "tests/test_gpu_fullsize.py::test_config4_prefill_chunks_sampled (10,752 rows vs the oracle)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1433,6 +1463,15 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probes: {n} bytes read, {n} bytes written, each")
         del a, b
+    if args.workload == "decode" and not args.core_only and not args.per_op:
+        result = run_decode(args, torch, bskv, CONFIGS[3])
+        # the other two main workloads, compactly, on the same run
+        torch.cuda.empty_cache()
+        result["decode_b4"] = side_decode_b4(args, torch, bskv, CONFIGS[2])
+        torch.cuda.empty_cache()
+        result["prefill"] = side_prefill(args, torch, bskv, CONFIGS[4])
+        print(json.dumps(result), flush=True)
+        return
     if args.workload == "decode-tiny":
         result = run_tiny(args, torch, bskv, CONFIGS[1])
     elif args.workload == "prefill":
