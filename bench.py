@@ -88,7 +88,7 @@ def log(*a):
 # decode workload
 # ---------------------------------------------------------------------------
 class DecodeBench:
-    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None, select_mode="immediate"):
+    def __init__(self, wl, torch, bskv, layers=None, B=None, T=None, select_mode="deferred"):
         from workloads import decode_inputs
         self.torch, self.bskv, self.wl = torch, bskv, wl
         self.select_mode = select_mode
@@ -646,7 +646,7 @@ def check_step_outputs(torch, bench):
 
 
 def run_decode(args, torch, bskv, wl, replicas=None):
-    bench = DecodeBench(wl, torch, bskv, layers=replicas)
+    bench = DecodeBench(wl, torch, bskv, layers=replicas, select_mode=args.select_mode)
     step_fn = bench.step_per_op if args.per_op else bench.step
     step_s, _ = time_graph(torch, step_fn, args.steps, args.warmup, use_graph=not args.no_graph)
     log(f"[bench] decode step {step_s * 1e3:.3f} ms ({'graph' if not args.no_graph else 'eager'})")
@@ -681,7 +681,8 @@ def run_decode(args, torch, bskv, wl, replicas=None):
         "config": {"workload": wl.name, "B": bench.B, "T": bench.T, "layers": bench.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "head_dim": wl.d, "hidden": wl.hidden, "block": wl.block, "topk": wl.topk, "n_init": wl.n_init,
                    "n_local": wl.n_local, "hip_graph": not args.no_graph,
-                   "path": "per-op" if args.per_op else "fused-layer"},
+                   "path": "per-op" if args.per_op else "fused-layer",
+                   "next_layer_topk": None if args.per_op else args.select_mode},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(dom),
                      "bytes_per_launch": bpl[dom], "us_per_launch": round(kt[dom] * 1e6, 3)},
@@ -1432,6 +1433,9 @@ def main():
     ap.add_argument("--drift", type=float, default=None,
                     help="offload-steady: random-walk step of the Forecast input per decode step")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
+    ap.add_argument("--select-mode", default="deferred", choices=["deferred", "immediate"],
+                    help="fused layer: the next layer's top-k in the next call's first kernel (deferred) or in this "
+                         "call's second kernel (immediate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
                     help="only the workload's own path: no comparison selectors, variants or widened projection "

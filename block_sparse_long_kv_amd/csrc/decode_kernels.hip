@@ -161,7 +161,7 @@ hipError_t launch_score_topk_decode(const ScoreTopkArgs& a) {
 
 // ------------------------------------------------------------------ decode attention
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads, 4) void attn_split_kernel(AttnDecodeParams p) {
+__global__ __launch_bounds__(kThreads, 3) void attn_split_kernel(AttnDecodeParams p) {
   __shared__ typename AttnSmemSel<T, D, G>::type sm;
   attn_split_wg<T, D, G>(p, blockIdx.y, blockIdx.x, sm);
 }

@@ -337,7 +337,11 @@ __device__ __forceinline__ void score_slice_proj_wg(const float* __restrict__ pa
   constexpr int LPR = 8;
   constexpr int F4 = D / 4 / LPR;
   constexpr int RPP = kThreads / LPR;   // 32 rows per pass
-  constexpr int UNR = 4;
+  // one pass of rows in flight: next to the attention workgroups of the same
+  // launch, fewer score rows in flight shorten the memory queues the
+  // attention's dependent block loads wait in (B8 x 128K fused layer: one
+  // pass 2-3% faster per step than two; 6% faster than four)
+  constexpr int UNR = 1;
   const int sub = threadIdx.x % LPR, row0 = threadIdx.x / LPR;
   float4 kv[UNR][F4];
   auto issue = [&](int base) {
@@ -700,6 +704,8 @@ __device__ __forceinline__ void attn_split_finish(const AttnDecodeParams& p, int
 //                 transposing ds_read_b64_tr_b16 (lane 4r+c of each 16-lane
 //                 group reads row r, columns 4c..4c+3; lane i receives column
 //                 i of the four rows)
+// Two register sets: the next block's K/V rows are in flight while the
+// current block is computed (~155 VGPRs: three workgroups per SIMD).
 // No barrier inside the block loop: a wave touches only its own LDS rows,
 // and LDS operations of one wave complete in order.  The running maximum
 // is lazy: it moves only when some lane's block maximum exceeds it by more
@@ -765,23 +771,50 @@ __device__ __forceinline__ void attn_split_mfma_wg(const AttnDecodeParams& p, in
   const int Lc = (int)min(L, (int64_t)0x7fffffff - kBlk);
   const int jend = (Lc + kBlk - 1) / kBlk;
   typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-  for (int u = u0; u < u1; ++u) {
-    const int j = list[u];
-    const int loc = p.slot ? p.slot[(int64_t)bg * p.U + u] : (p.ring ? u : j);
-    if (j < 0 || loc < 0 || loc >= nblk_buf || j >= jend) continue;   // nothing of this block is attended
-    const int nvalid = min(kBlk, Lc - j * kBlk);
-    const uint32_t boff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)loc * kBlk * p.st * 2));
-    uint4 kr[KS], vr[NVC];
+  // list entries through the constant address space: scalar loads, which
+  // do not wait behind the vector loads in flight
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+  const cint_ptr clist = (cint_ptr)list;
+  const cint_ptr cslot = (cint_ptr)(p.slot ? p.slot + (int64_t)bg * p.U : list);
+  // a descriptor with no records: loads through it return zeros and touch
+  // no memory (list slots that name no block)
+  const __amdgpu_buffer_rsrc_t rnull = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, 0, 0x00020000);
+  // Requests the K/V rows of list slot u into (kr, vr) and returns the
+  // slot's valid key count (-1: no block).  Every call issues the same eight
+  // loads in the same order (scheduling barriers keep that order), so the
+  // compiler's wait counts stay exact while the next slot is in flight.
+  auto issue = [&](int u, uint4 (&kr)[KS], uint4 (&vr)[NVC]) -> int {
+    int nv = -1;
+    uint32_t boff = 0;
+    bool none = true;
+    if (u < u1) {
+      const int j = clist[u];
+      const int loc = p.slot ? cslot[u] : (p.ring ? u : j);
+      if (!(j < 0 || loc < 0 || loc >= nblk_buf || j >= jend)) {
+        nv = min(kBlk, Lc - j * kBlk);
+        boff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)loc * kBlk * p.st * 2));
+        none = false;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * ks, (int)boff, 2);
+      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(none ? rnull : rk, ko + 64 * ks, (int)boff, 2);
       kr[ks] = make_uint4(x[0], x[1], x[2], x[3]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NVC; ++i) {
-      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * vstep, (int)boff, 2);
+      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(none ? rnull : rv, vo + i * vstep, (int)boff, 2);
       vr[i] = make_uint4(x[0], x[1], x[2], x[3]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    return nv;
+  };
+  // One block: scores, lazy softmax update, P V.  A slot with no block runs
+  // with every key masked (p = 0, V rows zero), so it adds nothing.
+  auto compute = [&](const uint4 (&kr)[KS], const uint4 (&vr)[NVC], int nv) {
+    const int nvalid = nv < 0 ? 0 : nv;
     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -825,8 +858,17 @@ __device__ __forceinline__ void attn_split_mfma_wg(const AttnDecodeParams& p, in
       const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + tr_off + ((2 * dt) ^ tr_sw) * 16));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
     }
+  };
+  // two register sets: slot u + 1 is requested before slot u is computed
+  uint4 kA[KS], vA[NVC], kB[KS], vB[NVC];
+  int nA = issue(u0, kA, vA), nB;
+  for (int u = u0; u < u1; u += 2) {
+    nB = issue(u + 1, kB, vB);
+    compute(kA, vA, nA);
+    if (u + 1 >= u1) break;
+    nA = issue(u + 2, kA, vA);
+    compute(kB, vB, nB);
   }
-
   // merge the four waves: lane l holds O[head l%16][d = 16dt + 4(l/16) + i]
   {
     float a, bb;
@@ -1029,13 +1071,15 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
 
 // Split plan of the decode attention: about `target` workgroups, at most
 // kMaxSplitsDecode splits, every split the same number of listed blocks.
-// Measured inside the fused decode layer (immediate top-k), same box,
-// interleaved: B8 x 128K (64 (b, g) units, U = 69) 512 workgroups (8 splits
-// of 9 blocks) with 512 score workgroups ran the step ~2% faster than 768
-// (12 of 6) with 768; B4 x 32K (32 units, U = 35) 384-512 beat 768 by 4%.
-// Above 64 units the earlier 768 is kept (at B16 it still gives 6 splits).
+// With two blocks in flight per wave (three workgroups per SIMD: 768 slots)
+// the attention needs fewer, longer splits: measured inside the fused decode
+// layer at B8 x 128K (64 (b, g) units, U = 69), 256 workgroups (4 splits of
+// 18 blocks) beside 512 score workgroups fill the 768 slots and ran the step
+// 6% faster than 192 or 512 attention workgroups, 13% faster than 320, 22%
+// faster than 128 (same box, top-k in the launch's tail).  Above 64
+// units the earlier 768 is kept (at B16 it gives 6 splits).
 __host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
-  const int target = n_bg <= 64 ? 512 : 768;
+  const int target = n_bg <= 64 ? 256 : 768;
   int ns = (target + n_bg - 1) / n_bg;
   if (ns > U) ns = U;
   if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads, 4) void layer_k2(LayerParams p) {
+__global__ __launch_bounds__(kThreads, 3) void layer_k2(LayerParams p) {
   extern __shared__ uint32_t keys[];   // immediate mode: top-k keys of problems above 8 * kThreads candidates
   __shared__ __attribute__((aligned(16))) union {
     typename AttnSmemSel<T, D, G>::type attn;
