@@ -341,24 +341,31 @@ __device__ __forceinline__ void topk_union_regs(const uint32_t* keys, int n, int
 }
 
 // Top-k + union for one selection problem of at most 8 * kThreads
-// candidates, run by all 256 threads, thread t holding the keys of
-// candidates 8t .. 8t+7 in registers (so its keys are in block-id order).
-// Same result as topk_union_regs<8> (MSB-first radix select, 8 bits per
-// pass, stopping once the bucket holding the topk-th key is taken whole;
-// ties to the lowest block ids), with one barrier per radix pass and one for
-// the output positions: each wave counts into its own histogram copies
-// (two per wave, double buffered over passes, cleared by the wave itself),
-// and every wave scans all copies and finds the threshold bucket on its own,
-// so nothing is broadcast.
-__device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur, int n_init, int n_local, int U,
-                                                int32_t* idx_out, int32_t* cnt_out, TopkShared& sh,
+// candidates, run by all 256 threads, thread t holding the keys of block ids
+// base + 8t .. base + 8t + 7 in registers (so its keys are in block-id
+// order); ids outside the candidates [c0, c1) take no part.  Same result as
+// topk_union_regs<8> (MSB-first radix select, 8 bits per pass, stopping once
+// the bucket holding the topk-th key is taken whole; ties to the lowest
+// block ids), with one barrier per radix pass and one for the output
+// positions: each wave counts into its own histogram copies (two per wave,
+// double buffered over passes, cleared by the wave itself, 16 bytes per
+// lane), and every wave scans all copies (16-byte reads: four digits per
+// lane and copy) and finds the threshold bucket on its own, so nothing is
+// broadcast.
+__device__ __forceinline__ void topk_union_fast(int base, int c0, int c1, int topk, int cur, int n_init, int n_local,
+                                                int U, int32_t* idx_out, int32_t* cnt_out, TopkShared& sh,
                                                 const uint32_t (&kin)[8]) {
   constexpr int KPT = 8;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int i0 = tid * KPT;
+  const int i0 = base + tid * KPT;   // block id of this thread's first key
+  const int n = c1 - c0;
   uint32_t kr[KPT];
+  bool valid[KPT];
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) kr[e] = (i0 + e < n) ? kin[e] : 0u;
+  for (int e = 0; e < KPT; ++e) {
+    valid[e] = i0 + e >= c0 && i0 + e < c1;
+    kr[e] = valid[e] ? kin[e] : 0u;
+  }
   const bool take_none = topk <= 0 || n <= 0;
   const bool take_all = !take_none && n <= topk;
   uint32_t prefix = 0, mask = 0;
@@ -371,24 +378,25 @@ __device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur
       // operations of one wave complete in order); the other waves read them
       // only after the barrier, and reuse of this buffer two passes later is
       // behind the next pass's barrier
-      for (int i = lane; i < 2 * 256; i += kWave) (&h[wid][0][0])[i] = 0;
+      *reinterpret_cast<int4*>(&h[wid][0][4 * lane]) = make_int4(0, 0, 0, 0);
+      *reinterpret_cast<int4*>(&h[wid][1][4 * lane]) = make_int4(0, 0, 0, 0);
       int* mine = h[wid][lane & 1];
 #pragma unroll
       for (int e = 0; e < KPT; ++e)
-        if (i0 + e < n && (kr[e] & mask) == prefix) atomicAdd(&mine[(kr[e] >> shift) & 255u], 1);
+        if (valid[e] && (kr[e] & mask) == prefix) atomicAdd(&mine[(kr[e] >> shift) & 255u], 1);
       __syncthreads();
-      // lane l looks at digits 255-4l .. 252-4l (descending) over all copies
-      int c[4], ls = 0;
+      // lane l looks at digits 255-4l .. 252-4l (descending): bins 252-4l ..
+      // 255-4l of every copy
+      int4 sum = make_int4(0, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int D = 255 - 4 * lane - r;
-        int v = 0;
+      for (int w = 0; w < 4; ++w)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) v += h[w][0][D] + h[w][1][D];
-        c[r] = v;
-        ls += v;
-      }
-      int run = wave_excl_scan(ls);
+        for (int cp = 0; cp < 2; ++cp) {
+          const int4 x = *reinterpret_cast<const int4*>(&h[w][cp][252 - 4 * lane]);
+          sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+        }
+      const int c[4] = {sum.w, sum.z, sum.y, sum.x};
+      int run = wave_excl_scan(sum.x + sum.y + sum.z + sum.w);
       int pick = -1, below = 0, in_bucket = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -417,7 +425,7 @@ __device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur
   int gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    if (i0 + e < n && !take_none) {
+    if (valid[e] && !take_none) {
       if (take_all) ++gt;
       else {
         const uint32_t km = kr[e] & mask;
@@ -440,7 +448,7 @@ __device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur
   const int a = min(n_init, local_lo);          // initial blocks below the local window
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    if (i0 + e < n && !take_none) {
+    if (valid[e] && !take_none) {
       bool sel;
       int pos;
       if (take_all) {
@@ -452,7 +460,7 @@ __device__ __forceinline__ void topk_union_fast(int n, int c0, int topk, int cur
         else if (km == prefix) { sel = eq_b < need; pos = a + gt_b + eq_b; ++eq_b; }
         else { sel = false; pos = 0; }
       }
-      if (sel && pos < U) idx_out[pos] = c0 + i0 + e;
+      if (sel && pos < U) idx_out[pos] = i0 + e;
     }
   }
   const int n_loc = cur - local_lo + 1;
@@ -477,7 +485,7 @@ __device__ __forceinline__ void topk_union(const uint32_t* keys, int n, int c0, 
     const int i0 = (int)threadIdx.x * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) kin[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
-    topk_union_fast(n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+    topk_union_fast(c0, c0, c0 + n, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
   } else {
     topk_union_regs<48>(keys, n, c0, topk, cur, n_init, n_local, U, idx_out, cnt_out, sh);
   }

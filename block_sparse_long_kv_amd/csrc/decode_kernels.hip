@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void topk_decode_kernel(const float* __re
   __shared__ TopkShared sh;
   const int bg = blockIdx.x;
   const DecodeCands dc = decode_cands(seq_len[bg / H], nb_cap, n_init, n_local);
-  topk_decode_wg(sc + (int64_t)bg * nb_cap, dc, topk, n_init, n_local, U, idx + (int64_t)bg * U, cnt + bg, keys, sh);
+  topk_decode_wg(sc + (int64_t)bg * nb_cap, nb_cap, dc, topk, n_init, n_local, U, idx + (int64_t)bg * U, cnt + bg, keys, sh);
 }
 
 size_t score_decode_workspace_bytes(int B, int H, int64_t nb_cap) { return (size_t)B * H * nb_cap * sizeof(float); }

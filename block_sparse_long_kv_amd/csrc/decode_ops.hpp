@@ -388,13 +388,29 @@ __device__ __forceinline__ void score_slice_proj_wg(const float* __restrict__ pa
 // earlier kernel, or agent-coherent by this one when CO).  keys: LDS, at
 // least (c1 - c0) entries.
 template <bool CO = false>
-__device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, DecodeCands dc, int topk, int n_init,
+__device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, int64_t row_len, DecodeCands dc, int topk,
+                                               int n_init,
                                                int n_local, int U,
                                int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out, uint32_t* keys,
                                TopkShared& sh) {
   const int n = dc.c1 - dc.c0;
+  if (!CO && dc.c1 <= 8 * kThreads && (row_len & 3) == 0 && ((uintptr_t)sc & 15) == 0) {
+    // thread t's eight row entries (block ids 8t .. 8t+7) in two aligned
+    // 16-byte loads, none past the row (its length is a multiple of four);
+    // ids outside the candidates are masked
+    const int i0 = 8 * (int)threadIdx.x;
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (i0 < dc.c1) x0 = *reinterpret_cast<const float4*>(sc + i0);
+    if (i0 + 4 < dc.c1) x1 = *reinterpret_cast<const float4*>(sc + i0 + 4);
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t kin[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kin[e] = orderable_key(v[e]);
+    topk_union_fast(0, dc.c0, dc.c1, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+    return;
+  }
   if (n <= 8 * kThreads) {
-    // thread t's eight candidates (8t .. 8t+7) straight into registers
+    // thread t's eight candidates (c0 + 8t .. c0 + 8t + 7) straight into registers
     uint32_t kin[8];
     float v[8];
 #pragma unroll
@@ -404,7 +420,7 @@ __device__ __forceinline__ void topk_decode_wg(const float* __restrict__ sc, Dec
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) kin[e] = orderable_key(v[e]);
-    topk_union_fast(n, dc.c0, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
+    topk_union_fast(dc.c0, dc.c0, dc.c1, topk, dc.cur, n_init, n_local, U, idx_out, cnt_out, sh, kin);
     return;
   }
   constexpr int PB = 8;   // loads in flight per thread

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
     // this layer's top-k + union (the longer chain: its workgroups go first)
     const int bg = blockIdx.x;
     const DecodeCands dc = decode_cands(p.seq_len[bg / p.H], p.nb_cap, p.n_init, p.n_local);
-    topk_decode_wg(p.scores_in + (int64_t)bg * p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
+    topk_decode_wg(p.scores_in + (int64_t)bg * p.nb_cap, p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U,
                    p.idx + (int64_t)bg * p.U, p.cnt + bg, keys, sm.topk);
     return;
   }
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 3) void layer_k2(LayerParams p) {
                                  lo, hi, sc, sm.fvec);
     // the last score workgroup of (b, g): top-k + union of the next layer
     if (arrive_last(p.sync + n_bg + bg, p.score_splits, last_flag))
-      topk_decode_wg<true>(sc, dc, p.topk, p.n_init, p.n_local, p.U, p.idx_next + (int64_t)bg * p.U, p.cnt_next + bg,
+      topk_decode_wg<true>(sc, p.nb_cap, dc, p.topk, p.n_init, p.n_local, p.U, p.idx_next + (int64_t)bg * p.U, p.cnt_next + bg,
                            keys, sm.topk);
     return;
   }

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void topk_prefill_kernel(const float* __r
   dc.c0 = n_init;
   dc.c1 = (int)min((int64_t)(dc.cur - n_local + 1), nb_cap);
   if (dc.c1 < dc.c0) dc.c1 = dc.c0;
-  topk_decode_wg(sc + prob * nb_cap, dc, topk, n_init, n_local, U, idx_out + prob * U, cnt_out + prob, keys, sh);
+  topk_decode_wg(sc + prob * nb_cap, nb_cap, dc, topk, n_init, n_local, U, idx_out + prob * U, cnt_out + prob, keys, sh);
 }
 
 // fp: [B*H, n_qb, D] fp32 summed Forecasts; sc: workspace [B*H, n_qb, nb_cap]
