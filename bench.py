@@ -57,9 +57,9 @@ METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
 # An entry holds the digest of the sources it was measured on and is reported
 # only while they are unchanged.
 PMC_TRAFFIC = {
-    "layer_k2": {"fetch_kib": 106864.7, "write_kib": 2747.4, "fetch_scale": 2.0, "write_scale": 1.0,
+    "layer_k2": {"fetch_kib": 107386.1, "write_kib": 1207.7, "fetch_scale": 2.0, "write_scale": 1.0,
                  "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                 "sha256": "3c881fcc53099718bd71c11df7e5fd3fb155965427c53353275150940c651e84"},
+                 "sha256": "5795e259080ac44c9854c40d6a4f20b9015423f0bfca9d44fc78a3e07ec30e5c"},
     "attn_prefill": {"fetch_kib": 366773.6, "write_kib": 65536.8, "fetch_scale": 2.0, "write_scale": 1.0,
                      "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
                      "sha256": "020ed1804106f3d38f17f8f90df91fe42bd829bf4070ca593a700da6d8b81dbf"},
@@ -645,8 +645,20 @@ def check_step_outputs(torch, bench):
     return {"layers_checked": len(snap), "lists_equal": True, "outputs_bit_equal": True}
 
 
+def decode_select_mode(args, wl):
+    """The fused layer's top-k placement for a run: as given, or (auto) in
+    the next call's first kernel for 64 or more (b, g) units per layer and
+    in this call's second kernel below that (B8 x 128K: 1.47-1.48 vs
+    1.55-1.56 ms per step; B4 x 32K: 24.0 vs 26.1 us per layer-step, same
+    box)."""
+    if args.select_mode != "auto":
+        return args.select_mode
+    return "deferred" if wl.B * wl.Hkv >= 64 else "immediate"
+
+
 def run_decode(args, torch, bskv, wl, replicas=None):
-    bench = DecodeBench(wl, torch, bskv, layers=replicas, select_mode=args.select_mode)
+    mode = decode_select_mode(args, wl)
+    bench = DecodeBench(wl, torch, bskv, layers=replicas, select_mode=mode)
     step_fn = bench.step_per_op if args.per_op else bench.step
     step_s, _ = time_graph(torch, step_fn, args.steps, args.warmup, use_graph=not args.no_graph)
     log(f"[bench] decode step {step_s * 1e3:.3f} ms ({'graph' if not args.no_graph else 'eager'})")
@@ -682,7 +694,7 @@ def run_decode(args, torch, bskv, wl, replicas=None):
                    "head_dim": wl.d, "hidden": wl.hidden, "block": wl.block, "topk": wl.topk, "n_init": wl.n_init,
                    "n_local": wl.n_local, "hip_graph": not args.no_graph,
                    "path": "per-op" if args.per_op else "fused-layer",
-                   "next_layer_topk": None if args.per_op else args.select_mode},
+                   "next_layer_topk": None if args.per_op else mode},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(dom),
                      "bytes_per_launch": bpl[dom], "us_per_launch": round(kt[dom] * 1e6, 3)},
@@ -1408,7 +1420,8 @@ def side_decode_b4(args, torch, bskv, wl):
     k2 = r["kernels"]["layer_k2"]
     return {"workload": wl.name, "tokens_per_s": r["value"], "us_per_layer_step": round(r["ms_per_step"] * 1e3 / 8, 3),
             "step_hbm_frac": r["step_hbm_frac"], "layer_k2_us": k2["us"], "layer_k2_hbm_frac": k2["hbm_frac"],
-            "layer_k1_us": r["kernels"]["layer_k1"]["us"], "outputs_checked": r["post_timing_check"]}
+            "layer_k1_us": r["kernels"]["layer_k1"]["us"], "next_layer_topk": r["config"]["next_layer_topk"],
+            "outputs_checked": r["post_timing_check"]}
 
 
 def side_prefill(args, torch, bskv, wl):
@@ -1433,9 +1446,9 @@ def main():
     ap.add_argument("--drift", type=float, default=None,
                     help="offload-steady: random-walk step of the Forecast input per decode step")
     ap.add_argument("--per-op", action="store_true", help="time the per-operation calls instead of the fused layer")
-    ap.add_argument("--select-mode", default="deferred", choices=["deferred", "immediate"],
+    ap.add_argument("--select-mode", default="auto", choices=["auto", "deferred", "immediate"],
                     help="fused layer: the next layer's top-k in the next call's first kernel (deferred) or in this "
-                         "call's second kernel (immediate)")
+                         "call's second kernel (immediate); auto: deferred from 64 (b, g) units per layer up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
                     help="only the workload's own path: no comparison selectors, variants or widened projection "
