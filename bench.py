@@ -1199,7 +1199,7 @@ class SteadyOffloadBench:
     input of every layer drifts by a random walk from step to step, which
     sets how many selected blocks change per step."""
 
-    def __init__(self, wl, torch, bskv, n_steps, S=128, drift=None):
+    def __init__(self, wl, torch, bskv, n_steps, S=128, drift=None, fused_fill=True):
         from workloads import decode_inputs, drift_walk
         self.torch, self.bskv, self.wl = torch, bskv, wl
         self.dev = torch.device("cuda:0")
@@ -1265,7 +1265,7 @@ class SteadyOffloadBench:
                                     host_k_dev=self.dk[l % self.HL], host_v_dev=self.dv[l % self.HL])
                        for l in range(self.L)]
         self.sched = CachedLookahead(self.caches, self.slot, self.fill, [self.n_fill[l] for l in range(self.L)],
-                                     device=self.dev, n_workgroups=self.B * H)
+                                     device=self.dev, n_workgroups=self.B * H, fused_fill=fused_fill)
         torch.cuda.synchronize()
         log(f"[bench] steady offload set-up ({self.HL} host layers pinned, {self.L} caches of {S} slots, "
             f"{self.L * self.standin_bytes / 1e9:.1f} GB stand-in weights) in {time.time() - t0:.1f}s")
@@ -1310,7 +1310,7 @@ def run_offload_steady(args, torch, bskv, wl):
     n_comp = max(3, n // 2)
     wg_sweep, n_sweep = (16, 32, 64, 128), 4
     total = warm + len(wg_sweep) * n_sweep + n + 2 * n_comp
-    bench = SteadyOffloadBench(wl, torch, bskv, total, drift=args.drift)
+    bench = SteadyOffloadBench(wl, torch, bskv, total, drift=args.drift, fused_fill=args.offload_fill == "fused")
     sync = torch.cuda.synchronize
     graphs = {}
 
@@ -1389,7 +1389,8 @@ def run_offload_steady(args, torch, bskv, wl):
                    "n_local": wl.n_local, "planted": wl.plant, "cache_slots": bench.S, "drift": bench.drift,
                    "standin": "per layer x@W_qkv (4096x6144), o-proj (4096x4096), FFN gate+up (4096x28672), "
                               "down (14336x4096), bf16",
-                   "prefetch_workgroups": bench.n_wg, "hip_graph": not args.no_graph},
+                   "prefetch_workgroups": bench.n_wg, "hip_graph": not args.no_graph,
+                   "fill": args.offload_fill},
         "roofline": {"bound": "host-link", "kernel": "prefetch_cache_fill", "achieved": round(copy_gbps, 2)
                      if copy_gbps else None, "peak": 64.0, "unit": "GB/s",
                      "frac": round(copy_gbps / 64.0, 4) if copy_gbps else None, "traffic": None,
@@ -1449,6 +1450,9 @@ def main():
     ap.add_argument("--select-mode", default="auto", choices=["auto", "deferred", "immediate"],
                     help="fused layer: the next layer's top-k in the next call's first kernel (deferred) or in this "
                          "call's second kernel (immediate); auto: deferred from 64 (b, g) units per layer up")
+    ap.add_argument("--offload-fill", default="fused", choices=["fused", "stream"],
+                    help="offload-steady: copy layer l+1's missing blocks inside layer l's attention launch (fused) "
+                         "or on a copy stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
                     help="only the workload's own path: no comparison selectors, variants or widened projection "

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     block_cache_plan,
     block_sparse_attn_decode,
     block_sparse_attn_decode_cached,
+    block_sparse_attn_decode_cached_fill,
     block_sparse_attn_prefill,
     decode_layer_lookahead,
     decode_layer_lookahead_noalloc,

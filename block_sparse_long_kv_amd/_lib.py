@@ -61,6 +61,8 @@ _proto("bskv_prefetch_cache_fill", _i, _p, _p, _i, ctypes.POINTER(_i64), _i64, _
        _i, _i, _i, _p)
 _proto("bskv_block_sparse_attn_decode_cached", _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p,
        _p, _sz, _p)
+_proto("bskv_block_sparse_attn_decode_cached_fill", _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f,
+       _p, _p, _sz, _p, _p, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _p, _i, _i, _p)
 _proto("bskv_decode_layer_lookahead_workspace", _sz, _i, _i, _i, _i, _i, _i64, _i, _i)
 _proto("bskv_decode_layer_lookahead", _i, _p, _p, _p, _i, ctypes.POINTER(_i64), _i64, _p, _p, _p, _p, _p, _f, _p, _p,
        _p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i, _p, _sz, _p)
@@ -493,6 +495,45 @@ def block_sparse_attn_decode_cached(q, cache: "BlockCache", slot, idx, cnt, seq_
                                                     _ptr(idx), _ptr(cnt), _ptr(seq_len), B, Hq, Hkv, d, 64, U, scale,
                                                     _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), sh),
            "block_sparse_attn_decode_cached")
+    return out
+
+
+def block_sparse_attn_decode_cached_fill(q, cache: "BlockCache", slot, idx, cnt, seq_len, src_k, src_v, fill_idx,
+                                         fill_slot, fill, n_fill, fill_cache: "BlockCache", scale: float | None = None,
+                                         out=None, ws=None, n_fill_workgroups: int | None = None, stream=None,
+                                         src_k_dev: int | None = None, src_v_dev: int | None = None):
+    """block_sparse_attn_decode_cached of one layer, with the copy of another
+    layer's missing blocks (prefetch_cache_fill's arguments: its source K/V,
+    list fill_idx, plan outputs fill_slot / fill / n_fill, cache fill_cache)
+    in the same launch -> fp32 [B, Hq, d]."""
+    B, Hq, d = q.shape
+    Hkv = cache.H
+    U = idx.shape[-1]
+    if q.dtype != cache.k.dtype or not q.is_contiguous():
+        raise ValueError("q contiguous, of the cache's dtype")
+    if fill_idx.shape[-1] != U:
+        raise ValueError("fill_idx: the same list length U")
+    if src_k.stride() != src_v.stride():
+        raise ValueError("src_k/src_v: identical strides")
+    if src_k.is_cuda:
+        pk, pv = src_k.data_ptr(), src_v.data_ptr()
+    else:
+        if not (src_k.is_pinned() and src_v.is_pinned()):
+            raise ValueError("host sources must be pinned")
+        pk = src_k_dev if src_k_dev is not None else host_device_pointer(src_k)
+        pv = src_v_dev if src_v_dev is not None else host_device_pointer(src_v)
+    scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    lay = (B, Hq, Hkv, d, U)
+    nbytes = workspace_bytes("attn", *lay)
+    ws = ws if ws is not None else _workspace(q.device, nbytes, sh, "attn", lay)
+    nwg = n_fill_workgroups if n_fill_workgroups is not None else B * Hkv
+    _check(lib.bskv_block_sparse_attn_decode_cached_fill(
+        _ptr(q), _ptr(cache.k), _ptr(cache.v), _dt(q), cache.S, _ptr(slot), _ptr(idx), _ptr(cnt), _ptr(seq_len), B, Hq,
+        Hkv, d, 64, U, scale, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), pk, pv, _strides3(src_k),
+        src_k.shape[2], _ptr(fill_idx), _ptr(fill_slot), _ptr(fill), _ptr(n_fill), _ptr(fill_cache.k),
+        _ptr(fill_cache.v), fill_cache.S, nwg, sh), "block_sparse_attn_decode_cached_fill")
     return out
 
 

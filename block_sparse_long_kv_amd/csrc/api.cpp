@@ -358,6 +358,42 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
   return finish(bskv::launch_attn_decode(a));
 }
 
+int bskv_block_sparse_attn_decode_cached_fill(
+    const void* q, const void* cache_k, const void* cache_v, int dtype, int n_slots, const int32_t* slot,
+    const int32_t* idx, const int32_t* cnt, const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+    int block, int U, float scale, float* out, void* ws, size_t ws_bytes, const void* src_k, const void* src_v,
+    const int64_t* src_strides, int64_t src_len, const int32_t* fill_idx, const int32_t* fill_slot,
+    const int32_t* fill, const int32_t* n_fill, void* fill_cache_k, void* fill_cache_v, int fill_n_slots,
+    int n_fill_workgroups, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BSKV_EDTYPE;
+  if (!q || !cache_k || !cache_v || !slot || !idx || !cnt || !seq_len || !out || !ws) return BSKV_EINVAL;
+  if (!src_k || !src_v || !fill_idx || !fill_slot || !fill || !n_fill || !fill_cache_k || !fill_cache_v)
+    return BSKV_EINVAL;
+  if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(ws) || !aligned16(src_k) ||
+      !aligned16(src_v) || !aligned16(fill_cache_k) || !aligned16(fill_cache_v))
+    return BSKV_EINVAL;
+  // the filled cache is another layer's: this launch reads cache_k / cache_v
+  if (fill_cache_k == cache_k || fill_cache_v == cache_v || fill_cache_k == cache_v || fill_cache_v == cache_k)
+    return BSKV_EINVAL;
+  if (B <= 0 || U <= 0 || n_slots <= 0 || fill_n_slots <= 0 || n_fill_workgroups < 1 || src_len < 0 ||
+      !strides_ok(src_strides, dtype))
+    return BSKV_EINVAL;
+  if (!group_ok(n_q_heads, n_kv_heads)) return BSKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || block != 64) return BSKV_EUNSUPPORTED;
+  if (n_slots > kCacheMaxSlots || fill_n_slots > kCacheMaxSlots || (int64_t)B * n_kv_heads > 65535 ||
+      n_fill_workgroups > 65535)
+    return BSKV_EUNSUPPORTED;
+  if (!(scale > 0.f) || scale != scale) return BSKV_EINVAL;
+  if (ws_bytes < bskv::attn_decode_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, U)) return BSKV_ENOSPC;
+  const bskv::CacheFillArgs f{src_k, src_v, src_strides[0], src_strides[1], src_strides[2], src_len, esize_of(dtype),
+                              fill_idx, fill_slot, fill, n_fill, fill_cache_k, fill_cache_v, B, n_kv_heads, head_dim,
+                              block, U, fill_n_slots, n_fill_workgroups, stream};
+  const int64_t st = head_dim, sg = (int64_t)n_slots * block * head_dim, sb = sg * n_kv_heads;
+  bskv::AttnDecodeArgs a{q, cache_k, cache_v, dtype, sb, sg, st, (int64_t)n_slots * block, 1, idx, cnt, seq_len, B,
+                         n_q_heads, n_kv_heads, head_dim, block, U, scale, out, ws, stream, slot, &f};
+  return finish(bskv::launch_attn_decode(a));
+}
+
 int bskv_qkvf_proj_decode(const void* x, const void* w_t, int B, int hidden, int n_q_heads, int n_kv_heads,
                           int head_dim, void* q_out, void* k_cache, void* v_cache, const int64_t* kv_strides,
                           int64_t kv_len, const int64_t* seq_len, float* f_out, hipStream_t stream) {

@@ -94,6 +94,9 @@ struct MultiheadSelectArgs {
 size_t multihead_select_workspace_bytes(int B, int H, int64_t nb_cap);
 hipError_t launch_multihead_select(const MultiheadSelectArgs& a);
 
+struct CacheFillArgs;
+struct CacheFillParams;
+
 struct AttnDecodeArgs {
   const void* q; const void* k; const void* v; int dtype;
   int64_t sb, sg, st; int64_t kv_len; int ring;
@@ -102,6 +105,7 @@ struct AttnDecodeArgs {
   float* out; void* ws;
   hipStream_t stream;
   const int32_t* slot = nullptr;     // block cache: listed block u is read from slot[u] of k, v
+  const CacheFillArgs* fill = nullptr;   // another layer's cache fill in the split kernel's launch
 };
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int U);
 hipError_t launch_attn_decode(const AttnDecodeArgs& a);
@@ -147,6 +151,7 @@ struct CacheFillArgs {
   hipStream_t stream;
 };
 hipError_t launch_cache_fill(const CacheFillArgs& a);
+CacheFillParams make_fill_params(const CacheFillArgs& a);
 hipError_t launch_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int n_bg, int S, hipStream_t stream);
 
 // One decode layer with lookahead selection of the next layer (3 kernels).

@@ -9,6 +9,7 @@
 // Forecast head per GQA group" (Sec. 4.1), "The problem InfLLM-V2 leaves on
 // the table" (mean-pooled keys).
 #include "bskv_launch.hpp"
+#include "cache_fill.hpp"
 #include "decode_ops.hpp"
 
 namespace bskv {
@@ -166,6 +167,23 @@ __global__ __launch_bounds__(kThreads, 3) void attn_split_kernel(AttnDecodeParam
   attn_split_wg<T, D, G>(p, blockIdx.y, blockIdx.x, sm);
 }
 
+// The split kernel with another layer's cache fill in the same launch: the
+// first n_fill workgroups copy that layer's missing blocks (host reads with
+// long latency; dispatched first, they overlap the whole attention), the
+// rest are the attention splits of this layer.
+template <typename T, int D, int G, int CPT>
+__global__ __launch_bounds__(kThreads, 3) void attn_split_fill_kernel(AttnDecodeParams p, CacheFillParams f,
+                                                                     int n_fill) {
+  __shared__ typename AttnSmemSel<T, D, G>::type sm;
+  const int bid = (int)blockIdx.x;
+  if (bid < n_fill) {
+    cache_fill_wg<CPT>(f, bid, n_fill);
+    return;
+  }
+  const int a = bid - n_fill;
+  attn_split_wg<T, D, G>(p, a / p.n_splits, a % p.n_splits, sm);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnDecodeParams p) {
   __shared__ CombineSmem<D, G> sm;
@@ -184,7 +202,11 @@ AttnDecodeParams make_attn_params(const AttnDecodeArgs& a, void* ws) {
   AttnDecodeParams p;
   int ns, bps;
   const int n_bg = a.B * a.Hkv, G = a.Hq / a.Hkv;
-  attn_split_plan(n_bg, a.U, ns, bps);
+  // a cache fill in the same launch takes its workgroups first; the split
+  // count never exceeds the workspace's (sized without a reserve)
+  int reserve = 0;
+  if (a.fill) reserve = a.fill->n_workgroups < n_bg ? a.fill->n_workgroups : n_bg;
+  attn_split_plan(n_bg, a.U, ns, bps, reserve);
   p.q = a.q; p.k = a.k; p.v = a.v;
   p.sb = a.sb; p.sg = a.sg; p.st = a.st; p.kv_len = a.kv_len; p.ring = a.ring; p.slot = a.slot;
   p.idx = a.idx; p.cnt = a.cnt; p.seq_len = a.seq_len;
@@ -199,18 +221,32 @@ AttnDecodeParams make_attn_params(const AttnDecodeArgs& a, void* ws) {
 }
 
 template <typename T, int D, int G>
-static void launch_attn_t(const AttnDecodeParams& p, int n_bg, hipStream_t s) {
-  hipLaunchKernelGGL((attn_split_kernel<T, D, G>), dim3(p.n_splits, n_bg), dim3(kThreads), 0, s, p);
+static void launch_attn_t(const AttnDecodeParams& p, int n_bg, const CacheFillArgs* fill, hipStream_t s) {
+  if (fill) {
+    const CacheFillParams f = make_fill_params(*fill);
+    const int n_fill = fill->n_workgroups < f.n_bg ? fill->n_workgroups : f.n_bg;
+    const dim3 grid(n_fill + p.n_splits * n_bg);
+    // chunks per block = 64 rows x (head_dim x element size / 16) = 512, 1024 or 2048
+    const int per_item = fill->block * f.row16;
+    if (per_item == 2 * kThreads)
+      hipLaunchKernelGGL((attn_split_fill_kernel<T, D, G, 2>), grid, dim3(kThreads), 0, s, p, f, n_fill);
+    else if (per_item == 4 * kThreads)
+      hipLaunchKernelGGL((attn_split_fill_kernel<T, D, G, 4>), grid, dim3(kThreads), 0, s, p, f, n_fill);
+    else
+      hipLaunchKernelGGL((attn_split_fill_kernel<T, D, G, 8>), grid, dim3(kThreads), 0, s, p, f, n_fill);
+  } else {
+    hipLaunchKernelGGL((attn_split_kernel<T, D, G>), dim3(p.n_splits, n_bg), dim3(kThreads), 0, s, p);
+  }
   hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3(n_bg), dim3(kThreads), 0, s, p);
 }
 
 template <typename T, int D>
-static void launch_attn_g(const AttnDecodeParams& p, int G, int n_bg, hipStream_t s) {
+static void launch_attn_g(const AttnDecodeParams& p, int G, int n_bg, const CacheFillArgs* fill, hipStream_t s) {
   switch (G) {
-    case 1: launch_attn_t<T, D, 1>(p, n_bg, s); break;
-    case 2: launch_attn_t<T, D, 2>(p, n_bg, s); break;
-    case 4: launch_attn_t<T, D, 4>(p, n_bg, s); break;
-    default: launch_attn_t<T, D, 8>(p, n_bg, s); break;
+    case 1: launch_attn_t<T, D, 1>(p, n_bg, fill, s); break;
+    case 2: launch_attn_t<T, D, 2>(p, n_bg, fill, s); break;
+    case 4: launch_attn_t<T, D, 4>(p, n_bg, fill, s); break;
+    default: launch_attn_t<T, D, 8>(p, n_bg, fill, s); break;
   }
 }
 
@@ -218,11 +254,11 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a) {
   const AttnDecodeParams p = make_attn_params(a, a.ws);
   const int n_bg = a.B * a.Hkv, G = a.Hq / a.Hkv;
   if (a.dtype == 0) {
-    if (a.D == 64) launch_attn_g<float, 64>(p, G, n_bg, a.stream);
-    else launch_attn_g<float, 128>(p, G, n_bg, a.stream);
+    if (a.D == 64) launch_attn_g<float, 64>(p, G, n_bg, a.fill, a.stream);
+    else launch_attn_g<float, 128>(p, G, n_bg, a.fill, a.stream);
   } else {
-    if (a.D == 64) launch_attn_g<bf16_bits, 64>(p, G, n_bg, a.stream);
-    else launch_attn_g<bf16_bits, 128>(p, G, n_bg, a.stream);
+    if (a.D == 64) launch_attn_g<bf16_bits, 64>(p, G, n_bg, a.fill, a.stream);
+    else launch_attn_g<bf16_bits, 128>(p, G, n_bg, a.fill, a.stream);
   }
   return hipGetLastError();
 }

@@ -1093,10 +1093,15 @@ __device__ __forceinline__ void attn_combine_wg(const AttnDecodeParams& p, int b
 // 18 blocks) beside 512 score workgroups fill the 768 slots and ran the step
 // 6% faster than 192 or 512 attention workgroups, 13% faster than 320, 22%
 // faster than 128 (same box, top-k in the launch's tail).  Above 64
-// units the earlier 768 is kept (at B16 it gives 6 splits).
-__host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps) {
-  const int target = n_bg <= 64 ? 256 : 768;
-  int ns = (target + n_bg - 1) / n_bg;
+// units the earlier 768 is kept (at B16 it gives 6 splits).  `reserve`:
+// workgroups of other work in the same launch; the attention then keeps to
+// the 768 slots left beside them (at most one split per unit fewer than
+// without), so none of its workgroups waits for a slot to free up.
+__host__ __device__ inline void attn_split_plan(int n_bg, int U, int& n_splits, int& bps, int reserve = 0) {
+  int target = n_bg <= 64 ? 256 : 768;
+  if (reserve > 0 && target > 768 - reserve) target = 768 - reserve;
+  int ns = target / n_bg;
+  if (reserve <= 0 || ns < 1) ns = (target + n_bg - 1) / n_bg;
   if (ns > U) ns = U;
   if (ns > kMaxSplitsDecode) ns = kMaxSplitsDecode;
   if (ns < 1) ns = 1;

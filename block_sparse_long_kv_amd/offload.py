@@ -18,7 +18,9 @@ waits for that copy before layer l+1 attends; Chinese SparDA overview,
                     has attended.
 ``CachedLookahead`` each layer keeps a resident cache of blocks per (b, g);
                     the lookup of layer l+1's list names the missing blocks,
-                    and only those are copied (steady state).
+                    and only those are copied (steady state): on the copy
+                    stream, or (fused_fill) by extra workgroups of layer l's
+                    attention launch on the compute stream.
 
 Both take per-layer inputs as ``OffloadLayer`` records and run eagerly or
 under HIP-graph capture (all ordering is by events on the two streams).
@@ -65,10 +67,13 @@ class OffloadLayer:
     host_v_dev: Optional[int] = None
 
     def device_pointers(self):
+        """Device addresses of the K/V source (its own for device tensors)."""
         if self.host_k_dev is None:
-            self.host_k_dev = _lib.host_device_pointer(self.host_k)
+            self.host_k_dev = (self.host_k.data_ptr() if self.host_k.is_cuda
+                               else _lib.host_device_pointer(self.host_k))
         if self.host_v_dev is None:
-            self.host_v_dev = _lib.host_device_pointer(self.host_v)
+            self.host_v_dev = (self.host_v.data_ptr() if self.host_v.is_cuda
+                               else _lib.host_device_pointer(self.host_v))
         return self.host_k_dev, self.host_v_dev
 
 
@@ -177,13 +182,20 @@ class CachedLookahead:
 
     caches: one BlockCache per layer.  slot, fill, n_fill: per-layer lookup
     outputs ([B, Hkv, U] int32 twice, [B, Hkv] int32).
+    fused_fill: the copy of layer l+1's missing blocks runs inside layer l's
+    attention launch (bskv_block_sparse_attn_decode_cached_fill: its first
+    n_workgroups workgroups copy while the rest attend), all on the compute
+    stream: no copy stream and no cross-stream waits; layer 0's copy runs on
+    its own ahead of the layers.
     """
 
     def __init__(self, caches: Sequence["_lib.BlockCache"], slot, fill, n_fill, device="cuda",
-                 n_workgroups: int = 128, copy_stream: Optional[torch.cuda.Stream] = None):
+                 n_workgroups: int = 128, copy_stream: Optional[torch.cuda.Stream] = None, fused_fill: bool = False):
         self.device = torch.device(device)
         self.caches, self.slot, self.fill, self.n_fill = list(caches), list(slot), list(fill), list(n_fill)
-        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(self.device)
+        self.fused_fill = fused_fill
+        self.copy_stream = None if fused_fill else (copy_stream if copy_stream is not None
+                                                    else torch.cuda.Stream(self.device))
         self.n_workgroups = n_workgroups
         self._events = {}
 
@@ -209,6 +221,14 @@ class CachedLookahead:
         _lib.block_sparse_attn_decode_cached(lay.q, self.caches[l], self.slot[l], lay.idx, lay.cnt, lay.seq_len,
                                              scale, out=lay.out, ws=ws_attn)
 
+    def attend_and_fill(self, lay: OffloadLayer, l: int, nxt: OffloadLayer, scale: float, ws_attn=None):
+        """Attention of layer l with the copy of layer l+1's missing blocks in the same launch."""
+        dk, dv = nxt.device_pointers()
+        _lib.block_sparse_attn_decode_cached_fill(
+            lay.q, self.caches[l], self.slot[l], lay.idx, lay.cnt, lay.seq_len, nxt.host_k, nxt.host_v, nxt.idx,
+            self.slot[l + 1], self.fill[l + 1], self.n_fill[l + 1], self.caches[l + 1], scale=scale, out=lay.out,
+            ws=ws_attn, n_fill_workgroups=self.n_workgroups, src_k_dev=dk, src_v_dev=dv)
+
     def step(self, layers: Sequence[OffloadLayer], topk: int, n_init: int, n_local: int, scale: float,
              ws_proj=None, ws_score=None, ws_attn=None, with_copy: bool = True,
              before_layer: Optional[Callable[[int], None]] = None,
@@ -220,10 +240,31 @@ class CachedLookahead:
         lookup exists, the copy of its missing blocks; then, once layer l's
         copy has landed, layer l's attention from its cache and
         after_layer(l).  on_fill(l, copy_stream) runs right before the copy
-        of layer l is issued, with the copy stream current."""
+        of layer l is issued, with the copy stream current (fused_fill: the
+        compute stream, before the launch that carries the copy)."""
+        L = len(layers)
+        if self.fused_fill:
+            self.plan(layers[0], 0, topk, n_init, n_local, ws_proj, ws_score)
+            if with_copy:
+                if on_fill is not None:
+                    on_fill(0, torch.cuda.current_stream(self.device))
+                self.fill_cache(layers[0], 0)
+            for l in range(L):
+                if before_layer is not None:
+                    before_layer(l)
+                if l + 1 < L:
+                    self.plan(layers[l + 1], l + 1, topk, n_init, n_local, ws_proj, ws_score)
+                if with_copy and l + 1 < L:
+                    if on_fill is not None:
+                        on_fill(l + 1, torch.cuda.current_stream(self.device))
+                    self.attend_and_fill(layers[l], l, layers[l + 1], scale, ws_attn)
+                else:
+                    self.attend(layers[l], l, scale, ws_attn)
+                if after_layer is not None:
+                    after_layer(l)
+            return
         comp = torch.cuda.current_stream(self.device)
         cs = self.copy_stream
-        L = len(layers)
 
         def issue(l):
             self.plan(layers[l], l, topk, n_init, n_local, ws_proj, ws_score)

@@ -397,9 +397,21 @@ int bskv_forecast_block_score_topk_pooled(const float* f_pooled, int n_qb, int64
  * bskv_block_sparse_attn_decode_cached: bskv_block_sparse_attn_decode with
  *   listed block u (logical id idx[u], masked by seq_len) read from cache slot
  *   slot[u]; ws as bskv_attn_decode_workspace().
+ * bskv_block_sparse_attn_decode_cached_fill: bskv_block_sparse_attn_decode_cached
+ *   of one layer with the copy of another layer's missing blocks
+ *   (bskv_prefetch_cache_fill's arguments, prefixed fill_: the source K/V,
+ *   that layer's list fill_idx, fill_slot, fill, n_fill from its plan, and
+ *   its cache fill_cache_k / fill_cache_v of fill_n_slots slots; same dtype,
+ *   B, heads, head_dim, block and U) in the same launch: the first
+ *   n_fill_workgroups workgroups copy while the rest attend.  For a
+ *   one-layer-ahead schedule on one stream: attention of layer l carries the
+ *   copy of layer l+1's blocks, so no second stream and no cross-stream wait
+ *   is needed.  The filled cache must not be the one this call reads
+ *   (EINVAL for the same pointers; partial overlap is not checked).
  * Ordering is the caller's: plan on the compute stream after the selection,
- * fill on the copy stream after the plan, attend after the fill; a layer's
- * plan must follow that layer's previous attention (slots are reused).
+ * fill on the copy stream after the plan (or inside the previous layer's
+ * attention launch), attend after the fill; a layer's plan must follow that
+ * layer's previous attention (slots are reused).
  * ----------------------------------------------------------------------- */
 int bskv_block_cache_reset(int32_t* tags, int64_t* stamps, int64_t* clock, int B, int n_kv_heads, int n_slots,
                            hipStream_t stream);
@@ -415,6 +427,13 @@ int bskv_block_sparse_attn_decode_cached(const void* q, const void* cache_k, con
                                          const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
                                          int block, int U, float scale, float* out, void* ws, size_t ws_bytes,
                                          hipStream_t stream);
+int bskv_block_sparse_attn_decode_cached_fill(
+    const void* q, const void* cache_k, const void* cache_v, int dtype, int n_slots, const int32_t* slot,
+    const int32_t* idx, const int32_t* cnt, const int64_t* seq_len, int B, int n_q_heads, int n_kv_heads, int head_dim,
+    int block, int U, float scale, float* out, void* ws, size_t ws_bytes, const void* src_k, const void* src_v,
+    const int64_t* src_strides, int64_t src_len, const int32_t* fill_idx, const int32_t* fill_slot,
+    const int32_t* fill, const int32_t* n_fill, void* fill_cache_k, void* fill_cache_v, int fill_n_slots,
+    int n_fill_workgroups, hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
  * One decode layer with one-layer-ahead selection.  [EXPL] "The fourth

@@ -204,6 +204,25 @@ def test_block_cache_validation():
     assert call(S=2048) == EUNSUP
     assert call(sc=0.0) == EINVAL
     assert call(wsb=ws - 4) == ENOSPC
+    # attention of one layer with another layer's cache fill in the same launch
+    af = lib.bskv_block_sparse_attn_decode_cached_fill
+    P2 = 0x20000
+
+    def fcall2(dt=1, d=128, S=128, fS=128, slot=P, fill=P, fck=P2, fcv=P2 + 0x100, src=P, nwg=64, sc=0.088, wsb=ws):
+        return af(P, P, P + 0x100, dt, S, slot, P, P, P, 2, 32, 8, d, 64, 69, sc, P, P, wsb, src, P, S3, 131072, P, P,
+                  fill, P, fck, fcv, fS, nwg, None)
+    assert fcall2(dt=5) == EDTYPE
+    assert fcall2(slot=None) == EINVAL
+    assert fcall2(fill=None) == EINVAL
+    assert fcall2(src=MIS) == EINVAL
+    assert fcall2(fck=P) == EINVAL            # fills the cache this call reads
+    assert fcall2(fcv=P + 0x100) == EINVAL
+    assert fcall2(nwg=0) == EINVAL
+    assert fcall2(fS=0) == EINVAL
+    assert fcall2(d=96) == EUNSUP
+    assert fcall2(fS=2048) == EUNSUP
+    assert fcall2(sc=0.0) == EINVAL
+    assert fcall2(wsb=ws - 4) == ENOSPC
 
 
 def test_qkvf_proj_validation():

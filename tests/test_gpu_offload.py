@@ -163,13 +163,15 @@ def test_ring_schedule_graph_replays():
         _check_layer(layers[l], sel, want, o_layers[l])
 
 
-def test_cached_schedule_over_steps_matches_oracle():
+@pytest.mark.parametrize("fused", [False, True])
+def test_cached_schedule_over_steps_matches_oracle(fused):
     """Steady state: 4 layers, 3 decode steps with the Forecast inputs
     drifting, a resident cache of 2U slots per (b, g) and layer, a delay on
-    the copy stream ahead of every fill.  Every layer of every step matches
-    the oracle's one-layer-ahead step on that step's inputs, and later steps
-    copy only part of each union (no planted blocks here, so the drift moves
-    some selections)."""
+    the copy stream ahead of every fill (fused: the copy of layer l+1 inside
+    layer l's attention launch, the delay on the compute stream before it).
+    Every layer of every step matches the oracle's one-layer-ahead step on
+    that step's inputs, and later steps copy only part of each union (no
+    planted blocks here, so the drift moves some selections)."""
     n_layers, n_steps, S = 4, 3, 2 * U
     cases, layers = _layers(n_layers, 700, plant=0)
     x0 = torch.stack([c["x_sel"] for c in cases])                      # [L, B, hidden]
@@ -181,7 +183,7 @@ def test_cached_schedule_over_steps_matches_oracle():
     slot = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(n_layers)]
     fill = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(n_layers)]
     n_fill = [torch.empty(B, HKV, dtype=torch.int32, device=DEV) for _ in range(n_layers)]
-    sched = CachedLookahead(caches, slot, fill, n_fill, device=DEV, n_workgroups=8)
+    sched = CachedLookahead(caches, slot, fill, n_fill, device=DEV, n_workgroups=8, fused_fill=fused)
 
     def delay(l, stream):
         torch.cuda._sleep(DELAY_CYCLES // 2)
@@ -201,3 +203,42 @@ def test_cached_schedule_over_steps_matches_oracle():
     total = n_layers * B * HKV * U
     assert fetched[0] == total, "the first step copies every listed block"
     assert all(0 < f < total for f in fetched[1:]), fetched
+
+
+def test_cached_attention_with_fill_equals_separate_calls():
+    """One launch (attention of layer 0 from its cache + copy of layer 1's
+    missing blocks) gives the same attention output and the same layer-1
+    cache, bit for bit, as the fill and the attention called separately."""
+    cases, layers = _layers(2, 800)
+    S = 2 * U
+    ws = _workspaces()
+    outs, cache_bytes = [], []
+    for fused in (False, True):
+        caches = [bskv.BlockCache(B, HKV, S, D, device=DEV) for _ in range(2)]
+        slot = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(2)]
+        fill = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(2)]
+        n_fill = [torch.empty(B, HKV, dtype=torch.int32, device=DEV) for _ in range(2)]
+        sched = CachedLookahead(caches, slot, fill, n_fill, device=DEV, n_workgroups=5)
+        for l in range(2):
+            sched.plan(layers[l], l, TOPK, N_INIT, N_LOCAL, ws["ws_proj"], ws["ws_score"])
+        sched.fill_cache(layers[0], 0)
+        layers[0].out.fill_(float("nan"))
+        if fused:
+            sched.attend_and_fill(layers[0], 0, layers[1], SCALE, ws["ws_attn"])
+        else:
+            sched.fill_cache(layers[1], 1)
+            sched.attend(layers[0], 0, SCALE, ws["ws_attn"])
+        torch.cuda.synchronize()
+        outs.append(layers[0].out.clone())
+        # the listed slots of layer 1 (the rest of the cache is never written)
+        sl = slot[1].long().clamp(min=0)
+        got = [c.gather(2, sl[..., None, None].expand(-1, -1, -1, 64, D)) for c in (caches[1].k, caches[1].v)]
+        cache_bytes.append(got)
+        assert int(n_fill[1].sum()) == B * HKV * U, "a first lookup copies every listed block"
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(cache_bytes[0][0], cache_bytes[1][0]) and torch.equal(cache_bytes[0][1], cache_bytes[1][1])
+    # and the filled blocks are the host blocks the list names
+    idx1 = layers[1].idx.cpu().long()
+    hk = layers[1].host_k.view(B, HKV, T // 64, 64, D)
+    want = torch.stack([torch.stack([hk[b, g, idx1[b, g]] for g in range(HKV)]) for b in range(B)])
+    assert torch.equal(cache_bytes[1][0].cpu(), want)
