@@ -40,7 +40,12 @@ constexpr int kMaxSplitsDecode = 32;   // attention splits per KV head
 // passes of kProjPass rows that reuse those registers; the 16 row lanes are
 // added through LDS, one barrier pair per pass.
 // ---------------------------------------------------------------------------
-constexpr int kProjRows = 128;   // rows of W per split
+// 256 rows of W per split: at hidden 4096 that is 16 splits x 8 column tiles =
+// 128 workgroups (bf16), which with the decode top-k's 64 workgroups in the
+// fused layer's first kernel leaves every workgroup a CU of its own (B8 x
+// 128K: first kernel 6.1-6.2 vs 7.1 us, step 1.417-1.423 vs 1.444-1.468 ms
+// against 128 rows; 512 rows 1.48-1.50 ms)
+constexpr int kProjRows = 256;
 constexpr int kProjPass = 4;     // batch rows per pass
 constexpr int kProjMaxB = 16;    // batch rows staged in LDS per round
 

@@ -86,15 +86,21 @@ def test_noalloc_layer_equals_the_workspace_call(mode):
 
 
 def test_noalloc_layer_rejects_a_layer_too_large_for_the_array():
+    cap = bskv.lib.bskv_decode_layer_lookahead_noalloc_capacity()
+    # the smallest compressed-key capacity (a multiple of 1024 blocks) whose
+    # layer workspace exceeds the array
+    nb = 1024
+    while bskv.workspace_bytes("layer", 64, 32, 8, 128, 4096, nb, 69, 1) <= cap:
+        nb += 1024
     q = torch.zeros(64, 32, 128, dtype=torch.bfloat16, device=DEV)
     k = torch.zeros(64, 8, 64 * 64, 128, dtype=torch.bfloat16, device=DEV)
-    kc = torch.zeros(64, 8, 4096, 128, dtype=torch.float32, device=DEV)     # 4096-block capacity
+    kc = torch.zeros(64, 8, nb, 128, dtype=torch.float32, device=DEV)
     idx = torch.zeros(64, 8, 69, dtype=torch.int32, device=DEV)
     cnt = torch.zeros(64, 8, dtype=torch.int32, device=DEV)
     lens = torch.full((64,), 64 * 64, dtype=torch.int64, device=DEV)
     x = torch.zeros(64, 4096, dtype=torch.bfloat16, device=DEV)
     w = torch.zeros(4096, 1024, dtype=torch.bfloat16, device=DEV)
-    assert bskv.workspace_bytes("layer", 64, 32, 8, 128, 4096, 4096, 69, 1) > bskv.lib.bskv_decode_layer_lookahead_noalloc_capacity()
+    assert bskv.workspace_bytes("layer", 64, 32, 8, 128, 4096, nb, 69, 1) > cap
     with pytest.raises(bskv.BskvError) as ei:
         bskv.decode_layer_lookahead_noalloc(q, k, k, lens, kc, idx, cnt, x=x, w=w, kc_next=kc.clone(), topk=64,
                                             n_init=1, n_local=4)
