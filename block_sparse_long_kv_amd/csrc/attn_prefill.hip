@@ -50,8 +50,12 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& r) { return __builtin_bit_cast(bf16x8_t, r); }
 
+// Two workgroups per CU for one and two heads per workgroup (two LDS stages
+// each), one for four (four stages, 128 KB); at head_dim 128 the one-head
+// form needs ~390 registers per lane (its 8 copy pieces per wave and tile add
+// address registers), so it runs one wave per SIMD and is declared so.
 template <int D, int HPW>
-__global__ __launch_bounds__(HPW * 128, 2) void attn_prefill_kernel(
+__global__ __launch_bounds__(HPW * 128, (HPW == 1 && D == 128) ? 1 : 2) void attn_prefill_kernel(
     const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v, int64_t sb,
     int64_t sg, int64_t st, int64_t kv_len, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int64_t q_start, int Tq, int Hkv, int G, int U, int n_qb, float qscale, bf16_bits* __restrict__ out) {

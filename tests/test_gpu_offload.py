@@ -242,3 +242,72 @@ def test_cached_attention_with_fill_equals_separate_calls():
     hk = layers[1].host_k.view(B, HKV, T // 64, 64, D)
     want = torch.stack([torch.stack([hk[b, g, idx1[b, g]] for g in range(HKV)]) for b in range(B)])
     assert torch.equal(cache_bytes[1][0].cpu(), want)
+
+
+def test_cached_attention_with_fill_short_lists_and_many_fill_workgroups():
+    """Short sequences (fewer candidates than k: lists padded with -1 past
+    cnt) and more fill workgroups than (b, g) units: the fused call still
+    equals the separate calls bit for bit, and its attention matches the
+    oracle on the GPU's lists."""
+    T2, lens2 = 64 * 12, [64 * 12, 64 * 7 - 5]
+    layers, cases = [], []
+    for l in range(2):
+        c = random_decode_case(900 + l, B=B, Hq=HQ, Hkv=HKV, d=D, T=T2, dtype="bf16", hidden=HID, seq_len=lens2,
+                               topk=TOPK, n_init=N_INIT, n_local=N_LOCAL)
+        hk = torch.empty(c["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty(c["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+        hk.copy_(c["k"])
+        hv.copy_(c["v"])
+        seq_len = c["seq_len"].to(DEV)
+        kc = torch.full((B, HKV, T2 // 64, D), float("nan"), dtype=torch.float32, device=DEV)
+        bskv.kv_block_meanpool(c["k"].to(DEV), seq_len, kc)
+        layers.append(OffloadLayer(
+            hk, hv, kc, c["x_sel"].to(DEV), c["w_sel"].to(DEV), c["q"].to(DEV), seq_len,
+            f=torch.empty(B, HKV, D, dtype=torch.float32, device=DEV),
+            idx=torch.empty(B, HKV, U, dtype=torch.int32, device=DEV),
+            cnt=torch.empty(B, HKV, dtype=torch.int32, device=DEV),
+            out=torch.empty(B, HQ, D, dtype=torch.float32, device=DEV)))
+        cases.append(c)
+    z = lambda n: torch.zeros(max(int(n), 256), dtype=torch.uint8, device=DEV)  # noqa: E731
+    ws = {"ws_proj": z(bskv.workspace_bytes("proj", B, HID, HKV, D, 1)),
+          "ws_score": z(bskv.workspace_bytes("score", B, HKV, 0, T2 // 64, D)),
+          "ws_attn": z(bskv.workspace_bytes("attn", B, HQ, HKV, D, U))}
+    S = U
+    outs, filled = [], []
+    for fused in (False, True):
+        caches = [bskv.BlockCache(B, HKV, S, D, device=DEV) for _ in range(2)]
+        slot = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(2)]
+        fill = [torch.empty(B, HKV, U, dtype=torch.int32, device=DEV) for _ in range(2)]
+        n_fill = [torch.empty(B, HKV, dtype=torch.int32, device=DEV) for _ in range(2)]
+        sched = CachedLookahead(caches, slot, fill, n_fill, device=DEV, n_workgroups=1000)
+        for l in range(2):
+            sched.plan(layers[l], l, TOPK, N_INIT, N_LOCAL, ws["ws_proj"], ws["ws_score"])
+        sched.fill_cache(layers[0], 0)
+        layers[0].out.fill_(float("nan"))
+        if fused:
+            sched.attend_and_fill(layers[0], 0, layers[1], SCALE, ws["ws_attn"])
+        else:
+            sched.fill_cache(layers[1], 1)
+            sched.attend(layers[0], 0, SCALE, ws["ws_attn"])
+        torch.cuda.synchronize()
+        outs.append(layers[0].out.clone())
+        cnt1 = layers[1].cnt.cpu()
+        assert int(cnt1.min()) < U, "some lists are padded"
+        assert torch.equal(n_fill[1].cpu(), cnt1), "a first lookup copies every listed block"
+        # the listed slots of layer 1 (entries past cnt name no slot)
+        got = []
+        sl, c1 = slot[1].cpu(), cnt1
+        for b in range(B):
+            for g in range(HKV):
+                for u in range(int(c1[b, g])):
+                    s_ = int(sl[b, g, u])
+                    got.append((caches[1].k[b, g, s_].cpu(), caches[1].v[b, g, s_].cpu()))
+        filled.append(got)
+    assert torch.equal(outs[0], outs[1])
+    assert all(torch.equal(a[0], b_[0]) and torch.equal(a[1], b_[1]) for a, b_ in zip(filled[0], filled[1]))
+    gi, gc = layers[0].idx.cpu().numpy(), layers[0].cnt.cpu().numpy()
+    k0, v0 = np64(cases[0]["k"]), np64(cases[0]["v"])
+    want = orc.attend_decode(np64(cases[0]["q"]), k0, v0, gi, gc, np.array(lens2), SCALE, 64)
+    got = np64(outs[1])
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) < 2e-2
