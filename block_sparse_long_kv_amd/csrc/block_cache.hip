@@ -135,11 +135,12 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
   }
 }
 
-// Copy of the missing blocks into their slots: workgroup w takes the (b, g)
-// w, w + grid, ... (cache_fill_wg).
+// Copy of the missing blocks into their slots, dealt out over the grid
+// (cache_fill_wg).
 template <int CPT>
 __global__ __launch_bounds__(kThreads) void cache_fill_kernel(CacheFillParams f) {
-  cache_fill_wg<CPT>(f, blockIdx.x, gridDim.x);
+  __shared__ CacheFillSmem sm;
+  cache_fill_wg<CPT>(f, blockIdx.x, gridDim.x, sm);
 }
 
 CacheFillParams make_fill_params(const CacheFillArgs& a) {

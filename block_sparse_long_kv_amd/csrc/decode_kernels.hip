@@ -161,10 +161,13 @@ hipError_t launch_score_topk_decode(const ScoreTopkArgs& a) {
 }
 
 // ------------------------------------------------------------------ decode attention
+// grid (units, splits): the workgroups of one split are consecutive, so
+// the XCDs, dealt consecutive workgroups in turn, all get the same mix of
+// long and short splits
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads, 3) void attn_split_kernel(AttnDecodeParams p) {
   __shared__ typename AttnSmemSel<T, D, G>::type sm;
-  attn_split_wg<T, D, G>(p, blockIdx.y, blockIdx.x, sm);
+  attn_split_wg<T, D, G>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 // The split kernel with another layer's cache fill in the same launch: the
@@ -174,14 +177,17 @@ __global__ __launch_bounds__(kThreads, 3) void attn_split_kernel(AttnDecodeParam
 template <typename T, int D, int G, int CPT>
 __global__ __launch_bounds__(kThreads, 3) void attn_split_fill_kernel(AttnDecodeParams p, CacheFillParams f,
                                                                      int n_fill) {
-  __shared__ typename AttnSmemSel<T, D, G>::type sm;
+  __shared__ union {
+    typename AttnSmemSel<T, D, G>::type attn;
+    CacheFillSmem fill;
+  } sm;
   const int bid = (int)blockIdx.x;
   if (bid < n_fill) {
-    cache_fill_wg<CPT>(f, bid, n_fill);
+    cache_fill_wg<CPT>(f, bid, n_fill, sm.fill);
     return;
   }
-  const int a = bid - n_fill;
-  attn_split_wg<T, D, G>(p, a / p.n_splits, a % p.n_splits, sm);
+  const int a = bid - n_fill, n_bg = ((int)gridDim.x - n_fill) / p.n_splits;   // split-major, as above
+  attn_split_wg<T, D, G>(p, a % n_bg, a / n_bg, sm.attn);
 }
 
 template <int D, int G>
@@ -235,7 +241,7 @@ static void launch_attn_t(const AttnDecodeParams& p, int n_bg, const CacheFillAr
     else
       hipLaunchKernelGGL((attn_split_fill_kernel<T, D, G, 8>), grid, dim3(kThreads), 0, s, p, f, n_fill);
   } else {
-    hipLaunchKernelGGL((attn_split_kernel<T, D, G>), dim3(p.n_splits, n_bg), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<T, D, G>), dim3(n_bg, p.n_splits), dim3(kThreads), 0, s, p);
   }
   hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3(n_bg), dim3(kThreads), 0, s, p);
 }

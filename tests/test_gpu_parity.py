@@ -826,6 +826,38 @@ def test_block_cache_plan_matches_oracle(S, U, universe, churn, calls):
     assert (cache.tags == -1).all() and (cache.stamps == -1).all() and (cache.clock == 0).all()
 
 
+@pytest.mark.parametrize("B,n_wg", [(500, 300), (520, 300), (6, 5)])
+def test_cache_fill_copies_every_missing_block(B, n_wg):
+    """The fill deals a layer's missing blocks out over its workgroups (up
+    to 4096 (b, g) units; above that each workgroup copies whole units):
+    every listed block lands in its slot, bytewise, at 4000 units, at 4160
+    units and with fewer workgroups than blocks; ragged list lengths."""
+    H, D, nb, U = 8, 64, 6, 4
+    g = torch.Generator(device=DEV).manual_seed(71 + B)
+    k = torch.randn(B, H, nb * 64, D, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(B, H, nb * 64, D, generator=g, device=DEV).to(torch.bfloat16)
+    # each unit lists cnt distinct ascending blocks of the nb (cnt 0..U), padded with -1
+    cnt = torch.randint(0, U + 1, (B, H), generator=g, device=DEV).to(torch.int32)
+    perm = torch.rand(B, H, nb, generator=g, device=DEV).argsort(-1)[..., :U].sort(-1).values
+    pos = torch.arange(U, device=DEV)
+    idx = torch.where(pos < cnt[..., None], perm, -1).to(torch.int32).contiguous()
+    cache = bskv.BlockCache(B, H, U + 1, D, device=DEV)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    slot, fill, n_fill = bskv.block_cache_plan(cache, idx, cnt)
+    bskv.prefetch_cache_fill(k, v, idx, slot, fill, n_fill, cache, n_workgroups=n_wg)
+    torch.cuda.synchronize()
+    assert torch.equal(n_fill, cnt), "a first lookup copies every listed block"
+    valid = pos < cnt[..., None].long()
+    j = idx.long().clamp(min=0)
+    s_ = slot.long().clamp(min=0)
+    for src, dst in ((k, cache.k), (v, cache.v)):
+        want = src.view(B, H, nb, 64, D).gather(2, j[..., None, None].expand(-1, -1, -1, 64, D))
+        got = dst.gather(2, s_[..., None, None].expand(-1, -1, -1, 64, D))
+        m = valid[..., None, None].expand_as(got)
+        assert torch.equal(got.view(torch.int16)[m], want.view(torch.int16)[m])
+
+
 @pytest.mark.parametrize("host", [True, False])
 def test_cache_fill_and_cached_attention_over_steps(host):
     """Three decode steps of one layer through a block cache smaller than the
