@@ -12,10 +12,11 @@
 //
 // One workgroup per (b, g): the slot table (tags, stamps) is read into LDS;
 // every slot looks its block up in the sorted list (binary search); the
-// missing entries are numbered by a block scan over the list; the unlisted
-// slots are ranked by (stamp, slot) with one comparison per pair (S <= 1024
-// slots, a few thousand LDS reads per thread at most); the k-th missing entry
-// takes the slot of rank k.  The copies are listed compactly (list positions
+// missing entries are numbered by a block scan over the list; the k-th
+// missing entry takes the unlisted slot of rank k by (stamp, slot), found by
+// k + 1 workgroup minimums when there are few misses, else by ranking every
+// unlisted slot against every other (S <= 1024 slots, a few thousand LDS
+// reads per thread at most).  The copies are listed compactly (list positions
 // of the missing entries, in list order), so the copy kernel touches only
 // the (b, g) that miss something: at steady state most have nothing to copy.
 #include "bskv_device.hpp"
@@ -46,8 +47,23 @@ struct CachePlanSmem {
   int64_t stamp[kCacheMaxSlots];
   int32_t victim[kCacheMaxSlots];
   uint8_t keep[kCacheMaxSlots];
+  int64_t wmin[2][4];
   int scan_tmp[4];
 };
+
+// Up to this many missing blocks per (b, g) the victims are found one at a
+// time (a workgroup minimum per victim) instead of ranking every unlisted
+// slot against every other.
+constexpr int kCacheArgminMiss = 16;
+
+__device__ __forceinline__ int64_t wave_min_i64(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const int64_t o = __shfl_xor(v, off);
+    v = o < v ? o : v;
+  }
+  return v;
+}
 
 __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ cnt, int U,
@@ -58,12 +74,17 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
                                                             int32_t* __restrict__ n_fill_out) {
   __shared__ CachePlanSmem sm;
   const int bg = blockIdx.x, tid = threadIdx.x;
-  const int c = max(0, min(cnt[bg], U));
   const int32_t* lst = idx + (int64_t)bg * U;
   int32_t* tg = tags + (int64_t)bg * S;
   int64_t* st = stamps + (int64_t)bg * S;
+  // every load is issued before any is used (one round trip): the count,
+  // the clock, the whole list (entries past the count are masked after),
+  // the slot table
+  const int c = max(0, min(cnt[bg], U));
+  const int64_t now = clock[bg] + 1;
   for (int u = tid; u < U; u += kThreads) {
-    sm.list[u] = u < c ? lst[u] : INT32_MAX;
+    const int32_t j = lst[u];
+    sm.list[u] = u < c ? j : INT32_MAX;
     sm.slot_of[u] = -1;
   }
   for (int s = tid; s < S; s += kThreads) {
@@ -97,8 +118,38 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
   for (int e = 0; e < PPT; ++e) mine += (u0 + e < c && sm.slot_of[u0 + e] < 0) ? 1 : 0;
   int n_miss;
   int rank = block_excl_scan(mine, sm.scan_tmp, n_miss);
-  // rank the unlisted slots by (stamp, slot); the first n_miss are taken
-  for (int s = tid; s < S; s += kThreads) {
+  // the n_miss unlisted slots of least (stamp, slot) are taken, in that
+  // order.  Few misses (the common case at steady state, none at all for
+  // most (b, g)): one workgroup minimum of the key (stamp + 1) * 1024 + slot
+  // per victim, the taken slot's key then set to the maximum.
+  if (n_miss > 0 && n_miss <= kCacheArgminMiss) {
+    constexpr int SPT = kCacheMaxSlots / kThreads;
+    const int lane = tid & 63, wid = tid >> 6;
+    int64_t key[SPT];
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      const int sl = tid + e * kThreads;
+      key[e] = (sl < S && !sm.keep[sl]) ? ((sm.stamp[sl] + 1) << 10) + sl : INT64_MAX;
+    }
+    for (int r = 0; r < n_miss; ++r) {
+      int64_t m = key[0];
+#pragma unroll
+      for (int e = 1; e < SPT; ++e) m = key[e] < m ? key[e] : m;
+      m = wave_min_i64(m);
+      if (lane == 0) sm.wmin[r & 1][wid] = m;
+      __syncthreads();
+      int64_t best = sm.wmin[r & 1][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) best = sm.wmin[r & 1][w] < best ? sm.wmin[r & 1][w] : best;
+      const int vs = (int)(best & 1023);
+      if (tid == 0) sm.victim[r] = vs;
+#pragma unroll
+      for (int e = 0; e < SPT; ++e)
+        if (tid + e * kThreads == vs) key[e] = INT64_MAX;
+    }
+  }
+  // more misses: rank every unlisted slot by (stamp, slot)
+  for (int s = tid; s < S && n_miss > kCacheArgminMiss; s += kThreads) {
     if (sm.keep[s]) continue;
     const int64_t ks = sm.stamp[s];
     int r = 0;
@@ -122,7 +173,6 @@ __global__ __launch_bounds__(kThreads) void cache_plan_kernel(const int32_t* __r
   }
   for (int k = n_miss + tid; k < U; k += kThreads) fill_out[(int64_t)bg * U + k] = -1;
   __syncthreads();
-  const int64_t now = clock[bg] + 1;
   for (int u = tid; u < U; u += kThreads) {
     const int s = u < c ? sm.slot_of[u] : -1;
     slot_out[(int64_t)bg * U + u] = s;

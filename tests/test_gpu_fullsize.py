@@ -16,7 +16,9 @@ DEV = torch.device("cuda:0")
 def test_config3_two_layers_sampled():
     """B8, T=131072, top-64 + 1 + 4: layer 0 selected by the layer-0
     projection, layer 1 by layer 0's Forecast (the fused layer calls: layer
-    0's call scores layer 1's candidates, layer 1's call selects from them)."""
+    0's call scores layer 1's candidates, layer 1's call selects from them).
+    Every batch element of both layers is checked against the oracle, which
+    pools its own compressed keys from the inputs."""
     wl = CONFIGS[3]
     L = 2
     layers = decode_inputs(wl, DEV, layers=L)
@@ -37,7 +39,7 @@ def test_config3_two_layers_sampled():
                                           scores=sc1, topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local)
     torch.cuda.synchronize()
     sel_gpu = [(idx0, cnt0, out0), (idx1, cnt1, out1)]
-    for b in (0, wl.B - 1):
+    for b in range(wl.B):
         for l, lay in enumerate(layers):
             idx, cnt, out = sel_gpu[l]
             k = np64(lay["k"][b:b + 1])

@@ -991,6 +991,43 @@ def test_decode_layer_equals_the_per_op_calls(dtype, d, G):
     assert max_abs(np64(out_b), want) < (1e-4 if dtype == "f32" else 2e-2)
 
 
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2)])
+def test_decode_layer_short_sequences(dtype, d, G):
+    """Sequences of 1, 64 and 65 tokens beside a long one: no candidates
+    (only the local and initial blocks), a just-completed first block (the
+    newest-block update writes block 0) and one token past it.  The fused
+    layer (deferred, then the next call ranking those scores) equals the
+    per-op calls bit for bit and the oracle."""
+    lens = [1, 64, 65, 64 * 30]
+    c, c2, kc, kc_next, idx, cnt = _layer_case(dtype, d, G, 4, 64 * 30, lens, 17)
+    scale = 1.0 / math.sqrt(d)
+    kc_a, kc_b = kc.clone(), kc.clone()
+    kc_a[:, :, 0] = float("nan")
+    kc_b[:, :, 0] = float("nan")
+    bskv.kv_block_meanpool(c["k"], c["seq_len"], kc_a, 0, kc.shape[2], newest_only=True)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], 4, d)
+    idx_a, cnt_a = bskv.forecast_block_score_topk(f, kc_next, 6, 1, 2, seq_len=c["seq_len"])
+    out_a = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    out_b, sc_next = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc_b, idx, cnt, scale,
+                                                 x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=6, n_init=1,
+                                                 n_local=2)
+    idx_b, cnt_b = _next_lists(c2, kc_next, sc_next, 6, 1, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(kc_a.nan_to_num(7.0), kc_b.nan_to_num(7.0))
+    assert torch.equal(idx_a, idx_b) and torch.equal(cnt_a, cnt_b)
+    assert torch.equal(out_a, out_b)
+    lens_np = np.array(lens)
+    assert int(cnt_b[0].max()) == 1 and int(cnt_b[1].max()) == 1, "one block, no candidates: the local block alone"
+    sel = orc.decode_select(orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), 4, d),
+                            orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens), lens_np, 6, 1, 2, 64)
+    check_selection(idx_b, cnt_b, sel, 6)
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens_np,
+                             scale, 64)
+    assert max_abs(np64(out_b), want) < (1e-4 if dtype == "f32" else 2e-2)
+    pooled = orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens)
+    assert max_abs(np64(kc_b)[1, :, 0], pooled[1, :, 0]) < 1e-4, "block 0 of the 64-token sequence"
+
+
 def test_decode_layer_top_k_from_scores_in_the_same_call():
     """A call given the previous call's scores writes its own lists first
     and attends over them: equal to the lists and output of the per-op
