@@ -37,7 +37,7 @@ constexpr int kQkvfMaxBatch = 64;
 
 // NW waves split the hidden axis; NB batch chunks of 16; UN hidden steps of
 // 32 per load batch (hidden / NW a multiple of 32 UN)
-template <int NW, int NB, int UN>
+template <int NW, int NB, int UN, bool XL>
 __global__ __launch_bounds__(NW * 64) void qkvf_decode_kernel(const bf16_bits* __restrict__ x,
                                                              const bf16_bits* __restrict__ w, int B, int hidden,
                                                              int Hq, int H, int D, bf16_bits* __restrict__ q,
@@ -46,10 +46,19 @@ __global__ __launch_bounds__(NW * 64) void qkvf_decode_kernel(const bf16_bits* _
                                                              const int64_t* __restrict__ seq_len,
                                                              float* __restrict__ f) {
   __shared__ float red[NW][NB][64][4];
+  extern __shared__ uint4 xs[];        // XL: the batch's x rows, padded by 64 bytes
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int kq = hidden / NW, k_begin = wid * kq;
+  const int rowq = hidden / 8 + 4;     // 16-byte units per staged row
+  if constexpr (XL) {
+    for (int i = tid; i < B * (hidden / 8); i += NW * 64) {
+      const int b = i / (hidden / 8), c = i % (hidden / 8);
+      xs[b * rowq + c] = ld16(x + (int64_t)b * hidden + 8 * c);
+    }
+    __syncthreads();
+  }
   const bf16_bits* wrow = w + (int64_t)(n0 + l16) * hidden + 8 * lg;
   f32x4_t acc[NB];
 #pragma unroll
@@ -67,7 +76,8 @@ __global__ __launch_bounds__(NW * 64) void qkvf_decode_kernel(const bf16_bits* _
       uint4 xb[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u)
-        xb[u] = b < B ? ld16(x + (int64_t)b * hidden + k + 32 * u + 8 * lg) : make_uint4(0, 0, 0, 0);
+        xb[u] = b < B ? (XL ? xs[b * rowq + (k + 32 * u) / 8 + lg] : ld16(x + (int64_t)b * hidden + k + 32 * u + 8 * lg))
+                      : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < UN; ++u)
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
@@ -109,18 +119,20 @@ __global__ __launch_bounds__(NW * 64) void qkvf_decode_kernel(const bf16_bits* _
 hipError_t launch_qkvf_decode(const QkvfDecodeArgs& a) {
   const int N = (a.Hq + 3 * a.H) * a.D;
   const dim3 grid(N / 16);
-#define BSKV_QKVF_DEC(NW, NB, UN)                                                                                 \
-  hipLaunchKernelGGL((qkvf_decode_kernel<NW, NB, UN>), grid, dim3(NW * 64), 0, a.stream, (const bf16_bits*)a.x,   \
+#define BSKV_QKVF_DEC(NW, NB, UN, XL)                                                                             \
+  hipLaunchKernelGGL((qkvf_decode_kernel<NW, NB, UN, XL>), grid, dim3(NW * 64),                                    \
+                     XL ? (size_t)a.B * (a.hidden / 8 + 4) * 16 : 0, a.stream, (const bf16_bits*)a.x,              \
                      (const bf16_bits*)a.w, a.B, a.hidden, a.Hq, a.H, a.D, (bf16_bits*)a.q, (bf16_bits*)a.k,       \
                      (bf16_bits*)a.v, a.sb, a.sg, a.st, a.kv_len, a.seq_len, a.f)
   // hidden is a multiple of 1024.  Up to 16 sequences, hidden a multiple of
   // 4096: eight waves of 512 hidden columns each issue all their weight loads
   // at once; otherwise four waves in steps of 8 x 32 (a quarter of hidden is
   // a multiple of 256)
-  if (a.B <= 16 && a.hidden % 4096 == 0) BSKV_QKVF_DEC(8, 1, 8);
-  else if (a.B <= 16) BSKV_QKVF_DEC(4, 1, 8);
-  else if (a.B <= 32) BSKV_QKVF_DEC(4, 2, 8);
-  else BSKV_QKVF_DEC(4, 4, 8);
+  if (a.B <= 8 && a.hidden == 4096) BSKV_QKVF_DEC(8, 1, 8, true);
+  else if (a.B <= 16 && a.hidden % 4096 == 0) BSKV_QKVF_DEC(8, 1, 8, false);
+  else if (a.B <= 16) BSKV_QKVF_DEC(4, 1, 8, false);
+  else if (a.B <= 32) BSKV_QKVF_DEC(4, 2, 8, false);
+  else BSKV_QKVF_DEC(4, 4, 8, false);
 #undef BSKV_QKVF_DEC
   return hipGetLastError();
 }

@@ -699,7 +699,8 @@ def _bf16_close(got, want, rel=2.0 ** -8, abs_tol=1e-3):
 
 
 @pytest.mark.parametrize("B,hidden,Hq,Hkv,d", [(3, 1024, 8, 2, 128), (16, 4096, 32, 8, 128), (5, 2048, 4, 4, 64),
-                                           (40, 1024, 8, 2, 64), (64, 1024, 4, 1, 128)])
+                                           (40, 1024, 8, 2, 64), (64, 1024, 4, 1, 128), (7, 4096, 16, 4, 64),
+                                           (1, 4096, 32, 8, 128)])
 def test_qkvf_proj_decode(B, hidden, Hq, Hkv, d):
     g = torch.Generator().manual_seed(B + hidden)
     x = torch.randn(B, hidden, generator=g).to(torch.bfloat16)
