@@ -13,10 +13,10 @@
 // One workgroup per (b, g): the slot table (tags, stamps) is read into LDS;
 // every slot looks its block up in the sorted list (binary search); the
 // missing entries are numbered by a block scan over the list; the k-th
-// missing entry takes the unlisted slot of rank k by (stamp, slot), found by
-// k + 1 workgroup minimums when there are few misses, else by ranking every
-// unlisted slot against every other (S <= 1024 slots, a few thousand LDS
-// reads per thread at most).  The copies are listed compactly (list positions
+// missing entry takes the unlisted slot of rank k by (stamp, slot); with few
+// misses the victims are found one workgroup minimum at a time, else every
+// unlisted slot is ranked against every other (S <= 1024 slots, a few
+// thousand LDS reads per thread at most).  The copies are listed compactly (list positions
 // of the missing entries, in list order), so the copy kernel touches only
 // the (b, g) that miss something: at steady state most have nothing to copy.
 #include "bskv_device.hpp"

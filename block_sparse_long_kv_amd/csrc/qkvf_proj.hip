@@ -33,6 +33,9 @@ namespace bskv {
 // B = the batch's x rows (up to 16 sequences per MFMA, several chunks for
 // larger batches); the waves' partial sums meet in LDS and wave 0 scatters:
 // Q (bf16), the new token's K and V into the cache (bf16) and F (fp32).
+// XL: the batch's x rows are first staged in LDS (rows padded by 64 bytes),
+// so the weight stream is the only global read in the loop (up to 8
+// sequences at hidden 4096: 66 KB, two workgroups per CU).
 constexpr int kQkvfMaxBatch = 64;
 
 // NW waves split the hidden axis; NB batch chunks of 16; UN hidden steps of
