@@ -1433,7 +1433,7 @@ def side_prefill(args, torch, bskv, wl):
     return {"workload": wl.name, "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"],
             "attn_ms_per_chunk": round(at["us"] / 1e3, 4), "attn_TFLOPs": at["TFLOPs"], "attn_mfma_frac": at["mfma_frac"],
             "score_topk_us_per_chunk": r["kernels"]["score_topk_prefill"]["us"],
-            "parity": "tests/test_gpu_fullsize.py::test_config4_prefill_chunks_sampled (10,752 rows vs the oracle)"}
+            "parity": "tests/test_gpu_fullsize.py::test_prefill_B4_128K_chunks_sampled (10,752 rows vs the oracle)"}
 
 
 def main():
@@ -1468,7 +1468,7 @@ def main():
 
     import torch
     import block_sparse_long_kv_amd as bskv
-    from workloads import CONFIGS
+    from workloads import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -1485,27 +1485,27 @@ def main():
         log(f"[bench] copy probes: {n} bytes read, {n} bytes written, each")
         del a, b
     if args.workload == "decode" and not args.core_only and not args.per_op:
-        result = run_decode(args, torch, bskv, CONFIGS[3])
+        result = run_decode(args, torch, bskv, WORKLOADS["decode-B8-128K-32L"])
         # the other two main workloads, compactly, on the same run
         torch.cuda.empty_cache()
-        result["decode_b4"] = side_decode_b4(args, torch, bskv, CONFIGS[2])
+        result["decode_b4"] = side_decode_b4(args, torch, bskv, WORKLOADS["decode-B4-32K"])
         torch.cuda.empty_cache()
-        result["prefill"] = side_prefill(args, torch, bskv, CONFIGS[4])
+        result["prefill"] = side_prefill(args, torch, bskv, WORKLOADS["prefill-B4-128K"])
         print(json.dumps(result), flush=True)
         return
     if args.workload == "decode-tiny":
-        result = run_tiny(args, torch, bskv, CONFIGS[1])
+        result = run_tiny(args, torch, bskv, WORKLOADS["tiny-decode-fp32"])
     elif args.workload == "prefill":
-        result = run_prefill(args, torch, bskv, CONFIGS[4])
+        result = run_prefill(args, torch, bskv, WORKLOADS["prefill-B4-128K"])
     elif args.workload == "offload":
-        result = run_offload(args, torch, bskv, CONFIGS[5])
+        result = run_offload(args, torch, bskv, WORKLOADS["offload-decode-B16-128K-32L"])
     elif args.workload == "offload-steady":
-        result = run_offload_steady(args, torch, bskv, CONFIGS[6])
+        result = run_offload_steady(args, torch, bskv, WORKLOADS["offload-steady-B16-128K-32L"])
     else:
         if args.workload == "decode":
-            result = run_decode(args, torch, bskv, CONFIGS[3])
+            result = run_decode(args, torch, bskv, WORKLOADS["decode-B8-128K-32L"])
         else:
-            result = run_decode(args, torch, bskv, CONFIGS[2], replicas=8)
+            result = run_decode(args, torch, bskv, WORKLOADS["decode-B4-32K"], replicas=8)
     print(json.dumps(result), flush=True)
 
 

@@ -7,19 +7,19 @@ import torch
 import block_sparse_long_kv_amd as bskv
 import oracle as orc
 from parity import check_selection, fp32_sum_close, max_abs, np64
-from workloads import CONFIGS, decode_inputs
+from workloads import WORKLOADS, decode_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def test_config3_two_layers_sampled():
+def test_decode_B8_128K_two_layers_sampled():
     """B8, T=131072, top-64 + 1 + 4: layer 0 selected by the layer-0
     projection, layer 1 by layer 0's Forecast (the fused layer calls: layer
     0's call scores layer 1's candidates, layer 1's call selects from them).
     Every batch element of both layers is checked against the oracle, which
     pools its own compressed keys from the inputs."""
-    wl = CONFIGS[3]
+    wl = WORKLOADS["decode-B8-128K-32L"]
     L = 2
     layers = decode_inputs(wl, DEV, layers=L)
     nb = wl.NB
@@ -54,7 +54,7 @@ def test_config3_two_layers_sampled():
             assert max_abs(np64(out[b:b + 1]), want) < 2e-2
 
 
-def test_config4_prefill_chunks_sampled():
+def test_prefill_B4_128K_chunks_sampled():
     """B4, T=131072, 2048-token chunks, top-64 + 1 + 32 local: selection and
     attention on sampled (batch, KV head, query block) problems of the first,
     a middle and the last chunk, at the kernels' full launch size.  Every
@@ -64,7 +64,7 @@ def test_config4_prefill_chunks_sampled():
     GPU's lists."""
     import math
     from workloads import prefill_inputs
-    wl = CONFIGS[4]
+    wl = WORKLOADS["prefill-B4-128K"]
     inp = prefill_inputs(wl, DEV)
     lens = torch.full((wl.B,), wl.T, dtype=torch.int64, device=DEV)
     kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
@@ -103,12 +103,12 @@ def test_config4_prefill_chunks_sampled():
     assert rows_checked >= 10_000 and on_oracle_lists > 0
 
 
-def test_config5_offload_sampled():
+def test_offload_B16_128K_sampled():
     """B16, T=131072 with the KV cache in host-pinned memory: the layer-0
     projection selects layer 0, its blocks are gathered from the host pool
     into the ring on a side stream, and attention reads the ring.  Checked on
     sampled batch elements against the oracle and bytewise against the host."""
-    wl = CONFIGS[5]
+    wl = WORKLOADS["offload-decode-B16-128K-32L"]
     lay = decode_inputs(wl, DEV, layers=1)[0]
     kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
     bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
@@ -153,7 +153,7 @@ def test_steady_offload_cache_full_size():
     the oracle's LRU exactly for every (b, g); the slots hold the host blocks
     bytewise and the cached attention matches the oracle on sampled batch
     elements."""
-    wl = CONFIGS[6]
+    wl = WORKLOADS["offload-steady-B16-128K-32L"]
     lay = decode_inputs(wl, DEV, layers=1)[0]
     kc = torch.empty(wl.B, wl.Hkv, wl.NB, wl.d, dtype=torch.float32, device=DEV)
     bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc)
@@ -195,11 +195,11 @@ def test_steady_offload_cache_full_size():
             assert max_abs(np64(out[b:b + 1]), want) < 2e-2
 
 
-def test_window_select_config3_sampled():
+def test_window_select_B8_128K_sampled():
     """B8, T=131072: 32-token windows at stride 16 over every (b, g), decode
     selection with block scores max-pooled from the windows, checked on two
     sampled batch elements (all KV heads) against the oracle."""
-    wl = CONFIGS[3]
+    wl = WORKLOADS["decode-B8-128K-32L"]
     lay = decode_inputs(wl, DEV, layers=1)[0]
     nw = (wl.T - 32) // 16 + 1
     kcw = torch.empty(wl.B, wl.Hkv, nw, wl.d, dtype=torch.float32, device=DEV)

@@ -17,7 +17,7 @@ import torch
 import block_sparse_long_kv_amd as bskv
 import oracle as orc
 from parity import check_selection, fp32_sum_close, max_abs, np64
-from workloads import CONFIGS, decode_inputs, random_decode_case, random_prefill_case
+from workloads import WORKLOADS, decode_inputs, random_decode_case, random_prefill_case
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -132,8 +132,8 @@ def _decode_select_both(c, topk, n_init, n_local, hidden=None):
     return idx, cnt, sc, sel
 
 
-def test_decode_selection_config1():
-    wl = CONFIGS[1]
+def test_decode_selection_tiny_fp32():
+    wl = WORKLOADS["tiny-decode-fp32"]
     lay = _gpu(decode_inputs(wl, "cpu")[0])
     idx, cnt, sc, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
     assert check_selection(idx, cnt, sel, wl.topk) == 0
@@ -146,8 +146,8 @@ def test_decode_selection_config1():
         assert got[j] == -math.inf
 
 
-def test_decode_selection_config2():
-    wl = CONFIGS[2]
+def test_decode_selection_B4_32K():
+    wl = WORKLOADS["decode-B4-32K"]
     lay = _gpu(decode_inputs(wl, "cpu")[0])
     idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
     assert check_selection(idx, cnt, sel, wl.topk) == 0
@@ -183,7 +183,7 @@ def test_decode_selection_exact_ties_take_lower_index():
 
 
 def test_decode_selection_repeatable():
-    wl = CONFIGS[2]
+    wl = WORKLOADS["decode-B4-32K"]
     lay = _gpu(decode_inputs(wl, "cpu", B=2, T=8192)[0])
     f = bskv.forecast_proj(lay["x_sel"], lay["w_sel"], wl.Hkv, wl.d)
     kc = _kc_gpu(lay["k"], lay["seq_len"])
@@ -434,8 +434,8 @@ def test_attn_decode_long_splits(dtype, d, G, tol):
     assert max_abs(np64(out), want) < tol
 
 
-def test_attn_decode_config1_end_to_end():
-    wl = CONFIGS[1]
+def test_attn_decode_tiny_fp32_end_to_end():
+    wl = WORKLOADS["tiny-decode-fp32"]
     lay = _gpu(decode_inputs(wl, "cpu")[0])
     idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
     assert check_selection(idx, cnt, sel, wl.topk) == 0
@@ -445,8 +445,8 @@ def test_attn_decode_config1_end_to_end():
     assert max_abs(np64(out), want) < 1e-4
 
 
-def test_attn_decode_config2_end_to_end():
-    wl = CONFIGS[2]
+def test_attn_decode_B4_32K_end_to_end():
+    wl = WORKLOADS["decode-B4-32K"]
     lay = _gpu(decode_inputs(wl, "cpu")[0])
     idx, cnt, _, sel = _decode_select_both(lay, wl.topk, wl.n_init, wl.n_local)
     assert check_selection(idx, cnt, sel, wl.topk) == 0
@@ -649,7 +649,7 @@ def test_prefetch_from_pinned_host_and_ring_attention():
     """The ring holds U blocks, far fewer than the sequence has: blocks whose id
     lies past the ring's length must still be attended (ring position u holds
     list entry u).  Ragged lengths, one with a partial newest block."""
-    wl = CONFIGS[5]
+    wl = WORKLOADS["offload-decode-B16-128K-32L"]
     B, T = 3, 64 * 200
     lay = decode_inputs(wl, DEV, layers=1, B=B, T=T)[0]
     lay["seq_len"] = torch.tensor([T, T - 64 * 37 - 5, 64 * 90], dtype=torch.int64, device=DEV)
@@ -867,7 +867,7 @@ def test_cache_fill_and_cached_attention_over_steps(host):
     listed blocks bytewise, the cached attention equals the resident one bit
     for bit and the oracle within bf16 tolerance.  Ragged lengths, a partial
     newest block."""
-    wl = CONFIGS[5]
+    wl = WORKLOADS["offload-decode-B16-128K-32L"]
     B, T, S = 3, 64 * 200, 96
     lay = decode_inputs(wl, DEV, layers=1, B=B, T=T)[0]
     lay["seq_len"] = torch.tensor([T, T - 64 * 37 - 5, 64 * 90], dtype=torch.int64, device=DEV)
@@ -927,7 +927,7 @@ def test_cache_fill_and_cached_attention_over_steps(host):
 
 # ----------------------------------------------------------------------------- fused decode layer
 def _layer_case(dtype, d, G, B, T, lens, seed):
-    wl = CONFIGS[2]
+    wl = WORKLOADS["decode-B4-32K"]
     Hkv = 4
     c = _gpu(random_decode_case(seed, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, hidden=512, seq_len=lens))
     c2 = _gpu(random_decode_case(seed + 100, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens))

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle as orc
-from workloads import CONFIGS, decode_inputs, random_decode_case
+from workloads import WORKLOADS, decode_inputs, random_decode_case
 
 
 def _np(t):
@@ -567,8 +567,8 @@ def test_decode_select_invariants(seed):
                 assert c <= U and (sel.idx[b, g, c:] == -1).all()
 
 
-def test_planted_config1_is_topk():
-    wl = CONFIGS[1]
+def test_planted_tiny_fp32_is_topk():
+    wl = WORKLOADS["tiny-decode-fp32"]
     lay = decode_inputs(wl, "cpu")[0]
     kc = orc.kv_block_meanpool(_np(lay["k"]), wl.block)
     sel = orc.decode_select(_np(lay["f"]), kc, _np(lay["seq_len"]).astype(np.int64), wl.topk, wl.n_init,
@@ -577,8 +577,8 @@ def test_planted_config1_is_topk():
     assert orc.kth_gap(sel.scores[0], wl.topk) > 0.5
 
 
-def test_planted_config2_is_topk():
-    wl = CONFIGS[2]
+def test_planted_B4_32K_is_topk():
+    wl = WORKLOADS["decode-B4-32K"]
     lay = decode_inputs(wl, "cpu")[0]
     f = orc.forecast_proj(_np(lay["x_sel"]), _np(lay["w_sel"]), wl.Hkv, wl.d)
     k = lay["k"]
@@ -760,7 +760,7 @@ def test_gather_selected_blocks_bytes():
 
 # --------------------------------------------------------------------------- lookahead
 def test_lookahead_uses_each_layers_own_forecast_and_keys():
-    wl = CONFIGS[2]
+    wl = WORKLOADS["decode-B4-32K"]
     rng = np.random.default_rng(11)
     L, B, H, d, hidden, T, blk = 3, 1, 2, 4, 6, 64, 8
     layers = []

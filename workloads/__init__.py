@@ -4,7 +4,7 @@ This package only draws inputs.  It holds none of the method's arithmetic
 (no pooling, scoring, selection or attention); the oracle and the HIP library
 each compute everything from the tensors drawn here.
 """
-from .configs import CONFIGS, Workload  # noqa: F401
+from .configs import WORKLOADS, Workload  # noqa: F401
 from .synth import (  # noqa: F401
     decode_inputs,
     drift_walk,

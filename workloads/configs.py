@@ -14,7 +14,6 @@ from dataclasses import dataclass
 
 @dataclass(frozen=True)
 class Workload:
-    key: int
     name: str
     kind: str                 # "decode" | "prefill" | "offload"
     dtype: str                # "f32" | "bf16": K, V, Q (and x, W) element type
@@ -53,20 +52,23 @@ class Workload:
         return 1.0 / (self.d ** 0.5)
 
 
-CONFIGS = {
-    1: Workload(1, "tiny-decode-fp32", "decode", "f32", B=1, Hq=4, Hkv=1, d=64, hidden=None,
-                T=4096, block=64, topk=8, n_init=1, n_local=2, layers=1, seed=0),
-    2: Workload(2, "decode-B4-32K", "decode", "bf16", B=4, Hq=32, Hkv=8, d=128, hidden=4096,
-                T=32768, block=64, topk=32, n_init=1, n_local=2, layers=1, seed=1),
-    3: Workload(3, "decode-B8-128K-32L", "decode", "bf16", B=8, Hq=32, Hkv=8, d=128, hidden=4096,
-                T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=2),
-    4: Workload(4, "prefill-B4-128K", "prefill", "bf16", B=4, Hq=32, Hkv=8, d=128, hidden=None,
-                T=131072, block=64, topk=64, n_init=1, n_local=32, layers=1, seed=3,
-                chunk=2048, plant_frac=0.05),
-    5: Workload(5, "offload-decode-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128,
-                hidden=4096, T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=4,
-                host_layers=4),
-    6: Workload(6, "offload-steady-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128, hidden=4096,
-                T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=5, host_layers=4, plant=32,
-                drift=0.05),
-}
+_ALL = [
+    Workload("tiny-decode-fp32", "decode", "f32", B=1, Hq=4, Hkv=1, d=64, hidden=None,
+            T=4096, block=64, topk=8, n_init=1, n_local=2, layers=1, seed=0),
+    Workload("decode-B4-32K", "decode", "bf16", B=4, Hq=32, Hkv=8, d=128, hidden=4096,
+            T=32768, block=64, topk=32, n_init=1, n_local=2, layers=1, seed=1),
+    Workload("decode-B8-128K-32L", "decode", "bf16", B=8, Hq=32, Hkv=8, d=128, hidden=4096,
+            T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=2),
+    Workload("prefill-B4-128K", "prefill", "bf16", B=4, Hq=32, Hkv=8, d=128, hidden=None,
+            T=131072, block=64, topk=64, n_init=1, n_local=32, layers=1, seed=3,
+            chunk=2048, plant_frac=0.05),
+    Workload("offload-decode-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128,
+            hidden=4096, T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=4,
+            host_layers=4),
+    Workload("offload-steady-B16-128K-32L", "offload", "bf16", B=16, Hq=32, Hkv=8, d=128, hidden=4096,
+            T=131072, block=64, topk=64, n_init=1, n_local=4, layers=32, seed=5, host_layers=4, plant=32,
+            drift=0.05),
+]
+
+# the workloads by name
+WORKLOADS = {w.name: w for w in _ALL}
