@@ -16,8 +16,9 @@
 // all G heads over its part of the row, one 8-lane sum gives the shared score.
 // Kernel 2 (softmax + top-k), one workgroup per (b, g): maximum and
 // exponential sum over the candidates (block reductions), the weights as
-// orderable keys in LDS, then the radix select + union of the Forecast
-// selector.
+// orderable keys, then the radix select + union of the Forecast selector;
+// up to 8 * kThreads candidates the row is read once and stays in
+// registers, above that the keys go through LDS.
 #include "decode_ops.hpp"
 #include "bskv_launch.hpp"
 
@@ -104,6 +105,34 @@ __global__ __launch_bounds__(kThreads) void mh_topk_kernel(const float* __restri
   const DecodeCands dc = decode_cands(seq_len[bg / H], nb_cap, n_init, n_local);
   const int n = dc.c1 - dc.c0;
   const float* row = sc + (int64_t)bg * nb_cap + dc.c0;
+  if (n <= 8 * kThreads) {
+    // the row read once into registers (thread t: candidates 8t .. 8t+7),
+    // the maximum, the sum and the weights from there
+    float v[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * (int)threadIdx.x + e;
+      v[e] = i < n ? row[i] : -INFINITY;
+      mx = fmaxf(mx, v[e]);
+    }
+    mx = block_reduce<0>(mx, red);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += 8 * (int)threadIdx.x + e < n ? __builtin_amdgcn_exp2f((v[e] - mx) * scale_log2e) : 0.f;
+    sum = block_reduce<1>(sum, red);
+    const float inv = n > 0 ? 1.f / sum : 0.f;
+    uint32_t kin[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * (int)threadIdx.x + e;
+      const float w = __builtin_amdgcn_exp2f((v[e] - mx) * scale_log2e) * inv;   // softmax weight
+      kin[e] = orderable_key(i < n ? w : 0.f);
+      if (w_out && i < n) w_out[(int64_t)bg * nb_cap + dc.c0 + i] = w;
+    }
+    topk_union_fast(dc.c0, dc.c0, dc.c1, topk, dc.cur, n_init, n_local, U, idx + (int64_t)bg * U, cnt + bg, sh, kin);
+    return;
+  }
   float mx = -INFINITY;
   for (int i = threadIdx.x; i < n; i += kThreads) mx = fmaxf(mx, row[i]);
   mx = block_reduce<0>(mx, red);
