@@ -198,11 +198,13 @@ def test_decode_selection_repeatable():
 @pytest.mark.parametrize("dtype,d,G,topk,lens", [("bf16", 128, 4, 32, [64 * 512] * 4),
                                                  ("f32", 64, 2, 8, [64 * 40, 64 * 33 + 17, 100, 64 * 40 - 1]),
                                                  ("bf16", 64, 8, 16, [64 * 300, 64 * 150 + 1]),
-                                                 ("f32", 128, 1, 64, [64 * 2048])])
+                                                 ("f32", 128, 1, 64, [64 * 2048]),
+                                                 ("bf16", 64, 2, 32, [64 * 2100 + 5, 64 * 1000])])
 def test_multihead_select_decode(dtype, d, G, topk, lens):
     """The baseline selector (per-head scores summed, softmax, top-k) against
     the oracle: lists equal outside the near-tie band, softmax weights to
-    float32 accuracy.  Ragged lengths, one with fewer candidates than k."""
+    float32 accuracy.  Ragged lengths, one with fewer candidates than k, one
+    with more than 2048 candidates (the top-k's keys through LDS)."""
     B, Hkv = len(lens), 2
     T = max(lens) + 64
     g = torch.Generator().manual_seed(100 + d + G)
