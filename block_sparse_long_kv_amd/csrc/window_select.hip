@@ -14,8 +14,9 @@
 // Decode selection: window scores F . K~w over the windows touching the
 // candidate blocks, in slices (the block selector's score slices on window
 // rows); then one workgroup per (b, g) max-pools them into block scores
-// (orderable keys in LDS) and runs the radix select + union of the block
-// selector.  Prefill selection: one workgroup per query block (below).
+// and runs the radix select + union of the block selector (on the 32/16
+// grid up to 2048 candidates each thread loads its 8 blocks' 33 windows at
+// once and keeps the keys in registers; otherwise the keys go through LDS).  Prefill selection: one workgroup per query block (below).
 #include "decode_ops.hpp"
 #include "bskv_launch.hpp"
 
@@ -118,6 +119,30 @@ __global__ __launch_bounds__(kThreads) void window_topk_kernel(const float* __re
   const int nwc = (int)min(win_count(L, window, stride), nw_cap);
   const int n = dc.c1 - dc.c0;
   const float* row = sc + (int64_t)bg * nw_cap;
+  if (window == 32 && stride == 16 && n <= 8 * kThreads) {
+    // thread t: candidates 8t .. 8t+7 (blocks j = c0 + 8t + e), whose windows
+    // 4j-1 .. 4j+3 are the 33 consecutive windows from 4(c0 + 8t) - 1: all
+    // loaded at once, each block's maximum and key from registers
+    const int i0 = 8 * (int)threadIdx.x;
+    const int w0 = 4 * (dc.c0 + i0) - 1;
+    float ws[33];
+#pragma unroll
+    for (int t = 0; t < 33; ++t) {
+      const int w = w0 + t;
+      ws[t] = (i0 < n && w >= 0 && w < nwc) ? row[w] : -INFINITY;
+    }
+    uint32_t kin[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float m = ws[4 * e];
+#pragma unroll
+      for (int t = 1; t < 5; ++t) m = fmaxf(m, ws[4 * e + t]);   // max-pool of the block's windows
+      kin[e] = orderable_key(m);
+      if (bs_out && i0 + e < n) bs_out[(int64_t)bg * nb_cap + dc.c0 + i0 + e] = m;
+    }
+    topk_union_fast(dc.c0, dc.c0, dc.c1, topk, dc.cur, n_init, n_local, U, idx + (int64_t)bg * U, cnt + bg, sh, kin);
+    return;
+  }
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int j = dc.c0 + i;
     const int lo = win_lo(j, window, stride), hi = min(win_hi(j, stride), nwc - 1);

@@ -303,7 +303,8 @@ def test_window_meanpool_newest_only_and_subrange():
     ("bf16", 128, 32, 16, 16, [64 * 300, 64 * 150 + 1, 64 * 150 + 16, 64 * 150 + 40]),
     ("f32", 64, 32, 16, 8, [64 * 40, 64 * 33 + 17, 100, 64 * 40 - 1]),
     ("bf16", 64, 64, 16, 12, [64 * 200, 64 * 77 + 63]),
-    ("f32", 128, 32, 32, 64, [64 * 2048, 64 * 1000 + 31])])
+    ("f32", 128, 32, 32, 64, [64 * 2048, 64 * 1000 + 31]),
+    ("bf16", 64, 32, 16, 32, [64 * 2100 + 5, 64 * 2048])])
 def test_window_select_decode(dtype, d, window, stride, topk, lens):
     """Selection on window-compressed keys against the oracle: lists equal
     outside the near-tie band, block scores (max over each block's complete
