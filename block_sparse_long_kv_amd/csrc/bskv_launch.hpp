@@ -25,7 +25,7 @@ struct ProjArgs {
 };
 size_t proj_workspace_bytes(int B, int hidden, int N, int dtype);
 hipError_t launch_proj(const ProjArgs& a);
-int proj_splits(int hidden);
+int proj_splits(int hidden, int dtype);
 template <typename T>
 void launch_proj_partial(const void* x, const void* w, int B, int hidden, int N, float* part, hipStream_t s);
 

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void proj_partial_kernel(const T* __restr
                                                               int B, int hidden, int N, float* __restrict__ part) {
   if constexpr (std::is_same<T, bf16_bits>::value) {
     __shared__ ProjMfmaSmem sm;
-    proj_partial_mfma_wg(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
+    proj_partial_mfma_wg<kProjRows>(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
   } else {
     __shared__ ProjSmem sm;
     proj_partial_wg<T>(x, w, B, hidden, N, blockIdx.x, blockIdx.y, part, sm);
@@ -71,17 +71,18 @@ __global__ __launch_bounds__(kThreads) void proj_reduce_kernel(const float* __re
   f[i] = proj_reduce_one(part, n_splits, B, N, i / N, i % N);
 }
 
-int proj_splits(int hidden) { return hidden / kProjRows; }
+// partials of the projection: one per kProjRows rows (fp32) or per
+// kProjPartRows rows (bf16, whatever row span its workgroups take)
+int proj_splits(int hidden, int dtype) { return hidden / (dtype == 0 ? kProjRows : kProjPartRows); }
 int proj_tiles(int N, int dtype) { return N / (dtype == 0 ? 64 : 128); }
 
 size_t proj_workspace_bytes(int B, int hidden, int N, int dtype) {
-  (void)dtype;
-  return (size_t)proj_splits(hidden) * B * N * sizeof(float);
+  return (size_t)proj_splits(hidden, dtype) * B * N * sizeof(float);
 }
 
 template <typename T>
 void launch_proj_partial(const void* x, const void* w, int B, int hidden, int N, float* part, hipStream_t s) {
-  dim3 grid(N / proj_tile_cols_host<T>(), proj_splits(hidden));
+  dim3 grid(N / proj_tile_cols_host<T>(), hidden / kProjRows);
   hipLaunchKernelGGL((proj_partial_kernel<T>), grid, dim3(kThreads), 0, s, (const T*)x, (const T*)w, B, hidden, N,
                      part);
 }
@@ -94,7 +95,7 @@ hipError_t launch_proj(const ProjArgs& a) {
   else launch_proj_partial<bf16_bits>(a.x, a.w, a.B, a.hidden, a.N, part, a.stream);
   const int n = a.B * a.N;
   hipLaunchKernelGGL(proj_reduce_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, a.stream, part,
-                     proj_splits(a.hidden), a.B, a.N, a.f);
+                     proj_splits(a.hidden, a.dtype), a.B, a.N, a.f);
   return hipGetLastError();
 }
 

@@ -46,6 +46,12 @@ constexpr int kMaxSplitsDecode = 32;   // attention splits per KV head
 // 128K: first kernel 6.1-6.2 vs 7.1 us, step 1.417-1.423 vs 1.444-1.468 ms
 // against 128 rows; 512 rows 1.48-1.50 ms)
 constexpr int kProjRows = 256;
+// bf16 (MFMA) workgroups take 128 or 256 rows of W but always store one
+// partial per 128 rows, so every caller sums the same partials in the same
+// order: the fused layer's first kernel spans 128 rows when it carries no
+// top-k (256 workgroups at hidden 4096; B4 x 32K layer-step 1 us shorter),
+// 256 rows beside the top-k, and the standalone projection 256.
+constexpr int kProjPartRows = 128;
 constexpr int kProjPass = 4;     // batch rows per pass
 constexpr int kProjMaxB = 16;    // batch rows staged in LDS per round
 
@@ -132,20 +138,25 @@ struct ProjMfmaSmem {
   bf16_bits w[kProjRows * kProjWStr];
 };
 
+// ROWS (128 or 256) rows of W from row span * ROWS; one partial per
+// kProjPartRows rows: partial index r / kProjPartRows.
+template <int ROWS>
 __device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ w, int B,
-                                     int hidden, int N, int tile, int split, float* __restrict__ part,
+                                     int hidden, int N, int tile, int span, float* __restrict__ part,
                                      ProjMfmaSmem& sm) {
+  static_assert(ROWS % kProjPartRows == 0 && ROWS <= kProjRows, "row span");
   constexpr int TC = 128;
-  constexpr int CPT = kProjRows * TC / 8 / kThreads;   // 16-byte chunks of the tile per thread
+  constexpr int CPT = ROWS * TC / 8 / kThreads;   // 16-byte chunks of the tile per thread
+  constexpr int KPP = kProjPartRows / 32;         // k-steps per partial
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int r_begin = split * kProjRows, n0 = tile * TC;
+  const int r_begin = span * ROWS, n0 = tile * TC;
   // x^T fragments (B operand) of batch rows b0 + l16, in the row order of
   // the transposed W reads
-  auto load_x = [&](int b0, bf16x8_t (&xb)[kProjRows / 32]) {
+  auto load_x = [&](int b0, bf16x8_t (&xb)[ROWS / 32]) {
     const int b = b0 + l16;
 #pragma unroll
-    for (int ks = 0; ks < kProjRows / 32; ++ks) {
+    for (int ks = 0; ks < ROWS / 32; ++ks) {
       uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
       if (b < B) {
         const bf16_bits* xp = x + (int64_t)b * hidden + r_begin + 32 * ks + 4 * lg;
@@ -162,7 +173,7 @@ __device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict
     raw[i] = ld16_nt(w + (int64_t)(r_begin + r) * N + n0 + cc * 8);
   }
   // the first 16 batch rows travel beside the W tile, not after it
-  bf16x8_t xb[kProjRows / 32];
+  bf16x8_t xb[ROWS / 32];
   load_x(0, xb);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -177,19 +188,25 @@ __device__ __forceinline__ void proj_partial_mfma_wg(const bf16_bits* __restrict
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int nt = 2 * wid + t;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kProjRows / 32; ++ks) {
-        const bf16_bits* v0 = &sm.w[(32 * ks + tr_row) * kProjWStr + 16 * nt + tr_col];
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * kProjWStr));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[ks], acc, 0, 0, 0);
+      for (int pp = 0; pp < ROWS / kProjPartRows; ++pp) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KPP; ++kk) {
+          const int ks = pp * KPP + kk;
+          const bf16_bits* v0 = &sm.w[(32 * ks + tr_row) * kProjWStr + 16 * nt + tr_col];
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)v0);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v0 + 16 * kProjWStr));
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[ks], acc, 0, 0, 0);
+        }
+        // lane (b, lg) holds F^T[n0 + 16 nt + 4 lg + i][b], i = 0..3, over
+        // the partial's 128 rows
+        const int64_t part_id = r_begin / kProjPartRows + pp;
+        if (b < B)
+          *reinterpret_cast<float4*>(&part[(part_id * B + b) * N + n0 + 16 * nt + 4 * lg]) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
-      // lane (b, lg) holds F^T[n0 + 16 nt + 4 lg + i][b], i = 0..3
-      if (b < B)
-        *reinterpret_cast<float4*>(&part[((int64_t)split * B + b) * N + n0 + 16 * nt + 4 * lg]) =
-            make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }

@@ -44,7 +44,9 @@ struct LayerParams {
   // lookahead: Forecast of this layer -> scores of the next layer
   int select;                       // 0: no next layer
   const void* x; const void* w; int hidden, N;
-  float* proj_part; int proj_tiles, proj_splits;
+  // proj_splits partials (kProjPartRows rows each for bf16); the first
+  // kernel's projection workgroups span proj_rows rows of W each
+  float* proj_part; int proj_tiles, proj_splits, proj_rows;
   const float* kc_next; float* scores_next; int score_splits;
   // immediate mode (idx_next != nullptr): the scores go to the workspace
   // and the last score workgroup of each (b, g) runs the next layer's top-k
@@ -98,10 +100,14 @@ __global__ __launch_bounds__(kThreads) void layer_k1(LayerParams p) {
     return;
   }
   const int pid = (int)blockIdx.x - n_topk;
-  if constexpr (kMfma)
-    proj_partial_mfma_wg((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles, pid / p.proj_tiles,
-                         p.proj_part, sm.proj);
-  else
+  if constexpr (kMfma) {
+    if (p.proj_rows == kProjPartRows)
+      proj_partial_mfma_wg<kProjPartRows>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles,
+                                          pid / p.proj_tiles, p.proj_part, sm.proj);
+    else
+      proj_partial_mfma_wg<kProjRows>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles,
+                                      pid / p.proj_tiles, p.proj_part, sm.proj);
+  } else
     proj_partial_wg<T>((const T*)p.x, (const T*)p.w, p.B, p.hidden, p.N, pid % p.proj_tiles, pid / p.proj_tiles,
                        p.proj_part, sm.proj);
 }
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 3) void layer_k2(LayerParams p) {
 size_t proj_workspace_bytes(int B, int hidden, int N, int dtype);
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int U);
 AttnDecodeParams make_attn_params(const AttnDecodeArgs& a, void* ws);
-int proj_splits(int hidden);
+int proj_splits(int hidden, int dtype);
 int proj_tiles(int N, int dtype);
 
 static size_t al256(size_t x) { return ((x + 255) / 256) * 256; }
@@ -199,7 +205,7 @@ template <typename T, int D, int G>
 static void launch_layer_t(const LayerParams& p, int stages, hipStream_t s) {
   const int n_bg = p.B * p.H;
   const int n_topk = p.scores_in ? n_bg : 0;
-  const int n_proj = p.select ? p.proj_tiles * p.proj_splits : 0;
+  const int n_proj = p.select ? p.proj_tiles * (p.hidden / p.proj_rows) : 0;
   const int64_t cap = p.nb_cap < kMaxCandidates ? p.nb_cap : kMaxCandidates;
   const size_t lds = (n_topk > 0 && cap > 8 * kThreads) ? (size_t)cap * sizeof(uint32_t) : 0;
   if ((stages & 1) && n_topk + n_proj > 0)
@@ -236,7 +242,11 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a) {
   p.x = a.x; p.w = a.w; p.hidden = a.hidden; p.N = H * D;
   p.proj_part = (float*)(ws + sync_b);
   p.proj_tiles = p.select ? proj_tiles(H * D, a.attn.dtype) : 0;
-  p.proj_splits = p.select ? proj_splits(a.hidden) : 0;
+  p.proj_splits = p.select ? proj_splits(a.hidden, a.attn.dtype) : 0;
+  // bf16 without this layer's top-k in the first kernel: 128-row spans (twice
+  // the workgroups, each with half the bytes in flight); beside the top-k
+  // 256-row spans, so that both roles find a CU each
+  p.proj_rows = (a.attn.dtype != 0 && !a.scores) ? kProjPartRows : kProjRows;
   p.kc_next = a.kc_next;
   p.idx_next = a.idx_next; p.cnt_next = a.cnt_next;
   p.scores_next = a.idx_next ? (float*)(ws + sync_b + proj_b) : a.scores_next;
