@@ -1225,3 +1225,51 @@ def test_decode_layer_immediate_mode_equals_deferred_and_per_op(dtype, d, G):
     sel = orc.decode_select(orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), Hkv, d),
                             orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens), np.array(lens), topk, 1, 2, 64)
     check_selection(i_im, n_im, sel, topk)
+
+
+@pytest.mark.gpu
+def test_decode_layer_projection_spans_give_identical_scores():
+    """The first kernel's projection workgroups span 128 rows of W when the
+    kernel carries no top-k and 256 rows beside one; partials are stored per
+    128 rows either way, so the next layer's raw candidate scores are bit for
+    bit the same in both forms, rank to the per-op selection's lists, and
+    match the oracle's scores to the fp32-sum bound."""
+    lens = [64 * 300, 64 * 300 - 17, 64 * 131 + 5, 64 * 300]
+    B, Hkv, G, d, T, topk, hidden = 4, 4, 4, 128, 64 * 300, 32, 1024
+    c = _gpu(random_decode_case(61, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16", hidden=hidden, seq_len=lens))
+    c2 = _gpu(random_decode_case(62, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16", seq_len=lens))
+    kc, kc_next = _kc_gpu(c["k"], c["seq_len"]), _kc_gpu(c2["k"], c2["seq_len"])
+    nb = kc.shape[2]
+    # this layer's own raw candidate scores (from c2's Forecast), for the form
+    # that ranks them in its first kernel
+    i_own, n_own, sc_own = bskv.forecast_block_score_topk(c2["f"].contiguous(), kc, topk, 1, 2, seq_len=c["seq_len"],
+                                                          return_scores=True)
+    nan = lambda: torch.full((B, Hkv, nb), float("nan"), dtype=torch.float32, device=DEV)  # noqa: E731
+    sc_a, sc_b = nan(), nan()
+    # 128-row spans: no top-k in the first kernel, this layer's lists given
+    out_a, _ = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), i_own, n_own,
+                                           x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, scores_next=sc_a, topk=topk,
+                                           n_init=1, n_local=2)
+    # 256-row spans: the first kernel also ranks sc_own into this layer's lists
+    i_b = torch.full_like(i_own, -7)
+    n_b = torch.full_like(n_own, -7)
+    out_b, _ = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), i_b, n_b,
+                                           scores=sc_own, x=c["x_sel"], w=c["w_sel"], kc_next=kc_next,
+                                           scores_next=sc_b, topk=topk, n_init=1, n_local=2)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], Hkv, d)
+    i_ref, n_ref = bskv.forecast_block_score_topk(f, kc_next, topk, 1, 2, seq_len=c["seq_len"])
+    i_a, n_a = _next_lists(c2, kc_next, sc_a, topk, 1, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(i_b, i_own) and torch.equal(n_b, n_own)
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(sc_a.nan_to_num(7.0), sc_b.nan_to_num(7.0)), "128- and 256-row spans differ"
+    assert torch.equal(i_a, i_ref) and torch.equal(n_a, n_ref)
+    f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), Hkv, d)
+    kc_next_or = orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens)
+    sel = orc.decode_select(f_or, kc_next_or, np.array(lens), topk, 1, 2, 64)
+    check_selection(i_a, n_a, sel, topk)
+    sc = np64(sc_a)
+    for bg, row in enumerate(sel.scores):
+        b, g = divmod(bg, Hkv)
+        for j, v in row.items():
+            assert abs(sc[b, g, j] - v) <= 1e-4 * max(1.0, abs(v)), (b, g, j)
