@@ -277,9 +277,10 @@ struct DecodeCands {
   int cur, c0, c1;   // query block; candidates are [c0, c1)
 };
 
+// An empty sequence (L < 1) has no query block: cur = -1, and the union
+// then holds no initial, local or candidate block (cnt 0).
 __device__ __forceinline__ DecodeCands decode_cands(int64_t L, int64_t nb_cap, int n_init, int n_local) {
-  if (L < 1) L = 1;
-  int64_t cur = (L - 1) / kBlk;
+  int64_t cur = L < 1 ? -1 : (L - 1) / kBlk;
   if (cur > nb_cap - 1 + n_local) cur = nb_cap - 1 + n_local;   // never read past the cache
   DecodeCands r;
   r.cur = (int)cur;

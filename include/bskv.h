@@ -146,7 +146,8 @@ int bskv_kv_block_meanpool(const void* k, int dtype, const int64_t* kv_strides, 
  *
  * Decode (n_q_tokens == 0): f is the fp32 Forecast [B, n_kv_heads, head_dim]
  *   (f_dtype must be BSKV_F32); the query is the last cached token, so
- *   cur = (seq_len[b]-1)/block.  idx_out [B, Hkv, U], cnt_out [B, Hkv].
+ *   cur = (seq_len[b]-1)/block; an empty sequence (seq_len[b] 0) lists no
+ *   block (cnt 0).  idx_out [B, Hkv, U], cnt_out [B, Hkv].
  *   scores_out (nullable) [B, Hkv, kc_nb_cap]: s_j for candidates, -inf
  *   elsewhere up to cur; rows beyond cur untouched.
  * Prefill (n_q_tokens > 0): f holds one Forecast per token
@@ -260,7 +261,8 @@ int bskv_multihead_block_score_topk(const void* q, int q_dtype, const float* kc,
  *   out[b, h] = softmax_t(scale * q[b,h] . k_t) v_t
  *
  * over the tokens t of the listed blocks idx[b, g, 0..cnt-1] with position
- * < seq_len[b].  Two launches: splits over the listed blocks (fp32 online
+ * < seq_len[b]; a head with no such token (cnt 0, or seq_len[b] 0) gets the
+ * zero vector.  Two launches: splits over the listed blocks (fp32 online
  * softmax), then their merge in split order (deterministic).
  * q      [B, n_q_heads, head_dim] dtype, contiguous
  * k, v   cache (kv_is_ring == 0): block idx[u] is read at token idx[u]*block;
@@ -283,7 +285,8 @@ int bskv_block_sparse_attn_decode(const void* q, const void* k, const void* v, i
  * position p = q_start + t (chunk-relative t) attends to the tokens of its
  * query block's list idx[b, g, t/block, 0..cnt-1] at positions <= p: a
  * listed block before the query block is used whole, the query block itself
- * up to p, and a listed block after it not at all.
+ * up to p, and a listed block after it not at all.  A token with no such key
+ * (an empty list) gets the zero vector.
  * q      [B, n_q_heads, n_q_tokens, head_dim] bf16, contiguous
  * k, v   cache holding at least q_start + n_q_tokens tokens (bf16)
  * idx    [B, Hkv, n_qb, U] int32, cnt [B, Hkv, n_qb] int32

@@ -492,6 +492,10 @@ def prefill_select_pooled(f_pooled, kc, q_start: int, topk: int, n_init: int, n_
 # a4: attention over the selected blocks only
 # --------------------------------------------------------------------------
 def _softmax_attend(qrow, keys, vals, scale):
+    # Reading R19: a query with no token to attend to (an empty block list,
+    # or every listed token masked) gets the zero vector, the empty sum.
+    if keys.shape[0] == 0:
+        return np.zeros(vals.shape[-1])
     logits = (keys @ qrow) * scale
     w = np.exp(logits - logits.max())
     w /= w.sum()

@@ -1273,3 +1273,73 @@ def test_decode_layer_projection_spans_give_identical_scores():
         b, g = divmod(bg, Hkv)
         for j, v in row.items():
             assert abs(sc[b, g, j] - v) <= 1e-4 * max(1.0, abs(v)), (b, g, j)
+
+
+def test_empty_sequence_selects_nothing_and_attends_to_nothing():
+    """An empty sequence in the batch (seq_len 0) has no query block: the
+    Forecast, multi-head and window selectors list no block for it (cnt 0),
+    as the oracle does, and attention gives it the zero vector (reading R19);
+    a caller's empty list for one group zeroes that group's heads only.  The
+    fused decode layer does the same.  Every other row matches the oracle."""
+    B, Hkv, G, d, T, topk = 3, 2, 4, 128, 64 * 40, 8
+    lens = [64 * 40, 0, 64 * 17 + 3]
+    c = _gpu(random_decode_case(71, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16", hidden=512))
+    c2 = _gpu(random_decode_case(72, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16"))
+    seq_len = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    kc, kc_next = _kc_gpu(c["k"], seq_len), _kc_gpu(c2["k"], seq_len)
+    scale = 1.0 / math.sqrt(d)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], Hkv, d)
+    idx, cnt = bskv.forecast_block_score_topk(f, kc, topk, 1, 2, seq_len=seq_len)
+    mi, mc = bskv.multihead_block_score_topk(c["q"], kc, topk, 1, 2, seq_len, scale)
+    kcw = _kcw_gpu(c["k"], seq_len, 32, 16)
+    wi, wc = bskv.forecast_window_score_topk(f, kcw, topk, 1, 2, seq_len=seq_len)
+    cnt_e = cnt.clone()
+    cnt_e[2, 1] = 0
+    out = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt_e, seq_len, scale)
+    out_l, sc_next = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], seq_len, kc.clone(), idx, cnt, scale,
+                                                 x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk, n_init=1,
+                                                 n_local=2)
+    i_next, n_next = _next_lists(c2 | {"seq_len": seq_len}, kc_next, sc_next, topk, 1, 2)
+    torch.cuda.synchronize()
+    k64 = np64(c["k"])
+    f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), Hkv, d)
+    sel = orc.decode_select(f_or, orc.kv_block_meanpool(k64, 64, seq_len=lens), np.array(lens), topk, 1, 2, 64)
+    msel = orc.multihead_select_decode(np64(c["q"]), orc.kv_block_meanpool(k64, 64, seq_len=lens), np.array(lens),
+                                       topk, 1, 2, 64, scale)
+    wsel = orc.decode_select_windows(f_or, orc.kv_window_meanpool(k64, 32, 16, seq_len=lens), np.array(lens), topk,
+                                     1, 2, 64, 32, 16)
+    nsel = orc.decode_select(f_or, orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens), np.array(lens), topk, 1,
+                             2, 64)
+    for (i_, c_), s in (((idx, cnt), sel), ((mi, mc), msel), ((wi, wc), wsel), ((i_next, n_next), nsel)):
+        assert int(c_[1].abs().sum()) == 0 and bool((i_[1] == -1).all())
+        check_selection(i_, c_, s, topk)
+    want = orc.attend_decode(np64(c["q"]), k64, np64(c["v"]), idx.cpu().numpy(), cnt_e.cpu().numpy(), lens, scale, 64)
+    got = np64(out)
+    assert (got[1] == 0).all() and (got[2, G:] == 0).all()
+    assert max_abs(got, want) < 2e-2
+    want_l = orc.attend_decode(np64(c["q"]), k64, np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens, scale, 64)
+    assert (np64(out_l)[1] == 0).all()
+    assert max_abs(np64(out_l), want_l) < 2e-2
+
+
+def test_prefill_empty_list_gives_zero_rows():
+    """A query block whose list a caller leaves empty (cnt 0) gets zero
+    output rows (reading R19); the other query blocks are unchanged."""
+    d, G, Hkv, q_start, Tq = 128, 4, 2, 1024, 256
+    c, q_chunk, _, _, sel = _prefill_case(33, 1, Hkv * G, Hkv, d, 2048, q_start, Tq, topk=5, n_local=3)
+    idx = torch.from_numpy(sel.idx.astype(np.int32)).to(DEV)
+    cnt = torch.from_numpy(sel.cnt.astype(np.int32)).to(DEV)
+    cnt_e = cnt.clone()
+    cnt_e[0, 1, 2] = 0                          # KV head 1, third query block of the chunk
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt_e, q_start)
+    ref = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, q_start)
+    torch.cuda.synchronize()
+    got, full = np64(out), np64(ref)
+    assert (got[0, G:2 * G, 128:192] == 0).all()
+    mask = np.ones(got.shape, dtype=bool)
+    mask[0, G:2 * G, 128:192] = False
+    assert np.array_equal(got[mask], full[mask])
+    rows = [(0, h, t) for h in range(Hkv * G) for t in (0, 127, 128, 191, 192, 255)]
+    want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), sel.idx, cnt_e.cpu().numpy(), q_start,
+                              1.0 / math.sqrt(d), 64, rows=rows)
+    assert max(max_abs(got[r], want[r]) for r in rows) < 2e-2

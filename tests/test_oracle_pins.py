@@ -729,6 +729,42 @@ def test_chunked_prefill_equals_unchunked():
         np.testing.assert_allclose(part, whole[:, :, q0:q0 + 16], rtol=0, atol=1e-13)
 
 
+def test_empty_token_sets_give_zero_rows():
+    """Reading R19: a query with nothing to attend to (an empty sequence, a
+    group whose list is empty, a prefill query block with an empty list)
+    gets the zero vector; every other row is the brute-force dense-mask
+    result, so the convention touches the empty rows only."""
+    c = random_decode_case(11, B=3, Hq=4, Hkv=2, d=4, T=40, block=8)
+    q, k, v = _np(c["q"]), _np(c["k"]), _np(c["v"])
+    lens = np.array([40, 0, 21])
+    kc = orc.kv_block_meanpool(k, 8, seq_len=lens)
+    sel = orc.decode_select(_np(c["f"]), kc, lens, 1, 1, 1, 8)
+    # the empty sequence selects nothing: no initial, local or candidate block
+    assert (sel.cnt[1] == 0).all() and (sel.idx[1] == -1).all()
+    idx, cnt = sel.idx.copy(), sel.cnt.copy()
+    cnt[2, 1] = 0                                   # a caller's empty list for one group
+    got = orc.attend_decode(q, k, v, idx, cnt, lens, 0.37, 8)
+    assert (got[1] == 0).all() and (got[2, 2:] == 0).all()
+    keep = [(0, h) for h in range(4)] + [(2, 0), (2, 1)]
+    with np.errstate(invalid="ignore"):   # the brute force's emptied rows are 0/0 and are not compared
+        want = _dense_masked_decode(q[[0, 2]], k[[0, 2]], v[[0, 2]], idx[[0, 2]], cnt[[0, 2]], lens[[0, 2]], 0.37, 8)
+    for b, h in keep:
+        np.testing.assert_allclose(got[b, h], want[0 if b == 0 else 1, h], rtol=0, atol=1e-12)
+    # prefill: query block 1's list emptied, query block 0 untouched
+    rng = np.random.default_rng(12)
+    qq = rng.standard_normal((1, 2, 16, 4))
+    kk = rng.standard_normal((1, 1, 16, 4))
+    vv = rng.standard_normal((1, 1, 16, 4))
+    ps = orc.prefill_select(rng.standard_normal((1, 1, 16, 4)), orc.kv_block_meanpool(kk, 8), 0, 1, 1, 1, 8)
+    pc = ps.cnt.copy()
+    pc[0, 0, 1] = 0
+    out = orc.attend_prefill(qq, kk, vv, ps.idx, pc, 0, 0.5, 8)
+    assert (out[:, :, 8:] == 0).all()
+    ref = orc.attend_prefill(qq, kk, vv, ps.idx, ps.cnt, 0, 0.5, 8)
+    np.testing.assert_array_equal(out[:, :, :8], ref[:, :, :8])
+    assert np.abs(ref[:, :, 8:]).max() > 0
+
+
 def test_attention_is_convex_combination():
     c = random_decode_case(5, B=1, Hq=4, Hkv=1, d=8, T=128, block=16)
     q, k, v = _np(c["q"]) * 4, _np(c["k"]), _np(c["v"])
