@@ -23,7 +23,11 @@
 //     workgroup, else two) filled by gfx950's global-to-LDS copies
 //     (global_load_lds_dwordx4): no registers hold the blocks in transit and
 //     no LDS writes are issued, and with four stages a block's copy is issued
-//     four slots before its first read.  Rows are unpadded (a copy writes
+//     four slots before its first read.  With four heads per workgroup group
+//     B issues every copy, in its softmax slots, so the MFMA slots carry no
+//     copy work (774-780 vs 786-792 us per B4 x 128K chunk with each wave
+//     copying its share, the MFMA group included); the smaller forms keep
+//     every wave copying.  Rows are unpadded (a copy writes
 //     1024 contiguous bytes) with 16-byte chunks XOR-swizzled per row, which
 //     keeps the K fragment reads and the transposing V reads
 //     (ds_read_b64_tr_b16, two per operand) free of extra bank conflicts.
@@ -65,8 +69,13 @@ __global__ __launch_bounds__(HPW * 128, (HPW == 1 && D == 128) ? 1 : 2) void att
   constexpr int RB = D * 2;            // bytes per K/V row
   constexpr int RCH = D / 8;           // 16-byte chunks per row
   constexpr int TILE = BLK * RB;       // bytes of one K or V block
-  constexpr int PPW = TILE / 1024 / NW;  // 1024-byte copy pieces per wave per tile
-  static_assert(PPW >= 1 && PPW * NW * 1024 == TILE, "copy pieces");
+  // the waves that copy K/V tiles: group B's with four heads per workgroup
+  // (the MFMA slots then carry no copy work), every wave otherwise (fewer
+  // copy pieces per wave: the two-head form would spill registers)
+  constexpr bool B_COPIES = HPW == 4;
+  constexpr int NCW = B_COPIES ? NW / 2 : NW;
+  constexpr int PPW = TILE / 1024 / NCW;  // 1024-byte copy pieces per copying wave per tile
+  static_assert(PPW >= 1 && PPW * NCW * 1024 == TILE, "copy pieces");
   // ring stages: four (a copy is issued four slots before its block is
   // read) for four heads per workgroup, two otherwise (so that two
   // workgroups still share a CU)
@@ -166,15 +175,15 @@ __global__ __launch_bounds__(HPW * 128, (HPW == 1 && D == 128) ? 1 : 2) void att
   // outside them is masked whole and its copy reads block 0 instead (K/V
   // hold at least one block here), so the stage holds finite values
   auto valid = [&](int jj) { return jj >= 0 && ((int64_t)jj + 1) * BLK <= kv_len; };
-  // this lane's share of a tile: piece wid*PPW + i covers LDS chunks
-  // 64 (wid*PPW + i) + lane, i.e. row r, stored chunk cs; the global chunk
-  // is the logical one, cs ^ swizzle(r)
+  // this lane's share of a tile: piece (wid - HPW)*PPW + i (group B copying)
+  // or wid*PPW + i (every wave) covers LDS chunks 64 piece + lane, i.e. row
+  // r, stored chunk cs; the global chunk is the logical one, cs ^ swizzle(r)
   const uint32_t ks_base = lds_u32(&Ks[0][0]), vs_base = lds_u32(&Vs[0][0]);
   auto copy_tile = [&](const bf16_bits* base, uint32_t lds_stage, int jj, bool is_v) {
     const bf16_bits* p0 = base + (int64_t)(valid(jj) ? jj : 0) * BLK * st;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-      const int piece = wid * PPW + i;
+      const int piece = (B_COPIES ? wid - HPW : wid) * PPW + i;
       const int qc = piece * 64 + lane, r = qc / RCH, cs = qc % RCH;
       const int cl = cs ^ (is_v ? 2 * (r % MD) : r % RCH);
       lds_dma16(p0 + (int64_t)r * st + cl * 8, __builtin_amdgcn_readfirstlane(lds_stage + piece * 1024));
@@ -314,22 +323,26 @@ __global__ __launch_bounds__(HPW * 128, (HPW == 1 && D == 128) ? 1 : 2) void att
   // Slots: group A runs M(0) S(0) M(1) S(1) ... S(c-1) M(c) in slots 0..2c,
   // group B the same sequence in slots 1..2c+1, where M(a) is the MFMA slot
   // of block a and S(a) its softmax slot; one barrier closes each slot.  K(u)
-  // is read in slots 2u and 2u+1, V(u) in slots 2u+2 and 2u+3.  Every wave
-  // copies its share of each tile: at the start of even slot 2m the copies
-  // of V(m-2+NST) and K(m-1+NST) go into the stages of V(m-2) and K(m-1),
-  // last read in slot 2m-1; before the barrier closing slot 2m-1 each wave
-  // waits for its copies of K(m) and V(m-1).  The prologue issues the copies
+  // is read in slots 2u and 2u+1, V(u) in slots 2u+2 and 2u+3.  The copying
+  // waves (group B with four heads, where it runs S(m-1) or, m = 0, idles;
+  // else every wave) issue their share of each tile at the start of even
+  // slot 2m: V(m-2+NST) and K(m-1+NST) go into the stages of V(m-2) and
+  // K(m-1), last read in slot 2m-1; before the barrier closing slot 2m-1
+  // each copying wave waits for its copies of K(m) and V(m-1), so after
+  // that barrier every wave may read them.  The prologue issues the copies
   // of the slots before 0 (K(0..NST-2), V(0..NST-3)) and waits for K(0).
+  if (!B_COPIES || grp == 1) {
 #pragma unroll
-  for (int m = 1 - NST; m < 0; ++m) issue(m);
-  wait_copies(0);
+    for (int m = 1 - NST; m < 0; ++m) issue(m);
+    wait_copies(0);
+  }
   __syncthreads();
   if (grp == 1) {                      // slot 0: group B idle
     issue(0);
     __syncthreads();
   }
   for (int a = 0;; ++a) {
-    if (grp == 0) issue(a);            // A: slot 2a
+    if (!B_COPIES && grp == 0) issue(a);   // A: slot 2a
     __builtin_amdgcn_s_setprio(1);
     mfma_slot(a);
     __builtin_amdgcn_s_setprio(0);
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(HPW * 128, (HPW == 1 && D == 128) ? 1 : 2) void att
     if (a == c) break;
     if (grp == 1) issue(a + 1);        // B: slot 2a+2
     softmax_slot(a);
-    if (grp == 0) wait_copies(a + 1);  // A: slot 2a+1 closes
+    if (!B_COPIES && grp == 0) wait_copies(a + 1);   // A: slot 2a+1 closes
     __syncthreads();
   }
   if (grp == 0) __syncthreads();       // slot 2c+1: group A idle
