@@ -60,9 +60,9 @@ PMC_TRAFFIC = {
     "layer_k2": {"fetch_kib": 103802.4, "write_kib": 1194.6, "fetch_scale": 2.0, "write_scale": 1.0,
                  "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
                  "sha256": "45f03f1a8924ecb849e1f28c4da9d1c9cf9dd93b0d19649f42678ec4d0849e26"},
-    "attn_prefill": {"fetch_kib": 367001.7, "write_kib": 65536.1, "fetch_scale": 2.0, "write_scale": 1.0,
+    "attn_prefill": {"fetch_kib": 366793.8, "write_kib": 65537.0, "fetch_scale": 2.0, "write_scale": 1.0,
                      "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                     "sha256": "a8258c7cfbbf494ba860b1227bec3a9d5de1a40e2719da36293943b8e5042893"},
+                     "sha256": "8579e641ec7c6cd782d2afd4e69ede7a0b13a6e53a14d83f5abfd243e51e7ce1"},
 }
 
 
