@@ -59,7 +59,7 @@ METRIC = "decode select+sparse-attn tokens/s at B×T (e.g. B8,128K); % HBM peak"
 PMC_TRAFFIC = {
     "layer_k2": {"fetch_kib": 103802.4, "write_kib": 1194.6, "fetch_scale": 2.0, "write_scale": 1.0,
                  "sources": ['block_sparse_long_kv_amd/csrc/fused_decode.hip', 'block_sparse_long_kv_amd/csrc/decode_ops.hpp', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
-                 "sha256": "45f03f1a8924ecb849e1f28c4da9d1c9cf9dd93b0d19649f42678ec4d0849e26"},
+                 "sha256": "7d5d7755f940a734ca4621627c724962321d0f4cd7463db6939bb6a426c72319"},
     "attn_prefill": {"fetch_kib": 366793.8, "write_kib": 65537.0, "fetch_scale": 2.0, "write_scale": 1.0,
                      "sources": ['block_sparse_long_kv_amd/csrc/attn_prefill.hip', 'block_sparse_long_kv_amd/csrc/bskv_device.hpp', 'block_sparse_long_kv_amd/csrc/bskv_launch.hpp'],
                      "sha256": "8579e641ec7c6cd782d2afd4e69ede7a0b13a6e53a14d83f5abfd243e51e7ce1"},

@@ -49,7 +49,7 @@ constexpr int kProjRows = 256;
 // bf16 (MFMA) workgroups take 128 or 256 rows of W but always store one
 // partial per 128 rows, so every caller sums the same partials in the same
 // order: the fused layer's first kernel spans 128 rows when it carries no
-// top-k (256 workgroups at hidden 4096; B4 x 32K layer-step 1 us shorter),
+// top-k (256 workgroups at hidden 4096; B4 x 32K: that kernel 4.2 vs 5.1 us),
 // 256 rows beside the top-k, and the standalone projection 256.
 constexpr int kProjPartRows = 128;
 constexpr int kProjPass = 4;     // batch rows per pass
