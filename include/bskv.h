@@ -93,7 +93,9 @@ const char* bskv_last_error(void);
  * w      [hidden, n_kv_heads*head_dim] dtype, contiguous (row-major)
  * f_out  [B, n_kv_heads, head_dim]   fp32, contiguous
  * hidden must be a multiple of 256.  ws: bskv_forecast_proj_workspace().
- * Two launches: 256-row partial products, then their sum in split order.
+ * Two launches: partial products (per 128 rows of w for bf16, 256 for
+ * fp32), then their sum in row order; the fused decode layer adds the same
+ * partials in the same order, so both give bit-identical Forecasts.
  * The same call serves the separate layer-0 projection ([EXPL] "Training"):
  * pass that projection's weights.  Deterministic: fixed summation order.
  * ----------------------------------------------------------------------- */
