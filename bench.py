@@ -720,10 +720,10 @@ def run_decode(args, torch, bskv, wl, replicas=None):
 # tiny fp32 decode (a correctness configuration: launch-bound)
 # ---------------------------------------------------------------------------
 def run_tiny(args, torch, bskv, wl):
-    """B1 x 4096, fp32, Forecast vectors given: newest-block pooling, score +
-    top-k + union, attention (split + merge) per step.  The work is ~378 KB,
-    so the step is launch-bound; the HBM fraction is reported but not
-    meaningful."""
+    """B1 x 4096, fp32, Forecast vectors given: score + top-k + union, then
+    attention (split + merge) with the newest-block pooling, per step (three
+    launches).  The work is ~378 KB, so the step is launch-bound; the HBM
+    fraction is reported but not meaningful."""
     from workloads import decode_inputs
     dev = torch.device("cuda:0")
     lay = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in decode_inputs(wl, "cpu")[0].items()}
@@ -735,15 +735,18 @@ def run_tiny(args, torch, bskv, wl):
     out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.float32, device=dev)
     ws_s = torch.zeros(max(256, bskv.workspace_bytes("score", wl.B, wl.Hkv, 0, nb, wl.d)), dtype=torch.uint8,
                        device=dev)
-    ws_a = torch.zeros(max(256, bskv.workspace_bytes("attn", wl.B, wl.Hq, wl.Hkv, wl.d, wl.U)), dtype=torch.uint8,
-                       device=dev)
+    ws_l = torch.zeros(max(256, bskv.workspace_bytes("layer", wl.B, wl.Hq, wl.Hkv, wl.d, 0, nb, wl.U, 0)),
+                       dtype=torch.uint8, device=dev)
 
     def step():
-        bskv.kv_block_meanpool(lay["k"], lay["seq_len"], kc, 0, nb, newest_only=True)
+        # selection from the given Forecast (scores, then top-k + union), then
+        # the fused layer's second kernel alone (no lookahead): attention
+        # splits, their merge and the newest-block pooling in one launch (the
+        # newest block is local, so the selection never reads its row)
         bskv.forecast_block_score_topk(lay["f"], kc, wl.topk, wl.n_init, wl.n_local, seq_len=lay["seq_len"],
                                        idx=idx, cnt=cnt, ws=ws_s)
-        bskv.block_sparse_attn_decode(lay["q"], lay["k"], lay["v"], idx, cnt, lay["seq_len"], wl.scale, out=out,
-                                      ws=ws_a)
+        bskv.decode_layer_lookahead(lay["q"], lay["k"], lay["v"], lay["seq_len"], kc, idx, cnt, wl.scale, out=out,
+                                    topk=wl.topk, n_init=wl.n_init, n_local=wl.n_local, ws=ws_l)
 
     step_s, _ = time_graph(torch, step, args.steps, args.warmup, use_graph=not args.no_graph)
     e = 4
