@@ -1343,3 +1343,43 @@ def test_prefill_empty_list_gives_zero_rows():
     want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), sel.idx, cnt_e.cpu().numpy(), q_start,
                               1.0 / math.sqrt(d), 64, rows=rows)
     assert max(max_abs(got[r], want[r]) for r in rows) < 2e-2
+
+
+def test_prefill_attention_lists_longer_than_128_blocks():
+    """Block lists of up to 159 entries (top-k 150 + 1 initial + 8 local):
+    the prefill kernel's ring runs through more than a hundred blocks per
+    query block; sampled rows against the oracle."""
+    d, G, Hkv, T, q_start, Tq, topk, n_local = 128, 4, 1, 64 * 300, 64 * 280, 256, 150, 8
+    c, q_chunk, idx, cnt, sel = _prefill_case(81, 1, Hkv * G, Hkv, d, T, q_start, Tq, topk=topk, n_local=n_local)
+    check_selection(idx, cnt, sel, topk)
+    assert int(cnt.max()) == topk + 1 + n_local
+    out = bskv.block_sparse_attn_prefill(q_chunk, c["k"], c["v"], idx, cnt, q_start)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = [(0, h, int(t)) for h in range(Hkv * G) for t in rng.choice(Tq, 6, replace=False)]
+    rows += [(0, 0, 0), (0, Hkv * G - 1, Tq - 1)]
+    want = orc.attend_prefill(np64(q_chunk), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(),
+                              q_start, 1.0 / math.sqrt(d), 64, rows=rows)
+    got = np64(out)
+    assert max(max_abs(got[r], want[r]) for r in rows) < 2e-2
+
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 2)])
+def test_decode_attention_lists_longer_than_128_blocks(dtype, d, G):
+    """Decode selection and attention with U = 203 (top-k 200): many blocks
+    per attention split, against the oracle."""
+    B, Hkv, T, topk = 2, 2, 64 * 400, 200
+    lens = [64 * 400, 64 * 371 + 9]
+    c = _gpu(random_decode_case(91, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype=dtype, seq_len=lens))
+    kc = _kc_gpu(c["k"], c["seq_len"])
+    idx, cnt = bskv.forecast_block_score_topk(c["f"], kc, topk, 1, 2, seq_len=c["seq_len"])
+    scale = 1.0 / math.sqrt(d)
+    out = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    torch.cuda.synchronize()
+    sel = orc.decode_select(np64(c["f"]), orc.kv_block_meanpool(np64(c["k"]), 64, seq_len=lens), np.array(lens), topk,
+                            1, 2, 64)
+    check_selection(idx, cnt, sel, topk)
+    assert int(cnt.max()) == topk + 3
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens,
+                             scale, 64)
+    assert max_abs(np64(out), want) < (1e-4 if dtype == "f32" else 2e-2)
