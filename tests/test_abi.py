@@ -359,3 +359,23 @@ def test_noalloc_layer_rejects_oversized_workspace_on_the_host():
     assert call(B=512) == ENOSPC
     assert b"16 MiB" in lib.bskv_last_error()
     assert call(hq=24) == EINVAL
+
+
+def test_largest_unit_counts_are_rejected_on_the_host():
+    """B * n_kv_heads above 65535 (the decode calls' per-(b, g) grid and the
+    fused layer's counter region) is BSKV_EUNSUPPORTED, found before any
+    workspace check or launch; 65535 itself passes that check (and then
+    fails only on the deliberately small workspace)."""
+    att = lib.bskv_block_sparse_attn_decode
+    lay = lib.bskv_decode_layer_lookahead
+
+    def call_att(B, hkv):
+        return att(P, P, P, 1, S3, 131072, 0, P, P, P, B, 4 * hkv, hkv, 128, 64, 69, 0.088, P, P, 256, None)
+
+    def call_lay(B, hkv):
+        return lay(P, P, P, 1, S3, 131072, P, P, None, P, P, 0.088, P, None, None, 0, None, None, None, None, B,
+                   4 * hkv, hkv, 128, 64, 2048, 64, 1, 4, 3, P, 256, None)
+    for fn in (call_att, call_lay):
+        assert fn(8192, 8) == EUNSUP          # 65536 units
+        assert fn(65536, 1) == EUNSUP
+        assert fn(65535, 1) == ENOSPC         # at the limit: only the workspace is short
