@@ -1383,3 +1383,46 @@ def test_decode_attention_lists_longer_than_128_blocks(dtype, d, G):
     want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens,
                              scale, 64)
     assert max_abs(np64(out), want) < (1e-4 if dtype == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("immediate", [False, True])
+def test_decode_layer_above_64_units(immediate):
+    """The fused layer above 64 (b, g) units (B20 x 8 KV heads = 160), where
+    its plans take 768 score and 768 attention workgroups, more than the
+    chip holds at once: lists, raw scores and outputs equal the per-op path
+    and the oracle, ragged lengths, and the counters end at zero."""
+    B, Hkv, G, d, T, topk = 20, 8, 4, 128, 64 * 60, 16
+    lens = [64 * 60 - (7 * b) % 200 for b in range(B)]
+    c = _gpu(random_decode_case(95, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16", hidden=1024, seq_len=lens))
+    c2 = _gpu(random_decode_case(96, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dtype="bf16", seq_len=lens))
+    kc, kc_next = _kc_gpu(c["k"], c["seq_len"]), _kc_gpu(c2["k"], c2["seq_len"])
+    nb = kc.shape[2]
+    scale = 1.0 / math.sqrt(d)
+    f = bskv.forecast_proj(c["x_sel"], c["w_sel"], Hkv, d)
+    idx, cnt = bskv.forecast_block_score_topk(c2["f"], kc, topk, 1, 2, seq_len=c["seq_len"])
+    i_ref, n_ref = bskv.forecast_block_score_topk(f, kc_next, topk, 1, 2, seq_len=c["seq_len"])
+    out_ref = bskv.block_sparse_attn_decode(c["q"], c["k"], c["v"], idx, cnt, c["seq_len"], scale)
+    ws = torch.zeros(bskv.workspace_bytes("layer", B, Hkv * G, Hkv, d, 1024, nb, topk + 3, 1), dtype=torch.uint8,
+                     device=DEV)
+    if immediate:
+        i_next = torch.full_like(idx, -7)
+        n_next = torch.full_like(cnt, -7)
+        out, _ = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, scale,
+                                             x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, idx_next=i_next,
+                                             cnt_next=n_next, topk=topk, n_init=1, n_local=2, ws=ws)
+    else:
+        out, sc = bskv.decode_layer_lookahead(c["q"], c["k"], c["v"], c["seq_len"], kc.clone(), idx, cnt, scale,
+                                              x=c["x_sel"], w=c["w_sel"], kc_next=kc_next, topk=topk, n_init=1,
+                                              n_local=2, ws=ws)
+        i_next, n_next = _next_lists(c2, kc_next, sc, topk, 1, 2, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    assert torch.equal(i_next, i_ref) and torch.equal(n_next, n_ref)
+    assert int(ws[: 2 * 65535 * 4].view(torch.int32).abs().sum()) == 0
+    f_or = orc.forecast_proj(np64(c["x_sel"]), np64(c["w_sel"]), Hkv, d)
+    sel = orc.decode_select(f_or, orc.kv_block_meanpool(np64(c2["k"]), 64, seq_len=lens), np.array(lens), topk, 1, 2,
+                            64)
+    check_selection(i_next, n_next, sel, topk)
+    want = orc.attend_decode(np64(c["q"]), np64(c["k"]), np64(c["v"]), idx.cpu().numpy(), cnt.cpu().numpy(), lens,
+                             scale, 64)
+    assert max_abs(np64(out), want) < 2e-2
